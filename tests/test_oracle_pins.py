@@ -1,0 +1,440 @@
+"""Pins for the CPU oracle against what the pages and the mathematics fix.
+
+Sources: "MoE Load Balancing: Find Expert Hotspots" (the 16-token fixture and
+its printed demand, balancedness, rank demand, capacity ledgers and remote
+routes), "MoE load balancing: 90/10 routing in production" (the nine-times
+share and the bias kept out of the gate), the MoonEP news article (maxvio is
+zero when balanced; equal per-rank load however skewed; slots = experts per
+rank keeps every touched expert local).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _pairs(g):
+    return np.array([[int(p[0]), int(p[1])] for p in g["pairs"].split(",")], np.int32)
+
+
+FIX = _gold("fixture16.json")
+DER = _gold("fixture16_plan_derived.json")
+
+
+def _mapping(groups, E):
+    m = np.empty(E, np.int32)
+    for r, grp in enumerate(groups):
+        for e in grp:
+            m[e] = r
+    return m
+
+
+# ---------------------------------------------------------------- router ----
+
+def test_fixture_logits_route_to_page_pairs():
+    ids, w, err = oracle.route(synth.fixture_logits(), None, 2)
+    assert err == 0
+    np.testing.assert_array_equal(ids, _pairs(FIX))
+
+
+def test_fixture_weights_closed_form():
+    # logits 2 and 1 -> weights e/(e+1) and 1/(e+1) = logistic(1), logistic(-1)
+    _, w, _ = oracle.route(synth.fixture_logits(), None, 2)
+    np.testing.assert_allclose(w[:, 0], 0.7310585786300049, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(w[:, 1], 0.2689414213699951, rtol=0, atol=1e-15)
+
+
+def test_bias_moves_selection_not_weights():
+    # A bias of +5 on every token's second expert reorders the pair; each
+    # expert keeps the weight its raw logit earns (bias outside the gate).
+    lg = synth.fixture_logits()
+    pairs = _pairs(FIX)
+    for t in range(16):
+        bias = np.zeros(8, np.float32)
+        bias[pairs[t, 1]] = 5.0
+        ids, w, err = oracle.route(lg[t:t + 1], bias, 2)
+        assert err == 0
+        assert list(ids[0]) == [pairs[t, 1], pairs[t, 0]]
+        assert w[0, 0] == pytest.approx(0.2689414213699951, abs=1e-15)
+        assert w[0, 1] == pytest.approx(0.7310585786300049, abs=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_matches_full_stable_sort(seed):
+    rng = np.random.default_rng(seed)
+    T, E = 64, [8, 13, 64, 128, 256, 5][seed]
+    k = min(E, [2, 3, 8, 8, 8, 5][seed])
+    # coarse values so that ties (including -0 vs +0) are frequent
+    lg = (rng.integers(-4, 5, size=(T, E)) * 0.5).astype(np.float32)
+    lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, -0.0, 0.0).astype(np.float32)
+    bias = (rng.integers(-2, 3, size=E) * 0.25).astype(np.float32) if seed % 2 else None
+    ids, w, err = oracle.route(lg, bias, k)
+    assert err == 0
+    for t in range(T):
+        s = lg[t] + (bias if bias is not None else np.float32(0))
+        s = s.astype(np.float32)
+        order = sorted(range(E), key=lambda e: (-float(s[e]), e))[:k]
+        assert list(ids[t]) == order
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert (w >= 0).all()
+
+
+def test_route_single_expert_weight_is_one():
+    lg = synth.router_logits(32, 16, 7)
+    _, w, _ = oracle.route(lg, None, 1)
+    np.testing.assert_array_equal(w, 1.0)
+
+
+def test_route_weights_equal_renormalised_full_softmax():
+    # softmax over the top-k == full softmax restricted to the top-k, renormalised
+    lg = synth.router_logits(16, 32, 3)
+    ids, w, _ = oracle.route(lg, None, 4)
+    full = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(full, ids, axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_route_negative_zero_ties_lower_id():
+    lg = np.array([[-0.0, 0.0, -1.0, 0.0]], np.float32)
+    ids, _, _ = oracle.route(lg, None, 3)
+    assert list(ids[0]) == [0, 1, 3]
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_route_flags_nonfinite(bad):
+    lg = synth.router_logits(4, 8, 1)
+    lg[2, 5] = bad
+    assert oracle.route(lg, None, 2)[2] & 1
+    bias = np.zeros(8, np.float32)
+    bias[3] = bad
+    assert oracle.route(synth.router_logits(4, 8, 1), bias, 2)[2] & 1
+
+
+# ---------------------------------------------------------------- counts ----
+
+def test_fixture_demand_and_rank_demand():
+    c = oracle.count(_pairs(FIX), 8, 4)
+    assert c["err"] == 0
+    np.testing.assert_array_equal(c["counts"], FIX["demand"])
+    assert c["counts"].sum() == FIX["assignments"] == FIX["T"] * FIX["k"]
+    np.testing.assert_array_equal(c["rank_load"], FIX["rank_demand_home"])
+    np.testing.assert_array_equal(c["offsets"], np.concatenate([[0], np.cumsum(FIX["demand"])]))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_eidx_is_a_stable_sort(seed):
+    # offsets[e] + eidx == position of the assignment in a stable sort by expert
+    rng = np.random.default_rng(100 + seed)
+    T, E, k = 200, [8, 16, 128, 256][seed], [2, 4, 8, 8][seed]
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    c = oracle.count(ids, E, [4, 4, 16, 32][seed])
+    flat = ids.ravel()
+    order = np.argsort(flat, kind="stable")
+    pos = np.empty_like(order)
+    pos[order] = np.arange(flat.size)
+    np.testing.assert_array_equal(c["offsets"][flat] + c["eidx"], pos)
+    np.testing.assert_array_equal(c["counts"], np.bincount(flat, minlength=E))
+
+
+def test_count_flags_range_and_repeats():
+    ids = _pairs(FIX).copy()
+    ids[3, 1] = 8
+    assert oracle.count(ids, 8, 4)["err"] & 2
+    ids = _pairs(FIX).copy()
+    ids[5, 1] = ids[5, 0]
+    assert oracle.count(ids, 8, 4)["err"] & 4
+    ids = _pairs(FIX).copy()
+    ids[0, 0] = -1
+    assert oracle.count(ids, 8, 4)["err"] & 2
+
+
+# ----------------------------------------------------------------- stats ----
+
+def test_fixture_statistics():
+    ids = _pairs(FIX)
+    c = oracle.count(ids, 8, 4)
+    prop = _mapping(FIX["proposed_mapping"], 8)
+    st = oracle.stats(ids, c["counts"], 4, mapping=prop, capacity_factor=FIX["capacity_factor"])
+    a, b = FIX["balancedness_expert"]
+    assert st["balancedness_expert"] == a / b
+    assert st["balancedness_expert"] == pytest.approx(0.444444, abs=5e-7)
+    # maxvio read as max/mean - 1: 9/4 - 1
+    assert st["maxvio_expert"] == 1.25
+    a, b = FIX["balancedness_rank_home"]
+    assert st["balancedness_rank_home"] == a / b
+    assert st["balancedness_rank_home"] == pytest.approx(0.533333, abs=5e-7)
+    np.testing.assert_array_equal(st["home_load"], FIX["rank_demand_home"])
+    np.testing.assert_array_equal(st["mapped_load"], FIX["rank_demand_proposed"])
+    a, b = FIX["balancedness_rank_proposed"]
+    assert st["balancedness_rank_mapped"] == a / b == 0.8
+    assert st["capacity"] == FIX["capacity"]
+    assert st["processed"] == FIX["processed_sum"]
+    assert st["overflow"] == FIX["overflow_sum"]
+    assert st["padding"] == FIX["padding_sum"]
+    assert st["remote_home"] == FIX["remote_home"]
+    assert st["remote_mapped"] == FIX["remote_proposed"]
+    assert st["remote_home"] / st["N"] == FIX["remote_share_home"]
+    assert st["remote_mapped"] / st["N"] == FIX["remote_share_proposed"]
+
+
+def test_fixture_capacity_ledgers():
+    cap = oracle.capacity(32, 8, 1.25)
+    assert cap == FIX["capacity"]
+    proc, over, pad = oracle.ledgers(FIX["demand"], cap)
+    np.testing.assert_array_equal(proc, FIX["processed"])
+    np.testing.assert_array_equal(over, FIX["overflow"])
+    np.testing.assert_array_equal(pad, FIX["padding"])
+    # processed + padding fills every expert's capacity; processed + overflow is raw demand
+    assert proc.sum() + pad.sum() == 8 * cap
+    np.testing.assert_array_equal(proc + over, FIX["demand"])
+
+
+def test_survivorship_traps_change_the_numbers():
+    # the page's three traps each produce a different (wrong) value
+    d = np.array(FIX["demand"])
+    proc, _, _ = oracle.ledgers(d, 5)
+    st_raw = oracle.stats(_pairs(FIX), d, 4)
+    assert st_raw["max_count"] == 9 and proc.max() == 5            # demand after dropping overflow
+    assert st_raw["balancedness_expert"] != (16 / 8) / 9            # tokens instead of assignments
+    assert st_raw["balancedness_expert"] != 9 / 4                   # max/mean instead of mean/max
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_maxvio_zero_iff_equal(seed):
+    rng = np.random.default_rng(seed)
+    E, R = 8, 4
+    if seed % 2:
+        counts = np.full(E, int(rng.integers(1, 20)), np.int32)
+    else:
+        counts = rng.integers(0, 20, E).astype(np.int32)
+        if (counts == counts[0]).all():
+            counts[0] += 1
+    ids = np.zeros((1, 1), np.int32)
+    st = oracle.stats(ids, counts, R)
+    assert (st["maxvio_expert"] == 0.0) == bool((counts == counts[0]).all())
+    assert st["maxvio_expert"] >= 0
+
+
+def test_nine_times_share():
+    # 90% of the assignments on 26 of 256 experts: 0.9 / (26/256) ~ 8.86
+    counts = np.array([1035] * 26 + [13] * 230, np.int32)
+    assert counts[:26].sum() == 0.9 * counts.sum()
+    assert oracle.hot_share(counts, 26) == pytest.approx(0.9 / (26 / 256), rel=1e-12)
+    assert round(oracle.hot_share(counts, 26)) == 9
+
+
+def test_empty_load_statistics():
+    st = oracle.stats(np.zeros((0, 2), np.int32), np.zeros(8, np.int32), 4)
+    assert st["maxvio_expert"] == 0.0 and st["balancedness_expert"] == 1.0
+
+
+# ------------------------------------------------------------------ plan ----
+
+def check_plan_invariants(counts, R, pl):
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    n = E // R
+    N = int(counts.sum())
+    q = pl["quota"]
+    assert q.sum() == N
+    assert set(q.tolist()) <= {N // R, -(-N // R)}
+    assert pl["win_off"][0] == 0
+    np.testing.assert_array_equal(np.diff(pl["win_off"]), q)
+    per_expert = np.zeros(E, np.int64)
+    receivers = 0
+    for r in range(R):
+        ns = pl["seg_num"][r]
+        ex = pl["seg_expert"][r, :ns]
+        rows = pl["seg_row"][r, :ns]
+        cnt = pl["seg_cnt"][r, :ns]
+        assert (pl["seg_expert"][r, ns:] == -1).all()
+        assert (cnt > 0).all()
+        assert cnt.sum() == q[r]                                   # equal load
+        assert (np.diff(ex) > 0).all()                             # expert id ascending
+        if ns:
+            assert rows[0] == pl["win_off"][r]
+            np.testing.assert_array_equal(rows[1:], rows[:-1] + cnt[:-1])
+        for e, c in zip(ex, cnt):
+            per_expert[e] += c
+        foreign = [e for e in ex if e // n != r]
+        assert len(foreign) == pl["slots_needed"][r] <= n          # <= n replicas per rank
+        assert sorted(foreign) == [e for e in pl["slot_expert"][r] if e >= 0]
+        if foreign:
+            receivers += 1
+            donors = {e // n for e in foreign}
+            assert donors == {pl["donor"][r]}                      # a single donor rank
+    np.testing.assert_array_equal(per_expert, counts)              # exactly once
+    assert receivers <= max(R - 1, 0)
+    home = np.array([counts[r * n:(r + 1) * n].sum() for r in range(R)])
+    balanced = bool((home == q).all())
+    assert balanced == (pl["slots_needed"].sum() == 0)             # replicas only when needed
+    # pieces: rank ascending, consistent with segments
+    for e in range(E):
+        np_ = pl["piece_num"][e]
+        ranks = pl["piece_rank"][e, :np_]
+        assert (np.diff(ranks) > 0).all()
+        assert pl["piece_cnt"][e, :np_].sum() == counts[e]
+        for r, row, c in zip(ranks, pl["piece_row"][e, :np_], pl["piece_cnt"][e, :np_]):
+            i = list(pl["seg_expert"][r, :pl["seg_num"][r]]).index(e)
+            assert pl["seg_row"][r, i] == row and pl["seg_cnt"][r, i] == c
+
+
+def test_fixture_plan_derived_golden():
+    pl = oracle.plan(FIX["demand"], 4)
+    np.testing.assert_array_equal(pl["quota"], DER["quota"])
+    np.testing.assert_array_equal(pl["win_off"], DER["win_off"])
+    for r in range(4):
+        segs = [[int(pl["seg_expert"][r, i]), int(pl["seg_row"][r, i]), int(pl["seg_cnt"][r, i])]
+                for i in range(pl["seg_num"][r])]
+        assert segs == DER["segments"][str(r)]
+    np.testing.assert_array_equal(pl["slot_expert"], DER["slot_expert"])
+    np.testing.assert_array_equal(pl["donor"], DER["donor"])
+    check_plan_invariants(FIX["demand"], 4, pl)
+
+
+def test_plan_exhaustive_small():
+    seen = 0
+    for E, R in [(1, 1), (2, 1), (2, 2), (3, 3), (4, 2), (4, 4), (6, 2), (6, 3), (6, 6)]:
+        hi = 4 if E <= 4 else 3
+        for counts in itertools.product(range(hi + 1), repeat=E):
+            if sum(counts) > 12:
+                continue
+            check_plan_invariants(counts, R, oracle.plan(counts, R))
+            seen += 1
+    assert seen > 3000
+
+
+@pytest.mark.parametrize("E,R", [(8, 4), (8, 8), (128, 16), (256, 32), (128, 1), (64, 64)])
+def test_plan_random_skew(E, R):
+    rng = np.random.default_rng(E * 1000 + R)
+    for trial in range(300 if E <= 8 else 60):
+        kind = trial % 3
+        if kind == 0:
+            counts = rng.integers(0, 50, E)
+        elif kind == 1:
+            counts = rng.zipf(1.5, E).clip(max=5000)
+        else:
+            counts = np.zeros(E, np.int64)
+            counts[rng.integers(0, E)] = rng.integers(1, 5000)
+        check_plan_invariants(counts, R, oracle.plan(counts, R))
+
+
+def test_plan_slots_equal_experts_per_rank_keeps_everything_local():
+    # with S = n slots every replica fits a slot, so no row is non-local
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        counts = rng.zipf(1.3, 128).clip(max=4000).astype(np.int32)
+        pl = oracle.plan(counts, 16)
+        ids = np.zeros((1, 1), np.int32)
+        st = oracle.stats(ids, counts, 16, S=8, pl=pl)
+        assert st["ranks_over_slots"] == 0 and st["nonlocal_rows"] == 0
+        assert st["planned_max"] - st["planned_min"] <= 1
+        assert st["maxvio_rank_planned"] <= (-(-counts.sum() // 16) * 16 - counts.sum()) / counts.sum()
+
+
+def test_plan_balanced_input_has_no_replicas():
+    pl = oracle.plan(np.full(128, 256, np.int32), 16)
+    assert pl["slots_needed"].sum() == 0 and (pl["donor"] == -1).all()
+
+
+# --------------------------------------------------------------- permute ----
+
+def test_fixture_permutation_derived_golden():
+    ids = _pairs(FIX)
+    c = oracle.count(ids, 8, 4)
+    pl = oracle.plan(c["counts"], 4)
+    x = synth.host_normal((16, 64), 1.0, 11)
+    buf, dest_row, row_src = oracle.permute(x, ids, c["eidx"], pl)
+    np.testing.assert_array_equal(dest_row, DER["dest_row"])
+    np.testing.assert_array_equal(buf, x[row_src])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_permutation_is_a_bijection_into_local_windows(seed):
+    rng = np.random.default_rng(seed)
+    T, E, k, R = 300, 64, 6, 8
+    n = E // R
+    lg = synth.router_logits(T, E, seed)
+    bias = synth.zipf_bias(E, 0.6, seed)
+    ids, _, _ = oracle.route(lg, bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    x = rng.integers(0, 1 << 15, size=(T, 8)).astype(np.uint16)
+    buf, dest_row, row_src = oracle.permute(x, ids, c["eidx"], pl)
+    flat = dest_row.ravel()
+    np.testing.assert_array_equal(np.sort(flat), np.arange(T * k))
+    np.testing.assert_array_equal(row_src[flat], np.repeat(np.arange(T), k))
+    np.testing.assert_array_equal(buf, x[row_src])
+    for d, e in zip(flat, ids.ravel()):
+        r = int(np.searchsorted(pl["win_off"], d, side="right") - 1)
+        assert e // n == r or e in pl["slot_expert"][r]
+    # k = 1, w = 1: combine returns x exactly
+    ids1 = ids[:, :1].copy()
+    c1 = oracle.count(ids1, E, R)
+    pl1 = oracle.plan(c1["counts"], R)
+    xf = synth.host_normal((T, 16), 1.0, seed)
+    buf1, dr1, _ = oracle.permute(xf, ids1, c1["eidx"], pl1)
+    out = oracle.combine(buf1.astype(np.float64), dr1, np.ones((T, 1)))
+    np.testing.assert_array_equal(out, xf.astype(np.float64))
+
+
+# ------------------------------------------------------------------- FFN ----
+
+def test_ffn_scalar_closed_form():
+    # H = F = 1, all weights 1, x = 1: y = silu(1) * 1 = logistic(1)
+    one = np.ones((1, 1), np.float32)
+    y = oracle.ffn_rows(one, one, one, one)
+    assert y[0, 0] == pytest.approx(0.7310585786300049, abs=1e-15)
+    y = oracle.ffn_rows(-one, one, one, one)          # silu(-1) * (-1) = logistic(-1)
+    assert y[0, 0] == pytest.approx(0.2689414213699951, abs=1e-15)
+
+
+def test_ffn_dense_reduces_to_matmul():
+    # one expert, k = 1: the layer is a dense SwiGLU FFN (library matmul check)
+    H, F, n = 24, 40, 7
+    x = synth.host_normal((n, H), 1.0, 1)
+    wg = synth.host_normal((F, H), H ** -0.5, 2)
+    wu = synth.host_normal((F, H), H ** -0.5, 3)
+    wd = synth.host_normal((H, F), F ** -0.5, 4)
+    y = oracle.ffn_rows(x, wg, wu, wd)
+    X, G, U, D = (a.astype(np.float64) for a in (x, wg, wu, wd))
+    g = X @ G.T
+    ref = ((g / (1 + np.exp(-g))) * (X @ U.T)) @ D.T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+    # linear in W_down, zero gate gives zero output
+    np.testing.assert_allclose(oracle.ffn_rows(x, wg, wu, 2 * wd), 2 * y, rtol=1e-12, atol=1e-13)
+    assert not oracle.ffn_rows(x, np.zeros_like(wg), wu, wd).any()
+
+
+# --------------------------------------------------------------- combine ----
+
+def test_combine_one_hot_and_order():
+    rng = np.random.default_rng(3)
+    T, k, H = 10, 3, 5
+    y = rng.standard_normal((T * k, H))
+    dest = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    w = np.zeros((T, k))
+    w[np.arange(T), rng.integers(0, k, T)] = 1.0
+    out = oracle.combine(y, dest, w)
+    np.testing.assert_array_equal(out, y[dest[np.arange(T), w.argmax(1)]])
+    w = rng.random((T, k))
+    perm = rng.permutation(k)
+    a = oracle.combine(y, dest, w)
+    b = oracle.combine(y, dest[:, perm], w[:, perm])
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+    sh = rng.standard_normal((T, H))
+    np.testing.assert_allclose(oracle.combine(y, dest, w, sh), a + sh, rtol=1e-13, atol=1e-15)
