@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""One MoE layer forward (route -> count -> plan -> permute -> grouped SwiGLU
+GEMM -> combine) on one MI355X, timed over K steps after W warm-up steps.
+
+Default workload: the Mixtral-style coarse layer in bf16 (T=2048 tokens,
+H=4096, E=8 experts, top-2, SwiGLU width 14336, R=8 virtual ranks, S=1),
+router skew maxvio 0.2 (N(0,1) logits plus a tuned Zipf bias). Inputs are
+seeded and synthetic and already resident in HBM when timing starts.
+
+Prints ONE JSON line. `value` is whole-layer tokens/s; `roofline` describes
+the dominant kernel (the gate/up half of the grouped GEMM), timed with HIP
+events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
+bounded token sample of the same workload (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer tokens/s at maxvio 0/1/20; grouped-GEMM MFMA % and permute HBM %"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--maxvio", type=float, default=None,
+                    help="router skew target (default: the workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def kernel_src_sha():
+    p = os.path.join(ROOT, "expert_load_balance_amd", "csrc", "gemm.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload, maxvio):
+    """HBM bytes per launch of the gate/up kernel from committed counter runs,
+    or None if absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "gemm_gateup_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    rec = d.get(f"{workload}@{maxvio:g}")
+    if not rec or rec.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(name, maxvio, lg, bias, x, wts, ntok):
+    """The oracle, as it stands, on the first `ntok` tokens of the workload.
+    Host copies of the inputs (only the experts those tokens use) are made
+    before the clock starts."""
+    import numpy as np
+
+    import oracle
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    E, k, R = w["E"], w["k"], w["R"]
+    xs = x[:ntok].float().cpu().numpy()
+    used = sorted(set(oracle.route(lg[:ntok], bias, k)[0].ravel().tolist()))
+    wg, wu, wd = ({e: t[e].float().cpu().numpy() for e in used} for t in wts)
+    t0 = time.perf_counter()
+    ids, gw, _ = oracle.route(lg[:ntok], bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    buf, dest_row, row_src = oracle.permute(xs, ids, c["eidx"], pl)
+    y = np.zeros((ntok * k, xs.shape[1]))
+    for e in range(E):
+        rows = []
+        for p in range(pl["piece_num"][e]):
+            rows.extend(range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p]))
+        if rows:
+            y[rows] = oracle.ffn_rows(buf[rows], wg[e], wu[e], wd[e])
+    oracle.combine(y, dest_row, gw)
+    dt = time.perf_counter() - t0
+    return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {ntok} of {w['T']} tokens of the same workload, full layer "
+                       f"(route, count, plan, permute, SwiGLU FFN, combine), "
+                       f"single-threaded C in double, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this layer is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import expert_load_balance_amd as moe
+    from expert_load_balance_amd.layer import STAGES, MoeLayerBuffers
+    import synth
+    from synth import workloads as wl
+
+    moe.load()
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
+    dtype = moe.MOE_BF16 if w["dtype"] == "bf16" else moe.MOE_F32
+    act = torch.bfloat16 if dtype == moe.MOE_BF16 else torch.float32
+    T, H, E, k, F, R, S = (w[c] for c in ("T", "H", "E", "k", "F", "R", "S"))
+    shape = moe.Shape(T, H, E, k, F, R, S, dtype)
+    dev = "cuda"
+
+    lg_np, bias_np = wl.logits_and_bias(name, maxvio)
+    lg = torch.from_numpy(lg_np).to(dev)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
+    x = synth.device_normal((T, H), 1.0, w["seed"] * 7 + 1, act, dev)
+    wts = (synth.device_normal((E, F, H), synth.weight_std(H), w["seed"] * 10 + 1, act, dev),
+           synth.device_normal((E, F, H), synth.weight_std(H), w["seed"] * 10 + 2, act, dev),
+           synth.device_normal((E, H, F), synth.weight_std(F), w["seed"] * 10 + 3, act, dev))
+    shared_F = w.get("shared_F")
+    shared = None
+    if shared_F:
+        shared = (synth.device_normal((1, shared_F, H), synth.weight_std(H), w["seed"] * 10 + 501, act, dev),
+                  synth.device_normal((1, shared_F, H), synth.weight_std(H), w["seed"] * 10 + 502, act, dev),
+                  synth.device_normal((1, H, shared_F), synth.weight_std(shared_F), w["seed"] * 10 + 503, act, dev))
+    L = MoeLayerBuffers(shape, dev, shared_F=shared_F)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[bench] {name}@{maxvio:g} warm-up done", file=sys.stderr, flush=True)
+
+    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for s in STAGES} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {}
+    for s in STAGES:
+        if s == "shared" and shared is None:
+            continue
+        v = sorted(m[s][0].elapsed_time(m[s][1]) for m in marks)
+        stage_ms[s] = dict(mean=sum(v) / len(v), p10=v[len(v) // 10], p90=v[(len(v) * 9) // 10])
+
+    st, loads = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
+                              err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
+    N = T * k
+    b = 2 if dtype == moe.MOE_BF16 else 4
+    gu_s = stage_ms["gemm_gateup"]["mean"] * 1e-3
+    dn_s = stage_ms["gemm_down"]["mean"] * 1e-3
+    gu_flops = 4.0 * N * H * F
+    dn_flops = 2.0 * N * H * F
+    achieved = gu_flops / gu_s / 1e12
+    perm_bytes = (T + N) * H * b
+    comb_bytes = (N + T) * H * b + (T * H * b if shared else 0)
+    ms = elapsed * 1e3 / args.steps
+    traffic = traffic_for(name, maxvio)
+    rec = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == moe.MOE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) router logits + Zipf expert bias, N(0,1) activations, "
+                "N(0,1/sqrt(fan_in)) weights)",
+        "config": {"workload": f"{name} T={T} H={H} E={E} k={k} F={F} R={R} S={S}"
+                               + (f" shared_F={shared_F}" if shared_F else ""),
+                   "maxvio_target": maxvio, "maxvio_realised": st["maxvio_expert"],
+                   "global_batch": T, "parallelism": "1 GPU, R virtual ranks"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "gateup_bf16_kernel",
+                     "flops_per_launch": gu_flops},
+        "stages_ms": {s: round(v["mean"], 4) for s, v in stage_ms.items()},
+        "gemm_down_tflops": dn_flops / dn_s / 1e12,
+        "grouped_gemm_mfma_frac": (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / PEAK_BF16_TFLOPS,
+        "permute_hbm_frac": perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "combine_hbm_frac": comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "plan": {"planned_max": st["planned_max"], "planned_min": st["planned_min"],
+                 "replica_pieces": st["replica_pieces"], "max_slots_needed": st["max_slots_needed"],
+                 "ranks_over_slots": st["ranks_over_slots"]},
+    }
+    if not args.no_cpu_baseline:
+        # about 2e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
+        ntok = args.cpu_tokens or max(1, min(T, int(2e10 / (k * 3 * H * F))))
+        rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, ntok)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,331 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) MoE-layer hot path.
+
+Argument marshalling only: every function here has the name of a C entry
+point declared in ``include/moe.h``, checks that the tensors it is given have
+the documented dtype, device and contiguity, and passes their device pointers
+and the current HIP stream through ctypes. All arithmetic runs in the HIP
+kernels; there is no CPU path. If the library has not been built, every call
+raises ``RuntimeError``.
+
+Build with ``python -m expert_load_balance_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MOE_F32", "MOE_BF16", "MoeError", "Shape", "StatsT", "lib_path", "load",
+    "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
+    "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
+    "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "plan_tables",
+    "EXPORTED_SYMBOLS",
+]
+
+MOE_F32 = 0
+MOE_BF16 = 1
+ERR_NONFINITE, ERR_RANGE, ERR_REPEAT = 1, 2, 4
+
+EXPORTED_SYMBOLS = (
+    "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes", "moe_route",
+    "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_gateup",
+    "moe_gemm_down", "moe_combine", "moe_stats",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_str(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "E", "k", "F", "R", "S", "dtype")]
+
+    def __init__(self, T, H, E, k, F, R, S, dtype=MOE_BF16):
+        super().__init__(T, H, E, k, F, R, S, dtype)
+
+    def replace(self, **kw):
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        d.update(kw)
+        return Shape(**d)
+
+    @property
+    def N(self) -> int:
+        return self.T * self.k
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class PlanLayoutT(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "quota", "win_off", "seg_num", "seg_expert", "seg_row", "seg_cnt", "slots_needed",
+        "slot_expert", "donor", "piece_num", "piece_rank", "piece_row", "piece_cnt", "total")]
+
+
+class StatsT(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("E", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("max_count", ctypes.c_int32), ("min_count", ctypes.c_int32),
+        ("active_experts", ctypes.c_int32),
+        ("maxvio_expert", ctypes.c_double), ("balancedness_expert", ctypes.c_double),
+        ("home_max", ctypes.c_int32),
+        ("maxvio_rank_home", ctypes.c_double), ("balancedness_rank_home", ctypes.c_double),
+        ("mapped_max", ctypes.c_int32),
+        ("maxvio_rank_mapped", ctypes.c_double), ("balancedness_rank_mapped", ctypes.c_double),
+        ("planned_max", ctypes.c_int32), ("planned_min", ctypes.c_int32),
+        ("maxvio_rank_planned", ctypes.c_double), ("balancedness_rank_planned", ctypes.c_double),
+        ("capacity", ctypes.c_int32),
+        ("processed", ctypes.c_int64), ("overflow", ctypes.c_int64), ("padding", ctypes.c_int64),
+        ("remote_home", ctypes.c_int64), ("remote_mapped", ctypes.c_int64),
+        ("remote_planned", ctypes.c_int64),
+        ("replica_pieces", ctypes.c_int32), ("max_slots_needed", ctypes.c_int32),
+        ("ranks_over_slots", ctypes.c_int32), ("nonlocal_rows", ctypes.c_int64),
+        ("err", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_VP = ctypes.c_void_p
+_SP = ctypes.POINTER(Shape)
+
+
+def load():
+    """Loads libmoe.so (once). Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libmoe.so is not built ({_LIB_PATH}); run "
+                           "`python -m expert_load_balance_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    st = ctypes.c_int
+    sig = {
+        "moe_status_str": (ctypes.c_char_p, [st]),
+        "moe_check_shape": (st, [_SP]),
+        "moe_plan_layout": (st, [_SP, ctypes.POINTER(PlanLayoutT)]),
+        "moe_workspace_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_route": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_count": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_plan": (st, [_SP, _VP, _VP, _VP]),
+        "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_gemm_gateup": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_gemm_down": (st, [_SP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_combine": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_stats": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_double, _VP,
+                           ctypes.c_size_t, ctypes.POINTER(StatsT), _VP, _VP]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------- marshalling --
+
+def _ptr(t, dtype=None, name="tensor", numel=None, nullable=False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} must not be None")
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _act_dtype(shape):
+    import torch
+
+    return torch.bfloat16 if shape.dtype == MOE_BF16 else torch.float32
+
+
+def _ok(status, where):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def moe_status_str(status: int) -> str:
+    return load().moe_status_str(int(status)).decode()
+
+
+def moe_check_shape(shape: Shape) -> int:
+    return load().moe_check_shape(ctypes.byref(shape))
+
+
+def moe_plan_layout(shape: Shape) -> dict:
+    out = PlanLayoutT()
+    _ok(load().moe_plan_layout(ctypes.byref(shape), ctypes.byref(out)), "moe_plan_layout")
+    return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def moe_workspace_bytes(shape: Shape) -> int:
+    return int(load().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_route(shape, logits, bias, ids, w, err, stream=None):
+    import torch
+
+    T, E, k = shape.T, shape.E, shape.k
+    args = (ctypes.byref(shape), _ptr(logits, torch.float32, "logits", T * E),
+            _ptr(bias, torch.float32, "bias", E, nullable=True),
+            _ptr(ids, torch.int32, "ids", T * k), _ptr(w, torch.float32, "w", T * k),
+            _ptr(err, torch.int32, "err", 1), _stream(stream))
+    _ok(load().moe_route(*args), "moe_route")
+
+
+def moe_count(shape, ids, counts, offsets, eidx, rank_load, err, ws, stream=None):
+    import torch
+
+    i32 = torch.int32
+    args = (ctypes.byref(shape), _ptr(ids, i32, "ids", shape.N), _ptr(counts, i32, "counts", shape.E),
+            _ptr(offsets, i32, "offsets", shape.E + 1), _ptr(eidx, i32, "eidx", shape.N),
+            _ptr(rank_load, i32, "rank_load", shape.R), _ptr(err, i32, "err", 1),
+            _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _ok(load().moe_count(*args), "moe_count")
+
+
+def moe_plan(shape, counts, plan, stream=None):
+    import torch
+
+    total = moe_plan_layout(shape)["total"]
+    _ok(load().moe_plan(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
+                        _ptr(plan, torch.int32, "plan", total), _stream(stream)), "moe_plan")
+
+
+def moe_permute(shape, x, ids, eidx, plan, buf, dest_row, row_src, stream=None):
+    import torch
+
+    i32, act = torch.int32, _act_dtype(shape)
+    args = (ctypes.byref(shape), _ptr(x, act, "x", shape.T * shape.H), _ptr(ids, i32, "ids", shape.N),
+            _ptr(eidx, i32, "eidx", shape.N), _ptr(plan, i32, "plan"),
+            _ptr(buf, act, "buf", shape.N * shape.H), _ptr(dest_row, i32, "dest_row", shape.N),
+            _ptr(row_src, i32, "row_src", shape.N), _stream(stream))
+    _ok(load().moe_permute(*args), "moe_permute")
+
+
+def _weights(shape, w_gate, w_up, w_down):
+    act = _act_dtype(shape)
+    n = shape.E * shape.F * shape.H
+    return (_ptr(w_gate, act, "w_gate", n) if w_gate is not None else None,
+            _ptr(w_up, act, "w_up", n) if w_up is not None else None,
+            _ptr(w_down, act, "w_down", n) if w_down is not None else None)
+
+
+def moe_grouped_gemm(shape, a, plan, w_gate, w_up, w_down, y, ws, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    g, u, d = _weights(shape, w_gate, w_up, w_down)
+    args = (ctypes.byref(shape), _ptr(a, act, "a", shape.N * shape.H),
+            _ptr(plan, torch.int32, "plan"), g, u, d, _ptr(y, act, "y", shape.N * shape.H),
+            _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _ok(load().moe_grouped_gemm(*args), "moe_grouped_gemm")
+
+
+def moe_gemm_gateup(shape, a, plan, w_gate, w_up, ws, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    g, u, _ = _weights(shape, w_gate, w_up, None)
+    args = (ctypes.byref(shape), _ptr(a, act, "a", shape.N * shape.H),
+            _ptr(plan, torch.int32, "plan"), g, u, _ptr(ws, None, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    _ok(load().moe_gemm_gateup(*args), "moe_gemm_gateup")
+
+
+def moe_gemm_down(shape, plan, w_down, y, ws, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    _, _, d = _weights(shape, None, None, w_down)
+    args = (ctypes.byref(shape), _ptr(plan, torch.int32, "plan"), d,
+            _ptr(y, act, "y", shape.N * shape.H), _ptr(ws, None, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    _ok(load().moe_gemm_down(*args), "moe_gemm_down")
+
+
+def moe_combine(shape, y, dest_row, w, shared_y, out, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    args = (ctypes.byref(shape), _ptr(y, act, "y", shape.N * shape.H),
+            _ptr(dest_row, torch.int32, "dest_row", shape.N), _ptr(w, torch.float32, "w", shape.N),
+            _ptr(shared_y, act, "shared_y", shape.T * shape.H, nullable=True),
+            _ptr(out, act, "out", shape.T * shape.H), _stream(stream))
+    _ok(load().moe_combine(*args), "moe_combine")
+
+
+def moe_stats(shape, counts, ids, plan, ws, dest_row=None, mapping=None, origin=None, err=None,
+              capacity_factor=1.0, stream=None, check=True):
+    """Synchronises the stream. Returns (stats dict, rank_loads [3][R] list).
+    With check=True a set device error word raises MoeError(MOE_EDATA)."""
+    import torch
+
+    i32 = torch.int32
+    out = StatsT()
+    loads = (ctypes.c_int32 * (3 * shape.R))()
+    st = load().moe_stats(
+        ctypes.byref(shape), _ptr(counts, i32, "counts", shape.E), _ptr(ids, i32, "ids", shape.N),
+        _ptr(plan, i32, "plan"), _ptr(dest_row, i32, "dest_row", shape.N, nullable=True),
+        _ptr(mapping, i32, "mapping", shape.E, nullable=True),
+        _ptr(origin, i32, "origin", shape.T, nullable=True),
+        _ptr(err, i32, "err", 1, nullable=True), float(capacity_factor), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), ctypes.byref(out), ctypes.cast(loads, _VP),
+        _stream(stream))
+    if st != 0 and (check or st != 4):
+        raise MoeError(st, "moe_stats")
+    R = shape.R
+    flat = list(loads)
+    return out.as_dict(), [flat[:R], flat[R:2 * R], flat[2 * R:]]
+
+
+def plan_tables(plan, shape) -> dict:
+    """Views of the plan block's tables (by the layout moe_plan_layout reports)."""
+    L = moe_plan_layout(shape)
+    R, E = shape.R, shape.E
+    n = E // R
+    sizes = dict(quota=(R,), win_off=(R + 1,), seg_num=(R,), seg_expert=(R, 2 * n),
+                 seg_row=(R, 2 * n), seg_cnt=(R, 2 * n), slots_needed=(R,), slot_expert=(R, n),
+                 donor=(R,), piece_num=(E,), piece_rank=(E, R), piece_row=(E, R),
+                 piece_cnt=(E, R))
+    out = {}
+    for name, shp in sizes.items():
+        cnt = 1
+        for s in shp:
+            cnt *= s
+        out[name] = plan[L[name]:L[name] + cnt].view(*shp)
+    return out

@@ -1,0 +1,253 @@
+// api.hip -- the extern "C" entry points of libmoe.so: validate on the host,
+// then launch on the caller's stream. Nothing here allocates device memory.
+// Operation semantics and their sources are documented in include/moe.h.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+moe_status_t check(const moe_shape_t* s)
+{
+    if (!s) return MOE_EINVAL;
+    if (s->T < 0 || s->E < 1 || s->E > 256 || s->k < 1 || s->k > s->E || s->k > 64) return MOE_EINVAL;
+    if (s->R < 1 || s->R > 64 || s->E % s->R != 0 || s->S < 0) return MOE_EINVAL;
+    if (s->H < 1 || s->F < 1) return MOE_EINVAL;
+    const int64_t N = (int64_t)s->T * s->k;
+    if (N >= (int64_t(1) << 31)) return MOE_EINVAL;
+    const int64_t wide = s->H > s->F ? s->H : s->F;
+    if (N * wide >= (int64_t(1) << 40)) return MOE_EINVAL;
+    if (s->dtype == MOE_BF16) {
+        if (s->H % 64 || s->F % 64) return MOE_EUNSUPPORTED;
+    } else if (s->dtype == MOE_F32) {
+        if (s->H % 4 || s->F % 4) return MOE_EUNSUPPORTED;
+    } else {
+        return MOE_EINVAL;
+    }
+    return MOE_OK;
+}
+
+inline moe_status_t dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
+
+inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_EDEVICE: return "HIP runtime error";
+    case MOE_EDATA: return "device error word set (non-finite logits or bad expert ids)";
+    }
+    return "unknown status";
+}
+
+moe_status_t moe_check_shape(const moe_shape_t* shape) { return check(shape); }
+
+moe_status_t moe_plan_layout(const moe_shape_t* shape, moe_plan_layout_t* out)
+{
+    const moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!out) return MOE_EINVAL;
+    const moe::PlanLayout L = moe::plan_layout(shape->E, shape->R);
+    out->quota = L.quota;
+    out->win_off = L.win_off;
+    out->seg_num = L.seg_num;
+    out->seg_expert = L.seg_expert;
+    out->seg_row = L.seg_row;
+    out->seg_cnt = L.seg_cnt;
+    out->slots_needed = L.slots_needed;
+    out->slot_expert = L.slot_expert;
+    out->donor = L.donor;
+    out->piece_num = L.piece_num;
+    out->piece_rank = L.piece_rank;
+    out->piece_row = L.piece_row;
+    out->piece_cnt = L.piece_cnt;
+    out->total = L.total;
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK) return 0;
+    return moe::ws_layout(*shape).total;
+}
+
+moe_status_t moe_route(const moe_shape_t* shape, const float* d_logits, const float* d_bias,
+                       int32_t* d_ids, float* d_w, int32_t* d_err, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_logits || !d_ids || !d_w || !d_err) return MOE_EINVAL;
+    return dev(moe_launch_route(*shape, d_logits, d_bias, d_ids, d_w, d_err, as_stream(stream)));
+}
+
+moe_status_t moe_count(const moe_shape_t* shape, const int32_t* d_ids, int32_t* d_counts,
+                       int32_t* d_offsets, int32_t* d_eidx, int32_t* d_rank_load, int32_t* d_err,
+                       void* d_ws, size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_ids || !d_counts || !d_offsets || !d_eidx || !d_rank_load || !d_err || !d_ws)
+        return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_count(*shape, d_ids, d_counts, d_offsets, d_eidx, d_rank_load, d_err,
+                                static_cast<char*>(d_ws), as_stream(stream)));
+}
+
+moe_status_t moe_plan(const moe_shape_t* shape, const int32_t* d_counts, int32_t* d_plan,
+                      moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_counts || !d_plan) return MOE_EINVAL;
+    return dev(moe_launch_plan(*shape, d_counts, d_plan, as_stream(stream)));
+}
+
+moe_status_t moe_permute(const moe_shape_t* shape, const void* d_x, const int32_t* d_ids,
+                         const int32_t* d_eidx, const int32_t* d_plan, void* d_buf,
+                         int32_t* d_dest_row, int32_t* d_row_src, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_x || !d_ids || !d_eidx || !d_plan || !d_buf || !d_dest_row || !d_row_src)
+        return MOE_EINVAL;
+    return dev(moe_launch_permute(*shape, d_x, d_ids, d_eidx, d_plan, d_buf, d_dest_row,
+                                  d_row_src, as_stream(stream)));
+}
+
+moe_status_t moe_gemm_gateup(const moe_shape_t* shape, const void* d_a, const int32_t* d_plan,
+                             const void* d_w_gate, const void* d_w_up, void* d_ws,
+                             size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_a || !d_plan || !d_w_gate || !d_w_up || !d_ws) return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_gemm_gateup(*shape, d_a, d_plan, d_w_gate, d_w_up,
+                                      static_cast<char*>(d_ws), as_stream(stream)));
+}
+
+moe_status_t moe_gemm_down(const moe_shape_t* shape, const int32_t* d_plan, const void* d_w_down,
+                           void* d_y, void* d_ws, size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_plan || !d_w_down || !d_y || !d_ws) return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_gemm_down(*shape, d_plan, d_w_down, d_y, static_cast<char*>(d_ws),
+                                    as_stream(stream)));
+}
+
+moe_status_t moe_grouped_gemm(const moe_shape_t* shape, const void* d_a, const int32_t* d_plan,
+                              const void* d_w_gate, const void* d_w_up, const void* d_w_down,
+                              void* d_y, void* d_ws, size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = moe_gemm_gateup(shape, d_a, d_plan, d_w_gate, d_w_up, d_ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_gemm_down(shape, d_plan, d_w_down, d_y, d_ws, ws_bytes, stream);
+}
+
+moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_t* d_dest_row,
+                         const float* d_w, const void* d_shared_y, void* d_out,
+                         moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_y || !d_dest_row || !d_w || !d_out) return MOE_EINVAL;
+    return dev(moe_launch_combine(*shape, d_y, d_dest_row, d_w, d_shared_y, d_out,
+                                  as_stream(stream)));
+}
+
+moe_status_t moe_stats(const moe_shape_t* shape, const int32_t* d_counts, const int32_t* d_ids,
+                       const int32_t* d_plan, const int32_t* d_dest_row,
+                       const int32_t* d_mapping, const int32_t* d_origin, const int32_t* d_err,
+                       double capacity_factor, void* d_ws, size_t ws_bytes, moe_stats_t* h_out,
+                       int32_t* h_rank_loads, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_counts || !d_ids || !d_plan || !d_ws || !h_out) return MOE_EINVAL;
+    if (!(capacity_factor > 0.0) || !isfinite(capacity_factor)) return MOE_EINVAL;
+    const moe::WsLayout W = moe::ws_layout(*shape);
+    if (ws_bytes < W.total) return MOE_EINVAL;
+    const int E = shape->E, R = shape->R;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    // capacity from the page's formula in the page's order: N / E * factor
+    const double capd = ceil((double)N / (double)E * capacity_factor);
+    if (!(capd < 2147483647.0)) return MOE_EINVAL;
+    const int32_t cap = (int32_t)capd;
+    int64_t* d_out = reinterpret_cast<int64_t*>(static_cast<char*>(d_ws) + W.stats);
+    hipStream_t hs = as_stream(stream);
+    hipError_t e = moe_launch_stats(*shape, d_counts, d_ids, d_plan, d_dest_row, d_mapping,
+                                    d_origin, d_err, cap, d_out, hs);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    int64_t h[moe::kStScalars + 3 * 64];
+    const size_t nb = sizeof(int64_t) * moe::stats_slots(R);
+    e = hipMemcpyAsync(h, d_out, nb, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return MOE_EDEVICE;
+
+    auto maxvio = [](int64_t mx, int M, int64_t total) {
+        return total <= 0 ? 0.0 : (double)(mx * (int64_t)M - total) / (double)total;
+    };
+    auto bal = [](int64_t mx, int M, int64_t total) {
+        return mx <= 0 ? 1.0 : (double)total / (double)(mx * (int64_t)M);
+    };
+    memset(h_out, 0, sizeof(*h_out));
+    h_out->N = h[moe::kStN];
+    h_out->E = E;
+    h_out->R = R;
+    h_out->max_count = (int32_t)h[moe::kStMax];
+    h_out->min_count = (int32_t)h[moe::kStMin];
+    h_out->active_experts = (int32_t)h[moe::kStActive];
+    h_out->maxvio_expert = maxvio(h[moe::kStMax], E, h[moe::kStN]);
+    h_out->balancedness_expert = bal(h[moe::kStMax], E, h[moe::kStN]);
+    int64_t hm = 0, mm = 0, pm = 0, pmin = -1;
+    for (int r = 0; r < R; ++r) {
+        const int64_t hv = h[moe::kStScalars + r], mv = h[moe::kStScalars + R + r],
+                      pv = h[moe::kStScalars + 2 * R + r];
+        hm = hv > hm ? hv : hm;
+        mm = mv > mm ? mv : mm;
+        pm = pv > pm ? pv : pm;
+        pmin = (pmin < 0 || pv < pmin) ? pv : pmin;
+        if (h_rank_loads) {
+            h_rank_loads[r] = (int32_t)hv;
+            h_rank_loads[R + r] = (int32_t)mv;
+            h_rank_loads[2 * R + r] = (int32_t)pv;
+        }
+    }
+    h_out->home_max = (int32_t)hm;
+    h_out->maxvio_rank_home = maxvio(hm, R, h_out->N);
+    h_out->balancedness_rank_home = bal(hm, R, h_out->N);
+    if (d_mapping) {
+        h_out->mapped_max = (int32_t)mm;
+        h_out->maxvio_rank_mapped = maxvio(mm, R, h_out->N);
+        h_out->balancedness_rank_mapped = bal(mm, R, h_out->N);
+    }
+    h_out->planned_max = (int32_t)pm;
+    h_out->planned_min = (int32_t)(pmin < 0 ? 0 : pmin);
+    h_out->maxvio_rank_planned = maxvio(pm, R, h_out->N);
+    h_out->balancedness_rank_planned = bal(pm, R, h_out->N);
+    h_out->capacity = cap;
+    h_out->processed = h[moe::kStProcessed];
+    h_out->overflow = h[moe::kStOverflow];
+    h_out->padding = h[moe::kStPadding];
+    h_out->remote_home = h[moe::kStRemoteHome];
+    h_out->remote_mapped = h[moe::kStRemoteMapped];
+    h_out->remote_planned = h[moe::kStRemotePlanned];
+    h_out->replica_pieces = (int32_t)h[moe::kStReplicas];
+    h_out->max_slots_needed = (int32_t)h[moe::kStMaxSlots];
+    h_out->ranks_over_slots = (int32_t)h[moe::kStOverSlots];
+    h_out->nonlocal_rows = h[moe::kStNonlocal];
+    h_out->err = (int32_t)h[moe::kStErr];
+    return h_out->err ? MOE_EDATA : MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// common.h -- internal helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// bf16 storage is the upper half of an IEEE fp32; conversions are exact one
+// way and round-to-nearest-even the other.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Two bf16 values packed in a uint32 (low half = lower address).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Plan block layout (int32 element offsets), the single definition used by
+// the host API and every kernel that reads the plan.
+struct PlanLayout {
+    int64_t quota, win_off, seg_num, seg_expert, seg_row, seg_cnt, slots_needed, slot_expert,
+        donor, piece_num, piece_rank, piece_row, piece_cnt, total;
+};
+
+__host__ __device__ inline PlanLayout plan_layout(int E, int R)
+{
+    const int64_t n = E / R;
+    PlanLayout L;
+    int64_t o = 0;
+    L.quota = o;        o += R;
+    L.win_off = o;      o += R + 1;
+    L.seg_num = o;      o += R;
+    L.seg_expert = o;   o += R * 2 * n;
+    L.seg_row = o;      o += R * 2 * n;
+    L.seg_cnt = o;      o += R * 2 * n;
+    L.slots_needed = o; o += R;
+    L.slot_expert = o;  o += R * n;
+    L.donor = o;        o += R;
+    L.piece_num = o;    o += E;
+    L.piece_rank = o;   o += (int64_t)E * R;
+    L.piece_row = o;    o += (int64_t)E * R;
+    L.piece_cnt = o;    o += (int64_t)E * R;
+    L.total = o;
+    return L;
+}
+
+// Workspace carve-up (bytes, 256-byte aligned regions).
+struct WsLayout {
+    size_t blk_hist, blk_base;  // count: int32[B][E] each
+    size_t sched;               // gemm: int32 schedule (see gemm.hip)
+    size_t h;                   // gemm: dtype[N][F] SwiGLU activations
+    size_t stats;               // stats: int64[kStatsSlots(R)]
+    size_t total;
+    int count_blocks;
+};
+
+constexpr int kCountChunk = 1024;  // assignments per counting workgroup
+
+// Statistics reduction slots (int64): fixed scalars, then three R-vectors.
+enum StatSlot {
+    kStN = 0, kStMax, kStMin, kStActive, kStProcessed, kStOverflow, kStPadding, kStRemoteHome,
+    kStRemoteMapped, kStRemotePlanned, kStReplicas, kStMaxSlots, kStOverSlots, kStNonlocal,
+    kStErr, kStScalars
+};
+__host__ __device__ inline int stats_slots(int R) { return kStScalars + 3 * R; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const moe_shape_t& s)
+{
+    WsLayout w;
+    const int64_t N = (int64_t)s.T * s.k;
+    const int64_t B = (N + kCountChunk - 1) / kCountChunk;
+    w.count_blocks = (int)B;
+    size_t o = 0;
+    w.blk_hist = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
+    w.blk_base = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
+    w.sched = o;     o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
+    w.h = o;         o = align256(o + (size_t)N * s.F * (s.dtype == MOE_BF16 ? 2 : 4));
+    w.stats = o;     o = align256(o + (size_t)stats_slots(s.R) * 8);
+    w.total = o;
+    return w;
+}
+
+}  // namespace moe
+
+// ---- launchers (one per kernel family; all asynchronous on `st`) ----------
+hipError_t moe_launch_route(const moe_shape_t& s, const float* logits, const float* bias,
+                            int32_t* ids, float* w, int32_t* err, hipStream_t st);
+hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                            int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
+                            char* ws, hipStream_t st);
+hipError_t moe_launch_plan(const moe_shape_t& s, const int32_t* counts, int32_t* plan,
+                           hipStream_t st);
+hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t* ids,
+                              const int32_t* eidx, const int32_t* plan, void* buf,
+                              int32_t* dest_row, int32_t* row_src, hipStream_t st);
+hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t* dest_row,
+                              const float* w, const void* shared_y, void* out, hipStream_t st);
+hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
+                                  const void* w_gate, const void* w_up, char* ws,
+                                  hipStream_t st);
+hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
+                                void* y, char* ws, hipStream_t st);
+hipError_t moe_launch_stats(const moe_shape_t& s, const int32_t* counts, const int32_t* ids,
+                            const int32_t* plan, const int32_t* dest_row, const int32_t* mapping,
+                            const int32_t* origin, const int32_t* err, int32_t capacity,
+                            int64_t* d_out, hipStream_t st);

@@ -1,0 +1,266 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path library, libmoe.so.
+ *
+ * One MoE layer, data-parallel forward, on one GPU:
+ *   moe_route        router top-k gating               (phase a)
+ *   moe_count        per-expert demand + stable index
+ *   moe_plan         equal-load replica plan over R virtual ranks
+ *   moe_permute      dispatch into a static-shape buffer (phase b)
+ *   moe_grouped_gemm SwiGLU expert FFN over the plan    (phase c)
+ *   moe_combine      gate-weighted gather back to tokens (phase d)
+ *   moe_stats        maxvio / balancedness / capacity / remote statistics
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Primer]  "DeepEP-on-EFA Guidance, section 1: what is MoE" -- the
+ *             four-phase layer: router, dispatch, batched grouped GEMM,
+ *             combine; a token travels only to its k experts.
+ *   [MoonEP]  "Moonshot AI drops MoonEP, claims 2.5x scaling boost for
+ *             trillion-parameter models", paragraphs 2-4 -- maxvio (zero when
+ *             balanced), the equal-load invariant, replicas planned on device
+ *             from the router output, zero-copy placement, static buffer
+ *             shapes, one contiguous weight tensor per projection, prefetch
+ *             slots (= experts per rank for training, 3-4 for inference).
+ *   [Hotspot] "MoE Load Balancing: Find Expert Hotspots" -- demand counting,
+ *             average/max balancedness, rank demand under a mapping, the
+ *             fixed-capacity ledger, remote routes, validation before use.
+ *   [Interview] "MoE load balancing: 90/10 routing in production" -- a
+ *             per-expert bias that steers selection without touching the gate.
+ *
+ * Conventions
+ *   - Every pointer named d_* is DEVICE memory owned by the caller; h_* is
+ *     host memory owned by the caller. The library never allocates device
+ *     memory and keeps no state between calls.
+ *   - Every call except moe_stats is asynchronous and stream-ordered on
+ *     `stream` (a hipStream_t; NULL means the default stream).
+ *   - Host-detectable problems (bad shape, NULL pointer, workspace too small)
+ *     return a status BEFORE anything is launched; outputs are untouched.
+ *   - Data problems found on the device (non-finite logits, bad ids) set bits
+ *     in a caller-provided device int32 error word with an order-free atomic
+ *     OR; the caller zeroes it. When it is non-zero the outputs are
+ *     unspecified (but every kernel stays in bounds). moe_stats reports it.
+ *   - All 2-D arrays are row-major. N = T*k assignments. n = E/R experts per
+ *     rank. dtype is the element type of activations, weights, buffers and
+ *     outputs (MOE_F32: float; MOE_BF16: bfloat16). Logits, biases and gate
+ *     weights are always float; ids, indices and tables are int32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,        /* bad shape, NULL pointer, or size out of range       */
+    MOE_EUNSUPPORTED = 2,  /* valid request this build does not implement         */
+    MOE_EDEVICE = 3,       /* a HIP runtime call failed                           */
+    MOE_EDATA = 4          /* the device error word is non-zero (moe_stats only)  */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Device error word bits. */
+#define MOE_ERR_NONFINITE 1 /* a logit or bias is NaN or infinite             */
+#define MOE_ERR_RANGE 2     /* an expert id is outside [0, E)                 */
+#define MOE_ERR_REPEAT 4    /* a token lists the same expert twice            */
+
+typedef void *moe_stream_t; /* a hipStream_t */
+
+/* Shape of one layer call.
+ * Limits (checked by every entry point): 0 <= T, 1 <= k <= min(E, 64),
+ * 1 <= E <= 256, 1 <= R <= 64, E % R == 0, 0 <= S, 1 <= H, 1 <= F,
+ * T*k < 2^31, (T*k)*max(H,F) < 2^40.
+ * MOE_BF16 additionally needs H % 64 == 0 and F % 64 == 0 (GEMM K-steps);
+ * MOE_F32 needs H % 4 == 0 and F % 4 == 0 (16-byte rows). */
+typedef struct moe_shape {
+    int32_t T;     /* tokens in the batch                                  */
+    int32_t H;     /* hidden width (row length of x, buf, y, out)          */
+    int32_t E;     /* routed experts                                       */
+    int32_t k;     /* experts per token (top-k)                            */
+    int32_t F;     /* expert SwiGLU width                                  */
+    int32_t R;     /* virtual expert-parallel ranks; rank r homes experts
+                      [r*n, (r+1)*n)                                       */
+    int32_t S;     /* prefetch slots per rank (locality budget, reported)  */
+    int32_t dtype; /* moe_dtype_t                                          */
+} moe_shape_t;
+
+/* The plan is one caller-allocated int32 device block of `total` elements;
+ * each table starts at the given element offset. Unused entries are -1.
+ *   quota[R]          rows every rank receives: floor(N/R) + [r < N mod R]
+ *   win_off[R+1]      first row of rank r's window in buf (prefix of quota)
+ *   seg_num[R]        segments in rank r's window
+ *   seg_expert[R][2n] expert of each segment, ascending within a window
+ *   seg_row[R][2n]    first buf row of each segment
+ *   seg_cnt[R][2n]    rows of each segment
+ *   slots_needed[R]   replica (non-home) experts rank r holds
+ *   slot_expert[R][n] those experts, ascending
+ *   donor[R]          the rank whose experts r replicates, or -1
+ *   piece_num[E]      pieces expert e is split into (<= R)
+ *   piece_rank[E][R]  rank of each piece, ascending
+ *   piece_row[E][R]   first buf row of each piece
+ *   piece_cnt[E][R]   rows of each piece                                   */
+typedef struct moe_plan_layout {
+    int64_t quota, win_off, seg_num, seg_expert, seg_row, seg_cnt, slots_needed, slot_expert,
+        donor, piece_num, piece_rank, piece_row, piece_cnt;
+    int64_t total; /* int32 elements in the block */
+} moe_plan_layout_t;
+
+/* Host-side statistics (moe_stats). Integers are exact; every double is one
+ * division of exact integers. */
+typedef struct moe_stats {
+    int64_t N;                       /* assignments T*k                          */
+    int32_t E, R;
+    int32_t max_count, min_count, active_experts;
+    double maxvio_expert;            /* max/mean - 1 over expert demand          */
+    double balancedness_expert;      /* mean/max over expert demand              */
+    int32_t home_max;
+    double maxvio_rank_home, balancedness_rank_home;      /* contiguous homes   */
+    int32_t mapped_max;
+    double maxvio_rank_mapped, balancedness_rank_mapped;  /* caller mapping     */
+    int32_t planned_max, planned_min;
+    double maxvio_rank_planned, balancedness_rank_planned;/* after the plan     */
+    int32_t capacity;                /* ceil(N / E * capacity_factor)            */
+    int64_t processed, overflow, padding; /* ledger sums from raw demand        */
+    int64_t remote_home, remote_mapped, remote_planned;   /* origin != dest     */
+    int32_t replica_pieces;          /* sum of slots_needed                      */
+    int32_t max_slots_needed;
+    int32_t ranks_over_slots;        /* ranks with slots_needed > S              */
+    int64_t nonlocal_rows;           /* rows of replicas past the first S slots  */
+    int32_t err;                     /* device error word                        */
+} moe_stats_t;
+
+/* Human-readable name of a status. Never NULL. */
+const char *moe_status_str(moe_status_t status);
+
+/* Validates a shape against the limits above. */
+moe_status_t moe_check_shape(const moe_shape_t *shape);
+
+/* Fills *out with the plan block layout for this shape. */
+moe_status_t moe_plan_layout(const moe_shape_t *shape, moe_plan_layout_t *out);
+
+/* Bytes of device workspace moe_count, moe_grouped_gemm and moe_stats need
+ * (count scratch, GEMM tile schedule, the SwiGLU activations h[N][F], the
+ * statistics reductions). 0 on a bad
+ * shape. The caller allocates it once per shape and may reuse it. */
+size_t moe_workspace_bytes(const moe_shape_t *shape);
+
+/* [Primer] phase (a); [Interview] editor's note (bias outside the gate).
+ * For every token t: score_e = logits[t][e] + bias[e] as one fp32 add; the k
+ * experts with the largest score, largest first, equal scores to the lower
+ * id, go to d_ids[t][0..k). The gate weights are the softmax of the RAW
+ * logits of those k experts (they sum to 1), in the same order.
+ *   d_logits float[T][E]; d_bias float[E] or NULL (no bias);
+ *   d_ids int32[T][k] out; d_w float[T][k] out; d_err int32[1] in/out.
+ * Non-finite logit or bias: d_err |= MOE_ERR_NONFINITE. */
+moe_status_t moe_route(const moe_shape_t *shape, const float *d_logits, const float *d_bias,
+                       int32_t *d_ids, float *d_w, int32_t *d_err, moe_stream_t stream);
+
+/* [Hotspot] "Separate expert demand from rank placement", "Work the 16-token
+ * hotspot fixture": demand counted per assignment, then per rank.
+ *   d_counts int32[E] out: assignments per expert.
+ *   d_offsets int32[E+1] out: exclusive prefix of counts.
+ *   d_eidx int32[N] out: for assignment t*k+j, the number of earlier
+ *     assignments (in flat order) with the same expert -- a stable index.
+ *   d_rank_load int32[R] out: sum of counts over rank r's home experts.
+ *   d_ws / ws_bytes: workspace of moe_workspace_bytes(shape) bytes.
+ * Ids outside [0, E) set MOE_ERR_RANGE and are not counted; a token naming
+ * an expert twice sets MOE_ERR_REPEAT. Results do not depend on thread
+ * timing (no ordered atomics). */
+moe_status_t moe_count(const moe_shape_t *shape, const int32_t *d_ids, int32_t *d_counts,
+                       int32_t *d_offsets, int32_t *d_eidx, int32_t *d_rank_load, int32_t *d_err,
+                       void *d_ws, size_t ws_bytes, moe_stream_t stream);
+
+/* [MoonEP] paragraphs 3-4: every rank receives the same number of
+ * assignments, by replicas planned on the device from the router output;
+ * with S = n slots every expert a rank computes is local.
+ * The pages state the invariant only; the plan is this alias-style rule:
+ * while an unfilled rank is below its quota, the rank with the largest
+ * deficit (ties: lower rank) is topped up to its quota from the home experts
+ * of the rank with the largest excess (ties: lower rank), taking the donor's
+ * experts in (count desc, id asc) order; what remains stays home. Segments
+ * within a window are ordered by expert id; an expert's pieces are ordered
+ * by rank and filled in stable (eidx) order. Every rank receives from at
+ * most one donor, so it holds at most n replica experts.
+ *   d_counts int32[E] in; d_plan int32[layout.total] out (whole block
+ *   written). Single workgroup; O(E*R) work; no host round trip. */
+moe_status_t moe_plan(const moe_shape_t *shape, const int32_t *d_counts, int32_t *d_plan,
+                      moe_stream_t stream);
+
+/* [Primer] phase (b) (a token goes only to its k experts); [MoonEP]
+ * paragraph 3 (zero-copy placement into static shapes). Assignment (t,j)
+ * with expert e and stable index v goes to piece p of e with
+ * cum_p <= v < cum_p + piece_cnt, row piece_row + v - cum_p.
+ *   d_x dtype[T][H] in; d_ids, d_eidx in; d_plan in;
+ *   d_buf dtype[N][H] out (every row written exactly once);
+ *   d_dest_row int32[T][k] out; d_row_src int32[N] out (source token). */
+moe_status_t moe_permute(const moe_shape_t *shape, const void *d_x, const int32_t *d_ids,
+                         const int32_t *d_eidx, const int32_t *d_plan, void *d_buf,
+                         int32_t *d_dest_row, int32_t *d_row_src, moe_stream_t stream);
+
+/* [Primer] phase (c), batched grouped GEMM of every expert over the rows it
+ * received; [MoonEP] paragraph 3: one contiguous weight tensor per
+ * projection. For every row i of d_a held by expert e (per the plan):
+ *   h = silu(W_gate[e] a_i) * (W_up[e] a_i),  silu(z) = z / (1 + e^-z),
+ *   y_i = W_down[e] h.
+ *   d_a dtype[N][H] (the permuted buffer); d_w_gate, d_w_up dtype[E][F][H];
+ *   d_w_down dtype[E][H][F]; d_y dtype[N][H] out (same row order as d_a).
+ * Replicas read their home expert's weights (one GPU holds every expert).
+ * In MOE_BF16 the products accumulate in fp32 and h is rounded to bf16.
+ * d_plan (from moe_plan) gives each expert's pieces of rows. A one-expert
+ * shape (E = R = k = 1) planned from counts = {T} is a dense SwiGLU FFN
+ * over T rows (e.g. an always-on shared expert).
+ * d_ws / ws_bytes: workspace of moe_workspace_bytes(shape) bytes (holds the
+ * tile schedule and h). */
+moe_status_t moe_grouped_gemm(const moe_shape_t *shape, const void *d_a, const int32_t *d_plan,
+                              const void *d_w_gate, const void *d_w_up, const void *d_w_down,
+                              void *d_y, void *d_ws, size_t ws_bytes, moe_stream_t stream);
+
+/* The two halves of moe_grouped_gemm, for callers that time or overlap them
+ * separately (same arguments; call gateup, then down, with the same d_ws).
+ * moe_gemm_gateup also builds the tile schedule in d_ws. */
+moe_status_t moe_gemm_gateup(const moe_shape_t *shape, const void *d_a, const int32_t *d_plan,
+                             const void *d_w_gate, const void *d_w_up, void *d_ws,
+                             size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_gemm_down(const moe_shape_t *shape, const int32_t *d_plan, const void *d_w_down,
+                           void *d_y, void *d_ws, size_t ws_bytes, moe_stream_t stream);
+
+/* [Primer] phase (d): expert outputs return to their token and are summed
+ * with the gate weights (the transpose of dispatch).
+ *   out[t] = sum_{j=0..k-1} w[t][j] * y[dest_row[t][j]]  (+ shared_y[t])
+ * accumulated in fp32 in j order, rounded once to dtype.
+ *   d_y dtype[N][H]; d_dest_row int32[T][k]; d_w float[T][k];
+ *   d_shared_y dtype[T][H] or NULL; d_out dtype[T][H] out. */
+moe_status_t moe_combine(const moe_shape_t *shape, const void *d_y, const int32_t *d_dest_row,
+                         const float *d_w, const void *d_shared_y, void *d_out,
+                         moe_stream_t stream);
+
+/* [MoonEP] paragraph 2 (maxvio, zero when balanced; read as max/mean - 1);
+ * [Hotspot] (average/max balancedness; rank demand under a mapping; the
+ * fixed-capacity ledger ceil(N / E * factor) with processed, overflow and
+ * padding from raw demand; remote routes where origin rank != destination
+ * rank). Reduces on the device, copies a few hundred bytes back and
+ * SYNCHRONISES the stream; not for the timed path.
+ *   d_counts int32[E]; d_ids int32[T][k]; d_plan (planned figures);
+ *   d_dest_row int32[T][k] or NULL (planned remote routes);
+ *   d_mapping int32[E] or NULL (expert -> rank for the "mapped" figures);
+ *   d_origin int32[T] or NULL (origin rank; NULL means t mod R);
+ *   d_err int32[1] or NULL; d_ws / ws_bytes: the moe_workspace_bytes(shape)
+ *   workspace (a small region of it receives the reductions; the count and
+ *   GEMM regions are left alone). capacity_factor > 0 and finite.
+ *   Returns MOE_EDATA (after filling *h_out) when the error word is non-zero. h_rank_loads, if not NULL, receives
+ *   int32[3][R]: home, mapped (zeros without a mapping) and planned loads. */
+moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const int32_t *d_ids,
+                       const int32_t *d_plan, const int32_t *d_dest_row,
+                       const int32_t *d_mapping, const int32_t *d_origin, const int32_t *d_err,
+                       double capacity_factor, void *d_ws, size_t ws_bytes, moe_stats_t *h_out,
+                       int32_t *h_rank_loads, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

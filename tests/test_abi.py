@@ -1,0 +1,82 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/moe.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_load_balance_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.lib_path()):
+        pytest.fail("libmoe.so is not built: run `python -m expert_load_balance_amd.build`")
+    return moe.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(moe.EXPORTED_SYMBOLS) == names
+
+
+def test_shape_validation(lib):
+    good = moe.Shape(16, 64, 8, 2, 128, 4, 2, moe.MOE_F32)
+    assert moe.moe_check_shape(good) == 0
+    bad = [dict(E=0), dict(E=257), dict(k=0), dict(k=9), dict(R=3), dict(R=0), dict(S=-1),
+           dict(T=-1), dict(H=0), dict(dtype=7), dict(E=256, k=65, R=4)]
+    for kw in bad:
+        assert moe.moe_check_shape(good.replace(**kw)) == 1, kw
+    assert moe.moe_check_shape(good.replace(H=62)) == 2          # fp32 rows are 16-byte vectors
+    assert moe.moe_check_shape(good.replace(dtype=moe.MOE_BF16, F=96)) == 2
+    assert moe.moe_check_shape(good.replace(T=1 << 28, k=8)) == 1  # N >= 2^31
+    assert moe.moe_check_shape(good.replace(T=0)) == 0
+
+
+def test_plan_layout_and_workspace(lib):
+    s = moe.Shape(4096, 2048, 128, 8, 768, 16, 8, moe.MOE_BF16)
+    L = moe.moe_plan_layout(s)
+    R, E, n = 16, 128, 8
+    assert L["quota"] == 0 and L["win_off"] == R and L["seg_num"] == 2 * R + 1
+    assert L["total"] == R + (R + 1) + R + 3 * R * 2 * n + R + R * n + R + E + 3 * E * R
+    ws = moe.moe_workspace_bytes(s)
+    assert ws >= 4096 * 8 * 768 * 2              # holds h [N][F] in bf16
+    assert moe.moe_workspace_bytes(s.replace(R=3)) == 0
+
+
+def test_null_and_bad_shape_rejected_before_launch(lib):
+    s = moe.Shape(16, 64, 8, 2, 128, 4, 2, moe.MOE_F32)
+    V = ctypes.c_void_p
+    p = V(16)  # never dereferenced: validation fails first
+    assert lib.moe_route(ctypes.byref(s), None, None, p, p, p, None) == 1
+    assert lib.moe_route(ctypes.byref(s.replace(R=3)), p, None, p, p, p, None) == 1
+    assert lib.moe_count(ctypes.byref(s), p, p, p, p, p, p, p, 1, None) == 1  # workspace too small
+    assert lib.moe_plan(ctypes.byref(s), None, p, None) == 1
+    assert lib.moe_permute(ctypes.byref(s), p, p, p, p, None, p, p, None) == 1
+    assert lib.moe_grouped_gemm(ctypes.byref(s), p, p, p, p, p, p, p, 1, None) == 1
+    assert lib.moe_combine(ctypes.byref(s), p, p, None, None, p, None) == 1
+    st = moe.StatsT()
+    assert lib.moe_stats(ctypes.byref(s), p, p, p, None, None, None, None, 0.0, p, 1 << 20,
+                         ctypes.byref(st), None, None) == 1                 # factor must be > 0
+    assert moe.moe_status_str(4).startswith("device error word")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "_LIB_PATH", "/nonexistent/libmoe.so")
+    with pytest.raises(RuntimeError):
+        moe.load()
