@@ -154,7 +154,7 @@ def _ptr(t, dtype=None, name="tensor", numel=None, nullable=False):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
-    return t.data_ptr()
+    return t.data_ptr() or None
 
 
 def _stream(stream):

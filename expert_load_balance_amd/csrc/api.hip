@@ -30,6 +30,9 @@ moe_status_t check(const moe_shape_t* s)
 
 inline moe_status_t dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
 
+// A pointer to a zero-length array may be NULL; any other NULL is an error.
+inline bool bad(const void* p, int64_t n) { return p == nullptr && n > 0; }
+
 inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -84,7 +87,8 @@ moe_status_t moe_route(const moe_shape_t* shape, const float* d_logits, const fl
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_logits || !d_ids || !d_w || !d_err) return MOE_EINVAL;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_logits, T) || bad(d_ids, N) || bad(d_w, N) || !d_err) return MOE_EINVAL;
     return dev(moe_launch_route(*shape, d_logits, d_bias, d_ids, d_w, d_err, as_stream(stream)));
 }
 
@@ -94,7 +98,9 @@ moe_status_t moe_count(const moe_shape_t* shape, const int32_t* d_ids, int32_t* 
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_ids || !d_counts || !d_offsets || !d_eidx || !d_rank_load || !d_err || !d_ws)
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_ids, N) || !d_counts || !d_offsets || bad(d_eidx, N) || !d_rank_load || !d_err ||
+        !d_ws)
         return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
     return dev(moe_launch_count(*shape, d_ids, d_counts, d_offsets, d_eidx, d_rank_load, d_err,
@@ -116,7 +122,9 @@ moe_status_t moe_permute(const moe_shape_t* shape, const void* d_x, const int32_
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_x || !d_ids || !d_eidx || !d_plan || !d_buf || !d_dest_row || !d_row_src)
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_x, T) || bad(d_ids, N) || bad(d_eidx, N) || !d_plan || bad(d_buf, N) ||
+        bad(d_dest_row, N) || bad(d_row_src, N))
         return MOE_EINVAL;
     return dev(moe_launch_permute(*shape, d_x, d_ids, d_eidx, d_plan, d_buf, d_dest_row,
                                   d_row_src, as_stream(stream)));
@@ -128,7 +136,8 @@ moe_status_t moe_gemm_gateup(const moe_shape_t* shape, const void* d_a, const in
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_a || !d_plan || !d_w_gate || !d_w_up || !d_ws) return MOE_EINVAL;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_a, N) || !d_plan || !d_w_gate || !d_w_up || !d_ws) return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
     return dev(moe_launch_gemm_gateup(*shape, d_a, d_plan, d_w_gate, d_w_up,
                                       static_cast<char*>(d_ws), as_stream(stream)));
@@ -139,7 +148,8 @@ moe_status_t moe_gemm_down(const moe_shape_t* shape, const int32_t* d_plan, cons
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_plan || !d_w_down || !d_y || !d_ws) return MOE_EINVAL;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (!d_plan || !d_w_down || bad(d_y, N) || !d_ws) return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
     return dev(moe_launch_gemm_down(*shape, d_plan, d_w_down, d_y, static_cast<char*>(d_ws),
                                     as_stream(stream)));
@@ -160,7 +170,8 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_y || !d_dest_row || !d_w || !d_out) return MOE_EINVAL;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_y, N) || bad(d_dest_row, N) || bad(d_w, N) || bad(d_out, T)) return MOE_EINVAL;
     return dev(moe_launch_combine(*shape, d_y, d_dest_row, d_w, d_shared_y, d_out,
                                   as_stream(stream)));
 }
@@ -173,7 +184,8 @@ moe_status_t moe_stats(const moe_shape_t* shape, const int32_t* d_counts, const 
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (!d_counts || !d_ids || !d_plan || !d_ws || !h_out) return MOE_EINVAL;
+    if (!d_counts || bad(d_ids, (int64_t)shape->T * shape->k) || !d_plan || !d_ws || !h_out)
+        return MOE_EINVAL;
     if (!(capacity_factor > 0.0) || !isfinite(capacity_factor)) return MOE_EINVAL;
     const moe::WsLayout W = moe::ws_layout(*shape);
     if (ws_bytes < W.total) return MOE_EINVAL;

@@ -16,21 +16,15 @@
 //   gate/up: h[row_start[e] + v][f] = silu(a_v . Wg[e][f]) * (a_v . Wu[e][f])
 //            (h stored expert-contiguous, rounded to bf16 in bf16 mode);
 //   down:    y[buf row of v][o] = h[row_start[e] + v] . Wd[e][o].
-// bf16 path: v_mfma_f32_16x16x32_bf16 (fp32 accumulate), 128x128 workgroup
-// tiles, 64-deep K steps double-buffered through LDS. Workgroup ids run
-// M-tile fastest so the M-tiles that share a weight tile are in flight
-// together and the weight bytes come from HBM once.
+// bf16 path: a persistent MFMA kernel (below); fp32 path: plain LDS-tiled
+// VALU kernels for small shapes.
 #include "common.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;   // rows per tile (both kernels)
-constexpr int kBK = 64;    // K per LDS stage
-constexpr int kLds = kBK + 8;  // padded LDS row (bf16 elements): 144 bytes
 
 // schedule layout inside the workspace region (int32):
 //   [0 .. E]        tile_start (prefix of ceil(c_e / BM))
@@ -111,234 +105,224 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p)
 }
 
 // ---------------------------------------------------------------- bf16 ----
-// gate/up: tile = 128 rows x 64 F-columns of both gate and up (128 B rows).
-// 4 waves in 2 (M) x 2 (N); each wave: 64 rows x 32 columns of gate and of up.
-__global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(
-    int E, int R, int H, int F, int mtiles, const uint16_t* __restrict__ a,
-    const int32_t* __restrict__ plan, const int32_t* __restrict__ sched,
-    const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu, uint16_t* __restrict__ h)
+// Persistent kernel, one 256-thread workgroup per CU. Workgroup tile: 256
+// rows x 256 B-rows (gate/up: 128 F-columns of gate and the same 128 of up;
+// down: 256 output columns); K in 64-deep stages, double-buffered.
+//  * Global -> LDS with global_load_lds_dwordx4 (lane l of an instruction
+//    lands at LDS base + 16 l), so no VGPRs stage the tiles.
+//  * A stage is 256 rows of 9 16-byte slots: 8 K-chunks + 1 pad (144-byte
+//    rows), which keeps the MFMA fragment reads (32 rows, one chunk) free of
+//    bank conflicts. DMA instruction q fills slots 64q .. 64q+63; a lane whose
+//    slot is a pad slot loads its row's first chunk into it (never read).
+//    Global reads stay 128-byte row runs.
+//  * Fragment addresses are one VGPR per lane plus immediate offsets.
+//  * Each stage is its own LDS array, so the wait for a prefetch into one
+//    stage does not block reads of the other.
+//  * 4 waves in 2 x 2, each 128 rows x 128 B-rows with
+//    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs);
+//    the next k-step's fragments are read between the current MFMAs.
+//    Operands are swapped so a lane holds 4 consecutive output columns: the
+//    epilogue stores 8 bytes per lane straight to global memory.
+//  * Tile order: expert, N-tile, M-tile (M fastest), so the M-tiles sharing
+//    a weight tile run together; each XCD takes a contiguous run of tiles so
+//    they share its L2.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kSlotsPerRow = kTK / 8 + 1;                  // 9
+constexpr int kRowElems = kSlotsPerRow * 8;                // 72 bf16 = 144 bytes
+constexpr int kStageElems = kTM * kRowElems;               // 36 KB per stage
+constexpr int kDmaPerStage = kTM * kSlotsPerRow / 64;      // 36 instructions
+constexpr int kDmaPerWave = kDmaPerStage / 4;              // 9
+enum { kGateUp = 0, kDown = 1 };
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* l)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLds];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kLds];
-    __shared__ int32_t rowmap[kBM];
-
-    const int mt = blockIdx.x % mtiles;
-    const int nt = blockIdx.x / mtiles;
-    const Tile tile = find_tile(mt, E, kBM, sched);
-    if (tile.rows <= 0) return;
-    const moe::PlanLayout L = moe::plan_layout(E, R);
-    const int tid = threadIdx.x;
-    if (tid < kBM) {
-        const int v = tile.v0 + (tid < tile.rows ? tid : 0);
-        rowmap[tid] = buf_row_of(tile.e, v, R, plan, L);
-    }
-    __syncthreads();
-
-    const int n0 = nt * 64;
-    const int lrow = tid >> 3;        // 0..31
-    const int lcol = (tid & 7) * 8;   // bf16 offset of this thread's 16 bytes
-    const uint16_t* arow[4];
-    const uint16_t* brow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow + 32 * i;
-        arow[i] = a + (size_t)rowmap[r] * H + lcol;
-        const int br = r < 64 ? r : r - 64;
-        const uint16_t* wbase = r < 64 ? wg : wu;
-        brow[i] = wbase + ((size_t)tile.e * F + n0 + br) * H + lcol;
-    }
-
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-
-    f32x4 accg[4][2], accu[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accu[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-    uint4 ra[4], rb[4];
-    const int KT = H / kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const uint4*>(arow[i]);
-        rb[i] = *reinterpret_cast<const uint4*>(brow[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&As[0][(lrow + 32 * i) * kLds + lcol]) = ra[i];
-        *reinterpret_cast<uint4*>(&Bs[0][(lrow + 32 * i) * kLds + lcol]) = rb[i];
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) {
-            const int ko = (kt + 1) * kBK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[i] = *reinterpret_cast<const uint4*>(arow[i] + ko);
-                rb[i] = *reinterpret_cast<const uint4*>(brow[i] + ko);
-            }
-        }
-        const uint16_t* as = As[cur];
-        const uint16_t* bs = Bs[cur];
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8 af[4], bgf[2], buf_[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_frag(as + (wm * 64 + i * 16 + fr) * kLds + kk + fk);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                bgf[j] = lds_frag(bs + (wn * 32 + j * 16 + fr) * kLds + kk + fk);
-                buf_[j] = lds_frag(bs + (64 + wn * 32 + j * 16 + fr) * kLds + kk + fk);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bgf[j], accg[i][j], 0, 0, 0);
-                    accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], buf_[j], accu[i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < KT) {
-            const int nb = cur ^ 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<uint4*>(&As[nb][(lrow + 32 * i) * kLds + lcol]) = ra[i];
-                *reinterpret_cast<uint4*>(&Bs[nb][(lrow + 32 * i) * kLds + lcol]) = rb[i];
-            }
-        }
-        __syncthreads();
-    }
-
-    // epilogue: h = silu(g) * u, rounded to bf16; output lane layout of the
-    // 16x16 MFMA: column = lane % 16, rows 4 * (lane / 16) + r.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-                const int col = n0 + wn * 32 + j * 16 + (lane & 15);
-                if (row < tile.rows) {
-                    const float g = accg[i][j][r], u = accu[i][j][r];
-                    h[(size_t)(tile.hrow0 + row) * F + col] = moe::f32_to_bf16_bits(moe::silu(g) * u);
-                }
-            }
+    __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
 }
 
-// down: tile = 128 rows x 128 output columns; 4 waves 2 x 2, each 64 x 64.
-__global__ __launch_bounds__(kThreads) void down_bf16_kernel(
-    int E, int R, int H, int F, int mtiles, const uint16_t* __restrict__ h,
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
+    int E, int R, int H, int F, int ntiles_n, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ plan, const int32_t* __restrict__ sched,
-    const uint16_t* __restrict__ wd, uint16_t* __restrict__ y)
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLds];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kLds];
-    __shared__ int32_t rowmap[kBM];
+    __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sA1[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB1[kStageElems];
+    __shared__ int32_t rowmap[kTM];
 
-    const int mt = blockIdx.x % mtiles;
-    const int nt = blockIdx.x / mtiles;
-    const Tile tile = find_tile(mt, E, kBM, sched);
-    if (tile.rows <= 0) return;
     const moe::PlanLayout L = moe::plan_layout(E, R);
+    const int K = MODE == kGateUp ? H : F;
+    const int KT = K / kTK;
+    const int total = sched[E] * ntiles_n;
+    const int P = gridDim.x;
+    const int per_xcd = P / 8;
+    const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+
     const int tid = threadIdx.x;
-    if (tid < kBM) rowmap[tid] = tid < tile.rows ? buf_row_of(tile.e, tile.v0 + tid, R, plan, L) : -1;
-    __syncthreads();
-
-    const int n0 = nt * 128;
-    const int lrow = tid >> 3;
-    const int lcol = (tid & 7) * 8;
-    const uint16_t* arow[4];
-    const uint16_t* brow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow + 32 * i;
-        const int ar = r < tile.rows ? r : 0;
-        arow[i] = h + (size_t)(tile.hrow0 + ar) * F + lcol;
-        const int bc = min(n0 + r, H - 1);
-        brow[i] = wd + ((size_t)tile.e * H + bc) * F + lcol;
-    }
-
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    const int fl = lane & 31, fh = lane >> 5;
+    // fragment base: row (lane & 31) of a 32-row block, K-chunk (lane >> 5)
+    const int frag_off = fl * kRowElems + fh * 8;
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int base = 0;; base += P) {
+        const int Lt = base + my_slot;
+        if (Lt >= total) break;
+        // ---- decode the tile: expert, N-tile, M-tile
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sched[mid] * ntiles_n <= Lt) lo = mid;
+            else hi = mid - 1;
+        }
+        const int e = lo;
+        const int mt_e = sched[e + 1] - sched[e];
+        const int local = Lt - sched[e] * ntiles_n;
+        const int nt = local / mt_e, mt = local % mt_e;
+        const int c_e = sched[E + 1 + e + 1] - sched[E + 1 + e];
+        const int v0 = mt * kTM;
+        const int rows = min(kTM, c_e - v0);
+        const int hrow0 = sched[E + 1 + e] + v0;
+        {
+            const int v = v0 + (tid < rows ? tid : 0);
+            rowmap[tid] = buf_row_of(e, v, R, plan, L);
+        }
+        __syncthreads();
 
-    uint4 ra[4], rb[4];
-    const int KT = F / kBK;
+        // ---- this lane's source for each of its 9 A and 9 B DMA instructions
+        const int n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
+        const uint16_t* wexp0 = MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F;
+        const uint16_t* wexp1 = MODE == kGateUp ? w1 + (size_t)e * F * H : nullptr;
+        const uint16_t* asrc[kDmaPerWave];
+        const uint16_t* bsrc[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const uint4*>(arow[i]);
-        rb[i] = *reinterpret_cast<const uint4*>(brow[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&As[0][(lrow + 32 * i) * kLds + lcol]) = ra[i];
-        *reinterpret_cast<uint4*>(&Bs[0][(lrow + 32 * i) * kLds + lcol]) = rb[i];
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) {
-            const int ko = (kt + 1) * kBK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[i] = *reinterpret_cast<const uint4*>(arow[i] + ko);
-                rb[i] = *reinterpret_cast<const uint4*>(brow[i] + ko);
+        for (int q = 0; q < kDmaPerWave; ++q) {
+            const int slot = 64 * (4 * q + wave) + lane;
+            const int r = slot / kSlotsPerRow, c = slot % kSlotsPerRow;
+            const int chunk = (c < 8 ? c : 0) * 8;
+            if (MODE == kGateUp) {
+                asrc[q] = a_src + (size_t)rowmap[r] * H + chunk;
+                const int f = min(n0 + (r & 127), F - 1);
+                bsrc[q] = (r < 128 ? wexp0 : wexp1) + (size_t)f * H + chunk;
+            } else {
+                asrc[q] = a_src + (size_t)(hrow0 + min(r, rows - 1)) * F + chunk;
+                const int o = min(n0 + r, H - 1);
+                bsrc[q] = wexp0 + (size_t)o * F + chunk;
             }
         }
-        const uint16_t* as = As[cur];
-        const uint16_t* bs = Bs[cur];
+
+        f32x16 acc[4][4];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8 af[4], bf[4];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_frag(as + (wm * 64 + i * 16 + fr) * kLds + kk + fk);
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = lds_frag(bs + (wn * 64 + j * 16 + fr) * kLds + kk + fk);
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+        auto issue = [&](uint16_t* sA, uint16_t* sB, int k0) {
+#pragma unroll
+            for (int q = 0; q < kDmaPerWave; ++q) {
+                dma16(asrc[q] + k0, sA + (4 * q + wave) * 512);
+                dma16(bsrc[q] + k0, sB + (4 * q + wave) * 512);
+            }
+            // keep the prefetch at the head of the stage: nothing moves across
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto frags = [&](const uint16_t* sA, const uint16_t* sB, int kk, bf16x8* af, bf16x8* bf) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+                af[i] = lds_frag(sA + frag_off + (wm * 128 + i * 32) * kRowElems + kk * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = MODE == kGateUp ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32)
+                                               : (wn * 128 + j * 32);
+                bf[j] = lds_frag(sB + frag_off + r0 * kRowElems + kk * 16);
+            }
+        };
+        // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run
+        // (scheduling fences keep the reads ahead of those MFMAs).
+        auto compute = [&](const uint16_t* sA, const uint16_t* sB) {
+            bf16x8 af[2][4], bf[2][4];
+            frags(sA, sB, 0, af[0], bf[0]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) frags(sA, sB, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            bf[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        issue(sA0, sB0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int kt = 0;
+        for (; kt + 2 <= KT; kt += 2) {
+            issue(sA1, sB1, (kt + 1) * kTK);
+            compute(sA0, sB0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * kTK);
+            compute(sA1, sB1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        if (kt < KT) {  // odd stage count: the last stage is already in sA0 / sB0
+            compute(sA0, sB0);
+            __syncthreads();
+        }
+
+        // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
+        // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + i * 32 + fl;
+            if (row >= rows) continue;
+            if (MODE == kGateUp) {
+                uint16_t* dst = out + (size_t)(hrow0 + row) * F;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = n0 + wn * 64 + j * 32 + g4 * 8 + fh * 4;
+                        if (col >= F) continue;
+                        float hv[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            hv[q] = moe::silu(acc[i][j][g4 * 4 + q]) * acc[i][j + 2][g4 * 4 + q];
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                    }
+            } else {
+                uint16_t* dst = out + (size_t)rowmap[row] * H;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) {
-            const int nb = cur ^ 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<uint4*>(&As[nb][(lrow + 32 * i) * kLds + lcol]) = ra[i];
-                *reinterpret_cast<uint4*>(&Bs[nb][(lrow + 32 * i) * kLds + lcol]) = rb[i];
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
+                        if (col >= H) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1]);
+                        pk.y = moe::pack_bf16x2(acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
+                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                    }
             }
         }
         __syncthreads();
     }
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-            if (row >= tile.rows) continue;
-            const int brow_out = rowmap[row];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-                if (col < H) y[(size_t)brow_out * H + col] = moe::f32_to_bf16_bits(acc[i][j][r]);
-            }
-        }
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -441,6 +425,21 @@ __global__ __launch_bounds__(kThreads) void down_f32_kernel(
         }
 }
 
+// Workgroups of the persistent bf16 kernels: one per CU, a multiple of 8 so
+// that every XCD gets the same number.
+int persistent_grid()
+{
+    static int grid = 0;
+    if (grid == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+        grid = cus >= 8 ? (cus / 8) * 8 : 8;
+    }
+    return grid;
+}
+
 int max_mtiles(const moe_shape_t& s, int bm)
 {
     const int64_t N = (int64_t)s.T * s.k;
@@ -456,15 +455,15 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
     const moe::WsLayout W = moe::ws_layout(s);
     int32_t* sched = reinterpret_cast<int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    const int bm = bf ? kBM : kFM;
+    const int bm = bf ? kTM : kFM;
     schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bm, plan, sched);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.T == 0) return e;
     const int mtiles = max_mtiles(s, bm);
     if (bf) {
-        const int nt = s.F / 64;
-        gateup_bf16_kernel<<<mtiles * nt, kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, mtiles, static_cast<const uint16_t*>(a), plan, sched,
+        const int ntn = (s.F + kTN / 2 - 1) / (kTN / 2);
+        gemm_bf16_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(
+            s.E, s.R, s.H, s.F, ntn, static_cast<const uint16_t*>(a), plan, sched,
             static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
             reinterpret_cast<uint16_t*>(ws + W.h));
     } else {
@@ -484,14 +483,13 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
     const moe::WsLayout W = moe::ws_layout(s);
     const int32_t* sched = reinterpret_cast<const int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    const int bm = bf ? kBM : kFM;
-    const int mtiles = max_mtiles(s, bm);
     if (bf) {
-        const int nt = (s.H + 127) / 128;
-        down_bf16_kernel<<<mtiles * nt, kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, mtiles, reinterpret_cast<const uint16_t*>(ws + W.h), plan, sched,
-            static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y));
+        const int ntn = (s.H + kTN - 1) / kTN;
+        gemm_bf16_kernel<kDown><<<persistent_grid(), kThreads, 0, st>>>(
+            s.E, s.R, s.H, s.F, ntn, reinterpret_cast<const uint16_t*>(ws + W.h), plan, sched,
+            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
     } else {
+        const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.H + kFM - 1) / kFM;
         down_f32_kernel<<<mtiles * nt, kThreads, 0, st>>>(
             s.E, s.R, s.H, s.F, mtiles, reinterpret_cast<const float*>(ws + W.h), plan, sched,

@@ -34,6 +34,7 @@
  *     `stream` (a hipStream_t; NULL means the default stream).
  *   - Host-detectable problems (bad shape, NULL pointer, workspace too small)
  *     return a status BEFORE anything is launched; outputs are untouched.
+ *     A pointer to an array of zero length (T = 0) may be NULL.
  *   - Data problems found on the device (non-finite logits, bad ids) set bits
  *     in a caller-provided device int32 error word with an order-free atomic
  *     OR; the caller zeroes it. When it is non-zero the outputs are
