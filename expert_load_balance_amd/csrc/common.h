@@ -67,6 +67,7 @@ __host__ __device__ inline PlanLayout plan_layout(int E, int R)
 struct WsLayout {
     size_t blk_hist, blk_base;  // count: int32[B][E] each
     size_t sched;               // gemm: int32 schedule (see gemm.hip)
+    size_t vrow;                // gemm: int32[N] expert-sorted row -> buf row
     size_t h;                   // gemm: dtype[N][F] SwiGLU activations
     size_t stats;               // stats: int64[kStatsSlots(R)]
     size_t total;
@@ -95,6 +96,7 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     w.blk_hist = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
     w.blk_base = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
     w.sched = o;     o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
+    w.vrow = o;      o = align256(o + (size_t)(N > 0 ? N : 1) * 4);
     w.h = o;         o = align256(o + (size_t)N * s.F * (s.dtype == MOE_BF16 ? 2 : 4));
     w.stats = o;     o = align256(o + (size_t)stats_slots(s.R) * 8);
     w.total = o;

@@ -23,6 +23,8 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// plain vector (not HIP's struct uint4) so staging arrays promote to registers
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
@@ -60,6 +62,38 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(int E, int R, int bm
         sched[0] = 0;
         sched[E + 1] = 0;
     }
+}
+
+// vrow[g] = buf row of the g-th row in expert-sorted order (expert e owns
+// g in [row_start[e], row_start[e+1]); its v-th row lives in the piece that
+// covers v, pieces taken in rank order).
+__global__ __launch_bounds__(kThreads) void vrow_kernel(int N, int E, int R,
+                                                        const int32_t* __restrict__ plan,
+                                                        const int32_t* __restrict__ sched,
+                                                        int32_t* __restrict__ vrow)
+{
+    const int g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= N) return;
+    const moe::PlanLayout L = moe::plan_layout(E, R);
+    const int32_t* row_start = sched + E + 1;
+    int lo = 0, hi = E - 1;  // last expert with row_start <= g
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (row_start[mid] <= g) lo = mid;
+        else hi = mid - 1;
+    }
+    const int v = g - row_start[lo];
+    const int np = plan[L.piece_num + lo];
+    int cum = 0, row = 0;
+    for (int p = 0; p < np && p < R; ++p) {
+        const int c = plan[L.piece_cnt + (size_t)lo * R + p];
+        if (v < cum + c) {
+            row = plan[L.piece_row + (size_t)lo * R + p] + (v - cum);
+            break;
+        }
+        cum += c;
+    }
+    vrow[g] = row;
 }
 
 struct Tile {
@@ -101,65 +135,68 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p)
 {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
 // ---------------------------------------------------------------- bf16 ----
 // Persistent kernel, one 256-thread workgroup per CU. Workgroup tile: 256
 // rows x 256 B-rows (gate/up: 128 F-columns of gate and the same 128 of up;
-// down: 256 output columns); K in 64-deep stages, double-buffered.
+// down: 256 output columns); K in 64-deep stages, two LDS buffers per operand.
 //  * Global -> LDS with global_load_lds_dwordx4 (lane l of an instruction
-//    lands at LDS base + 16 l), so no VGPRs stage the tiles.
-//  * A stage is 256 rows of 9 16-byte slots: 8 K-chunks + 1 pad (144-byte
-//    rows), which keeps the MFMA fragment reads (32 rows, one chunk) free of
-//    bank conflicts. DMA instruction q fills slots 64q .. 64q+63; a lane whose
-//    slot is a pad slot loads its row's first chunk into it (never read).
-//    Global reads stay 128-byte row runs.
-//  * Fragment addresses are one VGPR per lane plus immediate offsets.
-//  * Each stage is its own LDS array, so the wait for a prefetch into one
-//    stage does not block reads of the other.
+//    lands at its LDS base + 16 l): tiles never pass through VGPRs. A stage
+//    buffer is 256 rows of 9 16-byte slots (8 K-chunks + 1 pad = 144-byte
+//    rows), which keeps the MFMA fragment reads (32 consecutive rows, one
+//    chunk) free of bank conflicts; pad slots receive a harmless copy.
+//    Every DMA source is a wave-uniform base plus a fixed 32-bit lane offset.
 //  * 4 waves in 2 x 2, each 128 rows x 128 B-rows with
-//    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs);
-//    the next k-step's fragments are read between the current MFMAs.
+//    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs).
 //    Operands are swapped so a lane holds 4 consecutive output columns: the
 //    epilogue stores 8 bytes per lane straight to global memory.
+//  * Software pipeline per stage s: fragments of k-step kk+1 are read while
+//    the MFMAs of kk run; the barrier sits before the last k-step's MFMAs;
+//    after it the buffer stage s used is refilled with stage s+2 and the next
+//    stage's first fragments are read under those MFMAs.
 //  * Tile order: expert, N-tile, M-tile (M fastest), so the M-tiles sharing
 //    a weight tile run together; each XCD takes a contiguous run of tiles so
 //    they share its L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kSlotsPerRow = kTK / 8 + 1;                  // 9
-constexpr int kRowElems = kSlotsPerRow * 8;                // 72 bf16 = 144 bytes
-constexpr int kStageElems = kTM * kRowElems;               // 36 KB per stage
-constexpr int kDmaPerStage = kTM * kSlotsPerRow / 64;      // 36 instructions
-constexpr int kDmaPerWave = kDmaPerStage / 4;              // 9
+constexpr int kSlotsPerRow = kTK / 8 + 1;            // 8 K-chunks + 1 pad slot (16 bytes each)
+constexpr int kRowElems = kSlotsPerRow * 8;          // 72 bf16 = 144 bytes per LDS row
+constexpr int kStageElems = kTM * kRowElems;         // 36 KB per A or B stage buffer
+constexpr int kDmaPerStage = kTM * kSlotsPerRow / 64; // 36 DMA instructions per operand
+constexpr int kDmaPerWave = kDmaPerStage / 4;        // 9
+constexpr int kGateDma = 128 * kSlotsPerRow / 64;    // instructions 0..17 hold gate rows
 enum { kGateUp = 0, kDown = 1 };
 
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* l)
+// global -> LDS, 16 bytes per lane; lane l of the wave lands at l_base + 16 l
+__device__ __forceinline__ void dma16(const void* g, uint16_t* l_base)
 {
-    __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l_base, 16, 0, 0);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
-    int E, int R, int H, int F, int ntiles_n, const uint16_t* __restrict__ a_src,
-    const int32_t* __restrict__ plan, const int32_t* __restrict__ sched,
+    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t sA0[kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sA1[kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sB0[kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sB1[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sB1[kStageElems];
     __shared__ int32_t rowmap[kTM];
+    __shared__ int32_t ssched[2 * 257];  // tile_start[E+1], row_start[E+1]
 
-    const moe::PlanLayout L = moe::plan_layout(E, R);
+    for (int i = threadIdx.x; i < 2 * (E + 1); i += kThreads) ssched[i] = sched[i];
+    __syncthreads();
     const int K = MODE == kGateUp ? H : F;
     const int KT = K / kTK;
-    const int total = sched[E] * ntiles_n;
+    const int total = ssched[E] * ntiles_n;
     const int P = gridDim.x;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -168,8 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int fl = lane & 31, fh = lane >> 5;
-    // fragment base: row (lane & 31) of a 32-row block, K-chunk (lane >> 5)
-    const int frag_off = fl * kRowElems + fh * 8;
+    const int frag_off = fl * kRowElems + fh * 8;      // fragment row, K-chunk
 
     for (int base = 0;; base += P) {
         const int Lt = base + my_slot;
@@ -178,44 +214,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         int lo = 0, hi = E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (sched[mid] * ntiles_n <= Lt) lo = mid;
+            if (ssched[mid] * ntiles_n <= Lt) lo = mid;
             else hi = mid - 1;
         }
         const int e = lo;
-        const int mt_e = sched[e + 1] - sched[e];
-        const int local = Lt - sched[e] * ntiles_n;
+        const int mt_e = ssched[e + 1] - ssched[e];
+        const int local = Lt - ssched[e] * ntiles_n;
         const int nt = local / mt_e, mt = local % mt_e;
-        const int c_e = sched[E + 1 + e + 1] - sched[E + 1 + e];
+        const int c_e = ssched[E + 1 + e + 1] - ssched[E + 1 + e];
         const int v0 = mt * kTM;
         const int rows = min(kTM, c_e - v0);
-        const int hrow0 = sched[E + 1 + e] + v0;
-        {
-            const int v = v0 + (tid < rows ? tid : 0);
-            rowmap[tid] = buf_row_of(e, v, R, plan, L);
-        }
+        const int hrow0 = ssched[E + 1 + e] + v0;
+        rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : 0)];
         __syncthreads();
 
-        // ---- this lane's source for each of its 9 A and 9 B DMA instructions
+        // ---- DMA sources. Stage buffer = 256 rows x 9 slots; DMA instruction
+        // q (0..35) fills slots 64q .. 64q+63, lane l slot 64q + l, i.e. row
+        // (64q+l)/9, slot (64q+l)%9 (slot 8 is the pad: it gets the row's
+        // chunk 0, never read). Wave w issues instructions q = 4i + w. Each
+        // source is a wave-uniform base plus a fixed 32-bit lane offset.
         const int n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
-        const uint16_t* wexp0 = MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F;
-        const uint16_t* wexp1 = MODE == kGateUp ? w1 + (size_t)e * F * H : nullptr;
-        const uint16_t* asrc[kDmaPerWave];
-        const uint16_t* bsrc[kDmaPerWave];
+        const char* abase = reinterpret_cast<const char*>(MODE == kGateUp ? a_src : a_src + (size_t)hrow0 * F);
+        const char* bbase0 = reinterpret_cast<const char*>(
+            MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F);
+        const char* bbase1 = MODE == kGateUp ? reinterpret_cast<const char*>(w1 + (size_t)e * F * H)
+                                             : bbase0;
+        uint32_t aoff[kDmaPerWave], boff[kDmaPerWave];
 #pragma unroll
-        for (int q = 0; q < kDmaPerWave; ++q) {
-            const int slot = 64 * (4 * q + wave) + lane;
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            const int slot = 64 * (4 * i + wave) + lane;
             const int r = slot / kSlotsPerRow, c = slot % kSlotsPerRow;
-            const int chunk = (c < 8 ? c : 0) * 8;
+            const uint32_t chunk = (c < 8 ? c : 0) * 16;
             if (MODE == kGateUp) {
-                asrc[q] = a_src + (size_t)rowmap[r] * H + chunk;
-                const int f = min(n0 + (r & 127), F - 1);
-                bsrc[q] = (r < 128 ? wexp0 : wexp1) + (size_t)f * H + chunk;
+                aoff[i] = (uint32_t)rowmap[r] * (uint32_t)H * 2u + chunk;
+                const int f = min(n0 + (r & 127), F - 1);   // rows 0..127 gate, 128..255 up
+                boff[i] = (uint32_t)f * (uint32_t)H * 2u + chunk;
             } else {
-                asrc[q] = a_src + (size_t)(hrow0 + min(r, rows - 1)) * F + chunk;
+                aoff[i] = (uint32_t)min(r, rows - 1) * (uint32_t)F * 2u + chunk;
                 const int o = min(n0 + r, H - 1);
-                bsrc[q] = wexp0 + (size_t)o * F + chunk;
+                boff[i] = (uint32_t)o * (uint32_t)F * 2u + chunk;
             }
         }
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -226,13 +266,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
         auto issue = [&](uint16_t* sA, uint16_t* sB, int k0) {
+            const char* ab = abase + (size_t)k0 * 2;
+            const char* b0 = bbase0 + (size_t)k0 * 2;
+            const char* b1 = bbase1 + (size_t)k0 * 2;
 #pragma unroll
-            for (int q = 0; q < kDmaPerWave; ++q) {
-                dma16(asrc[q] + k0, sA + (4 * q + wave) * 512);
-                dma16(bsrc[q] + k0, sB + (4 * q + wave) * 512);
+            for (int i = 0; i < kDmaPerWave; ++i) {
+                const int q = 4 * i + wave_u;
+                dma16(ab + aoff[i], sA + q * 512);
+                dma16((q < kGateDma ? b0 : b1) + boff[i], sB + q * 512);
             }
-            // keep the prefetch at the head of the stage: nothing moves across
-            __builtin_amdgcn_sched_barrier(0);
         };
         auto frags = [&](const uint16_t* sA, const uint16_t* sB, int kk, bf16x8* af, bf16x8* bf) {
 #pragma unroll
@@ -245,43 +287,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                 bf[j] = lds_frag(sB + frag_off + r0 * kRowElems + kk * 16);
             }
         };
-        // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run
-        // (scheduling fences keep the reads ahead of those MFMAs).
-        auto compute = [&](const uint16_t* sA, const uint16_t* sB) {
-            bf16x8 af[2][4], bf[2][4];
-            frags(sA, sB, 0, af[0], bf[0]);
+        auto mfmas = [&](const bf16x8* af, const bf16x8* bf) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 3) frags(sA, sB, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        };
+
+        bf16x8 af[2][4], bf[2][4];
+        // One stage on buffer c while n holds the next one. do_issue: refill c
+        // with stage s_+2 right after the barrier that retires c's reads.
+        auto stage = [&](uint16_t* cA, uint16_t* cB, uint16_t* nA, uint16_t* nB, int s_,
+                         bool do_issue) {
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) {
+                frags(cA, cB, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            bf[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
+                mfmas(af[kk & 1], bf[kk & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into n has landed
+            __syncthreads();                // all of n landed; everyone is done reading c
+            if (do_issue && s_ + 2 < KT) issue(cA, cB, (s_ + 2) * kTK);
+            if (s_ + 1 < KT) frags(nA, nB, 0, af[0], bf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(af[1], bf[1]);
+            __builtin_amdgcn_sched_barrier(0);
         };
 
         issue(sA0, sB0, 0);
+        if (KT > 1) issue(sA1, sB1, kTK);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        frags(sA0, sB0, 0, af[0], bf[0]);
+        // Stages go in pairs (buffer 0, buffer 1). The refill of buffer 1 that
+        // the second stage of a pair owes is issued at the top of the next pair
+        // instead (the same barrier covers it), so no DMA is in flight across
+        // the loop back edge: the compiler then keeps tracking DMAs per buffer
+        // and never makes a read of one buffer wait for a refill of the other.
         int kt = 0;
         for (; kt + 2 <= KT; kt += 2) {
-            issue(sA1, sB1, (kt + 1) * kTK);
-            compute(sA0, sB0);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * kTK);
-            compute(sA1, sB1);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            if (kt >= 2) issue(sA1, sB1, (kt + 1) * kTK);
+            stage(sA0, sB0, sA1, sB1, kt, true);
+            stage(sA1, sB1, sA0, sB0, kt + 1, false);
         }
-        if (kt < KT) {  // odd stage count: the last stage is already in sA0 / sB0
-            compute(sA0, sB0);
-            __syncthreads();
-        }
+        if (kt < KT) stage(sA0, sB0, sA1, sB1, kt, true);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
         // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
@@ -462,8 +513,13 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
     const int mtiles = max_mtiles(s, bm);
     if (bf) {
         const int ntn = (s.F + kTN / 2 - 1) / (kTN / 2);
+        const int N = s.T * s.k;
+        int32_t* vrow = reinterpret_cast<int32_t*>(ws + W.vrow);
+        vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.R, plan, sched, vrow);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
         gemm_bf16_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, ntn, static_cast<const uint16_t*>(a), plan, sched,
+            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
             static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
             reinterpret_cast<uint16_t*>(ws + W.h));
     } else {
@@ -486,8 +542,9 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
     if (bf) {
         const int ntn = (s.H + kTN - 1) / kTN;
         gemm_bf16_kernel<kDown><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, ntn, reinterpret_cast<const uint16_t*>(ws + W.h), plan, sched,
-            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
+            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched,
+            reinterpret_cast<const int32_t*>(ws + W.vrow), static_cast<const uint16_t*>(w_down),
+            nullptr, static_cast<uint16_t*>(y));
     } else {
         const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.H + kFM - 1) / kFM;
