@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (a known "
+                         "byte count for calibrating HBM counters), then exit")
     return ap.parse_args()
 
 
@@ -105,6 +108,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": 2 * a.numel() * a.element_size()}))
+        return
 
     import expert_load_balance_amd as moe
     from expert_load_balance_amd.layer import STAGES, MoeLayerBuffers
@@ -203,8 +215,8 @@ def main():
                  "ranks_over_slots": st["ranks_over_slots"]},
     }
     if not args.no_cpu_baseline:
-        # about 2e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
-        ntok = args.cpu_tokens or max(1, min(T, int(2e10 / (k * 3 * H * F))))
+        # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
+        ntok = args.cpu_tokens or max(1, min(T, int(5e10 / (k * 3 * H * F))))
         rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, ntok)
     print(json.dumps(rec), flush=True)
 

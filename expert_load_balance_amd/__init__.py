@@ -18,7 +18,8 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "Shape", "StatsT", "lib_path", "load",
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
     "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
-    "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "plan_tables",
+    "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
+    "plan_tables",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -28,8 +29,8 @@ ERR_NONFINITE, ERR_RANGE, ERR_REPEAT = 1, 2, 4
 
 EXPORTED_SYMBOLS = (
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes", "moe_route",
-    "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_gateup",
-    "moe_gemm_down", "moe_combine", "moe_stats",
+    "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_schedule",
+    "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -121,6 +122,7 @@ def load():
         "moe_plan": (st, [_SP, _VP, _VP, _VP]),
         "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_gemm_schedule": (st, [_SP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_gemm_gateup": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_gemm_down": (st, [_SP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_combine": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -254,6 +256,14 @@ def moe_grouped_gemm(shape, a, plan, w_gate, w_up, w_down, y, ws, stream=None):
             _ptr(plan, torch.int32, "plan"), g, u, d, _ptr(y, act, "y", shape.N * shape.H),
             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _ok(load().moe_grouped_gemm(*args), "moe_grouped_gemm")
+
+
+def moe_gemm_schedule(shape, plan, ws, stream=None):
+    import torch
+
+    args = (ctypes.byref(shape), _ptr(plan, torch.int32, "plan"), _ptr(ws, None, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    _ok(load().moe_gemm_schedule(*args), "moe_gemm_schedule")
 
 
 def moe_gemm_gateup(shape, a, plan, w_gate, w_up, ws, stream=None):

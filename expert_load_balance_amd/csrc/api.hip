@@ -130,6 +130,16 @@ moe_status_t moe_permute(const moe_shape_t* shape, const void* d_x, const int32_
                                   d_row_src, as_stream(stream)));
 }
 
+moe_status_t moe_gemm_schedule(const moe_shape_t* shape, const int32_t* d_plan, void* d_ws,
+                               size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_plan || !d_ws) return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_gemm_schedule(*shape, d_plan, static_cast<char*>(d_ws), as_stream(stream)));
+}
+
 moe_status_t moe_gemm_gateup(const moe_shape_t* shape, const void* d_a, const int32_t* d_plan,
                              const void* d_w_gate, const void* d_w_up, void* d_ws,
                              size_t ws_bytes, moe_stream_t stream)
@@ -159,7 +169,9 @@ moe_status_t moe_grouped_gemm(const moe_shape_t* shape, const void* d_a, const i
                               const void* d_w_gate, const void* d_w_up, const void* d_w_down,
                               void* d_y, void* d_ws, size_t ws_bytes, moe_stream_t stream)
 {
-    moe_status_t st = moe_gemm_gateup(shape, d_a, d_plan, d_w_gate, d_w_up, d_ws, ws_bytes, stream);
+    moe_status_t st = moe_gemm_schedule(shape, d_plan, d_ws, ws_bytes, stream);
+    if (st == MOE_OK)
+        st = moe_gemm_gateup(shape, d_a, d_plan, d_w_gate, d_w_up, d_ws, ws_bytes, stream);
     if (st != MOE_OK) return st;
     return moe_gemm_down(shape, d_plan, d_w_down, d_y, d_ws, ws_bytes, stream);
 }

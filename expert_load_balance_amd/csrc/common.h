@@ -118,6 +118,8 @@ hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t
                               int32_t* dest_row, int32_t* row_src, hipStream_t st);
 hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t* dest_row,
                               const float* w, const void* shared_y, void* out, hipStream_t st);
+hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, char* ws,
+                                    hipStream_t st);
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
                                   hipStream_t st);

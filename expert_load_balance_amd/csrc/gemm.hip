@@ -499,30 +499,36 @@ int max_mtiles(const moe_shape_t& s, int bm)
 
 }  // namespace
 
-hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
-                                  const void* w_gate, const void* w_up, char* ws,
-                                  hipStream_t st)
+hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, char* ws,
+                                    hipStream_t st)
 {
     const moe::WsLayout W = moe::ws_layout(s);
     int32_t* sched = reinterpret_cast<int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    const int bm = bf ? kTM : kFM;
-    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bm, plan, sched);
+    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bf ? kTM : kFM, plan, sched);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || s.T == 0) return e;
-    const int mtiles = max_mtiles(s, bm);
-    if (bf) {
+    const int N = s.T * s.k;
+    if (e != hipSuccess || !bf || N == 0) return e;
+    int32_t* vrow = reinterpret_cast<int32_t*>(ws + W.vrow);
+    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.R, plan, sched, vrow);
+    return hipGetLastError();
+}
+
+hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
+                                  const void* w_gate, const void* w_up, char* ws,
+                                  hipStream_t st)
+{
+    if (s.T == 0) return hipSuccess;
+    const moe::WsLayout W = moe::ws_layout(s);
+    const int32_t* sched = reinterpret_cast<const int32_t*>(ws + W.sched);
+    if (s.dtype == MOE_BF16) {
         const int ntn = (s.F + kTN / 2 - 1) / (kTN / 2);
-        const int N = s.T * s.k;
-        int32_t* vrow = reinterpret_cast<int32_t*>(ws + W.vrow);
-        vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.R, plan, sched, vrow);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
         gemm_bf16_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
-            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
-            reinterpret_cast<uint16_t*>(ws + W.h));
+            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched,
+            reinterpret_cast<const int32_t*>(ws + W.vrow), static_cast<const uint16_t*>(w_gate),
+            static_cast<const uint16_t*>(w_up), reinterpret_cast<uint16_t*>(ws + W.h));
     } else {
+        const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.F + kFM - 1) / kFM;
         gateup_f32_kernel<<<mtiles * nt, kThreads, 0, st>>>(
             s.E, s.R, s.H, s.F, mtiles, static_cast<const float*>(a), plan, sched,

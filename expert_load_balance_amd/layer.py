@@ -10,9 +10,11 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, Shape, moe_combine, moe_count, moe_gemm_down, moe_gemm_gateup,
-               moe_permute, moe_plan, moe_plan_layout, moe_route, moe_workspace_bytes)
+               moe_gemm_schedule, moe_permute, moe_plan, moe_plan_layout, moe_route,
+               moe_workspace_bytes)
 
-STAGES = ("route", "count", "plan", "permute", "gemm_gateup", "gemm_down", "shared", "combine")
+STAGES = ("route", "count", "plan", "permute", "gemm_schedule", "gemm_gateup", "gemm_down",
+          "shared", "combine")
 
 
 def alloc(shape, dtype, device):
@@ -88,6 +90,9 @@ class MoeLayerBuffers:
         mark("permute", 0)
         moe_permute(s, x, self.ids, self.eidx, self.plan, self.buf, self.dest_row, self.row_src, st)
         mark("permute", 1)
+        mark("gemm_schedule", 0)
+        moe_gemm_schedule(s, self.plan, self.ws, st)
+        mark("gemm_schedule", 1)
         mark("gemm_gateup", 0)
         moe_gemm_gateup(s, self.buf, self.plan, w_gate, w_up, self.ws, st)
         mark("gemm_gateup", 1)
@@ -98,6 +103,7 @@ class MoeLayerBuffers:
         if self.shared_shape is not None and shared_w is not None:
             mark("shared", 0)
             sg, su, sd = shared_w
+            moe_gemm_schedule(self.shared_shape, self.shared_plan, self.shared_ws, st)
             moe_gemm_gateup(self.shared_shape, x, self.shared_plan, sg, su, self.shared_ws, st)
             moe_gemm_down(self.shared_shape, self.shared_plan, sd, self.shared_y, self.shared_ws, st)
             mark("shared", 1)

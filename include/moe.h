@@ -220,9 +220,13 @@ moe_status_t moe_grouped_gemm(const moe_shape_t *shape, const void *d_a, const i
                               const void *d_w_gate, const void *d_w_up, const void *d_w_down,
                               void *d_y, void *d_ws, size_t ws_bytes, moe_stream_t stream);
 
-/* The two halves of moe_grouped_gemm, for callers that time or overlap them
- * separately (same arguments; call gateup, then down, with the same d_ws).
- * moe_gemm_gateup also builds the tile schedule in d_ws. */
+/* The three steps of moe_grouped_gemm, for callers that time or overlap them
+ * separately (same arguments, same d_ws, in this order): moe_gemm_schedule
+ * builds the per-expert tile schedule and the expert-sorted row -> buf row
+ * map in d_ws from the plan; moe_gemm_gateup computes h; moe_gemm_down
+ * computes y. */
+moe_status_t moe_gemm_schedule(const moe_shape_t *shape, const int32_t *d_plan, void *d_ws,
+                               size_t ws_bytes, moe_stream_t stream);
 moe_status_t moe_gemm_gateup(const moe_shape_t *shape, const void *d_a, const int32_t *d_plan,
                              const void *d_w_gate, const void *d_w_up, void *d_ws,
                              size_t ws_bytes, moe_stream_t stream);
