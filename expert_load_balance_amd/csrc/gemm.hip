@@ -18,6 +18,8 @@
 //   down:    y[buf row of v][o] = h[row_start[e] + v] . Wd[e][o].
 // bf16 path: a persistent MFMA kernel (below); fp32 path: plain LDS-tiled
 // VALU kernels for small shapes.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -181,9 +183,10 @@ __device__ __forceinline__ void dma16(const void* g, uint16_t* l_base)
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
-    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    int E, int ntiles_n, int H, int F, int ksplit, int N, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
-    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out)
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
+    float* __restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
@@ -195,8 +198,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     for (int i = threadIdx.x; i < 2 * (E + 1); i += kThreads) ssched[i] = sched[i];
     __syncthreads();
     const int K = MODE == kGateUp ? H : F;
-    const int KT = K / kTK;
-    const int total = ssched[E] * ntiles_n;
+    const int KT_all = K / kTK;
+    const int KT_half = (KT_all + ksplit - 1) / ksplit;
+    const int total = ssched[E] * ntiles_n * ksplit;
     const int P = gridDim.x;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -208,9 +212,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const int frag_off = fl * kRowElems + fh * 8;      // fragment row, K-chunk
 
     for (int base = 0;; base += P) {
-        const int Lt = base + my_slot;
-        if (Lt >= total) break;
-        // ---- decode the tile: expert, N-tile, M-tile
+        const int Lu = base + my_slot;
+        if (Lu >= total) break;
+        // ---- decode the work unit: K-part (split-K), then the tile: expert,
+        // N-tile, M-tile
+        const int Lt = Lu / ksplit, kpart = Lu % ksplit;
+        const int KT = min(KT_all, (kpart + 1) * KT_half) - kpart * KT_half;
+        const int kofs = kpart * KT_half * kTK;
         int lo = 0, hi = E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -234,10 +242,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         // chunk 0, never read). Wave w issues instructions q = 4i + w. Each
         // source is a wave-uniform base plus a fixed 32-bit lane offset.
         const int n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
-        const char* abase = reinterpret_cast<const char*>(MODE == kGateUp ? a_src : a_src + (size_t)hrow0 * F);
+        const char* abase = reinterpret_cast<const char*>(
+            (MODE == kGateUp ? a_src : a_src + (size_t)hrow0 * F) + kofs);
         const char* bbase0 = reinterpret_cast<const char*>(
-            MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F);
-        const char* bbase1 = MODE == kGateUp ? reinterpret_cast<const char*>(w1 + (size_t)e * F * H)
+            (MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F) + kofs);
+        const char* bbase1 = MODE == kGateUp ? reinterpret_cast<const char*>(w1 + (size_t)e * F * H + kofs)
                                              : bbase0;
         uint32_t aoff[kDmaPerWave], boff[kDmaPerWave];
 #pragma unroll
@@ -296,10 +305,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         };
 
         bf16x8 af[2][4], bf[2][4];
-        // One stage on buffer c while n holds the next one. do_issue: refill c
-        // with stage s_+2 right after the barrier that retires c's reads.
-        auto stage = [&](uint16_t* cA, uint16_t* cB, uint16_t* nA, uint16_t* nB, int s_,
-                         bool do_issue) {
+        // One stage on buffer c while n holds the next one. REFILL: refill c
+        // with stage s_+2 right after the barrier that retires c's reads, its
+        // DMA instructions threaded between the last k-step's MFMAs (the caller
+        // guarantees s_+2 < KT). Otherwise no refill.
+        auto stage = [&](auto refill, uint16_t* cA, uint16_t* cB, uint16_t* nA, uint16_t* nB,
+                         int s_) {
+            constexpr bool REFILL = decltype(refill)::value;
 #pragma unroll
             for (int kk = 0; kk < 3; ++kk) {
                 frags(cA, cB, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
@@ -309,12 +321,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             }
             __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into n has landed
             __syncthreads();                // all of n landed; everyone is done reading c
-            if (do_issue && s_ + 2 < KT) issue(cA, cB, (s_ + 2) * kTK);
             if (s_ + 1 < KT) frags(nA, nB, 0, af[0], bf[0]);
             __builtin_amdgcn_sched_barrier(0);
+            if (REFILL) issue(cA, cB, (s_ + 2) * kTK);
             mfmas(af[1], bf[1]);
+            if (REFILL) {
+#pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 DMA
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         };
+        using Refill = std::true_type;
+        using NoRefill = std::false_type;
 
         issue(sA0, sB0, 0);
         if (KT > 1) issue(sA1, sB1, kTK);
@@ -326,13 +347,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         // instead (the same barrier covers it), so no DMA is in flight across
         // the loop back edge: the compiler then keeps tracking DMAs per buffer
         // and never makes a read of one buffer wait for a refill of the other.
+        // The loop runs while the first stage of a pair has a stage to refill
+        // (kt + 2 < KT); at most two stages remain after it, neither refills.
         int kt = 0;
-        for (; kt + 2 <= KT; kt += 2) {
+        for (; kt + 2 < KT; kt += 2) {
             if (kt >= 2) issue(sA1, sB1, (kt + 1) * kTK);
-            stage(sA0, sB0, sA1, sB1, kt, true);
-            stage(sA1, sB1, sA0, sB0, kt + 1, false);
+            stage(Refill{}, sA0, sB0, sA1, sB1, kt);
+            stage(NoRefill{}, sA1, sB1, sA0, sB0, kt + 1);
         }
-        if (kt < KT) stage(sA0, sB0, sA1, sB1, kt, true);
+        if (kt >= 2 && kt + 1 < KT) issue(sA1, sB1, (kt + 1) * kTK);
+        stage(NoRefill{}, sA0, sB0, sA1, sB1, kt);
+        if (kt + 1 < KT) stage(NoRefill{}, sA1, sB1, sA0, sB0, kt + 1);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
         // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
@@ -357,6 +382,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                         pk.y = moe::pack_bf16x2(hv[2], hv[3]);
                         *reinterpret_cast<uint2*>(dst + col) = pk;
                     }
+            } else if (ksplit > 1) {
+                // fp32 partial sums, expert-sorted rows; summed by ksum_kernel
+                float* dst = part + ((size_t)kpart * N + hrow0 + row) * H;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
+                        if (col >= H) continue;
+                        *reinterpret_cast<float4*>(dst + col) =
+                            make_float4(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1],
+                                        acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
+                    }
             } else {
                 uint16_t* dst = out + (size_t)rowmap[row] * H;
 #pragma unroll
@@ -374,6 +412,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         }
         __syncthreads();
     }
+}
+
+// Split-K epilogue of the down GEMM: y[vrow[g]] = bf16(part0[g] + part1[g]),
+// 8 columns per thread. Two partials, so the sum is independent of order.
+__global__ __launch_bounds__(kThreads) void ksum_kernel(int N, int H, const float* __restrict__ part,
+                                                        const int32_t* __restrict__ vrow,
+                                                        uint16_t* __restrict__ y)
+{
+    const int per_row = H / 8;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)N * per_row) return;
+    const int g = (int)(i / per_row), c = (int)(i % per_row) * 8;
+    const float* p0 = part + (size_t)g * H + c;
+    const float* p1 = p0 + (size_t)N * H;
+    const float4 a0 = *reinterpret_cast<const float4*>(p0), a1 = *reinterpret_cast<const float4*>(p0 + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(p1), b1 = *reinterpret_cast<const float4*>(p1 + 4);
+    uint4 o;
+    o.x = moe::pack_bf16x2(a0.x + b0.x, a0.y + b0.y);
+    o.y = moe::pack_bf16x2(a0.z + b0.z, a0.w + b0.w);
+    o.z = moe::pack_bf16x2(a1.x + b1.x, a1.y + b1.y);
+    o.w = moe::pack_bf16x2(a1.z + b1.z, a1.w + b1.w);
+    *reinterpret_cast<uint4*>(y + (size_t)vrow[g] * H + c) = o;
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -524,9 +584,9 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
     if (s.dtype == MOE_BF16) {
         const int ntn = (s.F + kTN / 2 - 1) / (kTN / 2);
         gemm_bf16_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched,
+            s.E, ntn, s.H, s.F, 1, s.T * s.k, static_cast<const uint16_t*>(a), sched,
             reinterpret_cast<const int32_t*>(ws + W.vrow), static_cast<const uint16_t*>(w_gate),
-            static_cast<const uint16_t*>(w_up), reinterpret_cast<uint16_t*>(ws + W.h));
+            static_cast<const uint16_t*>(w_up), reinterpret_cast<uint16_t*>(ws + W.h), nullptr);
     } else {
         const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.F + kFM - 1) / kFM;
@@ -547,10 +607,19 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
     const bool bf = s.dtype == MOE_BF16;
     if (bf) {
         const int ntn = (s.H + kTN - 1) / kTN;
+        const int ks = moe::down_ksplit(s);
+        const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
+        float* part = reinterpret_cast<float*>(ws + W.part);
         gemm_bf16_kernel<kDown><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched,
-            reinterpret_cast<const int32_t*>(ws + W.vrow), static_cast<const uint16_t*>(w_down),
-            nullptr, static_cast<uint16_t*>(y));
+            s.E, ntn, s.H, s.F, ks, s.T * s.k, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
+            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y), part);
+        if (ks > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t n = (int64_t)s.T * s.k * (s.H / 8);
+            ksum_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+                s.T * s.k, s.H, part, vrow, static_cast<uint16_t*>(y));
+        }
     } else {
         const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.H + kFM - 1) / kFM;

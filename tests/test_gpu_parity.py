@@ -117,6 +117,8 @@ SMALL = [
     ("bf16_dense_one_expert", 65, 128, 1, 1, 128, 1, 1, moe.MOE_BF16, 0.0),
     ("bf16_all_experts", 33, 64, 8, 8, 64, 2, 4, moe.MOE_BF16, 0.2),
     ("bf16_fewer_rows_than_ranks", 1, 64, 8, 2, 64, 4, 2, moe.MOE_BF16, 0.0),
+    ("bf16_odd_k_split", 300, 128, 8, 2, 192, 4, 2, moe.MOE_BF16, 0.3),
+    ("bf16_two_experts_wide", 520, 512, 2, 1, 256, 2, 1, moe.MOE_BF16, 0.0),
 ]
 
 
