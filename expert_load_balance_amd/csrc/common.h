@@ -11,7 +11,10 @@ namespace moe {
 constexpr int kWave = 64;
 
 // bf16 storage is the upper half of an IEEE fp32; conversions are exact one
-// way and round-to-nearest-even the other.
+// way and round-to-nearest-even the other (gfx950's v_cvt_pk_bf16_f32; NaN
+// stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
 {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -19,17 +22,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Two bf16 values packed in a uint32 (low half = lower address).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-           (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -135,51 +135,118 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
     return 0;
 }
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p)
-{
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
 // ---------------------------------------------------------------- bf16 ----
 // Persistent kernel, one 256-thread workgroup per CU. Workgroup tile: 256
 // rows x 256 B-rows (gate/up: 128 F-columns of gate and the same 128 of up;
-// down: 256 output columns); K in 64-deep stages, two LDS buffers per operand.
-//  * Global -> LDS with global_load_lds_dwordx4 (lane l of an instruction
-//    lands at its LDS base + 16 l): tiles never pass through VGPRs. A stage
-//    buffer is 256 rows of 9 16-byte slots (8 K-chunks + 1 pad = 144-byte
-//    rows), which keeps the MFMA fragment reads (32 consecutive rows, one
-//    chunk) free of bank conflicts; pad slots receive a harmless copy.
-//    Every DMA source is a wave-uniform base plus a fixed 32-bit lane offset.
+// down: 256 output columns); K in 64-deep stages.
+//  * LDS holds two stage slots (A 32 KB + B 32 KB each). A slot row is 128
+//    bytes, one full L1/L2 line of the source row, so every line is fetched
+//    once. K-chunk c of row r sits in slot c ^ swz(r), which keeps the MFMA
+//    fragment reads (32 consecutive rows, one chunk each) free of bank
+//    conflicts.
+//  * Global -> LDS with global_load_lds_dwordx4: lane l of an instruction
+//    lands at its LDS base + 16 l (8 rows of 128 bytes per instruction), so
+//    the swizzle is applied on the source side: each lane's source is a
+//    fixed 32-bit offset from a uniform base.
 //  * 4 waves in 2 x 2, each 128 rows x 128 B-rows with
 //    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs).
 //    Operands are swapped so a lane holds 4 consecutive output columns: the
 //    epilogue stores 8 bytes per lane straight to global memory.
-//  * Software pipeline per stage s: fragments of k-step kk+1 are read while
-//    the MFMAs of kk run; the barrier sits before the last k-step's MFMAs;
-//    after it the buffer stage s used is refilled with stage s+2 and the next
-//    stage's first fragments are read under those MFMAs.
+//  * Stage s, hand-scheduled over its 4 k-steps of 16 MFMAs: the fragments
+//    of all four k-steps are read from the slot during k-steps 0 and 1; one
+//    workgroup barrier follows (the slot is then free, and the other slot,
+//    stage s+1, has landed: each wave waits for its own copies first); the
+//    refill of the slot with stage s+2 and the first fragments of stage s+1
+//    are spread over k-steps 2 and 3.
+//  * The next tile's first two stages are issued right after the last
+//    stage's barrier, ahead of this tile's epilogue, whose arithmetic and
+//    stores then hide their latency.
 //  * Tile order: expert, N-tile, M-tile (M fastest), so the M-tiles sharing
 //    a weight tile run together; each XCD takes a contiguous run of tiles so
 //    they share its L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kSlotsPerRow = kTK / 8 + 1;            // 8 K-chunks + 1 pad slot (16 bytes each)
-constexpr int kRowElems = kSlotsPerRow * 8;          // 72 bf16 = 144 bytes per LDS row
-constexpr int kStageElems = kTM * kRowElems;         // 36 KB per A or B stage buffer
-constexpr int kDmaPerStage = kTM * kSlotsPerRow / 64; // 36 DMA instructions per operand
-constexpr int kDmaPerWave = kDmaPerStage / 4;        // 9
-constexpr int kGateDma = 128 * kSlotsPerRow / 64;    // instructions 0..17 hold gate rows
+constexpr int kOpBytes = kTM * kTK * 2;           // 32 KB: one operand of one stage
+constexpr int kSlotBytes = 2 * kOpBytes;          // A, then B
+constexpr int kCopiesWave = kOpBytes / 1024 / 4;  // 8 copies per operand per wave
 enum { kGateUp = 0, kDown = 1 };
 
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
+// Slot of K-chunk c (0..7) in LDS row r is c ^ swz(r): 8 consecutive rows
+// reading one chunk hit 8 distinct 16-byte groups of a 128-byte bank line,
+// 16 consecutive rows 16 distinct groups of a 256-byte line.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// global -> LDS, 16 bytes per lane; lane l of the wave lands at l_base + 16 l
-__device__ __forceinline__ void dma16(const void* g, uint16_t* l_base)
+// Global -> LDS copy, 16 bytes per lane; lane l's bytes land at lds + 16 l.
+// Written as asm so the compiler's wait-count pass does not see the slots as
+// targets of outstanding loads (it would wait for every copy in flight before
+// each LDS read); the kernel orders them itself with explicit vmcnt waits and
+// barriers. m0 is reserved but unused by the compiler in these kernels; each
+// copy sets it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds)
 {
-    __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l_base, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// half would wait for every copy in flight). LDS reads are complete
+// (lgkmcnt(0)) before it; copies are covered by the explicit vmcnt waits.
+__device__ __forceinline__ void slot_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uni_ptr(T* p)
+{
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* p)
+{
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (both about
+// 1 ulp); the product is rounded to bf16 right after.
+__device__ __forceinline__ float fast_silu(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+// Fragment-read slots. A fragment set (one k-step) is 8 reads: A blocks
+// 0..3 and B blocks 0..3 (ids 0..3 and 4..7), issued in the order a0 b0 b1
+// b2 b3 a1 a2 a3 (the first MFMAs of a k-step need every B block). During
+// k-steps 0 and 1 a read follows MFMAs m % 4 != 3 (12 per k-step): k-step 0
+// reads set 1 and the first half of set 2, k-step 1 the rest of set 2 and
+// set 3. During k-steps 2 and 3 a read follows MFMAs m % 4 == 0 (set 0 of the
+// next stage, half each) and a copy follows every odd MFMA.
+__host__ __device__ constexpr int read_order(int n) { return n == 0 ? 0 : n <= 4 ? n + 3 : n - 4; }
+
+struct Unit {
+    int e, n0, rows, hrow0, KT, kofs, kpart;
+};
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
@@ -188,195 +255,241 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
     float* __restrict__ part)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sB1[kStageElems];
-    __shared__ int32_t rowmap[kTM];
+    __shared__ __attribute__((aligned(1024))) char slots[2 * kSlotBytes];
+    __shared__ int32_t rowmap[2][kTM];
     __shared__ int32_t ssched[2 * 257];  // tile_start[E+1], row_start[E+1]
 
     for (int i = threadIdx.x; i < 2 * (E + 1); i += kThreads) ssched[i] = sched[i];
     __syncthreads();
     const int K = MODE == kGateUp ? H : F;
     const int KT_all = K / kTK;
-    const int KT_half = (KT_all + ksplit - 1) / ksplit;
+    const int KT_part = (KT_all + ksplit - 1) / ksplit;
     const int total = ssched[E] * ntiles_n * ksplit;
     const int P = gridDim.x;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = uni(tid >> 6), lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int fl = lane & 31, fh = lane >> 5;
-    const int frag_off = fl * kRowElems + fh * 8;      // fragment row, K-chunk
+    const int fr = lane & 31, fh = lane >> 5;
+    const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
+    // fragment byte offsets inside an operand stage, k-steps 0..3
+    uint32_t fa[4], fb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t ch = (uint32_t)(((2 * kk + fh) ^ swz(fr)) * 16);
+        fa[kk] = (uint32_t)(wm * 128 + fr) * 128u + ch;
+        fb[kk] = (uint32_t)((MODE == kGateUp ? wn * 64 : wn * 128) + fr) * 128u + ch;
+    }
 
-    for (int base = 0;; base += P) {
-        const int Lu = base + my_slot;
-        if (Lu >= total) break;
-        // ---- decode the work unit: K-part (split-K), then the tile: expert,
-        // N-tile, M-tile
-        const int Lt = Lu / ksplit, kpart = Lu % ksplit;
-        const int KT = min(KT_all, (kpart + 1) * KT_half) - kpart * KT_half;
-        const int kofs = kpart * KT_half * kTK;
+    // work unit -> (K-part, expert, N-tile, M-tile); uniform
+    auto decode = [&](int Lu) {
+        Unit u;
+        const int Lt = Lu / ksplit;
+        u.kpart = Lu % ksplit;
+        u.KT = min(KT_all, (u.kpart + 1) * KT_part) - u.kpart * KT_part;
+        u.kofs = u.kpart * KT_part * kTK;
         int lo = 0, hi = E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (ssched[mid] * ntiles_n <= Lt) lo = mid;
             else hi = mid - 1;
         }
-        const int e = lo;
-        const int mt_e = ssched[e + 1] - ssched[e];
-        const int local = Lt - ssched[e] * ntiles_n;
+        const int mt_e = ssched[lo + 1] - ssched[lo];
+        const int local = Lt - ssched[lo] * ntiles_n;
         const int nt = local / mt_e, mt = local % mt_e;
-        const int c_e = ssched[E + 1 + e + 1] - ssched[E + 1 + e];
+        const int c_e = ssched[E + 1 + lo + 1] - ssched[E + 1 + lo];
         const int v0 = mt * kTM;
-        const int rows = min(kTM, c_e - v0);
-        const int hrow0 = ssched[E + 1 + e] + v0;
-        rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : 0)];
-        __syncthreads();
+        u.e = uni(lo);
+        u.n0 = uni(nt * (MODE == kGateUp ? kTN / 2 : kTN));
+        u.rows = uni(min(kTM, c_e - v0));
+        u.hrow0 = uni(ssched[E + 1 + lo] + v0);
+        u.KT = uni(u.KT);
+        u.kofs = uni(u.kofs);
+        u.kpart = uni(u.kpart);
+        return u;
+    };
 
-        // ---- DMA sources. Stage buffer = 256 rows x 9 slots; DMA instruction
-        // q (0..35) fills slots 64q .. 64q+63, lane l slot 64q + l, i.e. row
-        // (64q+l)/9, slot (64q+l)%9 (slot 8 is the pad: it gets the row's
-        // chunk 0, never read). Wave w issues instructions q = 4i + w. Each
-        // source is a wave-uniform base plus a fixed 32-bit lane offset.
-        const int n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
-        const char* abase = reinterpret_cast<const char*>(
-            (MODE == kGateUp ? a_src : a_src + (size_t)hrow0 * F) + kofs);
-        const char* bbase0 = reinterpret_cast<const char*>(
-            (MODE == kGateUp ? w0 + (size_t)e * F * H : w0 + (size_t)e * H * F) + kofs);
-        const char* bbase1 = MODE == kGateUp ? reinterpret_cast<const char*>(w1 + (size_t)e * F * H + kofs)
-                                             : bbase0;
-        uint32_t aoff[kDmaPerWave], boff[kDmaPerWave];
+    // per-unit copy sources: uniform bases + per-lane 32-bit offsets. Copy
+    // instruction q (0..31) of an operand fills slot rows 8q .. 8q+7; wave w
+    // issues q = w + 4 i; lane l takes row 8q + l/8, slot chunk l % 8.
+    const char *abase = nullptr, *bbase0 = nullptr, *bbase1 = nullptr;
+    uint32_t aoff[kCopiesWave], boff[kCopiesWave];
+    auto setup = [&](const Unit& u, const int32_t* rmap) {
+        if (MODE == kGateUp) {
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src + u.kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)u.e * F * H + u.kofs));
+            bbase1 = uni_ptr(reinterpret_cast<const char*>(w1 + (size_t)u.e * F * H + u.kofs));
+        } else {
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)u.hrow0 * F + u.kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)u.e * H * F + u.kofs));
+            bbase1 = bbase0;
+        }
 #pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i) {
-            const int slot = 64 * (4 * i + wave) + lane;
-            const int r = slot / kSlotsPerRow, c = slot % kSlotsPerRow;
-            const uint32_t chunk = (c < 8 ? c : 0) * 16;
+        for (int i = 0; i < kCopiesWave; ++i) {
+            const int r = 8 * (wave + 4 * i) + (lane >> 3);
+            const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
             if (MODE == kGateUp) {
-                aoff[i] = (uint32_t)rowmap[r] * (uint32_t)H * 2u + chunk;
-                const int f = min(n0 + (r & 127), F - 1);   // rows 0..127 gate, 128..255 up
-                boff[i] = (uint32_t)f * (uint32_t)H * 2u + chunk;
+                aoff[i] = (uint32_t)rmap[r] * (uint32_t)H * 2u + ch;
+                boff[i] = (uint32_t)min(u.n0 + (r & 127), F - 1) * (uint32_t)H * 2u + ch;
             } else {
-                aoff[i] = (uint32_t)min(r, rows - 1) * (uint32_t)F * 2u + chunk;
-                const int o = min(n0 + r, H - 1);
-                boff[i] = (uint32_t)o * (uint32_t)F * 2u + chunk;
+                aoff[i] = (uint32_t)min(r, u.rows - 1) * (uint32_t)F * 2u + ch;
+                boff[i] = (uint32_t)min(u.n0 + r, H - 1) * (uint32_t)F * 2u + ch;
             }
         }
-        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    };
+    // copies of stage st into slot st % 2 (gate/up: B instructions q < 16,
+    // i.e. i < 4, hold gate rows)
+    auto copy_a = [&](int st, int i) {
+        copy16(abase + st * (kTK * 2), aoff[i], slots_u + (st & 1) * kSlotBytes + wave * 1024 + i * 4096);
+    };
+    auto copy_b = [&](int st, int i) {
+        copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
+               slots_u + (st & 1) * kSlotBytes + kOpBytes + wave * 1024 + i * 4096);
+    };
+    auto prologue = [&](const Unit& u) {
+        for (int st = 0; st < 2 && st < u.KT; ++st) {
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i) copy_a(st, i);
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i) copy_b(st, i);
+        }
+    };
 
-        f32x16 acc[4][4];
+    f32x16 acc[4][4];
+    bf16x8 af[4][4], bf[4][4];
+    // fragment id (0..3 A block, 4..7 B block) of k-step kk of stage st
+    auto read = [&](int st, int kk, int id) {
+        const char* base = slots + (st & 1) * kSlotBytes;
+        if (id < 4) {
+            af[kk][id] = lds_frag(base + fa[kk] + id * 4096);
+        } else {
+            const int j = id - 4;
+            bf[kk][j] = lds_frag(base + kOpBytes + fb[kk] +
+                                 (MODE == kGateUp ? (j >> 1) * 16384 + (j & 1) * 4096 : j * 4096));
+        }
+    };
+    auto mfma = [&](int kk, int m) {
+        const int i = m >> 2, j = m & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kk][j], af[kk][i], acc[i][j], 0, 0, 0);
+    };
+
+    // k-steps 0 and 1 of stage s: MFMAs interleaved with the reads of sets
+    // 1, 2, 3; then the wait for this wave's copies of stage s+1 and the
+    // barrier. Reads: n-th read of k-step kk covers set-read index
+    // 12 kk + n over the sequence (set 1: 8 reads, set 2: 8, set 3: 8).
+    auto first_half = [&](int s) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            int n = 0;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                mfma(kk, m);
+                if ((m & 3) != 3) {
+                    const int idx = 12 * kk + n++;  // 0..23
+                    read(s, 1 + idx / 8, read_order(idx % 8));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vm_lgkm<0>();
+        slot_barrier();
+    };
+    // k-steps 2 and 3 of stage s: COPY refills the slot with stage s+2;
+    // NEXT reads set 0 of stage s+1.
+    auto second_half = [&](auto copy_tag, auto next_tag, int s) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+#pragma unroll
+        for (int kk = 2; kk < 4; ++kk) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                mfma(kk, m);
+                if (NEXT && (m & 3) == 0) read(s + 1, 0, read_order(4 * (kk - 2) + (m >> 2)));
+                if (COPY && (m & 1)) {
+                    if (kk == 2) copy_a(s + 2, m >> 1);
+                    else copy_b(s + 2, m >> 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+
+    int Lu = my_slot;
+    if (Lu >= total) return;
+    Unit u = decode(Lu);
+    int par = 0;
+    rowmap[0][tid] = vrow[u.hrow0 + (tid < u.rows ? tid : 0)];
+    __syncthreads();
+    setup(u, rowmap[0]);
+    prologue(u);
+
+    for (;;) {
+        // next unit and its rows (read now, used at the end of this unit)
+        const int Ln = Lu + P;
+        const bool has_next = Ln < total;
+        Unit un = u;
+        int nrow = 0;
+        if (has_next) {
+            un = decode(Ln);
+            nrow = vrow[un.hrow0 + (tid < un.rows ? tid : 0)];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        // stage 0 landed (stage 1's copies, if any, were issued after it)
+        if (u.KT >= 2) wait_vm_lgkm<2 * kCopiesWave>();
+        else wait_vm_lgkm<0>();
+        slot_barrier();
+#pragma unroll
+        for (int n = 0; n < 8; ++n) read(0, 0, read_order(n));
 
-        auto issue = [&](uint16_t* sA, uint16_t* sB, int k0) {
-            const char* ab = abase + (size_t)k0 * 2;
-            const char* b0 = bbase0 + (size_t)k0 * 2;
-            const char* b1 = bbase1 + (size_t)k0 * 2;
-#pragma unroll
-            for (int i = 0; i < kDmaPerWave; ++i) {
-                const int q = 4 * i + wave_u;
-                dma16(ab + aoff[i], sA + q * 512);
-                dma16((q < kGateDma ? b0 : b1) + boff[i], sB + q * 512);
-            }
-        };
-        auto frags = [&](const uint16_t* sA, const uint16_t* sB, int kk, bf16x8* af, bf16x8* bf) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = lds_frag(sA + frag_off + (wm * 128 + i * 32) * kRowElems + kk * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r0 = MODE == kGateUp ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32)
-                                               : (wn * 128 + j * 32);
-                bf[j] = lds_frag(sB + frag_off + r0 * kRowElems + kk * 16);
-            }
-        };
-        auto mfmas = [&](const bf16x8* af, const bf16x8* bf) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-        };
-
-        bf16x8 af[2][4], bf[2][4];
-        // One stage on buffer c while n holds the next one. REFILL: refill c
-        // with stage s_+2 right after the barrier that retires c's reads, its
-        // DMA instructions threaded between the last k-step's MFMAs (the caller
-        // guarantees s_+2 < KT). Otherwise no refill.
-        auto stage = [&](auto refill, uint16_t* cA, uint16_t* cB, uint16_t* nA, uint16_t* nB,
-                         int s_) {
-            constexpr bool REFILL = decltype(refill)::value;
-#pragma unroll
-            for (int kk = 0; kk < 3; ++kk) {
-                frags(cA, cB, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(af[kk & 1], bf[kk & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into n has landed
-            __syncthreads();                // all of n landed; everyone is done reading c
-            if (s_ + 1 < KT) frags(nA, nB, 0, af[0], bf[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (REFILL) issue(cA, cB, (s_ + 2) * kTK);
-            mfmas(af[1], bf[1]);
-            if (REFILL) {
-#pragma unroll
-                for (int g = 0; g < 16; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 DMA
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        using Refill = std::true_type;
-        using NoRefill = std::false_type;
-
-        issue(sA0, sB0, 0);
-        if (KT > 1) issue(sA1, sB1, kTK);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        frags(sA0, sB0, 0, af[0], bf[0]);
-        // Stages go in pairs (buffer 0, buffer 1). The refill of buffer 1 that
-        // the second stage of a pair owes is issued at the top of the next pair
-        // instead (the same barrier covers it), so no DMA is in flight across
-        // the loop back edge: the compiler then keeps tracking DMAs per buffer
-        // and never makes a read of one buffer wait for a refill of the other.
-        // The loop runs while the first stage of a pair has a stage to refill
-        // (kt + 2 < KT); at most two stages remain after it, neither refills.
-        int kt = 0;
-        for (; kt + 2 < KT; kt += 2) {
-            if (kt >= 2) issue(sA1, sB1, (kt + 1) * kTK);
-            stage(Refill{}, sA0, sB0, sA1, sB1, kt);
-            stage(NoRefill{}, sA1, sB1, sA0, sB0, kt + 1);
+        int s = 0;
+        for (; s + 2 < u.KT; ++s) {
+            first_half(s);
+            second_half(Yes{}, Yes{}, s);
         }
-        if (kt >= 2 && kt + 1 < KT) issue(sA1, sB1, (kt + 1) * kTK);
-        stage(NoRefill{}, sA0, sB0, sA1, sB1, kt);
-        if (kt + 1 < KT) stage(NoRefill{}, sA1, sB1, sA0, sB0, kt + 1);
+        if (s + 1 < u.KT) {
+            first_half(s);
+            second_half(No{}, Yes{}, s);
+            ++s;
+        }
+        // last stage: after its barrier both slots are free, so the next
+        // unit's first stages go out before this unit's last MFMAs
+        first_half(s);
+        if (has_next) {
+            rowmap[par ^ 1][tid] = nrow;
+            wait_vm_lgkm<63>();
+            slot_barrier();
+            setup(un, rowmap[par ^ 1]);
+            prologue(un);
+        }
+        second_half(No{}, No{}, s);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
         // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + i * 32 + fl;
-            if (row >= rows) continue;
+            const int row = wm * 128 + i * 32 + fr;
+            if (row >= u.rows) continue;
             if (MODE == kGateUp) {
-                uint16_t* dst = out + (size_t)(hrow0 + row) * F;
+                uint16_t* dst = out + (size_t)(u.hrow0 + row) * F;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = n0 + wn * 64 + j * 32 + g4 * 8 + fh * 4;
+                        const int col = u.n0 + wn * 64 + j * 32 + g4 * 8 + fh * 4;
                         if (col >= F) continue;
                         float hv[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            hv[q] = moe::silu(acc[i][j][g4 * 4 + q]) * acc[i][j + 2][g4 * 4 + q];
+                            hv[q] = fast_silu(acc[i][j][g4 * 4 + q]) * acc[i][j + 2][g4 * 4 + q];
                         uint2 pk;
                         pk.x = moe::pack_bf16x2(hv[0], hv[1]);
                         pk.y = moe::pack_bf16x2(hv[2], hv[3]);
@@ -384,24 +497,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                     }
             } else if (ksplit > 1) {
                 // fp32 partial sums, expert-sorted rows; summed by ksum_kernel
-                float* dst = part + ((size_t)kpart * N + hrow0 + row) * H;
+                float* dst = part + ((size_t)u.kpart * N + u.hrow0 + row) * H;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
+                        const int col = u.n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
                         if (col >= H) continue;
                         *reinterpret_cast<float4*>(dst + col) =
                             make_float4(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1],
                                         acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
                     }
             } else {
-                uint16_t* dst = out + (size_t)rowmap[row] * H;
+                uint16_t* dst = out + (size_t)rowmap[par][row] * H;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
+                        const int col = u.n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
                         if (col >= H) continue;
                         uint2 pk;
                         pk.x = moe::pack_bf16x2(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1]);
@@ -410,7 +523,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                     }
             }
         }
-        __syncthreads();
+        if (!has_next) break;
+        Lu = Ln;
+        u = un;
+        par ^= 1;
     }
 }
 

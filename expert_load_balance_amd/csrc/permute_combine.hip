@@ -55,6 +55,14 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(int T, int k, int E, 
     const int t = blockIdx.x;
     const int N = T * k;
     const moe::PlanLayout L = moe::plan_layout(E, R);
+    const uint4* src = x + (size_t)t * row_vecs;
+    // the row does not depend on the routing: start reading it first
+    uint4 v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = i * kThreads + threadIdx.x;
+        if (c < row_vecs) v[i] = src[c];
+    }
     if (threadIdx.x < k) {
         const int a = t * k + threadIdx.x;
         const int d = dest_of(ids[a], eidx[a], E, R, N, plan, L);
@@ -62,15 +70,15 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(int T, int k, int E, 
         dest_row[a] = d;
         if (d >= 0) row_src[d] = t;
     }
-    const uint4* src = x + (size_t)t * row_vecs;
+    __syncthreads();
     for (int base = 0; base < row_vecs; base += VPT * kThreads) {
-        uint4 v[VPT];
+        if (base > 0) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int c = base + i * kThreads + threadIdx.x;
-            if (c < row_vecs) v[i] = src[c];
+            for (int i = 0; i < VPT; ++i) {
+                const int c = base + i * kThreads + threadIdx.x;
+                if (c < row_vecs) v[i] = src[c];
+            }
         }
-        __syncthreads();
         for (int j = 0; j < k; ++j) {
             const int d = sdest[j];
             if (d < 0) continue;
