@@ -68,7 +68,7 @@ struct WsLayout {
     size_t blk_hist, blk_base;  // count: int32[B][E] each
     size_t sched;               // gemm: int32 schedule (see gemm.hip)
     size_t vrow;                // gemm: int32[N] expert-sorted row -> buf row
-    size_t part;                // gemm down, split-K: float[2][N][H] partial sums (or empty)
+    size_t part;                // gemm bf16: float[units][256][256] partial tiles (K-split leftovers)
     size_t h;                   // gemm: dtype[N][F] SwiGLU activations
     size_t stats;               // stats: int64[kStatsSlots(R)]
     size_t total;
@@ -77,15 +77,26 @@ struct WsLayout {
 
 constexpr int kCountChunk = 1024;  // assignments per counting workgroup
 
-// The bf16 down GEMM splits K in two when its 256 x 256 tiles would not fill
-// two rounds of 256 CUs (upper bound of tiles: (N/256 + E) M-tiles per
-// 256-column N-tile); the two halves meet in fp32 partial buffers.
-inline int down_ksplit(const moe_shape_t& s)
+// bf16 grouped GEMM geometry shared by the workspace layout and the kernels:
+// 256 x 256 tiles, K in 64-deep stages, at most kGemmMaxGrid persistent
+// workgroups. Tiles left over after the last full round of workgroups are
+// split along K; each part writes a fp32 256 x 256 partial tile.
+constexpr int kGemmTile = 256;
+constexpr int kGemmStageK = 64;
+constexpr int kGemmMaxGrid = 256;
+
+// Upper bound on the partial tiles one bf16 GEMM launch can write: at most
+// one per workgroup, and at most (M-tiles x N-tiles) x stages.
+inline int64_t gemm_part_units(const moe_shape_t& s)
 {
-    if (s.dtype != MOE_BF16) return 1;
+    if (s.dtype != MOE_BF16) return 0;
     const int64_t N = (int64_t)s.T * s.k;
-    const int64_t tiles = ((N + 255) / 256 + s.E) * ((s.H + 255) / 256);
-    return (tiles < 2 * 256 && (s.F / 64) >= 2) ? 2 : 1;
+    if (N == 0) return 0;
+    const int64_t mt = N / kGemmTile + s.E;
+    const int64_t gu = mt * ((s.F + kGemmTile / 2 - 1) / (kGemmTile / 2)) * (s.H / kGemmStageK);
+    const int64_t dn = mt * ((s.H + kGemmTile - 1) / kGemmTile) * (s.F / kGemmStageK);
+    const int64_t u = gu > dn ? gu : dn;
+    return u < kGemmMaxGrid ? u : kGemmMaxGrid;
 }
 
 // Statistics reduction slots (int64): fixed scalars, then three R-vectors.
@@ -109,7 +120,7 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     w.blk_base = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
     w.sched = o;     o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
     w.vrow = o;      o = align256(o + (size_t)(N > 0 ? N : 1) * 4);
-    w.part = o;      o = align256(o + (down_ksplit(s) > 1 ? (size_t)2 * N * s.H * 4 : 0));
+    w.part = o;      o = align256(o + (size_t)gemm_part_units(s) * kGemmTile * kGemmTile * 4);
     w.h = o;         o = align256(o + (size_t)N * s.F * (s.dtype == MOE_BF16 ? 2 : 4));
     w.stats = o;     o = align256(o + (size_t)stats_slots(s.R) * 8);
     w.total = o;

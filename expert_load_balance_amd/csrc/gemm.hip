@@ -164,9 +164,15 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 //  * Tile order: expert, N-tile, M-tile (M fastest), so the M-tiles sharing
 //    a weight tile run together; each XCD takes a contiguous run of tiles so
 //    they share its L2.
+//  * Balance: workgroup p takes work units p, p + P, ... Whole tiles fill as
+//    many full rounds of the P workgroups as they can; the tiles left over
+//    (fewer than P) are split along K into as many parts as the idle
+//    workgroups allow, each part writing a fp32 partial tile that
+//    fixup_kernel sums (parts in order) and finishes. No workgroup waits on
+//    another.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kTM = moe::kGemmTile, kTN = moe::kGemmTile, kTK = moe::kGemmStageK;
 constexpr int kOpBytes = kTM * kTK * 2;           // 32 KB: one operand of one stage
 constexpr int kSlotBytes = 2 * kOpBytes;          // A, then B
 constexpr int kCopiesWave = kOpBytes / 1024 / 4;  // 8 copies per operand per wave
@@ -244,13 +250,66 @@ __device__ __forceinline__ float fast_silu(float z)
 // next stage, half each) and a copy follows every odd MFMA.
 __host__ __device__ constexpr int read_order(int n) { return n == 0 ? 0 : n <= 4 ? n + 3 : n - 4; }
 
+// Tile t of the launch (expert-major, then N-tile, then M-tile) from the
+// schedule (tile_start[E+1], row_start[E+1]).
+struct TileRef {
+    int e, n0, rows, hrow0;
+};
+template <int MODE>
+__device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, const int32_t* sc)
+{
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sc[mid] * ntiles_n <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int mt_e = sc[lo + 1] - sc[lo];
+    const int local = t - sc[lo] * ntiles_n;
+    const int nt = local / mt_e, mt = local % mt_e;
+    const int c_e = sc[E + 1 + lo + 1] - sc[E + 1 + lo];
+    const int v0 = mt * kTM;
+    TileRef r;
+    r.e = lo;
+    r.n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
+    r.rows = min(kTM, c_e - v0);
+    r.hrow0 = sc[E + 1 + lo] + v0;
+    return r;
+}
+
+// Work split of `tiles` tiles over P workgroups: `full` whole-tile units,
+// then L leftover tiles in S K-parts of KTp stages (S == 1: no split).
+struct Balance {
+    int full, L, S, KTp;
+};
+__device__ __forceinline__ Balance balance_of(int tiles, int P, int KT_all)
+{
+    Balance b;
+    b.full = tiles / P * P;
+    b.L = tiles - b.full;
+    b.S = 1;
+    b.KTp = KT_all;
+    if (b.L > 0) {
+        const int s0 = min(P / b.L, KT_all);
+        if (s0 > 1) {
+            b.KTp = (KT_all + s0 - 1) / s0;
+            b.S = (KT_all + b.KTp - 1) / b.KTp;  // every part non-empty
+        }
+    }
+    if (b.S == 1) {
+        b.full = tiles;
+        b.L = 0;
+    }
+    return b;
+}
+
 struct Unit {
-    int e, n0, rows, hrow0, KT, kofs, kpart;
+    int e, n0, rows, hrow0, KT, kofs, pidx;  // pidx: partial-tile slot, -1 for a whole tile
 };
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
-    int E, int ntiles_n, int H, int F, int ksplit, int N, const uint16_t* __restrict__ a_src,
+    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
     float* __restrict__ part)
@@ -263,9 +322,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     __syncthreads();
     const int K = MODE == kGateUp ? H : F;
     const int KT_all = K / kTK;
-    const int KT_part = (KT_all + ksplit - 1) / ksplit;
-    const int total = ssched[E] * ntiles_n * ksplit;
     const int P = gridDim.x;
+    const Balance bal = balance_of(ssched[E] * ntiles_n, P, KT_all);
+    const int total = bal.full + bal.L * bal.S;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
@@ -283,31 +342,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         fb[kk] = (uint32_t)((MODE == kGateUp ? wn * 64 : wn * 128) + fr) * 128u + ch;
     }
 
-    // work unit -> (K-part, expert, N-tile, M-tile); uniform
+    // work unit -> (tile, K range, partial slot); uniform. Partial units go
+    // part-major so that neighbouring workgroups share weight tiles.
     auto decode = [&](int Lu) {
-        Unit u;
-        const int Lt = Lu / ksplit;
-        u.kpart = Lu % ksplit;
-        u.KT = min(KT_all, (u.kpart + 1) * KT_part) - u.kpart * KT_part;
-        u.kofs = u.kpart * KT_part * kTK;
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (ssched[mid] * ntiles_n <= Lt) lo = mid;
-            else hi = mid - 1;
+        int t = Lu, k0 = 0, KT = KT_all, pidx = -1;
+        if (Lu >= bal.full) {
+            pidx = Lu - bal.full;
+            const int kp = pidx / bal.L;
+            t = bal.full + pidx % bal.L;
+            k0 = kp * bal.KTp;
+            KT = min(KT_all - k0, bal.KTp);
         }
-        const int mt_e = ssched[lo + 1] - ssched[lo];
-        const int local = Lt - ssched[lo] * ntiles_n;
-        const int nt = local / mt_e, mt = local % mt_e;
-        const int c_e = ssched[E + 1 + lo + 1] - ssched[E + 1 + lo];
-        const int v0 = mt * kTM;
-        u.e = uni(lo);
-        u.n0 = uni(nt * (MODE == kGateUp ? kTN / 2 : kTN));
-        u.rows = uni(min(kTM, c_e - v0));
-        u.hrow0 = uni(ssched[E + 1 + lo] + v0);
-        u.KT = uni(u.KT);
-        u.kofs = uni(u.kofs);
-        u.kpart = uni(u.kpart);
+        const TileRef r = tile_of<MODE>(t, E, ntiles_n, ssched);
+        Unit u;
+        u.e = uni(r.e);
+        u.n0 = uni(r.n0);
+        u.rows = uni(r.rows);
+        u.hrow0 = uni(r.hrow0);
+        u.KT = uni(KT);
+        u.kofs = uni(k0 * kTK);
+        u.pidx = uni(pidx);
         return u;
     };
 
@@ -478,7 +532,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         for (int i = 0; i < 4; ++i) {
             const int row = wm * 128 + i * 32 + fr;
             if (row >= u.rows) continue;
-            if (MODE == kGateUp) {
+            if (u.pidx >= 0) {
+                // fp32 partial tile [row][B-row], summed by fixup_kernel
+                float* dst = part + ((size_t)u.pidx * kTM + row) * kTN;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int bc = (MODE == kGateUp ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32
+                                                        : wn * 128 + j * 32) + g4 * 8 + fh * 4;
+                        *reinterpret_cast<float4*>(dst + bc) =
+                            make_float4(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1],
+                                        acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
+                    }
+            } else if (MODE == kGateUp) {
                 uint16_t* dst = out + (size_t)(u.hrow0 + row) * F;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
@@ -494,19 +561,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                         pk.x = moe::pack_bf16x2(hv[0], hv[1]);
                         pk.y = moe::pack_bf16x2(hv[2], hv[3]);
                         *reinterpret_cast<uint2*>(dst + col) = pk;
-                    }
-            } else if (ksplit > 1) {
-                // fp32 partial sums, expert-sorted rows; summed by ksum_kernel
-                float* dst = part + ((size_t)u.kpart * N + u.hrow0 + row) * H;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = u.n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
-                        if (col >= H) continue;
-                        *reinterpret_cast<float4*>(dst + col) =
-                            make_float4(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1],
-                                        acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
                     }
             } else {
                 uint16_t* dst = out + (size_t)rowmap[par][row] * H;
@@ -530,26 +584,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     }
 }
 
-// Split-K epilogue of the down GEMM: y[vrow[g]] = bf16(part0[g] + part1[g]),
-// 8 columns per thread. Two partials, so the sum is independent of order.
-__global__ __launch_bounds__(kThreads) void ksum_kernel(int N, int H, const float* __restrict__ part,
-                                                        const int32_t* __restrict__ vrow,
-                                                        uint16_t* __restrict__ y)
+// Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
+// partial tiles of each leftover tile in part order and writes the result
+// the whole-tile epilogue would have written (gate/up: bf16 silu(g) * u into
+// h; down: bf16 y rows at their buffer rows). Grid-stride over (tile, row,
+// 4-column group).
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, int H, int F, int P,
+                                                         const int32_t* __restrict__ sched,
+                                                         const int32_t* __restrict__ vrow,
+                                                         const float* __restrict__ part,
+                                                         uint16_t* __restrict__ out)
 {
-    const int per_row = H / 8;
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= (int64_t)N * per_row) return;
-    const int g = (int)(i / per_row), c = (int)(i % per_row) * 8;
-    const float* p0 = part + (size_t)g * H + c;
-    const float* p1 = p0 + (size_t)N * H;
-    const float4 a0 = *reinterpret_cast<const float4*>(p0), a1 = *reinterpret_cast<const float4*>(p0 + 4);
-    const float4 b0 = *reinterpret_cast<const float4*>(p1), b1 = *reinterpret_cast<const float4*>(p1 + 4);
-    uint4 o;
-    o.x = moe::pack_bf16x2(a0.x + b0.x, a0.y + b0.y);
-    o.y = moe::pack_bf16x2(a0.z + b0.z, a0.w + b0.w);
-    o.z = moe::pack_bf16x2(a1.x + b1.x, a1.y + b1.y);
-    o.w = moe::pack_bf16x2(a1.z + b1.z, a1.w + b1.w);
-    *reinterpret_cast<uint4*>(y + (size_t)vrow[g] * H + c) = o;
+    const int KT_all = (MODE == kGateUp ? H : F) / kTK;
+    const Balance bal = balance_of(sched[E] * ntiles_n, P, KT_all);
+    if (bal.S == 1) return;
+    constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
+    const int64_t items = (int64_t)bal.L * kTM * kQuads;
+    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < items;
+         w += (int64_t)gridDim.x * kThreads) {
+        const int c = (int)(w % kQuads) * 4;
+        const int row = (int)((w / kQuads) % kTM);
+        const int lt = (int)(w / ((int64_t)kQuads * kTM));
+        const TileRef r = tile_of<MODE>(bal.full + lt, E, ntiles_n, sched);
+        if (row >= r.rows) continue;
+        if (MODE == kGateUp) {
+            if (r.n0 + c >= F) continue;
+            float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+            for (int p = 0; p < bal.S; ++p) {
+                const float* src = part + ((size_t)(p * bal.L + lt) * kTM + row) * kTN + c;
+                const float4 a = *reinterpret_cast<const float4*>(src);
+                const float4 b = *reinterpret_cast<const float4*>(src + kTN / 2);
+                g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+                u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+            }
+            uint2 pk;
+            pk.x = moe::pack_bf16x2(fast_silu(g.x) * u.x, fast_silu(g.y) * u.y);
+            pk.y = moe::pack_bf16x2(fast_silu(g.z) * u.z, fast_silu(g.w) * u.w);
+            *reinterpret_cast<uint2*>(out + (size_t)(r.hrow0 + row) * F + r.n0 + c) = pk;
+        } else {
+            if (r.n0 + c >= H) continue;
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int p = 0; p < bal.S; ++p) {
+                const float4 a = *reinterpret_cast<const float4*>(
+                    part + ((size_t)(p * bal.L + lt) * kTM + row) * kTN + c);
+                y.x += a.x; y.y += a.y; y.z += a.z; y.w += a.w;
+            }
+            uint2 pk;
+            pk.x = moe::pack_bf16x2(y.x, y.y);
+            pk.y = moe::pack_bf16x2(y.z, y.w);
+            *reinterpret_cast<uint2*>(out + (size_t)vrow[r.hrow0 + row] * H + r.n0 + c) = pk;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -653,7 +739,8 @@ __global__ __launch_bounds__(kThreads) void down_f32_kernel(
 }
 
 // Workgroups of the persistent bf16 kernels: one per CU, a multiple of 8 so
-// that every XCD gets the same number.
+// that every XCD gets the same number, at most kGemmMaxGrid (the partial-tile
+// workspace is sized for that many).
 int persistent_grid()
 {
     static int grid = 0;
@@ -661,11 +748,14 @@ int persistent_grid()
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
+            cus = moe::kGemmMaxGrid;
         grid = cus >= 8 ? (cus / 8) * 8 : 8;
+        if (grid > moe::kGemmMaxGrid) grid = moe::kGemmMaxGrid;
     }
     return grid;
 }
+
+constexpr int kFixupGrid = 512;
 
 int max_mtiles(const moe_shape_t& s, int bm)
 {
@@ -699,10 +789,17 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
     const int32_t* sched = reinterpret_cast<const int32_t*>(ws + W.sched);
     if (s.dtype == MOE_BF16) {
         const int ntn = (s.F + kTN / 2 - 1) / (kTN / 2);
-        gemm_bf16_kernel<kGateUp><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, 1, s.T * s.k, static_cast<const uint16_t*>(a), sched,
-            reinterpret_cast<const int32_t*>(ws + W.vrow), static_cast<const uint16_t*>(w_gate),
-            static_cast<const uint16_t*>(w_up), reinterpret_cast<uint16_t*>(ws + W.h), nullptr);
+        const int P = persistent_grid();
+        const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
+        float* part = reinterpret_cast<float*>(ws + W.part);
+        uint16_t* h = reinterpret_cast<uint16_t*>(ws + W.h);
+        gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
+            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        fixup_kernel<kGateUp><<<kFixupGrid, kThreads, 0, st>>>(s.E, ntn, s.H, s.F, P, sched, vrow,
+                                                                part, h);
     } else {
         const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.F + kFM - 1) / kFM;
@@ -723,19 +820,16 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
     const bool bf = s.dtype == MOE_BF16;
     if (bf) {
         const int ntn = (s.H + kTN - 1) / kTN;
-        const int ks = moe::down_ksplit(s);
+        const int P = persistent_grid();
         const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
         float* part = reinterpret_cast<float*>(ws + W.part);
-        gemm_bf16_kernel<kDown><<<persistent_grid(), kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, ks, s.T * s.k, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
+        gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
             static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y), part);
-        if (ks > 1) {
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            const int64_t n = (int64_t)s.T * s.k * (s.H / 8);
-            ksum_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(
-                s.T * s.k, s.H, part, vrow, static_cast<uint16_t*>(y));
-        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        fixup_kernel<kDown><<<kFixupGrid, kThreads, 0, st>>>(s.E, ntn, s.H, s.F, P, sched, vrow, part,
+                                                              static_cast<uint16_t*>(y));
     } else {
         const int mtiles = max_mtiles(s, kFM);
         const int nt = (s.H + kFM - 1) / kFM;
