@@ -20,6 +20,10 @@ moe_status_t check(const moe_shape_t* s)
     if (N * wide >= (int64_t(1) << 40)) return MOE_EINVAL;
     if (s->dtype == MOE_BF16) {
         if (s->H % 64 || s->F % 64) return MOE_EUNSUPPORTED;
+        // the GEMM addresses rows of the buffer and of one expert's weights
+        // with 32-bit byte offsets
+        if (N * s->H * 2 >= (int64_t(1) << 32) || (int64_t)s->F * s->H * 2 >= (int64_t(1) << 32))
+            return MOE_EUNSUPPORTED;
     } else if (s->dtype == MOE_F32) {
         if (s->H % 4 || s->F % 4) return MOE_EUNSUPPORTED;
     } else {
