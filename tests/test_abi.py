@@ -45,6 +45,11 @@ def test_shape_validation(lib):
     assert moe.moe_check_shape(good.replace(dtype=moe.MOE_BF16, F=96)) == 2
     assert moe.moe_check_shape(good.replace(T=1 << 28, k=8)) == 1  # N >= 2^31
     assert moe.moe_check_shape(good.replace(T=0)) == 0
+    # bf16 GEMM copy offsets are 32-bit: buffer (N x H) and one expert's weights (F x H)
+    bf = good.replace(dtype=moe.MOE_BF16, H=8192, F=1024, E=8, R=4, k=8)
+    assert moe.moe_check_shape(bf.replace(T=32767)) == 0           # N*H*2 just below 2^32
+    assert moe.moe_check_shape(bf.replace(T=32768)) == 2           # N*H*2 == 2^32
+    assert moe.moe_check_shape(bf.replace(T=16, F=262144)) == 2     # F*H*2 >= 2^32
 
 
 def test_plan_layout_and_workspace(lib):
