@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--maxvio", type=float, default=None,
                     help="router skew target (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the other workloads / skews reported beside the headline")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,33 +102,34 @@ def cpu_baseline(name, maxvio, lg, bias, x, wts, ntok):
                        f"single-threaded C in double, {dt:.1f} s")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this layer is described, not built.", file=sys.stderr)
-        sys.exit(2)
-
+def time_back_to_back(fn, reps=50):
+    """Mean duration of one call when `reps` calls run back to back on the
+    current stream (launch gaps amortised), in seconds."""
     import torch
 
-    if args.copy_calibration:
-        a = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_per_launch": 2 * a.numel() * a.element_size()}))
-        return
+    for _ in range(5):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / reps
+
+
+def run_workload(name, maxvio, steps, warmup):
+    """Builds one workload on the GPU, runs `warmup` + `steps` layer steps and
+    returns its measurements (plus the inputs, for the CPU baseline)."""
+    import torch
 
     import expert_load_balance_amd as moe
     from expert_load_balance_amd.layer import STAGES, MoeLayerBuffers
     import synth
     from synth import workloads as wl
 
-    moe.load()
-    name = args.workload
     w = wl.WORKLOADS[name]
-    maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
     dtype = moe.MOE_BF16 if w["dtype"] == "bf16" else moe.MOE_F32
     act = torch.bfloat16 if dtype == moe.MOE_BF16 else torch.float32
     T, H, E, k, F, R, S = (w[c] for c in ("T", "H", "E", "k", "F", "R", "S"))
@@ -149,16 +152,16 @@ def main():
     L = MoeLayerBuffers(shape, dev, shared_F=shared_F)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
     torch.cuda.synchronize()
     print(f"[bench] {name}@{maxvio:g} warm-up done", file=sys.stderr, flush=True)
 
     marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for s in STAGES} for _ in range(args.steps)]
+              for s in STAGES} for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -170,31 +173,88 @@ def main():
         v = sorted(m[s][0].elapsed_time(m[s][1]) for m in marks)
         stage_ms[s] = dict(mean=sum(v) / len(v), p10=v[len(v) // 10], p90=v[(len(v) * 9) // 10])
 
-    st, loads = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
-                              err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
+    # the two row moves alone, back to back (their in-layer stage times also
+    # hold a launch gap each)
+    t_perm = time_back_to_back(lambda: moe.moe_permute(shape, x, L.ids, L.eidx, L.plan, L.buf,
+                                                       L.dest_row, L.row_src, stream=stream))
+    sy = L.shared_y if shared else None
+    t_comb = time_back_to_back(lambda: moe.moe_combine(shape, L.y, L.dest_row, L.w, sy, L.out,
+                                                       stream=stream))
+
+    st, _ = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
+                          err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
     N = T * k
     b = 2 if dtype == moe.MOE_BF16 else 4
     gu_s = stage_ms["gemm_gateup"]["mean"] * 1e-3
     dn_s = stage_ms["gemm_down"]["mean"] * 1e-3
     gu_flops = 4.0 * N * H * F
     dn_flops = 2.0 * N * H * F
-    achieved = gu_flops / gu_s / 1e12
     perm_bytes = (T + N) * H * b
     comb_bytes = (N + T) * H * b + (T * H * b if shared else 0)
-    ms = elapsed * 1e3 / args.steps
+    res = dict(
+        name=name, maxvio=maxvio, shape=(T, H, E, k, F, R, S), shared_F=shared_F, dtype=dtype,
+        tokens_per_s=T * steps / elapsed, ms_per_step=elapsed * 1e3 / steps, stage_ms=stage_ms,
+        gu_flops=gu_flops, gu_tflops=gu_flops / gu_s / 1e12, dn_tflops=dn_flops / dn_s / 1e12,
+        gemm_mfma_frac=(gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / PEAK_BF16_TFLOPS,
+        permute_us=t_perm * 1e6, combine_us=t_comb * 1e6,
+        permute_hbm_frac=perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS,
+        combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
+        permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        stats=st, inputs=(lg_np, bias_np, x, wts))
+    return res
+
+
+# Other workloads and skews reported beside the headline line (layer tokens/s,
+# grouped-GEMM MFMA fraction, permute / combine HBM fractions); decode at the
+# feasible maximum skew (15) for the maxvio-20 request.
+SWEEP = (("a3b", 0.0), ("a3b", 0.2), ("a3b", 1.0), ("dsv3", 20.0), ("dsv3", 0.0),
+         ("decode64", 1.0), ("decode256", 20.0), ("decode1024", 1.0), ("decode1024", 20.0))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this layer is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": 2 * a.numel() * a.element_size()}))
+        return
+
+    import expert_load_balance_amd as moe
+    from synth import workloads as wl
+
+    moe.load()
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
+    r = run_workload(name, maxvio, args.steps, args.warmup)
+    T, H, E, k, F, R, S = r["shape"]
+    shared_F = r["shared_F"]
+    st = r["stats"]
     traffic = traffic_for(name, maxvio)
+    achieved = r["gu_tflops"]
     rec = {
         "metric": METRIC,
-        "value": T * args.steps / elapsed,
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dtype == moe.MOE_BF16 else "f32",
+        "dtype": "bf16" if r["dtype"] == moe.MOE_BF16 else "f32",
         "data": "synthetic (seeded N(0,1) router logits + Zipf expert bias, N(0,1) activations, "
                 "N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": f"{name} T={T} H={H} E={E} k={k} F={F} R={R} S={S}"
@@ -203,13 +263,17 @@ def main():
                    "global_batch": T, "parallelism": "1 GPU, R virtual ranks"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "gateup_bf16_kernel",
-                     "flops_per_launch": gu_flops},
-        "stages_ms": {s: round(v["mean"], 4) for s, v in stage_ms.items()},
-        "gemm_down_tflops": dn_flops / dn_s / 1e12,
-        "grouped_gemm_mfma_frac": (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / PEAK_BF16_TFLOPS,
-        "permute_hbm_frac": perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "combine_hbm_frac": comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": traffic, "kernel": "gemm_bf16_kernel<0> (gate/up call)",
+                     "flops_per_launch": r["gu_flops"]},
+        "stages_ms": {s: round(v["mean"], 4) for s, v in r["stage_ms"].items()},
+        "gemm_down_tflops": r["dn_tflops"],
+        "grouped_gemm_mfma_frac": r["gemm_mfma_frac"],
+        "permute_hbm_frac": r["permute_hbm_frac"],
+        "combine_hbm_frac": r["combine_hbm_frac"],
+        "permute_us": r["permute_us"],
+        "combine_us": r["combine_us"],
+        "permute_hbm_frac_in_layer": r["permute_hbm_frac_in_layer"],
+        "combine_hbm_frac_in_layer": r["combine_hbm_frac_in_layer"],
         "plan": {"planned_max": st["planned_max"], "planned_min": st["planned_min"],
                  "replica_pieces": st["replica_pieces"], "max_slots_needed": st["max_slots_needed"],
                  "ranks_over_slots": st["ranks_over_slots"]},
@@ -217,7 +281,25 @@ def main():
     if not args.no_cpu_baseline:
         # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
         ntok = args.cpu_tokens or max(1, min(T, int(5e10 / (k * 3 * H * F))))
+        lg_np, bias_np, x, wts = r["inputs"]
         rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, ntok)
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        sweep = {}
+        for sname, smv in SWEEP:
+            q = run_workload(sname, smv, 10, 3)
+            sweep[f"{sname}@{smv:g}"] = {
+                "tokens_per_s": round(q["tokens_per_s"]), "ms_per_step": round(q["ms_per_step"], 4),
+                "maxvio_realised": round(q["stats"]["maxvio_expert"], 4),
+                "grouped_gemm_mfma_frac": round(q["gemm_mfma_frac"], 4),
+                "gemm_gateup_tflops": round(q["gu_tflops"], 1),
+                "gemm_down_tflops": round(q["dn_tflops"], 1),
+                "permute_hbm_frac": round(q["permute_hbm_frac"], 4),
+                "combine_hbm_frac": round(q["combine_hbm_frac"], 4)}
+            del q
+            torch.cuda.empty_cache()
+        rec["sweep"] = sweep
     print(json.dumps(rec), flush=True)
 
 
