@@ -587,8 +587,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
 // partial tiles of each leftover tile in part order and writes the result
 // the whole-tile epilogue would have written (gate/up: bf16 silu(g) * u into
-// h; down: bf16 y rows at their buffer rows). Grid-stride over (tile, row,
-// 4-column group).
+// h; down: bf16 y rows at their buffer rows). Workgroup b takes leftover
+// tile b / 16, rows 16 (b % 16) .. +15; a thread owns one 4-column group.
+constexpr int kFixupRows = 16;
+constexpr int kFixupSlabs = kTM / kFixupRows;
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, int H, int F, int P,
                                                          const int32_t* __restrict__ sched,
@@ -598,19 +601,20 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, in
 {
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
     const Balance bal = balance_of(sched[E] * ntiles_n, P, KT_all);
-    if (bal.S == 1) return;
+    const int lt = blockIdx.x / kFixupSlabs;
+    if (bal.S == 1 || lt >= bal.L) return;
+    const TileRef r = tile_of<MODE>(bal.full + lt, E, ntiles_n, sched);
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
-    const int64_t items = (int64_t)bal.L * kTM * kQuads;
-    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < items;
-         w += (int64_t)gridDim.x * kThreads) {
-        const int c = (int)(w % kQuads) * 4;
-        const int row = (int)((w / kQuads) % kTM);
-        const int lt = (int)(w / ((int64_t)kQuads * kTM));
-        const TileRef r = tile_of<MODE>(bal.full + lt, E, ntiles_n, sched);
-        if (row >= r.rows) continue;
+    constexpr int kRowsPerPass = kThreads / kQuads;
+    const int c = (threadIdx.x % kQuads) * 4;
+    const int row0 = (int)(blockIdx.x % kFixupSlabs) * kFixupRows;
+    const int row_end = min(r.rows, row0 + kFixupRows);
+    for (int row = row0 + threadIdx.x / kQuads; row < row_end;
+         row += kRowsPerPass) {
         if (MODE == kGateUp) {
             if (r.n0 + c >= F) continue;
             float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+#pragma unroll 4
             for (int p = 0; p < bal.S; ++p) {
                 const float* src = part + ((size_t)(p * bal.L + lt) * kTM + row) * kTN + c;
                 const float4 a = *reinterpret_cast<const float4*>(src);
@@ -625,6 +629,7 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, in
         } else {
             if (r.n0 + c >= H) continue;
             float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
             for (int p = 0; p < bal.S; ++p) {
                 const float4 a = *reinterpret_cast<const float4*>(
                     part + ((size_t)(p * bal.L + lt) * kTM + row) * kTN + c);
@@ -755,7 +760,8 @@ int persistent_grid()
     return grid;
 }
 
-constexpr int kFixupGrid = 512;
+// split leftover tiles: at most half the persistent grid (each gets >= 2 parts)
+constexpr int kFixupGrid = moe::kGemmMaxGrid / 2 * kFixupSlabs;
 
 int max_mtiles(const moe_shape_t& s, int bm)
 {
