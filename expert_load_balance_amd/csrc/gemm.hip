@@ -31,13 +31,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 // schedule layout inside the workspace region (int32):
-//   [0 .. E]        tile_start (prefix of ceil(c_e / BM))
-//   [E+1 .. 2E+1]   row_start  (prefix of c_e)
-__global__ __launch_bounds__(kThreads) void schedule_kernel(int E, int R, int bm,
+//   [0 .. E]            tile_start: prefix of the expert's M-tiles of bm rows
+//   [E+1 .. 2E+1]       row_start:  prefix of c_e
+//   [2E+2 .. 3E+2]      prefix of (0 < c_e <= sk1): one sk1-row tile each
+//   [3E+3 .. 4E+3]      prefix of (sk1 < c_e <= sk2): one sk2-row tile each
+// Experts with a skinny tile get no M-tile (sk1 = sk2 = 0: every expert is
+// cut into M-tiles).
+__global__ __launch_bounds__(kThreads) void schedule_kernel(int E, int R, int bm, int sk1, int sk2,
                                                             const int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ sched)
 {
-    __shared__ int32_t st[256], sr[256];
+    __shared__ int32_t st[256], sr[256], ss[256], s2[256];
     const moe::PlanLayout L = moe::plan_layout(E, R);
     const int e = threadIdx.x;
     int c = 0;
@@ -45,24 +49,36 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(int E, int R, int bm
         const int np = plan[L.piece_num + e];
         for (int p = 0; p < np && p < R; ++p) c += plan[L.piece_cnt + (size_t)e * R + p];
     }
-    st[e] = (c + bm - 1) / bm;
+    const bool t1 = c > 0 && c <= sk1;
+    const bool t2 = c > sk1 && c <= sk2;
+    st[e] = (t1 || t2) ? 0 : (c + bm - 1) / bm;
     sr[e] = c;
+    ss[e] = t1 ? 1 : 0;
+    s2[e] = t2 ? 1 : 0;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
         const int a = e >= off ? st[e - off] : 0;
         const int b = e >= off ? sr[e - off] : 0;
+        const int d = e >= off ? ss[e - off] : 0;
+        const int f = e >= off ? s2[e - off] : 0;
         __syncthreads();
         st[e] += a;
         sr[e] += b;
+        ss[e] += d;
+        s2[e] += f;
         __syncthreads();
     }
     if (e < E) {
         sched[e + 1] = st[e];
         sched[E + 1 + e + 1] = sr[e];
+        sched[2 * (E + 1) + e + 1] = ss[e];
+        sched[3 * (E + 1) + e + 1] = s2[e];
     }
     if (e == 0) {
         sched[0] = 0;
         sched[E + 1] = 0;
+        sched[2 * (E + 1)] = 0;
+        sched[3 * (E + 1)] = 0;
     }
 }
 
@@ -584,6 +600,189 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     }
 }
 
+// ------------------------------------------------------- bf16, skinny ----
+// Experts with at most 64 rows (decode-like batches, cold experts under
+// skew) get one SKM-row tile per N-tile (SKM = 32 or 64) instead of a mostly
+// empty 256-row M-tile. Such a tile is bound by streaming the expert's
+// weights, so its LDS stage holds only SKM rows of activations next to the
+// 32 KB weight tile and the ring is deeper: 4 stages for SKM = 32 (three
+// stages of weight copies in flight per CU), 3 for SKM = 64. Same N-tiles,
+// K stages, swizzle, copy wrapper and epilogues as the 256-row kernel; 4
+// waves, each SKM rows x 64 B-rows (gate/up: 32 gate and the same 32 up
+// columns).
+template <int SKM>
+struct Skinny {
+    static constexpr int kSlots = SKM == 32 ? 4 : 3;
+    static constexpr int kA = SKM * kTK * 2;                  // 4 or 8 KB of A per stage
+    static constexpr int kSlot = kA + kOpBytes;               // 36 or 40 KB per stage
+    static constexpr int kACopies = SKM / 32;                 // A copies per wave per stage
+    static constexpr int kPerStage = kACopies + kCopiesWave;  // copies per wave per stage
+    static constexpr int kBlocks = SKM / 32;                  // 32-row blocks per wave
+    static constexpr int kSchedOff = SKM == 32 ? 2 : 3;       // tile_start prefix (x (E+1))
+};
+
+template <int MODE, int SKM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
+    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out)
+{
+    using SK = Skinny<SKM>;
+    constexpr int kSkM = SKM, kSkSlots = SK::kSlots, kSkA = SK::kA, kSkSlot = SK::kSlot;
+    constexpr int kSkPerStage = SK::kPerStage, kNB = SK::kBlocks;
+    __shared__ __attribute__((aligned(1024))) char ring[kSkSlots * kSkSlot];
+    __shared__ int32_t rowmap[kSkM];
+    __shared__ int32_t ssched[2 * 257];  // skinny tile_start[E+1], row_start[E+1]
+
+    for (int i = threadIdx.x; i < E + 1; i += kThreads) {
+        ssched[i] = sched[SK::kSchedOff * (E + 1) + i];
+        ssched[E + 1 + i] = sched[E + 1 + i];
+    }
+    __syncthreads();
+    const int KT = (MODE == kGateUp ? H : F) / kTK;
+    const int total = ssched[E] * ntiles_n;
+    const int P = gridDim.x;
+    const int per_xcd = P / 8;
+    const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (my_slot >= total) return;
+
+    const int tid = threadIdx.x;
+    const int wave = uni(tid >> 6), lane = tid & 63;
+    const int fr = lane & 31, fh = lane >> 5;
+    const uint32_t ring_u = (uint32_t)(uintptr_t)ring;
+    // fragment byte offsets in a stage, k-steps 0..3: A rows 0..31 (row block
+    // i at 32 i); B block 0 rows (gate/up) 32 wave + fr, block 1 the up rows
+    // 128 further; (down) 64 wave + fr, block 1 32 further
+    uint32_t fa[4], fb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t ch = (uint32_t)(((2 * kk + fh) ^ swz(fr)) * 16);
+        fa[kk] = (uint32_t)fr * 128u + ch;
+        fb[kk] = (uint32_t)kSkA + (uint32_t)((MODE == kGateUp ? 32 : 64) * wave + fr) * 128u + ch;
+    }
+    constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
+
+    for (int Lu = my_slot; Lu < total; Lu += P) {
+        const TileRef r0 = tile_of<MODE>(Lu, E, ntiles_n, ssched);
+        const int e = uni(r0.e), n0 = uni(r0.n0), rows = uni(r0.rows), hrow0 = uni(r0.hrow0);
+        if (tid < kSkM) rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : rows - 1)];
+        wait_vm_lgkm<63>();
+        slot_barrier();
+
+        // copy sources: A row 8 wave + lane/8 (one instruction per wave), B as
+        // in the 256-row kernel (8 instructions per wave)
+        const char *abase, *bbase0, *bbase1;
+        if (MODE == kGateUp) {
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)e * F * H));
+            bbase1 = uni_ptr(reinterpret_cast<const char*>(w1 + (size_t)e * F * H));
+        } else {
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)hrow0 * F));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)e * H * F));
+            bbase1 = bbase0;
+        }
+        // A copy instruction q = wave + 4 i fills rows 8q .. 8q+7
+        uint32_t aoff[SK::kACopies], boff[kCopiesWave];
+#pragma unroll
+        for (int i = 0; i < SK::kACopies; ++i) {
+            const int ra = 8 * (wave + 4 * i) + (lane >> 3);
+            const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(ra)) * 16);
+            aoff[i] = MODE == kGateUp ? (uint32_t)rowmap[ra] * (uint32_t)H * 2u + ch
+                                      : (uint32_t)min(ra, rows - 1) * (uint32_t)F * 2u + ch;
+        }
+#pragma unroll
+        for (int i = 0; i < kCopiesWave; ++i) {
+            const int rb = 8 * (wave + 4 * i) + (lane >> 3);
+            const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(rb)) * 16);
+            boff[i] = MODE == kGateUp ? (uint32_t)min(n0 + (rb & 127), F - 1) * (uint32_t)H * 2u + ch
+                                      : (uint32_t)min(n0 + rb, H - 1) * (uint32_t)F * 2u + ch;
+        }
+        auto copy_stage = [&](int st) {
+            const uint32_t slot = ring_u + (uint32_t)(st % kSkSlots) * kSkSlot;
+#pragma unroll
+            for (int i = 0; i < SK::kACopies; ++i)
+                copy16(abase + st * (kTK * 2), aoff[i], slot + wave * 1024 + i * 4096);
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i)
+                copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
+                       slot + kSkA + wave * 1024 + i * 4096);
+        };
+        f32x16 acc[kNB][2];
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[b][j][q] = 0.0f;
+        constexpr int kAhead = kSkSlots - 1;  // stages in flight beyond the current one
+        for (int st = 0; st < kAhead && st < KT; ++st) copy_stage(st);
+
+        for (int s = 0; s < KT; ++s) {
+            // stage s landed: this wave's copies of later stages issued so far
+            const int after = min(KT - 1, s + kAhead - 1) - s;
+            if (after >= 2) wait_vm_lgkm<2 * kSkPerStage>();
+            else if (after == 1) wait_vm_lgkm<kSkPerStage>();
+            else wait_vm_lgkm<0>();
+            slot_barrier();  // ... in every wave; and stage s-1's slot is free
+            if (s + kAhead < KT) copy_stage(s + kAhead);
+            const char* slot = ring + (s % kSkSlots) * kSkSlot;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 af[kNB];
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) af[b] = lds_frag(slot + fa[kk] + b * 4096);
+                const bf16x8 bf0 = lds_frag(slot + fb[kk]);
+                const bf16x8 bf1 = lds_frag(slot + fb[kk] + kB1);
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) {
+                    acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf0, af[b], acc[b][0], 0, 0, 0);
+                    acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf1, af[b], acc[b][1], 0, 0, 0);
+                }
+            }
+        }
+
+        // epilogue: acc[b][j][4 g4 + q] is row 32 b + (lane & 31), B-row block
+        // j column 8 g4 + 4 (lane >> 5) + q
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            const int row = 32 * b + fr;
+            if (row >= rows) continue;
+            if (MODE == kGateUp) {
+                uint16_t* dst = out + (size_t)(hrow0 + row) * F;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int col = n0 + 32 * wave + g4 * 8 + fh * 4;
+                    if (col >= F) continue;
+                    float hv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        hv[q] = fast_silu(acc[b][0][g4 * 4 + q]) * acc[b][1][g4 * 4 + q];
+                    uint2 pk;
+                    pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                    pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                    *reinterpret_cast<uint2*>(dst + col) = pk;
+                }
+            } else {
+                uint16_t* dst = out + (size_t)rowmap[row] * H;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = n0 + 64 * wave + 32 * j + g4 * 8 + fh * 4;
+                        if (col >= H) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(acc[b][j][g4 * 4 + 0], acc[b][j][g4 * 4 + 1]);
+                        pk.y = moe::pack_bf16x2(acc[b][j][g4 * 4 + 2], acc[b][j][g4 * 4 + 3]);
+                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                    }
+            }
+        }
+        // everyone is done with the ring and rowmap before the next unit
+        wait_vm_lgkm<63>();
+        slot_barrier();
+    }
+}
+
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
 // partial tiles of each leftover tile in part order and writes the result
 // the whole-tile epilogue would have written (gate/up: bf16 silu(g) * u into
@@ -777,7 +976,8 @@ hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, c
     const moe::WsLayout W = moe::ws_layout(s);
     int32_t* sched = reinterpret_cast<int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bf ? kTM : kFM, plan, sched);
+    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bf ? kTM : kFM, bf ? 32 : 0, bf ? 64 : 0, plan,
+                                            sched);
     hipError_t e = hipGetLastError();
     const int N = s.T * s.k;
     if (e != hipSuccess || !bf || N == 0) return e;
@@ -799,6 +999,12 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
         float* part = reinterpret_cast<float*>(ws + W.part);
         uint16_t* h = reinterpret_cast<uint16_t*>(ws + W.h);
+        gemm_skinny_kernel<kGateUp, 32><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
+            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h);
+        gemm_skinny_kernel<kGateUp, 64><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
+            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h);
         gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(
             s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
             static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h, part);
@@ -829,6 +1035,12 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
         const int P = persistent_grid();
         const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
         float* part = reinterpret_cast<float*>(ws + W.part);
+        gemm_skinny_kernel<kDown, 32><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
+            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
+        gemm_skinny_kernel<kDown, 64><<<P, kThreads, 0, st>>>(
+            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
+            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
         gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(
             s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
             static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y), part);

@@ -119,6 +119,11 @@ SMALL = [
     ("bf16_fewer_rows_than_ranks", 1, 64, 8, 2, 64, 4, 2, moe.MOE_BF16, 0.0),
     ("bf16_odd_k_split", 300, 128, 8, 2, 192, 4, 2, moe.MOE_BF16, 0.3),
     ("bf16_two_experts_wide", 520, 512, 2, 1, 256, 2, 1, moe.MOE_BF16, 0.0),
+    # experts around 32 rows: skinny (<= 32 rows) and 256-row tiles in one launch,
+    # 16 K-stages through the skinny kernel's 4-stage ring
+    ("bf16_skinny_boundary", 64, 1024, 4, 2, 256, 2, 1, moe.MOE_BF16, 0.0),
+    # skinny tiles with 1 and 2 K-stages (gate/up K = 64, down K = 128)
+    ("bf16_skinny_short_k", 40, 64, 8, 2, 128, 4, 2, moe.MOE_BF16, 0.5),
 ]
 
 
