@@ -81,6 +81,8 @@ def _load():
         lib.orc_capacity.restype = ctypes.c_int32
         lib.orc_capacity.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_double]
         lib.orc_hot_share.restype = ctypes.c_double
+        lib.orc_capacity_dispatch.restype = None
+        lib.orc_repack.restype = None
         _lib = lib
     return _lib
 
@@ -195,6 +197,31 @@ def combine(y, dest_row, w, shared=None):
     _load().orc_combine(T, k, H, _p(y, F64P), _p(dest_row, I32P), _p(w, F64P), _p(sh, F64P),
                         _p(out, F64P))
     return out
+
+
+def capacity_dispatch(x, ids, eidx, E, cap):
+    """Fixed-capacity dispatch: buf [E*cap][...] (padding rows zero) and
+    dest_row (-1 where the assignment is dropped), byte-exact rows."""
+    x = np.ascontiguousarray(x)
+    ids = _i32(ids)
+    eidx = _i32(eidx).reshape(ids.shape)
+    T, k = ids.shape
+    row_bytes = x.strides[0] if x.ndim > 1 else x.itemsize
+    buf = np.empty((E * cap,) + x.shape[1:], x.dtype)
+    dest_row = np.empty((T, k), np.int32)
+    _load().orc_capacity_dispatch(T, k, E, cap, ctypes.c_size_t(row_bytes),
+                                  x.ctypes.data_as(ctypes.c_void_p), _p(ids, I32P), _p(eidx, I32P),
+                                  buf.ctypes.data_as(ctypes.c_void_p), _p(dest_row, I32P))
+    return buf, dest_row
+
+
+def repack(counts, R):
+    """Greedy balanced packing of experts onto R ranks (n = E/R each):
+    mapping[e] = rank."""
+    c = _i32(counts)
+    mapping = np.empty(c.shape[0], np.int32)
+    _load().orc_repack(c.shape[0], int(R), _p(c, I32P), _p(mapping, I32P))
+    return mapping
 
 
 def capacity(N, E, factor):

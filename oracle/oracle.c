@@ -318,6 +318,74 @@ void orc_permute(int T, int k, int E, int R, size_t row_bytes, const void *x,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Fixed-capacity dispatch: the static-capacity baseline that the equal-load
+ * plan replaces.
+ * [Hotspot] "Make expert capacity, overflow, and padding explicit": every
+ * expert has the same capacity; demand above it overflows (the assignment is
+ * dropped) and the unused slots below it are padding.
+ * Reading: an expert keeps its first cap assignments in stable order
+ * (eidx < cap). The buffer is [E][cap] rows: assignment (t,j) of expert e
+ * with eidx v < cap goes to row e*cap + v; padding rows are zero; a dropped
+ * (or out-of-range) assignment gets dest_row = -1.                          */
+void orc_capacity_dispatch(int T, int k, int E, int cap, size_t row_bytes, const void *x,
+                           const int32_t *ids, const int32_t *eidx, void *buf, int32_t *dest_row)
+{
+    memset(buf, 0, (size_t)E * (size_t)cap * row_bytes);
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            int v = eidx[(size_t)t * k + j];
+            int dest = -1;
+            if (e >= 0 && e < E && v >= 0 && v < cap) dest = e * cap + v;
+            dest_row[(size_t)t * k + j] = dest;
+            if (dest < 0) continue;
+            memcpy((char *)buf + (size_t)dest * row_bytes, (const char *)x + (size_t)t * row_bytes,
+                   row_bytes);
+        }
+    }
+}
+
+/* Repacking (EPLB-style static placement, the other baseline): assign the E
+ * experts to the R ranks, n = E/R each, so that rank demand is even.
+ * [Hotspot] "Separate expert demand from rank placement": for the fixture
+ * demand, the mapping {0,7},{1,6},{2,5},{3,4} takes rank demand from
+ * [15,9,5,3] to [10,8,7,7]. The pages print the mapping, not the rule.
+ * Reading: greedy balanced packing -- experts in order of decreasing demand
+ * (equal demand: lower id first) each go to the least-loaded rank that still
+ * holds fewer than n experts (equal load: lower rank). It reproduces the
+ * printed mapping. mapping[e] = rank of expert e.                          */
+void orc_repack(int E, int R, const int32_t *counts, int32_t *mapping)
+{
+    int n = E / R;
+    int *order = (int *)malloc(sizeof(int) * (size_t)E);
+    int64_t *load = (int64_t *)calloc((size_t)R, sizeof(int64_t));
+    int *held = (int *)calloc((size_t)R, sizeof(int));
+    for (int e = 0; e < E; ++e) order[e] = e;
+    /* selection sort by (count desc, id asc) */
+    for (int i = 0; i < E; ++i) {
+        int best = i;
+        for (int j = i + 1; j < E; ++j) {
+            int a = order[j], b = order[best];
+            if (counts[a] > counts[b] || (counts[a] == counts[b] && a < b)) best = j;
+        }
+        int tmp = order[i];
+        order[i] = order[best];
+        order[best] = tmp;
+    }
+    for (int i = 0; i < E; ++i) {
+        int e = order[i], best = -1;
+        for (int r = 0; r < R; ++r)
+            if (held[r] < n && (best < 0 || load[r] < load[best])) best = r;
+        mapping[e] = best;
+        load[best] += counts[e];
+        held[best] += 1;
+    }
+    free(order);
+    free(load);
+    free(held);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Expert FFN: [Primer] phase (c), each expert's feed-forward network on the
  * rows it received. The expert is a SwiGLU FFN:
  *   g = W_gate x, u = W_up x, h = silu(g) * u, silu(z) = z / (1 + e^-z),
@@ -364,6 +432,7 @@ void orc_combine(int T, int k, int H, const double *y, const int32_t *dest_row,
             double acc = 0.0;
             for (int j = 0; j < k; ++j) {
                 int d = dest_row[(size_t)t * k + j];
+                if (d < 0) continue; /* dropped by a fixed capacity: contributes nothing */
                 acc += w[(size_t)t * k + j] * y[(size_t)d * H + c];
             }
             if (shared) acc += shared[(size_t)t * H + c];

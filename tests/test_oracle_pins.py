@@ -438,3 +438,115 @@ def test_combine_one_hot_and_order():
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
     sh = rng.standard_normal((T, H))
     np.testing.assert_allclose(oracle.combine(y, dest, w, sh), a + sh, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- fixed capacity, repack ----
+# "MoE Load Balancing: Find Expert Hotspots", "Make expert capacity, overflow,
+# and padding explicit" (cap 5 for the fixture; processed 27, overflow 5,
+# padding 13) and "Separate expert demand from rank placement" (the mapping
+# {0,7},{1,6},{2,5},{3,4} takes rank demand to [10,8,7,7]).
+
+def test_fixture_capacity_dispatch_ledgers():
+    ids = _pairs(FIX)
+    T, k = ids.shape
+    c = oracle.count(ids, 8, 4)
+    cap = FIX["capacity"]
+    x = np.arange(T * 3, dtype=np.float32).reshape(T, 3) + 1.0   # no zero rows in x
+    buf, dest = oracle.capacity_dispatch(x, ids, c["eidx"], 8, cap)
+    kept = np.bincount(ids.ravel()[dest.ravel() >= 0], minlength=8)
+    np.testing.assert_array_equal(kept, FIX["processed"])
+    assert (dest < 0).sum() == sum(FIX["overflow"])
+    pad = (np.abs(buf).sum(1) == 0).reshape(8, cap).sum(1)
+    np.testing.assert_array_equal(pad, FIX["padding"])
+    assert kept.sum() == 27 and (dest < 0).sum() == 5 and pad.sum() == 13
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_capacity_dispatch_brute_force(seed):
+    # an assignment is kept iff fewer than cap earlier assignments (flat order)
+    # went to its expert; it then sits at row e*cap + (that number)
+    rng = np.random.default_rng(700 + seed)
+    T, E, k = 60, [8, 16, 32][seed], [2, 4, 8][seed]
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    cap = int(rng.integers(1, 2 * T * k // E))
+    x = rng.standard_normal((T, 5)).astype(np.float32)
+    buf, dest = oracle.capacity_dispatch(x, ids, oracle.count(ids, E, 1)["eidx"], E, cap)
+    seen = {}
+    want_buf = np.zeros((E * cap, 5), np.float32)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            v = seen.get(e, 0)
+            seen[e] = v + 1
+            if v < cap:
+                assert dest[t, j] == e * cap + v
+                want_buf[e * cap + v] = x[t]
+            else:
+                assert dest[t, j] == -1
+    np.testing.assert_array_equal(buf, want_buf)
+
+
+def test_combine_skips_dropped_assignments():
+    rng = np.random.default_rng(5)
+    T, k, H = 8, 2, 4
+    y = rng.standard_normal((T * k, H))
+    dest = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    w = rng.random((T, k))
+    full = oracle.combine(y, dest, w)
+    dropped = dest.copy()
+    dropped[::2, 1] = -1
+    w0 = w.copy()
+    w0[::2, 1] = 0.0
+    np.testing.assert_allclose(oracle.combine(y, dropped, w), oracle.combine(y, dest, w0),
+                               rtol=1e-15, atol=0)
+    assert not np.allclose(oracle.combine(y, dropped, w), full)
+
+
+def test_fixture_repack_reproduces_page_mapping():
+    m = oracle.repack(np.array(FIX["demand"], np.int32), 4)
+    np.testing.assert_array_equal(m, _mapping([[0, 7], [1, 6], [2, 5], [3, 4]], 8))
+    np.testing.assert_array_equal(np.bincount(m, weights=FIX["demand"], minlength=4), [10, 8, 7, 7])
+    st = oracle.stats(_pairs(FIX), np.array(FIX["demand"], np.int32), 4, mapping=m)
+    np.testing.assert_array_equal(st["mapped_load"], [10, 8, 7, 7])
+
+
+@pytest.mark.parametrize("counts, R, groups", [
+    ([5, 5, 1, 1], 2, [[0, 2], [1, 3]]),
+    ([7, 1, 1, 1, 1, 1], 3, [[0, 5], [1, 3], [2, 4]]),
+    ([3, 3, 3, 3], 4, [[0], [1], [2], [3]]),
+    ([0, 0, 0, 0, 0, 0, 0, 0], 2, [[0, 1, 2, 3], [4, 5, 6, 7]]),   # equal load: lower rank first
+])
+def test_repack_hand_examples(counts, R, groups):
+    np.testing.assert_array_equal(oracle.repack(np.array(counts, np.int32), R),
+                                  _mapping(groups, len(counts)))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_repack_invariants_and_brute_force_bounds(seed):
+    rng = np.random.default_rng(900 + seed)
+    E, R = 8, [2, 4, 2, 4][seed]
+    n = E // R
+    for _ in range(50):
+        c = rng.integers(0, 40, E).astype(np.int32)
+        m = oracle.repack(c, R)
+        np.testing.assert_array_equal(np.bincount(m, minlength=R), np.full(R, n))
+        got = np.bincount(m, weights=c, minlength=R).max()
+        # brute force over every balanced placement: the greedy rule is a
+        # heuristic, so only the bounds every balanced placement obeys hold
+        best = min(max(sum(c[list(g)]) for g in parts) for parts in _balanced_partitions(E, R))
+        assert best <= got <= np.sort(c)[::-1][:n].sum()
+
+
+def _balanced_partitions(E, R):
+    n = E // R
+
+    def rec(left, groups):
+        if not left:
+            yield groups
+            return
+        first = left[0]
+        for rest in itertools.combinations(left[1:], n - 1):
+            g = (first,) + rest
+            yield from rec([e for e in left if e not in g], groups + [g])
+
+    yield from rec(list(range(E)), [])
