@@ -19,7 +19,8 @@ __all__ = [
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
     "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
-    "plan_tables",
+    "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
+    "moe_repack", "capacity_shape", "plan_tables",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -30,7 +31,8 @@ ERR_NONFINITE, ERR_RANGE, ERR_REPEAT = 1, 2, 4
 EXPORTED_SYMBOLS = (
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes", "moe_route",
     "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_schedule",
-    "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
+    "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "moe_capacity_rows",
+    "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine", "moe_repack",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -128,6 +130,11 @@ def load():
         "moe_combine": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_stats": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_double, _VP,
                            ctypes.c_size_t, ctypes.POINTER(StatsT), _VP, _VP]),
+        "moe_capacity_rows": (ctypes.c_int32, [_SP, ctypes.c_double]),
+        "moe_capacity_dispatch": (st, [_SP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_capacity_plan": (st, [_SP, ctypes.c_int32, _VP, _VP]),
+        "moe_capacity_combine": (st, [_SP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_repack": (st, [_SP, _VP, _VP, _VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -339,3 +346,54 @@ def plan_tables(plan, shape) -> dict:
             cnt *= s
         out[name] = plan[L[name]:L[name] + cnt].view(*shp)
     return out
+
+
+# -------------------------------------------------- baselines of the plan --
+
+def moe_capacity_rows(shape, capacity_factor) -> int:
+    """Per-expert capacity ceil(N / E * factor); -1 for invalid input."""
+    return int(load().moe_capacity_rows(ctypes.byref(shape), float(capacity_factor)))
+
+
+def capacity_shape(shape, cap):
+    """The shape moe_grouped_gemm takes over the [E*cap] capacity buffer."""
+    return shape.replace(T=shape.E * cap, k=1)
+
+
+def moe_capacity_dispatch(shape, cap, counts, x, ids, eidx, buf, dest_row, stream=None):
+    import torch
+
+    i32, act = torch.int32, _act_dtype(shape)
+    args = (ctypes.byref(shape), int(cap), _ptr(counts, i32, "counts", shape.E),
+            _ptr(x, act, "x", shape.T * shape.H), _ptr(ids, i32, "ids", shape.N),
+            _ptr(eidx, i32, "eidx", shape.N), _ptr(buf, act, "buf", shape.E * cap * shape.H),
+            _ptr(dest_row, i32, "dest_row", shape.N), _stream(stream))
+    _ok(load().moe_capacity_dispatch(*args), "moe_capacity_dispatch")
+
+
+def moe_capacity_plan(shape, cap, plan, stream=None):
+    import torch
+
+    total = moe_plan_layout(shape)["total"]
+    _ok(load().moe_capacity_plan(ctypes.byref(shape), int(cap),
+                                 _ptr(plan, torch.int32, "plan", total), _stream(stream)),
+        "moe_capacity_plan")
+
+
+def moe_capacity_combine(shape, cap, y, dest_row, w, shared_y, out, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    args = (ctypes.byref(shape), int(cap), _ptr(y, act, "y", shape.E * cap * shape.H),
+            _ptr(dest_row, torch.int32, "dest_row", shape.N), _ptr(w, torch.float32, "w", shape.N),
+            _ptr(shared_y, act, "shared_y", shape.T * shape.H, nullable=True),
+            _ptr(out, act, "out", shape.T * shape.H), _stream(stream))
+    _ok(load().moe_capacity_combine(*args), "moe_capacity_combine")
+
+
+def moe_repack(shape, counts, mapping, stream=None):
+    import torch
+
+    _ok(load().moe_repack(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
+                          _ptr(mapping, torch.int32, "mapping", shape.E), _stream(stream)),
+        "moe_repack")

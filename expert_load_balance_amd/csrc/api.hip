@@ -192,6 +192,71 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
                                   as_stream(stream)));
 }
 
+int32_t moe_capacity_rows(const moe_shape_t* shape, double capacity_factor)
+{
+    if (check(shape) != MOE_OK) return -1;
+    if (!(capacity_factor > 0.0) || !isfinite(capacity_factor)) return -1;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    // the page's formula in the page's order: N / E * factor (as in moe_stats)
+    const double capd = ceil((double)N / (double)shape->E * capacity_factor);
+    if (!(capd * shape->E < 2147483647.0)) return -1;
+    return (int32_t)capd;
+}
+
+namespace {
+// cap >= 1 and the [E][cap] buffer addressable like an N-row one
+inline bool bad_cap(const moe_shape_t* s, int32_t cap)
+{
+    return cap < 1 || (int64_t)cap * s->E >= (int64_t(1) << 31);
+}
+}  // namespace
+
+moe_status_t moe_capacity_dispatch(const moe_shape_t* shape, int32_t cap, const int32_t* d_counts,
+                                   const void* d_x, const int32_t* d_ids, const int32_t* d_eidx,
+                                   void* d_buf, int32_t* d_dest_row, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (bad_cap(shape, cap)) return MOE_EINVAL;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (!d_counts || bad(d_x, T) || bad(d_ids, N) || bad(d_eidx, N) || !d_buf ||
+        bad(d_dest_row, N))
+        return MOE_EINVAL;
+    return dev(moe_launch_capacity_dispatch(*shape, cap, d_counts, d_x, d_ids, d_eidx, d_buf,
+                                            d_dest_row, as_stream(stream)));
+}
+
+moe_status_t moe_capacity_plan(const moe_shape_t* shape, int32_t cap, int32_t* d_plan,
+                               moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (bad_cap(shape, cap) || !d_plan) return MOE_EINVAL;
+    return dev(moe_launch_capacity_plan(*shape, cap, d_plan, as_stream(stream)));
+}
+
+moe_status_t moe_capacity_combine(const moe_shape_t* shape, int32_t cap, const void* d_y,
+                                  const int32_t* d_dest_row, const float* d_w,
+                                  const void* d_shared_y, void* d_out, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (bad_cap(shape, cap)) return MOE_EINVAL;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (!d_y || bad(d_dest_row, N) || bad(d_w, N) || bad(d_out, T)) return MOE_EINVAL;
+    return dev(moe_launch_combine_rows(*shape, (int64_t)cap * shape->E, d_y, d_dest_row, d_w,
+                                       d_shared_y, d_out, as_stream(stream)));
+}
+
+moe_status_t moe_repack(const moe_shape_t* shape, const int32_t* d_counts, int32_t* d_mapping,
+                        moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_counts || !d_mapping) return MOE_EINVAL;
+    return dev(moe_launch_repack(*shape, d_counts, d_mapping, as_stream(stream)));
+}
+
 moe_status_t moe_stats(const moe_shape_t* shape, const int32_t* d_counts, const int32_t* d_ids,
                        const int32_t* d_plan, const int32_t* d_dest_row,
                        const int32_t* d_mapping, const int32_t* d_origin, const int32_t* d_err,

@@ -149,6 +149,15 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
                                   hipStream_t st);
 hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
                                 void* y, char* ws, hipStream_t st);
+hipError_t moe_launch_combine_rows(const moe_shape_t& s, int64_t nrows, const void* y,
+                                   const int32_t* dest_row, const float* w, const void* shared_y,
+                                   void* out, hipStream_t st);
+hipError_t moe_launch_capacity_dispatch(const moe_shape_t& s, int cap, const int32_t* counts,
+                                        const void* x, const int32_t* ids, const int32_t* eidx,
+                                        void* buf, int32_t* dest_row, hipStream_t st);
+hipError_t moe_launch_capacity_plan(const moe_shape_t& s, int cap, int32_t* plan, hipStream_t st);
+hipError_t moe_launch_repack(const moe_shape_t& s, const int32_t* counts, int32_t* mapping,
+                             hipStream_t st);
 hipError_t moe_launch_stats(const moe_shape_t& s, const int32_t* counts, const int32_t* ids,
                             const int32_t* plan, const int32_t* dest_row, const int32_t* mapping,
                             const int32_t* origin, const int32_t* err, int32_t capacity,

@@ -142,7 +142,8 @@ struct Vec<false> {
 // are read four at a time before they are accumulated (fp32, in j order);
 // then the shared row is added.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void combine_kernel(int T, int k, int row_vecs, int nchunks,
+__global__ __launch_bounds__(kThreads) void combine_kernel(int T, int k, int64_t nrows, int row_vecs,
+                                                           int nchunks,
                                                            const uint4* __restrict__ y,
                                                            const int32_t* __restrict__ dest_row,
                                                            const float* __restrict__ w,
@@ -154,14 +155,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int k, int row
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (wid >= (int64_t)T * nchunks) return;
     const int t = (int)(wid / nchunks), ch = (int)(wid % nchunks);
-    const int N = T * k;
     const int c0 = ch * kChunkVecs + lane;
     int d = -1;
     float wl = 0.0f;
     if (lane < k) {
         const int a = t * k + lane;
         const int dd = dest_row[a];
-        d = (dd >= 0 && dd < N) ? dd : -1;
+        d = (dd >= 0 && dd < nrows) ? dd : -1;
         wl = w[a];
     }
     float acc[kVpl][V::kN];
@@ -237,8 +237,9 @@ hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t
     return hipGetLastError();
 }
 
-hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t* dest_row,
-                              const float* w, const void* shared_y, void* out, hipStream_t st)
+hipError_t moe_launch_combine_rows(const moe_shape_t& s, int64_t nrows, const void* y,
+                                   const int32_t* dest_row, const float* w, const void* shared_y,
+                                   void* out, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
     const int bytes = s.dtype == MOE_BF16 ? 2 : 4;
@@ -250,8 +251,16 @@ hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t
     const uint4* sv = static_cast<const uint4*>(shared_y);
     uint4* ov = static_cast<uint4*>(out);
     if (s.dtype == MOE_BF16)
-        combine_kernel<true><<<grid, kThreads, 0, st>>>(s.T, s.k, row_vecs, nchunks, yv, dest_row, w, sv, ov);
+        combine_kernel<true><<<grid, kThreads, 0, st>>>(s.T, s.k, nrows, row_vecs, nchunks, yv,
+                                                        dest_row, w, sv, ov);
     else
-        combine_kernel<false><<<grid, kThreads, 0, st>>>(s.T, s.k, row_vecs, nchunks, yv, dest_row, w, sv, ov);
+        combine_kernel<false><<<grid, kThreads, 0, st>>>(s.T, s.k, nrows, row_vecs, nchunks, yv,
+                                                         dest_row, w, sv, ov);
     return hipGetLastError();
+}
+
+hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t* dest_row,
+                              const float* w, const void* shared_y, void* out, hipStream_t st)
+{
+    return moe_launch_combine_rows(s, (int64_t)s.T * s.k, y, dest_row, w, shared_y, out, st);
 }

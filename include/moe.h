@@ -9,6 +9,8 @@
  *   moe_grouped_gemm SwiGLU expert FFN over the plan    (phase c)
  *   moe_combine      gate-weighted gather back to tokens (phase d)
  *   moe_stats        maxvio / balancedness / capacity / remote statistics
+ * and the two baselines the plan replaces: fixed-capacity dispatch
+ * (moe_capacity_*) and static repacking (moe_repack).
  *
  * Sources (web pages, cited by title and section):
  *   [Primer]  "DeepEP-on-EFA Guidance, section 1: what is MoE" -- the
@@ -263,6 +265,52 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
                        const int32_t *d_mapping, const int32_t *d_origin, const int32_t *d_err,
                        double capacity_factor, void *d_ws, size_t ws_bytes, moe_stats_t *h_out,
                        int32_t *h_rank_loads, moe_stream_t stream);
+
+/* ---- Baselines the equal-load plan replaces ------------------------------
+ * [Hotspot] "Make expert capacity, overflow, and padding explicit": a fixed
+ * capacity per expert; demand above it overflows (the assignment is
+ * dropped), unused slots below it are padding. And "Separate expert demand
+ * from rank placement": a static expert -> rank mapping that pairs hot and
+ * cold experts. */
+
+/* Per-expert capacity ceil(N / E * capacity_factor) (the moe_stats figure),
+ * or -1 for an invalid shape or factor, or when E * capacity does not fit
+ * int32. */
+int32_t moe_capacity_rows(const moe_shape_t *shape, double capacity_factor);
+
+/* Fixed-capacity dispatch into a static [E][cap] buffer. An expert keeps its
+ * first cap assignments in stable order: assignment (t,j) of expert e with
+ * eidx v < cap goes to row e*cap + v; the others are dropped (dest_row -1).
+ * Rows e*cap + v with v >= counts[e] are padding and are written as zeros.
+ *   cap >= 1, E*cap < 2^31; d_counts int32[E] (moe_count); d_x dtype[T][H];
+ *   d_ids, d_eidx int32[T][k]; d_buf dtype[E*cap][H] out (every row
+ *   written); d_dest_row int32[T][k] out. */
+moe_status_t moe_capacity_dispatch(const moe_shape_t *shape, int32_t cap, const int32_t *d_counts,
+                                   const void *d_x, const int32_t *d_ids, const int32_t *d_eidx,
+                                   void *d_buf, int32_t *d_dest_row, moe_stream_t stream);
+
+/* The plan block (moe_plan_layout) of the capacity layout: expert e is home
+ * on rank e / (E/R) with one piece of cap rows at row e*cap, no replicas.
+ * With it, moe_grouped_gemm over the shape {T = E*cap, k = 1, H, E, F, R, S,
+ * dtype} runs the expert FFN over the whole static buffer, padding rows
+ * included (they are zero and give zero rows). */
+moe_status_t moe_capacity_plan(const moe_shape_t *shape, int32_t cap, int32_t *d_plan,
+                               moe_stream_t stream);
+
+/* moe_combine over the capacity buffer: d_y dtype[E*cap][H]; dropped
+ * assignments (dest_row -1) contribute nothing; other arguments as in
+ * moe_combine. */
+moe_status_t moe_capacity_combine(const moe_shape_t *shape, int32_t cap, const void *d_y,
+                                  const int32_t *d_dest_row, const float *d_w,
+                                  const void *d_shared_y, void *d_out, moe_stream_t stream);
+
+/* Greedy balanced repacking: experts in order of decreasing demand (equal
+ * demand: lower id first) each go to the least-loaded rank that holds fewer
+ * than E/R experts (equal load: lower rank). Reproduces the page's mapping
+ * {0,7},{1,6},{2,5},{3,4} for the fixture demand. d_counts int32[E];
+ * d_mapping int32[E] out (expert -> rank; usable as moe_stats' d_mapping). */
+moe_status_t moe_repack(const moe_shape_t *shape, const int32_t *d_counts, int32_t *d_mapping,
+                        moe_stream_t stream);
 
 #ifdef __cplusplus
 }

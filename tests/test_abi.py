@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -85,3 +85,21 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(moe, "_LIB_PATH", "/nonexistent/libmoe.so")
     with pytest.raises(RuntimeError):
         moe.load()
+
+
+def test_capacity_rows_and_rejections(lib):
+    s = moe.Shape(16, 64, 8, 2, 128, 4, 2, moe.MOE_F32)
+    # the hotspot fixture's capacity: ceil(32 / 8 * 1.25) = 5
+    assert moe.moe_capacity_rows(s, 1.25) == 5
+    assert moe.moe_capacity_rows(s, 1.0) == 4
+    assert moe.moe_capacity_rows(s, 0.0) == -1
+    assert moe.moe_capacity_rows(s, float("nan")) == -1
+    assert moe.moe_capacity_rows(s.replace(R=3), 1.25) == -1
+    p = ctypes.c_void_p(1)
+    # cap < 1 and NULL buffers are rejected before any launch
+    assert lib.moe_capacity_dispatch(ctypes.byref(s), 0, p, p, p, p, p, p, None) == 1
+    assert lib.moe_capacity_dispatch(ctypes.byref(s), 5, None, p, p, p, p, p, None) == 1
+    assert lib.moe_capacity_plan(ctypes.byref(s), 0, p, None) == 1
+    assert lib.moe_capacity_combine(ctypes.byref(s), 5, None, p, p, None, p, None) == 1
+    assert lib.moe_repack(ctypes.byref(s), None, p, None) == 1
+    assert lib.moe_repack(ctypes.byref(s.replace(E=0)), p, p, None) == 1
