@@ -119,9 +119,62 @@ def time_back_to_back(fn, reps=50):
     return a.elapsed_time(b) * 1e-3 / reps
 
 
-def run_workload(name, maxvio, steps, warmup):
+def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shared=None):
+    """The same layer through the fixed-capacity baseline: route, count,
+    dispatch into [E][cap] (drop and pad), the expert FFN over the whole
+    static buffer, (the shared expert, through L's buffers,) combine. Returns
+    tokens/s and the drop / padding figures."""
+    import torch
+
+    import expert_load_balance_amd as moe
+    from expert_load_balance_amd.layer import alloc
+
+    s = shape
+    i32 = torch.int32
+    act = x.dtype
+    cap = moe.moe_capacity_rows(s, cf)
+    cs = moe.capacity_shape(s, cap)
+    ws = alloc((moe.moe_workspace_bytes(s),), torch.uint8, "cuda")
+    ws2 = alloc((moe.moe_workspace_bytes(cs),), torch.uint8, "cuda")
+    ids, w = alloc((s.T, s.k), i32, "cuda"), alloc((s.T, s.k), torch.float32, "cuda")
+    err = torch.zeros(1, dtype=i32, device="cuda")
+    counts, offsets = alloc((s.E,), i32, "cuda"), alloc((s.E + 1,), i32, "cuda")
+    eidx, rank_load = alloc((s.N,), i32, "cuda"), alloc((s.R,), i32, "cuda")
+    buf, y = alloc((s.E * cap, s.H), act, "cuda"), alloc((s.E * cap, s.H), act, "cuda")
+    dest, out = alloc((s.T, s.k), i32, "cuda"), alloc((s.T, s.H), act, "cuda")
+    plan = alloc((moe.moe_plan_layout(cs)["total"],), i32, "cuda")
+    moe.moe_capacity_plan(s, cap, plan)      # static: the layout does not depend on the routing
+
+    def step():
+        moe.moe_route(s, lg, bias, ids, w, err)
+        moe.moe_count(s, ids, counts, offsets, eidx, rank_load, err, ws)
+        moe.moe_capacity_dispatch(s, cap, counts, x, ids, eidx, buf, dest)
+        moe.moe_grouped_gemm(cs, buf, plan, *wts, y, ws2)
+        sy = None
+        if shared is not None:
+            moe.moe_grouped_gemm(L.shared_shape, x, L.shared_plan, *shared, L.shared_y, L.shared_ws)
+            sy = L.shared_y
+        moe.moe_capacity_combine(s, cap, y, dest, w, sy, out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    c = counts.cpu()
+    kept = int(torch.minimum(c, torch.tensor(cap)).sum())
+    return {"capacity_factor": cf, "capacity": cap, "tokens_per_s": s.T / dt,
+            "ms_per_step": dt * 1e3, "dropped_assignments": s.N - kept,
+            "padding_rows": s.E * cap - kept, "gemm_rows": s.E * cap}
+
+
+def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     """Builds one workload on the GPU, runs `warmup` + `steps` layer steps and
-    returns its measurements (plus the inputs, for the CPU baseline)."""
+    returns its measurements (plus the inputs, for the CPU baseline); with a
+    capacity factor, also the fixed-capacity baseline on the same inputs."""
     import torch
 
     import expert_load_balance_amd as moe
@@ -181,6 +234,11 @@ def run_workload(name, maxvio, steps, warmup):
     t_comb = time_back_to_back(lambda: moe.moe_combine(shape, L.y, L.dest_row, L.w, sy, L.out,
                                                        stream=stream))
 
+    cap_res = None
+    if capacity_factor is not None:
+        cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
+                                      L=L, shared=shared)
+
     st, _ = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
                           err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
     N = T * k
@@ -201,7 +259,7 @@ def run_workload(name, maxvio, steps, warmup):
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
         permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        stats=st, inputs=(lg_np, bias_np, x, wts))
+        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res)
     return res
 
 
@@ -237,7 +295,7 @@ def main():
     name = args.workload
     w = wl.WORKLOADS[name]
     maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
-    r = run_workload(name, maxvio, args.steps, args.warmup)
+    r = run_workload(name, maxvio, args.steps, args.warmup, capacity_factor=1.25)
     T, H, E, k, F, R, S = r["shape"]
     shared_F = r["shared_F"]
     st = r["stats"]
@@ -277,6 +335,7 @@ def main():
         "plan": {"planned_max": st["planned_max"], "planned_min": st["planned_min"],
                  "replica_pieces": st["replica_pieces"], "max_slots_needed": st["max_slots_needed"],
                  "ranks_over_slots": st["ranks_over_slots"]},
+        "fixed_capacity_baseline": r["capacity"],
     }
     if not args.no_cpu_baseline:
         # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
@@ -288,7 +347,8 @@ def main():
     if not args.no_sweep:
         sweep = {}
         for sname, smv in SWEEP:
-            q = run_workload(sname, smv, 10, 3)
+            q = run_workload(sname, smv, 10, 3, capacity_factor=1.25)
+            cq = q["capacity"]
             sweep[f"{sname}@{smv:g}"] = {
                 "tokens_per_s": round(q["tokens_per_s"]), "ms_per_step": round(q["ms_per_step"], 4),
                 "maxvio_realised": round(q["stats"]["maxvio_expert"], 4),
@@ -296,7 +356,10 @@ def main():
                 "gemm_gateup_tflops": round(q["gu_tflops"], 1),
                 "gemm_down_tflops": round(q["dn_tflops"], 1),
                 "permute_hbm_frac": round(q["permute_hbm_frac"], 4),
-                "combine_hbm_frac": round(q["combine_hbm_frac"], 4)}
+                "combine_hbm_frac": round(q["combine_hbm_frac"], 4),
+                "fixed_capacity_cf1.25": {"tokens_per_s": round(cq["tokens_per_s"]),
+                                          "dropped_assignments": cq["dropped_assignments"],
+                                          "padding_rows": cq["padding_rows"]}}
             del q
             torch.cuda.empty_cache()
         rec["sweep"] = sweep
