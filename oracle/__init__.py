@@ -83,6 +83,8 @@ def _load():
         lib.orc_hot_share.restype = ctypes.c_double
         lib.orc_capacity_dispatch.restype = None
         lib.orc_repack.restype = None
+        lib.orc_router_logits.restype = None
+        lib.orc_bias_update.restype = None
         _lib = lib
     return _lib
 
@@ -197,6 +199,28 @@ def combine(y, dest_row, w, shared=None):
     _load().orc_combine(T, k, H, _p(y, F64P), _p(dest_row, I32P), _p(w, F64P), _p(sh, F64P),
                         _p(out, F64P))
     return out
+
+
+def router_logits(x, w_router):
+    """logit[t][e] = sum_h x[t][h] * W_r[e][h], in double from float inputs."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w_router, dtype=np.float32)
+    T, H = x.shape
+    E = w.shape[0]
+    out = np.empty((T, E), np.float64)
+    _load().orc_router_logits(T, E, H, _p(x, F32P), _p(w, F32P), _p(out, F64P))
+    return out
+
+
+def bias_update(counts, bias, gamma, N=None):
+    """Sign-rule bias update (an assumption; see oracle.c) around the mean
+    demand N / E (N defaults to the sum of counts). -> new fp32 bias."""
+    c = _i32(counts)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    n = int(c.sum()) if N is None else int(N)
+    _load().orc_bias_update(c.shape[0], ctypes.c_int64(n), _p(c, I32P),
+                            ctypes.c_float(gamma), _p(b, F32P))
+    return b
 
 
 def capacity_dispatch(x, ids, eidx, E, cap):

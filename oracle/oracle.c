@@ -25,6 +25,10 @@
  *  [Interview] "MoE load balancing: 90/10 routing in production" (summary
  *            and editor's note): per-expert bias kept out of the gate.
  *
+ * One function follows no page: orc_bias_update (an assumed update rule,
+ * labelled as such below). The router's linear layer and the fixed-capacity
+ * and repacking rules are readings of the pages, also labelled.
+ *
  * Every function with a pin in tests/ is pinned there; none is "parity
  * unpinned".
  */
@@ -315,6 +319,40 @@ void orc_permute(int T, int k, int E, int R, size_t row_bytes, const void *x,
         }
     }
     (void)E;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router scores: [Primer] phase (a), the router scores every expert for
+ * every token. The pages do not print the router; the plain reading is a
+ * linear layer, logit[t][e] = sum_h x[t][h] * W_r[e][h] (W_r row-major
+ * [E][H]), evaluated here in double from the given (already rounded)
+ * inputs. The top-k step that follows is orc_route.                       */
+void orc_router_logits(int T, int E, int H, const float *x, const float *w_router, double *out)
+{
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += (double)x[(size_t)t * H + h] * (double)w_router[(size_t)e * H + h];
+            out[(size_t)t * E + e] = acc;
+        }
+}
+
+/* Bias update -- NOT ON THE PAGES, a labelled assumption. [Interview] keeps
+ * a per-expert balancing bias out of the gate (it shifts selection only) but
+ * prints no update rule; [MoonEP] paragraph 2 only asks that maxvio go to
+ * zero. The rule assumed here is the sign rule of auxiliary-loss-free
+ * balancing: an expert above the mean demand N/E loses gamma, one below it
+ * gains gamma, one at the mean keeps its bias. In fp32: delta = +-gamma (as
+ * float) or 0, decided in integers by the sign of N - E * counts[e], then one
+ * fp32 add.                                                                */
+void orc_bias_update(int E, int64_t N, const int32_t *counts, float gamma, float *bias)
+{
+    for (int e = 0; e < E; ++e) {
+        int64_t s = N - (int64_t)E * counts[e];
+        float delta = s > 0 ? gamma : (s < 0 ? -gamma : 0.0f);
+        bias[e] = bias[e] + delta;
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -550,3 +550,57 @@ def _balanced_partitions(E, R):
             yield from rec([e for e in left if e not in g], groups + [g])
 
     yield from rec(list(range(E)), [])
+
+
+# ------------------------------------------------------ router, bias update ----
+# "DeepEP-on-EFA Guidance, section 1", phase (a): the router scores every
+# expert for every token (read: a linear layer); "MoE load balancing: 90/10
+# routing in production": a per-expert bias kept out of the gate. The bias
+# update rule is not on the pages (a labelled assumption: the sign rule).
+
+def test_router_logits_special_cases():
+    rng = np.random.default_rng(11)
+    T, H, E = 7, 16, 16
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    # identity router: the logits are the first E features, exactly
+    np.testing.assert_array_equal(oracle.router_logits(x, np.eye(E, H, dtype=np.float32)), x[:, :E])
+    assert not oracle.router_logits(x, np.zeros((E, H), np.float32)).any()
+    # small integers: exact in double, so equal to the integer matrix product
+    xi = rng.integers(-5, 6, (T, H)).astype(np.float32)
+    wi = rng.integers(-5, 6, (E, H)).astype(np.float32)
+    want = xi.astype(np.int64) @ wi.astype(np.int64).T
+    np.testing.assert_array_equal(oracle.router_logits(xi, wi), want)
+    # one-hot rows pick single weights: logit[t][e] = W[e][h_t]
+    hs = rng.integers(0, H, T)
+    oh = np.zeros((T, H), np.float32)
+    oh[np.arange(T), hs] = 1.0
+    w = rng.standard_normal((E, H)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.router_logits(oh, w), w[:, hs].T)
+
+
+def test_bias_update_sign_rule():
+    counts = np.array([9, 6, 5, 4, 3, 2, 2, 1], np.int32)      # fixture demand, mean 4
+    b0 = np.linspace(-1, 1, 8).astype(np.float32)
+    g = np.float32(0.125)
+    b1 = oracle.bias_update(counts, b0, g)
+    np.testing.assert_array_equal(b1[:3], b0[:3] - g)          # above the mean
+    assert b1[3] == b0[3]                                       # at the mean
+    np.testing.assert_array_equal(b1[4:], b0[4:] + g)          # below the mean
+    # balanced demand keeps every bias
+    np.testing.assert_array_equal(oracle.bias_update(np.full(8, 4, np.int32), b0, g), b0)
+
+
+def test_bias_update_closed_loop_reduces_maxvio():
+    # route -> count -> update on fixed logits: the assumed rule drives the
+    # expert-level maxvio towards zero (the page's aim), starting from a skew
+    T, E, k = 512, 16, 2
+    lg = synth.router_logits(T, E, 21)
+    bias = synth.zipf_bias(E, 0.8, 21).astype(np.float32)
+    first = None
+    for _ in range(200):
+        ids, _, _ = oracle.route(lg, bias, k)
+        c = oracle.count(ids, E, 4)["counts"]
+        mv = (c.max() * E - T * k) / (T * k)
+        first = mv if first is None else first
+        bias = oracle.bias_update(c, bias, 0.01)
+    assert first > 0.8 and mv < 0.25
