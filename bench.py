@@ -234,6 +234,17 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     t_comb = time_back_to_back(lambda: moe.moe_combine(shape, L.y, L.dest_row, L.w, sy, L.out,
                                                        stream=stream))
 
+    # the router's scores + top-k (x read once; W_r is E x H), back to back
+    wr = synth.device_normal((E, H), synth.weight_std(H), w["seed"] * 10 + 9, act, dev)
+    r_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    r_err = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_router = time_back_to_back(lambda: moe.moe_router(shape, x, wr, bias, r_logits, r_ids, r_w,
+                                                        r_err, stream=stream))
+    router_bytes = (T * H + E * H) * (2 if dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
+    del wr, r_logits
+
     cap_res = None
     if capacity_factor is not None:
         cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
@@ -259,7 +270,9 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
         permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res)
+        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res,
+        router={"us": t_router * 1e6, "tflops": 2.0 * T * E * H / t_router / 1e12,
+                "hbm_frac": router_bytes / t_router / 1e9 / PEAK_HBM_GBS})
     return res
 
 
@@ -336,6 +349,7 @@ def main():
                  "replica_pieces": st["replica_pieces"], "max_slots_needed": st["max_slots_needed"],
                  "ranks_over_slots": st["ranks_over_slots"]},
         "fixed_capacity_baseline": r["capacity"],
+        "router_scores_topk": r["router"],
     }
     if not args.no_cpu_baseline:
         # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
@@ -357,6 +371,7 @@ def main():
                 "gemm_down_tflops": round(q["dn_tflops"], 1),
                 "permute_hbm_frac": round(q["permute_hbm_frac"], 4),
                 "combine_hbm_frac": round(q["combine_hbm_frac"], 4),
+                "router_us": round(q["router"]["us"], 2),
                 "fixed_capacity_cf1.25": {"tokens_per_s": round(cq["tokens_per_s"]),
                                           "dropped_assignments": cq["dropped_assignments"],
                                           "padding_rows": cq["padding_rows"]}}

@@ -20,7 +20,7 @@ __all__ = [
     "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
-    "moe_repack", "capacity_shape", "plan_tables",
+    "moe_repack", "capacity_shape", "moe_router", "moe_bias_update", "plan_tables",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_schedule",
     "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "moe_capacity_rows",
     "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine", "moe_repack",
+    "moe_router", "moe_bias_update",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -135,6 +136,8 @@ def load():
         "moe_capacity_plan": (st, [_SP, ctypes.c_int32, _VP, _VP]),
         "moe_capacity_combine": (st, [_SP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_repack": (st, [_SP, _VP, _VP, _VP]),
+        "moe_router": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_bias_update": (st, [_SP, _VP, _VP, ctypes.c_float, _VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -397,3 +400,26 @@ def moe_repack(shape, counts, mapping, stream=None):
     _ok(load().moe_repack(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
                           _ptr(mapping, torch.int32, "mapping", shape.E), _stream(stream)),
         "moe_repack")
+
+
+# ------------------------------------------------------------------ router --
+
+def moe_router(shape, x, w_router, bias, logits, ids, w, err, stream=None):
+    import torch
+
+    act, i32 = _act_dtype(shape), torch.int32
+    args = (ctypes.byref(shape), _ptr(x, act, "x", shape.T * shape.H),
+            _ptr(w_router, act, "w_router", shape.E * shape.H),
+            _ptr(bias, torch.float32, "bias", shape.E, nullable=True),
+            _ptr(logits, torch.float32, "logits", shape.T * shape.E),
+            _ptr(ids, i32, "ids", shape.N), _ptr(w, torch.float32, "w", shape.N),
+            _ptr(err, i32, "err", 1), _stream(stream))
+    _ok(load().moe_router(*args), "moe_router")
+
+
+def moe_bias_update(shape, counts, bias, gamma, stream=None):
+    import torch
+
+    _ok(load().moe_bias_update(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
+                               _ptr(bias, torch.float32, "bias", shape.E), float(gamma),
+                               _stream(stream)), "moe_bias_update")

@@ -192,6 +192,30 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
                                   as_stream(stream)));
 }
 
+moe_status_t moe_router(const moe_shape_t* shape, const void* d_x, const void* d_w_router,
+                        const float* d_bias, float* d_logits, int32_t* d_ids, float* d_w,
+                        int32_t* d_err, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_x, T) || !d_w_router || bad(d_logits, T) || bad(d_ids, N) || bad(d_w, N) || !d_err)
+        return MOE_EINVAL;
+    hipStream_t hs = as_stream(stream);
+    hipError_t e = moe_launch_router_logits(*shape, d_x, d_w_router, d_logits, hs);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    return dev(moe_launch_route(*shape, d_logits, d_bias, d_ids, d_w, d_err, hs));
+}
+
+moe_status_t moe_bias_update(const moe_shape_t* shape, const int32_t* d_counts, float* d_bias,
+                             float gamma, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!d_counts || !d_bias || !(gamma >= 0.0f) || !isfinite(gamma)) return MOE_EINVAL;
+    return dev(moe_launch_bias_update(*shape, d_counts, gamma, d_bias, as_stream(stream)));
+}
+
 int32_t moe_capacity_rows(const moe_shape_t* shape, double capacity_factor)
 {
     if (check(shape) != MOE_OK) return -1;

@@ -158,6 +158,10 @@ hipError_t moe_launch_capacity_dispatch(const moe_shape_t& s, int cap, const int
 hipError_t moe_launch_capacity_plan(const moe_shape_t& s, int cap, int32_t* plan, hipStream_t st);
 hipError_t moe_launch_repack(const moe_shape_t& s, const int32_t* counts, int32_t* mapping,
                              hipStream_t st);
+hipError_t moe_launch_router_logits(const moe_shape_t& s, const void* x, const void* w_router,
+                                    float* logits, hipStream_t st);
+hipError_t moe_launch_bias_update(const moe_shape_t& s, const int32_t* counts, float gamma,
+                                  float* bias, hipStream_t st);
 hipError_t moe_launch_stats(const moe_shape_t& s, const int32_t* counts, const int32_t* ids,
                             const int32_t* plan, const int32_t* dest_row, const int32_t* mapping,
                             const int32_t* origin, const int32_t* err, int32_t capacity,

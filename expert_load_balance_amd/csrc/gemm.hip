@@ -21,12 +21,12 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lds_pipe.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-// plain vector (not HIP's struct uint4) so staging arrays promote to registers
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace moe::lds;
+
 
 constexpr int kThreads = 256;
 
@@ -186,69 +186,11 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 //    workgroups allow, each part writing a fp32 partial tile that
 //    fixup_kernel sums (parts in order) and finishes. No workgroup waits on
 //    another.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kTM = moe::kGemmTile, kTN = moe::kGemmTile, kTK = moe::kGemmStageK;
 constexpr int kOpBytes = kTM * kTK * 2;           // 32 KB: one operand of one stage
 constexpr int kSlotBytes = 2 * kOpBytes;          // A, then B
 constexpr int kCopiesWave = kOpBytes / 1024 / 4;  // 8 copies per operand per wave
 enum { kGateUp = 0, kDown = 1 };
-
-// Slot of K-chunk c (0..7) in LDS row r is c ^ swz(r): 8 consecutive rows
-// reading one chunk hit 8 distinct 16-byte groups of a 128-byte bank line,
-// 16 consecutive rows 16 distinct groups of a 256-byte line.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
-
-// Global -> LDS copy, 16 bytes per lane; lane l's bytes land at lds + 16 l.
-// Written as asm so the compiler's wait-count pass does not see the slots as
-// targets of outstanding loads (it would wait for every copy in flight before
-// each LDS read); the kernel orders them itself with explicit vmcnt waits and
-// barriers. m0 is reserved but unused by the compiler in these kernels; each
-// copy sets it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14)
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm()
-{
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (whose release
-// half would wait for every copy in flight). LDS reads are complete
-// (lgkmcnt(0)) before it; copies are covered by the explicit vmcnt waits.
-__device__ __forceinline__ void slot_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-template <typename T>
-__device__ __forceinline__ T* uni_ptr(T* p)
-{
-    const uint64_t u = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const char* p)
-{
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
 
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (both about
 // 1 ulp); the product is rounded to bf16 right after.

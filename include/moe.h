@@ -10,7 +10,8 @@
  *   moe_combine      gate-weighted gather back to tokens (phase d)
  *   moe_stats        maxvio / balancedness / capacity / remote statistics
  * and the two baselines the plan replaces: fixed-capacity dispatch
- * (moe_capacity_*) and static repacking (moe_repack).
+ * (moe_capacity_*) and static repacking (moe_repack); the router's scores
+ * (moe_router) and an assumed balancing-bias update (moe_bias_update).
  *
  * Sources (web pages, cited by title and section):
  *   [Primer]  "DeepEP-on-EFA Guidance, section 1: what is MoE" -- the
@@ -265,6 +266,29 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
                        const int32_t *d_mapping, const int32_t *d_origin, const int32_t *d_err,
                        double capacity_factor, void *d_ws, size_t ws_bytes, moe_stats_t *h_out,
                        int32_t *h_rank_loads, moe_stream_t stream);
+
+/* ---- Router scores and the balancing bias ---------------------------------
+ * [Primer] phase (a): the router scores every expert for every token. The
+ * pages do not print the router; it is read as a linear layer. */
+
+/* logits[t][e] = sum_h x[t][h] * W_r[e][h], accumulated in fp32 (bf16 x and
+ * W_r: MFMA; fp32: FMA in h order), written to d_logits, then exactly
+ * moe_route on those logits (same bias, tie and error rules).
+ *   d_x dtype[T][H]; d_w_router dtype[E][H]; d_bias float[E] or NULL;
+ *   d_logits float[T][E] out; d_ids int32[T][k] out; d_w float[T][k] out;
+ *   d_err int32[1] (bit 1: non-finite logit or bias). */
+moe_status_t moe_router(const moe_shape_t *shape, const void *d_x, const void *d_w_router,
+                        const float *d_bias, float *d_logits, int32_t *d_ids, float *d_w,
+                        int32_t *d_err, moe_stream_t stream);
+
+/* Balancing-bias update. NOT ON THE PAGES: [Interview] keeps a per-expert
+ * bias out of the gate but prints no update rule; this is the sign rule of
+ * auxiliary-loss-free balancing, an assumption. bias[e] += gamma if
+ * counts[e] < N/E, -= gamma if counts[e] > N/E (decided in integers from
+ * N - E*counts[e], N = T*k), one fp32 add. d_counts int32[E];
+ * d_bias float[E] in/out; gamma >= 0 and finite. */
+moe_status_t moe_bias_update(const moe_shape_t *shape, const int32_t *d_counts, float *d_bias,
+                             float gamma, moe_stream_t stream);
 
 /* ---- Baselines the equal-load plan replaces ------------------------------
  * [Hotspot] "Make expert capacity, overflow, and padding explicit": a fixed
