@@ -228,11 +228,11 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
 
     # the two row moves alone, back to back (their in-layer stage times also
     # hold a launch gap each)
-    t_perm = time_back_to_back(lambda: moe.moe_permute(shape, x, L.ids, L.eidx, L.plan, L.buf,
-                                                       L.dest_row, L.row_src, stream=stream))
+    t_perm = time_back_to_back(moe.bind(moe.moe_permute, shape, x, L.ids, L.eidx, L.plan, L.buf,
+                                        L.dest_row, L.row_src, stream=stream))
     sy = L.shared_y if shared else None
-    t_comb = time_back_to_back(lambda: moe.moe_combine(shape, L.y, L.dest_row, L.w, sy, L.out,
-                                                       stream=stream))
+    t_comb = time_back_to_back(moe.bind(moe.moe_combine, shape, L.y, L.dest_row, L.w, sy, L.out,
+                                        stream=stream))
 
     # the router's scores + top-k (x read once; W_r is E x H), back to back
     wr = synth.device_normal((E, H), synth.weight_std(H), w["seed"] * 10 + 9, act, dev)
@@ -240,8 +240,8 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     r_err = torch.zeros(1, dtype=torch.int32, device=dev)
-    t_router = time_back_to_back(lambda: moe.moe_router(shape, x, wr, bias, r_logits, r_ids, r_w,
-                                                        r_err, stream=stream))
+    t_router = time_back_to_back(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
+                                          r_err, stream=stream))
     router_bytes = (T * H + E * H) * (2 if dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
     del wr, r_logits
 

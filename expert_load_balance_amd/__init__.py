@@ -20,7 +20,7 @@ __all__ = [
     "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
-    "moe_repack", "capacity_shape", "moe_router", "moe_bias_update", "plan_tables",
+    "moe_repack", "capacity_shape", "moe_router", "moe_bias_update", "plan_tables", "bind",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -188,6 +188,47 @@ def _act_dtype(shape):
 def _ok(status, where):
     if status != 0:
         raise MoeError(status, where)
+
+
+class _Recorder:
+    """Stands in for the loaded library while bind() runs a wrapper: records
+    each C call and its marshalled arguments instead of making it."""
+
+    def __init__(self, lib):
+        self.lib, self.calls = lib, []
+
+    def __getattr__(self, name):
+        fn = getattr(self.lib, name)
+
+        def record(*args):
+            self.calls.append((name, fn, args))
+            return 0
+
+        return record
+
+
+def bind(wrapper, *args, **kwargs):
+    """Marshals the arguments of one launch-only wrapper call (moe_permute,
+    moe_router, ...) once and returns a callable that repeats only its C
+    call(s). For timing loops, where the per-call checks and ctypes
+    conversions would otherwise cost more host time than a small kernel takes
+    on the device. The tensors passed must stay alive while the callable is
+    used."""
+    global _lib
+    real = load()
+    rec = _Recorder(real)
+    _lib = rec
+    try:
+        wrapper(*args, **kwargs)
+    finally:
+        _lib = real
+    calls = tuple(rec.calls)
+
+    def run():
+        for name, fn, a in calls:
+            _ok(fn(*a), name)
+
+    return run
 
 
 def moe_status_str(status: int) -> str:

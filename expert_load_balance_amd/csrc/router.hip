@@ -11,8 +11,10 @@
 //
 // bf16 router GEMM: one 256-thread workgroup per 32 tokens; all E (<= 256)
 // experts in one tile of EB = E rounded up to 32/64/128/256 rows; K in
-// 64-deep stages of whole 128-byte row lines through a three-stage LDS ring
-// (global -> LDS copies, the same swizzle and waits as the expert GEMM);
+// 64-deep stages of whole 128-byte row lines through an LDS ring of up to
+// 120 KB (global -> LDS copies, the same swizzle and waits as the expert
+// GEMM): a stage is 8 KB for EB = 32, so 15 stages can be in flight -- the
+// few workgroups of a small router are bound by copy latency, not bytes;
 // v_mfma_f32_32x32x16_bf16 with wave w owning experts 64w .. 64w+63. The
 // fp32 logits are written once and read by the top-k kernel.
 #include "common.h"
@@ -25,8 +27,8 @@ using namespace moe::lds;
 constexpr int kThreads = 256;
 constexpr int kRM = 32;              // tokens per tile
 constexpr int kRK = 64;              // K per stage
-constexpr int kRSlots = 3;
 constexpr int kRA = kRM * kRK * 2;   // 4 KB of x per stage
+constexpr int kRRing = 120 * 1024;   // LDS for the ring
 
 template <int EB>
 __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(int T, int E, int H,
@@ -35,8 +37,10 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(int T, int E, 
                                                                   float* __restrict__ logits)
 {
     constexpr int kSlot = kRA + EB * kRK * 2;
+    constexpr int kRSlots = kRRing / kSlot < 16 ? kRRing / kSlot : 16;
     constexpr int kBCopies = EB / 32;          // B copy instructions per wave per stage
     constexpr int kPerStage = 1 + kBCopies;    // copies per wave per stage
+    static_assert((kRSlots - 2) * kPerStage < 64, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) char ring[kRSlots * kSlot];
 
     const int KT = H / kRK;
@@ -87,7 +91,9 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(int T, int E, 
     constexpr int kAhead = kRSlots - 1;
     for (int st = 0; st < kAhead && st < KT; ++st) copy_stage(st);
     for (int s = 0; s < KT; ++s) {
-        if (s + 1 < KT) wait_vm_lgkm<kPerStage>();  // stage s landed (s+1 may be in flight)
+        // stage s landed: the copies of stages s+1 .. s+kAhead-1 may stay in
+        // flight (all of them exist away from the end of K; near it, wait for all)
+        if (s + kAhead - 1 < KT) wait_vm_lgkm<(kAhead - 1) * kPerStage>();
         else wait_vm_lgkm<0>();
         slot_barrier();  // ... in every wave; and stage s-1's slot is free
         if (s + kAhead < KT) copy_stage(s + kAhead);

@@ -53,6 +53,11 @@ CASES = [
     (300, 128, 128, 8, moe.MOE_BF16, 0.0),
     (70, 64, 200, 8, moe.MOE_BF16, 1.0),
     (129, 512, 256, 8, moe.MOE_BF16, 0.2),
+    # K longer than the LDS ring (15 / 10 / 6 / 3 stages for 32 / 64 / 128 /
+    # 256 expert rows): the ring wraps several times
+    (40, 2048, 8, 2, moe.MOE_BF16, 0.0),
+    (50, 1024, 40, 4, moe.MOE_BF16, 0.2),
+    (33, 1280, 100, 4, moe.MOE_BF16, 0.0),
     (16, 64, 8, 2, moe.MOE_F32, 0.0),
     (50, 96, 24, 4, moe.MOE_F32, 0.4),
 ]
@@ -129,3 +134,28 @@ def test_bias_update_bit_exact_and_closed_loop():
     c = host(cnt)
     first = oracle.count(oracle.route(lg, bias, k)[0], E, 8)["counts"]
     assert c.max() < first.max()                     # the loop evens out demand
+
+
+def test_bind_repeats_the_same_call():
+    """bind() marshals a wrapper's arguments once; the callable it returns
+    makes the same C call(s), here on changed input data."""
+    T, H, E, k = 70, 256, 24, 4
+    shape = moe.Shape(T, H, E, k, 64, 1, 0, moe.MOE_BF16)
+    x = synth.device_normal((T, H), 1.0, 71, torch.bfloat16, DEV)
+    wr = synth.device_normal((E, H), synth.weight_std(H), 72, torch.bfloat16, DEV)
+    logits = alloc((T, E), torch.float32, DEV)
+    ids = alloc((T, k), torch.int32, DEV)
+    w = alloc((T, k), torch.float32, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    logits.fill_(float("nan"))
+    run = moe.bind(moe.moe_router, shape, x, wr, None, logits, ids, w, err)
+    torch.cuda.synchronize()
+    assert np.isnan(host(logits)).all()              # binding launched nothing
+    x.copy_(synth.device_normal((T, H), 1.0, 73, torch.bfloat16, DEV))
+    run()
+    torch.cuda.synchronize()
+    gl, gi, gw, e2 = run_router(shape, x, wr, None)
+    np.testing.assert_array_equal(host(logits), gl)
+    np.testing.assert_array_equal(host(ids), gi)
+    np.testing.assert_array_equal(host(w), gw)
+    assert e2 == 0
