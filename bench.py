@@ -240,10 +240,11 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     r_err = torch.zeros(1, dtype=torch.int32, device=dev)
+    r_ws = torch.empty(max(1, moe.moe_router_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     t_router = time_back_to_back(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
-                                          r_err, stream=stream))
+                                          r_err, r_ws, stream=stream))
     router_bytes = (T * H + E * H) * (2 if dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
-    del wr, r_logits
+    del wr, r_logits, r_ws
 
     cap_res = None
     if capacity_factor is not None:

@@ -20,7 +20,8 @@ __all__ = [
     "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
-    "moe_repack", "capacity_shape", "moe_router", "moe_bias_update", "plan_tables", "bind",
+    "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
+    "bind",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_schedule",
     "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "moe_capacity_rows",
     "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine", "moe_repack",
-    "moe_router", "moe_bias_update",
+    "moe_router_workspace_bytes", "moe_router", "moe_bias_update",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -136,7 +137,8 @@ def load():
         "moe_capacity_plan": (st, [_SP, ctypes.c_int32, _VP, _VP]),
         "moe_capacity_combine": (st, [_SP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_repack": (st, [_SP, _VP, _VP, _VP]),
-        "moe_router": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_router_workspace_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_router": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_bias_update": (st, [_SP, _VP, _VP, ctypes.c_float, _VP]),
     }
     for name, (res, args) in sig.items():
@@ -190,15 +192,23 @@ def _ok(status, where):
         raise MoeError(status, where)
 
 
+# entry points that only compute on the host (sizes, layouts, checks)
+_HOST_ONLY = frozenset(("moe_status_str", "moe_check_shape", "moe_plan_layout",
+                        "moe_workspace_bytes", "moe_router_workspace_bytes", "moe_capacity_rows"))
+
+
 class _Recorder:
     """Stands in for the loaded library while bind() runs a wrapper: records
-    each C call and its marshalled arguments instead of making it."""
+    each launching C call and its marshalled arguments instead of making it
+    (host-only queries go through)."""
 
     def __init__(self, lib):
         self.lib, self.calls = lib, []
 
     def __getattr__(self, name):
         fn = getattr(self.lib, name)
+        if name in _HOST_ONLY:
+            return fn
 
         def record(*args):
             self.calls.append((name, fn, args))
@@ -445,16 +455,24 @@ def moe_repack(shape, counts, mapping, stream=None):
 
 # ------------------------------------------------------------------ router --
 
-def moe_router(shape, x, w_router, bias, logits, ids, w, err, stream=None):
+def moe_router_workspace_bytes(shape: Shape) -> int:
+    return int(load().moe_router_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_router(shape, x, w_router, bias, logits, ids, w, err, ws=None, stream=None):
+    """ws: a uint8 device tensor of at least moe_router_workspace_bytes(shape)
+    bytes, or None when that is 0."""
     import torch
 
     act, i32 = _act_dtype(shape), torch.int32
+    need = moe_router_workspace_bytes(shape)
     args = (ctypes.byref(shape), _ptr(x, act, "x", shape.T * shape.H),
             _ptr(w_router, act, "w_router", shape.E * shape.H),
             _ptr(bias, torch.float32, "bias", shape.E, nullable=True),
             _ptr(logits, torch.float32, "logits", shape.T * shape.E),
             _ptr(ids, i32, "ids", shape.N), _ptr(w, torch.float32, "w", shape.N),
-            _ptr(err, i32, "err", 1), _stream(stream))
+            _ptr(err, i32, "err", 1), _ptr(ws, torch.uint8, "ws", need, nullable=need == 0),
+            ws.numel() if ws is not None else 0, _stream(stream))
     _ok(load().moe_router(*args), "moe_router")
 
 

@@ -192,16 +192,35 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
                                   as_stream(stream)));
 }
 
+size_t moe_router_workspace_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK) return 0;
+    return moe::router_ws_bytes(*shape);
+}
+
 moe_status_t moe_router(const moe_shape_t* shape, const void* d_x, const void* d_w_router,
                         const float* d_bias, float* d_logits, int32_t* d_ids, float* d_w,
-                        int32_t* d_err, moe_stream_t stream)
+                        int32_t* d_err, void* d_ws, size_t ws_bytes, moe_stream_t stream)
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
     const int64_t T = shape->T, N = T * shape->k;
     if (bad(d_x, T) || !d_w_router || bad(d_logits, T) || bad(d_ids, N) || bad(d_w, N) || !d_err)
         return MOE_EINVAL;
+    // W_r rows are addressed with 32-bit byte offsets
+    if (shape->dtype == MOE_BF16 && (int64_t)shape->E * shape->H * 2 >= (int64_t(1) << 32))
+        return MOE_EUNSUPPORTED;
+    const moe::RouterSplit sp = moe::router_split(*shape);
+    const size_t need = moe::router_ws_bytes(*shape);
+    if (need > 0 && (!d_ws || ws_bytes < need)) return MOE_EINVAL;
     hipStream_t hs = as_stream(stream);
+    if (sp.parts > 1) {
+        float* planes = static_cast<float*>(d_ws);
+        hipError_t e = moe_launch_router_logits(*shape, d_x, d_w_router, planes, hs);
+        if (e != hipSuccess) return MOE_EDEVICE;
+        return dev(moe_launch_route(*shape, planes, d_bias, d_ids, d_w, d_err, hs, sp.parts,
+                                    T * shape->E, d_logits));
+    }
     hipError_t e = moe_launch_router_logits(*shape, d_x, d_w_router, d_logits, hs);
     if (e != hipSuccess) return MOE_EDEVICE;
     return dev(moe_launch_route(*shape, d_logits, d_bias, d_ids, d_w, d_err, hs));

@@ -127,11 +127,46 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     return w;
 }
 
+// Router GEMM work split (bf16): TM tokens per workgroup tile and `parts`
+// K-ranges of kt_part 64-deep stages each. With parts > 1 every range writes
+// an fp32 partial plane [T][E] to the caller's workspace and the top-k step
+// sums the planes in range order, so the result does not depend on timing.
+// Small T splits K until about 256 workgroups run (each range keeps at least
+// 4 stages; at most 16 ranges).
+struct RouterSplit {
+    int tm, parts, kt_part;
+};
+inline RouterSplit router_split(const moe_shape_t& s)
+{
+    if (s.dtype != MOE_BF16 || s.T <= 0) return {32, 1, 0};
+    const int KT = s.H / kGemmStageK;
+    const int eb = s.E <= 32 ? 32 : s.E <= 64 ? 64 : s.E <= 128 ? 128 : 256;
+    const int tm = (eb >= 128 && s.T >= 64 * 128) ? 64 : 32;
+    const int tiles = (s.T + tm - 1) / tm;
+    int parts = 1;
+    if (tiles < 256) {
+        parts = (256 + tiles - 1) / tiles;
+        const int most = KT / 4 > 1 ? KT / 4 : 1;
+        if (parts > most) parts = most;
+        if (parts > 16) parts = 16;
+    }
+    const int ktp = (KT + parts - 1) / parts;
+    return {tm, (KT + ktp - 1) / ktp, ktp};
+}
+inline size_t router_ws_bytes(const moe_shape_t& s)
+{
+    const RouterSplit r = router_split(s);
+    return r.parts > 1 ? (size_t)r.parts * s.T * s.E * 4 : 0;
+}
+
 }  // namespace moe
 
 // ---- launchers (one per kernel family; all asynchronous on `st`) ----------
+// logits: `nplanes` fp32 planes [T][E], `plane` floats apart, summed in
+// plane order; with logits_out != NULL the sums are also written there.
 hipError_t moe_launch_route(const moe_shape_t& s, const float* logits, const float* bias,
-                            int32_t* ids, float* w, int32_t* err, hipStream_t st);
+                            int32_t* ids, float* w, int32_t* err, hipStream_t st,
+                            int nplanes = 1, int64_t plane = 0, float* logits_out = nullptr);
 hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
                             int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
                             char* ws, hipStream_t st);
@@ -158,6 +193,7 @@ hipError_t moe_launch_capacity_dispatch(const moe_shape_t& s, int cap, const int
 hipError_t moe_launch_capacity_plan(const moe_shape_t& s, int cap, int32_t* plan, hipStream_t st);
 hipError_t moe_launch_repack(const moe_shape_t& s, const int32_t* counts, int32_t* mapping,
                              hipStream_t st);
+// router_split(s).parts == 1: logits [T][E]; else the partial planes.
 hipError_t moe_launch_router_logits(const moe_shape_t& s, const void* x, const void* w_router,
                                     float* logits, hipStream_t st);
 hipError_t moe_launch_bias_update(const moe_shape_t& s, const int32_t* counts, float gamma,

@@ -9,14 +9,19 @@
 // but prints no update rule; the sign rule of auxiliary-loss-free balancing is
 // used: above-mean experts lose gamma, below-mean ones gain gamma.
 //
-// bf16 router GEMM: one 256-thread workgroup per 32 tokens; all E (<= 256)
-// experts in one tile of EB = E rounded up to 32/64/128/256 rows; K in
-// 64-deep stages of whole 128-byte row lines through an LDS ring of up to
-// 120 KB (global -> LDS copies, the same swizzle and waits as the expert
-// GEMM): a stage is 8 KB for EB = 32, so 15 stages can be in flight -- the
-// few workgroups of a small router are bound by copy latency, not bytes;
-// v_mfma_f32_32x32x16_bf16 with wave w owning experts 64w .. 64w+63. The
-// fp32 logits are written once and read by the top-k kernel.
+// bf16 router GEMM. A workgroup (4 waves) owns a tile of TM = 32 or 64 tokens
+// against all E (<= 256) experts, padded to EB = 32/64/128/256 rows, over one
+// K-range (moe::router_split). K runs in 64-deep stages of whole 128-byte row
+// lines through an LDS ring of up to 120 KB (global -> LDS copies, the same
+// swizzle and waits as the expert GEMM); a small stage (8 KB at TM = EB = 32)
+// leaves up to 15 stages in flight. The 32x32 output tiles are shared out so
+// that every wave issues MFMAs: with four or more tiles each wave owns whole
+// tiles; with fewer, the waves of a tile split its four 16-deep K slices and
+// add their accumulators in wave order at the end. A stage's fragments are
+// all read before its MFMAs, so LDS latency is paid once per stage.
+// v_mfma_f32_32x32x16_bf16 takes the W_r fragment as its first operand, so a
+// lane holds four consecutive experts of one token. With more than one
+// K-range each range writes an fp32 partial plane that the top-k step sums.
 #include "common.h"
 #include "lds_pipe.h"
 
@@ -25,105 +30,177 @@ namespace {
 using namespace moe::lds;
 
 constexpr int kThreads = 256;
-constexpr int kRM = 32;              // tokens per tile
 constexpr int kRK = 64;              // K per stage
-constexpr int kRA = kRM * kRK * 2;   // 4 KB of x per stage
 constexpr int kRRing = 120 * 1024;   // LDS for the ring
 
-template <int EB>
-__global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(int T, int E, int H,
+template <int TM, int EB>
+struct RouterTile {
+    static constexpr int kTB = TM / 32;                          // token blocks
+    static constexpr int kNB = EB / 32;                          // expert blocks
+    static constexpr int kTiles = kTB * kNB;                     // 32x32 output tiles
+    static constexpr int kKW = kTiles >= 4 ? 1 : 4 / kTiles;     // waves sharing a tile
+    static constexpr int kTW = kTiles >= 4 ? kTiles / 4 : 1;     // tiles per wave
+    static constexpr int kKK = 4 / kKW;                          // K slices per wave per stage
+    static constexpr int kNBStep = kTiles >= 4 ? 4 / kTB : 0;    // expert-block step of a wave's tiles
+    static constexpr int kA = TM * kRK * 2;                      // x bytes per stage
+    static constexpr int kSlot = kA + EB * kRK * 2;
+    static constexpr int kCopies = (TM + EB) / 32;               // copies per wave per stage
+    static constexpr int kSlots = kRRing / kSlot < 16 ? kRRing / kSlot : 16;
+    static_assert(kSlots >= 3 && (kSlots - 2) * kCopies < 64, "ring depth");
+};
+
+// wait until at most n (uniform, 0 <= n <= N) stages of C copies each remain in flight
+template <int C, int N>
+__device__ __forceinline__ void wait_stages(int n)
+{
+    if constexpr (N > 0) {
+        if (n >= N) {
+            wait_vm_lgkm<N * C>();
+            return;
+        }
+        wait_stages<C, N - 1>(n);
+    } else {
+        wait_vm_lgkm<0>();
+    }
+}
+
+template <int TM, int EB>
+__global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(int T, int E, int H, int KTp,
                                                                   const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ wr,
-                                                                  float* __restrict__ logits)
+                                                                  float* __restrict__ out)
 {
-    constexpr int kSlot = kRA + EB * kRK * 2;
-    constexpr int kRSlots = kRRing / kSlot < 16 ? kRRing / kSlot : 16;
-    constexpr int kBCopies = EB / 32;          // B copy instructions per wave per stage
-    constexpr int kPerStage = 1 + kBCopies;    // copies per wave per stage
-    static_assert((kRSlots - 2) * kPerStage < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) char ring[kRSlots * kSlot];
+    using P = RouterTile<TM, EB>;
+    __shared__ __attribute__((aligned(1024))) char ring[P::kSlots * P::kSlot];
 
     const int KT = H / kRK;
-    const int t0 = blockIdx.x * kRM;
+    const int t0 = blockIdx.x * TM;
+    const int s0 = blockIdx.y * KTp;
+    const int ns = min(KT, s0 + KTp) - s0;  // >= 1: the launcher makes no empty range
+    float* outp = out + (size_t)blockIdx.y * T * E;
     const int tid = threadIdx.x;
     const int wave = uni(tid >> 6), lane = tid & 63;
     const int fr = lane & 31, fh = lane >> 5;
     const uint32_t ring_u = (uint32_t)(uintptr_t)ring;
-    const char* xb = uni_ptr(reinterpret_cast<const char*>(x));
-    const char* wb = uni_ptr(reinterpret_cast<const char*>(wr));
+    const char* xb = uni_ptr(reinterpret_cast<const char*>(x) + (size_t)s0 * kRK * 2);
+    const char* wb = uni_ptr(reinterpret_cast<const char*>(wr) + (size_t)s0 * kRK * 2);
 
-    // copy sources: x rows 8 wave + lane / 8 of the tile (token clamped to
-    // T-1); W_r rows 8q + lane / 8 for q = wave + 4 i (expert clamped to E-1)
-    uint32_t aoff, boff[kBCopies];
-    {
-        const int r = 8 * wave + (lane >> 3);
+    // copy sources: tile row 32 i + 8 wave + lane / 8 (token clamped to T-1,
+    // expert to E-1), K-chunk lane % 8 stored at its swizzled slot
+    uint32_t aoff[P::kTB], boff[P::kNB];
+#pragma unroll
+    for (int i = 0; i < P::kTB; ++i) {
+        const int r = 32 * i + 8 * wave + (lane >> 3);
         const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
-        aoff = (uint32_t)min(t0 + r, T - 1) * (uint32_t)H * 2u + ch;
+        aoff[i] = (uint32_t)min(t0 + r, T - 1) * (uint32_t)H * 2u + ch;
     }
 #pragma unroll
-    for (int i = 0; i < kBCopies; ++i) {
-        const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    for (int i = 0; i < P::kNB; ++i) {
+        const int r = 32 * i + 8 * wave + (lane >> 3);
         const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
         boff[i] = (uint32_t)min(r, E - 1) * (uint32_t)H * 2u + ch;
     }
-    auto copy_stage = [&](int st) {
-        const uint32_t slot = ring_u + (uint32_t)(st % kRSlots) * kSlot;
-        copy16(xb + st * (kRK * 2), aoff, slot + wave * 1024);
+    auto copy_stage = [&](int j) {
+        const uint32_t slot = ring_u + (uint32_t)(j % P::kSlots) * P::kSlot;
 #pragma unroll
-        for (int i = 0; i < kBCopies; ++i)
-            copy16(wb + st * (kRK * 2), boff[i], slot + kRA + wave * 1024 + i * 4096);
+        for (int i = 0; i < P::kTB; ++i) copy16(xb + j * (kRK * 2), aoff[i], slot + i * 4096 + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < P::kNB; ++i)
+            copy16(wb + j * (kRK * 2), boff[i], slot + P::kA + i * 4096 + wave * 1024);
     };
-    // fragments: x rows fr; W_r rows 64 wave + 32 j + fr
-    uint32_t fa[4], fb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t ch = (uint32_t)(((2 * kk + fh) ^ swz(fr)) * 16);
-        fa[kk] = (uint32_t)fr * 128u + ch;
-        fb[kk] = (uint32_t)kRA + (uint32_t)(64 * wave + fr) * 128u + ch;
-    }
-    const int nb = min(2, max(0, (EB - 64 * wave) / 32));  // this wave's 32-expert blocks
 
-    f32x16 acc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
-    constexpr int kAhead = kRSlots - 1;
-    for (int st = 0; st < kAhead && st < KT; ++st) copy_stage(st);
-    for (int s = 0; s < KT; ++s) {
-        // stage s landed: the copies of stages s+1 .. s+kAhead-1 may stay in
-        // flight (all of them exist away from the end of K; near it, wait for all)
-        if (s + kAhead - 1 < KT) wait_vm_lgkm<(kAhead - 1) * kPerStage>();
-        else wait_vm_lgkm<0>();
-        slot_barrier();  // ... in every wave; and stage s-1's slot is free
-        if (s + kAhead < KT) copy_stage(s + kAhead);
-        const char* slot = ring + (s % kRSlots) * kSlot;
-        if (nb > 0) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 af = lds_frag(slot + fa[kk]);
-                const bf16x8 b0 = lds_frag(slot + fb[kk]);
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af, acc[0], 0, 0, 0);
-                if (nb > 1) {
-                    const bf16x8 b1 = lds_frag(slot + fb[kk] + 32 * 128);
-                    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af, acc[1], 0, 0, 0);
-                }
-            }
-        }
+    // this wave's work: token block tb, expert blocks nb0 + i * kNBStep
+    // (i < kTW), K slices kk0 .. kk0 + kKK - 1 of every stage
+    int tb, nb0, kk0;
+    if constexpr (P::kTiles >= 4) {
+        tb = wave % P::kTB;
+        nb0 = wave / P::kTB;
+        kk0 = 0;
+    } else {
+        const int tile = wave / P::kKW;
+        tb = tile % P::kTB;
+        nb0 = tile / P::kTB;
+        kk0 = (wave % P::kKW) * P::kKK;
     }
-    // acc[j][4 g4 + q]: token t0 + (lane & 31), expert 64 wave + 32 j + 8 g4 + 4 (lane >> 5) + q
-    const int t = t0 + fr;
-    if (t < T) {
+    uint32_t fa[P::kKK], fb[P::kKK];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int kk = 0; kk < P::kKK; ++kk) {
+        const uint32_t ch = (uint32_t)(((2 * (kk0 + kk) + fh) ^ swz(fr)) * 16);
+        fa[kk] = (uint32_t)(32 * tb + fr) * 128u + ch;
+        fb[kk] = (uint32_t)P::kA + (uint32_t)(32 * nb0 + fr) * 128u + ch;
+    }
+
+    f32x16 acc[P::kTW];
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
+    for (int i = 0; i < P::kTW; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+    constexpr int kAhead = P::kSlots - 1;
+    for (int j = 0; j < kAhead && j < ns; ++j) copy_stage(j);
+    for (int j = 0; j < ns; ++j) {
+        // stage j landed; stages j+1 .. (at most kAhead-1 of them) may stay in flight
+        wait_stages<P::kCopies, kAhead - 1>(min(kAhead - 1, ns - 1 - j));
+        slot_barrier();  // ... in every wave; and stage j-1's slot is free
+        if (j + kAhead < ns) copy_stage(j + kAhead);
+        const char* slot = ring + (j % P::kSlots) * P::kSlot;
+        bf16x8 af[P::kKK], bfr[P::kKK][P::kTW];
+#pragma unroll
+        for (int kk = 0; kk < P::kKK; ++kk) {
+            af[kk] = lds_frag(slot + fa[kk]);
+#pragma unroll
+            for (int i = 0; i < P::kTW; ++i)
+                bfr[kk][i] = lds_frag(slot + fb[kk] + i * P::kNBStep * 32 * 128);
+        }
+#pragma unroll
+        for (int kk = 0; kk < P::kKK; ++kk)
+#pragma unroll
+            for (int i = 0; i < P::kTW; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][i], af[kk], acc[i], 0, 0, 0);
+    }
+
+    bool lead = true;
+    if constexpr (P::kKW > 1) {
+        // the waves of a tile add their K-slice accumulators in wave order
+        slot_barrier();  // every wave is done with the ring
+        float4* red = reinterpret_cast<float4*>(ring);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            red[(wave * 64 + lane) * 4 + q] =
+                make_float4(acc[0][4 * q], acc[0][4 * q + 1], acc[0][4 * q + 2], acc[0][4 * q + 3]);
+        __syncthreads();
+        lead = wave % P::kKW == 0;
+        if (lead) {
+#pragma unroll
+            for (int w2 = 1; w2 < P::kKW; ++w2)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int e = 64 * wave + 32 * j + 8 * g4 + 4 * fh + q;
-                    if (j < nb && e < E) logits[(size_t)t * E + e] = acc[j][g4 * 4 + q];
+                    const float4 v = red[((wave + w2) * 64 + lane) * 4 + q];
+                    acc[0][4 * q] += v.x;
+                    acc[0][4 * q + 1] += v.y;
+                    acc[0][4 * q + 2] += v.z;
+                    acc[0][4 * q + 3] += v.w;
                 }
+        }
     }
+    // acc[i][4 g4 + q]: token t0 + 32 tb + fr, expert 32 (nb0 + i kNBStep) + 8 g4 + 4 fh + q
+    const int t = t0 + 32 * tb + fr;
+    if (!lead || t >= T) return;
+    const bool vec = (E & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < P::kTW; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int e0 = 32 * (nb0 + i * P::kNBStep) + 8 * g4 + 4 * fh;
+            float* o = outp + (size_t)t * E + e0;
+            if (vec && e0 + 3 < E) {
+                *reinterpret_cast<float4*>(o) = make_float4(acc[i][4 * g4], acc[i][4 * g4 + 1],
+                                                            acc[i][4 * g4 + 2], acc[i][4 * g4 + 3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (e0 + q < E) o[q] = acc[i][4 * g4 + q];
+            }
+        }
 }
 
 // fp32 router (small shapes): one thread per (token, expert), fp32 FMA in h order.
@@ -155,22 +232,38 @@ __global__ __launch_bounds__(kThreads) void bias_update_kernel(int E, int64_t N,
 
 }  // namespace
 
+namespace {
+
+template <int TM, int EB>
+void launch_router(const moe_shape_t& s, const moe::RouterSplit& sp, const uint16_t* x,
+                   const uint16_t* w, float* out, hipStream_t st)
+{
+    const dim3 grid((s.T + TM - 1) / TM, sp.parts);
+    router_gemm_kernel<TM, EB><<<grid, kThreads, 0, st>>>(s.T, s.E, s.H, sp.kt_part, x, w, out);
+}
+
+template <int TM>
+void launch_router_eb(const moe_shape_t& s, const moe::RouterSplit& sp, const uint16_t* x,
+                      const uint16_t* w, float* out, hipStream_t st)
+{
+    if (s.E <= 32) launch_router<TM, 32>(s, sp, x, w, out, st);
+    else if (s.E <= 64) launch_router<TM, 64>(s, sp, x, w, out, st);
+    else if (s.E <= 128) launch_router<TM, 128>(s, sp, x, w, out, st);
+    else launch_router<TM, 256>(s, sp, x, w, out, st);
+}
+
+}  // namespace
+
 hipError_t moe_launch_router_logits(const moe_shape_t& s, const void* x, const void* w_router,
                                     float* logits, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
     if (s.dtype == MOE_BF16) {
-        const int grid = (s.T + kRM - 1) / kRM;
+        const moe::RouterSplit sp = moe::router_split(s);
         const uint16_t* xv = static_cast<const uint16_t*>(x);
         const uint16_t* wv = static_cast<const uint16_t*>(w_router);
-        if (s.E <= 32)
-            router_gemm_kernel<32><<<grid, kThreads, 0, st>>>(s.T, s.E, s.H, xv, wv, logits);
-        else if (s.E <= 64)
-            router_gemm_kernel<64><<<grid, kThreads, 0, st>>>(s.T, s.E, s.H, xv, wv, logits);
-        else if (s.E <= 128)
-            router_gemm_kernel<128><<<grid, kThreads, 0, st>>>(s.T, s.E, s.H, xv, wv, logits);
-        else
-            router_gemm_kernel<256><<<grid, kThreads, 0, st>>>(s.T, s.E, s.H, xv, wv, logits);
+        if (sp.tm == 64) launch_router_eb<64>(s, sp, xv, wv, logits, st);
+        else launch_router_eb<32>(s, sp, xv, wv, logits, st);
     } else {
         const int64_t n = (int64_t)s.T * s.E;
         router_f32_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(

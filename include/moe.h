@@ -271,15 +271,25 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
  * [Primer] phase (a): the router scores every expert for every token. The
  * pages do not print the router; it is read as a linear layer. */
 
+/* Device workspace moe_router needs for this shape, in bytes: 0 when one
+ * K-range covers H (fp32, or enough token tiles to fill the GPU); else
+ * parts * T * E * 4 for the per-range fp32 partial logits. 0 on a bad shape. */
+size_t moe_router_workspace_bytes(const moe_shape_t *shape);
+
 /* logits[t][e] = sum_h x[t][h] * W_r[e][h], accumulated in fp32 (bf16 x and
- * W_r: MFMA; fp32: FMA in h order), written to d_logits, then exactly
- * moe_route on those logits (same bias, tie and error rules).
+ * W_r: MFMA; where H is split into K-ranges, the ranges' fp32 partial sums
+ * are added in range order, so results are the same on every call; fp32: FMA
+ * in h order), written to d_logits, then exactly moe_route on those logits
+ * (same bias, tie and error rules).
  *   d_x dtype[T][H]; d_w_router dtype[E][H]; d_bias float[E] or NULL;
  *   d_logits float[T][E] out; d_ids int32[T][k] out; d_w float[T][k] out;
- *   d_err int32[1] (bit 1: non-finite logit or bias). */
+ *   d_err int32[1] (bit 1: non-finite logit or bias);
+ *   d_ws: moe_router_workspace_bytes(shape) bytes of device scratch (may be
+ *   NULL when that is 0), ws_bytes its size; MOE_EINVAL if too small.
+ * bf16 needs E * H * 2 < 2^32 (MOE_EUNSUPPORTED otherwise). */
 moe_status_t moe_router(const moe_shape_t *shape, const void *d_x, const void *d_w_router,
                         const float *d_bias, float *d_logits, int32_t *d_ids, float *d_w,
-                        int32_t *d_err, moe_stream_t stream);
+                        int32_t *d_err, void *d_ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Balancing-bias update. NOT ON THE PAGES: [Interview] keeps a per-expert
  * bias out of the gate but prints no update rule; this is the sign rule of

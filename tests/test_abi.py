@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -103,3 +103,29 @@ def test_capacity_rows_and_rejections(lib):
     assert lib.moe_capacity_combine(ctypes.byref(s), 5, None, p, p, None, p, None) == 1
     assert lib.moe_repack(ctypes.byref(s), None, p, None) == 1
     assert lib.moe_repack(ctypes.byref(s.replace(E=0)), p, p, None) == 1
+
+
+def test_router_workspace_and_rejections(lib):
+    """The router's K-split needs parts * T * E * 4 bytes of partial logits
+    (at most 16 parts); none for fp32 or when the token tiles alone fill the
+    GPU. Too small a workspace and too wide a W_r are rejected before launch."""
+    bf = moe.Shape(2048, 4096, 8, 2, 64, 1, 0, moe.MOE_BF16)
+    for T, H, E in [(2048, 4096, 8), (64, 4096, 128), (4096, 2048, 128), (8192, 7168, 256),
+                    (1, 64, 8), (100, 256, 64)]:
+        s = bf.replace(T=T, H=H, E=E, k=2)
+        b = moe.moe_router_workspace_bytes(s)
+        assert b % (T * E * 4) == 0 and b // (T * E * 4) in (0,) + tuple(range(2, 17)), (T, H, E)
+    assert moe.moe_router_workspace_bytes(bf.replace(T=64)) > 0            # 2 tiles: split K
+    assert moe.moe_router_workspace_bytes(bf.replace(T=1 << 16)) == 0      # 2048 tiles
+    assert moe.moe_router_workspace_bytes(bf.replace(H=128)) == 0          # 2 stages: no split
+    assert moe.moe_router_workspace_bytes(bf.replace(dtype=moe.MOE_F32)) == 0
+    assert moe.moe_router_workspace_bytes(bf.replace(R=3)) == 0
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    s = bf.replace(T=64)
+    need = moe.moe_router_workspace_bytes(s)
+    assert lib.moe_router(ctypes.byref(s), p, p, None, p, p, p, p, p, need - 1, None) == 1
+    assert lib.moe_router(ctypes.byref(s), p, p, None, p, p, p, p, None, need, None) == 1
+    assert lib.moe_router(ctypes.byref(s), p, p, None, p, p, p, None, p, need, None) == 1
+    wide = bf.replace(T=1, k=1, E=256, H=1 << 23, F=64)                  # E*H*2 == 2^32
+    assert moe.moe_check_shape(wide) == 0
+    assert lib.moe_router(ctypes.byref(wide), p, p, None, p, p, p, p, p, 1 << 40, None) == 2

@@ -188,7 +188,10 @@ def test_route_ties_and_signed_zero():
     lg = (rng.integers(-3, 4, size=(T, E)) * 0.5).astype(np.float32)
     lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, -0.0, 0.0).astype(np.float32)
     bias = (rng.integers(-1, 2, size=E) * 0.5).astype(np.float32)
-    for e_, k_ in [(64, 8), (13, 5), (256, 64), (200, 8), (2, 2)]:
+    # every group width of the top-k kernel: 1, 2, 4, 8, 16, 32 lanes per
+    # token, and 64 lanes with 1 to 4 experts per lane
+    for e_, k_ in [(64, 8), (13, 5), (256, 64), (200, 8), (2, 2), (32, 8), (20, 3), (8, 2),
+                   (5, 4), (4, 1), (1, 1), (128, 8), (150, 6)]:
         shape = moe.Shape(T, 64, e_, k_, 64, 1, 0, moe.MOE_BF16)
         lgx = np.ascontiguousarray(np.tile(lg, (1, 4))[:, :e_])
         bx = np.ascontiguousarray(np.tile(bias, 4)[:e_])

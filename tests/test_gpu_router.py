@@ -33,7 +33,8 @@ def run_router(shape, x, wr, bias):
     ids = alloc((shape.T, shape.k), torch.int32, DEV)
     w = alloc((shape.T, shape.k), torch.float32, DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    moe.moe_router(shape, x, wr, bias, logits, ids, w, err)
+    ws = alloc((moe.moe_router_workspace_bytes(shape),), torch.uint8, DEV)
+    moe.moe_router(shape, x, wr, bias, logits, ids, w, err, ws)
     torch.cuda.synchronize()
     return host(logits), host(ids), host(w), int(err.item())
 
@@ -139,8 +140,9 @@ def test_bias_update_bit_exact_and_closed_loop():
 def test_bind_repeats_the_same_call():
     """bind() marshals a wrapper's arguments once; the callable it returns
     makes the same C call(s), here on changed input data."""
-    T, H, E, k = 70, 256, 24, 4
+    T, H, E, k = 70, 1024, 24, 4
     shape = moe.Shape(T, H, E, k, 64, 1, 0, moe.MOE_BF16)
+    assert moe.moe_router_workspace_bytes(shape) > 0  # K split into partial planes
     x = synth.device_normal((T, H), 1.0, 71, torch.bfloat16, DEV)
     wr = synth.device_normal((E, H), synth.weight_std(H), 72, torch.bfloat16, DEV)
     logits = alloc((T, E), torch.float32, DEV)
@@ -148,7 +150,8 @@ def test_bind_repeats_the_same_call():
     w = alloc((T, k), torch.float32, DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     logits.fill_(float("nan"))
-    run = moe.bind(moe.moe_router, shape, x, wr, None, logits, ids, w, err)
+    ws = alloc((moe.moe_router_workspace_bytes(shape),), torch.uint8, DEV)
+    run = moe.bind(moe.moe_router, shape, x, wr, None, logits, ids, w, err, ws)
     torch.cuda.synchronize()
     assert np.isnan(host(logits)).all()              # binding launched nothing
     x.copy_(synth.device_normal((T, H), 1.0, 73, torch.bfloat16, DEV))
