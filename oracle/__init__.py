@@ -85,6 +85,7 @@ def _load():
         lib.orc_repack.restype = None
         lib.orc_router_logits.restype = None
         lib.orc_bias_update.restype = None
+        lib.orc_slot_sources.restype = None
         _lib = lib
     return _lib
 
@@ -295,3 +296,57 @@ def ledgers(counts, cap):
     """Per-expert processed / overflow / padding vectors at capacity cap."""
     c = np.asarray(counts, dtype=np.int64)
     return np.minimum(c, cap), np.maximum(c - cap, 0), np.maximum(cap - c, 0)
+
+
+def slot_sources(pl, S):
+    """Weight source of every plan segment under S replica slots per rank:
+    src [R, 2n] int32 = slot index j, -1 for the home expert's weights, -2
+    past the rank's segment count. (orc_slot_sources)"""
+    R, n = pl["slot_expert"].shape
+    src = np.empty((R, 2 * n), np.int32)
+    _load().orc_slot_sources(R * n, R, int(S), _p(_i32(pl["seg_num"]), I32P),
+                             _p(_i32(pl["seg_expert"]), I32P), _p(_i32(pl["slot_expert"]), I32P),
+                             _p(src, I32P))
+    return src
+
+
+def prefetch(pl, S, w_gate, w_up, w_down):
+    """The replica slot pool: pool[r, j] holds copies of (W_gate, W_up, W_down)
+    of rank r's j-th replica expert, flattened, for j < min(S, n) and
+    slot_expert[r, j] >= 0; slots without an expert stay zero.
+    w_gate, w_up: [E, F, H]; w_down: [E, H, F] (any dtype). -> [R, Sm, 3, F*H]."""
+    R, n = pl["slot_expert"].shape
+    Sm = min(int(S), n)
+    E, F, H = w_gate.shape
+    pool = np.zeros((R, Sm, 3, F * H), w_gate.dtype)
+    for r in range(R):
+        for j in range(Sm):
+            e = int(pl["slot_expert"][r, j])
+            if e >= 0:
+                pool[r, j, 0] = w_gate[e].ravel()
+                pool[r, j, 1] = w_up[e].ravel()
+                pool[r, j, 2] = w_down[e].ravel()
+    return pool
+
+
+def slot_ffn(buf, pl, S, w_gate, w_up, w_down, pool):
+    """The expert FFN of every buffer row, segment by segment, with each
+    segment's weights taken from its source (slot_sources): home weights or
+    pool[r, j] (whatever that slot holds). buf [N, H] -> y [N, H] double."""
+    R, n = pl["slot_expert"].shape
+    E, F, H = w_gate.shape
+    src = slot_sources(pl, S)
+    y = np.zeros((buf.shape[0], H))
+    for r in range(R):
+        for i in range(int(pl["seg_num"][r])):
+            e, row, cnt = (int(pl[t][r, i]) for t in ("seg_expert", "seg_row", "seg_cnt"))
+            if cnt == 0:
+                continue
+            j = int(src[r, i])
+            if j >= 0:
+                wg, wu, wd = (pool[r, j, q].reshape(shp) for q, shp in
+                              ((0, (F, H)), (1, (F, H)), (2, (H, F))))
+            else:
+                wg, wu, wd = w_gate[e], w_up[e], w_down[e]
+            y[row:row + cnt] = ffn_rows(buf[row:row + cnt], wg, wu, wd)
+    return y

@@ -26,8 +26,9 @@
  *            and editor's note): per-expert bias kept out of the gate.
  *
  * One function follows no page: orc_bias_update (an assumed update rule,
- * labelled as such below). The router's linear layer and the fixed-capacity
- * and repacking rules are readings of the pages, also labelled.
+ * labelled as such below). The router's linear layer, the fixed-capacity and
+ * repacking rules and the replica slot assignment are readings of the pages,
+ * also labelled.
  *
  * Every function with a pin in tests/ is pinned there; none is "parity
  * unpinned".
@@ -421,6 +422,43 @@ void orc_repack(int E, int R, const int32_t *counts, int32_t *mapping)
     free(order);
     free(load);
     free(held);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Replica weight slots: [MoonEP] paragraph 3 -- the planner's redundant
+ * expert copies are prefetched into a fixed number of weight slots per rank;
+ * paragraph 4 -- as many slots as experts per rank make every expert the
+ * grouped GEMM touches local, and a few slots usually suffice.
+ * Reading: rank r's replica experts take its slots in the order of
+ * slot_expert[r] (ascending expert id); slot j < S holds a copy of that
+ * expert's three projections. Segment i of rank r (expert e) reads
+ *   - the home weights when r is e's home rank (e / n == r),
+ *   - slot j when e is rank r's j-th replica expert and j < S,
+ *   - the home weights otherwise (a non-local read; orc_stats counts its
+ *     rows as non-local).
+ * src[r][i] = j, or -1 for the home weights; -2 for i >= seg_num[r].        */
+void orc_slot_sources(int E, int R, int S, const int32_t *seg_num, const int32_t *seg_expert,
+                      const int32_t *slot_expert, int32_t *src)
+{
+    int n = E / R;
+    for (int r = 0; r < R; ++r) {
+        for (int i = 0; i < 2 * n; ++i) {
+            int32_t *o = src + (size_t)r * 2 * n + i;
+            if (i >= seg_num[r]) {
+                *o = -2;
+                continue;
+            }
+            int e = seg_expert[(size_t)r * 2 * n + i];
+            *o = -1;
+            if (e / n == r) continue;
+            for (int q = 0; q < n && q < S; ++q) {
+                if (slot_expert[(size_t)r * n + q] == e) {
+                    *o = q;
+                    break;
+                }
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -604,3 +604,108 @@ def test_bias_update_closed_loop_reduces_maxvio():
         first = mv if first is None else first
         bias = oracle.bias_update(c, bias, 0.01)
     assert first > 0.8 and mv < 0.25
+
+
+# ---- replica weight slots (MoonEP news article, paragraphs 3-4) ----------
+
+def _fixture_plan():
+    c = oracle.count(_pairs(FIX), 8, 4)["counts"]
+    assert c.tolist() == [9, 6, 5, 4, 3, 2, 2, 1]
+    return oracle.plan(c, 4)
+
+
+def test_fixture_slot_sources():
+    """The derived fixture plan: ranks 0, 2, 3 each hold one replica (expert
+    2, 0, 0), so with S >= 1 those segments read slot 0 and every other
+    segment the home weights; with S = 0 every segment reads home weights."""
+    pl = _fixture_plan()
+    assert pl["slot_expert"].tolist() == DER["slot_expert"]
+    want = [[-1, -1, 0, -2], [-1, -1, -2, -2], [0, -1, -1, -2], [0, -1, -1, -2]]
+    assert oracle.slot_sources(pl, 2).tolist() == want
+    assert oracle.slot_sources(pl, 1).tolist() == want
+    no = [[-1 if v != -2 else -2 for v in row] for row in want]
+    assert oracle.slot_sources(pl, 0).tolist() == no
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_slot_sources_invariants(seed):
+    """Every local slot is read by exactly the segment of its expert; home
+    segments never read a slot; with S >= n every replica segment is local
+    (the slots = experts-per-rank guarantee); the rows read from home weights
+    by replica segments are exactly the stats' non-local rows."""
+    rng = np.random.default_rng(seed)
+    R = int(rng.choice([2, 4, 8]))
+    n = int(rng.integers(1, 5))
+    E, k, T = R * n, min(R * n, int(rng.integers(1, 4))), int(rng.integers(20, 200))
+    lg = synth.router_logits(T, E, seed + 30)
+    bias = synth.zipf_bias(E, float(rng.uniform(0, 2)), seed + 30).astype(np.float32)
+    ids, _, _ = oracle.route(lg, bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    for S in range(0, n + 2):
+        src = oracle.slot_sources(pl, S)
+        nonlocal_rows = 0
+        for r in range(R):
+            used = []
+            for i in range(2 * n):
+                if i >= pl["seg_num"][r]:
+                    assert src[r, i] == -2
+                    continue
+                e = pl["seg_expert"][r, i]
+                if e // n == r:
+                    assert src[r, i] == -1
+                elif src[r, i] >= 0:
+                    assert pl["slot_expert"][r, src[r, i]] == e and src[r, i] < S
+                    used.append(int(src[r, i]))
+                else:
+                    assert S < n
+                    nonlocal_rows += int(pl["seg_cnt"][r, i])
+            assert sorted(used) == list(range(min(S, int(pl["slots_needed"][r]))))
+        st = oracle.stats(ids, c["counts"], R, S=S, pl=pl)
+        assert st["nonlocal_rows"] == nonlocal_rows
+
+
+def test_fixture_prefetch_pool():
+    """The pool holds bit-exact copies of the slot experts' three projections
+    (rank 0 slot 0: expert 2; ranks 2 and 3 slot 0: expert 0); rank 1 has no
+    replica and its slot stays empty."""
+    pl = _fixture_plan()
+    rng = np.random.default_rng(5)
+    E, F, H = 8, 6, 4
+    wg = rng.standard_normal((E, F, H)).astype(np.float32)
+    wu = rng.standard_normal((E, F, H)).astype(np.float32)
+    wd = rng.standard_normal((E, H, F)).astype(np.float32)
+    pool = oracle.prefetch(pl, 2, wg, wu, wd)
+    assert pool.shape == (4, 2, 3, F * H)
+    for r, e in ((0, 2), (2, 0), (3, 0)):
+        assert np.array_equal(pool[r, 0, 0], wg[e].ravel())
+        assert np.array_equal(pool[r, 0, 1], wu[e].ravel())
+        assert np.array_equal(pool[r, 0, 2], wd[e].ravel())
+    assert not pool[1].any() and not pool[:, 1].any()
+
+
+def test_slot_ffn_reads_the_slots():
+    """With the prefetched pool the slot-reading FFN equals the home-weight
+    FFN exactly; doubling W_down in one slot doubles exactly the rows of the
+    segment that reads it (the FFN is linear in W_down) and nothing else."""
+    pl = _fixture_plan()
+    rng = np.random.default_rng(6)
+    E, F, H = 8, 6, 4
+    wg = rng.standard_normal((E, F, H))
+    wu = rng.standard_normal((E, F, H))
+    wd = rng.standard_normal((E, H, F))
+    buf = rng.standard_normal((32, H))
+    pool = oracle.prefetch(pl, 2, wg, wu, wd)
+    home = oracle.slot_ffn(buf, pl, 0, wg, wu, wd, pool)
+    y = oracle.slot_ffn(buf, pl, 2, wg, wu, wd, pool)
+    assert np.array_equal(y, home)
+    for r in range(4):
+        for i in range(int(pl["seg_num"][r])):
+            e, row, cnt = (int(pl[t][r, i]) for t in ("seg_expert", "seg_row", "seg_cnt"))
+            assert np.array_equal(home[row:row + cnt], oracle.ffn_rows(buf[row:row + cnt], wg[e],
+                                                                       wu[e], wd[e]))
+    pool2 = pool.copy()
+    pool2[2, 0, 2] *= 2.0                        # rank 2's slot: expert 0, rows 16..18
+    y2 = oracle.slot_ffn(buf, pl, 2, wg, wu, wd, pool2)
+    assert np.array_equal(y2[16:19], 2.0 * y[16:19])
+    assert np.array_equal(np.delete(y2, [16, 17, 18], 0), np.delete(y, [16, 17, 18], 0))
