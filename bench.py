@@ -246,6 +246,38 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     router_bytes = (T * H + E * H) * (2 if dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
     del wr, r_logits, r_ws
 
+    # replica slots: the prefetch copy of every filled slot, and the grouped
+    # GEMM by plan segment reading them, beside the expert-grouped GEMM
+    slots = None
+    pool_bytes = moe.moe_pool_bytes(shape)
+    if pool_bytes:
+        pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        n = E // R
+        se = moe.plan_tables(L.plan, shape)["slot_expert"].cpu().numpy()[:, :min(S, n)]
+        filled = int((se >= 0).sum())
+        t_pref = time_back_to_back(moe.bind(moe.moe_prefetch_replicas, shape, L.plan, *wts, pool,
+                                            stream=stream), reps=10)
+        t_gs = time_back_to_back(moe.bind(moe.moe_grouped_gemm_slots, shape, L.buf, L.plan, *wts,
+                                          pool, L.y, L.ws, stream=stream), reps=10)
+        t_ge = time_back_to_back(moe.bind(moe.moe_grouped_gemm, shape, L.buf, L.plan, *wts, L.y,
+                                          L.ws, stream=stream), reps=10)
+        moved = 2.0 * filled * 3 * F * H * (2 if dtype == moe.MOE_BF16 else 4)  # read + write
+        # the whole layer with the prefetch and the slot-reading GEMM
+        for _ in range(2):
+            L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
+        torch.cuda.synchronize()
+        t_layer = (time.perf_counter() - t1) / steps
+        slots = dict(S=S, slots_filled=filled, pool_gb=pool_bytes / 1e9,
+                     prefetch_us=t_pref * 1e6, prefetch_gbs=moved / t_pref / 1e9,
+                     prefetch_hbm_frac=moved / t_pref / 1e9 / PEAK_HBM_GBS,
+                     gemm_slots_ms=t_gs * 1e3, gemm_experts_ms=t_ge * 1e3,
+                     layer_tokens_per_s=T / t_layer, layer_ms_per_step=t_layer * 1e3)
+        del pool
+
     cap_res = None
     if capacity_factor is not None:
         cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
@@ -271,7 +303,11 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
         permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res,
+        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res, slots=slots,
+        # weight-streaming view of the two GEMM calls: every active expert's
+        # three projections read once (the bound when rows per expert are few)
+        gemm_weight_hbm_frac=st["active_experts"] * 3.0 * F * H * b / (gu_s + dn_s) / 1e9
+        / PEAK_HBM_GBS,
         router={"us": t_router * 1e6, "tflops": 2.0 * T * E * H / t_router / 1e12,
                 "hbm_frac": router_bytes / t_router / 1e9 / PEAK_HBM_GBS})
     return res
@@ -351,6 +387,8 @@ def main():
                  "ranks_over_slots": st["ranks_over_slots"]},
         "fixed_capacity_baseline": r["capacity"],
         "router_scores_topk": r["router"],
+        "replica_slots": r["slots"],
+        "gemm_weight_hbm_frac": r["gemm_weight_hbm_frac"],
     }
     if not args.no_cpu_baseline:
         # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
@@ -373,6 +411,10 @@ def main():
                 "permute_hbm_frac": round(q["permute_hbm_frac"], 4),
                 "combine_hbm_frac": round(q["combine_hbm_frac"], 4),
                 "router_us": round(q["router"]["us"], 2),
+                "gemm_weight_hbm_frac": round(q["gemm_weight_hbm_frac"], 4),
+                "replica_slots": None if q["slots"] is None else {
+                    k_: round(v_, 3) if isinstance(v_, float) else v_
+                    for k_, v_ in q["slots"].items()},
                 "fixed_capacity_cf1.25": {"tokens_per_s": round(cq["tokens_per_s"]),
                                           "dropped_assignments": cq["dropped_assignments"],
                                           "padding_rows": cq["padding_rows"]}}

@@ -21,7 +21,7 @@ __all__ = [
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
     "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
-    "bind",
+    "bind", "moe_pool_bytes", "moe_prefetch_replicas", "moe_grouped_gemm_slots",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = (
     "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm", "moe_gemm_schedule",
     "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "moe_capacity_rows",
     "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine", "moe_repack",
-    "moe_router_workspace_bytes", "moe_router", "moe_bias_update",
+    "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "moe_pool_bytes",
+    "moe_prefetch_replicas", "moe_grouped_gemm_slots",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -140,6 +141,10 @@ def load():
         "moe_router_workspace_bytes": (ctypes.c_size_t, [_SP]),
         "moe_router": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_bias_update": (st, [_SP, _VP, _VP, ctypes.c_float, _VP]),
+        "moe_pool_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_prefetch_replicas": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_grouped_gemm_slots": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
+                                        _VP, ctypes.c_size_t, _VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -194,7 +199,8 @@ def _ok(status, where):
 
 # entry points that only compute on the host (sizes, layouts, checks)
 _HOST_ONLY = frozenset(("moe_status_str", "moe_check_shape", "moe_plan_layout",
-                        "moe_workspace_bytes", "moe_router_workspace_bytes", "moe_capacity_rows"))
+                        "moe_workspace_bytes", "moe_router_workspace_bytes", "moe_capacity_rows",
+                        "moe_pool_bytes"))
 
 
 class _Recorder:
@@ -482,3 +488,40 @@ def moe_bias_update(shape, counts, bias, gamma, stream=None):
     _ok(load().moe_bias_update(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
                                _ptr(bias, torch.float32, "bias", shape.E), float(gamma),
                                _stream(stream)), "moe_bias_update")
+
+
+def moe_pool_bytes(shape: Shape) -> int:
+    return int(load().moe_pool_bytes(ctypes.byref(shape)))
+
+
+def moe_prefetch_replicas(shape, plan, w_gate, w_up, w_down, pool, stream=None):
+    """pool: a device tensor of at least moe_pool_bytes(shape) bytes (any
+    dtype), or None when that is 0."""
+    import torch
+
+    act = _act_dtype(shape)
+    need = moe_pool_bytes(shape)
+    n = shape.E * shape.F * shape.H
+    _ok(load().moe_prefetch_replicas(
+        ctypes.byref(shape), _ptr(plan, torch.int32, "plan"), _ptr(w_gate, act, "w_gate", n),
+        _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
+        _ptr(pool, None, "pool", nullable=need == 0), _nbytes(pool), _stream(stream)),
+        "moe_prefetch_replicas")
+
+
+def moe_grouped_gemm_slots(shape, a, plan, w_gate, w_up, w_down, pool, y, ws, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    need = moe_pool_bytes(shape)
+    n = shape.E * shape.F * shape.H
+    _ok(load().moe_grouped_gemm_slots(
+        ctypes.byref(shape), _ptr(a, act, "a", shape.N * shape.H), _ptr(plan, torch.int32, "plan"),
+        _ptr(w_gate, act, "w_gate", n), _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
+        _ptr(pool, None, "pool", nullable=need == 0), _nbytes(pool),
+        _ptr(y, act, "y", shape.N * shape.H), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_grouped_gemm_slots")
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()

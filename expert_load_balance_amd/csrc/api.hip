@@ -141,7 +141,8 @@ moe_status_t moe_gemm_schedule(const moe_shape_t* shape, const int32_t* d_plan, 
     if (st != MOE_OK) return st;
     if (!d_plan || !d_ws) return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
-    return dev(moe_launch_gemm_schedule(*shape, d_plan, static_cast<char*>(d_ws), as_stream(stream)));
+    return dev(moe_launch_gemm_schedule(*shape, d_plan, static_cast<char*>(d_ws), as_stream(stream),
+                                        moe::expert_groups(*shape)));
 }
 
 moe_status_t moe_gemm_gateup(const moe_shape_t* shape, const void* d_a, const int32_t* d_plan,
@@ -154,7 +155,8 @@ moe_status_t moe_gemm_gateup(const moe_shape_t* shape, const void* d_a, const in
     if (bad(d_a, N) || !d_plan || !d_w_gate || !d_w_up || !d_ws) return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
     return dev(moe_launch_gemm_gateup(*shape, d_a, d_plan, d_w_gate, d_w_up,
-                                      static_cast<char*>(d_ws), as_stream(stream)));
+                                      static_cast<char*>(d_ws), as_stream(stream),
+                                      moe::expert_groups(*shape)));
 }
 
 moe_status_t moe_gemm_down(const moe_shape_t* shape, const int32_t* d_plan, const void* d_w_down,
@@ -166,7 +168,7 @@ moe_status_t moe_gemm_down(const moe_shape_t* shape, const int32_t* d_plan, cons
     if (!d_plan || !d_w_down || bad(d_y, N) || !d_ws) return MOE_EINVAL;
     if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
     return dev(moe_launch_gemm_down(*shape, d_plan, d_w_down, d_y, static_cast<char*>(d_ws),
-                                    as_stream(stream)));
+                                    as_stream(stream), moe::expert_groups(*shape)));
 }
 
 moe_status_t moe_grouped_gemm(const moe_shape_t* shape, const void* d_a, const int32_t* d_plan,
@@ -178,6 +180,52 @@ moe_status_t moe_grouped_gemm(const moe_shape_t* shape, const void* d_a, const i
         st = moe_gemm_gateup(shape, d_a, d_plan, d_w_gate, d_w_up, d_ws, ws_bytes, stream);
     if (st != MOE_OK) return st;
     return moe_gemm_down(shape, d_plan, d_w_down, d_y, d_ws, ws_bytes, stream);
+}
+
+size_t moe_pool_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK) return 0;
+    return moe::pool_bytes(*shape);
+}
+
+moe_status_t moe_prefetch_replicas(const moe_shape_t* shape, const int32_t* d_plan,
+                                   const void* d_w_gate, const void* d_w_up, const void* d_w_down,
+                                   void* d_pool, size_t pool_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const size_t need = moe::pool_bytes(*shape);
+    if (!d_plan || !d_w_gate || !d_w_up || !d_w_down || (need > 0 && !d_pool) ||
+        pool_bytes < need)
+        return MOE_EINVAL;
+    return dev(moe_launch_prefetch(*shape, d_plan, d_w_gate, d_w_up, d_w_down, d_pool,
+                                   as_stream(stream)));
+}
+
+moe_status_t moe_grouped_gemm_slots(const moe_shape_t* shape, const void* d_a,
+                                    const int32_t* d_plan, const void* d_w_gate,
+                                    const void* d_w_up, const void* d_w_down, const void* d_pool,
+                                    size_t pool_bytes, void* d_y, void* d_ws, size_t ws_bytes,
+                                    moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    const size_t need = moe::pool_bytes(*shape);
+    if (bad(d_a, N) || !d_plan || !d_w_gate || !d_w_up || !d_w_down || bad(d_y, N) || !d_ws ||
+        (need > 0 && !d_pool) || pool_bytes < need)
+        return MOE_EINVAL;
+    const moe::WsLayout W = moe::ws_layout(*shape);
+    if (ws_bytes < W.total) return MOE_EINVAL;
+    char* ws = static_cast<char*>(d_ws);
+    hipStream_t hs = as_stream(stream);
+    uint64_t* wtab = reinterpret_cast<uint64_t*>(ws + W.wtab);
+    const moe::GemmGroups g{2 * shape->E, true, wtab};
+    hipError_t e = moe_launch_slot_table(*shape, d_plan, d_w_gate, d_w_up, d_w_down, d_pool, wtab, hs);
+    if (e == hipSuccess) e = moe_launch_gemm_schedule(*shape, d_plan, ws, hs, g);
+    if (e == hipSuccess) e = moe_launch_gemm_gateup(*shape, d_a, d_plan, d_w_gate, d_w_up, ws, hs, g);
+    if (e == hipSuccess) e = moe_launch_gemm_down(*shape, d_plan, d_w_down, d_y, ws, hs, g);
+    return dev(e);
 }
 
 moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_t* d_dest_row,

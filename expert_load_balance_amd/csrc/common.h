@@ -66,7 +66,8 @@ __host__ __device__ inline PlanLayout plan_layout(int E, int R)
 // Workspace carve-up (bytes, 256-byte aligned regions).
 struct WsLayout {
     size_t blk_hist, blk_base;  // count: int32[B][E] each
-    size_t sched;               // gemm: int32 schedule (see gemm.hip)
+    size_t sched;               // gemm: int32 schedule (see gemm.hip), up to 2E groups
+    size_t wtab;                // gemm by segment: uint64[2E][3] weight addresses
     size_t vrow;                // gemm: int32[N] expert-sorted row -> buf row
     size_t part;                // gemm bf16: float[units][256][256] partial tiles (K-split leftovers)
     size_t h;                   // gemm: dtype[N][F] SwiGLU activations
@@ -92,7 +93,7 @@ inline int64_t gemm_part_units(const moe_shape_t& s)
     if (s.dtype != MOE_BF16) return 0;
     const int64_t N = (int64_t)s.T * s.k;
     if (N == 0) return 0;
-    const int64_t mt = N / kGemmTile + s.E;
+    const int64_t mt = N / kGemmTile + 2 * s.E;  // at most 2E groups (by segment)
     const int64_t gu = mt * ((s.F + kGemmTile / 2 - 1) / (kGemmTile / 2)) * (s.H / kGemmStageK);
     const int64_t dn = mt * ((s.H + kGemmTile - 1) / kGemmTile) * (s.F / kGemmStageK);
     const int64_t u = gu > dn ? gu : dn;
@@ -118,13 +119,39 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     size_t o = 0;
     w.blk_hist = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
     w.blk_base = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
-    w.sched = o;     o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
+    w.sched = o;     o = align256(o + (size_t)(4 * (2 * s.E + 1) + 64) * 4);
+    w.wtab = o;      o = align256(o + (size_t)2 * s.E * 3 * 8);
     w.vrow = o;      o = align256(o + (size_t)(N > 0 ? N : 1) * 4);
     w.part = o;      o = align256(o + (size_t)gemm_part_units(s) * kGemmTile * kGemmTile * 4);
     w.h = o;         o = align256(o + (size_t)N * s.F * (s.dtype == MOE_BF16 ? 2 : 4));
     w.stats = o;     o = align256(o + (size_t)stats_slots(s.R) * 8);
     w.total = o;
     return w;
+}
+
+// Grouping of the grouped GEMM. By expert: G = E groups, an expert's pieces
+// gathered into one run of rows through a row map, weights at base + e*F*H.
+// By segment (replica slots): G = 2E groups, one per (rank r, segment
+// position i) of the plan (group r*2n + i), each a contiguous run of buffer
+// rows, with weights from a per-group table of byte addresses [G][3]
+// (gate, up, down) that may point into the replica slot pool.
+constexpr int kMaxGroups = 512;
+struct GemmGroups {
+    int G;
+    bool seg;
+    const uint64_t* wtab;
+};
+inline GemmGroups expert_groups(const moe_shape_t& s) { return GemmGroups{s.E, false, nullptr}; }
+
+// Replica slot pool: pool[r][j][3][F*H] for j < min(S, n) slots per rank.
+inline int pool_slots(const moe_shape_t& s)
+{
+    const int n = s.E / s.R;
+    return s.S < n ? s.S : n;
+}
+inline size_t pool_bytes(const moe_shape_t& s)
+{
+    return (size_t)s.R * pool_slots(s) * 3 * s.F * s.H * (s.dtype == MOE_BF16 ? 2 : 4);
 }
 
 // Router GEMM work split (bf16): TM tokens per workgroup tile and `parts`
@@ -178,12 +205,18 @@ hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t
 hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t* dest_row,
                               const float* w, const void* shared_y, void* out, hipStream_t st);
 hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, char* ws,
-                                    hipStream_t st);
+                                    hipStream_t st, const moe::GemmGroups& g);
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
-                                  hipStream_t st);
+                                  hipStream_t st, const moe::GemmGroups& g);
 hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
-                                void* y, char* ws, hipStream_t st);
+                                void* y, char* ws, hipStream_t st, const moe::GemmGroups& g);
+// replica slots: the pool copy, and the per-segment weight table
+hipError_t moe_launch_prefetch(const moe_shape_t& s, const int32_t* plan, const void* w_gate,
+                               const void* w_up, const void* w_down, void* pool, hipStream_t st);
+hipError_t moe_launch_slot_table(const moe_shape_t& s, const int32_t* plan, const void* w_gate,
+                                 const void* w_up, const void* w_down, const void* pool,
+                                 uint64_t* wtab, hipStream_t st);
 hipError_t moe_launch_combine_rows(const moe_shape_t& s, int64_t nrows, const void* y,
                                    const int32_t* dest_row, const float* w, const void* shared_y,
                                    void* out, hipStream_t st);

@@ -30,77 +30,97 @@ using namespace moe::lds;
 
 constexpr int kThreads = 256;
 
-// schedule layout inside the workspace region (int32):
-//   [0 .. E]            tile_start: prefix of the expert's M-tiles of bm rows
-//   [E+1 .. 2E+1]       row_start:  prefix of c_e
-//   [2E+2 .. 3E+2]      prefix of (0 < c_e <= sk1): one sk1-row tile each
-//   [3E+3 .. 4E+3]      prefix of (sk1 < c_e <= sk2): one sk2-row tile each
-// Experts with a skinny tile get no M-tile (sk1 = sk2 = 0: every expert is
+// schedule layout inside the workspace region (int32), G groups (experts, or
+// plan segments; see moe::GemmGroups):
+//   [0 .. G]            tile_start: prefix of the group's M-tiles of bm rows
+//   [G+1 .. 2G+1]       row_start:  prefix of the group's rows c_g
+//   [2G+2 .. 3G+2]      prefix of (0 < c_g <= sk1): one sk1-row tile each
+//   [3G+3 .. 4G+3]      prefix of (sk1 < c_g <= sk2): one sk2-row tile each
+// Groups with a skinny tile get no M-tile (sk1 = sk2 = 0: every group is
 // cut into M-tiles).
-__global__ __launch_bounds__(kThreads) void schedule_kernel(int E, int R, int bm, int sk1, int sk2,
+
+// rows of group g: by expert, the sum of its pieces; by segment, the
+// segment's count (group r*2n + i, none past seg_num[r])
+__device__ __forceinline__ int group_rows(int g, int E, int R, bool seg, const int32_t* plan,
+                                          const moe::PlanLayout& L)
+{
+    if (seg) {
+        const int n2 = 2 * (E / R);
+        const int r = g / n2, i = g % n2;
+        return i < plan[L.seg_num + r] ? plan[L.seg_cnt + g] : 0;
+    }
+    const int np = plan[L.piece_num + g];
+    int c = 0;
+    for (int p = 0; p < np && p < R; ++p) c += plan[L.piece_cnt + (size_t)g * R + p];
+    return c;
+}
+
+// One workgroup; thread t owns groups 2t and 2t+1 (G <= kMaxGroups).
+__global__ __launch_bounds__(kThreads) void schedule_kernel(int G, int E, int R, int seg, int bm,
+                                                            int sk1, int sk2,
                                                             const int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ sched)
 {
-    __shared__ int32_t st[256], sr[256], ss[256], s2[256];
+    __shared__ int32_t sh[4][kThreads];
     const moe::PlanLayout L = moe::plan_layout(E, R);
-    const int e = threadIdx.x;
-    int c = 0;
-    if (e < E) {
-        const int np = plan[L.piece_num + e];
-        for (int p = 0; p < np && p < R; ++p) c += plan[L.piece_cnt + (size_t)e * R + p];
+    const int tid = threadIdx.x;
+    int v[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int g = 2 * tid + h;
+        const int c = g < G ? group_rows(g, E, R, seg != 0, plan, L) : 0;
+        const bool t1 = c > 0 && c <= sk1;
+        const bool t2 = c > sk1 && c <= sk2;
+        v[h][0] = (t1 || t2) ? 0 : (c + bm - 1) / bm;
+        v[h][1] = c;
+        v[h][2] = t1 ? 1 : 0;
+        v[h][3] = t2 ? 1 : 0;
     }
-    const bool t1 = c > 0 && c <= sk1;
-    const bool t2 = c > sk1 && c <= sk2;
-    st[e] = (t1 || t2) ? 0 : (c + bm - 1) / bm;
-    sr[e] = c;
-    ss[e] = t1 ? 1 : 0;
-    s2[e] = t2 ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sh[q][tid] = v[0][q] + v[1][q];
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
-        const int a = e >= off ? st[e - off] : 0;
-        const int b = e >= off ? sr[e - off] : 0;
-        const int d = e >= off ? ss[e - off] : 0;
-        const int f = e >= off ? s2[e - off] : 0;
+        int a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = tid >= off ? sh[q][tid - off] : 0;
         __syncthreads();
-        st[e] += a;
-        sr[e] += b;
-        ss[e] += d;
-        s2[e] += f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sh[q][tid] += a[q];
         __syncthreads();
     }
-    if (e < E) {
-        sched[e + 1] = st[e];
-        sched[E + 1 + e + 1] = sr[e];
-        sched[2 * (E + 1) + e + 1] = ss[e];
-        sched[3 * (E + 1) + e + 1] = s2[e];
-    }
-    if (e == 0) {
-        sched[0] = 0;
-        sched[E + 1] = 0;
-        sched[2 * (E + 1)] = 0;
-        sched[3 * (E + 1)] = 0;
+    // inclusive prefix through group 2t+1 is sh[q][tid]; through 2t, minus v[1]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int32_t* out = sched + q * (G + 1);
+        if (tid == 0) out[0] = 0;
+        if (2 * tid < G) out[2 * tid + 1] = sh[q][tid] - v[1][q];
+        if (2 * tid + 1 < G) out[2 * tid + 2] = sh[q][tid];
     }
 }
 
-// vrow[g] = buf row of the g-th row in expert-sorted order (expert e owns
-// g in [row_start[e], row_start[e+1]); its v-th row lives in the piece that
-// covers v, pieces taken in rank order).
-__global__ __launch_bounds__(kThreads) void vrow_kernel(int N, int E, int R,
+// vrow[x] = buf row of the x-th row in group order (group g owns x in
+// [row_start[g], row_start[g+1])). By expert: its v-th row lives in the piece
+// that covers v, pieces taken in rank order. By segment: seg_row + v.
+__global__ __launch_bounds__(kThreads) void vrow_kernel(int N, int G, int E, int R, int seg,
                                                         const int32_t* __restrict__ plan,
                                                         const int32_t* __restrict__ sched,
                                                         int32_t* __restrict__ vrow)
 {
-    const int g = blockIdx.x * kThreads + threadIdx.x;
-    if (g >= N) return;
+    const int x = blockIdx.x * kThreads + threadIdx.x;
+    if (x >= N) return;
     const moe::PlanLayout L = moe::plan_layout(E, R);
-    const int32_t* row_start = sched + E + 1;
-    int lo = 0, hi = E - 1;  // last expert with row_start <= g
+    const int32_t* row_start = sched + G + 1;
+    int lo = 0, hi = G - 1;  // last group with row_start <= x (that group is non-empty)
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (row_start[mid] <= g) lo = mid;
+        if (row_start[mid] <= x) lo = mid;
         else hi = mid - 1;
     }
-    const int v = g - row_start[lo];
+    const int v = x - row_start[lo];
+    if (seg) {
+        vrow[x] = plan[L.seg_row + lo] + v;
+        return;
+    }
     const int np = plan[L.piece_num + lo];
     int cum = 0, row = 0;
     for (int p = 0; p < np && p < R; ++p) {
@@ -111,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void vrow_kernel(int N, int E, int R,
         }
         cum += c;
     }
-    vrow[g] = row;
+    vrow[x] = row;
 }
 
 struct Tile {
@@ -262,26 +282,37 @@ __device__ __forceinline__ Balance balance_of(int tiles, int P, int KT_all)
 }
 
 struct Unit {
-    int e, n0, rows, hrow0, KT, kofs, pidx;  // pidx: partial-tile slot, -1 for a whole tile
+    int e, n0, rows, hrow0, KT, kofs, pidx;  // e: group; pidx: partial-tile slot, -1 for a whole tile
 };
+
+// Weights of projection q (0 gate, 1 up, 2 down) for group g: from the
+// per-group table when there is one (grouping by segment), else expert g's
+// slice of the base tensor (F x H elements each).
+template <typename T>
+__device__ __forceinline__ const T* group_w(const uint64_t* wtab, const T* base, int g, int q, int F,
+                                            int H)
+{
+    if (wtab) return reinterpret_cast<const T*>(wtab[3 * g + q]);
+    return base + (size_t)g * F * H;
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
-    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
-    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
-    float* __restrict__ part)
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, float* __restrict__ part)
 {
     __shared__ __attribute__((aligned(1024))) char slots[2 * kSlotBytes];
     __shared__ int32_t rowmap[2][kTM];
-    __shared__ int32_t ssched[2 * 257];  // tile_start[E+1], row_start[E+1]
+    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // tile_start[G+1], row_start[G+1]
 
-    for (int i = threadIdx.x; i < 2 * (E + 1); i += kThreads) ssched[i] = sched[i];
+    for (int i = threadIdx.x; i < 2 * (G + 1); i += kThreads) ssched[i] = sched[i];
     __syncthreads();
     const int K = MODE == kGateUp ? H : F;
     const int KT_all = K / kTK;
     const int P = gridDim.x;
-    const Balance bal = balance_of(ssched[E] * ntiles_n, P, KT_all);
+    const Balance bal = balance_of(ssched[G] * ntiles_n, P, KT_all);
     const int total = bal.full + bal.L * bal.S;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -311,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             k0 = kp * bal.KTp;
             KT = min(KT_all - k0, bal.KTp);
         }
-        const TileRef r = tile_of<MODE>(t, E, ntiles_n, ssched);
+        const TileRef r = tile_of<MODE>(t, G, ntiles_n, ssched);
         Unit u;
         u.e = uni(r.e);
         u.n0 = uni(r.n0);
@@ -331,11 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     auto setup = [&](const Unit& u, const int32_t* rmap) {
         if (MODE == kGateUp) {
             abase = uni_ptr(reinterpret_cast<const char*>(a_src + u.kofs));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)u.e * F * H + u.kofs));
-            bbase1 = uni_ptr(reinterpret_cast<const char*>(w1 + (size_t)u.e * F * H + u.kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, u.e, 0, F, H) + u.kofs));
+            bbase1 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w1, u.e, 1, F, H) + u.kofs));
         } else {
             abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)u.hrow0 * F + u.kofs));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)u.e * H * F + u.kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, u.e, 2, F, H) + u.kofs));
             bbase1 = bbase0;
         }
 #pragma unroll
@@ -565,24 +596,25 @@ struct Skinny {
 
 template <int MODE, int SKM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
-    int E, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
-    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out)
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out)
 {
     using SK = Skinny<SKM>;
     constexpr int kSkM = SKM, kSkSlots = SK::kSlots, kSkA = SK::kA, kSkSlot = SK::kSlot;
     constexpr int kSkPerStage = SK::kPerStage, kNB = SK::kBlocks;
     __shared__ __attribute__((aligned(1024))) char ring[kSkSlots * kSkSlot];
     __shared__ int32_t rowmap[kSkM];
-    __shared__ int32_t ssched[2 * 257];  // skinny tile_start[E+1], row_start[E+1]
+    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // skinny tile_start[G+1], row_start[G+1]
 
-    for (int i = threadIdx.x; i < E + 1; i += kThreads) {
-        ssched[i] = sched[SK::kSchedOff * (E + 1) + i];
-        ssched[E + 1 + i] = sched[E + 1 + i];
+    for (int i = threadIdx.x; i < G + 1; i += kThreads) {
+        ssched[i] = sched[SK::kSchedOff * (G + 1) + i];
+        ssched[G + 1 + i] = sched[G + 1 + i];
     }
     __syncthreads();
     const int KT = (MODE == kGateUp ? H : F) / kTK;
-    const int total = ssched[E] * ntiles_n;
+    const int total = ssched[G] * ntiles_n;
     const int P = gridDim.x;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -605,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
     constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
 
     for (int Lu = my_slot; Lu < total; Lu += P) {
-        const TileRef r0 = tile_of<MODE>(Lu, E, ntiles_n, ssched);
+        const TileRef r0 = tile_of<MODE>(Lu, G, ntiles_n, ssched);
         const int e = uni(r0.e), n0 = uni(r0.n0), rows = uni(r0.rows), hrow0 = uni(r0.hrow0);
         if (tid < kSkM) rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : rows - 1)];
         wait_vm_lgkm<63>();
@@ -616,11 +648,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
         const char *abase, *bbase0, *bbase1;
         if (MODE == kGateUp) {
             abase = uni_ptr(reinterpret_cast<const char*>(a_src));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)e * F * H));
-            bbase1 = uni_ptr(reinterpret_cast<const char*>(w1 + (size_t)e * F * H));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 0, F, H)));
+            bbase1 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w1, e, 1, F, H)));
         } else {
             abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)hrow0 * F));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(w0 + (size_t)e * H * F));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 2, F, H)));
             bbase1 = bbase0;
         }
         // A copy instruction q = wave + 4 i fills rows 8q .. 8q+7
@@ -734,17 +766,17 @@ constexpr int kFixupRows = 16;
 constexpr int kFixupSlabs = kTM / kFixupRows;
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, int H, int F, int P,
+__global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, int H, int F, int P,
                                                          const int32_t* __restrict__ sched,
                                                          const int32_t* __restrict__ vrow,
                                                          const float* __restrict__ part,
                                                          uint16_t* __restrict__ out)
 {
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
-    const Balance bal = balance_of(sched[E] * ntiles_n, P, KT_all);
+    const Balance bal = balance_of(sched[G] * ntiles_n, P, KT_all);
     const int lt = blockIdx.x / kFixupSlabs;
     if (bal.S == 1 || lt >= bal.L) return;
-    const TileRef r = tile_of<MODE>(bal.full + lt, E, ntiles_n, sched);
+    const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, sched);
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
     constexpr int kRowsPerPass = kThreads / kQuads;
     const int c = (threadIdx.x % kQuads) * 4;
@@ -789,20 +821,32 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int E, int ntiles_n, in
 // 32-column tiles, K in chunks of 32, each thread 2 x 2 outputs.
 constexpr int kFM = 32;
 
+// Buffer row of row v of group g (by expert: through its pieces; by segment:
+// the segment's first row + v).
+__device__ __forceinline__ int group_buf_row(int g, int v, int R, bool seg, const int32_t* plan,
+                                             const moe::PlanLayout& L)
+{
+    return seg ? plan[L.seg_row + g] + v : buf_row_of(g, v, R, plan, L);
+}
+
 __global__ __launch_bounds__(kThreads) void gateup_f32_kernel(
-    int E, int R, int H, int F, int mtiles, const float* __restrict__ a,
+    int G, int E, int R, int seg, int H, int F, int mtiles, const float* __restrict__ a,
     const int32_t* __restrict__ plan, const int32_t* __restrict__ sched,
-    const float* __restrict__ wg, const float* __restrict__ wu, float* __restrict__ h)
+    const float* __restrict__ wg_all, const float* __restrict__ wu_all,
+    const uint64_t* __restrict__ wtab, float* __restrict__ h)
 {
     __shared__ float As[kFM][33], Gs[kFM][33], Us[kFM][33];
     __shared__ int32_t rowmap[kFM];
     const int mt = blockIdx.x % mtiles;
     const int nt = blockIdx.x / mtiles;
-    const Tile tile = find_tile(mt, E, kFM, sched);
+    const Tile tile = find_tile(mt, G, kFM, sched);
     if (tile.rows <= 0) return;
     const moe::PlanLayout L = moe::plan_layout(E, R);
     const int tid = threadIdx.x;
-    if (tid < kFM) rowmap[tid] = buf_row_of(tile.e, tile.v0 + (tid < tile.rows ? tid : 0), R, plan, L);
+    if (tid < kFM)
+        rowmap[tid] = group_buf_row(tile.e, tile.v0 + (tid < tile.rows ? tid : 0), R, seg != 0, plan, L);
+    const float* wg = group_w(wtab, wg_all, tile.e, 0, F, H);
+    const float* wu = group_w(wtab, wu_all, tile.e, 1, F, H);
     __syncthreads();
     const int n0 = nt * kFM;
     const int ty = tid / 16, tx = tid % 16;
@@ -814,8 +858,8 @@ __global__ __launch_bounds__(kThreads) void gateup_f32_kernel(
             const bool kin = kc < H;
             As[r][c] = kin ? a[(size_t)rowmap[r] * H + kc] : 0.f;
             const int f = min(n0 + r, F - 1);
-            Gs[r][c] = kin ? wg[((size_t)tile.e * F + f) * H + kc] : 0.f;
-            Us[r][c] = kin ? wu[((size_t)tile.e * F + f) * H + kc] : 0.f;
+            Gs[r][c] = kin ? wg[(size_t)f * H + kc] : 0.f;
+            Us[r][c] = kin ? wu[(size_t)f * H + kc] : 0.f;
         }
         __syncthreads();
         for (int c = 0; c < 32; ++c)
@@ -839,19 +883,21 @@ __global__ __launch_bounds__(kThreads) void gateup_f32_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void down_f32_kernel(
-    int E, int R, int H, int F, int mtiles, const float* __restrict__ h,
+    int G, int E, int R, int seg, int H, int F, int mtiles, const float* __restrict__ h,
     const int32_t* __restrict__ plan, const int32_t* __restrict__ sched,
-    const float* __restrict__ wd, float* __restrict__ y)
+    const float* __restrict__ wd_all, const uint64_t* __restrict__ wtab, float* __restrict__ y)
 {
     __shared__ float As[kFM][33], Bs[kFM][33];
     __shared__ int32_t rowmap[kFM];
     const int mt = blockIdx.x % mtiles;
     const int nt = blockIdx.x / mtiles;
-    const Tile tile = find_tile(mt, E, kFM, sched);
+    const Tile tile = find_tile(mt, G, kFM, sched);
     if (tile.rows <= 0) return;
     const moe::PlanLayout L = moe::plan_layout(E, R);
     const int tid = threadIdx.x;
-    if (tid < kFM) rowmap[tid] = tid < tile.rows ? buf_row_of(tile.e, tile.v0 + tid, R, plan, L) : -1;
+    if (tid < kFM)
+        rowmap[tid] = tid < tile.rows ? group_buf_row(tile.e, tile.v0 + tid, R, seg != 0, plan, L) : -1;
+    const float* wd = group_w(wtab, wd_all, tile.e, 2, F, H);
     __syncthreads();
     const int n0 = nt * kFM;
     const int ty = tid / 16, tx = tid % 16;
@@ -864,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void down_f32_kernel(
             const int ar = r < tile.rows ? r : 0;
             As[r][c] = kin ? h[(size_t)(tile.hrow0 + ar) * F + kc] : 0.f;
             const int o = min(n0 + r, H - 1);
-            Bs[r][c] = kin ? wd[((size_t)tile.e * H + o) * F + kc] : 0.f;
+            Bs[r][c] = kin ? wd[(size_t)o * F + kc] : 0.f;
         }
         __syncthreads();
         for (int c = 0; c < 32; ++c)
@@ -904,33 +950,34 @@ int persistent_grid()
 // split leftover tiles: at most half the persistent grid (each gets >= 2 parts)
 constexpr int kFixupGrid = moe::kGemmMaxGrid / 2 * kFixupSlabs;
 
-int max_mtiles(const moe_shape_t& s, int bm)
+int max_mtiles(const moe_shape_t& s, int bm, int G)
 {
     const int64_t N = (int64_t)s.T * s.k;
-    return (int)((N + bm - 1) / bm + s.E);
+    return (int)((N + bm - 1) / bm + G);
 }
 
 }  // namespace
 
 hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, char* ws,
-                                    hipStream_t st)
+                                    hipStream_t st, const moe::GemmGroups& g)
 {
     const moe::WsLayout W = moe::ws_layout(s);
     int32_t* sched = reinterpret_cast<int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.R, bf ? kTM : kFM, bf ? 32 : 0, bf ? 64 : 0, plan,
-                                            sched);
+    schedule_kernel<<<1, kThreads, 0, st>>>(g.G, s.E, s.R, g.seg ? 1 : 0, bf ? kTM : kFM,
+                                            bf ? 32 : 0, bf ? 64 : 0, plan, sched);
     hipError_t e = hipGetLastError();
     const int N = s.T * s.k;
     if (e != hipSuccess || !bf || N == 0) return e;
     int32_t* vrow = reinterpret_cast<int32_t*>(ws + W.vrow);
-    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.R, plan, sched, vrow);
+    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, g.G, s.E, s.R, g.seg ? 1 : 0,
+                                                                    plan, sched, vrow);
     return hipGetLastError();
 }
 
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
-                                  hipStream_t st)
+                                  hipStream_t st, const moe::GemmGroups& g)
 {
     if (s.T == 0) return hipSuccess;
     const moe::WsLayout W = moe::ws_layout(s);
@@ -941,61 +988,60 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
         float* part = reinterpret_cast<float*>(ws + W.part);
         uint16_t* h = reinterpret_cast<uint16_t*>(ws + W.h);
-        gemm_skinny_kernel<kGateUp, 32><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
-            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h);
-        gemm_skinny_kernel<kGateUp, 64><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
-            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h);
-        gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, static_cast<const uint16_t*>(a), sched, vrow,
-            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h, part);
+        const uint16_t* av = static_cast<const uint16_t*>(a);
+        const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+        const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+        gemm_skinny_kernel<kGateUp, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
+                                                                 wg, wu, g.wtab, h);
+        gemm_skinny_kernel<kGateUp, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
+                                                                 wg, wu, g.wtab, h);
+        gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
+                                                           wu, g.wtab, h, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        fixup_kernel<kGateUp><<<kFixupGrid, kThreads, 0, st>>>(s.E, ntn, s.H, s.F, P, sched, vrow,
+        fixup_kernel<kGateUp><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow,
                                                                 part, h);
     } else {
-        const int mtiles = max_mtiles(s, kFM);
+        const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.F + kFM - 1) / kFM;
         gateup_f32_kernel<<<mtiles * nt, kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, mtiles, static_cast<const float*>(a), plan, sched,
-            static_cast<const float*>(w_gate), static_cast<const float*>(w_up),
+            g.G, s.E, s.R, g.seg ? 1 : 0, s.H, s.F, mtiles, static_cast<const float*>(a), plan,
+            sched, static_cast<const float*>(w_gate), static_cast<const float*>(w_up), g.wtab,
             reinterpret_cast<float*>(ws + W.h));
     }
     return hipGetLastError();
 }
 
 hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
-                                void* y, char* ws, hipStream_t st)
+                                void* y, char* ws, hipStream_t st, const moe::GemmGroups& g)
 {
     if (s.T == 0) return hipSuccess;
     const moe::WsLayout W = moe::ws_layout(s);
     const int32_t* sched = reinterpret_cast<const int32_t*>(ws + W.sched);
-    const bool bf = s.dtype == MOE_BF16;
-    if (bf) {
+    if (s.dtype == MOE_BF16) {
         const int ntn = (s.H + kTN - 1) / kTN;
         const int P = persistent_grid();
         const int32_t* vrow = reinterpret_cast<const int32_t*>(ws + W.vrow);
         float* part = reinterpret_cast<float*>(ws + W.part);
-        gemm_skinny_kernel<kDown, 32><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
-            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
-        gemm_skinny_kernel<kDown, 64><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
-            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y));
-        gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(
-            s.E, ntn, s.H, s.F, reinterpret_cast<const uint16_t*>(ws + W.h), sched, vrow,
-            static_cast<const uint16_t*>(w_down), nullptr, static_cast<uint16_t*>(y), part);
+        const uint16_t* hv = reinterpret_cast<const uint16_t*>(ws + W.h);
+        const uint16_t* wd = static_cast<const uint16_t*>(w_down);
+        uint16_t* yv = static_cast<uint16_t*>(y);
+        gemm_skinny_kernel<kDown, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
+                                                               nullptr, g.wtab, yv);
+        gemm_skinny_kernel<kDown, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
+                                                               nullptr, g.wtab, yv);
+        gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
+                                                         nullptr, g.wtab, yv, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        fixup_kernel<kDown><<<kFixupGrid, kThreads, 0, st>>>(s.E, ntn, s.H, s.F, P, sched, vrow, part,
-                                                              static_cast<uint16_t*>(y));
+        fixup_kernel<kDown><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow, part,
+                                                              yv);
     } else {
-        const int mtiles = max_mtiles(s, kFM);
+        const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.H + kFM - 1) / kFM;
         down_f32_kernel<<<mtiles * nt, kThreads, 0, st>>>(
-            s.E, s.R, s.H, s.F, mtiles, reinterpret_cast<const float*>(ws + W.h), plan, sched,
-            static_cast<const float*>(w_down), static_cast<float*>(y));
+            g.G, s.E, s.R, g.seg ? 1 : 0, s.H, s.F, mtiles, reinterpret_cast<const float*>(ws + W.h),
+            plan, sched, static_cast<const float*>(w_down), g.wtab, static_cast<float*>(y));
     }
     return hipGetLastError();
 }

@@ -10,8 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, Shape, moe_combine, moe_count, moe_gemm_down, moe_gemm_gateup,
-               moe_gemm_schedule, moe_permute, moe_plan, moe_plan_layout, moe_route,
-               moe_workspace_bytes)
+               moe_gemm_schedule, moe_grouped_gemm_slots, moe_permute, moe_plan, moe_plan_layout,
+               moe_prefetch_replicas, moe_route, moe_workspace_bytes)
 
 STAGES = ("route", "count", "plan", "permute", "gemm_schedule", "gemm_gateup", "gemm_down",
           "shared", "combine")
@@ -64,11 +64,15 @@ class MoeLayerBuffers:
             moe_plan(self.shared_shape, self.shared_counts, self.shared_plan)
 
     def forward(self, logits, bias, x, w_gate, w_up, w_down, shared_w=None, stream=None,
-                marks=None):
+                marks=None, pool=None):
         """Route -> count -> plan -> permute -> grouped GEMM -> (shared) -> combine.
 
         marks: optional dict stage -> (start_event, end_event) recorded around
-        each stage on the stream. Returns self.out."""
+        each stage on the stream. pool: a device buffer of
+        moe_pool_bytes(shape) bytes; with it the planned replicas are
+        prefetched into their slots after the plan and the grouped GEMM runs
+        by plan segment, reading them (stages "prefetch" and "gemm_slots").
+        Returns self.out."""
         s = self.shape
         st = stream if stream is not None else torch.cuda.current_stream()
 
@@ -87,18 +91,28 @@ class MoeLayerBuffers:
         mark("plan", 0)
         moe_plan(s, self.counts, self.plan, st)
         mark("plan", 1)
+        if pool is not None:
+            mark("prefetch", 0)
+            moe_prefetch_replicas(s, self.plan, w_gate, w_up, w_down, pool, st)
+            mark("prefetch", 1)
         mark("permute", 0)
         moe_permute(s, x, self.ids, self.eidx, self.plan, self.buf, self.dest_row, self.row_src, st)
         mark("permute", 1)
-        mark("gemm_schedule", 0)
-        moe_gemm_schedule(s, self.plan, self.ws, st)
-        mark("gemm_schedule", 1)
-        mark("gemm_gateup", 0)
-        moe_gemm_gateup(s, self.buf, self.plan, w_gate, w_up, self.ws, st)
-        mark("gemm_gateup", 1)
-        mark("gemm_down", 0)
-        moe_gemm_down(s, self.plan, w_down, self.y, self.ws, st)
-        mark("gemm_down", 1)
+        if pool is not None:
+            mark("gemm_slots", 0)
+            moe_grouped_gemm_slots(s, self.buf, self.plan, w_gate, w_up, w_down, pool, self.y,
+                                   self.ws, st)
+            mark("gemm_slots", 1)
+        else:
+            mark("gemm_schedule", 0)
+            moe_gemm_schedule(s, self.plan, self.ws, st)
+            mark("gemm_schedule", 1)
+            mark("gemm_gateup", 0)
+            moe_gemm_gateup(s, self.buf, self.plan, w_gate, w_up, self.ws, st)
+            mark("gemm_gateup", 1)
+            mark("gemm_down", 0)
+            moe_gemm_down(s, self.plan, w_down, self.y, self.ws, st)
+            mark("gemm_down", 1)
         shared_y = None
         if self.shared_shape is not None and shared_w is not None:
             mark("shared", 0)

@@ -9,9 +9,10 @@
  *   moe_grouped_gemm SwiGLU expert FFN over the plan    (phase c)
  *   moe_combine      gate-weighted gather back to tokens (phase d)
  *   moe_stats        maxvio / balancedness / capacity / remote statistics
- * and the two baselines the plan replaces: fixed-capacity dispatch
- * (moe_capacity_*) and static repacking (moe_repack); the router's scores
- * (moe_router) and an assumed balancing-bias update (moe_bias_update).
+ * the replica slot pool (moe_prefetch_replicas, moe_grouped_gemm_slots); the
+ * two baselines the plan replaces: fixed-capacity dispatch (moe_capacity_*)
+ * and static repacking (moe_repack); the router's scores (moe_router) and an
+ * assumed balancing-bias update (moe_bias_update).
  *
  * Sources (web pages, cited by title and section):
  *   [Primer]  "DeepEP-on-EFA Guidance, section 1: what is MoE" -- the
@@ -235,6 +236,45 @@ moe_status_t moe_gemm_gateup(const moe_shape_t *shape, const void *d_a, const in
                              size_t ws_bytes, moe_stream_t stream);
 moe_status_t moe_gemm_down(const moe_shape_t *shape, const int32_t *d_plan, const void *d_w_down,
                            void *d_y, void *d_ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ---- Replica weight slots ------------------------------------------------
+ * [MoonEP] paragraphs 3-4: the planned redundant expert copies are prefetched
+ * into a fixed number S of weight slots per rank; S = experts per rank makes
+ * every expert the grouped GEMM touches local, and 3-4 slots usually suffice
+ * in inference. One pool serves every layer of a model (it holds only the
+ * current layer's replicas). Reading: rank r's replica experts take its
+ * slots in slot_expert[r] order (ascending expert id); slot j < min(S, n)
+ * holds that expert's three projections. */
+
+/* Bytes of the slot pool for this shape: R * min(S, n) * 3 * F * H * dtype
+ * bytes, laid out pool[r][j][q][F*H] with q = 0 gate [F][H], 1 up [F][H],
+ * 2 down [H][F] (each exactly the home expert's slice). 0 on a bad shape or
+ * when S = 0. */
+size_t moe_pool_bytes(const moe_shape_t *shape);
+
+/* The prefetch: copies, for every rank r and slot j < min(S, n) that the plan
+ * fills (slot_expert[r][j] >= 0), that expert's gate, up and down slices into
+ * pool[r][j], bit for bit. Slots without an expert are not written.
+ *   d_plan the moe_plan block; d_w_gate, d_w_up dtype[E][F][H];
+ *   d_w_down dtype[E][H][F]; d_pool / pool_bytes >= moe_pool_bytes(shape)
+ *   (d_pool may be NULL when that is 0). */
+moe_status_t moe_prefetch_replicas(const moe_shape_t *shape, const int32_t *d_plan,
+                                   const void *d_w_gate, const void *d_w_up, const void *d_w_down,
+                                   void *d_pool, size_t pool_bytes, moe_stream_t stream);
+
+/* moe_grouped_gemm as the R ranks would run it: one group per plan segment
+ * (rank r's i-th expert run, contiguous rows of d_a), each with its own
+ * weights -- the slot pool[r][j] for a replica segment whose expert holds
+ * slot j < min(S, n) of rank r, the home slices for a home segment and for
+ * a replica without a slot (a non-local read). y is the same function of the
+ * weights as moe_grouped_gemm's when the pool holds moe_prefetch_replicas'
+ * copies. Arguments as moe_grouped_gemm plus d_pool / pool_bytes (as
+ * moe_prefetch_replicas); d_ws: moe_workspace_bytes(shape). */
+moe_status_t moe_grouped_gemm_slots(const moe_shape_t *shape, const void *d_a,
+                                    const int32_t *d_plan, const void *d_w_gate,
+                                    const void *d_w_up, const void *d_w_down, const void *d_pool,
+                                    size_t pool_bytes, void *d_y, void *d_ws, size_t ws_bytes,
+                                    moe_stream_t stream);
 
 /* [Primer] phase (d): expert outputs return to their token and are summed
  * with the gate weights (the transpose of dispatch).

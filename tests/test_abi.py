@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 22
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -129,3 +129,22 @@ def test_router_workspace_and_rejections(lib):
     wide = bf.replace(T=1, k=1, E=256, H=1 << 23, F=64)                  # E*H*2 == 2^32
     assert moe.moe_check_shape(wide) == 0
     assert lib.moe_router(ctypes.byref(wide), p, p, None, p, p, p, p, p, 1 << 40, None) == 2
+
+
+def test_pool_bytes_and_slot_rejections(lib):
+    s = moe.Shape(16, 64, 8, 2, 128, 4, 2, moe.MOE_F32)          # n = 2
+    assert moe.moe_pool_bytes(s) == 4 * 2 * 3 * 128 * 64 * 4
+    assert moe.moe_pool_bytes(s.replace(S=5)) == moe.moe_pool_bytes(s)   # at most n slots
+    assert moe.moe_pool_bytes(s.replace(S=1)) == 4 * 1 * 3 * 128 * 64 * 4
+    assert moe.moe_pool_bytes(s.replace(S=0)) == 0
+    assert moe.moe_pool_bytes(s.replace(dtype=moe.MOE_BF16)) == 4 * 2 * 3 * 128 * 64 * 2
+    assert moe.moe_pool_bytes(s.replace(R=3)) == 0
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    need = moe.moe_pool_bytes(s)
+    assert lib.moe_prefetch_replicas(ctypes.byref(s), p, p, p, p, p, need - 1, None) == 1
+    assert lib.moe_prefetch_replicas(ctypes.byref(s), None, p, p, p, p, need, None) == 1
+    assert lib.moe_prefetch_replicas(ctypes.byref(s), p, p, p, p, None, need, None) == 1
+    assert lib.moe_grouped_gemm_slots(ctypes.byref(s), p, p, p, p, p, p, need, p, p, 1,
+                                      None) == 1                       # workspace too small
+    assert lib.moe_grouped_gemm_slots(ctypes.byref(s), p, p, p, p, p, p, need - 1, p, p,
+                                      1 << 30, None) == 1              # pool too small

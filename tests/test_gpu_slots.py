@@ -1,0 +1,214 @@
+"""GPU parity of the replica weight slots (MoonEP news article, paragraphs
+3-4: planned expert copies prefetched into S slots per rank; S = experts per
+rank makes every expert the GEMM touches local) against the CPU oracle.
+
+Bar: the pool copy is bit-exact (every filled slot equals the oracle's
+prefetch; slots without an expert are not written); the slot-reading grouped
+GEMM is within the bf16 / fp32 bar of the oracle's segment-by-segment FFN
+with each segment's weights taken from its source (slot or home). A pool
+deliberately different from the home weights shows that replica segments
+read their slot and nothing else does. Full-size shapes check sampled slots
+and rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as wl
+
+torch = pytest.importorskip("torch")
+import expert_load_balance_amd as moe  # noqa: E402
+from expert_load_balance_amd.layer import alloc  # noqa: E402
+
+from test_gpu_parity import DEV, assert_tol, host, make_weights, raw_bits, run_layer  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+SENTINEL = 0x5A5A  # int16 pattern left in slots that must not be written
+
+
+def make_pool(shape):
+    nbytes = moe.moe_pool_bytes(shape)
+    pool = torch.empty(max(nbytes, 2) // 2, dtype=torch.int16, device=DEV)
+    pool.fill_(SENTINEL)
+    return pool
+
+
+def pool_view(pool, shape):
+    """[R, Sm, 3, F*H] view in the weights' dtype."""
+    n = shape.E // shape.R
+    Sm = min(shape.S, n)
+    act = torch.bfloat16 if shape.dtype == moe.MOE_BF16 else torch.float32
+    return pool.view(act).view(shape.R, Sm, 3, shape.F * shape.H)
+
+
+def check_pool(pool, shape, pl, wts):
+    """Filled slots equal the oracle's prefetch bit for bit; empty slots
+    still hold the sentinel."""
+    pv = pool_view(pool, shape)
+    ref = oracle.prefetch(pl, shape.S, *(raw_bits(w).cpu().numpy() for w in wts))
+    got = raw_bits(pv).cpu().numpy()
+    for r in range(pv.shape[0]):
+        for j in range(pv.shape[1]):
+            if pl["slot_expert"][r, j] >= 0:
+                np.testing.assert_array_equal(got[r, j], ref[r, j], err_msg=f"slot ({r},{j})")
+            else:
+                assert (got[r, j].view(np.int16) == SENTINEL).all() if got.dtype == np.int16 \
+                    else (got[r, j].view(np.int16) == SENTINEL).all()
+
+
+def slot_run(shape, lg, bias, seed, modify=None):
+    """route/count/plan/permute, prefetch, then the slot GEMM; returns host
+    arrays for the oracle comparison."""
+    act = torch.bfloat16 if shape.dtype == moe.MOE_BF16 else torch.float32
+    x = synth.device_normal((shape.T, shape.H), 1.0, seed, act, DEV)
+    wts = make_weights(shape.E, shape.F, shape.H, shape.dtype, seed)
+    L = run_layer(shape, lg, bias, x, wts)
+    gt = moe.plan_tables(L.plan, shape)
+    pl = {k: host(v) for k, v in gt.items()}
+    pool = make_pool(shape)
+    moe.moe_prefetch_replicas(shape, L.plan, *wts, pool if pool.numel() > 1 else None)
+    torch.cuda.synchronize()
+    if modify is not None:
+        modify(pool_view(pool, shape), pl)
+    y = alloc((shape.N, shape.H), act, DEV)
+    moe.moe_grouped_gemm_slots(shape, L.buf, L.plan, *wts, pool if pool.numel() > 1 else None,
+                               y, L.ws)
+    torch.cuda.synchronize()
+    return L, pl, pool, wts, y
+
+
+SMALL = [
+    # name, T, H, E, k, F, R, S, dtype, bias strength
+    ("tiny_f32", 16, 64, 8, 2, 128, 4, 2, moe.MOE_F32, 0.8),
+    ("f32_multi_tile", 150, 96, 8, 2, 100, 4, 1, moe.MOE_F32, 0.6),
+    ("bf16_multi_tile", 700, 256, 8, 2, 384, 4, 2, moe.MOE_BF16, 0.5),
+    ("bf16_fine_grained_s_lt_n", 512, 128, 128, 8, 64, 16, 3, moe.MOE_BF16, 0.9),
+    ("bf16_s_ge_n", 300, 128, 16, 4, 192, 4, 6, moe.MOE_BF16, 1.0),
+    ("bf16_no_slots", 200, 128, 16, 4, 128, 8, 0, moe.MOE_BF16, 0.8),
+    ("bf16_one_rank", 97, 128, 4, 2, 64, 1, 2, moe.MOE_BF16, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_slots_small(case):
+    name, T, H, E, k, F, R, S, dtype, sb = case
+    _say(f"[case] slots {name}")
+    shape = moe.Shape(T, H, E, k, F, R, S, dtype)
+    lg = synth.router_logits(T, E, 41)
+    bias = synth.zipf_bias(E, sb, 41).astype(np.float32) if sb else None
+    L, pl, pool, wts, y = slot_run(shape, lg, bias, 42)
+    if moe.moe_pool_bytes(shape):
+        check_pool(pool, shape, pl, wts)
+    buf = host(L.buf).astype(np.float64)
+    wh = [host(w).astype(np.float64) for w in wts]
+    ph = host(pool_view(pool, shape)).astype(np.float64) if moe.moe_pool_bytes(shape) else None
+    ref = oracle.slot_ffn(buf, pl, S, *wh, ph)
+    assert_tol(host(y), ref, dtype, "y (slots)")
+
+
+def test_slot_gemm_reads_the_slots():
+    """Doubling W_down in every filled slot doubles exactly the rows of the
+    replica segments that read a slot (the FFN is linear in W_down; x2 is
+    exact in bf16), checked against the oracle on the modified pool, and
+    leaves home rows alone."""
+    shape = moe.Shape(512, 128, 16, 4, 128, 4, 2, moe.MOE_BF16)
+    lg = synth.router_logits(512, 16, 43)
+    bias = synth.zipf_bias(16, 1.2, 43).astype(np.float32)
+
+    def double_down(pv, pl):
+        pv[:, :, 2] *= 2
+
+    L, pl, pool, wts, y = slot_run(shape, lg, bias, 44, modify=double_down)
+    src = oracle.slot_sources(pl, shape.S)
+    assert (src >= 0).any()                          # some segment reads a slot
+    buf = host(L.buf).astype(np.float64)
+    wh = [host(w).astype(np.float64) for w in wts]
+    ph = host(pool_view(pool, shape)).astype(np.float64)
+    ref = oracle.slot_ffn(buf, pl, shape.S, *wh, ph)
+    assert_tol(host(y), ref, shape.dtype, "y (modified pool)")
+    home = oracle.slot_ffn(buf, pl, 0, *wh, ph)
+    slot_rows = np.zeros(shape.N, bool)
+    for r in range(shape.R):
+        for i in range(int(pl["seg_num"][r])):
+            if src[r, i] >= 0:
+                slot_rows[pl["seg_row"][r, i]:pl["seg_row"][r, i] + pl["seg_cnt"][r, i]] = True
+    assert np.allclose(ref[slot_rows], 2 * home[slot_rows]) and slot_rows.any()
+    assert np.array_equal(ref[~slot_rows], home[~slot_rows])
+
+
+@pytest.mark.parametrize("name,maxvio", [("mixtral", 0.2), ("a3b", 1), ("decode64", 20)])
+def test_slots_full_size(name, maxvio):
+    """Full size: every filled slot equals its home slices (on the device);
+    sampled slots bit-exact against the oracle's prefetch on the host; the
+    slot GEMM against the expert-grouped GEMM on all rows (the same function
+    of the same weights) and against the oracle on sampled replica rows."""
+    _say(f"[case] slots full {name}@{maxvio}")
+    torch.cuda.empty_cache()
+    w_ = wl.WORKLOADS[name]
+    T, H, E, k, F, R, S = (w_[c] for c in ("T", "H", "E", "k", "F", "R", "S"))
+    shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
+    lg, bias = wl.logits_and_bias(name, maxvio)
+    L, pl, pool, wts, y = slot_run(shape, lg, bias, w_["seed"])
+    pv = pool_view(pool, shape)
+    filled = [(r, j) for r in range(R) for j in range(pv.shape[1]) if pl["slot_expert"][r, j] >= 0]
+    assert filled                                     # the skew makes replicas
+    for r, j in filled:
+        e = int(pl["slot_expert"][r, j])
+        for q, w in enumerate(wts):
+            assert torch.equal(raw_bits(pv[r, j, q]), raw_bits(w[e].reshape(-1))), (r, j, q)
+    rng = np.random.default_rng(7)
+    for r, j in [filled[0], filled[-1]]:
+        e = int(pl["slot_expert"][r, j])
+        rows = np.sort(rng.choice(F, 8, replace=False))
+        for q in (0, 1):
+            np.testing.assert_array_equal(raw_bits(pv[r, j, q].view(F, H)[rows]).cpu().numpy(),
+                                          raw_bits(wts[q][e][rows]).cpu().numpy())
+    # the slot GEMM vs the expert-grouped GEMM (both already on device)
+    moe.moe_grouped_gemm(shape, L.buf, L.plan, *wts, L.y, L.ws)
+    torch.cuda.synchronize()
+    assert_tol(host(y), host(L.y).astype(np.float64), moe.MOE_BF16, "y slots vs y experts")
+    # sampled rows of the first replica segment that reads a slot, vs the oracle
+    src = oracle.slot_sources(pl, S)
+    r, i = map(int, np.argwhere(src >= 0)[0])
+    j, e = int(src[r, i]), int(pl["seg_expert"][r, i])
+    row0, cnt = int(pl["seg_row"][r, i]), int(pl["seg_cnt"][r, i])
+    rows = np.unique(np.linspace(row0, row0 + cnt - 1, 6).astype(int))
+    wsl = [pv[r, j, q].float().cpu().numpy() for q in range(3)]
+    ref = oracle.ffn_rows(host(L.buf[rows]).astype(np.float64), wsl[0].reshape(F, H),
+                          wsl[1].reshape(F, H), wsl[2].reshape(H, F))
+    assert_tol(host(y[rows]), ref, moe.MOE_BF16, f"replica rows of expert {e} on rank {r}")
+
+
+def test_layer_forward_with_pool():
+    """The layer with the prefetch after the plan and the slot-reading GEMM:
+    its output against the oracle's route -> count -> plan -> permute ->
+    slot FFN -> combine."""
+    from expert_load_balance_amd.layer import MoeLayerBuffers
+
+    T, H, E, k, F, R, S = 400, 128, 16, 4, 192, 4, 2
+    shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
+    _say("[case] layer forward with pool")
+    lg = synth.router_logits(T, E, 47)
+    bias = synth.zipf_bias(E, 1.0, 47).astype(np.float32)
+    x = synth.device_normal((T, H), 1.0, 48, torch.bfloat16, DEV)
+    wts = make_weights(E, F, H, moe.MOE_BF16, 48)
+    L = MoeLayerBuffers(shape, DEV)
+    pool = make_pool(shape)
+    L.forward(torch.from_numpy(lg).to(DEV), torch.from_numpy(bias).to(DEV), x, *wts, pool=pool)
+    torch.cuda.synchronize()
+    ids, w, _ = oracle.route(lg, bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    xh = host(x).astype(np.float64)
+    buf, dest_row, _ = oracle.permute(xh, ids, c["eidx"], pl)
+    wh = [host(t).astype(np.float64) for t in wts]
+    y = oracle.slot_ffn(buf, pl, S, *wh, oracle.prefetch(pl, S, *wh))
+    assert (oracle.slot_sources(pl, S) >= 0).any()
+    assert_tol(host(L.out), oracle.combine(y, dest_row, w), moe.MOE_BF16, "out (slots)")
