@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other workloads / skews reported beside the headline")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the layer (skip the isolated router, replica-slot and "
+                         "fixed-capacity measurements, which launch the same GEMM kernels); "
+                         "for kernel traces and counters of the layer alone")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -171,7 +175,66 @@ def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shar
             "padding_rows": s.E * cap - kept, "gemm_rows": s.E * cap}
 
 
-def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
+def time_router(shape, x, bias, seed, act, stream):
+    """The router's scores + top-k (x read once; W_r is E x H), back to back.
+    Returns (seconds per call, algorithmic bytes)."""
+    import torch
+
+    import expert_load_balance_amd as moe
+    import synth
+
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    dev = "cuda"
+    wr = synth.device_normal((E, H), synth.weight_std(H), seed * 10 + 9, act, dev)
+    r_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    r_err = torch.zeros(1, dtype=torch.int32, device=dev)
+    r_ws = torch.empty(max(1, moe.moe_router_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    t = time_back_to_back(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
+                                   r_err, r_ws, stream=stream))
+    nbytes = (T * H + E * H) * (2 if shape.dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
+    return t, nbytes
+
+
+def time_slots(shape, L, lg, bias, x, wts, shared, steps, stream):
+    """Replica slots: the prefetch copy of every filled slot, the grouped GEMM
+    by plan segment reading them beside the expert-grouped GEMM, and the whole
+    layer with both."""
+    import torch
+
+    import expert_load_balance_amd as moe
+
+    T, H, E, F, R, S = shape.T, shape.H, shape.E, shape.F, shape.R, shape.S
+    pool_bytes = moe.moe_pool_bytes(shape)
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    n = E // R
+    se = moe.plan_tables(L.plan, shape)["slot_expert"].cpu().numpy()[:, :min(S, n)]
+    filled = int((se >= 0).sum())
+    t_pref = time_back_to_back(moe.bind(moe.moe_prefetch_replicas, shape, L.plan, *wts, pool,
+                                        stream=stream), reps=10)
+    t_gs = time_back_to_back(moe.bind(moe.moe_grouped_gemm_slots, shape, L.buf, L.plan, *wts,
+                                      pool, L.y, L.ws, stream=stream), reps=10)
+    t_ge = time_back_to_back(moe.bind(moe.moe_grouped_gemm, shape, L.buf, L.plan, *wts, L.y,
+                                      L.ws, stream=stream), reps=10)
+    moved = 2.0 * filled * 3 * F * H * (2 if shape.dtype == moe.MOE_BF16 else 4)  # read + write
+    for _ in range(2):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
+    torch.cuda.synchronize()
+    t_layer = (time.perf_counter() - t1) / steps
+    del pool
+    return dict(S=S, slots_filled=filled, pool_gb=pool_bytes / 1e9,
+                prefetch_us=t_pref * 1e6, prefetch_gbs=moved / t_pref / 1e9,
+                prefetch_hbm_frac=moved / t_pref / 1e9 / PEAK_HBM_GBS,
+                gemm_slots_ms=t_gs * 1e3, gemm_experts_ms=t_ge * 1e3,
+                layer_tokens_per_s=T / t_layer, layer_ms_per_step=t_layer * 1e3)
+
+
+def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True):
     """Builds one workload on the GPU, runs `warmup` + `steps` layer steps and
     returns its measurements (plus the inputs, for the CPU baseline); with a
     capacity factor, also the fixed-capacity baseline on the same inputs."""
@@ -210,14 +273,20 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     torch.cuda.synchronize()
     print(f"[bench] {name}@{maxvio:g} warm-up done", file=sys.stderr, flush=True)
 
-    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for s in STAGES} for _ in range(steps)]
+    # the timed steps carry no event records (those sit between kernels in
+    # the queue); a second pass with per-stage events gives the breakdown
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks[i])
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for s in STAGES} for _ in range(steps)]
+    for i in range(steps):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks[i])
+    torch.cuda.synchronize()
 
     stage_ms = {}
     for s in STAGES:
@@ -234,52 +303,16 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
     t_comb = time_back_to_back(moe.bind(moe.moe_combine, shape, L.y, L.dest_row, L.w, sy, L.out,
                                         stream=stream))
 
-    # the router's scores + top-k (x read once; W_r is E x H), back to back
-    wr = synth.device_normal((E, H), synth.weight_std(H), w["seed"] * 10 + 9, act, dev)
-    r_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    r_err = torch.zeros(1, dtype=torch.int32, device=dev)
-    r_ws = torch.empty(max(1, moe.moe_router_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
-    t_router = time_back_to_back(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
-                                          r_err, r_ws, stream=stream))
-    router_bytes = (T * H + E * H) * (2 if dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
-    del wr, r_logits, r_ws
+    t_router = router_bytes = None
+    if extras:
+        t_router, router_bytes = time_router(shape, x, bias, w["seed"], act, stream)
 
-    # replica slots: the prefetch copy of every filled slot, and the grouped
-    # GEMM by plan segment reading them, beside the expert-grouped GEMM
     slots = None
-    pool_bytes = moe.moe_pool_bytes(shape)
-    if pool_bytes:
-        pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
-        n = E // R
-        se = moe.plan_tables(L.plan, shape)["slot_expert"].cpu().numpy()[:, :min(S, n)]
-        filled = int((se >= 0).sum())
-        t_pref = time_back_to_back(moe.bind(moe.moe_prefetch_replicas, shape, L.plan, *wts, pool,
-                                            stream=stream), reps=10)
-        t_gs = time_back_to_back(moe.bind(moe.moe_grouped_gemm_slots, shape, L.buf, L.plan, *wts,
-                                          pool, L.y, L.ws, stream=stream), reps=10)
-        t_ge = time_back_to_back(moe.bind(moe.moe_grouped_gemm, shape, L.buf, L.plan, *wts, L.y,
-                                          L.ws, stream=stream), reps=10)
-        moved = 2.0 * filled * 3 * F * H * (2 if dtype == moe.MOE_BF16 else 4)  # read + write
-        # the whole layer with the prefetch and the slot-reading GEMM
-        for _ in range(2):
-            L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(steps):
-            L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, pool=pool)
-        torch.cuda.synchronize()
-        t_layer = (time.perf_counter() - t1) / steps
-        slots = dict(S=S, slots_filled=filled, pool_gb=pool_bytes / 1e9,
-                     prefetch_us=t_pref * 1e6, prefetch_gbs=moved / t_pref / 1e9,
-                     prefetch_hbm_frac=moved / t_pref / 1e9 / PEAK_HBM_GBS,
-                     gemm_slots_ms=t_gs * 1e3, gemm_experts_ms=t_ge * 1e3,
-                     layer_tokens_per_s=T / t_layer, layer_ms_per_step=t_layer * 1e3)
-        del pool
+    if extras and moe.moe_pool_bytes(shape):
+        slots = time_slots(shape, L, lg, bias, x, wts, shared, steps, stream)
 
     cap_res = None
-    if capacity_factor is not None:
+    if capacity_factor is not None and extras:
         cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
                                       L=L, shared=shared)
 
@@ -308,8 +341,9 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None):
         # three projections read once (the bound when rows per expert are few)
         gemm_weight_hbm_frac=st["active_experts"] * 3.0 * F * H * b / (gu_s + dn_s) / 1e9
         / PEAK_HBM_GBS,
-        router={"us": t_router * 1e6, "tflops": 2.0 * T * E * H / t_router / 1e12,
-                "hbm_frac": router_bytes / t_router / 1e9 / PEAK_HBM_GBS})
+        router=None if t_router is None else {
+            "us": t_router * 1e6, "tflops": 2.0 * T * E * H / t_router / 1e12,
+            "hbm_frac": router_bytes / t_router / 1e9 / PEAK_HBM_GBS})
     return res
 
 
@@ -345,7 +379,8 @@ def main():
     name = args.workload
     w = wl.WORKLOADS[name]
     maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
-    r = run_workload(name, maxvio, args.steps, args.warmup, capacity_factor=1.25)
+    r = run_workload(name, maxvio, args.steps, args.warmup, capacity_factor=1.25,
+                     extras=not args.layer_only)
     T, H, E, k, F, R, S = r["shape"]
     shared_F = r["shared_F"]
     st = r["stats"]
@@ -397,7 +432,7 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, ntok)
     del r
     torch.cuda.empty_cache()
-    if not args.no_sweep:
+    if not args.no_sweep and not args.layer_only:
         sweep = {}
         for sname, smv in SWEEP:
             q = run_workload(sname, smv, 10, 3, capacity_factor=1.25)
