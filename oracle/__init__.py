@@ -86,6 +86,9 @@ def _load():
         lib.orc_router_logits.restype = None
         lib.orc_bias_update.restype = None
         lib.orc_slot_sources.restype = None
+        for fn in ("orc_combine_backward", "orc_ffn_backward_rows", "orc_permute_backward",
+                   "orc_route_backward"):
+            getattr(lib, fn).restype = None
         _lib = lib
     return _lib
 
@@ -350,3 +353,91 @@ def slot_ffn(buf, pl, S, w_gate, w_up, w_down, pool):
                 wg, wu, wd = w_gate[e], w_up[e], w_down[e]
             y[row:row + cnt] = ffn_rows(buf[row:row + cnt], wg, wu, wd)
     return y
+
+
+# ---- backward (the chain rule of the forward functions above, in double) ----
+
+def combine_backward(dout, y, dest_row, w):
+    """dy [nrows, H] (w * dout scattered to the assignment rows) and dw [T, k]
+    (<dout[t], y[dest]>). (orc_combine_backward)"""
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    dest_row = _i32(dest_row)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    T, k = dest_row.shape
+    nrows, H = y.shape
+    dy = np.empty((nrows, H), np.float64)
+    dw = np.empty((T, k), np.float64)
+    _load().orc_combine_backward(T, k, H, ctypes.c_int64(nrows), _p(dout, F64P), _p(y, F64P),
+                                 _p(dest_row, I32P), _p(w, F64P), _p(dy, F64P), _p(dw, F64P))
+    return dy, dw
+
+
+def ffn_backward_rows(x, dy, w_gate, w_up, w_down):
+    """SwiGLU FFN backward on rows x [n, H] of one expert given dy [n, H].
+    -> (dx [n, H], dW_gate [F, H], dW_up [F, H], dW_down [H, F]), double.
+    (orc_ffn_backward_rows)"""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    wg = np.ascontiguousarray(w_gate, dtype=np.float32)
+    wu = np.ascontiguousarray(w_up, dtype=np.float32)
+    wd = np.ascontiguousarray(w_down, dtype=np.float32)
+    n, H = x.shape
+    F = wg.shape[0]
+    dx = np.empty((n, H), np.float64)
+    dwg = np.zeros((F, H), np.float64)
+    dwu = np.zeros((F, H), np.float64)
+    dwd = np.zeros((H, F), np.float64)
+    _load().orc_ffn_backward_rows(n, H, F, _p(x, F32P), _p(dy, F64P), _p(wg, F32P), _p(wu, F32P),
+                                  _p(wd, F32P), _p(dx, F64P), _p(dwg, F64P), _p(dwu, F64P),
+                                  _p(dwd, F64P))
+    return dx, dwg, dwu, dwd
+
+
+def permute_backward(dbuf, dest_row):
+    """dx [T, H] = sum_j dbuf[dest[t, j]]. (orc_permute_backward)"""
+    dbuf = np.ascontiguousarray(dbuf, dtype=np.float64)
+    dest_row = _i32(dest_row)
+    T, k = dest_row.shape
+    nrows, H = dbuf.shape
+    dx = np.empty((T, H), np.float64)
+    _load().orc_permute_backward(T, k, H, ctypes.c_int64(nrows), _p(dbuf, F64P),
+                                 _p(dest_row, I32P), _p(dx, F64P))
+    return dx
+
+
+def route_backward(ids, w, dw, E):
+    """dlogits [T, E] of the gate weights' softmax over the selected raw
+    logits. (orc_route_backward)"""
+    ids = _i32(ids)
+    T, k = ids.shape
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    dw = np.ascontiguousarray(dw, dtype=np.float64)
+    dl = np.empty((T, E), np.float64)
+    _load().orc_route_backward(T, E, k, _p(ids, I32P), _p(w, F64P), _p(dw, F64P), _p(dl, F64P))
+    return dl
+
+
+def expert_ffn_backward(buf, dy, pl, w_gate, w_up, w_down):
+    """The grouped FFN backward over the plan: every expert's rows (all of
+    its pieces, home and replicas) through ffn_backward_rows; each expert's
+    weight gradient is the sum over all of its rows -- the replicas'
+    contributions reduced into the home expert.
+    -> (dbuf [N, H], dW_gate [E, F, H], dW_up [E, F, H], dW_down [E, H, F])."""
+    E, F, H = w_gate.shape
+    dbuf = np.zeros((buf.shape[0], H))
+    dwg = np.zeros((E, F, H))
+    dwu = np.zeros((E, F, H))
+    dwd = np.zeros((E, H, F))
+    for e in range(E):
+        rows = []
+        for p in range(int(pl["piece_num"][e])):
+            r0, c = int(pl["piece_row"][e, p]), int(pl["piece_cnt"][e, p])
+            rows.extend(range(r0, r0 + c))
+        if not rows:
+            continue
+        rows = np.array(rows)
+        dx, dwg[e], dwu[e], dwd[e] = ffn_backward_rows(buf[rows], dy[rows], w_gate[e], w_up[e],
+                                                       w_down[e])
+        dbuf[rows] = dx
+    return dbuf, dwg, dwu, dwd

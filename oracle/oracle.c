@@ -2,7 +2,8 @@
  * oracle.c -- plain, slow, single-threaded CPU reference for one MoE layer's
  * hot path: router top-k gating, demand counting, the equal-load replica plan,
  * dispatch permutation, the SwiGLU expert FFN, the gate-weighted combine and
- * the load statistics.
+ * the load statistics; and the layer's backward (combine, expert FFN,
+ * dispatch, gate).
  *
  * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this file. It shares no code, header,
@@ -422,6 +423,131 @@ void orc_repack(int E, int R, const int32_t *counts, int32_t *mapping)
     free(order);
     free(load);
     free(held);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the layer. [Primer] phases (a)-(d) run in reverse: combine,
+ * expert FFN, dispatch, router gate. [MoonEP] paragraph 3: in training the
+ * replicas' weight gradients are reduced into the home expert; on one GPU
+ * every piece of an expert contributes to that expert's one gradient, so the
+ * reduction is the sum over all of its rows. The chain rule written out, in
+ * double, from the same rounded inputs as the forward functions above.      */
+
+/* Combine: out[t] = sum_j w[t][j] * y[dest[t][j]], so
+ *   dy[dest[t][j]] += w[t][j] * dout[t]   (rows nobody reads stay zero),
+ *   dw[t][j] = <dout[t], y[dest[t][j]]>   (zero for a dropped assignment). */
+void orc_combine_backward(int T, int k, int H, int64_t nrows, const double *dout,
+                          const double *y, const int32_t *dest_row, const double *w,
+                          double *dy, double *dw)
+{
+    memset(dy, 0, sizeof(double) * (size_t)nrows * H);
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int d = dest_row[(size_t)t * k + j];
+            double acc = 0.0;
+            if (d >= 0 && d < nrows) {
+                for (int c = 0; c < H; ++c) {
+                    dy[(size_t)d * H + c] += w[(size_t)t * k + j] * dout[(size_t)t * H + c];
+                    acc += dout[(size_t)t * H + c] * y[(size_t)d * H + c];
+                }
+            }
+            dw[(size_t)t * k + j] = acc;
+        }
+    }
+}
+
+/* SwiGLU expert FFN on nrows rows of one expert, backward. With
+ * g = W_gate x, u = W_up x, s = 1/(1+e^-g), h = g s u, y = W_down h:
+ *   dh = W_down^T dy;  du = dh g s;  dg = dh u s (1 + g (1 - s));
+ *   dx = W_gate^T dg + W_up^T du;
+ *   dW_down += dy h^T, dW_gate += dg x^T, dW_up += du x^T  (accumulated).
+ * x [nrows][H], w_gate/w_up [F][H], w_down [H][F] (float values); dy, dx
+ * [nrows][H] and the weight gradients (same shapes as the weights) double. */
+void orc_ffn_backward_rows(int nrows, int H, int F, const float *x, const double *dy,
+                           const float *w_gate, const float *w_up, const float *w_down,
+                           double *dx, double *dw_gate, double *dw_up, double *dw_down)
+{
+    size_t nf = (size_t)(F > 0 ? F : 1);
+    double *g = (double *)malloc(sizeof(double) * nf);
+    double *u = (double *)malloc(sizeof(double) * nf);
+    double *dg = (double *)malloc(sizeof(double) * nf);
+    double *du = (double *)malloc(sizeof(double) * nf);
+    for (int i = 0; i < nrows; ++i) {
+        const float *xr = x + (size_t)i * H;
+        const double *dyr = dy + (size_t)i * H;
+        for (int f = 0; f < F; ++f) {
+            double a = 0.0, b = 0.0;
+            for (int c = 0; c < H; ++c) {
+                a += (double)w_gate[(size_t)f * H + c] * (double)xr[c];
+                b += (double)w_up[(size_t)f * H + c] * (double)xr[c];
+            }
+            g[f] = a;
+            u[f] = b;
+        }
+        for (int f = 0; f < F; ++f) {
+            double s = 1.0 / (1.0 + exp(-g[f]));
+            double h = g[f] * s * u[f];
+            double dh = 0.0;
+            for (int o = 0; o < H; ++o) {
+                dh += (double)w_down[(size_t)o * F + f] * dyr[o];
+                dw_down[(size_t)o * F + f] += dyr[o] * h;
+            }
+            du[f] = dh * g[f] * s;
+            dg[f] = dh * u[f] * s * (1.0 + g[f] * (1.0 - s));
+        }
+        for (int c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int f = 0; f < F; ++f)
+                acc += (double)w_gate[(size_t)f * H + c] * dg[f] + (double)w_up[(size_t)f * H + c] * du[f];
+            dx[(size_t)i * H + c] = acc;
+        }
+        for (int f = 0; f < F; ++f) {
+            for (int c = 0; c < H; ++c) {
+                dw_gate[(size_t)f * H + c] += dg[f] * (double)xr[c];
+                dw_up[(size_t)f * H + c] += du[f] * (double)xr[c];
+            }
+        }
+    }
+    free(g);
+    free(u);
+    free(dg);
+    free(du);
+}
+
+/* Dispatch: buf[dest[t][j]] = x[t], so dx[t] = sum_j dbuf[dest[t][j]]. */
+void orc_permute_backward(int T, int k, int H, int64_t nrows, const double *dbuf,
+                          const int32_t *dest_row, double *dx)
+{
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int d = dest_row[(size_t)t * k + j];
+                if (d >= 0 && d < nrows) acc += dbuf[(size_t)d * H + c];
+            }
+            dx[(size_t)t * H + c] = acc;
+        }
+    }
+}
+
+/* Gate: w[t][j] = softmax over the selected experts' RAW logits, so
+ *   dlogits[t][ids[t][j]] = w_j (dw_j - sum_j' w_j' dw_j'),
+ * zero for experts not selected (a small change of their logit does not
+ * change the selection or the weights). The balancing bias only selects and
+ * gets no gradient. */
+void orc_route_backward(int T, int E, int k, const int32_t *ids, const double *w,
+                        const double *dw, double *dlogits)
+{
+    memset(dlogits, 0, sizeof(double) * (size_t)T * E);
+    for (int t = 0; t < T; ++t) {
+        double dot = 0.0;
+        for (int j = 0; j < k; ++j) dot += w[(size_t)t * k + j] * dw[(size_t)t * k + j];
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            if (e >= 0 && e < E)
+                dlogits[(size_t)t * E + e] = w[(size_t)t * k + j] * (dw[(size_t)t * k + j] - dot);
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

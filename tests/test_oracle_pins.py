@@ -709,3 +709,127 @@ def test_slot_ffn_reads_the_slots():
     y2 = oracle.slot_ffn(buf, pl, 2, wg, wu, wd, pool2)
     assert np.array_equal(y2[16:19], 2.0 * y[16:19])
     assert np.array_equal(np.delete(y2, [16, 17, 18], 0), np.delete(y, [16, 17, 18], 0))
+
+
+# ---- backward: central differences of the forward functions ---------------
+
+def _grid(rng, shape, bits=6):
+    """Values m * 2^-bits in [-1, 1]: exact in float32, and so are their
+    +- 2^-12 neighbours used by the central differences below."""
+    return (rng.integers(-(1 << bits), (1 << bits) + 1, size=shape) / (1 << bits)).astype(np.float64)
+
+
+def test_ffn_backward_matches_central_differences():
+    """Every entry of dx, dW_gate, dW_up and dW_down against
+    (L(+eps) - L(-eps)) / 2 eps of L = <dy, ffn_rows(x, W)>, eps = 2^-12
+    (an independent path: the forward oracle, evaluated in double)."""
+    rng = np.random.default_rng(11)
+    n, H, F = 3, 4, 5
+    x = _grid(rng, (n, H))
+    wg, wu = _grid(rng, (F, H)), _grid(rng, (F, H))
+    wd = _grid(rng, (H, F))
+    dy = rng.standard_normal((n, H))
+    dx, dwg, dwu, dwd = oracle.ffn_backward_rows(x, dy, wg, wu, wd)
+    eps = 2.0 ** -12
+
+    def loss(x_, wg_, wu_, wd_):
+        return float((dy * oracle.ffn_rows(x_, wg_, wu_, wd_)).sum())
+
+    def fd(arr, which):
+        out = np.empty(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            vals = []
+            for sgn in (1, -1):
+                a = arr.copy()
+                a[idx] += sgn * eps
+                args = [x, wg, wu, wd]
+                args[which] = a
+                vals.append(loss(*args))
+            out[idx] = (vals[0] - vals[1]) / (2 * eps)
+        return out
+
+    for got, arr, which in ((dx, x, 0), (dwg, wg, 1), (dwu, wu, 2), (dwd, wd, 3)):
+        ref = fd(arr, which)
+        assert np.abs(got - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max()), which
+
+
+def test_combine_backward_is_the_adjoint():
+    """L = <dout, combine(y, dest, w)> is linear in y and in w, so dy and dw
+    are fixed exactly by <dy, y'> = L(y') and <dw, w'> = L(w') for any y',
+    w'; dropped assignments (dest -1) get dw = 0 and their rows stay 0."""
+    rng = np.random.default_rng(12)
+    T, k, H, nrows = 6, 3, 5, 20
+    dest = rng.permutation(nrows)[:T * k].reshape(T, k).astype(np.int32)
+    dest[2, 1] = -1
+    y = rng.standard_normal((nrows, H))
+    w = rng.random((T, k))
+    dout = rng.standard_normal((T, H))
+    dy, dw = oracle.combine_backward(dout, y, dest, w)
+    for _ in range(3):
+        y2 = rng.standard_normal((nrows, H))
+        assert np.isclose((dy * y2).sum(), (dout * oracle.combine(y2, dest, w)).sum(), rtol=1e-12)
+        w2 = rng.random((T, k))
+        assert np.isclose((dw * w2).sum(), (dout * oracle.combine(y, dest, w2)).sum(), rtol=1e-12)
+    assert dw[2, 1] == 0.0
+    unused = np.setdiff1d(np.arange(nrows), dest[dest >= 0])
+    assert not dy[unused].any()
+
+
+def test_permute_backward_is_the_adjoint():
+    """<permute(x), dbuf> = <x, permute_backward(dbuf)> on the fixture plan."""
+    pl = _fixture_plan()
+    ids = _pairs(FIX)
+    c = oracle.count(ids, 8, 4)
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((16, 7))
+    buf, dest, _ = oracle.permute(x, ids, c["eidx"], pl)
+    dbuf = rng.standard_normal(buf.shape)
+    dx = oracle.permute_backward(dbuf, dest)
+    assert np.isclose((buf * dbuf).sum(), (x * dx).sum(), rtol=1e-12)
+
+
+def test_route_backward_matches_central_differences():
+    """dlogits against central differences of L = <dw, w(logits)> through the
+    forward top-k + softmax; logits on a 2^-8 grid with distinct values, so a
+    2^-14 step never changes the selection. Unselected experts get 0."""
+    rng = np.random.default_rng(14)
+    T, E, k = 4, 9, 3
+    lg = np.stack([rng.permutation(np.arange(E) - E // 2) for _ in range(T)]) / 8.0
+    lg = (lg + rng.integers(-3, 4, size=(T, E)) / 256.0).astype(np.float32)
+    ids, w, _ = oracle.route(lg, None, k)
+    dw = rng.standard_normal((T, k))
+    dl = oracle.route_backward(ids, w, dw, E)
+    eps = 2.0 ** -14
+    for t in range(T):
+        for e in range(E):
+            vals = []
+            for sgn in (1, -1):
+                l2 = lg.copy()
+                l2[t, e] += np.float32(sgn * eps)
+                i2, w2, _ = oracle.route(l2, None, k)
+                assert np.array_equal(i2, ids)
+                vals.append(float((dw * w2).sum()))
+            ref = (vals[0] - vals[1]) / (2 * eps)
+            assert abs(dl[t, e] - ref) <= 1e-6, (t, e)
+            if e not in ids[t]:
+                assert dl[t, e] == 0.0
+
+
+def test_expert_backward_reduces_replicas_into_home():
+    """On the fixture plan expert 0 has a home piece and two replica pieces:
+    its weight gradient is the sum of the per-piece gradients (the replicas'
+    contributions reduced into the home expert), equal to one call over all
+    of its rows."""
+    pl = _fixture_plan()
+    rng = np.random.default_rng(15)
+    E, H, F, N = 8, 4, 6, 32
+    buf = _grid(rng, (N, H))
+    dy = rng.standard_normal((N, H))
+    wg, wu = _grid(rng, (E, F, H)), _grid(rng, (E, F, H))
+    wd = _grid(rng, (E, H, F))
+    dbuf, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dy, pl, wg, wu, wd)
+    assert int(pl["piece_num"][0]) == 3
+    parts = [oracle.ffn_backward_rows(buf[r0:r0 + c], dy[r0:r0 + c], wg[0], wu[0], wd[0])
+             for r0, c in zip(pl["piece_row"][0][:3], pl["piece_cnt"][0][:3])]
+    for q, got in ((1, dwg[0]), (2, dwu[0]), (3, dwd[0])):
+        assert np.allclose(got, sum(p[q] for p in parts), rtol=1e-12, atol=1e-12)
