@@ -22,6 +22,8 @@ __all__ = [
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
     "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
     "bind", "moe_pool_bytes", "moe_prefetch_replicas", "moe_grouped_gemm_slots",
+    "moe_backward_workspace_bytes", "moe_combine_backward", "moe_ffn_backward",
+    "moe_permute_backward", "moe_route_backward",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,7 +37,8 @@ EXPORTED_SYMBOLS = (
     "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats", "moe_capacity_rows",
     "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine", "moe_repack",
     "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "moe_pool_bytes",
-    "moe_prefetch_replicas", "moe_grouped_gemm_slots",
+    "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
+    "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -142,6 +145,12 @@ def load():
         "moe_router": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_bias_update": (st, [_SP, _VP, _VP, ctypes.c_float, _VP]),
         "moe_pool_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_backward_workspace_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_combine_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_ffn_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                  ctypes.c_size_t, _VP]),
+        "moe_permute_backward": (st, [_SP, _VP, _VP, _VP, _VP]),
+        "moe_route_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP]),
         "moe_prefetch_replicas": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_grouped_gemm_slots": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
                                         _VP, ctypes.c_size_t, _VP]),
@@ -200,7 +209,7 @@ def _ok(status, where):
 # entry points that only compute on the host (sizes, layouts, checks)
 _HOST_ONLY = frozenset(("moe_status_str", "moe_check_shape", "moe_plan_layout",
                         "moe_workspace_bytes", "moe_router_workspace_bytes", "moe_capacity_rows",
-                        "moe_pool_bytes"))
+                        "moe_pool_bytes", "moe_backward_workspace_bytes"))
 
 
 class _Recorder:
@@ -525,3 +534,57 @@ def moe_grouped_gemm_slots(shape, a, plan, w_gate, w_up, w_down, pool, y, ws, st
 
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
+
+
+# ---- backward ----------------------------------------------------------------
+
+def moe_backward_workspace_bytes(shape: Shape) -> int:
+    return int(load().moe_backward_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_combine_backward(shape, dout, y, dest_row, w, dy, dw, stream=None):
+    import torch
+
+    act, N = _act_dtype(shape), shape.N
+    _ok(load().moe_combine_backward(
+        ctypes.byref(shape), _ptr(dout, act, "dout", shape.T * shape.H), _ptr(y, act, "y", N * shape.H),
+        _ptr(dest_row, torch.int32, "dest_row", N), _ptr(w, torch.float32, "w", N),
+        _ptr(dy, act, "dy", N * shape.H), _ptr(dw, torch.float32, "dw", N), _stream(stream)),
+        "moe_combine_backward")
+
+
+def moe_ffn_backward(shape, buf, plan, w_gate, w_up, w_down, dy, dbuf, dw_gate, dw_up, dw_down,
+                     ws, stream=None):
+    """ws: a uint8 device tensor of at least moe_backward_workspace_bytes(shape)."""
+    import torch
+
+    act, N = _act_dtype(shape), shape.N
+    n = shape.E * shape.F * shape.H
+    f32 = torch.float32
+    _ok(load().moe_ffn_backward(
+        ctypes.byref(shape), _ptr(buf, act, "buf", N * shape.H), _ptr(plan, torch.int32, "plan"),
+        _ptr(w_gate, act, "w_gate", n), _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
+        _ptr(dy, act, "dy", N * shape.H), _ptr(dbuf, act, "dbuf", N * shape.H),
+        _ptr(dw_gate, f32, "dw_gate", n), _ptr(dw_up, f32, "dw_up", n),
+        _ptr(dw_down, f32, "dw_down", n), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_ffn_backward")
+
+
+def moe_permute_backward(shape, dbuf, dest_row, dx, stream=None):
+    import torch
+
+    act = _act_dtype(shape)
+    _ok(load().moe_permute_backward(
+        ctypes.byref(shape), _ptr(dbuf, act, "dbuf", shape.N * shape.H),
+        _ptr(dest_row, torch.int32, "dest_row", shape.N), _ptr(dx, act, "dx", shape.T * shape.H),
+        _stream(stream)), "moe_permute_backward")
+
+
+def moe_route_backward(shape, ids, w, dw, dlogits, stream=None):
+    import torch
+
+    N = shape.N
+    _ok(load().moe_route_backward(
+        ctypes.byref(shape), _ptr(ids, torch.int32, "ids", N), _ptr(w, torch.float32, "w", N),
+        _ptr(dw, torch.float32, "dw", N), _ptr(dlogits, torch.float32, "dlogits", shape.T * shape.E),
+        _stream(stream)), "moe_route_backward")

@@ -240,6 +240,66 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
                                   as_stream(stream)));
 }
 
+size_t moe_backward_workspace_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK || shape->dtype != MOE_BF16) return 0;
+    return moe::bwd_ws_layout(*shape).total;
+}
+
+moe_status_t moe_combine_backward(const moe_shape_t* shape, const void* d_dout, const void* d_y,
+                                  const int32_t* d_dest_row, const float* d_w, void* d_dy,
+                                  float* d_dw, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (shape->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_dout, T) || bad(d_y, N) || bad(d_dest_row, N) || bad(d_w, N) || bad(d_dy, N) ||
+        bad(d_dw, N))
+        return MOE_EINVAL;
+    return dev(moe_launch_combine_backward(*shape, d_dout, d_y, d_dest_row, d_w, d_dy, d_dw,
+                                           as_stream(stream)));
+}
+
+moe_status_t moe_ffn_backward(const moe_shape_t* shape, const void* d_buf, const int32_t* d_plan,
+                              const void* d_w_gate, const void* d_w_up, const void* d_w_down,
+                              const void* d_dy, void* d_dbuf, float* d_dw_gate, float* d_dw_up,
+                              float* d_dw_down, void* d_ws, size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (shape->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_buf, N) || !d_plan || !d_w_gate || !d_w_up || !d_w_down || bad(d_dy, N) ||
+        bad(d_dbuf, N) || !d_dw_gate || !d_dw_up || !d_dw_down || !d_ws)
+        return MOE_EINVAL;
+    if (ws_bytes < moe::bwd_ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_ffn_backward(*shape, d_buf, d_plan, d_w_gate, d_w_up, d_w_down, d_dy,
+                                       d_dbuf, d_dw_gate, d_dw_up, d_dw_down,
+                                       static_cast<char*>(d_ws), as_stream(stream)));
+}
+
+moe_status_t moe_permute_backward(const moe_shape_t* shape, const void* d_dbuf,
+                                  const int32_t* d_dest_row, void* d_dx, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_dbuf, N) || bad(d_dest_row, N) || bad(d_dx, T)) return MOE_EINVAL;
+    return dev(moe_launch_combine_rows(*shape, N, d_dbuf, d_dest_row, nullptr, nullptr, d_dx,
+                                       as_stream(stream)));
+}
+
+moe_status_t moe_route_backward(const moe_shape_t* shape, const int32_t* d_ids, const float* d_w,
+                                const float* d_dw, float* d_dlogits, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t T = shape->T, N = T * shape->k;
+    if (bad(d_ids, N) || bad(d_w, N) || bad(d_dw, N) || bad(d_dlogits, T)) return MOE_EINVAL;
+    return dev(moe_launch_route_backward(*shape, d_ids, d_w, d_dw, d_dlogits, as_stream(stream)));
+}
+
 size_t moe_router_workspace_bytes(const moe_shape_t* shape)
 {
     if (check(shape) != MOE_OK) return 0;

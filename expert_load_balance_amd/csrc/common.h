@@ -129,6 +129,30 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     return w;
 }
 
+// Workspace of the FFN backward (bytes, 256-byte aligned regions): the
+// by-expert schedule with 256-row M-tiles, the expert-order row map, a zero
+// page, x and dy in expert order, the recomputed g | u, dg | du and h.
+struct BwdWsLayout {
+    size_t sched, vrow, zero, xs, dys, gu, dgu, hb, total;
+};
+inline BwdWsLayout bwd_ws_layout(const moe_shape_t& s)
+{
+    const size_t N = (size_t)s.T * s.k;
+    const size_t n1 = N > 0 ? N : 1;
+    BwdWsLayout b;
+    size_t o = 0;
+    b.sched = o; o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
+    b.vrow = o;  o = align256(o + n1 * 4);
+    b.zero = o;  o = align256(o + 512);
+    b.xs = o;    o = align256(o + n1 * s.H * 2);
+    b.dys = o;   o = align256(o + n1 * s.H * 2);
+    b.gu = o;    o = align256(o + n1 * 2 * s.F * 2);
+    b.dgu = o;   o = align256(o + n1 * 2 * s.F * 2);
+    b.hb = o;    o = align256(o + n1 * s.F * 2);
+    b.total = o;
+    return b;
+}
+
 // Grouping of the grouped GEMM. By expert: G = E groups, an expert's pieces
 // gathered into one run of rows through a row map, weights at base + e*F*H.
 // By segment (replica slots): G = 2E groups, one per (rank r, segment
@@ -211,6 +235,20 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
                                   hipStream_t st, const moe::GemmGroups& g);
 hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
                                 void* y, char* ws, hipStream_t st, const moe::GemmGroups& g);
+// by-expert schedule with 256-row M-tiles only (no skinny tiles) + row map
+hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan, int32_t* sched,
+                                       int32_t* vrow, hipStream_t st);
+// the expert FFN backward (bf16): gathers, recompute, dgrad, wgrad
+hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const void* dy, void* dbuf, float* dw_gate, float* dw_up,
+                                   float* dw_down, char* ws, hipStream_t st);
+// combine / dispatch / gate backward
+hipError_t moe_launch_combine_backward(const moe_shape_t& s, const void* dout, const void* y,
+                                       const int32_t* dest_row, const float* w, void* dy,
+                                       float* dw, hipStream_t st);
+hipError_t moe_launch_route_backward(const moe_shape_t& s, const int32_t* ids, const float* w,
+                                     const float* dw, float* dlogits, hipStream_t st);
 // replica slots: the pool copy, and the per-segment weight table
 hipError_t moe_launch_prefetch(const moe_shape_t& s, const int32_t* plan, const void* w_gate,
                                const void* w_up, const void* w_down, void* pool, hipStream_t st);

@@ -975,6 +975,18 @@ hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, c
     return hipGetLastError();
 }
 
+hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan, int32_t* sched,
+                                       int32_t* vrow, hipStream_t st)
+{
+    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.E, s.R, 0, kTM, 0, 0, plan, sched);
+    hipError_t e = hipGetLastError();
+    const int N = s.T * s.k;
+    if (e != hipSuccess || N == 0) return e;
+    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.E, s.R, 0, plan, sched,
+                                                                    vrow);
+    return hipGetLastError();
+}
+
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
                                   hipStream_t st, const moe::GemmGroups& g)

@@ -1,0 +1,446 @@
+// gemm_bwd.hip -- the grouped GEMMs of the expert FFN backward (bf16 in,
+// fp32 accumulate, v_mfma_f32_32x32x16_bf16).
+//
+// The chain rule of the SwiGLU expert FFN ("DeepEP-on-EFA Guidance, section
+// 1", phase (c), run in reverse): with g = x W_gate^T, u = x W_up^T,
+// h = silu(g) u, y = h W_down^T and the incoming dy,
+//   dh = dy W_down            dg = dh u s (1 + g (1 - s)),  du = dh silu(g)
+//   dx = dg W_gate + du W_up  (s = 1 / (1 + e^-g))
+//   dW_down = dy^T h,  dW_gate = dg^T x,  dW_up = du^T x  (sums over the
+// expert's rows: every piece of an expert, home or replica, adds into the
+// one gradient of the home expert -- "Moonshot AI drops MoonEP ..."
+// paragraph 3 reduces replica gradients home).
+//
+// Rows are first gathered into expert order (x and dy), so every operand is
+// a run of contiguous rows. Five instances of one kernel:
+//   GU   g | u = x [W_gate; W_up]^T   (recomputed; M = rows, N = 2F, K = H)
+//   DH   dh = dy W_down, with the SwiGLU backward in the epilogue
+//        (M = rows, N = F, K = H) -> dg | du, h
+//   DX   dx = [dg | du] [W_gate; W_up]   (M = rows, N = H, K = 2F),
+//        rows scattered back to buffer order
+//   WD   dW_down = dy^T h                 (M = H, N = F, K = rows)
+//   WGU  [dW_gate; dW_up] = [dg | du]^T x (M = 2F, N = H, K = rows)
+// An operand is either K-contiguous (rows of the tile along K: the forward
+// kernel's 128-byte swizzled rows, one ds_read_b128 per fragment) or
+// k-major (rows of 256 elements per k, as the weights are laid out for DH
+// and DX and the activations for the weight gradients): its 64 k-rows of a
+// stage sit in LDS as 512-byte rows with 16-byte chunk c at c ^ 4 (k & 3),
+// and each fragment is two ds_read_b64_tr_b16 (gfx950's transposing LDS
+// read) -- no transposed copy of any tensor is made. Tiles are 256 x 256,
+// four waves in 2 x 2, K in 64-deep stages through two 64 KB LDS slots
+// (global -> LDS copies, one stage ahead). The weight gradients are fp32,
+// written once per (expert, tile); K past an expert's rows reads a zero page.
+#include "common.h"
+#include "lds_pipe.h"
+
+namespace {
+
+using namespace moe::lds;
+
+constexpr int kThreads = 256;
+constexpr int kT = 256;          // tile rows and columns
+constexpr int kK = 64;           // K per stage
+constexpr int kOp = kT * kK * 2; // 32 KB: one operand of one stage
+constexpr int kSlot = 2 * kOp;   // A, then B
+
+enum Kind { kGU = 0, kDH = 1, kDX = 2, kWD = 3, kWGU = 4 };
+
+struct BwdArgs {
+    int G, H, F;
+    const int32_t* sched;  // by-expert schedule, 256-row M-tiles, no skinny tiles
+    const int32_t* vrow;   // expert-order row -> buffer row
+    const uint16_t* xs;    // x in expert order [N][H]
+    const uint16_t* dys;   // dy in expert order [N][H]
+    const uint16_t *wg, *wu, *wd;
+    uint16_t* gu;          // [N][2F]: g | u
+    uint16_t* dgu;         // [N][2F]: dg | du
+    uint16_t* hb;          // [N][F]: h
+    uint16_t* dxbuf;       // [N][H], buffer order
+    float *dwg, *dwu, *dwd;
+    const char* zero;      // >= 512 zero bytes
+};
+
+// chunk swizzle of a k-major row: 4 consecutive k-rows cover all 64 banks
+__device__ __forceinline__ int kswz(int kr) { return (kr & 3) << 2; }
+
+template <int KIND>
+struct Traits {
+    // operand kinds: true = k-major
+    static constexpr bool kAC = KIND == kWD || KIND == kWGU;
+    static constexpr bool kBC = KIND != kGU;
+    static constexpr bool kWgrad = KIND == kWD || KIND == kWGU;
+};
+
+struct Tile {
+    int e, m0, n0, rows, hrow0, ns;  // rows: valid M rows (dgrad) or K rows (wgrad)
+};
+
+__device__ __forceinline__ float sigm(float z)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+template <int KIND>
+__device__ __forceinline__ int tiles_total(const BwdArgs& a, int ntn, int mtw, int ntw)
+{
+    if (Traits<KIND>::kWgrad) return a.G * mtw * ntw;
+    return a.sched[a.G] * ntn;
+}
+
+template <int KIND>
+__device__ __forceinline__ Tile tile_at(int t, const BwdArgs& a, int ntn, int mtw, int ntw)
+{
+    const int32_t* ts = a.sched;
+    const int32_t* rs = a.sched + a.G + 1;
+    Tile r;
+    if (Traits<KIND>::kWgrad) {
+        r.e = t / (mtw * ntw);
+        const int local = t % (mtw * ntw);
+        r.m0 = (local / ntw) * kT;
+        r.n0 = (local % ntw) * kT;
+        r.hrow0 = rs[r.e];
+        r.rows = rs[r.e + 1] - rs[r.e];
+        r.ns = (r.rows + kK - 1) / kK;
+        return r;
+    }
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] * ntn <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int mt_e = ts[lo + 1] - ts[lo];
+    const int local = t - ts[lo] * ntn;
+    r.e = lo;
+    r.n0 = (local / mt_e) * kT;
+    r.m0 = (local % mt_e) * kT;
+    const int c_e = rs[lo + 1] - rs[lo];
+    r.rows = min(kT, c_e - r.m0);
+    r.hrow0 = rs[lo] + r.m0;
+    const int K = KIND == kDX ? 2 * a.F : a.H;
+    r.ns = K / kK;
+    return r;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
+{
+    using TR = Traits<KIND>;
+    __shared__ __attribute__((aligned(1024))) char slots[2 * kSlot];
+
+    const int H = a.H, F = a.F;
+    const int ntn = KIND == kGU ? (2 * F + kT - 1) / kT : KIND == kDH ? (F + kT - 1) / kT
+                                                                      : (H + kT - 1) / kT;
+    const int mtw = KIND == kWD ? (H + kT - 1) / kT : (2 * F + kT - 1) / kT;
+    const int ntw = KIND == kWD ? (F + kT - 1) / kT : (H + kT - 1) / kT;
+    const int total = tiles_total<KIND>(a, ntn, mtw, ntw);
+
+    const int tid = threadIdx.x;
+    const int wave = uni(tid >> 6), lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, fh = lane >> 5;
+    const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
+    const char* zero = a.zero;
+
+    // fragment offsets, k-steps 0..3. K-contiguous: row fr of a 32-row block
+    // (block b at + 4096 b). k-major: lane reads 4 columns m (+ 32 b) at k-row
+    // kr; chunk 4 b + (m >> 3) sits at (4 b + (m >> 3)) ^ 4 (kr & 3), and as
+    // m >> 3 < 4 and kr & 3 = (lane >> 2) & 3 for every read of this lane, the
+    // block part is ((b ^ ((lane >> 2) & 3)) << 6) bytes, added per block.
+    uint32_t frow[4], fcol0[4], fcol1[4];
+    const int m_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        frow[kk] = (uint32_t)fr * 128u + (uint32_t)(((2 * kk + fh) ^ swz(fr)) * 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kr = 16 * kk + 8 * fh + 4 * h + ((lane & 15) >> 2);
+            const uint32_t off = (uint32_t)kr * 512u + (uint32_t)((m_in >> 3) << 4) +
+                                 (uint32_t)((m_in & 7) * 2);
+            (h ? fcol1 : fcol0)[kk] = off;
+        }
+    }
+    const int lx = (lane >> 2) & 3;
+    uint32_t xa[4], xb[4];  // block parts of this wave's A and B column blocks
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xa[i] = (uint32_t)(((wm * 4 + i) ^ lx) << 6);
+        xb[i] = (uint32_t)(((wn * 4 + i) ^ lx) << 6);
+    }
+
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        const Tile tl = tile_at<KIND>(t, a, ntn, mtw, ntw);
+        const int e = uni(tl.e), m0 = uni(tl.m0), n0 = uni(tl.n0), rows = uni(tl.rows);
+        const int hrow0 = uni(tl.hrow0), ns = uni(tl.ns);
+        const size_t FH = (size_t)F * H;
+
+        // K-contiguous operands (uniform base + 32-bit lane offsets, as in the
+        // forward kernel): copy q covers tile rows 8q .. 8q+7, lane l row
+        // 8q + l/8, chunk l % 8 stored at its swizzled slot. Rows past the
+        // tile's valid rows repeat the last one (their results are dropped).
+        const char* abase = nullptr;
+        const char* bbase[8];
+        uint32_t aoff[8], boff[8];
+        if (!TR::kAC) {
+            const int lda = KIND == kDX ? 2 * F : H;
+            const uint16_t* src = KIND == kGU ? a.xs : KIND == kDH ? a.dys : a.dgu;
+            abase = uni_ptr(reinterpret_cast<const char*>(src + (size_t)hrow0 * lda));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 8 * (wave + 4 * i) + (lane >> 3);
+                aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)lda * 2u +
+                          (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+            }
+        }
+        if (!TR::kBC) {  // GU: rows n of [W_gate; W_up] (F % 8 == 0: one side per copy)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = wave + 4 * i;
+                const int row = 8 * q + (lane >> 3);
+                const bool up = n0 + 8 * q >= F;
+                const int n = min(n0 + row, 2 * F - 1) - (up ? F : 0);
+                bbase[i] = uni_ptr(reinterpret_cast<const char*>((up ? a.wu : a.wg) + e * FH));
+                boff[i] = (uint32_t)n * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+            }
+        }
+        // k-major operands: k-row k (absolute in the K range), column chunk c
+        // (8 elements) of the tile; NULL selects the zero page
+        auto a_krow = [&](int k, int c) -> const char* {
+            const int col = m0 + 8 * c;
+            if (k >= rows) return nullptr;
+            if (KIND == kWD) return col < H ? (const char*)(a.dys + (size_t)(hrow0 + k) * H + col) : nullptr;
+            return col < 2 * F ? (const char*)(a.dgu + (size_t)(hrow0 + k) * 2 * F + col) : nullptr;
+        };
+        auto b_krow = [&](int k, int c) -> const char* {
+            const int col = n0 + 8 * c;
+            if (KIND == kDH)  // k = h: W_down[e][h][col]
+                return col < F ? (const char*)(a.wd + e * FH + (size_t)k * F + col) : nullptr;
+            if (KIND == kDX)  // k = f in [0, 2F): W_gate / W_up rows
+                return col >= H ? nullptr
+                       : k < F  ? (const char*)(a.wg + e * FH + (size_t)k * H + col)
+                                : (const char*)(a.wu + e * FH + (size_t)(k - F) * H + col);
+            if (k >= rows) return nullptr;
+            if (KIND == kWD) return col < F ? (const char*)(a.hb + (size_t)(hrow0 + k) * F + col) : nullptr;
+            return col < H ? (const char*)(a.xs + (size_t)(hrow0 + k) * H + col) : nullptr;  // WGU
+        };
+
+        // stage s into slot s & 1: 32 copies per operand, q = wave + 4 i
+        auto copy_stage = [&](int s) {
+            const uint32_t slot = slots_u + (uint32_t)(s & 1) * kSlot;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = wave + 4 * i;
+                if (TR::kAC) {
+                    const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
+                    const char* p = a_krow(s * kK + kr, c);
+                    copy16_at(p ? p : zero + c * 16, slot + q * 1024);
+                } else {
+                    copy16(abase + s * (kK * 2), aoff[i], slot + q * 1024);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = wave + 4 * i;
+                if (TR::kBC) {
+                    const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
+                    const char* p = b_krow(s * kK + kr, c);
+                    copy16_at(p ? p : zero + c * 16, slot + kOp + q * 1024);
+                } else {
+                    copy16(bbase[i] + s * (kK * 2), boff[i], slot + kOp + q * 1024);
+                }
+            }
+        };
+
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+        wait_vm_lgkm<0>();
+        slot_barrier();  // the previous tile's last slot is no longer read
+        if (ns > 0) copy_stage(0);
+        for (int s = 0; s < ns; ++s) {
+            wait_vm_lgkm<0>();
+            slot_barrier();  // stage s landed in every wave; slot (s+1) & 1 is free
+            if (s + 1 < ns) copy_stage(s + 1);
+            const char* sa = slots + (s & 1) * kSlot;
+            const char* sb = sa + kOp;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 af[4], bfr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int blk = wm * 4 + i;  // 32-row / 32-column block of A
+                    af[i] = TR::kAC ? lds_frag_tr(sa + fcol0[kk] + xa[i], sa + fcol1[kk] + xa[i])
+                                    : lds_frag(sa + frow[kk] + blk * 4096);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int blk = wn * 4 + j;
+                    bfr[j] = TR::kBC ? lds_frag_tr(sb + fcol0[kk] + xb[j], sb + fcol1[kk] + xb[j])
+                                     : lds_frag(sb + frow[kk] + blk * 4096);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+                // one k-step's fragments live at a time (no register spills)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        // epilogue: acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + fr,
+        // 128 wn + 32 j + 8 g4 + 4 fh + q) of the tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = wm * 128 + i * 32 + fr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = wn * 128 + j * 32 + g4 * 8 + fh * 4;
+                    const float v0 = acc[i][j][g4 * 4], v1 = acc[i][j][g4 * 4 + 1];
+                    const float v2 = acc[i][j][g4 * 4 + 2], v3 = acc[i][j][g4 * 4 + 3];
+                    if (KIND == kGU) {
+                        const int col = n0 + n;
+                        if (m >= rows || col >= 2 * F) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(v0, v1);
+                        pk.y = moe::pack_bf16x2(v2, v3);
+                        *reinterpret_cast<uint2*>(a.gu + (size_t)(hrow0 + m) * 2 * F + col) = pk;
+                    } else if (KIND == kDH) {
+                        const int col = n0 + n;
+                        if (m >= rows || col >= F) continue;
+                        const size_t r2 = (size_t)(hrow0 + m) * 2 * F;
+                        const uint2 gp = *reinterpret_cast<const uint2*>(a.gu + r2 + col);
+                        const uint2 up = *reinterpret_cast<const uint2*>(a.gu + r2 + F + col);
+                        const float g[4] = {__uint_as_float(gp.x << 16), __uint_as_float(gp.x & 0xffff0000u),
+                                            __uint_as_float(gp.y << 16), __uint_as_float(gp.y & 0xffff0000u)};
+                        const float u[4] = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
+                                            __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
+                        const float dh[4] = {v0, v1, v2, v3};
+                        float dg[4], du[4], hv[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float sg = sigm(g[q]);
+                            const float sl = g[q] * sg;
+                            hv[q] = sl * u[q];
+                            du[q] = dh[q] * sl;
+                            dg[q] = dh[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
+                        }
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(dg[0], dg[1]);
+                        pk.y = moe::pack_bf16x2(dg[2], dg[3]);
+                        *reinterpret_cast<uint2*>(a.dgu + r2 + col) = pk;
+                        pk.x = moe::pack_bf16x2(du[0], du[1]);
+                        pk.y = moe::pack_bf16x2(du[2], du[3]);
+                        *reinterpret_cast<uint2*>(a.dgu + r2 + F + col) = pk;
+                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                        *reinterpret_cast<uint2*>(a.hb + (size_t)(hrow0 + m) * F + col) = pk;
+                    } else if (KIND == kDX) {
+                        const int col = n0 + n;
+                        if (m >= rows || col >= H) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(v0, v1);
+                        pk.y = moe::pack_bf16x2(v2, v3);
+                        *reinterpret_cast<uint2*>(a.dxbuf + (size_t)a.vrow[hrow0 + m] * H + col) = pk;
+                    } else if (KIND == kWD) {
+                        const int row = m0 + m, col = n0 + n;
+                        if (row >= H || col >= F) continue;
+                        *reinterpret_cast<float4*>(a.dwd + e * FH + (size_t)row * F + col) =
+                            make_float4(v0, v1, v2, v3);
+                    } else {  // WGU
+                        const int row = m0 + m, col = n0 + n;
+                        if (row >= 2 * F || col >= H) continue;
+                        float* dst = row < F ? a.dwg + e * FH + (size_t)row * H
+                                             : a.dwu + e * FH + (size_t)(row - F) * H;
+                        *reinterpret_cast<float4*>(dst + col) = make_float4(v0, v1, v2, v3);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// rows of src (buffer order) into expert order: dst[x] = src[vrow[x]]
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(int N, int row_vecs,
+                                                               const int32_t* __restrict__ vrow,
+                                                               const uint4* __restrict__ src,
+                                                               uint4* __restrict__ dst)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)N * row_vecs) return;
+    const int x = (int)(i / row_vecs), c = (int)(i % row_vecs);
+    dst[i] = src[(size_t)vrow[x] * row_vecs + c];
+}
+
+__global__ void zero_kernel(uint4* p, int n)
+{
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+template <int KIND>
+hipError_t launch_kind(const BwdArgs& a, int grid, hipStream_t st)
+{
+    bwd_gemm_kernel<KIND><<<grid, kThreads, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const void* dy, void* dbuf, float* dw_gate, float* dw_up,
+                                   float* dw_down, char* ws, hipStream_t st)
+{
+    const int64_t N = (int64_t)s.T * s.k;
+    const moe::BwdWsLayout B = moe::bwd_ws_layout(s);
+    int32_t* sched = reinterpret_cast<int32_t*>(ws + B.sched);
+    int32_t* vrow = reinterpret_cast<int32_t*>(ws + B.vrow);
+    // the zero page, then the by-expert schedule with 256-row M-tiles only
+    zero_kernel<<<1, kThreads, 0, st>>>(reinterpret_cast<uint4*>(ws + B.zero), 32);
+    hipError_t e = moe_launch_gemm_schedule_bm(s, plan, sched, vrow, st);
+    if (e != hipSuccess) return e;
+    BwdArgs a;
+    a.G = s.E;
+    a.H = s.H;
+    a.F = s.F;
+    a.sched = sched;
+    a.vrow = vrow;
+    a.xs = reinterpret_cast<const uint16_t*>(ws + B.xs);
+    a.dys = reinterpret_cast<const uint16_t*>(ws + B.dys);
+    a.wg = static_cast<const uint16_t*>(w_gate);
+    a.wu = static_cast<const uint16_t*>(w_up);
+    a.wd = static_cast<const uint16_t*>(w_down);
+    a.gu = reinterpret_cast<uint16_t*>(ws + B.gu);
+    a.dgu = reinterpret_cast<uint16_t*>(ws + B.dgu);
+    a.hb = reinterpret_cast<uint16_t*>(ws + B.hb);
+    a.dxbuf = static_cast<uint16_t*>(dbuf);
+    a.dwg = dw_gate;
+    a.dwu = dw_up;
+    a.dwd = dw_down;
+    a.zero = ws + B.zero;
+    const int grid = moe::kGemmMaxGrid;
+    if (N > 0) {
+        const int row_vecs = s.H * 2 / 16;
+        const int64_t n = N * row_vecs;
+        const unsigned gb = (unsigned)((n + kThreads - 1) / kThreads);
+        gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
+                                                    static_cast<const uint4*>(buf),
+                                                    reinterpret_cast<uint4*>(ws + B.xs));
+        gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
+                                                    static_cast<const uint4*>(dy),
+                                                    reinterpret_cast<uint4*>(ws + B.dys));
+        if ((e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
+        if ((e = launch_kind<kDH>(a, grid, st)) != hipSuccess) return e;
+        if ((e = launch_kind<kDX>(a, grid, st)) != hipSuccess) return e;
+    }
+    if ((e = launch_kind<kWD>(a, grid, st)) != hipSuccess) return e;
+    return launch_kind<kWGU>(a, grid, st);
+}

@@ -34,6 +34,17 @@ __device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// The same copy from a per-lane 64-bit address (no uniform base): for
+// operands whose rows come from several places (a zero page for padding).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_at(const void* addr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(addr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in bits 15:14)
 template <int VM>
@@ -68,6 +79,24 @@ __device__ __forceinline__ T* uni_ptr(T* p)
 __device__ __forceinline__ bf16x8 lds_frag(const char* p)
 {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// MFMA fragment from a k-major LDS tile (rows = k, contiguous along m) with
+// gfx950's transposing LDS read: within each 16-lane group, lane j of the
+// result gets element j of the 16 x 4 block the group's lanes read (lane i
+// reads 4 consecutive m at k-row i / 4), i.e. one column m, four k-rows. Two
+// reads (k-rows 0-3 and 4-7 of the lane's eight) make the 8-element operand.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 lds_frag_tr(const char* p0, const char* p1)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) char*)p0));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) char*)p1));
+    const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 }  // namespace lds

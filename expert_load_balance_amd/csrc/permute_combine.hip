@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int k, int64_t
         const int a = t * k + lane;
         const int dd = dest_row[a];
         d = (dd >= 0 && dd < nrows) ? dd : -1;
-        wl = w[a];
+        wl = w ? w[a] : 1.0f;  // no weights: the plain sum (dispatch's backward)
     }
     float acc[kVpl][V::kN];
 #pragma unroll

@@ -9,7 +9,9 @@
  *   moe_grouped_gemm SwiGLU expert FFN over the plan    (phase c)
  *   moe_combine      gate-weighted gather back to tokens (phase d)
  *   moe_stats        maxvio / balancedness / capacity / remote statistics
- * the replica slot pool (moe_prefetch_replicas, moe_grouped_gemm_slots); the
+ * the backward (moe_combine_backward, moe_ffn_backward, moe_permute_backward,
+ * moe_route_backward); the replica slot pool (moe_prefetch_replicas,
+ * moe_grouped_gemm_slots); the
  * two baselines the plan replaces: fixed-capacity dispatch (moe_capacity_*)
  * and static repacking (moe_repack); the router's scores (moe_router) and an
  * assumed balancing-bias update (moe_bias_update).
@@ -306,6 +308,59 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
                        const int32_t *d_mapping, const int32_t *d_origin, const int32_t *d_err,
                        double capacity_factor, void *d_ws, size_t ws_bytes, moe_stats_t *h_out,
                        int32_t *h_rank_loads, moe_stream_t stream);
+
+/* ---- Backward (training) ---------------------------------------------------
+ * [Primer] phases (a)-(d) in reverse, with the plan tables of the forward.
+ * [MoonEP] paragraph 3: replica gradients are reduced into the home expert --
+ * here every piece of an expert (home or replica) adds into that expert's one
+ * weight gradient. bf16 activations and weights (MOE_EUNSUPPORTED for fp32
+ * except moe_permute_backward and moe_route_backward). */
+
+/* Device workspace moe_ffn_backward needs: x and dy in expert order, the
+ * recomputed g | u, dg | du and h (about N * (2H + 5F) * 2 bytes), a
+ * schedule and a zero page. 0 on a bad shape or fp32. */
+size_t moe_backward_workspace_bytes(const moe_shape_t *shape);
+
+/* Combine backward. With out[t] = sum_j w[t][j] y[dest_row[t][j]]:
+ *   dy[dest_row[t][j]] = w[t][j] * dout[t]   (bf16, one rounding)
+ *   dw[t][j] = sum_h dout[t][h] * y[dest_row[t][j]][h]   (fp32 accumulate)
+ * Rows of dy that no assignment names are not written (with the equal-load
+ * plan every row is named once). d_dout dtype[T][H]; d_y dtype[N][H];
+ * d_dest_row int32[T][k]; d_w float[T][k]; d_dy dtype[N][H] out;
+ * d_dw float[T][k] out. */
+moe_status_t moe_combine_backward(const moe_shape_t *shape, const void *d_dout, const void *d_y,
+                                  const int32_t *d_dest_row, const float *d_w, void *d_dy,
+                                  float *d_dw, moe_stream_t stream);
+
+/* SwiGLU expert FFN backward over the plan (the moe_grouped_gemm forward's
+ * adjoint): recomputes g | u from d_buf, then
+ *   dh = dy W_down, dg = dh u s (1 + g (1 - s)), du = dh silu(g) (s the
+ *   logistic of g), dbuf = dg W_gate + du W_up,
+ *   dW_down[e] = sum over e's rows of dy h^T, dW_gate[e] = sum dg x^T,
+ *   dW_up[e] = sum du x^T   (fp32, overwritten; zero for idle experts).
+ * d_buf dtype[N][H] (the permuted input); d_plan the moe_plan block;
+ * weights as moe_grouped_gemm; d_dy dtype[N][H] (buffer order); d_dbuf
+ * dtype[N][H] out (buffer order); d_dw_gate, d_dw_up float[E][F][H] out;
+ * d_dw_down float[E][H][F] out; d_ws / ws_bytes >=
+ * moe_backward_workspace_bytes(shape). */
+moe_status_t moe_ffn_backward(const moe_shape_t *shape, const void *d_buf, const int32_t *d_plan,
+                              const void *d_w_gate, const void *d_w_up, const void *d_w_down,
+                              const void *d_dy, void *d_dbuf, float *d_dw_gate, float *d_dw_up,
+                              float *d_dw_down, void *d_ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Dispatch backward: dx[t] = sum_j dbuf[dest_row[t][j]] (fp32 accumulate in
+ * j order, one rounding). d_dbuf dtype[N][H]; d_dest_row int32[T][k];
+ * d_dx dtype[T][H] out. */
+moe_status_t moe_permute_backward(const moe_shape_t *shape, const void *d_dbuf,
+                                  const int32_t *d_dest_row, void *d_dx, moe_stream_t stream);
+
+/* Gate backward: w is the softmax of the selected raw logits, so
+ *   dlogits[t][ids[t][j]] = w[t][j] * (dw[t][j] - sum_j' w[t][j'] dw[t][j']),
+ * and 0 for experts not selected ([Interview] editor's note: the balancing
+ * bias only selects; it has no gradient here). d_ids int32[T][k];
+ * d_w, d_dw float[T][k]; d_dlogits float[T][E] out. */
+moe_status_t moe_route_backward(const moe_shape_t *shape, const int32_t *d_ids, const float *d_w,
+                                const float *d_dw, float *d_dlogits, moe_stream_t stream);
 
 /* ---- Router scores and the balancing bias ---------------------------------
  * [Primer] phase (a): the router scores every expert for every token. The

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 25
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -148,3 +148,24 @@ def test_pool_bytes_and_slot_rejections(lib):
                                       None) == 1                       # workspace too small
     assert lib.moe_grouped_gemm_slots(ctypes.byref(s), p, p, p, p, p, p, need - 1, p, p,
                                       1 << 30, None) == 1              # pool too small
+
+
+def test_backward_workspace_and_rejections(lib):
+    bf = moe.Shape(2048, 4096, 8, 2, 14336, 8, 1, moe.MOE_BF16)
+    N, H, F = 4096, 4096, 14336
+    b = moe.moe_backward_workspace_bytes(bf)
+    assert b >= N * (2 * H + 5 * F) * 2                      # x, dy, g|u, dg|du, h
+    assert moe.moe_backward_workspace_bytes(bf.replace(dtype=moe.MOE_F32)) == 0
+    assert moe.moe_backward_workspace_bytes(bf.replace(R=3)) == 0
+    s = moe.Shape(64, 128, 8, 2, 128, 4, 1, moe.MOE_BF16)
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    need = moe.moe_backward_workspace_bytes(s)
+    assert lib.moe_ffn_backward(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, p, need - 1,
+                                None) == 1                    # workspace too small
+    assert lib.moe_ffn_backward(ctypes.byref(s.replace(dtype=moe.MOE_F32)), p, p, p, p, p, p, p,
+                                p, p, p, p, 1 << 30, None) == 2
+    assert lib.moe_combine_backward(ctypes.byref(s), p, p, p, p, None, p, None) == 1
+    assert lib.moe_combine_backward(ctypes.byref(s.replace(dtype=moe.MOE_F32)), p, p, p, p, p, p,
+                                    None) == 2
+    assert lib.moe_permute_backward(ctypes.byref(s), None, p, p, None) == 1
+    assert lib.moe_route_backward(ctypes.byref(s), p, p, None, p, None) == 1

@@ -1,0 +1,176 @@
+"""GPU parity of the layer's backward (the chain rule of the forward: combine,
+SwiGLU expert FFN with the replicas' weight gradients summed into the home
+expert, dispatch, gate) against the CPU oracle, whose backward is pinned by
+central differences of the forward.
+
+Bar: bf16 outputs (dy, dbuf, dx) and the weight gradients -- fp32 stores,
+but computed through the bf16-rounded g, u, dg, du and h -- within
+2e-2 * max|ref|; dw and dlogits (fp32 from bf16 inputs) within 1e-5 * max|ref|.
+The oracle runs in double on the GPU's own bf16 inputs of each step.
+Full-size shapes check sampled rows of dbuf and sampled columns f of every
+weight gradient (the FFN splits over f, so the oracle on those columns gives
+the exact entries).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as wl
+
+torch = pytest.importorskip("torch")
+import expert_load_balance_amd as moe  # noqa: E402
+from expert_load_balance_amd.layer import alloc  # noqa: E402
+
+from test_gpu_parity import DEV, assert_tol, host, make_weights, run_layer  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+class Backward:
+    """Forward through the layer, then every backward entry point."""
+
+    def __init__(self, shape, lg, bias, seed):
+        s = shape
+        self.shape = s
+        act = torch.bfloat16
+        self.x = synth.device_normal((s.T, s.H), 1.0, seed, act, DEV)
+        self.wts = make_weights(s.E, s.F, s.H, s.dtype, seed)
+        self.L = run_layer(s, lg, bias, self.x, self.wts)
+        L = self.L
+        self.dout = synth.device_normal((s.T, s.H), 1.0, seed + 100, act, DEV)
+        self.dy = alloc((s.N, s.H), act, DEV)
+        self.dw = alloc((s.T, s.k), torch.float32, DEV)
+        moe.moe_combine_backward(s, self.dout, L.y, L.dest_row, L.w, self.dy, self.dw)
+        self.dbuf = alloc((s.N, s.H), act, DEV)
+        self.dW = [alloc((s.E, s.F, s.H), torch.float32, DEV), alloc((s.E, s.F, s.H), torch.float32, DEV),
+                   alloc((s.E, s.H, s.F), torch.float32, DEV)]
+        for t in self.dW:
+            t.fill_(float("nan"))                     # every entry must be written
+        self.ws = alloc((moe.moe_backward_workspace_bytes(s),), torch.uint8, DEV)
+        moe.moe_ffn_backward(s, L.buf, L.plan, *self.wts, self.dy, self.dbuf, *self.dW, self.ws)
+        self.dx = alloc((s.T, s.H), act, DEV)
+        moe.moe_permute_backward(s, self.dbuf, L.dest_row, self.dx)
+        self.dlogits = alloc((s.T, s.E), torch.float32, DEV)
+        moe.moe_route_backward(s, L.ids, L.w, self.dw, self.dlogits)
+        torch.cuda.synchronize()
+        self.pl = {k_: host(v) for k_, v in moe.plan_tables(L.plan, s).items()}
+
+
+SMALL = [
+    # name, T, H, E, k, F, R, bias strength
+    ("ragged_f", 300, 128, 8, 2, 192, 4, 0.6),
+    ("multi_tile", 700, 256, 8, 2, 384, 4, 0.5),
+    ("idle_experts", 100, 256, 16, 4, 128, 4, 3.0),
+    ("k1_tiny", 64, 64, 4, 1, 64, 2, 0.0),
+    ("many_experts", 512, 128, 64, 8, 64, 16, 0.8),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_small(case):
+    name, T, H, E, k, F, R, sb = case
+    _say(f"[case] backward {name}")
+    shape = moe.Shape(T, H, E, k, F, R, 1, moe.MOE_BF16)
+    lg = synth.router_logits(T, E, 51)
+    bias = synth.zipf_bias(E, sb, 51).astype(np.float32) if sb else None
+    b = Backward(shape, lg, bias, 52)
+    L = b.L
+    dest = host(L.dest_row)
+    y = host(L.y).astype(np.float64)
+    w = host(L.w).astype(np.float64)
+    dout = host(b.dout).astype(np.float64)
+    # combine backward on the GPU's own y and w
+    dy_ref, dw_ref = oracle.combine_backward(dout, y, dest, w)
+    assert_tol(host(b.dy), dy_ref, moe.MOE_BF16, "dy")
+    assert_tol(host(b.dw), dw_ref, moe.MOE_F32, "dw")
+    # FFN backward on the GPU's buf and dy
+    buf = host(L.buf).astype(np.float64)
+    dyg = host(b.dy).astype(np.float64)
+    wh = [host(t).astype(np.float64) for t in b.wts]
+    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dyg, b.pl, *wh)
+    assert_tol(host(b.dbuf), dbuf_ref, moe.MOE_BF16, "dbuf")
+    for got, ref, nm in zip(b.dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
+        g = host(got)
+        assert np.isfinite(g).all(), nm
+        assert_tol(g, ref, moe.MOE_BF16, nm)
+    idle = np.where(host(L.counts) == 0)[0]
+    for e in idle:                                   # experts nobody chose: zero gradients
+        assert not host(b.dW[0][e]).any() and not host(b.dW[2][e]).any()
+    # dispatch and gate backward
+    assert_tol(host(b.dx), oracle.permute_backward(host(b.dbuf).astype(np.float64), dest),
+               moe.MOE_BF16, "dx")
+    dl_ref = oracle.route_backward(host(L.ids), w, host(b.dw).astype(np.float64), E)
+    assert_tol(host(b.dlogits), dl_ref, moe.MOE_F32, "dlogits")
+    if name == "idle_experts":
+        assert len(idle) > 0
+
+
+def test_backward_chain_against_the_oracle_layer():
+    """The whole chain from dout, every step in the oracle (double, from the
+    forward's bf16 inputs): dx, dlogits and the weight gradients."""
+    T, H, E, k, F, R = 256, 128, 8, 2, 128, 4
+    shape = moe.Shape(T, H, E, k, F, R, 1, moe.MOE_BF16)
+    lg = synth.router_logits(T, E, 53)
+    bias = synth.zipf_bias(E, 0.7, 53).astype(np.float32)
+    b = Backward(shape, lg, bias, 54)
+    ids, w, _ = oracle.route(lg, bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    xh = host(b.x).astype(np.float64)
+    buf, dest, _ = oracle.permute(xh, ids, c["eidx"], pl)
+    wh = [host(t).astype(np.float64) for t in b.wts]
+    y = np.zeros((T * k, H))
+    for e in range(E):
+        rows = [r for p in range(pl["piece_num"][e])
+                for r in range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p])]
+        if rows:
+            y[rows] = oracle.ffn_rows(buf[rows], wh[0][e], wh[1][e], wh[2][e])
+    dy, dw = oracle.combine_backward(host(b.dout).astype(np.float64), y, dest, w)
+    dbuf, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dy, pl, *wh)
+    assert_tol(host(b.dx), oracle.permute_backward(dbuf, dest), moe.MOE_BF16, "dx (chain)")
+    assert_tol(host(b.dlogits), oracle.route_backward(ids, w, dw, E), moe.MOE_BF16,
+               "dlogits (chain)")
+    for got, ref, nm in zip(b.dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
+        assert_tol(host(got), ref, moe.MOE_BF16, nm + " (chain)")
+
+
+@pytest.mark.parametrize("name,maxvio", [("mixtral", 0.2), ("a3b", 1)])
+def test_backward_full_size(name, maxvio):
+    _say(f"[case] backward full {name}@{maxvio}")
+    torch.cuda.empty_cache()
+    w_ = wl.WORKLOADS[name]
+    T, H, E, k, F, R, S = (w_[c] for c in ("T", "H", "E", "k", "F", "R", "S"))
+    shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
+    lg, bias = wl.logits_and_bias(name, maxvio)
+    b = Backward(shape, lg, bias, w_["seed"])
+    L, pl = b.L, b.pl
+    counts = host(L.counts)
+    for t, nm in zip(b.dW, ("dW_gate", "dW_up", "dW_down")):
+        assert bool(torch.isfinite(t).all()), nm
+    rng = np.random.default_rng(9)
+    e = int(np.argmax(counts))                      # the hottest expert: home + replica pieces
+    rows = np.array([r for p in range(pl["piece_num"][e])
+                     for r in range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p])])
+    assert pl["piece_num"][e] >= 1 and len(rows) == counts[e]
+    xr = host(L.buf[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    dyr = host(b.dy[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    wg, wu, wd = (host(t[e]).astype(np.float64) for t in b.wts)
+    # sampled columns f of the weight gradients (exact: the FFN splits over f)
+    fs = np.sort(rng.choice(F, 6, replace=False))
+    _, g_s, u_s, d_s = oracle.ffn_backward_rows(xr, dyr, wg[fs], wu[fs], wd[:, fs])
+    assert_tol(host(b.dW[0][e])[fs], g_s, moe.MOE_BF16, "dW_gate (sampled f)")
+    assert_tol(host(b.dW[1][e])[fs], u_s, moe.MOE_BF16, "dW_up (sampled f)")
+    assert_tol(host(b.dW[2][e])[:, fs], d_s, moe.MOE_BF16, "dW_down (sampled f)")
+    # sampled rows of dbuf (full F)
+    pick = rng.choice(len(rows), 3, replace=False)
+    dx_s, _, _, _ = oracle.ffn_backward_rows(xr[pick], dyr[pick], wg, wu, wd)
+    assert_tol(host(b.dbuf[torch.from_numpy(rows[pick]).to(DEV)]), dx_s, moe.MOE_BF16,
+               "dbuf (sampled rows)")
+    # experts with no rows have zero gradients
+    for e0 in np.where(counts == 0)[0][:2]:
+        assert not bool(b.dW[2][int(e0)].any())
