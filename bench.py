@@ -197,6 +197,57 @@ def time_router(shape, x, bias, seed, act, stream):
     return t, nbytes
 
 
+def time_backward(shape, L, wts, seed, stream):
+    """The layer's backward from a seeded dout: combine, the expert FFN
+    (recompute + dgrad + wgrad), dispatch and gate backward, each back to back
+    on the stream, and the whole chain once per call."""
+    import torch
+
+    import expert_load_balance_amd as moe
+    import synth
+
+    T, H, E, k, F = shape.T, shape.H, shape.E, shape.k, shape.F
+    N = T * k
+    dev = "cuda"
+    act = torch.bfloat16
+    dout = synth.device_normal((T, H), 1.0, seed * 10 + 7, act, dev)
+    dy = torch.empty((N, H), dtype=act, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dbuf = torch.empty((N, H), dtype=act, device=dev)
+    dx = torch.empty((T, H), dtype=act, device=dev)
+    dl = torch.empty((T, E), dtype=torch.float32, device=dev)
+    dW = [torch.empty((E, F, H), dtype=torch.float32, device=dev),
+          torch.empty((E, F, H), dtype=torch.float32, device=dev),
+          torch.empty((E, H, F), dtype=torch.float32, device=dev)]
+    ws = torch.empty(moe.moe_backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    c_comb = moe.bind(moe.moe_combine_backward, shape, dout, L.y, L.dest_row, L.w, dy, dw,
+                      stream=stream)
+    c_ffn = moe.bind(moe.moe_ffn_backward, shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws,
+                     stream=stream)
+    c_perm = moe.bind(moe.moe_permute_backward, shape, dbuf, L.dest_row, dx, stream=stream)
+    c_route = moe.bind(moe.moe_route_backward, shape, L.ids, L.w, dw, dl, stream=stream)
+
+    def chain():
+        c_comb()
+        c_ffn()
+        c_perm()
+        c_route()
+
+    t_comb = time_back_to_back(c_comb, reps=20)
+    t_ffn = time_back_to_back(c_ffn, reps=5)
+    t_perm = time_back_to_back(c_perm, reps=20)
+    t_route = time_back_to_back(c_route, reps=20)
+    t_all = time_back_to_back(chain, reps=5)
+    flops_exec = 16.0 * N * H * F   # g|u recompute 4, dh 2, dx 4, dW_down 2, dW_gate|up 4
+    flops_alg = 12.0 * N * H * F    # without the recompute
+    del dW, ws
+    return dict(ms=t_all * 1e3, combine_backward_us=t_comb * 1e6, ffn_backward_ms=t_ffn * 1e3,
+                permute_backward_us=t_perm * 1e6, route_backward_us=t_route * 1e6,
+                ffn_backward_tflops=flops_exec / t_ffn / 1e12,
+                ffn_backward_mfma_frac=flops_exec / t_ffn / 1e12 / PEAK_BF16_TFLOPS,
+                ffn_backward_alg_tflops=flops_alg / t_ffn / 1e12)
+
+
 def time_slots(shape, L, lg, bias, x, wts, shared, steps, stream):
     """Replica slots: the prefetch copy of every filled slot, the grouped GEMM
     by plan segment reading them beside the expert-grouped GEMM, and the whole
@@ -311,6 +362,10 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
     if extras and moe.moe_pool_bytes(shape):
         slots = time_slots(shape, L, lg, bias, x, wts, shared, steps, stream)
 
+    bwd = None
+    if extras and dtype == moe.MOE_BF16:
+        bwd = time_backward(shape, L, wts, w["seed"], stream)
+
     cap_res = None
     if capacity_factor is not None and extras:
         cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
@@ -336,7 +391,7 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
         permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res, slots=slots,
+        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res, slots=slots, backward=bwd,
         # weight-streaming view of the two GEMM calls: every active expert's
         # three projections read once (the bound when rows per expert are few)
         gemm_weight_hbm_frac=st["active_experts"] * 3.0 * F * H * b / (gu_s + dn_s) / 1e9
@@ -423,6 +478,9 @@ def main():
         "fixed_capacity_baseline": r["capacity"],
         "router_scores_topk": r["router"],
         "replica_slots": r["slots"],
+        "backward": None if r["backward"] is None else dict(
+            r["backward"], train_step_tokens_per_s=r["tokens_per_s"] * r["ms_per_step"]
+            / (r["ms_per_step"] + r["backward"]["ms"])),
         "gemm_weight_hbm_frac": r["gemm_weight_hbm_frac"],
     }
     if not args.no_cpu_baseline:
@@ -447,6 +505,8 @@ def main():
                 "combine_hbm_frac": round(q["combine_hbm_frac"], 4),
                 "router_us": round(q["router"]["us"], 2),
                 "gemm_weight_hbm_frac": round(q["gemm_weight_hbm_frac"], 4),
+                "backward": None if q["backward"] is None else {
+                    k_: round(v_, 3) for k_, v_ in q["backward"].items()},
                 "replica_slots": None if q["slots"] is None else {
                     k_: round(v_, 3) if isinstance(v_, float) else v_
                     for k_, v_ in q["slots"].items()},

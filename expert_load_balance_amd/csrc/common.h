@@ -133,8 +133,16 @@ inline WsLayout ws_layout(const moe_shape_t& s)
 // by-expert schedule with 256-row M-tiles, the expert-order row map, a zero
 // page, x and dy in expert order, the recomputed g | u, dg | du and h.
 struct BwdWsLayout {
-    size_t sched, vrow, zero, xs, dys, gu, dgu, hb, total;
+    size_t sched, vrow, zero, xs, dys, gu, dgu, hb, dxpart, total;
 };
+// Bound on the dx GEMM's K-split: 4 when its tiles (at most N/256 + E
+// M-tiles x H/256 N-tiles) cannot fill four rounds of the persistent grid.
+inline int bwd_dx_split_max(const moe_shape_t& s)
+{
+    const int64_t N = (int64_t)s.T * s.k;
+    const int64_t tiles = (N / kGemmTile + s.E) * ((s.H + kGemmTile - 1) / kGemmTile);
+    return tiles >= 4 * kGemmMaxGrid ? 1 : 4;
+}
 inline BwdWsLayout bwd_ws_layout(const moe_shape_t& s)
 {
     const size_t N = (size_t)s.T * s.k;
@@ -149,6 +157,8 @@ inline BwdWsLayout bwd_ws_layout(const moe_shape_t& s)
     b.gu = o;    o = align256(o + n1 * 2 * s.F * 2);
     b.dgu = o;   o = align256(o + n1 * 2 * s.F * 2);
     b.hb = o;    o = align256(o + n1 * s.F * 2);
+    const int sp = bwd_dx_split_max(s);
+    b.dxpart = o; o = align256(o + (sp > 1 ? (size_t)sp * n1 * s.H * 4 : 4));
     b.total = o;
     return b;
 }

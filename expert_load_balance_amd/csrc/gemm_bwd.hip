@@ -46,7 +46,7 @@ constexpr int kSlot = 2 * kOp;   // A, then B
 enum Kind { kGU = 0, kDH = 1, kDX = 2, kWD = 3, kWGU = 4 };
 
 struct BwdArgs {
-    int G, H, F;
+    int G, H, F, N;
     const int32_t* sched;  // by-expert schedule, 256-row M-tiles, no skinny tiles
     const int32_t* vrow;   // expert-order row -> buffer row
     const uint16_t* xs;    // x in expert order [N][H]
@@ -58,7 +58,29 @@ struct BwdArgs {
     uint16_t* dxbuf;       // [N][H], buffer order
     float *dwg, *dwu, *dwd;
     const char* zero;      // >= 512 zero bytes
+    int dx_split_max;      // DX K-split bound (partials allocated for it)
+    float* dxpart;         // DX partials [split][N][H], expert order
 };
+
+// DX K-split: the part count in [1, smax] that fills the workgroups best
+// (ties: fewer parts), each part at least 8 stages. Few, long tiles (a few
+// experts with a wide F) otherwise leave a round of workgroups mostly idle.
+__host__ __device__ inline int dx_split(int tiles, int P, int smax, int stages)
+{
+    int best = 1;
+    double best_u = 0.0;
+    for (int sp = 1; sp <= smax; ++sp) {
+        if (sp > 1 && stages / sp < 8) break;
+        const long units = (long)tiles * sp;
+        const long rounds = (units + P - 1) / P;
+        const double u = rounds > 0 ? (double)units / (double)(rounds * P) : 1.0;
+        if (u > best_u + 1e-9) {
+            best_u = u;
+            best = sp;
+        }
+    }
+    return best;
+}
 
 // chunk swizzle of a k-major row: 4 consecutive k-rows cover all 64 banks
 __device__ __forceinline__ int kswz(int kr) { return (kr & 3) << 2; }
@@ -133,7 +155,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
                                                                       : (H + kT - 1) / kT;
     const int mtw = KIND == kWD ? (H + kT - 1) / kT : (2 * F + kT - 1) / kT;
     const int ntw = KIND == kWD ? (F + kT - 1) / kT : (H + kT - 1) / kT;
-    const int total = tiles_total<KIND>(a, ntn, mtw, ntw);
+    const int tiles = tiles_total<KIND>(a, ntn, mtw, ntw);
+    const int nsplit = KIND == kDX ? dx_split(tiles, gridDim.x, a.dx_split_max, 2 * F / kK) : 1;
+    const int total = tiles * nsplit;  // units: part-major, then tile
 
     const int tid = threadIdx.x;
     const int wave = uni(tid >> 6), lane = tid & 63;
@@ -168,10 +192,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
         xb[i] = (uint32_t)(((wn * 4 + i) ^ lx) << 6);
     }
 
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        const Tile tl = tile_at<KIND>(t, a, ntn, mtw, ntw);
+    // each XCD (workgroups are dealt to the 8 XCDs round-robin) takes a
+    // contiguous run of tiles, so tiles sharing an operand share that L2
+    const int P = gridDim.x;
+    const int my_slot = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
+    for (int u = my_slot; u < total; u += P) {
+        const int part = u / tiles;
+        const Tile tl = tile_at<KIND>(u % tiles, a, ntn, mtw, ntw);
         const int e = uni(tl.e), m0 = uni(tl.m0), n0 = uni(tl.n0), rows = uni(tl.rows);
-        const int hrow0 = uni(tl.hrow0), ns = uni(tl.ns);
+        // this unit's K stages [s0, s0 + ns) of the tile's tl.ns
+        const int s0 = uni(part * tl.ns / nsplit);
+        const int hrow0 = uni(tl.hrow0), ns = uni((part + 1) * tl.ns / nsplit - s0);
         const size_t FH = (size_t)F * H;
 
         // K-contiguous operands (uniform base + 32-bit lane offsets, as in the
@@ -190,6 +221,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
                 const int row = 8 * (wave + 4 * i) + (lane >> 3);
                 aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)lda * 2u +
                           (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+            }
+        }
+        // dgrad k-major weights (DH: W_down rows h; DX: W_gate / W_up rows f):
+        // K is never ragged there, so a uniform base per stage and one 32-bit
+        // lane offset per copy; columns past the end repeat the last chunk
+        // (those output columns are dropped)
+        if (KIND == kDH || KIND == kDX) {
+            const int ld = KIND == kDH ? F : H;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = wave + 4 * i;
+                const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
+                const int col = min(n0 + 8 * c, ld - 8);
+                boff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)col * 2u;
             }
         }
         if (!TR::kBC) {  // GU: rows n of [W_gate; W_up] (F % 8 == 0: one side per copy)
@@ -211,22 +256,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
             if (KIND == kWD) return col < H ? (const char*)(a.dys + (size_t)(hrow0 + k) * H + col) : nullptr;
             return col < 2 * F ? (const char*)(a.dgu + (size_t)(hrow0 + k) * 2 * F + col) : nullptr;
         };
-        auto b_krow = [&](int k, int c) -> const char* {
+        auto b_krow = [&](int k, int c) -> const char* {  // weight gradients only
             const int col = n0 + 8 * c;
-            if (KIND == kDH)  // k = h: W_down[e][h][col]
-                return col < F ? (const char*)(a.wd + e * FH + (size_t)k * F + col) : nullptr;
-            if (KIND == kDX)  // k = f in [0, 2F): W_gate / W_up rows
-                return col >= H ? nullptr
-                       : k < F  ? (const char*)(a.wg + e * FH + (size_t)k * H + col)
-                                : (const char*)(a.wu + e * FH + (size_t)(k - F) * H + col);
             if (k >= rows) return nullptr;
             if (KIND == kWD) return col < F ? (const char*)(a.hb + (size_t)(hrow0 + k) * F + col) : nullptr;
             return col < H ? (const char*)(a.xs + (size_t)(hrow0 + k) * H + col) : nullptr;  // WGU
         };
 
-        // stage s into slot s & 1: 32 copies per operand, q = wave + 4 i
-        auto copy_stage = [&](int s) {
-            const uint32_t slot = slots_u + (uint32_t)(s & 1) * kSlot;
+        // local stage j (absolute s = s0 + j) into slot j & 1: 32 copies per
+        // operand, q = wave + 4 i
+        auto copy_stage = [&](int j) {
+            const uint32_t slot = slots_u + (uint32_t)(j & 1) * kSlot;
+            const int s = s0 + j;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int q = wave + 4 * i;
@@ -238,10 +279,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
                     copy16(abase + s * (kK * 2), aoff[i], slot + q * 1024);
                 }
             }
+            // DH / DX: this stage's 64 weight rows start at a uniform base
+            const char* wbase = nullptr;
+            if (KIND == kDH) {
+                wbase = reinterpret_cast<const char*>(a.wd + e * FH + (size_t)s * kK * F);
+            } else if (KIND == kDX) {
+                const int k0 = s * kK;  // F % 64 == 0: a stage is all gate or all up
+                wbase = k0 < F ? reinterpret_cast<const char*>(a.wg + e * FH + (size_t)k0 * H)
+                               : reinterpret_cast<const char*>(a.wu + e * FH + (size_t)(k0 - F) * H);
+            }
+            wbase = uni_ptr(wbase);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int q = wave + 4 * i;
-                if (TR::kBC) {
+                if (KIND == kDH || KIND == kDX) {
+                    copy16(wbase, boff[i], slot + kOp + q * 1024);
+                } else if (TR::kBC) {
                     const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
                     const char* p = b_krow(s * kK + kr, c);
                     copy16_at(p ? p : zero + c * 16, slot + kOp + q * 1024);
@@ -259,40 +312,86 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+        // Two stages in flight: stage s's fragments are all read into
+        // registers during its first two k-steps, then (every wave done
+        // reading) its slot takes stage s + 2 while k-steps 2 and 3 run.
+        constexpr int kCopies = 16;  // copy instructions per wave per stage
         wait_vm_lgkm<0>();
-        slot_barrier();  // the previous tile's last slot is no longer read
+        slot_barrier();  // the previous tile's slots are no longer read
         if (ns > 0) copy_stage(0);
+        if (ns > 1) copy_stage(1);
         for (int s = 0; s < ns; ++s) {
-            wait_vm_lgkm<0>();
-            slot_barrier();  // stage s landed in every wave; slot (s+1) & 1 is free
-            if (s + 1 < ns) copy_stage(s + 1);
+            if (s + 1 < ns) wait_vm_lgkm<kCopies>();  // stage s landed; s+1 may be in flight
+            else wait_vm_lgkm<0>();
+            slot_barrier();
             const char* sa = slots + (s & 1) * kSlot;
             const char* sb = sa + kOp;
+            bf16x8 af[4][4], bfr[4][4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 af[4], bfr[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int blk = wm * 4 + i;  // 32-row / 32-column block of A
-                    af[i] = TR::kAC ? lds_frag_tr(sa + fcol0[kk] + xa[i], sa + fcol1[kk] + xa[i])
-                                    : lds_frag(sa + frow[kk] + blk * 4096);
+                    af[kk][i] = TR::kAC ? lds_frag_tr(sa + fcol0[kk] + xa[i], sa + fcol1[kk] + xa[i])
+                                        : lds_frag(sa + frow[kk] + blk * 4096);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int blk = wn * 4 + j;
-                    bfr[j] = TR::kBC ? lds_frag_tr(sb + fcol0[kk] + xb[j], sb + fcol1[kk] + xb[j])
-                                     : lds_frag(sb + frow[kk] + blk * 4096);
+                    bfr[kk][j] = TR::kBC ? lds_frag_tr(sb + fcol0[kk] + xb[j], sb + fcol1[kk] + xb[j])
+                                         : lds_frag(sb + frow[kk] + blk * 4096);
                 }
+            }
+            // dgrad: B first, so a lane holds 4 consecutive output columns
+            // (8-byte bf16 stores); weight gradients: A first, so 32 lanes
+            // hold 32 consecutive columns of one row (128-byte fp32 stores)
+            auto mfmas = [&](int kk) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-                // one k-step's fragments live at a time (no register spills)
-                __builtin_amdgcn_sched_barrier(0);
+                        acc[i][j] = TR::kWgrad
+                            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0);
+            };
+            mfmas(0);
+            mfmas(1);
+            if (s + 2 < ns) {
+                // every fragment of stage s is in registers (lgkmcnt(0)) in
+                // every wave: its slot is free; stage s+1 may still be landing
+                wait_vm_lgkm<kCopies>();
+                slot_barrier();
+                copy_stage(s + 2);
             }
+            mfmas(2);
+            mfmas(3);
         }
 
+        if (TR::kWgrad) {
+            // acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + 8 g4 + 4 fh + q,
+            // 128 wn + 32 j + fr): one fp32 store per value, 32 lanes along a row
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = n0 + wn * 128 + j * 32 + fr;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int row = m0 + wm * 128 + i * 32 + g4 * 8 + fh * 4 + q;
+                            const float v = acc[i][j][g4 * 4 + q];
+                            if (KIND == kWD) {
+                                if (row < H && col < F) a.dwd[e * FH + (size_t)row * F + col] = v;
+                            } else if (row < 2 * F && col < H) {
+                                float* dst = row < F ? a.dwg + e * FH + (size_t)row * H
+                                                     : a.dwu + e * FH + (size_t)(row - F) * H;
+                                dst[col] = v;
+                            }
+                        }
+                }
+            continue;
+        }
         // epilogue: acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + fr,
         // 128 wn + 32 j + 8 g4 + 4 fh + q) of the tile
 #pragma unroll
@@ -345,21 +444,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
                     } else if (KIND == kDX) {
                         const int col = n0 + n;
                         if (m >= rows || col >= H) continue;
+                        if (nsplit > 1) {  // fp32 partial, summed by dx_fixup_kernel
+                            float* dst = a.dxpart + ((size_t)part * a.N + hrow0 + m) * H + col;
+                            *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+                            continue;
+                        }
                         uint2 pk;
                         pk.x = moe::pack_bf16x2(v0, v1);
                         pk.y = moe::pack_bf16x2(v2, v3);
                         *reinterpret_cast<uint2*>(a.dxbuf + (size_t)a.vrow[hrow0 + m] * H + col) = pk;
-                    } else if (KIND == kWD) {
-                        const int row = m0 + m, col = n0 + n;
-                        if (row >= H || col >= F) continue;
-                        *reinterpret_cast<float4*>(a.dwd + e * FH + (size_t)row * F + col) =
-                            make_float4(v0, v1, v2, v3);
-                    } else {  // WGU
-                        const int row = m0 + m, col = n0 + n;
-                        if (row >= 2 * F || col >= H) continue;
-                        float* dst = row < F ? a.dwg + e * FH + (size_t)row * H
-                                             : a.dwu + e * FH + (size_t)(row - F) * H;
-                        *reinterpret_cast<float4*>(dst + col) = make_float4(v0, v1, v2, v3);
                     }
                 }
             }
@@ -377,6 +470,31 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int N, int row_ve
     if (i >= (int64_t)N * row_vecs) return;
     const int x = (int)(i / row_vecs), c = (int)(i % row_vecs);
     dst[i] = src[(size_t)vrow[x] * row_vecs + c];
+}
+
+// DX partials summed in part order, rounded once, rows scattered back to
+// buffer order. The part count is the DX kernel's own choice.
+__global__ __launch_bounds__(kThreads) void dx_fixup_kernel(BwdArgs a, int P)
+{
+    const int H = a.H;
+    const int tiles = a.sched[a.G] * ((H + kT - 1) / kT);
+    const int nsplit = dx_split(tiles, P, a.dx_split_max, 2 * a.F / kK);
+    if (nsplit <= 1) return;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 4 columns each
+    if (i >= (int64_t)a.N * (H / 4)) return;
+    const int x = (int)(i / (H / 4)), c = (int)(i % (H / 4)) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < nsplit; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(a.dxpart + ((size_t)p * a.N + x) * H + c);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 pk;
+    pk.x = moe::pack_bf16x2(acc.x, acc.y);
+    pk.y = moe::pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(a.dxbuf + (size_t)a.vrow[x] * H + c) = pk;
 }
 
 __global__ void zero_kernel(uint4* p, int n)
@@ -411,6 +529,9 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
     a.G = s.E;
     a.H = s.H;
     a.F = s.F;
+    a.N = (int)N;
+    a.dx_split_max = moe::bwd_dx_split_max(s);
+    a.dxpart = reinterpret_cast<float*>(ws + B.dxpart);
     a.sched = sched;
     a.vrow = vrow;
     a.xs = reinterpret_cast<const uint16_t*>(ws + B.xs);
@@ -440,6 +561,11 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
         if ((e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
         if ((e = launch_kind<kDH>(a, grid, st)) != hipSuccess) return e;
         if ((e = launch_kind<kDX>(a, grid, st)) != hipSuccess) return e;
+        if (a.dx_split_max > 1) {
+            const int64_t n4 = N * (s.H / 4);
+            dx_fixup_kernel<<<(unsigned)((n4 + kThreads - 1) / kThreads), kThreads, 0, st>>>(a, grid);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     if ((e = launch_kind<kWD>(a, grid, st)) != hipSuccess) return e;
     return launch_kind<kWGU>(a, grid, st);

@@ -68,6 +68,8 @@ SMALL = [
     ("idle_experts", 100, 256, 16, 4, 128, 4, 3.0),
     ("k1_tiny", 64, 64, 4, 1, 64, 2, 0.0),
     ("many_experts", 512, 128, 64, 8, 64, 16, 0.8),
+    # 2F / 64 = 16 stages and few tiles: the dx GEMM splits K in two parts
+    ("dx_k_split", 300, 256, 2, 1, 512, 2, 0.0),
 ]
 
 
