@@ -242,7 +242,7 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_
 
 size_t moe_backward_workspace_bytes(const moe_shape_t* shape)
 {
-    if (check(shape) != MOE_OK || shape->dtype != MOE_BF16) return 0;
+    if (check(shape) != MOE_OK) return 0;
     return moe::bwd_ws_layout(*shape).total;
 }
 
@@ -252,7 +252,6 @@ moe_status_t moe_combine_backward(const moe_shape_t* shape, const void* d_dout, 
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (shape->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
     const int64_t T = shape->T, N = T * shape->k;
     if (bad(d_dout, T) || bad(d_y, N) || bad(d_dest_row, N) || bad(d_w, N) || bad(d_dy, N) ||
         bad(d_dw, N))
@@ -268,7 +267,6 @@ moe_status_t moe_ffn_backward(const moe_shape_t* shape, const void* d_buf, const
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
-    if (shape->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
     const int64_t N = (int64_t)shape->T * shape->k;
     if (bad(d_buf, N) || !d_plan || !d_w_gate || !d_w_up || !d_w_down || bad(d_dy, N) ||
         bad(d_dbuf, N) || !d_dw_gate || !d_dw_up || !d_dw_down || !d_ws)

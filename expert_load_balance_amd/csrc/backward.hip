@@ -18,9 +18,10 @@ namespace {
 constexpr int kThreads = 256;
 
 // One wavefront per token: the wave walks the row in 1 KB chunks (one
-// 16-byte vector per lane), writes the k scaled rows of dy and accumulates
-// the k dot products per lane; a butterfly adds the lanes at the end, so dw
-// does not depend on timing.
+// 16-byte vector per lane: 8 bf16 or 4 fp32), writes the k scaled rows of dy
+// and accumulates the k dot products per lane; a butterfly adds the lanes at
+// the end, so dw does not depend on timing.
+template <bool BF16>
 __global__ __launch_bounds__(kThreads) void combine_backward_kernel(int T, int k, int64_t nrows,
                                                                     int row_vecs,
                                                                     const uint4* __restrict__ dout,
@@ -53,11 +54,17 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(int T, int k
                 uint32_t o[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float g0 = __uint_as_float(gw[q] << 16), g1 = __uint_as_float(gw[q] & 0xffff0000u);
-                    const float v0 = __uint_as_float(vw[q] << 16), v1 = __uint_as_float(vw[q] & 0xffff0000u);
-                    acc = fmaf(g0, v0, acc);
-                    acc = fmaf(g1, v1, acc);
-                    o[q] = moe::pack_bf16x2(wj * g0, wj * g1);
+                    if (BF16) {
+                        const float g0 = __uint_as_float(gw[q] << 16), g1 = __uint_as_float(gw[q] & 0xffff0000u);
+                        const float v0 = __uint_as_float(vw[q] << 16), v1 = __uint_as_float(vw[q] & 0xffff0000u);
+                        acc = fmaf(g0, v0, acc);
+                        acc = fmaf(g1, v1, acc);
+                        o[q] = moe::pack_bf16x2(wj * g0, wj * g1);
+                    } else {
+                        const float g0 = __uint_as_float(gw[q]), v0 = __uint_as_float(vw[q]);
+                        acc = fmaf(g0, v0, acc);
+                        o[q] = __float_as_uint(wj * g0);
+                    }
                 }
                 dy[(size_t)dj * row_vecs + c] = make_uint4(o[0], o[1], o[2], o[3]);
             }
@@ -97,11 +104,19 @@ hipError_t moe_launch_combine_backward(const moe_shape_t& s, const void* dout, c
                                        float* dw, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
-    const int row_vecs = s.H * 2 / 16;
+    const bool bf = s.dtype == MOE_BF16;
+    const int row_vecs = s.H * (bf ? 2 : 4) / 16;
     const int grid = (s.T + kThreads / 64 - 1) / (kThreads / 64);
-    combine_backward_kernel<<<grid, kThreads, 0, st>>>(
-        s.T, s.k, (int64_t)s.T * s.k, row_vecs, static_cast<const uint4*>(dout),
-        static_cast<const uint4*>(y), dest_row, w, static_cast<uint4*>(dy), dw);
+    const uint4* dv = static_cast<const uint4*>(dout);
+    const uint4* yv = static_cast<const uint4*>(y);
+    uint4* dyv = static_cast<uint4*>(dy);
+    const int64_t nrows = (int64_t)s.T * s.k;
+    if (bf)
+        combine_backward_kernel<true><<<grid, kThreads, 0, st>>>(s.T, s.k, nrows, row_vecs, dv, yv,
+                                                                 dest_row, w, dyv, dw);
+    else
+        combine_backward_kernel<false><<<grid, kThreads, 0, st>>>(s.T, s.k, nrows, row_vecs, dv, yv,
+                                                                  dest_row, w, dyv, dw);
     return hipGetLastError();
 }
 

@@ -152,12 +152,13 @@ inline BwdWsLayout bwd_ws_layout(const moe_shape_t& s)
     b.sched = o; o = align256(o + (size_t)(4 * (s.E + 1) + 64) * 4);
     b.vrow = o;  o = align256(o + n1 * 4);
     b.zero = o;  o = align256(o + 512);
-    b.xs = o;    o = align256(o + n1 * s.H * 2);
-    b.dys = o;   o = align256(o + n1 * s.H * 2);
-    b.gu = o;    o = align256(o + n1 * 2 * s.F * 2);
-    b.dgu = o;   o = align256(o + n1 * 2 * s.F * 2);
-    b.hb = o;    o = align256(o + n1 * s.F * 2);
-    const int sp = bwd_dx_split_max(s);
+    const size_t eb = s.dtype == MOE_BF16 ? 2 : 4;
+    b.xs = o;    o = align256(o + n1 * s.H * eb);
+    b.dys = o;   o = align256(o + n1 * s.H * eb);
+    b.gu = o;    o = align256(o + n1 * 2 * s.F * eb);
+    b.dgu = o;   o = align256(o + n1 * 2 * s.F * eb);
+    b.hb = o;    o = align256(o + n1 * s.F * eb);
+    const int sp = s.dtype == MOE_BF16 ? bwd_dx_split_max(s) : 1;
     b.dxpart = o; o = align256(o + (sp > 1 ? (size_t)sp * n1 * s.H * 4 : 4));
     b.total = o;
     return b;

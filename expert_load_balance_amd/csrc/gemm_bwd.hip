@@ -503,6 +503,108 @@ __global__ void zero_kernel(uint4* p, int n)
     if (i < n) p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// ---- fp32 (small shapes): one thread per output element, FMA in index
+// order, rows in expert order; e(x) by a search over row_start.
+__device__ __forceinline__ int expert_of_row(int x, int E, const int32_t* row_start)
+{
+    int lo = 0, hi = E - 1;  // last expert with row_start <= x (non-empty)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (row_start[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// per (row x, f): g, u, h; dh = dy . W_down[:, f]; dg, du
+__global__ __launch_bounds__(kThreads) void bwd_f32_rows_kernel(int N, int E, int H, int F,
+                                                                const int32_t* __restrict__ sched,
+                                                                const float* __restrict__ xs,
+                                                                const float* __restrict__ dys,
+                                                                const float* __restrict__ wg,
+                                                                const float* __restrict__ wu,
+                                                                const float* __restrict__ wd,
+                                                                float* __restrict__ dgu,
+                                                                float* __restrict__ hb)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)N * F) return;
+    const int x = (int)(i / F), f = (int)(i % F);
+    const int e = expert_of_row(x, E, sched + E + 1);
+    const size_t FH = (size_t)F * H;
+    const float* xr = xs + (size_t)x * H;
+    const float* dyr = dys + (size_t)x * H;
+    float g = 0.f, u = 0.f, dh = 0.f;
+    for (int c = 0; c < H; ++c) {
+        g = fmaf(wg[e * FH + (size_t)f * H + c], xr[c], g);
+        u = fmaf(wu[e * FH + (size_t)f * H + c], xr[c], u);
+        dh = fmaf(wd[e * FH + (size_t)c * F + f], dyr[c], dh);
+    }
+    const float s = 1.0f / (1.0f + expf(-g));
+    const float sl = g * s;
+    hb[(size_t)x * F + f] = sl * u;
+    dgu[(size_t)x * 2 * F + f] = dh * u * s * (1.0f + g * (1.0f - s));
+    dgu[(size_t)x * 2 * F + F + f] = dh * sl;
+}
+
+// per (row x, c): dx = dg . W_gate[:, c] + du . W_up[:, c], to buffer order
+__global__ __launch_bounds__(kThreads) void bwd_f32_dx_kernel(int N, int E, int H, int F,
+                                                              const int32_t* __restrict__ sched,
+                                                              const int32_t* __restrict__ vrow,
+                                                              const float* __restrict__ dgu,
+                                                              const float* __restrict__ wg,
+                                                              const float* __restrict__ wu,
+                                                              float* __restrict__ dbuf)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)N * H) return;
+    const int x = (int)(i / H), c = (int)(i % H);
+    const int e = expert_of_row(x, E, sched + E + 1);
+    const size_t FH = (size_t)F * H;
+    const float* d = dgu + (size_t)x * 2 * F;
+    float acc = 0.f;
+    for (int f = 0; f < F; ++f) {
+        acc = fmaf(wg[e * FH + (size_t)f * H + c], d[f], acc);
+        acc = fmaf(wu[e * FH + (size_t)f * H + c], d[F + f], acc);
+    }
+    dbuf[(size_t)vrow[x] * H + c] = acc;
+}
+
+// per (expert e, row m, column n) of the weight gradients, summed over e's
+// rows in order: dW_down[e][o][f] = sum dy[r][o] h[r][f];
+// dW_gate[e][f][c] = sum dg[r][f] x[r][c]; dW_up the same with du
+__global__ __launch_bounds__(kThreads) void bwd_f32_wgrad_kernel(int E, int H, int F,
+                                                                 const int32_t* __restrict__ sched,
+                                                                 const float* __restrict__ xs,
+                                                                 const float* __restrict__ dys,
+                                                                 const float* __restrict__ dgu,
+                                                                 const float* __restrict__ hb,
+                                                                 float* __restrict__ dwg,
+                                                                 float* __restrict__ dwu,
+                                                                 float* __restrict__ dwd)
+{
+    const size_t FH = (size_t)F * H;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)E * 3 * FH) return;
+    const int e = (int)(i / (3 * FH));
+    const size_t j = (size_t)(i % (3 * FH));
+    const int q = (int)(j / FH);
+    const size_t w = j % FH;
+    const int32_t* rs = sched + E + 1;
+    const int r0 = rs[e], r1 = rs[e + 1];
+    float acc = 0.f;
+    if (q == 2) {  // dW_down [H][F]
+        const int o = (int)(w / F), f = (int)(w % F);
+        for (int r = r0; r < r1; ++r) acc = fmaf(dys[(size_t)r * H + o], hb[(size_t)r * F + f], acc);
+        dwd[e * FH + w] = acc;
+    } else {  // dW_gate / dW_up [F][H]
+        const int f = (int)(w / H), c = (int)(w % H);
+        for (int r = r0; r < r1; ++r)
+            acc = fmaf(dgu[(size_t)r * 2 * F + q * F + f], xs[(size_t)r * H + c], acc);
+        (q == 0 ? dwg : dwu)[e * FH + w] = acc;
+    }
+}
+
 template <int KIND>
 hipError_t launch_kind(const BwdArgs& a, int grid, hipStream_t st)
 {
@@ -548,6 +650,35 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
     a.dwd = dw_down;
     a.zero = ws + B.zero;
     const int grid = moe::kGemmMaxGrid;
+    if (s.dtype == MOE_F32) {
+        const float* xs = reinterpret_cast<const float*>(ws + B.xs);
+        const float* dys = reinterpret_cast<const float*>(ws + B.dys);
+        float* dgu = reinterpret_cast<float*>(ws + B.dgu);
+        float* hb = reinterpret_cast<float*>(ws + B.hb);
+        const float* wgf = static_cast<const float*>(w_gate);
+        const float* wuf = static_cast<const float*>(w_up);
+        const float* wdf = static_cast<const float*>(w_down);
+        if (N > 0) {
+            const int row_vecs = s.H * 4 / 16;
+            const int64_t n = N * row_vecs;
+            const unsigned gb = (unsigned)((n + kThreads - 1) / kThreads);
+            gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
+                                                        static_cast<const uint4*>(buf),
+                                                        reinterpret_cast<uint4*>(ws + B.xs));
+            gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
+                                                        static_cast<const uint4*>(dy),
+                                                        reinterpret_cast<uint4*>(ws + B.dys));
+            const int64_t nf = N * s.F, nh = N * s.H;
+            bwd_f32_rows_kernel<<<(unsigned)((nf + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+                (int)N, s.E, s.H, s.F, sched, xs, dys, wgf, wuf, wdf, dgu, hb);
+            bwd_f32_dx_kernel<<<(unsigned)((nh + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+                (int)N, s.E, s.H, s.F, sched, vrow, dgu, wgf, wuf, static_cast<float*>(dbuf));
+        }
+        const int64_t nw = (int64_t)s.E * 3 * s.F * s.H;
+        bwd_f32_wgrad_kernel<<<(unsigned)((nw + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+            s.E, s.H, s.F, sched, xs, dys, dgu, hb, dw_gate, dw_up, dw_down);
+        return hipGetLastError();
+    }
     if (N > 0) {
         const int row_vecs = s.H * 2 / 16;
         const int64_t n = N * row_vecs;

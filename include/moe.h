@@ -313,12 +313,13 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
  * [Primer] phases (a)-(d) in reverse, with the plan tables of the forward.
  * [MoonEP] paragraph 3: replica gradients are reduced into the home expert --
  * here every piece of an expert (home or replica) adds into that expert's one
- * weight gradient. bf16 activations and weights (MOE_EUNSUPPORTED for fp32
- * except moe_permute_backward and moe_route_backward). */
+ * weight gradient. bf16 runs on MFMA; fp32 (small shapes such as the
+ * hotspot fixture) on plain FMA kernels, one thread per output element. */
 
 /* Device workspace moe_ffn_backward needs: x and dy in expert order, the
- * recomputed g | u, dg | du and h (about N * (2H + 5F) * 2 bytes), a
- * schedule and a zero page. 0 on a bad shape or fp32. */
+ * recomputed g | u, dg | du and h (about N * (2H + 5F) * dtype bytes), a
+ * schedule, a zero page and (bf16, few wide experts) fp32 partials of dx.
+ * 0 on a bad shape. */
 size_t moe_backward_workspace_bytes(const moe_shape_t *shape);
 
 /* Combine backward. With out[t] = sum_j w[t][j] y[dest_row[t][j]]:

@@ -155,17 +155,15 @@ def test_backward_workspace_and_rejections(lib):
     N, H, F = 4096, 4096, 14336
     b = moe.moe_backward_workspace_bytes(bf)
     assert b >= N * (2 * H + 5 * F) * 2                      # x, dy, g|u, dg|du, h
-    assert moe.moe_backward_workspace_bytes(bf.replace(dtype=moe.MOE_F32)) == 0
+    assert moe.moe_backward_workspace_bytes(bf.replace(dtype=moe.MOE_F32)) >= N * (2 * H + 5 * F) * 4
     assert moe.moe_backward_workspace_bytes(bf.replace(R=3)) == 0
     s = moe.Shape(64, 128, 8, 2, 128, 4, 1, moe.MOE_BF16)
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     need = moe.moe_backward_workspace_bytes(s)
     assert lib.moe_ffn_backward(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, p, need - 1,
                                 None) == 1                    # workspace too small
-    assert lib.moe_ffn_backward(ctypes.byref(s.replace(dtype=moe.MOE_F32)), p, p, p, p, p, p, p,
-                                p, p, p, p, 1 << 30, None) == 2
+    assert lib.moe_ffn_backward(ctypes.byref(s), p, None, p, p, p, p, p, p, p, p, p, 1 << 30,
+                                None) == 1                    # no plan
     assert lib.moe_combine_backward(ctypes.byref(s), p, p, p, p, None, p, None) == 1
-    assert lib.moe_combine_backward(ctypes.byref(s.replace(dtype=moe.MOE_F32)), p, p, p, p, p, p,
-                                    None) == 2
     assert lib.moe_permute_backward(ctypes.byref(s), None, p, p, None) == 1
     assert lib.moe_route_backward(ctypes.byref(s), p, p, None, p, None) == 1

@@ -3,9 +3,11 @@ SwiGLU expert FFN with the replicas' weight gradients summed into the home
 expert, dispatch, gate) against the CPU oracle, whose backward is pinned by
 central differences of the forward.
 
-Bar: bf16 outputs (dy, dbuf, dx) and the weight gradients -- fp32 stores,
-but computed through the bf16-rounded g, u, dg, du and h -- within
-2e-2 * max|ref|; dw and dlogits (fp32 from bf16 inputs) within 1e-5 * max|ref|.
+Bar (bf16 layers): bf16 outputs (dy, dbuf, dx) and the weight gradients --
+fp32 stores, but computed through the bf16-rounded g, u, dg, du and h --
+within 2e-2 * max|ref|; dw and dlogits (fp32 from bf16 inputs) within
+1e-5 * max|ref|. fp32 layers (the hotspot fixture and a random small shape):
+everything within 1e-5 * max|ref|.
 The oracle runs in double on the GPU's own bf16 inputs of each step.
 Full-size shapes check sampled rows of dbuf and sampled columns f of every
 weight gradient (the FFN splits over f, so the oracle on those columns gives
@@ -37,7 +39,7 @@ class Backward:
     def __init__(self, shape, lg, bias, seed):
         s = shape
         self.shape = s
-        act = torch.bfloat16
+        act = torch.bfloat16 if s.dtype == moe.MOE_BF16 else torch.float32
         self.x = synth.device_normal((s.T, s.H), 1.0, seed, act, DEV)
         self.wts = make_weights(s.E, s.F, s.H, s.dtype, seed)
         self.L = run_layer(s, lg, bias, self.x, self.wts)
@@ -73,13 +75,24 @@ SMALL = [
 ]
 
 
+SMALL_F32 = [
+    ("f32_random", 150, 96, 8, 2, 100, 4, 0.4, moe.MOE_F32),
+    ("f32_hotspot_fixture", 16, 64, 8, 2, 128, 4, None, moe.MOE_F32),
+]
+SMALL = [c + (moe.MOE_BF16,) for c in SMALL] + SMALL_F32
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_small(case):
-    name, T, H, E, k, F, R, sb = case
+    name, T, H, E, k, F, R, sb, dtype = case
     _say(f"[case] backward {name}")
-    shape = moe.Shape(T, H, E, k, F, R, 1, moe.MOE_BF16)
-    lg = synth.router_logits(T, E, 51)
-    bias = synth.zipf_bias(E, sb, 51).astype(np.float32) if sb else None
+    shape = moe.Shape(T, H, E, k, F, R, 1, dtype)
+    if sb is None:                                  # the page's 16 tokens
+        lg, bias = synth.fixture_logits(), None
+    else:
+        lg = synth.router_logits(T, E, 51)
+        bias = synth.zipf_bias(E, sb, 51).astype(np.float32) if sb else None
+    act_tol = dtype                                 # bf16 outputs: bf16 bar; fp32: fp32 bar
     b = Backward(shape, lg, bias, 52)
     L = b.L
     dest = host(L.dest_row)
@@ -88,24 +101,24 @@ def test_backward_small(case):
     dout = host(b.dout).astype(np.float64)
     # combine backward on the GPU's own y and w
     dy_ref, dw_ref = oracle.combine_backward(dout, y, dest, w)
-    assert_tol(host(b.dy), dy_ref, moe.MOE_BF16, "dy")
+    assert_tol(host(b.dy), dy_ref, act_tol, "dy")
     assert_tol(host(b.dw), dw_ref, moe.MOE_F32, "dw")
     # FFN backward on the GPU's buf and dy
     buf = host(L.buf).astype(np.float64)
     dyg = host(b.dy).astype(np.float64)
     wh = [host(t).astype(np.float64) for t in b.wts]
     dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dyg, b.pl, *wh)
-    assert_tol(host(b.dbuf), dbuf_ref, moe.MOE_BF16, "dbuf")
+    assert_tol(host(b.dbuf), dbuf_ref, act_tol, "dbuf")
     for got, ref, nm in zip(b.dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
         g = host(got)
         assert np.isfinite(g).all(), nm
-        assert_tol(g, ref, moe.MOE_BF16, nm)
+        assert_tol(g, ref, act_tol, nm)
     idle = np.where(host(L.counts) == 0)[0]
     for e in idle:                                   # experts nobody chose: zero gradients
         assert not host(b.dW[0][e]).any() and not host(b.dW[2][e]).any()
     # dispatch and gate backward
     assert_tol(host(b.dx), oracle.permute_backward(host(b.dbuf).astype(np.float64), dest),
-               moe.MOE_BF16, "dx")
+               act_tol, "dx")
     dl_ref = oracle.route_backward(host(L.ids), w, host(b.dw).astype(np.float64), E)
     assert_tol(host(b.dlogits), dl_ref, moe.MOE_F32, "dlogits")
     if name == "idle_experts":
