@@ -197,10 +197,11 @@ def time_router(shape, x, bias, seed, act, stream):
     return t, nbytes
 
 
-def time_backward(shape, L, wts, seed, stream):
+def time_backward(shape, L, lg, bias, x, wts, shared, seed, stream):
     """The layer's backward from a seeded dout: combine, the expert FFN
-    (recompute + dgrad + wgrad), dispatch and gate backward, each back to back
-    on the stream, and the whole chain once per call."""
+    (dgrad + wgrad, from the g | u a training forward kept; and with the
+    recompute), dispatch and gate backward, each back to back on the stream;
+    the whole chain; and a training step = the training forward + the chain."""
     import torch
 
     import expert_load_balance_amd as moe
@@ -220,10 +221,14 @@ def time_backward(shape, L, wts, seed, stream):
           torch.empty((E, F, H), dtype=torch.float32, device=dev),
           torch.empty((E, H, F), dtype=torch.float32, device=dev)]
     ws = torch.empty(moe.moe_backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    gu = torch.empty((N, 2 * F), dtype=act, device=dev)
+    L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, gu=gu)
     c_comb = moe.bind(moe.moe_combine_backward, shape, dout, L.y, L.dest_row, L.w, dy, dw,
                       stream=stream)
-    c_ffn = moe.bind(moe.moe_ffn_backward, shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws,
+    c_ffn = moe.bind(moe.moe_ffn_backward, shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws, gu=gu,
                      stream=stream)
+    c_ffn_re = moe.bind(moe.moe_ffn_backward, shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws,
+                        stream=stream)
     c_perm = moe.bind(moe.moe_permute_backward, shape, dbuf, L.dest_row, dx, stream=stream)
     c_route = moe.bind(moe.moe_route_backward, shape, L.ids, L.w, dw, dl, stream=stream)
 
@@ -233,19 +238,25 @@ def time_backward(shape, L, wts, seed, stream):
         c_perm()
         c_route()
 
+    def step():
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, gu=gu)
+        chain()
+
     t_comb = time_back_to_back(c_comb, reps=20)
     t_ffn = time_back_to_back(c_ffn, reps=5)
+    t_ffn_re = time_back_to_back(c_ffn_re, reps=5)
     t_perm = time_back_to_back(c_perm, reps=20)
     t_route = time_back_to_back(c_route, reps=20)
     t_all = time_back_to_back(chain, reps=5)
-    flops_exec = 16.0 * N * H * F   # g|u recompute 4, dh 2, dx 4, dW_down 2, dW_gate|up 4
-    flops_alg = 12.0 * N * H * F    # without the recompute
-    del dW, ws
+    t_step = time_back_to_back(step, reps=5)
+    flops = 12.0 * N * H * F      # dh 2, dx 4, dW_down 2, dW_gate|up 4 (x N H F)
+    del dW, ws, gu
     return dict(ms=t_all * 1e3, combine_backward_us=t_comb * 1e6, ffn_backward_ms=t_ffn * 1e3,
                 permute_backward_us=t_perm * 1e6, route_backward_us=t_route * 1e6,
-                ffn_backward_tflops=flops_exec / t_ffn / 1e12,
-                ffn_backward_mfma_frac=flops_exec / t_ffn / 1e12 / PEAK_BF16_TFLOPS,
-                ffn_backward_alg_tflops=flops_alg / t_ffn / 1e12)
+                ffn_backward_tflops=flops / t_ffn / 1e12,
+                ffn_backward_mfma_frac=flops / t_ffn / 1e12 / PEAK_BF16_TFLOPS,
+                ffn_backward_recompute_ms=t_ffn_re * 1e3,
+                train_step_ms=t_step * 1e3, train_step_tokens_per_s=T / t_step)
 
 
 def time_slots(shape, L, lg, bias, x, wts, shared, steps, stream):
@@ -364,7 +375,7 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
 
     bwd = None
     if extras and dtype == moe.MOE_BF16:
-        bwd = time_backward(shape, L, wts, w["seed"], stream)
+        bwd = time_backward(shape, L, lg, bias, x, wts, shared, w["seed"], stream)
 
     cap_res = None
     if capacity_factor is not None and extras:
@@ -478,9 +489,7 @@ def main():
         "fixed_capacity_baseline": r["capacity"],
         "router_scores_topk": r["router"],
         "replica_slots": r["slots"],
-        "backward": None if r["backward"] is None else dict(
-            r["backward"], train_step_tokens_per_s=r["tokens_per_s"] * r["ms_per_step"]
-            / (r["ms_per_step"] + r["backward"]["ms"])),
+        "backward": r["backward"],
         "gemm_weight_hbm_frac": r["gemm_weight_hbm_frac"],
     }
     if not args.no_cpu_baseline:

@@ -23,7 +23,7 @@ __all__ = [
     "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
     "bind", "moe_pool_bytes", "moe_prefetch_replicas", "moe_grouped_gemm_slots",
     "moe_backward_workspace_bytes", "moe_combine_backward", "moe_ffn_backward",
-    "moe_permute_backward", "moe_route_backward",
+    "moe_permute_backward", "moe_route_backward", "moe_grouped_gemm_train",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "moe_pool_bytes",
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
+    "moe_grouped_gemm_train",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -147,8 +148,10 @@ def load():
         "moe_pool_bytes": (ctypes.c_size_t, [_SP]),
         "moe_backward_workspace_bytes": (ctypes.c_size_t, [_SP]),
         "moe_combine_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
-        "moe_ffn_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+        "moe_ffn_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                   ctypes.c_size_t, _VP]),
+        "moe_grouped_gemm_train": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        ctypes.c_size_t, _VP]),
         "moe_permute_backward": (st, [_SP, _VP, _VP, _VP, _VP]),
         "moe_route_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP]),
         "moe_prefetch_replicas": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -554,8 +557,9 @@ def moe_combine_backward(shape, dout, y, dest_row, w, dy, dw, stream=None):
 
 
 def moe_ffn_backward(shape, buf, plan, w_gate, w_up, w_down, dy, dbuf, dw_gate, dw_up, dw_down,
-                     ws, stream=None):
-    """ws: a uint8 device tensor of at least moe_backward_workspace_bytes(shape)."""
+                     ws, gu=None, stream=None):
+    """ws: a uint8 device tensor of at least moe_backward_workspace_bytes(shape);
+    gu: None (recompute g | u) or moe_grouped_gemm_train's buffer."""
     import torch
 
     act, N = _act_dtype(shape), shape.N
@@ -564,7 +568,7 @@ def moe_ffn_backward(shape, buf, plan, w_gate, w_up, w_down, dy, dbuf, dw_gate, 
     _ok(load().moe_ffn_backward(
         ctypes.byref(shape), _ptr(buf, act, "buf", N * shape.H), _ptr(plan, torch.int32, "plan"),
         _ptr(w_gate, act, "w_gate", n), _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
-        _ptr(dy, act, "dy", N * shape.H), _ptr(dbuf, act, "dbuf", N * shape.H),
+        _ptr(gu, act, "gu", N * 2 * shape.F, nullable=True), _ptr(dy, act, "dy", N * shape.H), _ptr(dbuf, act, "dbuf", N * shape.H),
         _ptr(dw_gate, f32, "dw_gate", n), _ptr(dw_up, f32, "dw_up", n),
         _ptr(dw_down, f32, "dw_down", n), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_ffn_backward")
@@ -588,3 +592,17 @@ def moe_route_backward(shape, ids, w, dw, dlogits, stream=None):
         ctypes.byref(shape), _ptr(ids, torch.int32, "ids", N), _ptr(w, torch.float32, "w", N),
         _ptr(dw, torch.float32, "dw", N), _ptr(dlogits, torch.float32, "dlogits", shape.T * shape.E),
         _stream(stream)), "moe_route_backward")
+
+
+def moe_grouped_gemm_train(shape, a, plan, w_gate, w_up, w_down, y, gu, ws, stream=None):
+    """moe_grouped_gemm that also keeps g | u (bf16 [N][2F], expert order) in gu."""
+    import torch
+
+    act, N = _act_dtype(shape), shape.N
+    n = shape.E * shape.F * shape.H
+    _ok(load().moe_grouped_gemm_train(
+        ctypes.byref(shape), _ptr(a, act, "a", N * shape.H), _ptr(plan, torch.int32, "plan"),
+        _ptr(w_gate, act, "w_gate", n), _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
+        _ptr(y, act, "y", N * shape.H),
+        _ptr(gu, act, "gu", N * 2 * shape.F, nullable=shape.dtype != MOE_BF16),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_grouped_gemm_train")

@@ -228,6 +228,29 @@ moe_status_t moe_grouped_gemm_slots(const moe_shape_t* shape, const void* d_a,
     return dev(e);
 }
 
+moe_status_t moe_grouped_gemm_train(const moe_shape_t* shape, const void* d_a,
+                                    const int32_t* d_plan, const void* d_w_gate,
+                                    const void* d_w_up, const void* d_w_down, void* d_y,
+                                    void* d_gu, void* d_ws, size_t ws_bytes, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_a, N) || !d_plan || !d_w_gate || !d_w_up || !d_w_down || bad(d_y, N) ||
+        (shape->dtype == MOE_BF16 && bad(d_gu, N)) || !d_ws)
+        return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    char* ws = static_cast<char*>(d_ws);
+    hipStream_t hs = as_stream(stream);
+    const moe::GemmGroups g = moe::expert_groups(*shape);
+    hipError_t e = moe_launch_gemm_schedule(*shape, d_plan, ws, hs, g);
+    if (e == hipSuccess)
+        e = moe_launch_gemm_gateup(*shape, d_a, d_plan, d_w_gate, d_w_up, ws, hs, g,
+                                   shape->dtype == MOE_BF16 ? d_gu : nullptr);
+    if (e == hipSuccess) e = moe_launch_gemm_down(*shape, d_plan, d_w_down, d_y, ws, hs, g);
+    return dev(e);
+}
+
 moe_status_t moe_combine(const moe_shape_t* shape, const void* d_y, const int32_t* d_dest_row,
                          const float* d_w, const void* d_shared_y, void* d_out,
                          moe_stream_t stream)
@@ -262,8 +285,9 @@ moe_status_t moe_combine_backward(const moe_shape_t* shape, const void* d_dout, 
 
 moe_status_t moe_ffn_backward(const moe_shape_t* shape, const void* d_buf, const int32_t* d_plan,
                               const void* d_w_gate, const void* d_w_up, const void* d_w_down,
-                              const void* d_dy, void* d_dbuf, float* d_dw_gate, float* d_dw_up,
-                              float* d_dw_down, void* d_ws, size_t ws_bytes, moe_stream_t stream)
+                              const void* d_gu, const void* d_dy, void* d_dbuf, float* d_dw_gate,
+                              float* d_dw_up, float* d_dw_down, void* d_ws, size_t ws_bytes,
+                              moe_stream_t stream)
 {
     moe_status_t st = check(shape);
     if (st != MOE_OK) return st;
@@ -272,7 +296,9 @@ moe_status_t moe_ffn_backward(const moe_shape_t* shape, const void* d_buf, const
         bad(d_dbuf, N) || !d_dw_gate || !d_dw_up || !d_dw_down || !d_ws)
         return MOE_EINVAL;
     if (ws_bytes < moe::bwd_ws_layout(*shape).total) return MOE_EINVAL;
-    return dev(moe_launch_ffn_backward(*shape, d_buf, d_plan, d_w_gate, d_w_up, d_w_down, d_dy,
+    // fp32 always recomputes (the saved g | u are a bf16 training forward's)
+    const void* gu = shape->dtype == MOE_BF16 ? d_gu : nullptr;
+    return dev(moe_launch_ffn_backward(*shape, d_buf, d_plan, d_w_gate, d_w_up, d_w_down, gu, d_dy,
                                        d_dbuf, d_dw_gate, d_dw_up, d_dw_down,
                                        static_cast<char*>(d_ws), as_stream(stream)));
 }

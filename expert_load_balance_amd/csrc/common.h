@@ -241,9 +241,12 @@ hipError_t moe_launch_combine(const moe_shape_t& s, const void* y, const int32_t
                               const float* w, const void* shared_y, void* out, hipStream_t st);
 hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, char* ws,
                                     hipStream_t st, const moe::GemmGroups& g);
+// gu_out (bf16 [N][2F] in expert order, g | u), when not NULL, also receives
+// the gate and up projections (training: the backward then skips its recompute)
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
-                                  hipStream_t st, const moe::GemmGroups& g);
+                                  hipStream_t st, const moe::GemmGroups& g,
+                                  void* gu_out = nullptr);
 hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const void* w_down,
                                 void* y, char* ws, hipStream_t st, const moe::GemmGroups& g);
 // by-expert schedule with 256-row M-tiles only (no skinny tiles) + row map
@@ -252,8 +255,8 @@ hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan
 // the expert FFN backward (bf16): gathers, recompute, dgrad, wgrad
 hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
                                    const void* w_gate, const void* w_up, const void* w_down,
-                                   const void* dy, void* dbuf, float* dw_gate, float* dw_up,
-                                   float* dw_down, char* ws, hipStream_t st);
+                                   const void* gu, const void* dy, void* dbuf, float* dw_gate,
+                                   float* dw_up, float* dw_down, char* ws, hipStream_t st);
 // combine / dispatch / gate backward
 hipError_t moe_launch_combine_backward(const moe_shape_t& s, const void* dout, const void* y,
                                        const int32_t* dest_row, const float* w, void* dy,

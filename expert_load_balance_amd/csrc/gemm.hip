@@ -281,6 +281,21 @@ __device__ __forceinline__ Balance balance_of(int tiles, int P, int KT_all)
     return b;
 }
 
+// g | u of one row (bf16) at row x of gu [N][2F]: 4 columns from col, taken
+// from accumulator group g4 of the gate and up fragments
+__device__ __forceinline__ void store_gu(uint16_t* gu, int x, int F, int col, const f32x16& g,
+                                         const f32x16& u, int g4)
+{
+    uint16_t* d = gu + (size_t)x * 2 * F + col;
+    uint2 pk;
+    pk.x = moe::pack_bf16x2(g[g4 * 4], g[g4 * 4 + 1]);
+    pk.y = moe::pack_bf16x2(g[g4 * 4 + 2], g[g4 * 4 + 3]);
+    *reinterpret_cast<uint2*>(d) = pk;
+    pk.x = moe::pack_bf16x2(u[g4 * 4], u[g4 * 4 + 1]);
+    pk.y = moe::pack_bf16x2(u[g4 * 4 + 2], u[g4 * 4 + 3]);
+    *reinterpret_cast<uint2*>(d + F) = pk;
+}
+
 struct Unit {
     int e, n0, rows, hrow0, KT, kofs, pidx;  // e: group; pidx: partial-tile slot, -1 for a whole tile
 };
@@ -301,7 +316,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, float* __restrict__ part)
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, float* __restrict__ part,
+    uint16_t* __restrict__ gu_out)
 {
     __shared__ __attribute__((aligned(1024))) char slots[2 * kSlotBytes];
     __shared__ int32_t rowmap[2][kTM];
@@ -550,6 +566,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                         pk.x = moe::pack_bf16x2(hv[0], hv[1]);
                         pk.y = moe::pack_bf16x2(hv[2], hv[3]);
                         *reinterpret_cast<uint2*>(dst + col) = pk;
+                        if (gu_out)  // training: keep g | u for the backward
+                            store_gu(gu_out, u.hrow0 + row, F, col, acc[i][j], acc[i][j + 2], g4);
                     }
             } else {
                 uint16_t* dst = out + (size_t)rowmap[par][row] * H;
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out)
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out)
 {
     using SK = Skinny<SKM>;
     constexpr int kSkM = SKM, kSkSlots = SK::kSlots, kSkA = SK::kA, kSkSlot = SK::kSlot;
@@ -735,6 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
                     pk.x = moe::pack_bf16x2(hv[0], hv[1]);
                     pk.y = moe::pack_bf16x2(hv[2], hv[3]);
                     *reinterpret_cast<uint2*>(dst + col) = pk;
+                    if (gu_out) store_gu(gu_out, hrow0 + row, F, col, acc[b][0], acc[b][1], g4);
                 }
             } else {
                 uint16_t* dst = out + (size_t)rowmap[row] * H;
@@ -770,7 +789,8 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
                                                          const int32_t* __restrict__ sched,
                                                          const int32_t* __restrict__ vrow,
                                                          const float* __restrict__ part,
-                                                         uint16_t* __restrict__ out)
+                                                         uint16_t* __restrict__ out,
+                                                         uint16_t* __restrict__ gu_out)
 {
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
     const Balance bal = balance_of(sched[G] * ntiles_n, P, KT_all);
@@ -799,6 +819,15 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
             pk.x = moe::pack_bf16x2(fast_silu(g.x) * u.x, fast_silu(g.y) * u.y);
             pk.y = moe::pack_bf16x2(fast_silu(g.z) * u.z, fast_silu(g.w) * u.w);
             *reinterpret_cast<uint2*>(out + (size_t)(r.hrow0 + row) * F + r.n0 + c) = pk;
+            if (gu_out) {
+                uint16_t* d = gu_out + (size_t)(r.hrow0 + row) * 2 * F + r.n0 + c;
+                pk.x = moe::pack_bf16x2(g.x, g.y);
+                pk.y = moe::pack_bf16x2(g.z, g.w);
+                *reinterpret_cast<uint2*>(d) = pk;
+                pk.x = moe::pack_bf16x2(u.x, u.y);
+                pk.y = moe::pack_bf16x2(u.z, u.w);
+                *reinterpret_cast<uint2*>(d + F) = pk;
+            }
         } else {
             if (r.n0 + c >= H) continue;
             float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -989,8 +1018,9 @@ hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan
 
 hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int32_t* plan,
                                   const void* w_gate, const void* w_up, char* ws,
-                                  hipStream_t st, const moe::GemmGroups& g)
+                                  hipStream_t st, const moe::GemmGroups& g, void* gu_out_v)
 {
+    uint16_t* gu_out = static_cast<uint16_t*>(gu_out_v);
     if (s.T == 0) return hipSuccess;
     const moe::WsLayout W = moe::ws_layout(s);
     const int32_t* sched = reinterpret_cast<const int32_t*>(ws + W.sched);
@@ -1004,15 +1034,15 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
         const uint16_t* wu = static_cast<const uint16_t*>(w_up);
         gemm_skinny_kernel<kGateUp, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
-                                                                 wg, wu, g.wtab, h);
+                                                                 wg, wu, g.wtab, h, gu_out);
         gemm_skinny_kernel<kGateUp, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
-                                                                 wg, wu, g.wtab, h);
+                                                                 wg, wu, g.wtab, h, gu_out);
         gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
-                                                           wu, g.wtab, h, part);
+                                                           wu, g.wtab, h, part, gu_out);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         fixup_kernel<kGateUp><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow,
-                                                                part, h);
+                                                                part, h, gu_out);
     } else {
         const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.F + kFM - 1) / kFM;
@@ -1039,15 +1069,15 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
         const uint16_t* wd = static_cast<const uint16_t*>(w_down);
         uint16_t* yv = static_cast<uint16_t*>(y);
         gemm_skinny_kernel<kDown, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                               nullptr, g.wtab, yv);
+                                                               nullptr, g.wtab, yv, nullptr);
         gemm_skinny_kernel<kDown, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                               nullptr, g.wtab, yv);
+                                                               nullptr, g.wtab, yv, nullptr);
         gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                         nullptr, g.wtab, yv, part);
+                                                         nullptr, g.wtab, yv, part, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         fixup_kernel<kDown><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow, part,
-                                                              yv);
+                                                              yv, nullptr);
     } else {
         const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.H + kFM - 1) / kFM;

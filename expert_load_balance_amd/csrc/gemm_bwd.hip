@@ -616,8 +616,8 @@ hipError_t launch_kind(const BwdArgs& a, int grid, hipStream_t st)
 
 hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
                                    const void* w_gate, const void* w_up, const void* w_down,
-                                   const void* dy, void* dbuf, float* dw_gate, float* dw_up,
-                                   float* dw_down, char* ws, hipStream_t st)
+                                   const void* gu, const void* dy, void* dbuf, float* dw_gate,
+                                   float* dw_up, float* dw_down, char* ws, hipStream_t st)
 {
     const int64_t N = (int64_t)s.T * s.k;
     const moe::BwdWsLayout B = moe::bwd_ws_layout(s);
@@ -641,7 +641,8 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
     a.wg = static_cast<const uint16_t*>(w_gate);
     a.wu = static_cast<const uint16_t*>(w_up);
     a.wd = static_cast<const uint16_t*>(w_down);
-    a.gu = reinterpret_cast<uint16_t*>(ws + B.gu);
+    // g | u saved by the training forward, else recomputed into the workspace
+    a.gu = gu ? static_cast<uint16_t*>(const_cast<void*>(gu)) : reinterpret_cast<uint16_t*>(ws + B.gu);
     a.dgu = reinterpret_cast<uint16_t*>(ws + B.dgu);
     a.hb = reinterpret_cast<uint16_t*>(ws + B.hb);
     a.dxbuf = static_cast<uint16_t*>(dbuf);
@@ -689,7 +690,7 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
         gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
                                                     static_cast<const uint4*>(dy),
                                                     reinterpret_cast<uint4*>(ws + B.dys));
-        if ((e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
+        if (!gu && (e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
         if ((e = launch_kind<kDH>(a, grid, st)) != hipSuccess) return e;
         if ((e = launch_kind<kDX>(a, grid, st)) != hipSuccess) return e;
         if (a.dx_split_max > 1) {

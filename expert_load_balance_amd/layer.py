@@ -10,8 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, Shape, moe_combine, moe_count, moe_gemm_down, moe_gemm_gateup,
-               moe_gemm_schedule, moe_grouped_gemm_slots, moe_permute, moe_plan, moe_plan_layout,
-               moe_prefetch_replicas, moe_route, moe_workspace_bytes)
+               moe_gemm_schedule, moe_grouped_gemm_slots, moe_grouped_gemm_train, moe_permute,
+               moe_plan, moe_plan_layout, moe_prefetch_replicas, moe_route, moe_workspace_bytes)
 
 STAGES = ("route", "count", "plan", "permute", "gemm_schedule", "gemm_gateup", "gemm_down",
           "shared", "combine")
@@ -64,7 +64,7 @@ class MoeLayerBuffers:
             moe_plan(self.shared_shape, self.shared_counts, self.shared_plan)
 
     def forward(self, logits, bias, x, w_gate, w_up, w_down, shared_w=None, stream=None,
-                marks=None, pool=None):
+                marks=None, pool=None, gu=None):
         """Route -> count -> plan -> permute -> grouped GEMM -> (shared) -> combine.
 
         marks: optional dict stage -> (start_event, end_event) recorded around
@@ -72,7 +72,8 @@ class MoeLayerBuffers:
         moe_pool_bytes(shape) bytes; with it the planned replicas are
         prefetched into their slots after the plan and the grouped GEMM runs
         by plan segment, reading them (stages "prefetch" and "gemm_slots").
-        Returns self.out."""
+        gu: a bf16 [N, 2F] buffer; with it the grouped GEMM also keeps g | u
+        for the backward (stage "gemm_train"). Returns self.out."""
         s = self.shape
         st = stream if stream is not None else torch.cuda.current_stream()
 
@@ -98,7 +99,12 @@ class MoeLayerBuffers:
         mark("permute", 0)
         moe_permute(s, x, self.ids, self.eidx, self.plan, self.buf, self.dest_row, self.row_src, st)
         mark("permute", 1)
-        if pool is not None:
+        if gu is not None:
+            mark("gemm_train", 0)
+            moe_grouped_gemm_train(s, self.buf, self.plan, w_gate, w_up, w_down, self.y, gu,
+                                   self.ws, st)
+            mark("gemm_train", 1)
+        elif pool is not None:
             mark("gemm_slots", 0)
             moe_grouped_gemm_slots(s, self.buf, self.plan, w_gate, w_up, w_down, pool, self.y,
                                    self.ws, st)

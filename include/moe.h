@@ -340,14 +340,27 @@ moe_status_t moe_combine_backward(const moe_shape_t *shape, const void *d_dout, 
  *   dW_down[e] = sum over e's rows of dy h^T, dW_gate[e] = sum dg x^T,
  *   dW_up[e] = sum du x^T   (fp32, overwritten; zero for idle experts).
  * d_buf dtype[N][H] (the permuted input); d_plan the moe_plan block;
- * weights as moe_grouped_gemm; d_dy dtype[N][H] (buffer order); d_dbuf
+ * weights as moe_grouped_gemm; d_gu: NULL to recompute g | u, or the buffer
+ * moe_grouped_gemm_train filled in this step's forward (bf16); d_dy
+ * dtype[N][H] (buffer order); d_dbuf
  * dtype[N][H] out (buffer order); d_dw_gate, d_dw_up float[E][F][H] out;
  * d_dw_down float[E][H][F] out; d_ws / ws_bytes >=
  * moe_backward_workspace_bytes(shape). */
 moe_status_t moe_ffn_backward(const moe_shape_t *shape, const void *d_buf, const int32_t *d_plan,
                               const void *d_w_gate, const void *d_w_up, const void *d_w_down,
-                              const void *d_dy, void *d_dbuf, float *d_dw_gate, float *d_dw_up,
-                              float *d_dw_down, void *d_ws, size_t ws_bytes, moe_stream_t stream);
+                              const void *d_gu, const void *d_dy, void *d_dbuf, float *d_dw_gate,
+                              float *d_dw_up, float *d_dw_down, void *d_ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
+/* The forward grouped GEMM of a training step: moe_grouped_gemm, and (bf16)
+ * the gate and up projections kept in d_gu bf16[N][2F] (row x in expert
+ * order -- the order moe_ffn_backward uses -- g in columns [0, F), u in
+ * [F, 2F)), so that moe_ffn_backward(d_gu = this buffer) skips its
+ * recompute. fp32: d_gu is not written (the fp32 backward recomputes). */
+moe_status_t moe_grouped_gemm_train(const moe_shape_t *shape, const void *d_a,
+                                    const int32_t *d_plan, const void *d_w_gate,
+                                    const void *d_w_up, const void *d_w_down, void *d_y,
+                                    void *d_gu, void *d_ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Dispatch backward: dx[t] = sum_j dbuf[dest_row[t][j]] (fp32 accumulate in
  * j order, one rounding). d_dbuf dtype[N][H]; d_dest_row int32[T][k];

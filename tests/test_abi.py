@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -160,10 +160,12 @@ def test_backward_workspace_and_rejections(lib):
     s = moe.Shape(64, 128, 8, 2, 128, 4, 1, moe.MOE_BF16)
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     need = moe.moe_backward_workspace_bytes(s)
-    assert lib.moe_ffn_backward(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, p, need - 1,
+    assert lib.moe_ffn_backward(ctypes.byref(s), p, p, p, p, p, None, p, p, p, p, p, p, need - 1,
                                 None) == 1                    # workspace too small
-    assert lib.moe_ffn_backward(ctypes.byref(s), p, None, p, p, p, p, p, p, p, p, p, 1 << 30,
+    assert lib.moe_ffn_backward(ctypes.byref(s), p, None, p, p, p, None, p, p, p, p, p, p, 1 << 30,
                                 None) == 1                    # no plan
+    assert lib.moe_grouped_gemm_train(ctypes.byref(s), p, p, p, p, p, p, None, p, 1 << 30,
+                                      None) == 1              # bf16 needs the g | u buffer
     assert lib.moe_combine_backward(ctypes.byref(s), p, p, p, p, None, p, None) == 1
     assert lib.moe_permute_backward(ctypes.byref(s), None, p, p, None) == 1
     assert lib.moe_route_backward(ctypes.byref(s), p, p, None, p, None) == 1

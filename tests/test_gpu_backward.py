@@ -189,3 +189,35 @@ def test_backward_full_size(name, maxvio):
     # experts with no rows have zero gradients
     for e0 in np.where(counts == 0)[0][:2]:
         assert not bool(b.dW[2][int(e0)].any())
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[-1] == moe.MOE_BF16][:3] + [
+    ("mixtral_like", 300, 256, 4, 2, 1024, 4, 0.5, moe.MOE_BF16)], ids=lambda c: c[0])
+def test_backward_with_saved_gate_up(case):
+    """The training forward keeps g | u (moe_grouped_gemm_train): its y is
+    bit-identical to the plain forward's, and the backward fed with the saved
+    g | u (no recompute) meets the same oracle bar as the recomputing one."""
+    name, T, H, E, k, F, R, sb, dtype = case
+    _say(f"[case] backward with saved g|u {name}")
+    shape = moe.Shape(T, H, E, k, F, R, 1, dtype)
+    lg = synth.router_logits(T, E, 55)
+    bias = synth.zipf_bias(E, sb, 55).astype(np.float32) if sb else None
+    b = Backward(shape, lg, bias, 56)
+    L = b.L
+    y2 = alloc((shape.N, H), torch.bfloat16, DEV)
+    gu = alloc((shape.N, 2 * F), torch.bfloat16, DEV)
+    moe.moe_grouped_gemm_train(shape, L.buf, L.plan, *b.wts, y2, gu, L.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
+    dbuf2 = alloc((shape.N, H), torch.bfloat16, DEV)
+    dW2 = [torch.full_like(t, float("nan")) for t in b.dW]
+    moe.moe_ffn_backward(shape, L.buf, L.plan, *b.wts, b.dy, dbuf2, *dW2, b.ws, gu=gu)
+    torch.cuda.synchronize()
+    buf = host(L.buf).astype(np.float64)
+    dyg = host(b.dy).astype(np.float64)
+    wh = [host(t).astype(np.float64) for t in b.wts]
+    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dyg, b.pl, *wh)
+    assert_tol(host(dbuf2), dbuf_ref, moe.MOE_BF16, "dbuf (saved g|u)")
+    for got, ref, nm in zip(dW2, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
+        assert_tol(host(got), ref, moe.MOE_BF16, nm + " (saved g|u)")
+    assert_tol(host(dbuf2), host(b.dbuf).astype(np.float64), moe.MOE_BF16, "saved vs recomputed")
