@@ -229,6 +229,9 @@ def time_backward(shape, L, lg, bias, x, wts, shared, seed, stream):
                      stream=stream)
     c_ffn_re = moe.bind(moe.moe_ffn_backward, shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws,
                         stream=stream)
+    rgrad = torch.empty(moe.moe_replica_grad_bytes(shape) // 4, dtype=torch.float32, device=dev)
+    c_ffn_rep = moe.bind(moe.moe_ffn_backward_replicas, shape, L.buf, L.plan, *wts, dy, dbuf, *dW,
+                         rgrad, ws, gu=gu, stream=stream)
     c_perm = moe.bind(moe.moe_permute_backward, shape, dbuf, L.dest_row, dx, stream=stream)
     c_route = moe.bind(moe.moe_route_backward, shape, L.ids, L.w, dw, dl, stream=stream)
 
@@ -245,6 +248,8 @@ def time_backward(shape, L, lg, bias, x, wts, shared, seed, stream):
     t_comb = time_back_to_back(c_comb, reps=20)
     t_ffn = time_back_to_back(c_ffn, reps=5)
     t_ffn_re = time_back_to_back(c_ffn_re, reps=5)
+    t_ffn_rep = time_back_to_back(c_ffn_rep, reps=5)
+    del rgrad
     t_perm = time_back_to_back(c_perm, reps=20)
     t_route = time_back_to_back(c_route, reps=20)
     t_all = time_back_to_back(chain, reps=5)
@@ -256,6 +261,7 @@ def time_backward(shape, L, lg, bias, x, wts, shared, seed, stream):
                 ffn_backward_tflops=flops / t_ffn / 1e12,
                 ffn_backward_mfma_frac=flops / t_ffn / 1e12 / PEAK_BF16_TFLOPS,
                 ffn_backward_recompute_ms=t_ffn_re * 1e3,
+                ffn_backward_replica_slots_ms=t_ffn_rep * 1e3,
                 train_step_ms=t_step * 1e3, train_step_tokens_per_s=T / t_step)
 
 

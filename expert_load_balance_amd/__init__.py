@@ -24,6 +24,7 @@ __all__ = [
     "bind", "moe_pool_bytes", "moe_prefetch_replicas", "moe_grouped_gemm_slots",
     "moe_backward_workspace_bytes", "moe_combine_backward", "moe_ffn_backward",
     "moe_permute_backward", "moe_route_backward", "moe_grouped_gemm_train",
+    "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "moe_pool_bytes",
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
-    "moe_grouped_gemm_train",
+    "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -152,6 +153,9 @@ def load():
                                   ctypes.c_size_t, _VP]),
         "moe_grouped_gemm_train": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                         ctypes.c_size_t, _VP]),
+        "moe_replica_grad_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_ffn_backward_replicas": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           _VP, _VP, ctypes.c_size_t, _VP, ctypes.c_size_t, _VP]),
         "moe_permute_backward": (st, [_SP, _VP, _VP, _VP, _VP]),
         "moe_route_backward": (st, [_SP, _VP, _VP, _VP, _VP, _VP]),
         "moe_prefetch_replicas": (st, [_SP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -212,7 +216,8 @@ def _ok(status, where):
 # entry points that only compute on the host (sizes, layouts, checks)
 _HOST_ONLY = frozenset(("moe_status_str", "moe_check_shape", "moe_plan_layout",
                         "moe_workspace_bytes", "moe_router_workspace_bytes", "moe_capacity_rows",
-                        "moe_pool_bytes", "moe_backward_workspace_bytes"))
+                        "moe_pool_bytes", "moe_backward_workspace_bytes",
+                        "moe_replica_grad_bytes"))
 
 
 class _Recorder:
@@ -606,3 +611,26 @@ def moe_grouped_gemm_train(shape, a, plan, w_gate, w_up, w_down, y, gu, ws, stre
         _ptr(y, act, "y", N * shape.H),
         _ptr(gu, act, "gu", N * 2 * shape.F, nullable=shape.dtype != MOE_BF16),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "moe_grouped_gemm_train")
+
+
+def moe_replica_grad_bytes(shape: Shape) -> int:
+    return int(load().moe_replica_grad_bytes(ctypes.byref(shape)))
+
+
+def moe_ffn_backward_replicas(shape, buf, plan, w_gate, w_up, w_down, dy, dbuf, dw_gate, dw_up,
+                              dw_down, rgrad, ws, gu=None, stream=None):
+    """moe_ffn_backward with per-replica gradients in rgrad (float32, at least
+    moe_replica_grad_bytes(shape) bytes) reduced into the home experts."""
+    import torch
+
+    act, N = _act_dtype(shape), shape.N
+    n = shape.E * shape.F * shape.H
+    f32 = torch.float32
+    _ok(load().moe_ffn_backward_replicas(
+        ctypes.byref(shape), _ptr(buf, act, "buf", N * shape.H), _ptr(plan, torch.int32, "plan"),
+        _ptr(w_gate, act, "w_gate", n), _ptr(w_up, act, "w_up", n), _ptr(w_down, act, "w_down", n),
+        _ptr(gu, act, "gu", N * 2 * shape.F, nullable=True), _ptr(dy, act, "dy", N * shape.H),
+        _ptr(dbuf, act, "dbuf", N * shape.H), _ptr(dw_gate, f32, "dw_gate", n),
+        _ptr(dw_up, f32, "dw_up", n), _ptr(dw_down, f32, "dw_down", n),
+        _ptr(rgrad, f32, "rgrad"), _nbytes(rgrad), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_ffn_backward_replicas")

@@ -303,6 +303,34 @@ moe_status_t moe_ffn_backward(const moe_shape_t* shape, const void* d_buf, const
                                        static_cast<char*>(d_ws), as_stream(stream)));
 }
 
+size_t moe_replica_grad_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK) return 0;
+    return moe::replica_grad_bytes(*shape);
+}
+
+moe_status_t moe_ffn_backward_replicas(const moe_shape_t* shape, const void* d_buf,
+                                       const int32_t* d_plan, const void* d_w_gate,
+                                       const void* d_w_up, const void* d_w_down, const void* d_gu,
+                                       const void* d_dy, void* d_dbuf, float* d_dw_gate,
+                                       float* d_dw_up, float* d_dw_down, float* d_rgrad,
+                                       size_t rgrad_bytes, void* d_ws, size_t ws_bytes,
+                                       moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (shape->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_buf, N) || !d_plan || !d_w_gate || !d_w_up || !d_w_down || bad(d_dy, N) ||
+        bad(d_dbuf, N) || !d_dw_gate || !d_dw_up || !d_dw_down || !d_rgrad || !d_ws)
+        return MOE_EINVAL;
+    if (rgrad_bytes < moe::replica_grad_bytes(*shape)) return MOE_EINVAL;
+    if (ws_bytes < moe::bwd_ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_ffn_backward(*shape, d_buf, d_plan, d_w_gate, d_w_up, d_w_down, d_gu,
+                                       d_dy, d_dbuf, d_dw_gate, d_dw_up, d_dw_down,
+                                       static_cast<char*>(d_ws), as_stream(stream), d_rgrad));
+}
+
 moe_status_t moe_permute_backward(const moe_shape_t* shape, const void* d_dbuf,
                                   const int32_t* d_dest_row, void* d_dx, moe_stream_t stream)
 {

@@ -133,8 +133,14 @@ inline WsLayout ws_layout(const moe_shape_t& s)
 // by-expert schedule with 256-row M-tiles, the expert-order row map, a zero
 // page, x and dy in expert order, the recomputed g | u, dg | du and h.
 struct BwdWsLayout {
-    size_t sched, vrow, zero, xs, dys, gu, dgu, hb, dxpart, total;
+    size_t sched, vrow, zero, xs, dys, gu, dgu, hb, dxpart, rgroups, slot_of, total;
 };
+// Replica weight-gradient slots (training, one per rank and replica
+// position): [R][n][3][F*H] fp32, gate | up | down of the replica held there.
+inline size_t replica_grad_bytes(const moe_shape_t& s)
+{
+    return (size_t)s.R * (s.E / s.R) * 3 * s.F * s.H * 4;
+}
 // Bound on the dx GEMM's K-split: 4 when its tiles (at most N/256 + E
 // M-tiles x H/256 N-tiles) cannot fill four rounds of the persistent grid.
 inline int bwd_dx_split_max(const moe_shape_t& s)
@@ -160,6 +166,8 @@ inline BwdWsLayout bwd_ws_layout(const moe_shape_t& s)
     b.hb = o;    o = align256(o + n1 * s.F * eb);
     const int sp = s.dtype == MOE_BF16 ? bwd_dx_split_max(s) : 1;
     b.dxpart = o; o = align256(o + (sp > 1 ? (size_t)sp * n1 * s.H * 4 : 4));
+    b.rgroups = o; o = align256(o + (size_t)2 * s.E * 4 * 4);   // {e, k0, k1, out} per group
+    b.slot_of = o; o = align256(o + (size_t)s.E * s.R * 4);      // [E][R] replica slot or -1
     b.total = o;
     return b;
 }
@@ -253,10 +261,14 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
 hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan, int32_t* sched,
                                        int32_t* vrow, hipStream_t st);
 // the expert FFN backward (bf16): gathers, recompute, dgrad, wgrad
+// rgrad (bf16 layers): NULL, or the replica gradient slots -- then each
+// replica piece's weight gradient goes to its slot and a reduction adds the
+// slots into their home experts (rank order)
 hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
                                    const void* w_gate, const void* w_up, const void* w_down,
                                    const void* gu, const void* dy, void* dbuf, float* dw_gate,
-                                   float* dw_up, float* dw_down, char* ws, hipStream_t st);
+                                   float* dw_up, float* dw_down, char* ws, hipStream_t st,
+                                   float* rgrad = nullptr);
 // combine / dispatch / gate backward
 hipError_t moe_launch_combine_backward(const moe_shape_t& s, const void* dout, const void* y,
                                        const int32_t* dest_row, const float* w, void* dy,

@@ -60,6 +60,10 @@ struct BwdArgs {
     const char* zero;      // >= 512 zero bytes
     int dx_split_max;      // DX K-split bound (partials allocated for it)
     float* dxpart;         // DX partials [split][N][H], expert order
+    // replica mode of the weight gradients: groups [2E] of {e, k0, k1, out}
+    // (out -1: the home gradient; >= 0: replica slot r*n + j; -2: unused)
+    const int32_t* rgroups;
+    float* rgrad;          // [R*n][3][F*H]
 };
 
 // DX K-split: the part count in [1, smax] that fills the workgroups best
@@ -95,6 +99,7 @@ struct Traits {
 
 struct Tile {
     int e, m0, n0, rows, hrow0, ns;  // rows: valid M rows (dgrad) or K rows (wgrad)
+    int out;                         // wgrad: -1 home gradient, >= 0 replica slot, -2 none
 };
 
 __device__ __forceinline__ float sigm(float z)
@@ -105,7 +110,7 @@ __device__ __forceinline__ float sigm(float z)
 template <int KIND>
 __device__ __forceinline__ int tiles_total(const BwdArgs& a, int ntn, int mtw, int ntw)
 {
-    if (Traits<KIND>::kWgrad) return a.G * mtw * ntw;
+    if (Traits<KIND>::kWgrad) return (a.rgroups ? 2 * a.G : a.G) * mtw * ntw;
     return a.sched[a.G] * ntn;
 }
 
@@ -116,15 +121,26 @@ __device__ __forceinline__ Tile tile_at(int t, const BwdArgs& a, int ntn, int mt
     const int32_t* rs = a.sched + a.G + 1;
     Tile r;
     if (Traits<KIND>::kWgrad) {
-        r.e = t / (mtw * ntw);
+        const int g = t / (mtw * ntw);
         const int local = t % (mtw * ntw);
         r.m0 = (local / ntw) * kT;
         r.n0 = (local % ntw) * kT;
-        r.hrow0 = rs[r.e];
-        r.rows = rs[r.e + 1] - rs[r.e];
+        if (a.rgroups) {  // one group per home expert / replica slot: a row range of e
+            const int32_t* gr = a.rgroups + 4 * g;
+            r.e = gr[0];
+            r.out = gr[3];
+            r.hrow0 = rs[r.e] + gr[1];
+            r.rows = gr[2] - gr[1];
+        } else {
+            r.e = g;
+            r.out = -1;
+            r.hrow0 = rs[r.e];
+            r.rows = rs[r.e + 1] - rs[r.e];
+        }
         r.ns = (r.rows + kK - 1) / kK;
         return r;
     }
+    r.out = -1;
     int lo = 0, hi = a.G - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -199,6 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
     for (int u = my_slot; u < total; u += P) {
         const int part = u / tiles;
         const Tile tl = tile_at<KIND>(u % tiles, a, ntn, mtw, ntw);
+        if (TR::kWgrad && uni(tl.out) == -2) continue;  // an unused replica slot
         const int e = uni(tl.e), m0 = uni(tl.m0), n0 = uni(tl.n0), rows = uni(tl.rows);
         // this unit's K stages [s0, s0 + ns) of the tile's tl.ns
         const int s0 = uni(part * tl.ns / nsplit);
@@ -368,6 +385,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
         }
 
         if (TR::kWgrad) {
+            // the expert's own gradient, or its replica slot's
+            const int out = uni(tl.out);
+            float* gdst = out < 0 ? a.dwg + e * FH : a.rgrad + ((size_t)out * 3 + 0) * FH;
+            float* udst = out < 0 ? a.dwu + e * FH : a.rgrad + ((size_t)out * 3 + 1) * FH;
+            float* ddst = out < 0 ? a.dwd + e * FH : a.rgrad + ((size_t)out * 3 + 2) * FH;
             // acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + 8 g4 + 4 fh + q,
             // 128 wn + 32 j + fr): one fp32 store per value, 32 lanes along a row
 #pragma unroll
@@ -382,10 +404,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
                             const int row = m0 + wm * 128 + i * 32 + g4 * 8 + fh * 4 + q;
                             const float v = acc[i][j][g4 * 4 + q];
                             if (KIND == kWD) {
-                                if (row < H && col < F) a.dwd[e * FH + (size_t)row * F + col] = v;
+                                if (row < H && col < F) ddst[(size_t)row * F + col] = v;
                             } else if (row < 2 * F && col < H) {
-                                float* dst = row < F ? a.dwg + e * FH + (size_t)row * H
-                                                     : a.dwu + e * FH + (size_t)(row - F) * H;
+                                float* dst = row < F ? gdst + (size_t)row * H
+                                                     : udst + (size_t)(row - F) * H;
                                 dst[col] = v;
                             }
                         }
@@ -495,6 +517,90 @@ __global__ __launch_bounds__(kThreads) void dx_fixup_kernel(BwdArgs a, int P)
     pk.x = moe::pack_bf16x2(acc.x, acc.y);
     pk.y = moe::pack_bf16x2(acc.z, acc.w);
     *reinterpret_cast<uint2*>(a.dxbuf + (size_t)a.vrow[x] * H + c) = pk;
+}
+
+// Replica mode: one group per expert (its home piece's rows, possibly none)
+// and one per replica slot (r, j) of the plan (the replica piece's rows on
+// rank r); rows are offsets into the expert's rows in expert order, where
+// its pieces follow in rank order. slot_of[e][r] = j, or -1.
+__global__ __launch_bounds__(kThreads) void replica_groups_kernel(int E, int R,
+                                                                  const int32_t* __restrict__ plan,
+                                                                  int32_t* __restrict__ groups,
+                                                                  int32_t* __restrict__ slot_of)
+{
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    const int n = E / R;
+    const moe::PlanLayout L = moe::plan_layout(E, R);
+    if (t >= E) {  // replica slot t - E without an expert: unused
+        const int sl = t - E;
+        if (sl < R * n && plan[L.slot_expert + sl] < 0) {
+            int32_t* g = groups + 4 * (E + sl);
+            g[0] = 0; g[1] = 0; g[2] = 0; g[3] = -2;
+        }
+        return;
+    }
+    const int e = t, home = e / n;
+    for (int r = 0; r < R; ++r) slot_of[(size_t)e * R + r] = -1;
+    int32_t* hg = groups + 4 * e;
+    hg[0] = e; hg[1] = 0; hg[2] = 0; hg[3] = -1;
+    const int np = plan[L.piece_num + e];
+    int cum = 0;
+    for (int p = 0; p < np && p < R; ++p) {
+        const int r = plan[L.piece_rank + (size_t)e * R + p];
+        const int c = plan[L.piece_cnt + (size_t)e * R + p];
+        if (r == home) {
+            hg[1] = cum;
+            hg[2] = cum + c;
+        } else if (r >= 0 && r < R) {
+            for (int j = 0; j < n; ++j) {
+                if (plan[L.slot_expert + (size_t)r * n + j] == e) {
+                    int32_t* g = groups + 4 * (E + r * n + j);
+                    g[0] = e; g[1] = cum; g[2] = cum + c; g[3] = r * n + j;
+                    slot_of[(size_t)e * R + r] = j;
+                    break;
+                }
+            }
+        }
+        cum += c;
+    }
+}
+
+// The replica-gradient reduction: dW[e] += the gradients in e's replica
+// slots, added in rank order after the home part; experts without replicas
+// are left alone. blockIdx.y = expert; 4 floats per thread, grid-stride.
+__global__ __launch_bounds__(kThreads) void reduce_replicas_kernel(int E, int R, int64_t FH,
+                                                                   const int32_t* __restrict__ slot_of,
+                                                                   const float* __restrict__ rgrad,
+                                                                   float* __restrict__ dwg,
+                                                                   float* __restrict__ dwu,
+                                                                   float* __restrict__ dwd)
+{
+    const int e = blockIdx.y;
+    const int n = E / R;
+    const int32_t* so = slot_of + (size_t)e * R;
+    bool any = false;
+    for (int r = 0; r < R; ++r) any |= so[r] >= 0;
+    if (!any) return;
+    const int64_t n4 = 3 * FH / 4;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * kThreads) {
+        const int64_t w = i * 4;
+        const int q = (int)(w / FH);
+        const int64_t o = w % FH;
+        float* d = (q == 0 ? dwg : q == 1 ? dwu : dwd) + (size_t)e * FH + o;
+        float4 acc = *reinterpret_cast<const float4*>(d);
+        for (int r = 0; r < R; ++r) {
+            const int j = so[r];
+            if (j < 0) continue;
+            const float4 v = *reinterpret_cast<const float4*>(
+                rgrad + ((size_t)(r * n + j) * 3 + q) * FH + o);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        *reinterpret_cast<float4*>(d) = acc;
+    }
 }
 
 __global__ void zero_kernel(uint4* p, int n)
@@ -617,7 +723,8 @@ hipError_t launch_kind(const BwdArgs& a, int grid, hipStream_t st)
 hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
                                    const void* w_gate, const void* w_up, const void* w_down,
                                    const void* gu, const void* dy, void* dbuf, float* dw_gate,
-                                   float* dw_up, float* dw_down, char* ws, hipStream_t st)
+                                   float* dw_up, float* dw_down, char* ws, hipStream_t st,
+                                   float* rgrad)
 {
     const int64_t N = (int64_t)s.T * s.k;
     const moe::BwdWsLayout B = moe::bwd_ws_layout(s);
@@ -634,6 +741,17 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
     a.N = (int)N;
     a.dx_split_max = moe::bwd_dx_split_max(s);
     a.dxpart = reinterpret_cast<float*>(ws + B.dxpart);
+    a.rgroups = nullptr;
+    a.rgrad = rgrad;
+    int32_t* slot_of = reinterpret_cast<int32_t*>(ws + B.slot_of);
+    if (rgrad && s.dtype == MOE_BF16) {
+        int32_t* groups = reinterpret_cast<int32_t*>(ws + B.rgroups);
+        const int nt = s.E + s.R * (s.E / s.R);
+        replica_groups_kernel<<<(nt + kThreads - 1) / kThreads, kThreads, 0, st>>>(s.E, s.R, plan,
+                                                                                 groups, slot_of);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        a.rgroups = groups;
+    }
     a.sched = sched;
     a.vrow = vrow;
     a.xs = reinterpret_cast<const uint16_t*>(ws + B.xs);
@@ -700,5 +818,12 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
         }
     }
     if ((e = launch_kind<kWD>(a, grid, st)) != hipSuccess) return e;
-    return launch_kind<kWGU>(a, grid, st);
+    if ((e = launch_kind<kWGU>(a, grid, st)) != hipSuccess) return e;
+    if (a.rgroups) {
+        const int64_t FH = (int64_t)s.F * s.H;
+        reduce_replicas_kernel<<<dim3(1024, s.E), kThreads, 0, st>>>(s.E, s.R, FH, slot_of, rgrad,
+                                                                     dw_gate, dw_up, dw_down);
+        e = hipGetLastError();
+    }
+    return e;
 }

@@ -352,6 +352,31 @@ moe_status_t moe_ffn_backward(const moe_shape_t *shape, const void *d_buf, const
                               float *d_dw_up, float *d_dw_down, void *d_ws, size_t ws_bytes,
                               moe_stream_t stream);
 
+/* Bytes of the replica weight-gradient slots: R * n * 3 * F * H * 4 (fp32),
+ * laid out [R][n][3][F*H] -- slot r*n + j holds the gradient of rank r's
+ * j-th replica expert (slot_expert order), gate | up | down. 0 on a bad
+ * shape. */
+size_t moe_replica_grad_bytes(const moe_shape_t *shape);
+
+/* moe_ffn_backward with the replica-gradient reduction made explicit, as R
+ * ranks run it ([MoonEP] paragraph 3): each replica piece's weight gradient
+ * (its rows on the rank that holds the replica) is written to its slot in
+ * d_rgrad; each expert's home piece writes the expert's gradient (zero when
+ * the plan moved all of its rows away); then every slot is added into its
+ * home expert's gradient, after the home part, in rank order. The result
+ * equals moe_ffn_backward's up to fp32 summation order; the slots keep the
+ * per-replica gradients. bf16 only (MOE_EUNSUPPORTED for fp32).
+ *   d_rgrad / rgrad_bytes >= moe_replica_grad_bytes(shape); slots of ranks
+ *   without that replica are not written; other arguments as
+ *   moe_ffn_backward. */
+moe_status_t moe_ffn_backward_replicas(const moe_shape_t *shape, const void *d_buf,
+                                       const int32_t *d_plan, const void *d_w_gate,
+                                       const void *d_w_up, const void *d_w_down, const void *d_gu,
+                                       const void *d_dy, void *d_dbuf, float *d_dw_gate,
+                                       float *d_dw_up, float *d_dw_down, float *d_rgrad,
+                                       size_t rgrad_bytes, void *d_ws, size_t ws_bytes,
+                                       moe_stream_t stream);
+
 /* The forward grouped GEMM of a training step: moe_grouped_gemm, and (bf16)
  * the gate and up projections kept in d_gu bf16[N][2F] (row x in expert
  * order -- the order moe_ffn_backward uses -- g in columns [0, F), u in

@@ -441,3 +441,42 @@ def expert_ffn_backward(buf, dy, pl, w_gate, w_up, w_down):
                                                        w_down[e])
         dbuf[rows] = dx
     return dbuf, dwg, dwu, dwd
+
+
+def replica_backward(buf, dy, pl, w_gate, w_up, w_down):
+    """The replica-gradient reduction written out (MoonEP article, paragraph
+    3: replica gradients are reduced into the home expert): each expert's home
+    piece gives the home part of its gradient; each replica piece (rank r,
+    slot j of slot_expert[r]) gives a slot gradient from its own rows; the
+    expert's gradient is the home part plus its slots in rank order.
+    -> (dW_gate, dW_up, dW_down reduced, slots {(r, j): (g, u, d)})."""
+    E, F, H = w_gate.shape
+    R, n = pl["slot_expert"].shape
+    dwg = np.zeros((E, F, H))
+    dwu = np.zeros((E, F, H))
+    dwd = np.zeros((E, H, F))
+    slots = {}
+    parts = {e: [] for e in range(E)}
+    for e in range(E):
+        for p in range(int(pl["piece_num"][e])):
+            r = int(pl["piece_rank"][e, p])
+            r0, c = int(pl["piece_row"][e, p]), int(pl["piece_cnt"][e, p])
+            if c == 0:
+                continue
+            _, g, u, d = ffn_backward_rows(buf[r0:r0 + c], dy[r0:r0 + c], w_gate[e], w_up[e],
+                                           w_down[e])
+            if r == e // n:
+                dwg[e] += g
+                dwu[e] += u
+                dwd[e] += d
+            else:
+                j = int(np.where(pl["slot_expert"][r] == e)[0][0])
+                slots[(r, j)] = (g, u, d)
+                parts[e].append((r, j))
+    for e in range(E):
+        for r, j in sorted(parts[e]):
+            g, u, d = slots[(r, j)]
+            dwg[e] += g
+            dwu[e] += u
+            dwd[e] += d
+    return dwg, dwu, dwd, slots

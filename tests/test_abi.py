@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 31
+    assert len(names) == 33
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -169,3 +169,16 @@ def test_backward_workspace_and_rejections(lib):
     assert lib.moe_combine_backward(ctypes.byref(s), p, p, p, p, None, p, None) == 1
     assert lib.moe_permute_backward(ctypes.byref(s), None, p, p, None) == 1
     assert lib.moe_route_backward(ctypes.byref(s), p, p, None, p, None) == 1
+
+
+def test_replica_grad_bytes_and_rejections(lib):
+    s = moe.Shape(64, 128, 8, 2, 128, 4, 1, moe.MOE_BF16)       # n = 2
+    assert moe.moe_replica_grad_bytes(s) == 4 * 2 * 3 * 128 * 128 * 4
+    assert moe.moe_replica_grad_bytes(s.replace(R=3)) == 0
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    need = moe.moe_replica_grad_bytes(s)
+    big = 1 << 40
+    assert lib.moe_ffn_backward_replicas(ctypes.byref(s), p, p, p, p, p, None, p, p, p, p, p, p,
+                                         need - 1, p, big, None) == 1      # slots too small
+    assert lib.moe_ffn_backward_replicas(ctypes.byref(s.replace(dtype=moe.MOE_F32)), p, p, p, p,
+                                         p, None, p, p, p, p, p, p, need, p, big, None) == 2

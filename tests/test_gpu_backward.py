@@ -221,3 +221,47 @@ def test_backward_with_saved_gate_up(case):
     for got, ref, nm in zip(dW2, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
         assert_tol(host(got), ref, moe.MOE_BF16, nm + " (saved g|u)")
     assert_tol(host(dbuf2), host(b.dbuf).astype(np.float64), moe.MOE_BF16, "saved vs recomputed")
+
+
+@pytest.mark.parametrize("case", [
+    ("skewed_4ranks", 400, 128, 8, 2, 256, 4, 1.5),
+    ("fine_grained", 512, 128, 32, 4, 128, 8, 1.0),
+], ids=lambda c: c[0])
+def test_backward_replica_reduction(case):
+    """moe_ffn_backward_replicas: every filled replica slot holds its replica
+    piece's weight gradient (against the oracle on that piece's rows), slots
+    without a replica are not written, and the reduced gradients match the
+    oracle and moe_ffn_backward's (fp32 bar: only the summation grouping
+    differs)."""
+    name, T, H, E, k, F, R, sb = case
+    _say(f"[case] backward replica reduction {name}")
+    shape = moe.Shape(T, H, E, k, F, R, E // R, moe.MOE_BF16)
+    lg = synth.router_logits(T, E, 57)
+    bias = synth.zipf_bias(E, sb, 57).astype(np.float32)
+    b = Backward(shape, lg, bias, 58)
+    L = b.L
+    n = E // R
+    rgrad = torch.full((moe.moe_replica_grad_bytes(shape) // 4,), float("nan"), dtype=torch.float32,
+                       device=DEV)
+    dW2 = [torch.full_like(t, float("nan")) for t in b.dW]
+    dbuf2 = alloc((shape.N, H), torch.bfloat16, DEV)
+    moe.moe_ffn_backward_replicas(shape, L.buf, L.plan, *b.wts, b.dy, dbuf2, *dW2, rgrad, b.ws)
+    torch.cuda.synchronize()
+    buf = host(L.buf).astype(np.float64)
+    dyg = host(b.dy).astype(np.float64)
+    wh = [host(t).astype(np.float64) for t in b.wts]
+    rg, ru, rd, slots = oracle.replica_backward(buf, dyg, b.pl, *wh)
+    assert len(slots) > 0
+    rv = host(rgrad).reshape(R, n, 3, F * H)
+    for r in range(R):
+        for j in range(n):
+            if (r, j) in slots:
+                g, u, d = slots[(r, j)]
+                for q, ref, nm in ((0, g, "gate"), (1, u, "up"), (2, d, "down")):
+                    assert_tol(rv[r, j, q], ref.ravel(), moe.MOE_BF16, f"slot ({r},{j}) {nm}")
+            else:
+                assert np.isnan(rv[r, j]).all()               # not written
+    for got, ref, ref2, nm in zip(dW2, (rg, ru, rd), b.dW, ("dW_gate", "dW_up", "dW_down")):
+        assert_tol(host(got), ref, moe.MOE_BF16, nm + " (replica reduction)")
+        assert_tol(host(got), host(ref2).astype(np.float64), moe.MOE_F32, nm + " vs expert sums")
+    assert torch.equal(dbuf2.view(torch.int16), b.dbuf.view(torch.int16))

@@ -833,3 +833,28 @@ def test_expert_backward_reduces_replicas_into_home():
              for r0, c in zip(pl["piece_row"][0][:3], pl["piece_cnt"][0][:3])]
     for q, got in ((1, dwg[0]), (2, dwu[0]), (3, dwd[0])):
         assert np.allclose(got, sum(p[q] for p in parts), rtol=1e-12, atol=1e-12)
+
+
+def test_replica_backward_reduction_equals_the_expert_sum():
+    """Home part plus replica slots (rank order) equals the gradient over all
+    of an expert's rows, for every expert of a skewed random plan; every slot
+    of the plan holds exactly its replica piece's gradient."""
+    rng = np.random.default_rng(16)
+    T, E, k, R, H, F = 60, 8, 2, 4, 4, 6
+    lg = synth.router_logits(T, E, 16)
+    bias = synth.zipf_bias(E, 1.5, 16).astype(np.float32)
+    ids, _, _ = oracle.route(lg, bias, k)
+    c = oracle.count(ids, E, R)
+    pl = oracle.plan(c["counts"], R)
+    assert (pl["slot_expert"] >= 0).sum() >= 2               # replicas exist
+    N = T * k
+    buf = _grid(rng, (N, H))
+    dy = rng.standard_normal((N, H))
+    wg, wu = _grid(rng, (E, F, H)), _grid(rng, (E, F, H))
+    wd = _grid(rng, (E, H, F))
+    dwg, dwu, dwd, slots = oracle.replica_backward(buf, dy, pl, wg, wu, wd)
+    _, eg, eu, ed = oracle.expert_ffn_backward(buf, dy, pl, wg, wu, wd)
+    for a_, b_ in ((dwg, eg), (dwu, eu), (dwd, ed)):
+        assert np.allclose(a_, b_, rtol=1e-12, atol=1e-12)
+    assert set(slots) == {(r, j) for r in range(R) for j in range(E // R)
+                          if pl["slot_expert"][r, j] >= 0}
