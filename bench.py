@@ -44,6 +44,10 @@ def parse():
                     help="time only the layer (skip the isolated router, replica-slot and "
                          "fixed-capacity measurements, which launch the same GEMM kernels); "
                          "for kernel traces and counters of the layer alone")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the training step of the workload: the training forward (g|u "
+                         "kept) and the backward chain, --steps times; one JSON line of its "
+                         "figures (for kernel traces of the backward)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -426,6 +430,67 @@ SWEEP = (("a3b", 0.0), ("a3b", 0.2), ("a3b", 1.0), ("dsv3", 20.0), ("dsv3", 0.0)
          ("decode64", 1.0), ("decode256", 20.0), ("decode1024", 1.0), ("decode1024", 20.0))
 
 
+def run_backward_only(args):
+    """The workload's training step alone: warm-up, then --steps training
+    forwards (keeping g|u) each followed by the backward chain (combine, FFN
+    from the kept g|u, dispatch, gate), bracketed by synchronisations."""
+    import torch
+
+    import expert_load_balance_amd as moe
+    from expert_load_balance_amd.layer import MoeLayerBuffers
+    import synth
+    from synth import workloads as wl
+
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
+    T, H, E, k, F, R, S = (w[c] for c in ("T", "H", "E", "k", "F", "R", "S"))
+    shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
+    dev, act = "cuda", torch.bfloat16
+    lg_np, bias_np = wl.logits_and_bias(name, maxvio)
+    lg = torch.from_numpy(lg_np).to(dev)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
+    x = synth.device_normal((T, H), 1.0, w["seed"] * 7 + 1, act, dev)
+    wts = (synth.device_normal((E, F, H), synth.weight_std(H), w["seed"] * 10 + 1, act, dev),
+           synth.device_normal((E, F, H), synth.weight_std(H), w["seed"] * 10 + 2, act, dev),
+           synth.device_normal((E, H, F), synth.weight_std(F), w["seed"] * 10 + 3, act, dev))
+    L = MoeLayerBuffers(shape, dev)
+    N = T * k
+    gu = torch.empty((N, 2 * F), dtype=act, device=dev)
+    dout = synth.device_normal((T, H), 1.0, w["seed"] * 10 + 7, act, dev)
+    dy = torch.empty((N, H), dtype=act, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dbuf = torch.empty((N, H), dtype=act, device=dev)
+    dx = torch.empty((T, H), dtype=act, device=dev)
+    dl = torch.empty((T, E), dtype=torch.float32, device=dev)
+    dW = [torch.empty((E, F, H), dtype=torch.float32, device=dev),
+          torch.empty((E, F, H), dtype=torch.float32, device=dev),
+          torch.empty((E, H, F), dtype=torch.float32, device=dev)]
+    ws = torch.empty(moe.moe_backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.forward(lg, bias, x, *wts, stream=stream, gu=gu)
+        moe.moe_combine_backward(shape, dout, L.y, L.dest_row, L.w, dy, dw, stream=stream)
+        moe.moe_ffn_backward(shape, L.buf, L.plan, *wts, dy, dbuf, *dW, ws, gu=gu, stream=stream)
+        moe.moe_permute_backward(shape, dbuf, L.dest_row, dx, stream=stream)
+        moe.moe_route_backward(shape, L.ids, L.w, dw, dl, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / args.steps
+    return {"metric": "MoE-layer training step (forward + backward) tokens/s", "value": T / t,
+            "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup, "ms_per_step": t * 1e3,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{name} T={T} H={H} E={E} k={k} F={F} R={R} S={S}",
+                       "maxvio_target": maxvio}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -448,6 +513,9 @@ def main():
     from synth import workloads as wl
 
     moe.load()
+    if args.backward_only:
+        print(json.dumps(run_backward_only(args)), flush=True)
+        return
     name = args.workload
     w = wl.WORKLOADS[name]
     maxvio = args.maxvio if args.maxvio is not None else w["maxvio"][0]
