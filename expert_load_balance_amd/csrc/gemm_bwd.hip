@@ -484,29 +484,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
 
 // The weight gradients, warp-specialised. Their fp32 outputs (F x H floats
 // per matrix and expert) outweigh the bf16 operands, so the stores must run
-// under the MFMAs: four compute waves never load from global memory (their
+// under the MFMAs: eight compute waves never load from global memory (their
 // vmcnt only ever counts their own stores, so no wait of theirs waits for
 // one), and two loader waves stream the operand stages into a ring of LDS
 // slots, across tile boundaries, one barrier per stage.
-//   tile 256 (M) x 128 (N), K in 32-deep stages of k-major rows (A 512 bytes,
-//   B 256 bytes per k-row, chunk c at c ^ 4 (k & 3), transposing reads);
-//   M is the gradient's contiguous dimension (h for dW_gate|up, f for
-//   dW_down), so each lane holds four consecutive floats of a gradient row
-//   and a tile's 128 KB leave as 32 dwordx4 stores per wave.
+//   tile 256 x 256, K in 32-deep stages of k-major rows (512 bytes per k-row
+//   and operand, chunk c at c ^ 4 (k & 3), transposing reads), compute waves
+//   2 x 4, each 128 x 64. M is the gradient's contiguous dimension (h for
+//   dW_gate|up, f for dW_down).
 //   Stage g sits in slot g % kWSlots. At barrier g the loaders have waited
 //   for stage g's copies and the compute waves have consumed stage g - 1's
 //   fragments; the loaders then refill slot (g - 1) % kWSlots with stage
-//   g + kWSlots - 1.
-constexpr int kWM = 256, kWN = 128, kWK = 32;
-constexpr int kWA = kWK * kWM * 2;  // 16 KB
-constexpr int kWB = kWK * kWN * 2;  // 8 KB
-constexpr int kWSlot = kWA + kWB;
-constexpr int kWSlots = 6;                                // 144 KB of LDS
-constexpr int kWLoaders = 2;                              // loader waves
-constexpr int kWThreads = (4 + kWLoaders) * 64;
-constexpr int kWCopies = kWSlot / 1024 / kWLoaders;       // 12 copies per loader wave per stage
+//   g + kWSlots - 1. A tile's last stage is followed by one more barrier,
+//   after which that stage's slot (not refilled before the next barrier)
+//   is the compute waves' scratch: each 32 x 32 fp32 block turns there so
+//   that every dwordx4 store writes whole 128-byte lines.
+constexpr int kWT = 256, kWK = 32;
+constexpr int kWOp = kWK * kWT * 2;                       // 16 KB: one operand of a stage
+constexpr int kWSlot = 2 * kWOp;                          // A, then B
+constexpr int kWSlots = 5;                                // 160 KB of LDS
+constexpr int kWCompute = 8, kWLoaders = 2;               // waves
+constexpr int kWThreads = (kWCompute + kWLoaders) * 64;
+constexpr int kWCopies = kWSlot / 1024 / kWLoaders;       // 16 copies per loader wave per stage
 static_assert(kWCopies * (kWSlots - 2) < 64, "vmcnt range");
-constexpr int kWScratch = 32 * 32 * 4;                   // a compute wave's 32 x 32 fp32 block
+constexpr int kWScratch = 32 * 32 * 4;                    // a compute wave's 32 x 32 fp32 block
+static_assert(kWCompute * kWScratch <= kWSlot, "scratch fits a slot");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -534,8 +536,8 @@ __device__ __forceinline__ WTile wtile(const BwdArgs& a, int u, int mtw, int ntw
     // consecutive tiles covers 4 A panels and few B panels
     const int band = local / (4 * ntw), rb = local % (4 * ntw);
     const int bm = min(4, mtw - band * 4);
-    t.m0 = uni((band * 4 + rb % bm) * kWM);
-    t.n0 = uni((rb / bm) * kWN);
+    t.m0 = uni((band * 4 + rb % bm) * kWT);
+    t.n0 = uni((rb / bm) * kWT);
     int k0 = 0, k1 = 0;
     if (a.rgroups) {
         t.out = ldc(a.rgroups, 4 * g + 3);
@@ -558,11 +560,11 @@ __device__ __forceinline__ WTile wtile(const BwdArgs& a, int u, int mtw, int ntw
 template <int KIND>
 __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char slots[kWSlots * kWSlot + 4 * kWScratch];
+    __shared__ __attribute__((aligned(1024))) char slots[kWSlots * kWSlot];
     const int H = a.H, F = a.F;
     // A columns (M, the gradient's contiguous dimension), B columns (N)
     const int M = KIND == kWD ? F : H, Nc = KIND == kWD ? H : 2 * F;
-    const int mtw = (M + kWM - 1) / kWM, ntw = (Nc + kWN - 1) / kWN;
+    const int mtw = (M + kWT - 1) / kWT, ntw = (Nc + kWT - 1) / kWT;
     const int groups = a.rgroups ? 2 * a.G : a.G;
     const int total = groups * mtw * ntw;
     const int tid = threadIdx.x;
@@ -572,22 +574,21 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
     // contiguous run of tiles, so tiles sharing an operand share that L2
     const int my_slot = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
 
-    if (wave >= 4) {
-        // loader: A copy q (q = lw + 2 i, i < 8) covers k-rows 2q, 2q + 1;
-        // B copy q (i < 4) k-rows 4q .. 4q + 3
-        const int lw = wave - 4;
+    if (wave >= kWCompute) {
+        // loader lw: copies q = lw + 2 i (i < 8) of each operand, copy q
+        // covering k-rows 2q and 2q + 1 (512 bytes each)
+        const int lw = wave - kWCompute;
         const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
         const char* zero = a.zero;
-        int lu = my_slot, ls = 0;
-        WTile lt = {};
-        // operand rows: A (M wide) and B (N wide), elements per row
         const uint16_t* asrc = KIND == kWD ? a.hb : a.xs;
         const uint16_t* bsrc = KIND == kWD ? a.dys : a.dgu;
         const int astride = KIND == kWD ? F : H, bstride = KIND == kWD ? H : 2 * F;
-        // per-tile lane offsets of the full-stage copies (k-row kr of the
-        // stage, chunk column clamped into the matrix: a column past M or N
-        // only feeds outputs that are not stored)
-        uint32_t aoff[8], boff[4];
+        // issue cursor (lu, ls) and its tile lt; per-tile lane offsets of the
+        // full-stage copies (the chunk column clamped into the matrix: a
+        // column past M or N only feeds outputs that are not stored)
+        int lu = my_slot, ls = 0;
+        WTile lt = {};
+        uint32_t aoff[8], boff[8];
         auto seek = [&]() {
             for (; lu < total; lu += P) {
                 lt = wtile(a, lu, mtw, ntw);
@@ -597,14 +598,8 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int kr = 2 * (lw + 2 * i) + (lane >> 5), c = (lane & 31) ^ kswz(kr);
-                const int col = min(lt.m0 + 8 * c, M - 8);
-                aoff[i] = (uint32_t)(kr * astride + col) * 2u;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kr = 4 * (lw + 2 * i) + (lane >> 4), c = (lane & 15) ^ kswz(kr);
-                const int col = min(lt.n0 + 8 * c, Nc - 8);
-                boff[i] = (uint32_t)(kr * bstride + col) * 2u;
+                aoff[i] = (uint32_t)(kr * astride + min(lt.m0 + 8 * c, M - 8)) * 2u;
+                boff[i] = (uint32_t)(kr * bstride + min(lt.n0 + 8 * c, Nc - 8)) * 2u;
             }
         };
         seek();
@@ -620,28 +615,20 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) copy16(ab, aoff[i], slot + (lw + 2 * i) * 1024);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) copy16(bb, boff[i], slot + kWA + (lw + 2 * i) * 1024);
+                for (int i = 0; i < 8; ++i) copy16(bb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
             } else {
                 // the ragged last stage: k-rows past the rows read the zero page
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int q = lw + 2 * i;
                     const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
-                    const int k = kb + kr, col = lt.m0 + 8 * c;
-                    const char* p = zero + c * 16;
-                    if (k < lt.rows && col < M)
-                        p = (const char*)(asrc + (size_t)(lt.hrow0 + k) * astride + col);
-                    copy16_at(p, slot + q * 1024);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int q = lw + 2 * i;
-                    const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ kswz(kr);
-                    const int k = kb + kr, col = lt.n0 + 8 * c;
-                    const char* p = zero + c * 16;
-                    if (k < lt.rows && col < Nc)
-                        p = (const char*)(bsrc + (size_t)(lt.hrow0 + k) * bstride + col);
-                    copy16_at(p, slot + kWA + q * 1024);
+                    const int k = kb + kr, ca = lt.m0 + 8 * c, cb = lt.n0 + 8 * c;
+                    const bool kin = k < lt.rows;
+                    const size_t row = (size_t)(lt.hrow0 + k);
+                    const char* pa = kin && ca < M ? (const char*)(asrc + row * astride + ca) : zero + c * 16;
+                    const char* pb = kin && cb < Nc ? (const char*)(bsrc + row * bstride + cb) : zero + c * 16;
+                    copy16_at(pa, slot + q * 1024);
+                    copy16_at(pb, slot + kWOp + q * 1024);
                 }
             }
             ++issued;
@@ -651,51 +638,66 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
                 seek();
             }
         };
+        // consume cursor: stages left in the tile being computed, for the
+        // barrier that ends each tile
+        int cu = my_slot, crem = 0;
+        auto cseek = [&]() {
+            for (; cu < total; cu += P) {
+                crem = wtile(a, cu, mtw, ntw).ns;
+                if (crem > 0) break;
+            }
+        };
+        cseek();
         while (issued < kWSlots - 1 && lu < total) issue();
         for (int g = 0; g < issued; ++g) {
             // stage g landed; the stages issued after it may be in flight
             const int after = issued - 1 - g;
-            if (after >= 4) wait_vm_lgkm<4 * kWCopies>();
-            else if (after == 3) wait_vm_lgkm<3 * kWCopies>();
+            if (after >= 3) wait_vm_lgkm<3 * kWCopies>();
             else if (after == 2) wait_vm_lgkm<2 * kWCopies>();
             else if (after == 1) wait_vm_lgkm<kWCopies>();
             else wait_vm_lgkm<0>();
             slot_barrier();
             if (lu < total) issue();
+            if (--crem == 0) {
+                slot_barrier();  // the tile's end: its last slot becomes scratch
+                cu += P;
+                cseek();
+            }
         }
         return;
     }
 
-    // compute waves, 2 x 2, each 128 x 64 of the tile
-    const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 31, fh = lane >> 5;
-    // k-major fragments (k-steps 0..1, reads h = 0, 1): lane reads 4 columns
-    // m_in (+ 32 b) at k-row kr; block b's 64 bytes sit at (b ^ (kr & 3)) * 64
-    uint32_t fa0[2], fa1[2], fb0[2], fb1[2];
-    const int m_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kr = 16 * kk + 8 * fh + 4 * h + ((lane & 15) >> 2);
-            const uint32_t in = (uint32_t)((m_in >> 3) << 4) + (uint32_t)((m_in & 7) * 2);
-            (h ? fa1 : fa0)[kk] = (uint32_t)kr * 512u + in;
-            (h ? fb1 : fb0)[kk] = (uint32_t)kr * 256u + in;
-        }
-    }
-    const int lx = (lane >> 2) & 3;
-    uint32_t xa[4], xb[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = (uint32_t)(((wm * 4 + i) ^ lx) << 6);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) xb[j] = (uint32_t)(((wn * 2 + j) ^ lx) << 6);
-
-    char* scr = slots + kWSlots * kWSlot + wave * kWScratch;
+    // compute waves, 2 x 4, each 128 x 64 of the tile
+    const int wm = wave >> 2, wn = wave & 3;
     const size_t FH = (size_t)F * H;
     int g = 0;  // stages consumed
     for (int u = my_slot; u < total; u += P) {
         const WTile t = wtile(a, u, mtw, ntw);
         if (t.out == -2) continue;  // an unused replica slot
+        // k-major fragments (k-steps 0..1, reads h = 0, 1): lane reads 4
+        // columns m_in (+ 32 b) at k-row kr; block b's 64 bytes sit at
+        // (b ^ (kr & 3)) * 64 (bits 6..8 of the offset, which the rest of it
+        // leaves clear), so block b0 + i of A (B) is at fa (fb) ^ (i << 6).
+        // Recomputed per tile from an opaque copy of the lane index, so that
+        // they are not held (or spilled) across the epilogue.
+        uint32_t fa0[2], fa1[2], fb0[2], fb1[2];
+        {
+            int ln;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            const int m_in = 16 * ((ln >> 4) & 1) + 4 * (ln & 3);
+            const int lx = (ln >> 2) & 3;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kr = 16 * kk + 8 * (ln >> 5) + 4 * h + ((ln & 15) >> 2);
+                    const uint32_t in = (uint32_t)kr * 512u + (uint32_t)((m_in >> 3) << 4) +
+                                        (uint32_t)((m_in & 7) * 2);
+                    (h ? fa1 : fa0)[kk] = in | (uint32_t)(((wm * 4) ^ lx) << 6);
+                    (h ? fb1 : fb0)[kk] = in | (uint32_t)(((wn * 2) ^ lx) << 6);
+                }
+            }
+        }
         f32x16 acc[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -707,30 +709,40 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
         for (int s = 0; s < t.ns; ++s, ++g) {
             slot_barrier();
             const char* sa = slots + (g % kWSlots) * kWSlot;
-            const char* sb = sa + kWA;
-            bf16x8 af[2][4], bfr[2][2];
+            const char* sb = sa + kWOp;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 af[4], bfr[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[kk][i] = lds_frag_tr(sa + fa0[kk] + xa[i], sa + fa1[kk] + xa[i]);
+                for (int i = 0; i < 4; ++i)
+                    af[i] = lds_frag_tr(sa + (fa0[kk] ^ (i << 6)), sa + (fa1[kk] ^ (i << 6)));
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bfr[kk][j] = lds_frag_tr(sb + fb0[kk] + xb[j], sb + fb1[kk] + xb[j]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+                for (int j = 0; j < 2; ++j)
+                    bfr[j] = lds_frag_tr(sb + (fb0[kk] ^ (j << 6)), sb + (fb1[kk] ^ (j << 6)));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j],
-                                                                            acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
         }
 
         // acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + 8 g4 + 4 fh + q,
         // 64 wn + 32 j + fr): four consecutive floats of gradient row n. Each
-        // 32 x 32 block turns in the wave's LDS scratch (row n, 16-byte unit u
-        // at u ^ (n & 7): conflict-free both ways), so that every dwordx4
-        // store writes whole 128-byte lines of 8 rows.
+        // 32 x 32 block turns in the wave's scratch (row n, 16-byte unit u at
+        // u ^ (n & 7): conflict-free both ways), so that every dwordx4 store
+        // writes whole 128-byte lines of 8 rows. An empty tile (no rows of
+        // its expert) stores zeros straight away.
+        // indices from the lane, again through an opaque copy (not hoisted out
+        // of the tile loop and held through it)
+        int el;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+        const int er = el & 31, eh = el >> 5;
+        char* scr = nullptr;
+        if (t.ns > 0) {
+            slot_barrier();  // every wave has read the last stage's slot
+            scr = slots + ((g - 1) % kWSlots) * kWSlot + wave * kWScratch;
+        }
         float* gdst = t.out < 0 ? a.dwg + t.e * FH : a.rgrad + ((size_t)t.out * 3 + 0) * FH;
         float* udst = t.out < 0 ? a.dwu + t.e * FH : a.rgrad + ((size_t)t.out * 3 + 1) * FH;
         float* ddst = t.out < 0 ? a.dwd + t.e * FH : a.rgrad + ((size_t)t.out * 3 + 2) * FH;
@@ -738,19 +750,21 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
+                if (scr) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x4 v = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                                     acc[i][j][4 * g4 + 3]};
-                    const int u = 2 * g4 + fh;
-                    *reinterpret_cast<f32x4*>(scr + fr * 128 + ((u ^ (fr & 7)) << 4)) = v;
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 v = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                         acc[i][j][4 * g4 + 3]};
+                        const int u4 = 2 * g4 + eh;
+                        *reinterpret_cast<f32x4*>(scr + er * 128 + ((u4 ^ (er & 7)) << 4)) = v;
+                    }
                 }
-                const int m = t.m0 + wm * 128 + i * 32 + 4 * (lane & 7);
+                const int m = t.m0 + wm * 128 + i * 32 + 4 * (el & 7);
 #pragma unroll
                 for (int rb = 0; rb < 32; rb += 8) {
-                    const int r = rb + (lane >> 3);
-                    const f32x4 v =
-                        *reinterpret_cast<const f32x4*>(scr + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
+                    const int r = rb + (el >> 3);
+                    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if (scr) v = *reinterpret_cast<const f32x4*>(scr + r * 128 + (((el & 7) ^ (r & 7)) << 4));
                     const int n = t.n0 + wn * 64 + j * 32 + r;
                     if (m >= M || n >= Nc) continue;
                     float* dst;
