@@ -777,6 +777,283 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
     }
 }
 
+// The data gradients DH and DX on the same ring (32-deep stages, two loader
+// waves, eight compute waves 2 x 4 of 128 x 64, one barrier per stage). A
+// (dy or dg | du rows) is K-contiguous: a stage holds 64-byte segments of 256
+// rows, 16-byte unit c of row r at c ^ ((r >> 2) & 3), so the 16 rows one
+// ds_read_b128 pass reads hit 16 distinct bank groups; B is the weights'
+// k-major rows as above. Rows past an M-tile's valid rows repeat its last
+// row and weight columns past the end repeat the last chunk (those outputs
+// are dropped). Units: K-split part, then expert, N-tile, M-tile (M
+// fastest). The bf16 outputs are small beside the weight gradients' and
+// leave straight from the accumulators.
+struct DTile {
+    int e, m0, n0, rows, hrow0, s0, ns, part;
+};
+
+__device__ __forceinline__ DTile dtile(const BwdArgs& a, int u, int tiles, int ntn, int nsplit, int k32)
+{
+    const int32_t* ts = a.sched;
+    const int32_t* rs = a.sched + a.G + 1;
+    const int part = u / tiles, t = u % tiles;
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ldc(ts, mid) * ntn <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int t0 = ldc(ts, lo), mt_e = ldc(ts, lo + 1) - t0;
+    const int local = t - t0 * ntn;
+    DTile d;
+    d.e = uni(lo);
+    d.n0 = uni((local / mt_e) * kWT);
+    d.m0 = uni((local % mt_e) * kWT);
+    const int r0 = ldc(rs, lo);
+    d.rows = uni(min(kWT, ldc(rs, lo + 1) - r0 - d.m0));
+    d.hrow0 = uni(r0 + d.m0);
+    d.part = uni(part);
+    d.s0 = uni(part * k32 / nsplit);
+    d.ns = uni((part + 1) * k32 / nsplit - d.s0);
+    return d;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char slots[kWSlots * kWSlot];
+    const int H = a.H, F = a.F;
+    const int K = KIND == kDX ? 2 * F : H, k32 = K / kWK;
+    const int Nc = KIND == kDX ? H : F;  // output columns
+    const int ntn = (Nc + kWT - 1) / kWT;
+    const int tiles = a.sched[a.G] * ntn;
+    const int P = gridDim.x;
+    const int nsplit = KIND == kDX ? dx_split(tiles, P, a.dx_split_max, 2 * F / kK) : 1;
+    const int total = tiles * nsplit;
+    const int tid = threadIdx.x;
+    const int wave = uni(tid >> 6), lane = tid & 63;
+    const int my_slot = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
+    const size_t FH = (size_t)F * H;
+
+    if (wave >= kWCompute) {
+        // loader lw: A copy q (q = lw + 2 i, i < 8) covers rows 16q .. 16q + 15
+        // (four lanes a row), B copy q k-rows 2q and 2q + 1
+        const int lw = wave - kWCompute;
+        const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
+        const uint16_t* asrc = KIND == kDX ? a.dgu : a.dys;
+        const int lda = KIND == kDX ? 2 * F : H;
+        const int ldb = KIND == kDX ? H : F;  // weight row length (B columns)
+        int lu = my_slot, ls = 0;
+        DTile lt = {};
+        uint32_t aoff[8], boff[8];
+        auto seek = [&]() {
+            for (; lu < total; lu += P) {
+                lt = dtile(a, lu, tiles, ntn, nsplit, k32);
+                if (lt.ns > 0) break;
+            }
+            if (lu >= total) return;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = lw + 2 * i;
+                const int row = 16 * q + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
+                aoff[i] = (uint32_t)min(row, lt.rows - 1) * (uint32_t)lda * 2u + (uint32_t)c * 16u;
+                const int kr = 2 * q + (lane >> 5), cb = (lane & 31) ^ kswz(kr);
+                boff[i] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)min(lt.n0 + 8 * cb, ldb - 8) * 2u;
+            }
+        };
+        seek();
+        int issued = 0;
+        auto issue = [&]() {
+            const uint32_t slot = slots_u + (uint32_t)(issued % kWSlots) * kWSlot;
+            const int s = lt.s0 + ls;
+            const uint16_t* ab = uni_ptr(asrc + (size_t)lt.hrow0 * lda + s * kWK);
+            const uint16_t* wb;
+            if (KIND == kDH) {
+                wb = a.wd + lt.e * FH + (size_t)s * kWK * F;
+            } else {
+                const int k0 = s * kWK;  // F % 32 == 0: a stage is all gate or all up
+                wb = k0 < F ? a.wg + lt.e * FH + (size_t)k0 * H : a.wu + lt.e * FH + (size_t)(k0 - F) * H;
+            }
+            wb = uni_ptr(wb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) copy16(ab, aoff[i], slot + (lw + 2 * i) * 1024);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) copy16(wb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
+            ++issued;
+            if (++ls >= lt.ns) {
+                ls = 0;
+                lu += P;
+                seek();
+            }
+        };
+        while (issued < kWSlots - 1 && lu < total) issue();
+        for (int g = 0; g < issued; ++g) {
+            const int after = issued - 1 - g;
+            if (after >= 3) wait_vm_lgkm<3 * kWCopies>();
+            else if (after == 2) wait_vm_lgkm<2 * kWCopies>();
+            else if (after == 1) wait_vm_lgkm<kWCopies>();
+            else wait_vm_lgkm<0>();
+            slot_barrier();
+            if (lu < total) issue();
+        }
+        return;
+    }
+
+    const int wm = wave >> 2, wn = wave & 3;
+    int g = 0;  // stages consumed
+    for (int u = my_slot; u < total; u += P) {
+        const DTile t = dtile(a, u, tiles, ntn, nsplit, k32);
+        if (t.ns <= 0) continue;
+        // fragment offsets from an opaque copy of the lane index (recomputed
+        // per tile, not held through the epilogue): A row 32 blk + fr, unit
+        // 2 kk + fh; B as in the weight gradients
+        uint32_t fa[2], fb0[2], fb1[2];
+        {
+            int ln;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            const int fr = ln & 31, fh = ln >> 5;
+            const int m_in = 16 * ((ln >> 4) & 1) + 4 * (ln & 3);
+            const int lx = (ln >> 2) & 3;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                fa[kk] = (uint32_t)(fr * 64 + 16 * ((2 * kk + fh) ^ ((fr >> 2) & 3)) + wm * 4 * 2048);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kr = 16 * kk + 8 * fh + 4 * h + ((ln & 15) >> 2);
+                    const uint32_t in = (uint32_t)kr * 512u + (uint32_t)((m_in >> 3) << 4) +
+                                        (uint32_t)((m_in & 7) * 2);
+                    (h ? fb1 : fb0)[kk] = in | (uint32_t)(((wn * 2) ^ lx) << 6);
+                }
+            }
+        }
+        f32x16 acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+        for (int s = 0; s < t.ns; ++s, ++g) {
+            slot_barrier();
+            const char* sa = slots + (g % kWSlots) * kWSlot;
+            const char* sb = sa + kWOp;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 af[4], bfr[2];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) af[i] = lds_frag(sa + fa[kk] + i * 2048);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bfr[j] = lds_frag_tr(sb + (fb0[kk] ^ (j << 6)), sb + (fb1[kk] ^ (j << 6)));
+                // B first: a lane holds 4 consecutive output columns
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            }
+        }
+
+        // acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + fr,
+        // 64 wn + 32 j + 8 g4 + 4 fh + q) of the tile
+        int el;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+        const int er = el & 31, eh = el >> 5;
+        if (KIND == kDX && nsplit > 1) {
+            // fp32 partials (expert order), summed by dx_fixup_kernel
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = wm * 128 + i * 32 + er;
+                if (m >= t.rows) continue;
+                float* prow = a.dxpart + ((size_t)t.part * a.N + t.hrow0 + m) * H;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
+                        if (col >= H) continue;
+                        *reinterpret_cast<f32x4*>(prow + col) =
+                            f32x4{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                  acc[i][j][4 * g4 + 3]};
+                    }
+            }
+        } else if (KIND == kDX) {
+            // bf16 rows scattered back to buffer order (every row index
+            // loaded before the first store)
+            int orow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                orow[i] = a.vrow[t.hrow0 + min(wm * 128 + i * 32 + er, t.rows - 1)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = wm * 128 + i * 32 + er;
+                if (m >= t.rows) continue;
+                uint16_t* orp = a.dxbuf + (size_t)orow[i] * H;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
+                        if (col >= H) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]);
+                        pk.y = moe::pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+                        *reinterpret_cast<uint2*>(orp + col) = pk;
+                    }
+            }
+        } else {
+            // DH: the SwiGLU backward, 32 x 32 block by block (the block's
+            // g | u loaded before any of its stores)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = wm * 128 + i * 32 + er;
+                if (m >= t.rows) continue;
+                const size_t r2 = (size_t)(t.hrow0 + m) * 2 * F;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    uint2 gp[4], up[4];
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = min(t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4, F - 4);
+                        gp[g4] = *reinterpret_cast<const uint2*>(a.gu + r2 + col);
+                        up[g4] = *reinterpret_cast<const uint2*>(a.gu + r2 + F + col);
+                    }
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
+                        if (col >= F) continue;
+                        const uint2 gq = gp[g4], uq = up[g4];
+                        const float gv[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xffff0000u),
+                                             __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xffff0000u)};
+                        const float uv[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xffff0000u),
+                                             __uint_as_float(uq.y << 16), __uint_as_float(uq.y & 0xffff0000u)};
+                        float dg[4], du[4], hv[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float dh = acc[i][j][4 * g4 + q];
+                            const float sg = sigm(gv[q]);
+                            const float sl = gv[q] * sg;
+                            hv[q] = sl * uv[q];
+                            du[q] = dh * sl;
+                            dg[q] = dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                        }
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(dg[0], dg[1]);
+                        pk.y = moe::pack_bf16x2(dg[2], dg[3]);
+                        *reinterpret_cast<uint2*>(a.dgu + r2 + col) = pk;
+                        pk.x = moe::pack_bf16x2(du[0], du[1]);
+                        pk.y = moe::pack_bf16x2(du[2], du[3]);
+                        *reinterpret_cast<uint2*>(a.dgu + r2 + F + col) = pk;
+                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                        *reinterpret_cast<uint2*>(a.hb + (size_t)(t.hrow0 + m) * F + col) = pk;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // rows of src (buffer order) into expert order: dst[x] = src[vrow[x]]
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int N, int row_vecs,
                                                                const int32_t* __restrict__ vrow,
@@ -1104,8 +1381,10 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
                                                     static_cast<const uint4*>(dy),
                                                     reinterpret_cast<uint4*>(ws + B.dys));
         if (!gu && (e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
-        if ((e = launch_kind<kDH>(a, grid, st)) != hipSuccess) return e;
-        if ((e = launch_kind<kDX>(a, grid, st)) != hipSuccess) return e;
+        dgrad_kernel<kDH><<<grid, kWThreads, 0, st>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        dgrad_kernel<kDX><<<grid, kWThreads, 0, st>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         if (a.dx_split_max > 1) {
             const int64_t n4 = N * (s.H / 4);
             dx_fixup_kernel<<<(unsigned)((n4 + kThreads - 1) / kThreads), kThreads, 0, st>>>(a, grid);
