@@ -12,24 +12,25 @@
 // paragraph 3 reduces replica gradients home).
 //
 // Rows are first gathered into expert order (x and dy), so every operand is
-// a run of contiguous rows. Five instances of one kernel:
+// a run of contiguous rows. Five GEMMs, three instances of the row kernel
+// and two of the weight-gradient kernel:
 //   GU   g | u = x [W_gate; W_up]^T   (recomputed; M = rows, N = 2F, K = H)
 //   DH   dh = dy W_down, with the SwiGLU backward in the epilogue
 //        (M = rows, N = F, K = H) -> dg | du, h
 //   DX   dx = [dg | du] [W_gate; W_up]   (M = rows, N = H, K = 2F),
 //        rows scattered back to buffer order
-//   WD   dW_down = dy^T h                 (M = H, N = F, K = rows)
-//   WGU  [dW_gate; dW_up] = [dg | du]^T x (M = 2F, N = H, K = rows)
-// An operand is either K-contiguous (rows of the tile along K: the forward
-// kernel's 128-byte swizzled rows, one ds_read_b128 per fragment) or
-// k-major (rows of 256 elements per k, as the weights are laid out for DH
-// and DX and the activations for the weight gradients): its 64 k-rows of a
-// stage sit in LDS as 512-byte rows with 16-byte chunk c at c ^ 4 (k & 3),
-// and each fragment is two ds_read_b64_tr_b16 (gfx950's transposing LDS
-// read) -- no transposed copy of any tensor is made. Tiles are 256 x 256,
-// four waves in 2 x 2, K in 64-deep stages through two 64 KB LDS slots
-// (global -> LDS copies, one stage ahead). The weight gradients are fp32,
-// written once per (expert, tile); K past an expert's rows reads a zero page.
+//   WD   dW_down = dy^T h                 (M = F, N = H, K = rows)
+//   WGU  [dW_gate; dW_up] = x^T [dg | du] (M = H, N = 2F, K = rows)
+// An operand is either K-contiguous (rows of the tile along K) or k-major
+// (rows of 256 elements per k, as the weights are laid out for DH and DX and
+// the activations for the weight gradients): its k-rows sit in LDS as
+// 512-byte rows with 16-byte chunk c at c ^ 4 (k & 3), and each fragment is
+// two ds_read_b64_tr_b16 (gfx950's transposing LDS read) -- no transposed
+// copy of any tensor is made. Both kernels are warp-specialised: two loader
+// waves stream 32-deep stages of a 256 x 256 tile's operands through a ring
+// of five LDS slots (global -> LDS copies), eight compute waves only read
+// LDS, issue MFMAs and store. The weight gradients are fp32, written once
+// per (expert, tile); K past an expert's rows reads a zero page.
 #include "common.h"
 #include "lds_pipe.h"
 
@@ -37,11 +38,8 @@ namespace {
 
 using namespace moe::lds;
 
-constexpr int kThreads = 256;
-constexpr int kT = 256;          // tile rows and columns
-constexpr int kK = 64;           // K per stage
-constexpr int kOp = kT * kK * 2; // 32 KB: one operand of one stage
-constexpr int kSlot = 2 * kOp;   // A, then B
+constexpr int kThreads = 256;   // the elementwise and fp32 kernels
+constexpr int kK = 64;          // K granule of the DX K-split's part-length rule
 
 enum Kind { kGU = 0, kDH = 1, kDX = 2, kWD = 3, kWGU = 4 };
 
@@ -89,397 +87,9 @@ __host__ __device__ inline int dx_split(int tiles, int P, int smax, int stages)
 // chunk swizzle of a k-major row: 4 consecutive k-rows cover all 64 banks
 __device__ __forceinline__ int kswz(int kr) { return (kr & 3) << 2; }
 
-template <int KIND>
-struct Traits {
-    // operand kinds: true = k-major
-    static constexpr bool kAC = KIND == kWD || KIND == kWGU;
-    static constexpr bool kBC = KIND != kGU;
-    static constexpr bool kWgrad = KIND == kWD || KIND == kWGU;
-};
-
-struct Tile {
-    int e, m0, n0, rows, hrow0, ns;  // rows: valid M rows (dgrad) or K rows (wgrad)
-    int out;                         // wgrad: -1 home gradient, >= 0 replica slot, -2 none
-};
-
 __device__ __forceinline__ float sigm(float z)
 {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-}
-
-template <int KIND>
-__device__ __forceinline__ int tiles_total(const BwdArgs& a, int ntn, int mtw, int ntw)
-{
-    if (Traits<KIND>::kWgrad) return (a.rgroups ? 2 * a.G : a.G) * mtw * ntw;
-    return a.sched[a.G] * ntn;
-}
-
-template <int KIND>
-__device__ __forceinline__ Tile tile_at(int t, const BwdArgs& a, int ntn, int mtw, int ntw)
-{
-    const int32_t* ts = a.sched;
-    const int32_t* rs = a.sched + a.G + 1;
-    Tile r;
-    if (Traits<KIND>::kWgrad) {
-        const int g = t / (mtw * ntw);
-        const int local = t % (mtw * ntw);
-        r.m0 = (local / ntw) * kT;
-        r.n0 = (local % ntw) * kT;
-        if (a.rgroups) {  // one group per home expert / replica slot: a row range of e
-            const int32_t* gr = a.rgroups + 4 * g;
-            r.e = gr[0];
-            r.out = gr[3];
-            r.hrow0 = rs[r.e] + gr[1];
-            r.rows = gr[2] - gr[1];
-        } else {
-            r.e = g;
-            r.out = -1;
-            r.hrow0 = rs[r.e];
-            r.rows = rs[r.e + 1] - rs[r.e];
-        }
-        r.ns = (r.rows + kK - 1) / kK;
-        return r;
-    }
-    r.out = -1;
-    int lo = 0, hi = a.G - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (ts[mid] * ntn <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    const int mt_e = ts[lo + 1] - ts[lo];
-    const int local = t - ts[lo] * ntn;
-    r.e = lo;
-    r.n0 = (local / mt_e) * kT;
-    r.m0 = (local % mt_e) * kT;
-    const int c_e = rs[lo + 1] - rs[lo];
-    r.rows = min(kT, c_e - r.m0);
-    r.hrow0 = rs[lo] + r.m0;
-    const int K = KIND == kDX ? 2 * a.F : a.H;
-    r.ns = K / kK;
-    return r;
-}
-
-template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void bwd_gemm_kernel(BwdArgs a)
-{
-    using TR = Traits<KIND>;
-    __shared__ __attribute__((aligned(1024))) char slots[2 * kSlot];
-
-    const int H = a.H, F = a.F;
-    const int ntn = KIND == kGU ? (2 * F + kT - 1) / kT : KIND == kDH ? (F + kT - 1) / kT
-                                                                      : (H + kT - 1) / kT;
-    const int mtw = KIND == kWD ? (H + kT - 1) / kT : (2 * F + kT - 1) / kT;
-    const int ntw = KIND == kWD ? (F + kT - 1) / kT : (H + kT - 1) / kT;
-    const int tiles = tiles_total<KIND>(a, ntn, mtw, ntw);
-    const int nsplit = KIND == kDX ? dx_split(tiles, gridDim.x, a.dx_split_max, 2 * F / kK) : 1;
-    const int total = tiles * nsplit;  // units: part-major, then tile
-
-    const int tid = threadIdx.x;
-    const int wave = uni(tid >> 6), lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int fr = lane & 31, fh = lane >> 5;
-    const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
-    const char* zero = a.zero;
-
-    // fragment offsets, k-steps 0..3. K-contiguous: row fr of a 32-row block
-    // (block b at + 4096 b). k-major: lane reads 4 columns m (+ 32 b) at k-row
-    // kr; chunk 4 b + (m >> 3) sits at (4 b + (m >> 3)) ^ 4 (kr & 3), and as
-    // m >> 3 < 4 and kr & 3 = (lane >> 2) & 3 for every read of this lane, the
-    // block part is ((b ^ ((lane >> 2) & 3)) << 6) bytes, added per block.
-    uint32_t frow[4], fcol0[4], fcol1[4];
-    const int m_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        frow[kk] = (uint32_t)fr * 128u + (uint32_t)(((2 * kk + fh) ^ swz(fr)) * 16);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kr = 16 * kk + 8 * fh + 4 * h + ((lane & 15) >> 2);
-            const uint32_t off = (uint32_t)kr * 512u + (uint32_t)((m_in >> 3) << 4) +
-                                 (uint32_t)((m_in & 7) * 2);
-            (h ? fcol1 : fcol0)[kk] = off;
-        }
-    }
-    const int lx = (lane >> 2) & 3;
-    uint32_t xa[4], xb[4];  // block parts of this wave's A and B column blocks
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        xa[i] = (uint32_t)(((wm * 4 + i) ^ lx) << 6);
-        xb[i] = (uint32_t)(((wn * 4 + i) ^ lx) << 6);
-    }
-
-    // each XCD (workgroups are dealt to the 8 XCDs round-robin) takes a
-    // contiguous run of tiles, so tiles sharing an operand share that L2
-    const int P = gridDim.x;
-    const int my_slot = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
-    for (int u = my_slot; u < total; u += P) {
-        const int part = u / tiles;
-        const Tile tl = tile_at<KIND>(u % tiles, a, ntn, mtw, ntw);
-        if (TR::kWgrad && uni(tl.out) == -2) continue;  // an unused replica slot
-        const int e = uni(tl.e), m0 = uni(tl.m0), n0 = uni(tl.n0), rows = uni(tl.rows);
-        // this unit's K stages [s0, s0 + ns) of the tile's tl.ns
-        const int s0 = uni(part * tl.ns / nsplit);
-        const int hrow0 = uni(tl.hrow0), ns = uni((part + 1) * tl.ns / nsplit - s0);
-        const size_t FH = (size_t)F * H;
-
-        // K-contiguous operands (uniform base + 32-bit lane offsets, as in the
-        // forward kernel): copy q covers tile rows 8q .. 8q+7, lane l row
-        // 8q + l/8, chunk l % 8 stored at its swizzled slot. Rows past the
-        // tile's valid rows repeat the last one (their results are dropped).
-        const char* abase = nullptr;
-        const char* bbase[8];
-        uint32_t aoff[8], boff[8];
-        if (!TR::kAC) {
-            const int lda = KIND == kDX ? 2 * F : H;
-            const uint16_t* src = KIND == kGU ? a.xs : KIND == kDH ? a.dys : a.dgu;
-            abase = uni_ptr(reinterpret_cast<const char*>(src + (size_t)hrow0 * lda));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 8 * (wave + 4 * i) + (lane >> 3);
-                aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)lda * 2u +
-                          (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-            }
-        }
-        // dgrad k-major weights (DH: W_down rows h; DX: W_gate / W_up rows f):
-        // K is never ragged there, so a uniform base per stage and one 32-bit
-        // lane offset per copy; columns past the end repeat the last chunk
-        // (those output columns are dropped)
-        if (KIND == kDH || KIND == kDX) {
-            const int ld = KIND == kDH ? F : H;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = wave + 4 * i;
-                const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
-                const int col = min(n0 + 8 * c, ld - 8);
-                boff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)col * 2u;
-            }
-        }
-        if (!TR::kBC) {  // GU: rows n of [W_gate; W_up] (F % 8 == 0: one side per copy)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = wave + 4 * i;
-                const int row = 8 * q + (lane >> 3);
-                const bool up = n0 + 8 * q >= F;
-                const int n = min(n0 + row, 2 * F - 1) - (up ? F : 0);
-                bbase[i] = uni_ptr(reinterpret_cast<const char*>((up ? a.wu : a.wg) + e * FH));
-                boff[i] = (uint32_t)n * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-            }
-        }
-        // k-major operands: k-row k (absolute in the K range), column chunk c
-        // (8 elements) of the tile; NULL selects the zero page
-        auto a_krow = [&](int k, int c) -> const char* {
-            const int col = m0 + 8 * c;
-            if (k >= rows) return nullptr;
-            if (KIND == kWD) return col < H ? (const char*)(a.dys + (size_t)(hrow0 + k) * H + col) : nullptr;
-            return col < 2 * F ? (const char*)(a.dgu + (size_t)(hrow0 + k) * 2 * F + col) : nullptr;
-        };
-        auto b_krow = [&](int k, int c) -> const char* {  // weight gradients only
-            const int col = n0 + 8 * c;
-            if (k >= rows) return nullptr;
-            if (KIND == kWD) return col < F ? (const char*)(a.hb + (size_t)(hrow0 + k) * F + col) : nullptr;
-            return col < H ? (const char*)(a.xs + (size_t)(hrow0 + k) * H + col) : nullptr;  // WGU
-        };
-
-        // local stage j (absolute s = s0 + j) into slot j & 1: 32 copies per
-        // operand, q = wave + 4 i
-        auto copy_stage = [&](int j) {
-            const uint32_t slot = slots_u + (uint32_t)(j & 1) * kSlot;
-            const int s = s0 + j;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = wave + 4 * i;
-                if (TR::kAC) {
-                    const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
-                    const char* p = a_krow(s * kK + kr, c);
-                    copy16_at(p ? p : zero + c * 16, slot + q * 1024);
-                } else {
-                    copy16(abase + s * (kK * 2), aoff[i], slot + q * 1024);
-                }
-            }
-            // DH / DX: this stage's 64 weight rows start at a uniform base
-            const char* wbase = nullptr;
-            if (KIND == kDH) {
-                wbase = reinterpret_cast<const char*>(a.wd + e * FH + (size_t)s * kK * F);
-            } else if (KIND == kDX) {
-                const int k0 = s * kK;  // F % 64 == 0: a stage is all gate or all up
-                wbase = k0 < F ? reinterpret_cast<const char*>(a.wg + e * FH + (size_t)k0 * H)
-                               : reinterpret_cast<const char*>(a.wu + e * FH + (size_t)(k0 - F) * H);
-            }
-            wbase = uni_ptr(wbase);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = wave + 4 * i;
-                if (KIND == kDH || KIND == kDX) {
-                    copy16(wbase, boff[i], slot + kOp + q * 1024);
-                } else if (TR::kBC) {
-                    const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
-                    const char* p = b_krow(s * kK + kr, c);
-                    copy16_at(p ? p : zero + c * 16, slot + kOp + q * 1024);
-                } else {
-                    copy16(bbase[i] + s * (kK * 2), boff[i], slot + kOp + q * 1024);
-                }
-            }
-        };
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-        // Two stages in flight: stage s's fragments are all read into
-        // registers during its first two k-steps, then (every wave done
-        // reading) its slot takes stage s + 2 while k-steps 2 and 3 run.
-        constexpr int kCopies = 16;  // copy instructions per wave per stage
-        wait_vm_lgkm<0>();
-        slot_barrier();  // the previous tile's slots are no longer read
-        if (ns > 0) copy_stage(0);
-        if (ns > 1) copy_stage(1);
-        for (int s = 0; s < ns; ++s) {
-            if (s + 1 < ns) wait_vm_lgkm<kCopies>();  // stage s landed; s+1 may be in flight
-            else wait_vm_lgkm<0>();
-            slot_barrier();
-            const char* sa = slots + (s & 1) * kSlot;
-            const char* sb = sa + kOp;
-            bf16x8 af[4][4], bfr[4][4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int blk = wm * 4 + i;  // 32-row / 32-column block of A
-                    af[kk][i] = TR::kAC ? lds_frag_tr(sa + fcol0[kk] + xa[i], sa + fcol1[kk] + xa[i])
-                                        : lds_frag(sa + frow[kk] + blk * 4096);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int blk = wn * 4 + j;
-                    bfr[kk][j] = TR::kBC ? lds_frag_tr(sb + fcol0[kk] + xb[j], sb + fcol1[kk] + xb[j])
-                                         : lds_frag(sb + frow[kk] + blk * 4096);
-                }
-            }
-            // dgrad: B first, so a lane holds 4 consecutive output columns
-            // (8-byte bf16 stores); weight gradients: A first, so 32 lanes
-            // hold 32 consecutive columns of one row (128-byte fp32 stores)
-            auto mfmas = [&](int kk) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = TR::kWgrad
-                            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0)
-                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0);
-            };
-            mfmas(0);
-            mfmas(1);
-            if (s + 2 < ns) {
-                // every fragment of stage s is in registers (lgkmcnt(0)) in
-                // every wave: its slot is free; stage s+1 may still be landing
-                wait_vm_lgkm<kCopies>();
-                slot_barrier();
-                copy_stage(s + 2);
-            }
-            mfmas(2);
-            mfmas(3);
-        }
-
-        if (TR::kWgrad) {
-            // the expert's own gradient, or its replica slot's
-            const int out = uni(tl.out);
-            float* gdst = out < 0 ? a.dwg + e * FH : a.rgrad + ((size_t)out * 3 + 0) * FH;
-            float* udst = out < 0 ? a.dwu + e * FH : a.rgrad + ((size_t)out * 3 + 1) * FH;
-            float* ddst = out < 0 ? a.dwd + e * FH : a.rgrad + ((size_t)out * 3 + 2) * FH;
-            // acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + 8 g4 + 4 fh + q,
-            // 128 wn + 32 j + fr): one fp32 store per value, 32 lanes along a row
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = n0 + wn * 128 + j * 32 + fr;
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int row = m0 + wm * 128 + i * 32 + g4 * 8 + fh * 4 + q;
-                            const float v = acc[i][j][g4 * 4 + q];
-                            if (KIND == kWD) {
-                                if (row < H && col < F) ddst[(size_t)row * F + col] = v;
-                            } else if (row < 2 * F && col < H) {
-                                float* dst = row < F ? gdst + (size_t)row * H
-                                                     : udst + (size_t)(row - F) * H;
-                                dst[col] = v;
-                            }
-                        }
-                }
-            continue;
-        }
-        // epilogue: acc[i][j][4 g4 + q] is (m, n) = (128 wm + 32 i + fr,
-        // 128 wn + 32 j + 8 g4 + 4 fh + q) of the tile
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = wm * 128 + i * 32 + fr;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = wn * 128 + j * 32 + g4 * 8 + fh * 4;
-                    const float v0 = acc[i][j][g4 * 4], v1 = acc[i][j][g4 * 4 + 1];
-                    const float v2 = acc[i][j][g4 * 4 + 2], v3 = acc[i][j][g4 * 4 + 3];
-                    if (KIND == kGU) {
-                        const int col = n0 + n;
-                        if (m >= rows || col >= 2 * F) continue;
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(v0, v1);
-                        pk.y = moe::pack_bf16x2(v2, v3);
-                        *reinterpret_cast<uint2*>(a.gu + (size_t)(hrow0 + m) * 2 * F + col) = pk;
-                    } else if (KIND == kDH) {
-                        const int col = n0 + n;
-                        if (m >= rows || col >= F) continue;
-                        const size_t r2 = (size_t)(hrow0 + m) * 2 * F;
-                        const uint2 gp = *reinterpret_cast<const uint2*>(a.gu + r2 + col);
-                        const uint2 up = *reinterpret_cast<const uint2*>(a.gu + r2 + F + col);
-                        const float g[4] = {__uint_as_float(gp.x << 16), __uint_as_float(gp.x & 0xffff0000u),
-                                            __uint_as_float(gp.y << 16), __uint_as_float(gp.y & 0xffff0000u)};
-                        const float u[4] = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
-                                            __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
-                        const float dh[4] = {v0, v1, v2, v3};
-                        float dg[4], du[4], hv[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float sg = sigm(g[q]);
-                            const float sl = g[q] * sg;
-                            hv[q] = sl * u[q];
-                            du[q] = dh[q] * sl;
-                            dg[q] = dh[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
-                        }
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(dg[0], dg[1]);
-                        pk.y = moe::pack_bf16x2(dg[2], dg[3]);
-                        *reinterpret_cast<uint2*>(a.dgu + r2 + col) = pk;
-                        pk.x = moe::pack_bf16x2(du[0], du[1]);
-                        pk.y = moe::pack_bf16x2(du[2], du[3]);
-                        *reinterpret_cast<uint2*>(a.dgu + r2 + F + col) = pk;
-                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
-                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
-                        *reinterpret_cast<uint2*>(a.hb + (size_t)(hrow0 + m) * F + col) = pk;
-                    } else if (KIND == kDX) {
-                        const int col = n0 + n;
-                        if (m >= rows || col >= H) continue;
-                        if (nsplit > 1) {  // fp32 partial, summed by dx_fixup_kernel
-                            float* dst = a.dxpart + ((size_t)part * a.N + hrow0 + m) * H + col;
-                            *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-                            continue;
-                        }
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(v0, v1);
-                        pk.y = moe::pack_bf16x2(v2, v3);
-                        *reinterpret_cast<uint2*>(a.dxbuf + (size_t)a.vrow[hrow0 + m] * H + col) = pk;
-                    }
-                }
-            }
-        }
-    }
 }
 
 // The weight gradients, warp-specialised. Their fp32 outputs (F x H floats
@@ -777,16 +387,17 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
     }
 }
 
-// The data gradients DH and DX on the same ring (32-deep stages, two loader
+// The row GEMMs GU, DH and DX on the same ring (32-deep stages, two loader
 // waves, eight compute waves 2 x 4 of 128 x 64, one barrier per stage). A
-// (dy or dg | du rows) is K-contiguous: a stage holds 64-byte segments of 256
-// rows, 16-byte unit c of row r at c ^ ((r >> 2) & 3), so the 16 rows one
-// ds_read_b128 pass reads hit 16 distinct bank groups; B is the weights'
-// k-major rows as above. Rows past an M-tile's valid rows repeat its last
-// row and weight columns past the end repeat the last chunk (those outputs
-// are dropped). Units: K-split part, then expert, N-tile, M-tile (M
-// fastest). The bf16 outputs are small beside the weight gradients' and
-// leave straight from the accumulators.
+// (x, dy or dg | du rows) is K-contiguous: a stage holds 64-byte segments of
+// 256 rows, 16-byte unit c of row r at c ^ ((r >> 2) & 3), so the 16 rows
+// one ds_read_b128 pass reads hit 16 distinct bank groups. B is the weights:
+// for DH and DX their k-major rows as above, for GU the rows n of
+// [W_gate; W_up], K-contiguous like A. Rows past an M-tile's valid rows
+// repeat its last row and weight columns (rows) past the end repeat the last
+// one (those outputs are dropped). Units: K-split part, then expert, N-tile,
+// M-tile (M fastest). The bf16 outputs are small beside the weight
+// gradients' and leave straight from the accumulators.
 struct DTile {
     int e, m0, n0, rows, hrow0, s0, ns, part;
 };
@@ -823,7 +434,7 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
     __shared__ __attribute__((aligned(1024))) char slots[kWSlots * kWSlot];
     const int H = a.H, F = a.F;
     const int K = KIND == kDX ? 2 * F : H, k32 = K / kWK;
-    const int Nc = KIND == kDX ? H : F;  // output columns
+    const int Nc = KIND == kDX ? H : KIND == kGU ? 2 * F : F;  // output columns
     const int ntn = (Nc + kWT - 1) / kWT;
     const int tiles = a.sched[a.G] * ntn;
     const int P = gridDim.x;
@@ -839,12 +450,13 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
         // (four lanes a row), B copy q k-rows 2q and 2q + 1
         const int lw = wave - kWCompute;
         const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
-        const uint16_t* asrc = KIND == kDX ? a.dgu : a.dys;
+        const uint16_t* asrc = KIND == kDX ? a.dgu : KIND == kGU ? a.xs : a.dys;
         const int lda = KIND == kDX ? 2 * F : H;
-        const int ldb = KIND == kDX ? H : F;  // weight row length (B columns)
+        const int ldb = KIND == kDX ? H : KIND == kGU ? H : F;  // weight row length
         int lu = my_slot, ls = 0;
         DTile lt = {};
         uint32_t aoff[8], boff[8];
+        const uint16_t* gbase[8];  // GU: the weight matrix of copy i's 16 rows
         auto seek = [&]() {
             for (; lu < total; lu += P) {
                 lt = dtile(a, lu, tiles, ntn, nsplit, k32);
@@ -856,8 +468,16 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
                 const int q = lw + 2 * i;
                 const int row = 16 * q + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
                 aoff[i] = (uint32_t)min(row, lt.rows - 1) * (uint32_t)lda * 2u + (uint32_t)c * 16u;
-                const int kr = 2 * q + (lane >> 5), cb = (lane & 31) ^ kswz(kr);
-                boff[i] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)min(lt.n0 + 8 * cb, ldb - 8) * 2u;
+                if (KIND == kGU) {
+                    // rows n0 + 16q .. + 15 of [W_gate; W_up] (F % 16 == 0: one side)
+                    const bool up = lt.n0 + 16 * q >= F;
+                    const int n = min(lt.n0 + row, 2 * F - 1) - (up ? F : 0);
+                    gbase[i] = uni_ptr((up ? a.wu : a.wg) + lt.e * FH);
+                    boff[i] = (uint32_t)n * (uint32_t)H * 2u + (uint32_t)c * 16u;
+                } else {
+                    const int kr = 2 * q + (lane >> 5), cb = (lane & 31) ^ kswz(kr);
+                    boff[i] = (uint32_t)kr * (uint32_t)ldb * 2u + (uint32_t)min(lt.n0 + 8 * cb, ldb - 8) * 2u;
+                }
             }
         };
         seek();
@@ -866,10 +486,10 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
             const uint32_t slot = slots_u + (uint32_t)(issued % kWSlots) * kWSlot;
             const int s = lt.s0 + ls;
             const uint16_t* ab = uni_ptr(asrc + (size_t)lt.hrow0 * lda + s * kWK);
-            const uint16_t* wb;
+            const uint16_t* wb = nullptr;
             if (KIND == kDH) {
                 wb = a.wd + lt.e * FH + (size_t)s * kWK * F;
-            } else {
+            } else if (KIND == kDX) {
                 const int k0 = s * kWK;  // F % 32 == 0: a stage is all gate or all up
                 wb = k0 < F ? a.wg + lt.e * FH + (size_t)k0 * H : a.wu + lt.e * FH + (size_t)(k0 - F) * H;
             }
@@ -877,7 +497,8 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) copy16(ab, aoff[i], slot + (lw + 2 * i) * 1024);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) copy16(wb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
+            for (int i = 0; i < 8; ++i)
+                copy16(KIND == kGU ? gbase[i] + s * kWK : wb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
             ++issued;
             if (++ls >= lt.ns) {
                 ls = 0;
@@ -906,7 +527,7 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
         // fragment offsets from an opaque copy of the lane index (recomputed
         // per tile, not held through the epilogue): A row 32 blk + fr, unit
         // 2 kk + fh; B as in the weight gradients
-        uint32_t fa[2], fb0[2], fb1[2];
+        uint32_t fa[2], fb0[2], fb1[2];  // GU: fb0 is B's K-contiguous offset
         {
             int ln;
             asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
@@ -916,6 +537,8 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 fa[kk] = (uint32_t)(fr * 64 + 16 * ((2 * kk + fh) ^ ((fr >> 2) & 3)) + wm * 4 * 2048);
+                fb0[kk] = fb1[kk] = (uint32_t)(fr * 64 + 16 * ((2 * kk + fh) ^ ((fr >> 2) & 3)) + wn * 2 * 2048);
+                if (KIND == kGU) continue;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kr = 16 * kk + 8 * fh + 4 * h + ((ln & 15) >> 2);
@@ -944,7 +567,8 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
                 for (int i = 0; i < 4; ++i) af[i] = lds_frag(sa + fa[kk] + i * 2048);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    bfr[j] = lds_frag_tr(sb + (fb0[kk] ^ (j << 6)), sb + (fb1[kk] ^ (j << 6)));
+                    bfr[j] = KIND == kGU ? lds_frag(sb + fb0[kk] + j * 2048)
+                                         : lds_frag_tr(sb + (fb0[kk] ^ (j << 6)), sb + (fb1[kk] ^ (j << 6)));
                 // B first: a lane holds 4 consecutive output columns
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -959,7 +583,25 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
         int el;
         asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
         const int er = el & 31, eh = el >> 5;
-        if (KIND == kDX && nsplit > 1) {
+        if (KIND == kGU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = wm * 128 + i * 32 + er;
+                if (m >= t.rows) continue;
+                uint16_t* grow = a.gu + (size_t)(t.hrow0 + m) * 2 * F;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
+                        if (col >= 2 * F) continue;
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]);
+                        pk.y = moe::pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+                        *reinterpret_cast<uint2*>(grow + col) = pk;
+                    }
+            }
+        } else if (KIND == kDX && nsplit > 1) {
             // fp32 partials (expert order), summed by dx_fixup_kernel
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1071,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int N, int row_ve
 __global__ __launch_bounds__(kThreads) void dx_fixup_kernel(BwdArgs a, int P)
 {
     const int H = a.H;
-    const int tiles = a.sched[a.G] * ((H + kT - 1) / kT);
+    const int tiles = a.sched[a.G] * ((H + kWT - 1) / kWT);
     const int nsplit = dx_split(tiles, P, a.dx_split_max, 2 * a.F / kK);
     if (nsplit <= 1) return;
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 4 columns each
@@ -1283,13 +925,6 @@ __global__ __launch_bounds__(kThreads) void bwd_f32_wgrad_kernel(int E, int H, i
     }
 }
 
-template <int KIND>
-hipError_t launch_kind(const BwdArgs& a, int grid, hipStream_t st)
-{
-    bwd_gemm_kernel<KIND><<<grid, kThreads, 0, st>>>(a);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const int32_t* plan,
@@ -1380,7 +1015,10 @@ hipError_t moe_launch_ffn_backward(const moe_shape_t& s, const void* buf, const 
         gather_rows_kernel<<<gb, kThreads, 0, st>>>((int)N, row_vecs, vrow,
                                                     static_cast<const uint4*>(dy),
                                                     reinterpret_cast<uint4*>(ws + B.dys));
-        if (!gu && (e = launch_kind<kGU>(a, grid, st)) != hipSuccess) return e;
+        if (!gu) {
+            dgrad_kernel<kGU><<<grid, kWThreads, 0, st>>>(a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         dgrad_kernel<kDH><<<grid, kWThreads, 0, st>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         dgrad_kernel<kDX><<<grid, kWThreads, 0, st>>>(a);
