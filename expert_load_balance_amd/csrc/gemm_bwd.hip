@@ -115,7 +115,8 @@ constexpr int kWSlot = 2 * kWOp;                          // A, then B
 constexpr int kWSlots = 5;                                // 160 KB of LDS
 constexpr int kWCompute = 8, kWLoaders = 2;               // waves
 constexpr int kWThreads = (kWCompute + kWLoaders) * 64;
-constexpr int kWCopies = kWSlot / 1024 / kWLoaders;       // 16 copies per loader wave per stage
+constexpr int kWCopies = kWSlot / 1024 / kWLoaders;       // copies per loader wave per stage
+constexpr int kWPer = kWCopies / 2;                       // of them per operand
 static_assert(kWCopies * (kWSlots - 2) < 64, "vmcnt range");
 constexpr int kWScratch = 32 * 32 * 4;                    // a compute wave's 32 x 32 fp32 block
 static_assert(kWCompute * kWScratch <= kWSlot, "scratch fits a slot");
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
     const int my_slot = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
 
     if (wave >= kWCompute) {
-        // loader lw: copies q = lw + 2 i (i < 8) of each operand, copy q
+        // loader lw: copies q = lw + kWLoaders i (i < kWPer) of each operand, copy q
         // covering k-rows 2q and 2q + 1 (512 bytes each)
         const int lw = wave - kWCompute;
         const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
         // column past M or N only feeds outputs that are not stored)
         int lu = my_slot, ls = 0;
         WTile lt = {};
-        uint32_t aoff[8], boff[8];
+        uint32_t aoff[kWPer], boff[kWPer];
         auto seek = [&]() {
             for (; lu < total; lu += P) {
                 lt = wtile(a, lu, mtw, ntw);
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
             }
             if (lu >= total) return;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int kr = 2 * (lw + 2 * i) + (lane >> 5), c = (lane & 31) ^ kswz(kr);
+            for (int i = 0; i < kWPer; ++i) {
+                const int kr = 2 * (lw + kWLoaders * i) + (lane >> 5), c = (lane & 31) ^ kswz(kr);
                 aoff[i] = (uint32_t)(kr * astride + min(lt.m0 + 8 * c, M - 8)) * 2u;
                 boff[i] = (uint32_t)(kr * bstride + min(lt.n0 + 8 * c, Nc - 8)) * 2u;
             }
@@ -223,14 +224,14 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(BwdArgs a)
                 const uint16_t* ab = uni_ptr(asrc + r0 * astride);
                 const uint16_t* bb = uni_ptr(bsrc + r0 * bstride);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) copy16(ab, aoff[i], slot + (lw + 2 * i) * 1024);
+                for (int i = 0; i < kWPer; ++i) copy16(ab, aoff[i], slot + (lw + kWLoaders * i) * 1024);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) copy16(bb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
+                for (int i = 0; i < kWPer; ++i) copy16(bb, boff[i], slot + kWOp + (lw + kWLoaders * i) * 1024);
             } else {
                 // the ragged last stage: k-rows past the rows read the zero page
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int q = lw + 2 * i;
+                for (int i = 0; i < kWPer; ++i) {
+                    const int q = lw + kWLoaders * i;
                     const int kr = 2 * q + (lane >> 5), c = (lane & 31) ^ kswz(kr);
                     const int k = kb + kr, ca = lt.m0 + 8 * c, cb = lt.n0 + 8 * c;
                     const bool kin = k < lt.rows;
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
     const size_t FH = (size_t)F * H;
 
     if (wave >= kWCompute) {
-        // loader lw: A copy q (q = lw + 2 i, i < 8) covers rows 16q .. 16q + 15
+        // loader lw: A copy q (q = lw + kWLoaders i, i < kWPer) covers rows 16q .. 16q + 15
         // (four lanes a row), B copy q k-rows 2q and 2q + 1
         const int lw = wave - kWCompute;
         const uint32_t slots_u = (uint32_t)(uintptr_t)slots;
@@ -455,8 +456,8 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
         const int ldb = KIND == kDX ? H : KIND == kGU ? H : F;  // weight row length
         int lu = my_slot, ls = 0;
         DTile lt = {};
-        uint32_t aoff[8], boff[8];
-        const uint16_t* gbase[8];  // GU: the weight matrix of copy i's 16 rows
+        uint32_t aoff[kWPer], boff[kWPer];
+        const uint16_t* gbase[kWPer];  // GU: the weight matrix of copy i's 16 rows
         auto seek = [&]() {
             for (; lu < total; lu += P) {
                 lt = dtile(a, lu, tiles, ntn, nsplit, k32);
@@ -464,8 +465,8 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
             }
             if (lu >= total) return;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = lw + 2 * i;
+            for (int i = 0; i < kWPer; ++i) {
+                const int q = lw + kWLoaders * i;
                 const int row = 16 * q + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
                 aoff[i] = (uint32_t)min(row, lt.rows - 1) * (uint32_t)lda * 2u + (uint32_t)c * 16u;
                 if (KIND == kGU) {
@@ -484,6 +485,29 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
         int issued = 0;
         auto issue = [&]() {
             const uint32_t slot = slots_u + (uint32_t)(issued % kWSlots) * kWSlot;
+            if (KIND == kDH && ls >= lt.ns) {
+                // g | u rows 32 c .. 32 c + 31 of the tile: copy q is row q,
+                // lanes 0..31 its 256 g columns, 32..63 its 256 u columns;
+                // logical 16-byte unit v at v ^ (q & 31) (rows past the
+                // tile's repeat its last; columns past F repeat the last chunk)
+                const int c = ls - lt.ns;
+                const uint16_t* gb = uni_ptr(a.gu + (size_t)lt.hrow0 * 2 * F);
+#pragma unroll
+                for (int i = 0; i < 2 * kWPer; ++i) {
+                    const int q = lw + kWLoaders * i;
+                    const int row = min(32 * c + q, lt.rows - 1);
+                    const int v = lane ^ (q & 31);
+                    const int col = min(lt.n0 + 8 * (v & 31), F - 8) + (v >= 32 ? F : 0);
+                    copy16(gb, (uint32_t)(row * 2 * F + col) * 2u, slot + q * 1024);
+                }
+                ++issued;
+                if (++ls >= lt.ns + (lt.rows + 31) / 32) {
+                    ls = 0;
+                    lu += P;
+                    seek();
+                }
+                return;
+            }
             const int s = lt.s0 + ls;
             const uint16_t* ab = uni_ptr(asrc + (size_t)lt.hrow0 * lda + s * kWK);
             const uint16_t* wb = nullptr;
@@ -495,12 +519,12 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
             }
             wb = uni_ptr(wb);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) copy16(ab, aoff[i], slot + (lw + 2 * i) * 1024);
+            for (int i = 0; i < kWPer; ++i) copy16(ab, aoff[i], slot + (lw + kWLoaders * i) * 1024);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                copy16(KIND == kGU ? gbase[i] + s * kWK : wb, boff[i], slot + kWOp + (lw + 2 * i) * 1024);
+            for (int i = 0; i < kWPer; ++i)
+                copy16(KIND == kGU ? gbase[i] + s * kWK : wb, boff[i], slot + kWOp + (lw + kWLoaders * i) * 1024);
             ++issued;
-            if (++ls >= lt.ns) {
+            if (++ls >= lt.ns + (KIND == kDH ? (lt.rows + 31) / 32 : 0)) {
                 ls = 0;
                 lu += P;
                 seek();
@@ -644,54 +668,57 @@ __global__ __launch_bounds__(kWThreads, 1) void dgrad_kernel(BwdArgs a)
                     }
             }
         } else {
-            // DH: the SwiGLU backward, 32 x 32 block by block (the block's
-            // g | u loaded before any of its stores)
+            // DH: the SwiGLU backward. The tile's g | u follows its K stages
+            // through the ring, 32 rows a slot: slot c = 4 hb + i holds rows
+            // 32 c .. 32 c + 31, row block i of the waves with wm = hb (the
+            // other four only pass the barrier)
+            const int nch = (t.rows + 31) / 32;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = wm * 128 + i * 32 + er;
-                if (m >= t.rows) continue;
-                const size_t r2 = (size_t)(t.hrow0 + m) * 2 * F;
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    uint2 gp[4], up[4];
+                for (int i = 0; i < 4; ++i) {
+                    if (hb * 4 + i >= nch) break;
+                    slot_barrier();
+                    const char* sg = slots + (g % kWSlots) * kWSlot + er * 1024;
+                    ++g;
+                    const int m = wm * 128 + i * 32 + er;
+                    if (wm != hb || m >= t.rows) continue;
+                    const size_t r2 = (size_t)(t.hrow0 + m) * 2 * F;
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = min(t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4, F - 4);
-                        gp[g4] = *reinterpret_cast<const uint2*>(a.gu + r2 + col);
-                        up[g4] = *reinterpret_cast<const uint2*>(a.gu + r2 + F + col);
-                    }
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
-                        if (col >= F) continue;
-                        const uint2 gq = gp[g4], uq = up[g4];
-                        const float gv[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xffff0000u),
-                                             __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xffff0000u)};
-                        const float uv[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xffff0000u),
-                                             __uint_as_float(uq.y << 16), __uint_as_float(uq.y & 0xffff0000u)};
-                        float dg[4], du[4], hv[4];
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int col = t.n0 + wn * 64 + j * 32 + g4 * 8 + eh * 4;
+                            if (col >= F) continue;
+                            const int v = wn * 8 + j * 4 + g4;  // logical unit of the 8 columns
+                            const uint2 gq = *reinterpret_cast<const uint2*>(sg + ((v ^ er) << 4) + eh * 8);
+                            const uint2 uq = *reinterpret_cast<const uint2*>(sg + (((v + 32) ^ er) << 4) + eh * 8);
+                            const float gv[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xffff0000u),
+                                                 __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xffff0000u)};
+                            const float uv[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xffff0000u),
+                                                 __uint_as_float(uq.y << 16), __uint_as_float(uq.y & 0xffff0000u)};
+                            float dg[4], du[4], hv[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float dh = acc[i][j][4 * g4 + q];
-                            const float sg = sigm(gv[q]);
-                            const float sl = gv[q] * sg;
-                            hv[q] = sl * uv[q];
-                            du[q] = dh * sl;
-                            dg[q] = dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                            for (int q = 0; q < 4; ++q) {
+                                const float dh = acc[i][j][4 * g4 + q];
+                                const float sgm = sigm(gv[q]);
+                                const float sl = gv[q] * sgm;
+                                hv[q] = sl * uv[q];
+                                du[q] = dh * sl;
+                                dg[q] = dh * uv[q] * sgm * (1.0f + gv[q] * (1.0f - sgm));
+                            }
+                            uint2 pk;
+                            pk.x = moe::pack_bf16x2(dg[0], dg[1]);
+                            pk.y = moe::pack_bf16x2(dg[2], dg[3]);
+                            *reinterpret_cast<uint2*>(a.dgu + r2 + col) = pk;
+                            pk.x = moe::pack_bf16x2(du[0], du[1]);
+                            pk.y = moe::pack_bf16x2(du[2], du[3]);
+                            *reinterpret_cast<uint2*>(a.dgu + r2 + F + col) = pk;
+                            pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                            pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                            *reinterpret_cast<uint2*>(a.hb + (size_t)(t.hrow0 + m) * F + col) = pk;
                         }
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(dg[0], dg[1]);
-                        pk.y = moe::pack_bf16x2(dg[2], dg[3]);
-                        *reinterpret_cast<uint2*>(a.dgu + r2 + col) = pk;
-                        pk.x = moe::pack_bf16x2(du[0], du[1]);
-                        pk.y = moe::pack_bf16x2(du[2], du[3]);
-                        *reinterpret_cast<uint2*>(a.dgu + r2 + F + col) = pk;
-                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
-                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
-                        *reinterpret_cast<uint2*>(a.hb + (size_t)(t.hrow0 + m) * F + col) = pk;
-                    }
                 }
-            }
         }
     }
 }
