@@ -6,7 +6,10 @@
 // under the expert -> rank mapping) and "Work the 16-token hotspot fixture"
 // (an unknown id or a token repeating an expert stops the count).
 //
-// Three launches, none of whose results depend on thread timing:
+// Up to 16384 assignments, one workgroup of 1024 threads does all three
+// steps below in one launch (the same arithmetic, the scan over its own
+// histogram, the rank rounds 1024 assignments wide). Above that, three
+// launches, none of whose results depend on thread timing:
 //   1. hist: workgroup b histograms assignments [b*C, (b+1)*C) in LDS (the
 //      adds are order-free), writes blk_hist[b][E], and checks ids.
 //   2. scan: one workgroup; thread e scans blk_hist[.][e] over workgroups
@@ -144,6 +147,106 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(int N, int E,
     }
 }
 
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / moe::kWave;
+constexpr int kFusedMax = 16384;  // assignments handled by the one-workgroup path
+
+__global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k, int E, int R,
+                                                                     const int32_t* __restrict__ ids,
+                                                                     int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ eidx,
+                                                                     int32_t* __restrict__ rank_load,
+                                                                     int32_t* err)
+{
+    __shared__ int32_t hist[256];
+    __shared__ int32_t sc[256];
+    __shared__ int32_t base[256];
+    __shared__ int32_t wcnt[kFusedWaves][256];
+    const int tid = threadIdx.x;
+    const int wave = tid / moe::kWave;
+    const int lane = tid % moe::kWave;
+    if (tid < 256) hist[tid] = 0;
+    for (int x = tid; x < kFusedWaves * 256; x += kFusedThreads) (&wcnt[0][0])[x] = 0;
+    __syncthreads();
+
+    // histogram and id checks
+    int bad = 0;
+    for (int a = tid; a < N; a += kFusedThreads) {
+        const int32_t e = ids[a];
+        const int j = a % k;
+        for (int jj = 1; jj <= j; ++jj)
+            if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
+        if (e < 0 || e >= E) {
+            bad |= MOE_ERR_RANGE;
+            continue;
+        }
+        atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+
+    // inclusive Hillis-Steele scan of the 256 counts
+    if (tid < 256) sc[tid] = tid < E ? hist[tid] : 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int32_t v = (tid < 256 && tid >= off) ? sc[tid - off] : 0;
+        __syncthreads();
+        if (tid < 256) sc[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        counts[tid] = hist[tid];
+        offsets[tid + 1] = sc[tid];
+        base[tid] = 0;  // eidx counts within the expert
+    }
+    if (tid == 0) offsets[0] = 0;
+    if (tid < R) {
+        const int n = E / R;
+        rank_load[tid] = sc[(tid + 1) * n - 1] - (tid > 0 ? sc[tid * n - 1] : 0);
+    }
+    __syncthreads();
+
+    // stable within-expert index, 1024 assignments a round (as in the rank
+    // kernel: a ballot multisplit per wavefront, then the wavefront prefix)
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r0 = 0; r0 < N; r0 += kFusedThreads) {
+        const int a = r0 + tid;
+        const bool valid = a < N;
+        const int32_t e = valid ? ids[a] : -1;
+        const bool ok = valid && e >= 0 && e < E;
+        uint64_t match = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = ok && ((e >> b) & 1);
+            const uint64_t bal = __ballot(bit);
+            match &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(match & lt_mask);
+        if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
+        __syncthreads();
+        if (ok) {
+            int32_t pre = base[e];
+            for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+            eidx[a] = pre + rank;
+        } else if (valid) {
+            eidx[a] = -1;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int32_t sum = 0;
+#pragma unroll
+            for (int w = 0; w < kFusedWaves; ++w) {
+                sum += wcnt[w][tid];
+                wcnt[w][tid] = 0;
+            }
+            base[tid] += sum;
+        }
+        __syncthreads();
+    }
+    if (bad) atomicOr(err, bad);
+}
+
 }  // namespace
 
 hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
@@ -155,6 +258,11 @@ hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* c
     int32_t* blk_hist = reinterpret_cast<int32_t*>(ws + L.blk_hist);
     int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
     const int B = L.count_blocks;
+    if (N <= kFusedMax) {
+        count_fused_kernel<<<1, kFusedThreads, 0, st>>>((int)N, s.k, s.E, s.R, ids, counts, offsets,
+                                                         eidx, rank_load, err);
+        return hipGetLastError();
+    }
     if (B > 0) {
         count_hist_kernel<<<B, kThreads, 0, st>>>((int)N, s.k, s.E, ids, blk_hist, err);
         hipError_t e = hipGetLastError();
