@@ -612,20 +612,21 @@ struct Skinny {
     static constexpr int kSchedOff = SKM == 32 ? 2 : 3;       // tile_start prefix (x (E+1))
 };
 
+// the SKM-row tiles of one launch (a phase of the skinny kernel below);
+// ring, rowmap and ssched are the kernel's LDS, shared by its phases
 template <int MODE, int SKM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
+__device__ __forceinline__ void skinny_phase(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out)
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
+    char* ring, int32_t* rowmap, int32_t* ssched)
 {
     using SK = Skinny<SKM>;
     constexpr int kSkM = SKM, kSkSlots = SK::kSlots, kSkA = SK::kA, kSkSlot = SK::kSlot;
     constexpr int kSkPerStage = SK::kPerStage, kNB = SK::kBlocks;
-    __shared__ __attribute__((aligned(1024))) char ring[kSkSlots * kSkSlot];
-    __shared__ int32_t rowmap[kSkM];
-    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // skinny tile_start[G+1], row_start[G+1]
 
+    __syncthreads();  // the previous phase is done with ssched
     for (int i = threadIdx.x; i < G + 1; i += kThreads) {
         ssched[i] = sched[SK::kSchedOff * (G + 1) + i];
         ssched[G + 1 + i] = sched[G + 1 + i];
@@ -774,6 +775,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
         wait_vm_lgkm<63>();
         slot_barrier();
     }
+}
+
+// Both skinny tile sizes in one launch: the 32-row tiles, then the 64-row.
+constexpr int kSkinnyRing = Skinny<32>::kSlots * Skinny<32>::kSlot > Skinny<64>::kSlots * Skinny<64>::kSlot
+                                ? Skinny<32>::kSlots * Skinny<32>::kSlot
+                                : Skinny<64>::kSlots * Skinny<64>::kSlot;
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
+    int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
+    const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out)
+{
+    __shared__ __attribute__((aligned(1024))) char ring[kSkinnyRing];
+    __shared__ int32_t rowmap[64];
+    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // skinny tile_start[G+1], row_start[G+1]
+    skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring,
+                           rowmap, ssched);
+    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring,
+                           rowmap, ssched);
 }
 
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
@@ -1033,10 +1055,8 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const uint16_t* av = static_cast<const uint16_t*>(a);
         const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
         const uint16_t* wu = static_cast<const uint16_t*>(w_up);
-        gemm_skinny_kernel<kGateUp, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
-                                                                 wg, wu, g.wtab, h, gu_out);
-        gemm_skinny_kernel<kGateUp, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow,
-                                                                 wg, wu, g.wtab, h, gu_out);
+        gemm_skinny_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
+                                                             wu, g.wtab, h, gu_out);
         gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
                                                            wu, g.wtab, h, part, gu_out);
         hipError_t e = hipGetLastError();
@@ -1068,10 +1088,8 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
         const uint16_t* hv = reinterpret_cast<const uint16_t*>(ws + W.h);
         const uint16_t* wd = static_cast<const uint16_t*>(w_down);
         uint16_t* yv = static_cast<uint16_t*>(y);
-        gemm_skinny_kernel<kDown, 32><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                               nullptr, g.wtab, yv, nullptr);
-        gemm_skinny_kernel<kDown, 64><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                               nullptr, g.wtab, yv, nullptr);
+        gemm_skinny_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
+                                                           nullptr, g.wtab, yv, nullptr);
         gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
                                                          nullptr, g.wtab, yv, part, nullptr);
         hipError_t e = hipGetLastError();
