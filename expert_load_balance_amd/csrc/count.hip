@@ -66,10 +66,17 @@ __global__ __launch_bounds__(kThreads) void count_scan_kernel(int B, int E, int 
     const int e = threadIdx.x;
     int32_t run = 0;
     if (e < E) {
-        for (int b = 0; b < B; ++b) {
-            const int32_t h = blk_hist[(size_t)b * E + e];
-            blk_base[(size_t)b * E + e] = run;
-            run += h;
+        // 16 loads in flight at a time, then their running sum
+        for (int b0 = 0; b0 < B; b0 += 16) {
+            int32_t h[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) h[j] = b0 + j < B ? blk_hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (b0 + j >= B) break;
+                blk_base[(size_t)(b0 + j) * E + e] = run;
+                run += h[j];
+            }
         }
         counts[e] = run;
     }
