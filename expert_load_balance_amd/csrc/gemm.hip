@@ -175,7 +175,9 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 // Persistent kernel, one 256-thread workgroup per CU. Workgroup tile: 256
 // rows x 256 B-rows (gate/up: 128 F-columns of gate and the same 128 of up;
 // down: 256 output columns); K in 64-deep stages.
-//  * LDS holds two stage slots (A 32 KB + B 32 KB each). A slot row is 128
+//  * LDS holds a ring of operand slots of 32 KB: two for A, three for B, so
+//    the weights (from HBM, unlike the activation rows every N-tile of an
+//    expert shares in L2) are copied two stages ahead. A slot row is 128
 //    bytes, one full L1/L2 line of the source row, so every line is fetched
 //    once. K-chunk c of row r sits in slot c ^ swz(r), which keeps the MFMA
 //    fragment reads (32 consecutive rows, one chunk each) free of bank
@@ -189,11 +191,11 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 //    Operands are swapped so a lane holds 4 consecutive output columns: the
 //    epilogue stores 8 bytes per lane straight to global memory.
 //  * Stage s, hand-scheduled over its 4 k-steps of 16 MFMAs: the fragments
-//    of all four k-steps are read from the slot during k-steps 0 and 1; one
-//    workgroup barrier follows (the slot is then free, and the other slot,
-//    stage s+1, has landed: each wave waits for its own copies first); the
-//    refill of the slot with stage s+2 and the first fragments of stage s+1
-//    are spread over k-steps 2 and 3.
+//    of all four k-steps are read from its slots during k-steps 0 and 1; one
+//    workgroup barrier follows (the slots are then free, and stage s+1 has
+//    landed: each wave waits for its own copies first); the copies of A of
+//    stage s+2 and B of stage s+3 into the freed slots and the first
+//    fragments of stage s+1 are spread over k-steps 2 and 3.
 //  * The next tile's first two stages are issued right after the last
 //    stage's barrier, ahead of this tile's epilogue, whose arithmetic and
 //    stores then hide their latency.
@@ -208,8 +210,8 @@ __device__ __forceinline__ int buf_row_of(int e, int v, int R, const int32_t* pl
 //    another.
 constexpr int kTM = moe::kGemmTile, kTN = moe::kGemmTile, kTK = moe::kGemmStageK;
 constexpr int kOpBytes = kTM * kTK * 2;           // 32 KB: one operand of one stage
-constexpr int kSlotBytes = 2 * kOpBytes;          // A, then B
 constexpr int kCopiesWave = kOpBytes / 1024 / 4;  // 8 copies per operand per wave
+constexpr int kASlots = 2, kBSlots = 3;           // LDS ring: 5 x 32 KB = 160 KB
 enum { kGateUp = 0, kDown = 1 };
 
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (both about
@@ -229,29 +231,29 @@ __device__ __forceinline__ float fast_silu(float z)
 __host__ __device__ constexpr int read_order(int n) { return n == 0 ? 0 : n <= 4 ? n + 3 : n - 4; }
 
 // Tile t of the launch (expert-major, then N-tile, then M-tile) from the
-// schedule (tile_start[E+1], row_start[E+1]).
+// schedule (tile_start[E+1], row_start[E+1]); sc(i) reads its entry i.
 struct TileRef {
     int e, n0, rows, hrow0;
 };
-template <int MODE>
-__device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, const int32_t* sc)
+template <int MODE, typename SC>
+__device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
 {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (sc[mid] * ntiles_n <= t) lo = mid;
+        if (sc(mid) * ntiles_n <= t) lo = mid;
         else hi = mid - 1;
     }
-    const int mt_e = sc[lo + 1] - sc[lo];
-    const int local = t - sc[lo] * ntiles_n;
+    const int mt_e = sc(lo + 1) - sc(lo);
+    const int local = t - sc(lo) * ntiles_n;
     const int nt = local / mt_e, mt = local % mt_e;
-    const int c_e = sc[E + 1 + lo + 1] - sc[E + 1 + lo];
+    const int c_e = sc(E + 1 + lo + 1) - sc(E + 1 + lo);
     const int v0 = mt * kTM;
     TileRef r;
     r.e = lo;
     r.n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
     r.rows = min(kTM, c_e - v0);
-    r.hrow0 = sc[E + 1 + lo] + v0;
+    r.hrow0 = sc(E + 1 + lo) + v0;
     return r;
 }
 
@@ -319,16 +321,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, float* __restrict__ part,
     uint16_t* __restrict__ gu_out)
 {
-    __shared__ __attribute__((aligned(1024))) char slots[2 * kSlotBytes];
-    __shared__ int32_t rowmap[2][kTM];
-    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // tile_start[G+1], row_start[G+1]
+    // the whole LDS: A slots 0, 1, then B slots 0, 1, 2
+    __shared__ __attribute__((aligned(1024))) char slots[(kASlots + kBSlots) * kOpBytes];
+    auto sc = [&](int i) { return ldc(sched, i); };
 
-    for (int i = threadIdx.x; i < 2 * (G + 1); i += kThreads) ssched[i] = sched[i];
-    __syncthreads();
     const int K = MODE == kGateUp ? H : F;
     const int KT_all = K / kTK;
     const int P = gridDim.x;
-    const Balance bal = balance_of(ssched[G] * ntiles_n, P, KT_all);
+    const Balance bal = balance_of(sc(G) * ntiles_n, P, KT_all);
     const int total = bal.full + bal.L * bal.S;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             k0 = kp * bal.KTp;
             KT = min(KT_all - k0, bal.KTp);
         }
-        const TileRef r = tile_of<MODE>(t, G, ntiles_n, ssched);
+        const TileRef r = tile_of<MODE>(t, G, ntiles_n, sc);
         Unit u;
         u.e = uni(r.e);
         u.n0 = uni(r.n0);
@@ -370,12 +370,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         return u;
     };
 
+    // Rows a lane needs from vrow, per unit: gate/up, the activation row of
+    // each of its copies (slot row 8 (wave + 4 i) + lane / 8); down, the
+    // output row of each of its accumulator blocks i (tile row
+    // wm * 128 + 32 i + lane % 32). Rows past the unit's end read row 0's.
+    constexpr int kRowLoads = MODE == kGateUp ? kCopiesWave : 4;
+    auto load_rows = [&](const Unit& u, int* rw) {
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) {
+            const int r = MODE == kGateUp ? 8 * (wave + 4 * i) + (lane >> 3) : wm * 128 + 32 * i + fr;
+            rw[i] = vrow[u.hrow0 + (r < u.rows ? r : 0)];
+        }
+    };
+
     // per-unit copy sources: uniform bases + per-lane 32-bit offsets. Copy
     // instruction q (0..31) of an operand fills slot rows 8q .. 8q+7; wave w
     // issues q = w + 4 i; lane l takes row 8q + l/8, slot chunk l % 8.
     const char *abase = nullptr, *bbase0 = nullptr, *bbase1 = nullptr;
     uint32_t aoff[kCopiesWave], boff[kCopiesWave];
-    auto setup = [&](const Unit& u, const int32_t* rmap) {
+    auto setup = [&](const Unit& u, const int* rw) {
         if (MODE == kGateUp) {
             abase = uni_ptr(reinterpret_cast<const char*>(a_src + u.kofs));
             bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, u.e, 0, F, H) + u.kofs));
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             const int r = 8 * (wave + 4 * i) + (lane >> 3);
             const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
             if (MODE == kGateUp) {
-                aoff[i] = (uint32_t)rmap[r] * (uint32_t)H * 2u + ch;
+                aoff[i] = (uint32_t)rw[i] * (uint32_t)H * 2u + ch;
                 boff[i] = (uint32_t)min(u.n0 + (r & 127), F - 1) * (uint32_t)H * 2u + ch;
             } else {
                 aoff[i] = (uint32_t)min(r, u.rows - 1) * (uint32_t)F * 2u + ch;
@@ -398,15 +411,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             }
         }
     };
-    // copies of stage st into slot st % 2 (gate/up: B instructions q < 16,
-    // i.e. i < 4, hold gate rows)
+    // LDS byte offsets of stage st's A and B operands
+    auto a_slot = [](int st) { return (uint32_t)(st & 1) * kOpBytes; };
+    auto b_slot = [](int st) { return (uint32_t)(kASlots + st % kBSlots) * kOpBytes; };
+    // copies of stage st (gate/up: B instructions q < 16, i.e. i < 4, hold
+    // gate rows)
     auto copy_a = [&](int st, int i) {
-        copy16(abase + st * (kTK * 2), aoff[i], slots_u + (st & 1) * kSlotBytes + wave * 1024 + i * 4096);
+        copy16(abase + st * (kTK * 2), aoff[i], slots_u + a_slot(st) + wave * 1024 + i * 4096);
     };
     auto copy_b = [&](int st, int i) {
         copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
-               slots_u + (st & 1) * kSlotBytes + kOpBytes + wave * 1024 + i * 4096);
+               slots_u + b_slot(st) + wave * 1024 + i * 4096);
     };
+    // A and B of stages 0 and 1, then B of stage 2 (in this order: the waits
+    // below count the copies issued after the ones they wait for)
     auto prologue = [&](const Unit& u) {
         for (int st = 0; st < 2 && st < u.KT; ++st) {
 #pragma unroll
@@ -414,18 +432,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < kCopiesWave; ++i) copy_b(st, i);
         }
+        if (u.KT > 2) {
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i) copy_b(2, i);
+        }
     };
 
     f32x16 acc[4][4];
     bf16x8 af[4][4], bf[4][4];
     // fragment id (0..3 A block, 4..7 B block) of k-step kk of stage st
     auto read = [&](int st, int kk, int id) {
-        const char* base = slots + (st & 1) * kSlotBytes;
         if (id < 4) {
-            af[kk][id] = lds_frag(base + fa[kk] + id * 4096);
+            af[kk][id] = lds_frag(slots + a_slot(st) + fa[kk] + id * 4096);
         } else {
             const int j = id - 4;
-            bf[kk][j] = lds_frag(base + kOpBytes + fb[kk] +
+            bf[kk][j] = lds_frag(slots + b_slot(st) + fb[kk] +
                                  (MODE == kGateUp ? (j >> 1) * 16384 + (j & 1) * 4096 : j * 4096));
         }
     };
@@ -435,10 +456,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     };
 
     // k-steps 0 and 1 of stage s: MFMAs interleaved with the reads of sets
-    // 1, 2, 3; then the wait for this wave's copies of stage s+1 and the
+    // 1, 2, 3; then the wait for this wave's copies of stage s+1 (WAIT: the
+    // copies issued after them, B of stage s+2 when it exists) and the
     // barrier. Reads: n-th read of k-step kk covers set-read index
     // 12 kk + n over the sequence (set 1: 8 reads, set 2: 8, set 3: 8).
-    auto first_half = [&](int s) {
+    auto first_half = [&](auto wait_tag, int s) {
+        constexpr int WAIT = decltype(wait_tag)::value;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             int n = 0;
@@ -452,13 +475,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        wait_vm_lgkm<0>();
+        wait_vm_lgkm<WAIT>();
         slot_barrier();
     };
-    // k-steps 2 and 3 of stage s: COPY refills the slot with stage s+2;
-    // NEXT reads set 0 of stage s+1.
-    auto second_half = [&](auto copy_tag, auto next_tag, int s) {
-        constexpr bool COPY = decltype(copy_tag)::value;
+    // k-steps 2 and 3 of stage s: stage s's slots are free; CA copies A of
+    // stage s+2 into its A slot, CB B of stage s+3 into its B slot; NEXT
+    // reads set 0 of stage s+1.
+    auto second_half = [&](auto ca_tag, auto cb_tag, auto next_tag, int s) {
+        constexpr bool CA = decltype(ca_tag)::value;
+        constexpr bool CB = decltype(cb_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
 #pragma unroll
         for (int kk = 2; kk < 4; ++kk) {
@@ -466,9 +491,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             for (int m = 0; m < 16; ++m) {
                 mfma(kk, m);
                 if (NEXT && (m & 3) == 0) read(s + 1, 0, read_order(4 * (kk - 2) + (m >> 2)));
-                if (COPY && (m & 1)) {
-                    if (kk == 2) copy_a(s + 2, m >> 1);
-                    else copy_b(s + 2, m >> 1);
+                if (m & 1) {
+                    if (kk == 2 && CA) copy_a(s + 2, m >> 1);
+                    if (kk == 3 && CB) copy_b(s + 3, m >> 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -476,25 +501,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     };
     using Yes = std::true_type;
     using No = std::false_type;
+    using W0 = std::integral_constant<int, 0>;
+    using W8 = std::integral_constant<int, kCopiesWave>;
 
     int Lu = my_slot;
     if (Lu >= total) return;
     Unit u = decode(Lu);
-    int par = 0;
-    rowmap[0][tid] = vrow[u.hrow0 + (tid < u.rows ? tid : 0)];
-    __syncthreads();
-    setup(u, rowmap[0]);
+    int rw[kRowLoads];
+    load_rows(u, rw);
+    setup(u, rw);
     prologue(u);
 
     for (;;) {
-        // next unit and its rows (read now, used at the end of this unit)
+        // next unit and its rows (read now, used at the end of this unit;
+        // these loads go out after this unit's first copies)
         const int Ln = Lu + P;
         const bool has_next = Ln < total;
         Unit un = u;
-        int nrow = 0;
+        int nrw[kRowLoads];
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) nrw[i] = 0;
         if (has_next) {
             un = decode(Ln);
-            nrow = vrow[un.hrow0 + (tid < un.rows ? tid : 0)];
+            load_rows(un, nrw);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -502,34 +531,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-        // stage 0 landed (stage 1's copies, if any, were issued after it)
-        if (u.KT >= 2) wait_vm_lgkm<2 * kCopiesWave>();
-        else wait_vm_lgkm<0>();
+        // stage 0 landed: the copies of stages 1 and 2 (and, with a next
+        // unit, its row loads) were issued after it
+        if (has_next) {
+            if (u.KT >= 3) wait_vm_lgkm<3 * kCopiesWave + kRowLoads>();
+            else if (u.KT == 2) wait_vm_lgkm<2 * kCopiesWave + kRowLoads>();
+            else wait_vm_lgkm<kRowLoads>();
+        } else {
+            if (u.KT >= 3) wait_vm_lgkm<3 * kCopiesWave>();
+            else if (u.KT == 2) wait_vm_lgkm<2 * kCopiesWave>();
+            else wait_vm_lgkm<0>();
+        }
         slot_barrier();
 #pragma unroll
         for (int n = 0; n < 8; ++n) read(0, 0, read_order(n));
 
         int s = 0;
-        for (; s + 2 < u.KT; ++s) {
-            first_half(s);
-            second_half(Yes{}, Yes{}, s);
+        for (; s + 3 < u.KT; ++s) {
+            first_half(W8{}, s);
+            second_half(Yes{}, Yes{}, Yes{}, s);
         }
-        if (s + 1 < u.KT) {
-            first_half(s);
-            second_half(No{}, Yes{}, s);
+        if (s + 2 < u.KT) {
+            first_half(W8{}, s);
+            second_half(Yes{}, No{}, Yes{}, s);
             ++s;
         }
-        // last stage: after its barrier both slots are free, so the next
-        // unit's first stages go out before this unit's last MFMAs
-        first_half(s);
+        if (s + 1 < u.KT) {
+            first_half(W0{}, s);
+            second_half(No{}, No{}, Yes{}, s);
+            ++s;
+        }
+        // last stage: after its barrier every slot is free, so the next
+        // unit's first stages go out before this unit's last MFMAs. Its row
+        // loads completed with the wait above; the empty asm keeps their
+        // first use here, where no copy is in flight to wait for.
+        first_half(W0{}, s);
         if (has_next) {
-            rowmap[par ^ 1][tid] = nrow;
-            wait_vm_lgkm<63>();
-            slot_barrier();
-            setup(un, rowmap[par ^ 1]);
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i) asm volatile("" : "+v"(nrw[i]));
+            setup(un, nrw);
             prologue(un);
         }
-        second_half(No{}, No{}, s);
+        second_half(No{}, No{}, No{}, s);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
         // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
@@ -570,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
                             store_gu(gu_out, u.hrow0 + row, F, col, acc[i][j], acc[i][j + 2], g4);
                     }
             } else {
-                uint16_t* dst = out + (size_t)rowmap[par][row] * H;
+                uint16_t* dst = out + (size_t)rw[i] * H;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -587,7 +630,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         if (!has_next) break;
         Lu = Ln;
         u = un;
-        par ^= 1;
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) rw[i] = nrw[i];
     }
 }
 
@@ -656,7 +700,7 @@ __device__ __forceinline__ void skinny_phase(
     constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
 
     for (int Lu = my_slot; Lu < total; Lu += P) {
-        const TileRef r0 = tile_of<MODE>(Lu, G, ntiles_n, ssched);
+        const TileRef r0 = tile_of<MODE>(Lu, G, ntiles_n, [&](int i) { return ssched[i]; });
         const int e = uni(r0.e), n0 = uni(r0.n0), rows = uni(r0.rows), hrow0 = uni(r0.hrow0);
         if (tid < kSkM) rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : rows - 1)];
         wait_vm_lgkm<63>();
@@ -818,7 +862,7 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
     const Balance bal = balance_of(sched[G] * ntiles_n, P, KT_all);
     const int lt = blockIdx.x / kFixupSlabs;
     if (bal.S == 1 || lt >= bal.L) return;
-    const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, sched);
+    const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, [&](int i) { return sched[i]; });
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
     constexpr int kRowsPerPass = kThreads / kQuads;
     const int c = (threadIdx.x % kQuads) * 4;

@@ -127,15 +127,6 @@ struct WTile {
     int e, out, hrow0, rows, ns, m0, n0;
 };
 
-// A uniform read of a table no kernel writes while this one runs, as a scalar
-// load: a vector load would make the compiler wait for every vector memory
-// operation in flight (the loader's copies, the compute waves' stores).
-__device__ __forceinline__ int ldc(const int32_t* p, int i)
-{
-    typedef const __attribute__((address_space(4))) int32_t cint;
-    return ((cint*)p)[i];
-}
-
 // tile u of the weight-gradient stream: group (home expert, or a row range of
 // one in replica mode), then its M x N tiles
 __device__ __forceinline__ WTile wtile(const BwdArgs& a, int u, int mtw, int ntw)

@@ -66,6 +66,15 @@ __device__ __forceinline__ void slot_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// A uniform read of a table no kernel writes while this one runs, as a scalar
+// load: a vector load would make the compiler wait for every vector memory
+// operation in flight (copies, stores) before its first use.
+__device__ __forceinline__ int ldc(const int32_t* p, int i)
+{
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    return ((cint*)p)[i];
+}
+
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 template <typename T>
 __device__ __forceinline__ T* uni_ptr(T* p)
