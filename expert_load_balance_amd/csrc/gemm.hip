@@ -411,9 +411,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             }
         }
     };
-    // LDS byte offsets of stage st's A and B operands
-    auto a_slot = [](int st) { return (uint32_t)(st & 1) * kOpBytes; };
-    auto b_slot = [](int st) { return (uint32_t)(kASlots + st % kBSlots) * kOpBytes; };
+    // LDS byte offsets of stage st's A and B operands. zo is zero, set by an
+    // opaque move at the top of every unit: offsets of fixed stages (the
+    // prologue's, the first reads) are then computed where they are used,
+    // not hoisted out of the unit loop to hold registers across it.
+    uint32_t zo = 0;
+    auto a_slot = [&](int st) { return zo + (uint32_t)(st & 1) * kOpBytes; };
+    auto b_slot = [&](int st) { return zo + (uint32_t)(kASlots + st % kBSlots) * kOpBytes; };
     // copies of stage st (gate/up: B instructions q < 16, i.e. i < 4, hold
     // gate rows)
     auto copy_a = [&](int st, int i) {
@@ -423,14 +427,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
                slots_u + b_slot(st) + wave * 1024 + i * 4096);
     };
-    // A and B of stages 0 and 1, then B of stage 2 (in this order: the waits
-    // below count the copies issued after the ones they wait for)
-    auto prologue = [&](const Unit& u) {
-        for (int st = 0; st < 2 && st < u.KT; ++st) {
+    // A and B of stage 0 (head), then of stage 1 and B of stage 2 (tail), in
+    // this order: the waits below count the copies issued after the ones
+    // they wait for. Between the two a finished tile can be staged in the
+    // slots the tail fills.
+    auto prologue_head = [&]() {
 #pragma unroll
-            for (int i = 0; i < kCopiesWave; ++i) copy_a(st, i);
+        for (int i = 0; i < kCopiesWave; ++i) copy_a(0, i);
 #pragma unroll
-            for (int i = 0; i < kCopiesWave; ++i) copy_b(st, i);
+        for (int i = 0; i < kCopiesWave; ++i) copy_b(0, i);
+    };
+    auto prologue_tail = [&](const Unit& u) {
+        if (u.KT > 1) {
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i) copy_a(1, i);
+#pragma unroll
+            for (int i = 0; i < kCopiesWave; ++i) copy_b(1, i);
         }
         if (u.KT > 2) {
 #pragma unroll
@@ -504,19 +516,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     using W0 = std::integral_constant<int, 0>;
     using W8 = std::integral_constant<int, kCopiesWave>;
 
-    int Lu = my_slot;
-    if (Lu >= total) return;
+    // The whole tiles, then the K-parts of split tiles, in two loops of their
+    // own (each with its epilogue: one loop holding both would not fit its
+    // registers). Workgroup p takes units p, p + P, ... of each range.
+    auto run = [&](auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    const int end = SPLIT ? total : bal.full;
+    int Lu = (SPLIT ? bal.full : 0) + my_slot;
+    if (Lu >= end) return;
     Unit u = decode(Lu);
     int rw[kRowLoads];
     load_rows(u, rw);
     setup(u, rw);
-    prologue(u);
+    prologue_head();
+    prologue_tail(u);
 
     for (;;) {
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zo));
         // next unit and its rows (read now, used at the end of this unit;
         // these loads go out after this unit's first copies)
         const int Ln = Lu + P;
-        const bool has_next = Ln < total;
+        const bool has_next = Ln < end;
         Unit un = u;
         int nrw[kRowLoads];
 #pragma unroll
@@ -562,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             ++s;
         }
         // last stage: after its barrier every slot is free, so the next
-        // unit's first stages go out before this unit's last MFMAs. Its row
+        // unit's first stage goes out before this unit's last MFMAs. Its row
         // loads completed with the wait above; the empty asm keeps their
         // first use here, where no copy is in flight to wait for.
         first_half(W0{}, s);
@@ -570,69 +590,137 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < kRowLoads; ++i) asm volatile("" : "+v"(nrw[i]));
             setup(un, nrw);
-            prologue(un);
+            prologue_head();
         }
         second_half(No{}, No{}, No{}, s);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
-        // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3: 8-byte stores.
+        // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3.
+        // The finished tile is staged in B slots 1 and 2 (64 KB at a time),
+        // then stored as whole 128-byte lines. A staged row's 16-byte unit c
+        // sits at unit c ^ (row % 16 or 32), which spreads both the writes (32
+        // rows, one unit) and the 16-byte reads (one row) over every bank.
+        char* stg = slots + (kASlots + 1) * kOpBytes;
+        // the lane index through an opaque copy, so that the epilogue's
+        // per-lane offsets are computed here, not hoisted out of the unit
+        // loop where they would stay live across the K loop
+        int ln, wv;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        asm volatile("s_mov_b32 %0, %1" : "=s"(wv) : "s"(wave));
+        const int er = ln & 31, eh = ln >> 5, ewm = wv >> 1, ewn = wv & 1;
+        if constexpr (!SPLIT) {
+            // whole tile (the down tile in two halves of 128 rows)
+            if (MODE == kGateUp) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + i * 32 + fr;
-            if (row >= u.rows) continue;
-            if (u.pidx >= 0) {
-                // fp32 partial tile [row][B-row], summed by fixup_kernel
-                float* dst = part + ((size_t)u.pidx * kTM + row) * kTN;
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ewm * 128 + i * 32 + er;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int bc = (MODE == kGateUp ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32
-                                                        : wn * 128 + j * 32) + g4 * 8 + fh * 4;
-                        *reinterpret_cast<float4*>(dst + bc) =
-                            make_float4(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1],
-                                        acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
-                    }
-            } else if (MODE == kGateUp) {
-                uint16_t* dst = out + (size_t)(u.hrow0 + row) * F;
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            float hv[4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                            for (int q = 0; q < 4; ++q)
+                                hv[q] = fast_silu(acc[i][j][g4 * 4 + q]) * acc[i][j + 2][g4 * 4 + q];
+                            uint2 pk;
+                            pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                            pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                            const int c = ewn * 8 + j * 4 + g4;
+                            *reinterpret_cast<uint2*>(stg + row * 256 + ((c ^ (row & 15)) << 4) + eh * 8) = pk;
+                            const int col = u.n0 + c * 8 + eh * 4;
+                            if (gu_out && row < u.rows && col < F)  // training: keep g | u
+                                store_gu(gu_out, u.hrow0 + row, F, col, acc[i][j], acc[i][j + 2], g4);
+                        }
+                }
+                wait_vm_lgkm<63>();
+                slot_barrier();
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = u.n0 + wn * 64 + j * 32 + g4 * 8 + fh * 4;
-                        if (col >= F) continue;
-                        float hv[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            hv[q] = fast_silu(acc[i][j][g4 * 4 + q]) * acc[i][j + 2][g4 * 4 + q];
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
-                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
-                        *reinterpret_cast<uint2*>(dst + col) = pk;
-                        if (gu_out)  // training: keep g | u for the backward
-                            store_gu(gu_out, u.hrow0 + row, F, col, acc[i][j], acc[i][j + 2], g4);
-                    }
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 4 * (4 * q + wv) + (ln >> 4), c = ln & 15;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+                    const int col = u.n0 + c * 8;
+                    if (row < u.rows && col < F)
+                        *reinterpret_cast<u32x4*>(out + (size_t)(u.hrow0 + row) * F + col) = v;
+                }
+                wait_vm_lgkm<63>();
+                slot_barrier();
             } else {
-                uint16_t* dst = out + (size_t)rw[i] * H;
+                // output rows of the staged half, in A slot 1
+                int32_t* orows = reinterpret_cast<int32_t*>(slots + kOpBytes);
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * p + ii, lr = ewm * 64 + ii * 32 + er;
+                        if (eh == 0) orows[lr] = rw[i];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                uint2 pk;
+                                pk.x = moe::pack_bf16x2(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1]);
+                                pk.y = moe::pack_bf16x2(acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
+                                const int c = ewn * 16 + j * 4 + g4;
+                                *reinterpret_cast<uint2*>(stg + lr * 512 + ((c ^ (lr & 31)) << 4) + eh * 8) = pk;
+                            }
+                    }
+                    wait_vm_lgkm<63>();
+                    slot_barrier();
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int lr = 2 * (4 * q + wv) + (ln >> 5), c = ln & 31;
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + lr * 512 + ((c ^ (lr & 31)) << 4));
+                        const int row = (lr >> 6) * 128 + (2 * p + ((lr >> 5) & 1)) * 32 + (lr & 31);
+                        const int col = u.n0 + c * 8;
+                        if (row < u.rows && col < H)
+                            *reinterpret_cast<u32x4*>(out + (size_t)orows[lr] * H + col) = v;
+                    }
+                    wait_vm_lgkm<63>();
+                    slot_barrier();
+                }
+            }
+        } else {
+            // K-part of a split tile: the fp32 partial tile [row][B-row] that
+            // fixup_kernel sums, staged 64 rows (64 KB) at a time and stored
+            // as whole rows; its padding rows are stored too (fixup reads
+            // only the tile's rows)
+            float* dst = part + (size_t)u.pidx * kTM * kTN;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int lr = ewm * 32 + er;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = u.n0 + wn * 128 + j * 32 + g4 * 8 + fh * 4;
-                        if (col >= H) continue;
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1]);
-                        pk.y = moe::pack_bf16x2(acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]);
-                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                        const int c = ((MODE == kGateUp ? (j >> 1) * 128 + ewn * 64 + (j & 1) * 32
+                                                        : ewn * 128 + j * 32) + g4 * 8) / 4 + eh;
+                        *reinterpret_cast<float4*>(stg + lr * 1024 + ((c ^ (lr & 15)) << 4)) =
+                            make_float4(acc[p][j][g4 * 4 + 0], acc[p][j][g4 * 4 + 1],
+                                        acc[p][j][g4 * 4 + 2], acc[p][j][g4 * 4 + 3]);
                     }
+                wait_vm_lgkm<63>();
+                slot_barrier();
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = 4 * q + wv;
+                    const float4 v = *reinterpret_cast<const float4*>(stg + r * 1024 + ((ln ^ (r & 15)) << 4));
+                    const int row = (r >> 5) * 128 + p * 32 + (r & 31);
+                    *reinterpret_cast<float4*>(dst + (size_t)row * kTN + ln * 4) = v;
+                }
+                wait_vm_lgkm<63>();
+                slot_barrier();
             }
         }
+        if (has_next) prologue_tail(un);
         if (!has_next) break;
         Lu = Ln;
         u = un;
 #pragma unroll
         for (int i = 0; i < kRowLoads; ++i) rw[i] = nrw[i];
     }
+    };
+    run(No{});
+    run(Yes{});
 }
 
 // ------------------------------------------------------- bf16, skinny ----
