@@ -20,7 +20,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Assignment (t,j) -> destination row; -1 if the inputs are out of range.
+// Assignment (e, v) -> destination row: it lands in the piece of expert e
+// whose running count range holds v, at that piece's row + (v - rows before
+// it); -1 if the inputs are out of range. One lane walks the pieces.
 __device__ __forceinline__ int dest_of(int e, int v, int E, int R, int N, const int32_t* plan,
                                        const moe::PlanLayout& L)
 {
@@ -38,6 +40,60 @@ __device__ __forceinline__ int dest_of(int e, int v, int E, int R, int N, const 
         cum += c;
     }
     return -1;
+}
+
+// Destination rows of token t's k assignments; lane j < k returns
+// assignment j's row. When the k experts' pieces fit one wavefront (k * G <=
+// 64, G = R rounded up to a power of two), lane j * G + p reads piece p of
+// assignment j's expert, all pieces at once: one round trip to memory after
+// the ids instead of one per piece; a prefix sum over the group's lanes
+// gives the ranges and a ballot the matching piece. Otherwise each lane
+// j < k walks its expert's pieces (measured faster than several passes of
+// the wavefront-wide lookup).
+__device__ __forceinline__ int resolve_dests(int t, int k, int E, int R, int N,
+                                             const int32_t* __restrict__ ids,
+                                             const int32_t* __restrict__ eidx,
+                                             const int32_t* __restrict__ plan)
+{
+    const int lane = threadIdx.x & 63;
+    int e = -1, v = -1;
+    if (lane < k) {
+        e = ids[t * k + lane];
+        v = eidx[t * k + lane];
+    }
+    const moe::PlanLayout L = moe::plan_layout(E, R);
+    const int G = R <= 1 ? 1 : 1 << (32 - __builtin_clz(R - 1));
+    if (k * G > 64) return lane < k ? dest_of(e, v, E, R, N, plan, L) : -1;
+    const int j = lane / G, p = lane % G;
+    int d = -1;
+    {
+        const int ej = __shfl(e, j < k ? j : 0), vj = __shfl(v, j < k ? j : 0);
+        const bool ok = j < k && ej >= 0 && ej < E && vj >= 0 && p < R;
+        int np = 0, c = 0, r = 0;
+        if (ok) {
+            np = plan[L.piece_num + ej];
+            c = plan[L.piece_cnt + (size_t)ej * R + p];
+            r = plan[L.piece_row + (size_t)ej * R + p];
+        }
+        if (p >= np) c = 0;
+        int s = c;
+        for (int off = 1; off < G; off <<= 1) {
+            const int y = __shfl_up(s, off, G);
+            if (p >= off) s += y;
+        }
+        const int before = s - c;
+        const bool hit = ok && p < np && vj >= before && vj < s;
+        const int row = r + (vj - before);
+        const uint64_t m = __ballot(hit);
+        for (int jj = 0; jj < k; ++jj) {
+            const uint64_t gm = (m >> (jj * G)) & (G == 64 ? ~0ull : ((1ull << G) - 1));
+            if (gm == 0) continue;
+            const int src = jj * G + __ffsll((unsigned long long)gm) - 1;
+            const int dj = __builtin_amdgcn_readlane(row, src);
+            if (lane == jj) d = (dj >= 0 && dj < N) ? dj : -1;
+        }
+    }
+    return d;
 }
 
 // Work split: one wavefront per (token, row chunk); a chunk is 64 lanes x VPL
@@ -73,15 +129,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(int T, int k, int E, 
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (c0 + 64 * i < row_vecs) v[i] = src[c0 + 64 * i];
-    int d = -1;
-    if (lane < k) {
-        const moe::PlanLayout L = moe::plan_layout(E, R);
-        const int a = t * k + lane;
-        d = dest_of(ids[a], eidx[a], E, R, N, plan, L);
-        if (ch == 0) {
-            dest_row[a] = d;
-            if (d >= 0) row_src[d] = t;
-        }
+    const int d = resolve_dests(t, k, E, R, N, ids, eidx, plan);
+    if (lane < k && ch == 0) {
+        dest_row[t * k + lane] = d;
+        if (d >= 0) row_src[d] = t;
     }
     for (int j = 0; j < k; ++j) {
         const int dj = __builtin_amdgcn_readlane(d, j);
