@@ -55,13 +55,19 @@ __device__ __forceinline__ int group_rows(int g, int E, int R, bool seg, const i
     return c;
 }
 
-// One workgroup; thread t owns groups 2t and 2t+1 (G <= kMaxGroups).
+// Thread t of a workgroup owns groups 2t and 2t+1 (G <= kMaxGroups). Every
+// workgroup computes the schedule; workgroup 0 writes it. With vrow, the
+// same launch then fills vrow (below), workgroup b its rows 256 b ..
+// 256 b + 255, from the row prefix it holds in LDS: one launch instead of two
+// dependent ones.
 __global__ __launch_bounds__(kThreads) void schedule_kernel(int G, int E, int R, int seg, int bm,
-                                                            int sk1, int sk2,
+                                                            int sk1, int sk2, int N,
                                                             const int32_t* __restrict__ plan,
-                                                            int32_t* __restrict__ sched)
+                                                            int32_t* __restrict__ sched,
+                                                            int32_t* __restrict__ vrow)
 {
     __shared__ int32_t sh[4][kThreads];
+    __shared__ int32_t rs[moe::kMaxGroups + 1];
     const moe::PlanLayout L = moe::plan_layout(E, R);
     const int tid = threadIdx.x;
     int v[2][4];
@@ -89,44 +95,44 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(int G, int E, int R,
         __syncthreads();
     }
     // inclusive prefix through group 2t+1 is sh[q][tid]; through 2t, minus v[1]
+    if (blockIdx.x == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        int32_t* out = sched + q * (G + 1);
-        if (tid == 0) out[0] = 0;
-        if (2 * tid < G) out[2 * tid + 1] = sh[q][tid] - v[1][q];
-        if (2 * tid + 1 < G) out[2 * tid + 2] = sh[q][tid];
+        for (int q = 0; q < 4; ++q) {
+            int32_t* out = sched + q * (G + 1);
+            if (tid == 0) out[0] = 0;
+            if (2 * tid < G) out[2 * tid + 1] = sh[q][tid] - v[1][q];
+            if (2 * tid + 1 < G) out[2 * tid + 2] = sh[q][tid];
+        }
     }
-}
+    if (vrow == nullptr) return;
 
-// vrow[x] = buf row of the x-th row in group order (group g owns x in
-// [row_start[g], row_start[g+1])). By expert: its v-th row lives in the piece
-// that covers v, pieces taken in rank order. By segment: seg_row + v.
-__global__ __launch_bounds__(kThreads) void vrow_kernel(int N, int G, int E, int R, int seg,
-                                                        const int32_t* __restrict__ plan,
-                                                        const int32_t* __restrict__ sched,
-                                                        int32_t* __restrict__ vrow)
-{
-    const int x = blockIdx.x * kThreads + threadIdx.x;
+    // vrow[x] = buf row of the x-th row in group order (group g owns x in
+    // [row_start[g], row_start[g+1])). By expert: its v-th row lives in the
+    // piece that covers v, pieces taken in rank order. By segment: seg_row + v.
+    if (tid == 0) rs[0] = 0;
+    if (2 * tid < G) rs[2 * tid + 1] = sh[1][tid] - v[1][1];
+    if (2 * tid + 1 < G) rs[2 * tid + 2] = sh[1][tid];
+    __syncthreads();
+    const int x = blockIdx.x * kThreads + tid;
     if (x >= N) return;
-    const moe::PlanLayout L = moe::plan_layout(E, R);
-    const int32_t* row_start = sched + G + 1;
+    const int32_t* row_start = rs;
     int lo = 0, hi = G - 1;  // last group with row_start <= x (that group is non-empty)
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (row_start[mid] <= x) lo = mid;
         else hi = mid - 1;
     }
-    const int v = x - row_start[lo];
+    const int vr = x - row_start[lo];
     if (seg) {
-        vrow[x] = plan[L.seg_row + lo] + v;
+        vrow[x] = plan[L.seg_row + lo] + vr;
         return;
     }
     const int np = plan[L.piece_num + lo];
     int cum = 0, row = 0;
     for (int p = 0; p < np && p < R; ++p) {
         const int c = plan[L.piece_cnt + (size_t)lo * R + p];
-        if (v < cum + c) {
-            row = plan[L.piece_row + (size_t)lo * R + p] + (v - cum);
+        if (vr < cum + c) {
+            row = plan[L.piece_row + (size_t)lo * R + p] + (vr - cum);
             break;
         }
         cum += c;
@@ -1147,26 +1153,21 @@ hipError_t moe_launch_gemm_schedule(const moe_shape_t& s, const int32_t* plan, c
     const moe::WsLayout W = moe::ws_layout(s);
     int32_t* sched = reinterpret_cast<int32_t*>(ws + W.sched);
     const bool bf = s.dtype == MOE_BF16;
-    schedule_kernel<<<1, kThreads, 0, st>>>(g.G, s.E, s.R, g.seg ? 1 : 0, bf ? kTM : kFM,
-                                            bf ? 32 : 0, bf ? 64 : 0, plan, sched);
-    hipError_t e = hipGetLastError();
     const int N = s.T * s.k;
-    if (e != hipSuccess || !bf || N == 0) return e;
-    int32_t* vrow = reinterpret_cast<int32_t*>(ws + W.vrow);
-    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, g.G, s.E, s.R, g.seg ? 1 : 0,
-                                                                    plan, sched, vrow);
+    int32_t* vrow = bf && N > 0 ? reinterpret_cast<int32_t*>(ws + W.vrow) : nullptr;
+    const int grid = vrow ? (N + kThreads - 1) / kThreads : 1;
+    schedule_kernel<<<grid, kThreads, 0, st>>>(g.G, s.E, s.R, g.seg ? 1 : 0, bf ? kTM : kFM,
+                                               bf ? 32 : 0, bf ? 64 : 0, N, plan, sched, vrow);
     return hipGetLastError();
 }
 
 hipError_t moe_launch_gemm_schedule_bm(const moe_shape_t& s, const int32_t* plan, int32_t* sched,
                                        int32_t* vrow, hipStream_t st)
 {
-    schedule_kernel<<<1, kThreads, 0, st>>>(s.E, s.E, s.R, 0, kTM, 0, 0, plan, sched);
-    hipError_t e = hipGetLastError();
     const int N = s.T * s.k;
-    if (e != hipSuccess || N == 0) return e;
-    vrow_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(N, s.E, s.E, s.R, 0, plan, sched,
-                                                                    vrow);
+    const int grid = N > 0 ? (N + kThreads - 1) / kThreads : 1;
+    schedule_kernel<<<grid, kThreads, 0, st>>>(s.E, s.E, s.R, 0, kTM, 0, 0, N, plan, sched,
+                                               N > 0 ? vrow : nullptr);
     return hipGetLastError();
 }
 
