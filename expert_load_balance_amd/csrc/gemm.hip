@@ -524,25 +524,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
     // The whole tiles, then the K-parts of split tiles, in two loops of their
     // own (each with its epilogue: one loop holding both would not fit its
-    // registers). Workgroup p takes units p, p + P, ... of each range.
+    // registers). Workgroup p takes units p, p + P, ... of each range. The
+    // first loop's last unit already issues the first K-part's copies and
+    // hands it over (carry_*), as between any two units.
+    int carry_Lu = -1;
+    Unit carry_u{};
+    int carry_rw[kRowLoads];
     auto run = [&](auto split_tag) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     const int end = SPLIT ? total : bal.full;
-    int Lu = (SPLIT ? bal.full : 0) + my_slot;
-    if (Lu >= end) return;
-    Unit u = decode(Lu);
+    int Lu;
+    Unit u;
     int rw[kRowLoads];
-    load_rows(u, rw);
-    setup(u, rw);
-    prologue_head();
-    prologue_tail(u);
+    if (SPLIT && carry_Lu >= 0) {
+        Lu = carry_Lu;
+        u = carry_u;
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) rw[i] = carry_rw[i];
+    } else {
+        Lu = (SPLIT ? bal.full : 0) + my_slot;
+        if (Lu >= end) return;
+        u = decode(Lu);
+        load_rows(u, rw);
+        setup(u, rw);
+        prologue_head();
+        prologue_tail(u);
+    }
 
     for (;;) {
         asm volatile("s_mov_b32 %0, 0" : "=s"(zo));
         // next unit and its rows (read now, used at the end of this unit;
         // these loads go out after this unit's first copies)
         const int Ln = Lu + P;
-        const bool has_next = Ln < end;
+        const bool has_next = Ln < total;
         Unit un = u;
         int nrw[kRowLoads];
 #pragma unroll
@@ -719,6 +733,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         }
         if (has_next) prologue_tail(un);
         if (!has_next) break;
+        if (Ln >= end) {  // the next unit is the K-part loop's first
+            carry_Lu = Ln;
+            carry_u = un;
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i) carry_rw[i] = nrw[i];
+            break;
+        }
         Lu = Ln;
         u = un;
 #pragma unroll
