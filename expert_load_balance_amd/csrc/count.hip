@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(int N, int E,
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / moe::kWave;
 constexpr int kFusedMax = 16384;  // assignments handled by the one-workgroup path
+constexpr int kFusedRounds = kFusedMax / kFusedThreads;  // ids per thread
 
 __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k, int E, int R,
                                                                      const int32_t* __restrict__ ids,
@@ -170,17 +171,28 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
     __shared__ int32_t sc[256];
     __shared__ int32_t base[256];
     __shared__ int32_t wcnt[kFusedWaves][256];
+    __shared__ int32_t wsum[4];
     const int tid = threadIdx.x;
     const int wave = tid / moe::kWave;
     const int lane = tid % moe::kWave;
     if (tid < 256) hist[tid] = 0;
     for (int x = tid; x < kFusedWaves * 256; x += kFusedThreads) (&wcnt[0][0])[x] = 0;
+    // the thread's ids, assignments tid + 1024 i, read once for both passes
+    int32_t ev[kFusedRounds];
+#pragma unroll
+    for (int i = 0; i < kFusedRounds; ++i) {
+        const int a = tid + i * kFusedThreads;
+        ev[i] = a < N ? ids[a] : -1;
+    }
     __syncthreads();
 
     // histogram and id checks
     int bad = 0;
-    for (int a = tid; a < N; a += kFusedThreads) {
-        const int32_t e = ids[a];
+#pragma unroll
+    for (int i = 0; i < kFusedRounds; ++i) {
+        const int a = tid + i * kFusedThreads;
+        if (a >= N) break;
+        const int32_t e = ev[i];
         const int j = a % k;
         for (int jj = 1; jj <= j; ++jj)
             if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
@@ -192,15 +204,24 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
     }
     __syncthreads();
 
-    // inclusive Hillis-Steele scan of the 256 counts
-    if (tid < 256) sc[tid] = tid < E ? hist[tid] : 0;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int32_t v = (tid < 256 && tid >= off) ? sc[tid - off] : 0;
-        __syncthreads();
-        if (tid < 256) sc[tid] += v;
-        __syncthreads();
+    // inclusive scan of the 256 counts: wavefronts 0..3 scan 64 each with
+    // shuffles, then add the totals of the wavefronts before them
+    int32_t inc = 0;
+    if (tid < 256) {
+        inc = tid < E ? hist[tid] : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) wsum[wave] = inc;
     }
+    __syncthreads();
+    if (tid < 256) {
+        for (int w = 0; w < wave; ++w) inc += wsum[w];
+        sc[tid] = inc;
+    }
+    __syncthreads();
     if (tid < E) {
         counts[tid] = hist[tid];
         offsets[tid + 1] = sc[tid];
@@ -218,10 +239,13 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int r0 = 0; r0 < N; r0 += kFusedThreads) {
+#pragma unroll
+    for (int i = 0; i < kFusedRounds; ++i) {
+        const int r0 = i * kFusedThreads;
+        if (r0 >= N) break;
         const int a = r0 + tid;
         const bool valid = a < N;
-        const int32_t e = valid ? ids[a] : -1;
+        const int32_t e = ev[i];
         const bool ok = valid && e >= 0 && e < E;
         uint64_t match = __ballot(ok);
         for (int b = 0; b < nbits; ++b) {
