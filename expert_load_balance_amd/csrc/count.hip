@@ -6,10 +6,10 @@
 // under the expert -> rank mapping) and "Work the 16-token hotspot fixture"
 // (an unknown id or a token repeating an expert stops the count).
 //
-// Up to 16384 assignments, one workgroup of 1024 threads does all three
-// steps below in one launch (the same arithmetic, the scan over its own
-// histogram, the rank rounds 1024 assignments wide). Above that, three
-// launches, none of whose results depend on thread timing:
+// Up to 16384 assignments, one workgroup of 1024 threads does it all in one
+// launch (count_fused_kernel: each wavefront ranks a contiguous chunk, then
+// the chunk bases). Above that, three launches, none of whose results
+// depend on thread timing:
 //   1. hist: workgroup b histograms assignments [b*C, (b+1)*C) in LDS (the
 //      adds are order-free), writes blk_hist[b][E], and checks ids.
 //   2. scan: one workgroup; thread e scans blk_hist[.][e] over workgroups
@@ -159,6 +159,14 @@ constexpr int kFusedWaves = kFusedThreads / moe::kWave;
 constexpr int kFusedMax = 16384;  // assignments handled by the one-workgroup path
 constexpr int kFusedRounds = kFusedMax / kFusedThreads;  // ids per thread
 
+// The one-workgroup path. Wavefront w takes the contiguous assignments
+// [w C, (w + 1) C), C = 64 ceil(N / 1024), 64 at a time in order: lanes
+// holding the same expert are found with ballots over the id bits, and a
+// lane's index within the wavefront's chunk is the chunk's running count of
+// that expert (a per-wavefront LDS row, no barrier) plus its rank among the
+// matching lower lanes. After one barrier, the exclusive prefix over the
+// wavefronts of each expert's chunk counts gives the chunk bases, and their
+// sum the counts.
 __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k, int E, int R,
                                                                      const int32_t* __restrict__ ids,
                                                                      int32_t* __restrict__ counts,
@@ -169,84 +177,45 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
 {
     __shared__ int32_t hist[256];
     __shared__ int32_t sc[256];
-    __shared__ int32_t base[256];
     __shared__ int32_t wcnt[kFusedWaves][256];
     __shared__ int32_t wsum[4];
     const int tid = threadIdx.x;
     const int wave = tid / moe::kWave;
     const int lane = tid % moe::kWave;
-    if (tid < 256) hist[tid] = 0;
     for (int x = tid; x < kFusedWaves * 256; x += kFusedThreads) (&wcnt[0][0])[x] = 0;
-    // the thread's ids, assignments tid + 1024 i, read once for both passes
+    const int C = 64 * ((N + kFusedThreads - 1) / kFusedThreads);
+    const int a0 = wave * C + lane;
+    // the lane's ids, assignments a0 + 64 i, and their checks
     int32_t ev[kFusedRounds];
-#pragma unroll
-    for (int i = 0; i < kFusedRounds; ++i) {
-        const int a = tid + i * kFusedThreads;
-        ev[i] = a < N ? ids[a] : -1;
-    }
-    __syncthreads();
-
-    // histogram and id checks
     int bad = 0;
 #pragma unroll
     for (int i = 0; i < kFusedRounds; ++i) {
-        const int a = tid + i * kFusedThreads;
-        if (a >= N) break;
+        const int a = a0 + 64 * i;
+        ev[i] = 64 * i < C && a < N ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kFusedRounds; ++i) {
+        const int a = a0 + 64 * i;
+        if (64 * i >= C || a >= N) break;
         const int32_t e = ev[i];
         const int j = a % k;
         for (int jj = 1; jj <= j; ++jj)
             if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
-        if (e < 0 || e >= E) {
-            bad |= MOE_ERR_RANGE;
-            continue;
-        }
-        atomicAdd(&hist[e], 1);
+        if (e < 0 || e >= E) bad |= MOE_ERR_RANGE;
     }
     __syncthreads();
 
-    // inclusive scan of the 256 counts: wavefronts 0..3 scan 64 each with
-    // shuffles, then add the totals of the wavefronts before them
-    int32_t inc = 0;
-    if (tid < 256) {
-        inc = tid < E ? hist[tid] : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(inc, off);
-            if (lane >= off) inc += y;
-        }
-        if (lane == 63) wsum[wave] = inc;
-    }
-    __syncthreads();
-    if (tid < 256) {
-        for (int w = 0; w < wave; ++w) inc += wsum[w];
-        sc[tid] = inc;
-    }
-    __syncthreads();
-    if (tid < E) {
-        counts[tid] = hist[tid];
-        offsets[tid + 1] = sc[tid];
-        base[tid] = 0;  // eidx counts within the expert
-    }
-    if (tid == 0) offsets[0] = 0;
-    if (tid < R) {
-        const int n = E / R;
-        rank_load[tid] = sc[(tid + 1) * n - 1] - (tid > 0 ? sc[tid * n - 1] : 0);
-    }
-    __syncthreads();
-
-    // stable within-expert index, 1024 assignments a round (as in the rank
-    // kernel: a ballot multisplit per wavefront, then the wavefront prefix)
+    // index within the wavefront's chunk
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int32_t loc[kFusedRounds];
 #pragma unroll
     for (int i = 0; i < kFusedRounds; ++i) {
-        const int r0 = i * kFusedThreads;
-        if (r0 >= N) break;
-        const int a = r0 + tid;
-        const bool valid = a < N;
+        loc[i] = -1;
+        if (64 * i >= C) break;
         const int32_t e = ev[i];
-        const bool ok = valid && e >= 0 && e < E;
+        const bool ok = a0 + 64 * i < N && e >= 0 && e < E;
         uint64_t match = __ballot(ok);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = ok && ((e >> b) & 1);
@@ -254,26 +223,58 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
             match &= bit ? bal : ~bal;
         }
         const int rank = __popcll(match & lt_mask);
-        if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
-        __syncthreads();
-        if (ok) {
-            int32_t pre = base[e];
-            for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-            eidx[a] = pre + rank;
-        } else if (valid) {
-            eidx[a] = -1;
-        }
-        __syncthreads();
+        // every matching lane reads the running count before the first of
+        // them (rank 0) advances it: one wavefront's LDS operations execute
+        // in order
+        const int32_t prev = ok ? wcnt[wave][e] : 0;
+        if (ok) loc[i] = prev + rank;
+        if (ok && rank == 0) wcnt[wave][e] = prev + __popcll(match);
+    }
+    __syncthreads();
+
+    // chunk bases (exclusive prefix over the wavefronts) and counts
+    if (tid < 256) {
+        int32_t run = 0;
         if (tid < E) {
-            int32_t sum = 0;
 #pragma unroll
             for (int w = 0; w < kFusedWaves; ++w) {
-                sum += wcnt[w][tid];
-                wcnt[w][tid] = 0;
+                const int32_t c = wcnt[w][tid];
+                wcnt[w][tid] = run;
+                run += c;
             }
-            base[tid] += sum;
         }
-        __syncthreads();
+        hist[tid] = run;
+        // inclusive scan of the 256 counts: wavefronts 0..3 scan 64 each
+        // with shuffles, then add the totals of the wavefronts before them
+        int32_t inc = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        sc[tid] = inc;
+    }
+    __syncthreads();
+    if (tid < 256) {
+        for (int w = 0; w < wave; ++w) sc[tid] += wsum[w];
+    }
+    // eidx: index within the chunk + the chunk's base
+#pragma unroll
+    for (int i = 0; i < kFusedRounds; ++i) {
+        const int a = a0 + 64 * i;
+        if (64 * i >= C || a >= N) break;
+        eidx[a] = loc[i] >= 0 ? loc[i] + wcnt[wave][ev[i]] : -1;
+    }
+    __syncthreads();
+    if (tid < E) {
+        counts[tid] = hist[tid];
+        offsets[tid + 1] = sc[tid];
+    }
+    if (tid == 0) offsets[0] = 0;
+    if (tid < R) {
+        const int n = E / R;
+        rank_load[tid] = sc[(tid + 1) * n - 1] - (tid > 0 ? sc[tid * n - 1] : 0);
     }
     if (bad) atomicOr(err, bad);
 }
