@@ -242,6 +242,29 @@ def test_count_flags_bad_ids():
         np.testing.assert_array_equal(host(L.eidx), c["eidx"])
 
 
+def test_count_repeats_across_chunks():
+    # k = 7 does not divide 64: tokens straddle the 64-assignment rounds and
+    # the per-wavefront chunks of the one-workgroup count (N = 9100: chunks of
+    # 576). Token 9 (assignments 63..69) repeats across a round, token 82
+    # (574..580) across two chunks; the clean ids must raise nothing.
+    T, k, E, R = 1300, 7, 16, 4
+    shape = moe.Shape(T, 64, E, k, 64, R, 1, moe.MOE_BF16)
+    base = ((np.arange(T)[:, None] + np.arange(k)[None, :]) % E).astype(np.int32)
+    for t, j in [(None, None), (9, 2), (82, 5), (1299, 6)]:
+        ids = base.copy()
+        if t is not None:
+            ids[t, j] = ids[t, 0]
+        L = MoeLayerBuffers(shape, DEV)
+        d_ids = torch.from_numpy(ids).to(DEV)
+        moe.moe_count(shape, d_ids, L.counts, L.offsets, L.eidx, L.rank_load, L.err, L.ws)
+        torch.cuda.synchronize()
+        c = oracle.count(ids, E, R)
+        assert (int(L.err.item()) & moe.ERR_REPEAT) == (c["err"] & moe.ERR_REPEAT), (t, j)
+        assert bool(c["err"] & moe.ERR_REPEAT) == (t is not None)
+        np.testing.assert_array_equal(host(L.counts), c["counts"])
+        np.testing.assert_array_equal(host(L.eidx), c["eidx"])
+
+
 PLAN_VECTORS = [
     ("fixture", [9, 6, 5, 4, 3, 2, 2, 1], 4),
     ("balanced", [7] * 16, 8),
