@@ -755,14 +755,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 // skew) get one SKM-row tile per N-tile (SKM = 32 or 64) instead of a mostly
 // empty 256-row M-tile. Such a tile is bound by streaming the expert's
 // weights, so its LDS stage holds only SKM rows of activations next to the
-// 32 KB weight tile and the ring is deeper: 4 stages for SKM = 32 (three
-// stages of weight copies in flight per CU), 3 for SKM = 64. Same N-tiles,
+// 32 KB weight tile and the ring is deeper: 4 stages (three stages of weight
+// copies in flight per CU; 160 KB for SKM = 64), 3 for down's SKM = 64.
+// Same N-tiles,
 // K stages, swizzle, copy wrapper and epilogues as the 256-row kernel; 4
 // waves, each SKM rows x 64 B-rows (gate/up: 32 gate and the same 32 up
 // columns).
 template <int SKM>
 struct Skinny {
-    static constexpr int kSlots = SKM == 32 ? 4 : 3;
+    static constexpr int kSlots = 4;
     static constexpr int kA = SKM * kTK * 2;                  // 4 or 8 KB of A per stage
     static constexpr int kSlot = kA + kOpBytes;               // 36 or 40 KB per stage
     static constexpr int kACopies = SKM / 32;                 // A copies per wave per stage
@@ -771,28 +772,31 @@ struct Skinny {
     static constexpr int kSchedOff = SKM == 32 ? 2 : 3;       // tile_start prefix (x (E+1))
 };
 
-// the SKM-row tiles of one launch (a phase of the skinny kernel below);
-// ring, rowmap and ssched are the kernel's LDS, shared by its phases
+// the SKM-row tiles of one launch (a phase of the skinny kernel below); the
+// ring is the kernel's whole LDS, shared by its phases. The schedule is read
+// with scalar loads and each lane keeps the gathered rows it needs in
+// registers, so that all four slots fit for both tile heights.
 template <int MODE, int SKM>
 __device__ __forceinline__ void skinny_phase(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
-    char* ring, int32_t* rowmap, int32_t* ssched)
+    char* ring)
 {
     using SK = Skinny<SKM>;
-    constexpr int kSkM = SKM, kSkSlots = SK::kSlots, kSkA = SK::kA, kSkSlot = SK::kSlot;
+    // down's 64-row tiles keep three slots (measured 1-5 % faster than four
+    // on the decode and dsv3 shapes, where gate/up gains 3-6 % from four)
+    constexpr int kSkSlots = SKM == 64 && MODE == kDown ? 3 : SK::kSlots;
+    constexpr int kSkA = SK::kA, kSkSlot = SK::kSlot;
     constexpr int kSkPerStage = SK::kPerStage, kNB = SK::kBlocks;
 
-    __syncthreads();  // the previous phase is done with ssched
-    for (int i = threadIdx.x; i < G + 1; i += kThreads) {
-        ssched[i] = sched[SK::kSchedOff * (G + 1) + i];
-        ssched[G + 1 + i] = sched[G + 1 + i];
-    }
-    __syncthreads();
+    // entry i of (this height's tile_start[G+1], row_start[G+1])
+    auto ssched = [&](int i) {
+        return i <= G ? ldc(sched, SK::kSchedOff * (G + 1) + i) : ldc(sched, i);
+    };
     const int KT = (MODE == kGateUp ? H : F) / kTK;
-    const int total = ssched[G] * ntiles_n;
+    const int total = ssched(G) * ntiles_n;
     const int P = gridDim.x;
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -814,12 +818,24 @@ __device__ __forceinline__ void skinny_phase(
     }
     constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
 
+    // the next unit's tile is looked up while this one's copies fly
+    TileRef rn = tile_of<MODE>(my_slot, G, ntiles_n, ssched);
     for (int Lu = my_slot; Lu < total; Lu += P) {
-        const TileRef r0 = tile_of<MODE>(Lu, G, ntiles_n, [&](int i) { return ssched[i]; });
+        const TileRef r0 = rn;
         const int e = uni(r0.e), n0 = uni(r0.n0), rows = uni(r0.rows), hrow0 = uni(r0.hrow0);
-        if (tid < kSkM) rowmap[tid] = vrow[hrow0 + (tid < rows ? tid : rows - 1)];
-        wait_vm_lgkm<63>();
-        slot_barrier();
+        // gathered rows: gate/up, the activation row of each A copy (needed
+        // for the copies); down, the output row of each accumulator block,
+        // read after the first copies go out (rows past the tile's repeat its
+        // last)
+        int grow[kNB > SK::kACopies ? kNB : SK::kACopies];
+        auto load_grow = [&]() {
+#pragma unroll
+            for (int i = 0; i < (MODE == kGateUp ? SK::kACopies : kNB); ++i) {
+                const int r = MODE == kGateUp ? 8 * (wave + 4 * i) + (lane >> 3) : 32 * i + fr;
+                grow[i] = vrow[hrow0 + (r < rows ? r : rows - 1)];
+            }
+        };
+        if (MODE == kGateUp) load_grow();
 
         // copy sources: A row 8 wave + lane/8 (one instruction per wave), B as
         // in the 256-row kernel (8 instructions per wave)
@@ -839,7 +855,7 @@ __device__ __forceinline__ void skinny_phase(
         for (int i = 0; i < SK::kACopies; ++i) {
             const int ra = 8 * (wave + 4 * i) + (lane >> 3);
             const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(ra)) * 16);
-            aoff[i] = MODE == kGateUp ? (uint32_t)rowmap[ra] * (uint32_t)H * 2u + ch
+            aoff[i] = MODE == kGateUp ? (uint32_t)grow[i] * (uint32_t)H * 2u + ch
                                       : (uint32_t)min(ra, rows - 1) * (uint32_t)F * 2u + ch;
         }
 #pragma unroll
@@ -868,6 +884,8 @@ __device__ __forceinline__ void skinny_phase(
                 for (int q = 0; q < 16; ++q) acc[b][j][q] = 0.0f;
         constexpr int kAhead = kSkSlots - 1;  // stages in flight beyond the current one
         for (int st = 0; st < kAhead && st < KT; ++st) copy_stage(st);
+        if (MODE == kDown) load_grow();
+        if (Lu + P < total) rn = tile_of<MODE>(Lu + P, G, ntiles_n, ssched);
 
         for (int s = 0; s < KT; ++s) {
             // stage s landed: this wave's copies of later stages issued so far
@@ -916,7 +934,7 @@ __device__ __forceinline__ void skinny_phase(
                     if (gu_out) store_gu(gu_out, hrow0 + row, F, col, acc[b][0], acc[b][1], g4);
                 }
             } else {
-                uint16_t* dst = out + (size_t)rowmap[row] * H;
+                uint16_t* dst = out + (size_t)grow[b] * H;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -930,7 +948,7 @@ __device__ __forceinline__ void skinny_phase(
                     }
             }
         }
-        // everyone is done with the ring and rowmap before the next unit
+        // everyone is done with the ring before the next unit
         wait_vm_lgkm<63>();
         slot_barrier();
     }
@@ -949,12 +967,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out)
 {
     __shared__ __attribute__((aligned(1024))) char ring[kSkinnyRing];
-    __shared__ int32_t rowmap[64];
-    __shared__ int32_t ssched[2 * (moe::kMaxGroups + 1)];  // skinny tile_start[G+1], row_start[G+1]
-    skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring,
-                           rowmap, ssched);
-    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring,
-                           rowmap, ssched);
+    skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring);
+    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring);
 }
 
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
