@@ -2,15 +2,22 @@
 """One MoE layer forward (route -> count -> plan -> permute -> grouped SwiGLU
 GEMM -> combine) on one MI355X, timed over K steps after W warm-up steps.
 
-Default workload: the Mixtral-style coarse layer in bf16 (T=2048 tokens,
-H=4096, E=8 experts, top-2, SwiGLU width 14336, R=8 virtual ranks, S=1),
-router skew maxvio 0.2 (N(0,1) logits plus a tuned Zipf bias). Inputs are
-seeded and synthetic and already resident in HBM when timing starts.
+Default workload: the DeepSeek-V3-shaped layer in bf16 (T=8192 tokens,
+H=7168, 256 routed experts top-8 plus one always-on shared expert, SwiGLU
+width 2048, R=32 virtual ranks, S=8) at router skew maxvio 20, with the same
+layer at maxvio 0 reported beside it. Inputs are seeded and synthetic and
+already resident in HBM when timing starts.
 
-Prints ONE JSON line. `value` is whole-layer tokens/s; `roofline` describes
-the dominant kernel (the gate/up half of the grouped GEMM), timed with HIP
-events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
-bounded token sample of the same workload (a baseline, not a target).
+Timing: before every timed step a 512 MB device write evicts the L2 and the
+Infinity Cache; each step is bracketed by HIP events on the layer's stream,
+and the K steps by synchronisations. `value` = T / mean step time.
+
+Prints ONE JSON line. `roofline` describes the dominant kernel group, the
+routed grouped GEMM (schedule + gate/up + down calls): algorithmic bytes
+(active experts' weights once + buffer rows read + output rows written) or
+flops per call, whichever bound is tighter, over its HIP-event duration;
+`cpu_baseline` times the CPU oracle, pinned to one core, on the same
+workload (a baseline, not a target).
 """
 from __future__ import annotations
 
@@ -34,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--maxvio", type=float, default=None,
                     help="router skew target (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -48,8 +55,9 @@ def parse():
                     help="only the training step of the workload: the training forward (g|u "
                          "kept) and the backward chain, --steps times; one JSON line of its "
                          "figures (for kernel traces of the backward)")
-    ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-ffn-rows", type=int, default=None,
+                    help="buffer rows in the oracle's timed FFN sample (default: about 15 s "
+                         "of FFN work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (a known "
                          "byte count for calibrating HBM counters), then exit")
@@ -62,10 +70,22 @@ def kernel_src_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def traffic_for(workload, maxvio):
-    """HBM bytes per launch of the gate/up kernel from committed counter runs,
-    or None if absent or taken on a different kernel source."""
-    p = os.path.join(ROOT, "profiles", "gemm_gateup_traffic.json")
+    """HBM bytes per call of the routed grouped GEMM (its kernels' launches,
+    summed) from committed counter runs, or None if absent or taken on a
+    different kernel source."""
+    p = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -73,46 +93,99 @@ def traffic_for(workload, maxvio):
     rec = d.get(f"{workload}@{maxvio:g}")
     if not rec or rec.get("kernel_src_sha") != kernel_src_sha():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
 
 
-def cpu_baseline(name, maxvio, lg, bias, x, wts, ntok):
-    """The oracle, as it stands, on the first `ntok` tokens of the workload.
-    Host copies of the inputs (only the experts those tokens use) are made
-    before the clock starts."""
+def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, ffn_budget_s=15.0):
+    """The oracle, as it stands, on the same workload, single-threaded and
+    pinned to one host core. Route, count, plan, permute and combine run on
+    every token; the SwiGLU FFN runs on the first `n_ffn_rows` rows of the
+    buffer (by default about `ffn_budget_s` seconds of work; all rows when
+    they fit) and, with the shared expert on as many tokens, is extrapolated
+    per row to the whole layer (every row costs the same 3*H*F multiply-adds).
+    Host copies of the inputs are made before the clock starts."""
     import numpy as np
 
     import oracle
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[name]
-    E, k, R = w["E"], w["k"], w["R"]
-    xs = x[:ntok].float().cpu().numpy()
-    used = sorted(set(oracle.route(lg[:ntok], bias, k)[0].ravel().tolist()))
-    wg, wu, wd = ({e: t[e].float().cpu().numpy() for e in used} for t in wts)
-    t0 = time.perf_counter()
-    ids, gw, _ = oracle.route(lg[:ntok], bias, k)
-    c = oracle.count(ids, E, R)
-    pl = oracle.plan(c["counts"], R)
-    buf, dest_row, row_src = oracle.permute(xs, ids, c["eidx"], pl)
-    y = np.zeros((ntok * k, xs.shape[1]))
-    for e in range(E):
-        rows = []
-        for p in range(pl["piece_num"][e]):
-            rows.extend(range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p]))
-        if rows:
-            y[rows] = oracle.ffn_rows(buf[rows], wg[e], wu[e], wd[e])
-    oracle.combine(y, dest_row, gw)
-    dt = time.perf_counter() - t0
-    return dict(value=ntok / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {ntok} of {w['T']} tokens of the same workload, full layer "
-                       f"(route, count, plan, permute, SwiGLU FFN, combine), "
-                       f"single-threaded C in double, {dt:.1f} s")
+    T, H, E, k, F, R = (w[c] for c in ("T", "H", "E", "k", "F", "R"))
+    N = T * k
+    est_row_s = 3.0 * H * F / 1.6e9                # the plain C loop: ~1.6 G multiply-adds/s
+    n_rows = n_ffn_rows or max(1, min(N, int(ffn_budget_s / est_row_s)))
+    n_rows = min(n_rows, N)
+    xs = x.float().cpu().numpy()
+    ids0, _, _ = oracle.route(lg, bias, k)
+    c0 = oracle.count(ids0, E, R)
+    pl0 = oracle.plan(c0["counts"], R)
+    # experts owning the first n_rows buffer rows (window order), and their weights
+    seg = []
+    for r in range(R):
+        for i in range(int(pl0["seg_num"][r])):
+            seg.append((int(pl0["seg_row"][r, i]), int(pl0["seg_cnt"][r, i]),
+                        int(pl0["seg_expert"][r, i])))
+    seg.sort()
+    take = [(r0, min(cnt, n_rows - r0), e) for r0, cnt, e in seg if r0 < n_rows and cnt > 0]
+    used = sorted({e for _, _, e in take})
+    wh = {e: tuple(t[e].float().cpu().numpy() for t in wts) for e in used}
+    sh = tuple(t[0].float().cpu().numpy() for t in shared) if shared is not None else None
+    n_sh = min(T, max(1, n_rows // k)) if shared is not None else 0
+
+    prev = os.sched_getaffinity(0)
+    core = min(prev)
+    os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        ids, gw, _ = oracle.route(lg, bias, k)
+        c = oracle.count(ids, E, R)
+        pl = oracle.plan(c["counts"], R)
+        buf, dest_row, _ = oracle.permute(xs, ids, c["eidx"], pl)
+        t1 = time.perf_counter()
+        y = np.zeros((N, H))
+        for r0, cnt, e in take:
+            y[r0:r0 + cnt] = oracle.ffn_rows(buf[r0:r0 + cnt], *wh[e])
+        t2 = time.perf_counter()
+        if n_sh:
+            oracle.ffn_rows(xs[:n_sh], *sh)
+        t3 = time.perf_counter()
+        oracle.combine(y, dest_row, gw)
+        t4 = time.perf_counter()
+    finally:
+        os.sched_setaffinity(0, prev)
+    t_ffn_row = (t2 - t1) / n_rows
+    t_sh_row = (t3 - t2) / n_sh if n_sh else 0.0
+    t_layer = (t1 - t0) + (t4 - t3) + t_ffn_row * N + t_sh_row * (T if shared is not None else 0)
+    extrap = n_rows < N or (shared is not None and n_sh < T)
+    sample = (f"route, count, plan, permute and combine on all {T} tokens "
+              f"({(t1 - t0) + (t4 - t3):.1f} s); SwiGLU FFN on the first {n_rows} of {N} buffer rows "
+              f"({t2 - t1:.1f} s)"
+              + (f" and the shared expert on {n_sh} of {T} tokens ({t3 - t2:.1f} s)" if n_sh else "")
+              + (", extrapolated per row to the whole layer" if extrap else "")
+              + f"; plain single-threaded C in double, pinned to core {core}")
+    return dict(value=T / t_layer, unit="tokens/s", cores=1, kind="oracle", sample=sample,
+                ffn_extrapolated=extrap, seconds_measured=t4 - t0,
+                cpu_model=cpu_model(), nproc=os.cpu_count(), affinity_cores=len(prev))
+
+
+class Flusher:
+    """Writes a 512 MB device buffer: more than the 256 MB Infinity Cache and
+    the L2s, so the next kernel reads its operands from HBM."""
+
+    def __init__(self, nbytes=512 << 20):
+        import torch
+
+        self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.v = 0
+
+    def __call__(self):
+        self.v ^= 0x5A5A5A5A
+        self.buf.fill_(self.v)
 
 
 def time_back_to_back(fn, reps=50):
     """Mean duration of one call when `reps` calls run back to back on the
-    current stream (launch gaps amortised), in seconds."""
+    current stream (launch gaps amortised, caches warm), in seconds."""
     import torch
 
     for _ in range(5):
@@ -125,6 +198,25 @@ def time_back_to_back(fn, reps=50):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e-3 / reps
+
+
+def time_flushed(fn, flush, reps=30):
+    """Mean HIP-event duration of one call on the current stream with the
+    caches flushed before each call, in seconds."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / reps
 
 
 def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shared=None):
@@ -179,9 +271,9 @@ def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shar
             "padding_rows": s.E * cap - kept, "gemm_rows": s.E * cap}
 
 
-def time_router(shape, x, bias, seed, act, stream):
-    """The router's scores + top-k (x read once; W_r is E x H), back to back.
-    Returns (seconds per call, algorithmic bytes)."""
+def time_router(shape, x, bias, seed, act, stream, flush):
+    """The router's scores + top-k (x read once; W_r is E x H), caches flushed
+    before each call. Returns (seconds per call, algorithmic bytes)."""
     import torch
 
     import expert_load_balance_amd as moe
@@ -195,8 +287,8 @@ def time_router(shape, x, bias, seed, act, stream):
     r_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     r_err = torch.zeros(1, dtype=torch.int32, device=dev)
     r_ws = torch.empty(max(1, moe.moe_router_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
-    t = time_back_to_back(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
-                                   r_err, r_ws, stream=stream))
+    t = time_flushed(moe.bind(moe.moe_router, shape, x, wr, bias, r_logits, r_ids, r_w,
+                              r_err, r_ws, stream=stream), flush)
     nbytes = (T * H + E * H) * (2 if shape.dtype == moe.MOE_BF16 else 4) + T * E * 4 * 2
     return t, nbytes
 
@@ -340,52 +432,86 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
     L = MoeLayerBuffers(shape, dev, shared_F=shared_F)
     stream = torch.cuda.current_stream()
 
+    flush = Flusher()
+
+    def fwd(marks=None):
+        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks)
+
     # Untimed: the GPU's clocks settle over the first ~10 steps of load (the
     # first steps after idle run 5-15 % slower), so the layer runs in batches
     # of steps for about 0.2 s before the counted warm-up steps.
     t_settle = time.perf_counter() + 0.2
     while time.perf_counter() < t_settle:
         for _ in range(10):
-            L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
+            fwd()
         torch.cuda.synchronize()
     for _ in range(warmup):
-        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
+        flush()
+        fwd()
     torch.cuda.synchronize()
     print(f"[bench] {name}@{maxvio:g} warm-up done", file=sys.stderr, flush=True)
 
-    # the timed steps carry no event records (those sit between kernels in
-    # the queue); a second pass with per-stage events gives the breakdown
+    # Timed steps: caches flushed before each, the step and its routed grouped
+    # GEMM bracketed by HIP events on the layer's stream.
+    def ev():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    step_ev = [ev() for _ in range(steps)]
+    gemm_ev = [ev() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream)
+        flush()
+        step_ev[i][0].record(stream)
+        fwd(marks={"gemm": gemm_ev[i]})
+        step_ev[i][1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    wall = time.perf_counter() - t0
 
-    marks = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for s in STAGES} for _ in range(steps)]
+    def dist(pairs):
+        v = sorted(a.elapsed_time(b) for a, b in pairs)
+        return dict(mean=sum(v) / len(v), median=v[len(v) // 2], p10=v[len(v) // 10],
+                    p90=v[(len(v) * 9) // 10])
+
+    step_ms = dist(step_ev)
+    gemm_ms = dist(gemm_ev)
+
+    # the same steps back to back without flushes (warm caches, no events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    warm_s = (time.perf_counter() - t1) / steps
+
+    # per-stage breakdown: a second flushed pass with events between stages
+    marks = [{s: ev() for s in STAGES} for _ in range(steps)]
     for i in range(steps):
-        L.forward(lg, bias, x, *wts, shared_w=shared, stream=stream, marks=marks[i])
+        flush()
+        fwd(marks=marks[i])
     torch.cuda.synchronize()
-
     stage_ms = {}
     for s in STAGES:
         if s == "shared" and shared is None:
             continue
-        v = sorted(m[s][0].elapsed_time(m[s][1]) for m in marks)
-        stage_ms[s] = dict(mean=sum(v) / len(v), p10=v[len(v) // 10], p90=v[(len(v) * 9) // 10])
+        stage_ms[s] = dist([m[s] for m in marks])
 
-    # the two row moves alone, back to back (their in-layer stage times also
-    # hold a launch gap each)
-    t_perm = time_back_to_back(moe.bind(moe.moe_permute, shape, x, L.ids, L.eidx, L.plan, L.buf,
-                                        L.dest_row, L.row_src, stream=stream))
+    # the row moves and the top-k alone, caches flushed before each launch
+    t_perm = time_flushed(moe.bind(moe.moe_permute, shape, x, L.ids, L.eidx, L.plan, L.buf,
+                                   L.dest_row, L.row_src, stream=stream), flush)
     sy = L.shared_y if shared else None
-    t_comb = time_back_to_back(moe.bind(moe.moe_combine, shape, L.y, L.dest_row, L.w, sy, L.out,
-                                        stream=stream))
+    t_comb = time_flushed(moe.bind(moe.moe_combine, shape, L.y, L.dest_row, L.w, sy, L.out,
+                                   stream=stream), flush)
+    route_ids = torch.empty_like(L.ids)
+    route_w = torch.empty_like(L.w)
+    route_err = torch.zeros_like(L.err)
+    t_route = time_flushed(moe.bind(moe.moe_route, shape, lg, bias, route_ids, route_w, route_err,
+                                    stream=stream), flush)
+    del route_ids, route_w, route_err
 
     t_router = router_bytes = None
     if extras:
-        t_router, router_bytes = time_router(shape, x, bias, w["seed"], act, stream)
+        t_router, router_bytes = time_router(shape, x, bias, w["seed"], act, stream, flush)
 
     slots = None
     if extras and moe.moe_pool_bytes(shape):
@@ -399,6 +525,7 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
     if capacity_factor is not None and extras:
         cap_res = time_capacity_layer(shape, lg, bias, x, wts, capacity_factor, steps, warmup,
                                       L=L, shared=shared)
+    del flush
 
     st, _ = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
                           err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
@@ -406,36 +533,91 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
     b = 2 if dtype == moe.MOE_BF16 else 4
     gu_s = stage_ms["gemm_gateup"]["mean"] * 1e-3
     dn_s = stage_ms["gemm_down"]["mean"] * 1e-3
-    gu_flops = 4.0 * N * H * F
-    dn_flops = 2.0 * N * H * F
+    gemm_s = gemm_ms["mean"] * 1e-3
+    gemm_flops = 6.0 * N * H * F
+    # algorithmic bytes of the routed grouped GEMM: every active expert's three
+    # projections read once, the buffer rows read once, the output rows
+    # written once (the h round trip between the two calls is not counted)
+    gemm_bytes = st["active_experts"] * 3.0 * F * H * b + 2.0 * N * H * b
     perm_bytes = (T + N) * H * b
     comb_bytes = (N + T) * H * b + (T * H * b if shared else 0)
+    route_bytes = T * E * 4 + (E * 4 if bias is not None else 0) + T * k * 8
     res = dict(
         name=name, maxvio=maxvio, shape=(T, H, E, k, F, R, S), shared_F=shared_F, dtype=dtype,
-        tokens_per_s=T * steps / elapsed, ms_per_step=elapsed * 1e3 / steps, stage_ms=stage_ms,
-        gu_flops=gu_flops, gu_tflops=gu_flops / gu_s / 1e12, dn_tflops=dn_flops / dn_s / 1e12,
-        gemm_mfma_frac=(gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / PEAK_BF16_TFLOPS,
-        permute_us=t_perm * 1e6, combine_us=t_comb * 1e6,
+        tokens_per_s=T / (step_ms["mean"] * 1e-3), ms_per_step=step_ms["mean"], step_ms=step_ms,
+        wall_s=wall, warm_tokens_per_s=T / warm_s, warm_ms_per_step=warm_s * 1e3,
+        stage_ms=stage_ms, gemm_ms=gemm_ms,
+        gemm_flops=gemm_flops, gemm_bytes=gemm_bytes,
+        gemm_tflops=gemm_flops / gemm_s / 1e12, gemm_gbs=gemm_bytes / gemm_s / 1e9,
+        gemm_mfma_frac=gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS,
+        gemm_hbm_frac=gemm_bytes / gemm_s / 1e9 / PEAK_HBM_GBS,
+        gemm_bound="hbm" if gemm_bytes / PEAK_HBM_GBS > gemm_flops / 1e3 / PEAK_BF16_TFLOPS
+        else "mfma",
+        gu_tflops=4.0 * N * H * F / gu_s / 1e12, dn_tflops=2.0 * N * H * F / dn_s / 1e12,
+        permute_us=t_perm * 1e6, combine_us=t_comb * 1e6, route_us=t_route * 1e6,
         permute_hbm_frac=perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
+        route_hbm_frac=route_bytes / t_route / 1e9 / PEAK_HBM_GBS,
         permute_hbm_frac_in_layer=perm_bytes / (stage_ms["permute"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac_in_layer=comb_bytes / (stage_ms["combine"]["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        stats=st, inputs=(lg_np, bias_np, x, wts), capacity=cap_res, slots=slots, backward=bwd,
-        # weight-streaming view of the two GEMM calls: every active expert's
-        # three projections read once (the bound when rows per expert are few)
-        gemm_weight_hbm_frac=st["active_experts"] * 3.0 * F * H * b / (gu_s + dn_s) / 1e9
-        / PEAK_HBM_GBS,
+        stats=st, inputs=(lg_np, bias_np, x, wts, shared), capacity=cap_res, slots=slots,
+        backward=bwd,
+        shared_gemm=None if shared is None else {
+            "ms": stage_ms["shared"]["mean"],
+            "mfma_frac": 6.0 * T * H * shared_F / (stage_ms["shared"]["mean"] * 1e-3) / 1e12
+            / PEAK_BF16_TFLOPS},
         router=None if t_router is None else {
             "us": t_router * 1e6, "tflops": 2.0 * T * E * H / t_router / 1e12,
             "hbm_frac": router_bytes / t_router / 1e9 / PEAK_HBM_GBS})
     return res
 
 
-# Other workloads and skews reported beside the headline line (layer tokens/s,
-# grouped-GEMM MFMA fraction, permute / combine HBM fractions); decode at the
-# feasible maximum skew (15) for the maxvio-20 request.
-SWEEP = (("a3b", 0.0), ("a3b", 0.2), ("a3b", 1.0), ("dsv3", 20.0), ("dsv3", 0.0),
-         ("decode64", 1.0), ("decode256", 20.0), ("decode1024", 1.0), ("decode1024", 20.0))
+# Every other shape and skew point of the workload list, reported beside the
+# headline (layer tokens/s, grouped-GEMM fractions, permute / combine / route
+# HBM fractions); decode at the feasible maximum skew (15) for the maxvio-20
+# request.
+SWEEP = (("mixtral", 0.2), ("a3b", 0.0), ("a3b", 0.2), ("a3b", 1.0),
+         ("decode64", 1.0), ("decode64", 20.0), ("decode256", 1.0), ("decode256", 20.0),
+         ("decode1024", 1.0), ("decode1024", 20.0))
+
+
+def summary(q):
+    """The per-point figures of a run_workload result (rounded)."""
+    def r4(v):
+        return None if v is None else round(v, 4)
+
+    out = {
+        "tokens_per_s": round(q["tokens_per_s"]), "ms_per_step": r4(q["ms_per_step"]),
+        "step_ms_p10_p90": [r4(q["step_ms"]["p10"]), r4(q["step_ms"]["p90"])],
+        "warm_tokens_per_s": round(q["warm_tokens_per_s"]),
+        "maxvio_realised": r4(q["stats"]["maxvio_expert"]),
+        "active_experts": q["stats"]["active_experts"],
+        "gemm_ms": r4(q["gemm_ms"]["mean"]), "gemm_bound": q["gemm_bound"],
+        "gemm_hbm_frac": r4(q["gemm_hbm_frac"]), "grouped_gemm_mfma_frac": r4(q["gemm_mfma_frac"]),
+        "gemm_gateup_tflops": round(q["gu_tflops"], 1), "gemm_down_tflops": round(q["dn_tflops"], 1),
+        "permute_hbm_frac": r4(q["permute_hbm_frac"]), "combine_hbm_frac": r4(q["combine_hbm_frac"]),
+        "route_hbm_frac": r4(q["route_hbm_frac"]),
+        "permute_us": round(q["permute_us"], 2), "combine_us": round(q["combine_us"], 2),
+        "route_us": round(q["route_us"], 2),
+        "plan": {k_: q["stats"][k_] for k_ in ("planned_max", "planned_min", "replica_pieces",
+                                               "max_slots_needed", "ranks_over_slots")},
+        "stages_ms": {s_: r4(v["mean"]) for s_, v in q["stage_ms"].items()},
+    }
+    if q["shared_gemm"] is not None:
+        out["shared_gemm"] = {k_: r4(v_) for k_, v_ in q["shared_gemm"].items()}
+    if q["router"] is not None:
+        out["router_us"] = round(q["router"]["us"], 2)
+    if q["backward"] is not None:
+        out["backward"] = {k_: round(v_, 3) for k_, v_ in q["backward"].items()}
+    if q["slots"] is not None:
+        out["replica_slots"] = {k_: round(v_, 3) if isinstance(v_, float) else v_
+                                for k_, v_ in q["slots"].items()}
+    if q["capacity"] is not None:
+        cq = q["capacity"]
+        out["fixed_capacity_cf1.25"] = {"tokens_per_s": round(cq["tokens_per_s"]),
+                                        "dropped_assignments": cq["dropped_assignments"],
+                                        "padding_rows": cq["padding_rows"]}
+    return out
 
 
 def run_backward_only(args):
@@ -538,8 +720,7 @@ def main():
     T, H, E, k, F, R, S = r["shape"]
     shared_F = r["shared_F"]
     st = r["stats"]
-    traffic = traffic_for(name, maxvio)
-    achieved = r["gu_tflops"]
+    hbm = r["gemm_bound"] == "hbm"
     rec = {
         "metric": METRIC,
         "value": r["tokens_per_s"],
@@ -558,58 +739,52 @@ def main():
                                + (f" shared_F={shared_F}" if shared_F else ""),
                    "maxvio_target": maxvio, "maxvio_realised": st["maxvio_expert"],
                    "global_batch": T, "parallelism": "1 GPU, R virtual ranks"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "gemm_bf16_kernel<0> (gate/up call)",
-                     "flops_per_launch": r["gu_flops"]},
-        "stages_ms": {s: round(v["mean"], 4) for s, v in r["stage_ms"].items()},
-        "gemm_down_tflops": r["dn_tflops"],
-        "grouped_gemm_mfma_frac": r["gemm_mfma_frac"],
-        "permute_hbm_frac": r["permute_hbm_frac"],
-        "combine_hbm_frac": r["combine_hbm_frac"],
-        "permute_us": r["permute_us"],
-        "combine_us": r["combine_us"],
-        "permute_hbm_frac_in_layer": r["permute_hbm_frac_in_layer"],
-        "combine_hbm_frac_in_layer": r["combine_hbm_frac_in_layer"],
-        "plan": {"planned_max": st["planned_max"], "planned_min": st["planned_min"],
-                 "replica_pieces": st["replica_pieces"], "max_slots_needed": st["max_slots_needed"],
-                 "ranks_over_slots": st["ranks_over_slots"]},
-        "fixed_capacity_baseline": r["capacity"],
-        "router_scores_topk": r["router"],
-        "replica_slots": r["slots"],
-        "backward": r["backward"],
-        "gemm_weight_hbm_frac": r["gemm_weight_hbm_frac"],
+        "timing": "HIP events per step on the layer's stream, 512 MB cache flush before each "
+                  "step; value = T / mean step",
+        "step_ms": {k_: round(v_, 4) for k_, v_ in r["step_ms"].items()},
+        "warm_back_to_back": {"tokens_per_s": r["warm_tokens_per_s"],
+                              "ms_per_step": r["warm_ms_per_step"]},
+        "roofline": {"bound": r["gemm_bound"],
+                     "achieved": r["gemm_gbs"] if hbm else r["gemm_tflops"],
+                     "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
+                     "unit": "GB/s" if hbm else "TFLOP/s",
+                     "frac": r["gemm_hbm_frac"] if hbm else r["gemm_mfma_frac"],
+                     "traffic": traffic_for(name, maxvio),
+                     "kernel": "routed grouped GEMM: schedule_kernel + gemm_skinny_kernel<0> + "
+                               "gemm_bf16_kernel<0> + fixup_kernel<0> + gemm_skinny_kernel<1> + "
+                               "gemm_bf16_kernel<1> + fixup_kernel<1>",
+                     "ms_per_call": r["gemm_ms"]["mean"],
+                     "bytes_per_call": r["gemm_bytes"], "flops_per_call": r["gemm_flops"],
+                     "mfma_frac": r["gemm_mfma_frac"], "hbm_frac": r["gemm_hbm_frac"]},
     }
+    rec.update({k_: v_ for k_, v_ in summary(r).items()
+                if k_ not in ("tokens_per_s", "ms_per_step")})
+    rec["gemm_src_sha16"] = kernel_src_sha()
     if not args.no_cpu_baseline:
-        # about 5e10 multiply-adds of FFN work: 10-30 s for the plain C oracle
-        ntok = args.cpu_tokens or max(1, min(T, int(5e10 / (k * 3 * H * F))))
-        lg_np, bias_np, x, wts = r["inputs"]
-        rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, ntok)
+        lg_np, bias_np, x, wts, shared = r["inputs"]
+        rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, shared,
+                                           n_ffn_rows=args.cpu_ffn_rows)
     del r
     torch.cuda.empty_cache()
+    # the workload's other skew points beside the headline (dsv3: maxvio 0)
+    others = [m for m in w["maxvio"] if m is not None and m != maxvio]
+    if others and args.maxvio is None:
+        comp = {}
+        for m in others:
+            q = run_workload(name, m, args.steps, args.warmup, capacity_factor=1.25,
+                             extras=not args.layer_only)
+            comp[f"{name}@{m:g}"] = summary(q)
+            comp[f"{name}@{m:g}"]["gemm_traffic"] = traffic_for(name, m)
+            del q
+            torch.cuda.empty_cache()
+        rec["companion"] = comp
     if not args.no_sweep and not args.layer_only:
         sweep = {}
         for sname, smv in SWEEP:
+            if sname == name:
+                continue
             q = run_workload(sname, smv, 10, 3, capacity_factor=1.25)
-            cq = q["capacity"]
-            sweep[f"{sname}@{smv:g}"] = {
-                "tokens_per_s": round(q["tokens_per_s"]), "ms_per_step": round(q["ms_per_step"], 4),
-                "maxvio_realised": round(q["stats"]["maxvio_expert"], 4),
-                "grouped_gemm_mfma_frac": round(q["gemm_mfma_frac"], 4),
-                "gemm_gateup_tflops": round(q["gu_tflops"], 1),
-                "gemm_down_tflops": round(q["dn_tflops"], 1),
-                "permute_hbm_frac": round(q["permute_hbm_frac"], 4),
-                "combine_hbm_frac": round(q["combine_hbm_frac"], 4),
-                "router_us": round(q["router"]["us"], 2),
-                "gemm_weight_hbm_frac": round(q["gemm_weight_hbm_frac"], 4),
-                "backward": None if q["backward"] is None else {
-                    k_: round(v_, 3) for k_, v_ in q["backward"].items()},
-                "replica_slots": None if q["slots"] is None else {
-                    k_: round(v_, 3) if isinstance(v_, float) else v_
-                    for k_, v_ in q["slots"].items()},
-                "fixed_capacity_cf1.25": {"tokens_per_s": round(cq["tokens_per_s"]),
-                                          "dropped_assignments": cq["dropped_assignments"],
-                                          "padding_rows": cq["padding_rows"]}}
+            sweep[f"{sname}@{smv:g}"] = summary(q)
             del q
             torch.cuda.empty_cache()
         rec["sweep"] = sweep

@@ -7,9 +7,9 @@
 // logits.
 //
 // Mapping: a group of G lanes (G = the next power of two >= E, at most one
-// wavefront; 32 above 64 experts with 4096 tokens or more) owns one token;
-// lane l holds experts l, l+G, l+2G, ... in
-// registers, so the row is read with unit-stride coalesced loads. Each of
+// wavefront; 32 above 64 experts with 4096 tokens or more and k <= 32) owns
+// one token; lane l holds experts l, l+G, l+2G, ... in registers, so the row
+// is read with unit-stride coalesced loads. Each of
 // the k rounds takes a per-lane best among untaken experts and an all-reduce
 // over the group (DPP moves and permlane swaps, no LDS) under the total order
 // (score desc, id asc), so every lane agrees on the winner and its logit. After k rounds
@@ -260,8 +260,9 @@ hipError_t moe_launch_route(const moe_shape_t& s, const float* logits, const flo
     if (E <= 64) return launch<64, 1>(s, logits, bias, ids, w, err, st, pl);
     // above 64 experts, many tokens: two tokens a wavefront, 32 lanes each
     // (measured 8-14 % faster at 4096 and 8192 tokens; at 1024 tokens a token
-    // a wavefront is faster)
-    if (s.T >= 4096) {
+    // a wavefront is faster). Lane j of a group holds the j-th winner, so a
+    // 32-lane group serves k <= 32 only; larger k keeps 64 lanes a token.
+    if (s.T >= 4096 && s.k <= 32) {
         if (E <= 128) return launch<32, 4>(s, logits, bias, ids, w, err, st, pl);
         if (E <= 192) return launch<32, 6>(s, logits, bias, ids, w, err, st, pl);
         return launch<32, 8>(s, logits, bias, ids, w, err, st, pl);

@@ -68,7 +68,8 @@ class MoeLayerBuffers:
         """Route -> count -> plan -> permute -> grouped GEMM -> (shared) -> combine.
 
         marks: optional dict stage -> (start_event, end_event) recorded around
-        each stage on the stream. pool: a device buffer of
+        each stage on the stream ("gemm" spans the routed grouped GEMM's three
+        calls: schedule, gate/up, down). pool: a device buffer of
         moe_pool_bytes(shape) bytes; with it the planned replicas are
         prefetched into their slots after the plan and the grouped GEMM runs
         by plan segment, reading them (stages "prefetch" and "gemm_slots").
@@ -110,6 +111,7 @@ class MoeLayerBuffers:
                                    self.ws, st)
             mark("gemm_slots", 1)
         else:
+            mark("gemm", 0)
             mark("gemm_schedule", 0)
             moe_gemm_schedule(s, self.plan, self.ws, st)
             mark("gemm_schedule", 1)
@@ -119,6 +121,7 @@ class MoeLayerBuffers:
             mark("gemm_down", 0)
             moe_gemm_down(s, self.plan, w_down, self.y, self.ws, st)
             mark("gemm_down", 1)
+            mark("gemm", 1)
         shared_y = None
         if self.shared_shape is not None and shared_w is not None:
             mark("shared", 0)

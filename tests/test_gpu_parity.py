@@ -66,7 +66,9 @@ def run_layer(shape, lg, bias, x, wts, shared_w=None, shared_F=None):
 
 
 def check_integer_path(L, lg, bias, x_host):
-    """route ids/weights, count, plan, permute, bit-exact against the oracle."""
+    """route ids/weights, count, plan, permute, bit-exact against the oracle.
+    Returns the oracle's (ids, w, count dict, plan) and, with x_host, its
+    (dest_row, row_src) in ``check_integer_path.perm``."""
     s = L.shape
     ids, w, err = oracle.route(lg, bias, s.k)
     assert err == 0
@@ -87,6 +89,8 @@ def check_integer_path(L, lg, bias, x_host):
         np.testing.assert_array_equal(host(L.row_src), row_src, err_msg="row_src")
         gbuf = L.buf.view(torch.int16 if L.buf.dtype == torch.bfloat16 else torch.int32)
         np.testing.assert_array_equal(host(gbuf), buf, err_msg="buf")
+        del buf
+        check_integer_path.perm = (dest_row, row_src)
     assert int(L.err.item()) == 0
     return ids, w, c, pl
 
@@ -140,16 +144,17 @@ def test_layer_small_full_parity(case):
     L = run_layer(shape, lg, bias, x, wts)
     xh = host(x)
     ids, w, c, pl = check_integer_path(L, lg, bias, host(raw_bits(x)))
+    dest_ref, src_ref = check_integer_path.perm
     # FFN per expert on its rows, oracle in double from the same rounded inputs
     wg, wu, wd = (host(t) for t in wts)
-    buf_ref = xh[host(L.row_src)]
+    buf_ref = xh[src_ref]
     y_ref = np.zeros((T * k, H))
     for e in range(E):
         rows = expert_rows(pl, e)
         if rows.size:
             y_ref[rows] = oracle.ffn_rows(buf_ref[rows], wg[e], wu[e], wd[e])
     assert_tol(host(L.y), y_ref, dtype, "y")
-    out_ref = oracle.combine(y_ref, host(L.dest_row), w)
+    out_ref = oracle.combine(y_ref, dest_ref, w)
     assert_tol(host(L.out), out_ref, dtype, "out (end to end)")
 
 
@@ -203,6 +208,32 @@ def test_route_ties_and_signed_zero():
         rid, rw, rerr = oracle.route(lgx, bx, k_)
         np.testing.assert_array_equal(host(ids), rid)
         assert_tol(host(w), rw, moe.MOE_F32, "w")
+        assert int(err.item()) == 0 == rerr
+
+
+def test_route_many_tokens_every_k():
+    """At 4096 tokens and more than 64 experts two tokens share a wavefront
+    (32 lanes each) when k <= 32; larger k keeps a wavefront per token. Ids
+    bit-exact and weights within the fp32 bar against the oracle on both
+    sides of that switch, including k = 32, 33, 40 and 64."""
+    T = 4096
+    for e_, k_, seed in [(128, 8, 61), (128, 32, 62), (128, 33, 63), (128, 40, 64),
+                         (256, 64, 65), (200, 48, 66), (256, 8, 67)]:
+        _say(f"[case] route T={T} E={e_} k={k_}")
+        lg = synth.router_logits(T, e_, seed)
+        bias = synth.zipf_bias(e_, 0.3, seed)
+        shape = moe.Shape(T, 64, e_, k_, 64, 1, 0, moe.MOE_BF16)
+        ids = alloc((T, k_), torch.int32, DEV)
+        w = alloc((T, k_), torch.float32, DEV)
+        ids.fill_(-1)
+        w.fill_(-1.0)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        moe.moe_route(shape, torch.from_numpy(lg).to(DEV), torch.from_numpy(bias).to(DEV), ids, w,
+                      err)
+        torch.cuda.synchronize()
+        rid, rw, rerr = oracle.route(lg, bias, k_)
+        np.testing.assert_array_equal(host(ids), rid, err_msg=f"ids E={e_} k={k_}")
+        assert_tol(host(w), rw, moe.MOE_F32, f"w E={e_} k={k_}")
         assert int(err.item()) == 0 == rerr
 
 
@@ -348,10 +379,19 @@ def test_host_rejects_before_launch():
 
 # ------------------------------------------------------- full-size, sampled --
 
-FULL = [("mixtral", 0.2), ("a3b", 0), ("a3b", 1), ("dsv3", 20), ("dsv3", 0),
-        ("decode64", 1), ("decode1024", 20), ("decode256", 20)]
+# Every shape and router-skew point of the workload list: the Mixtral-style
+# layer at maxvio 0.2, the 30B-A3B shape at 0 / 0.2 / 1, the DeepSeek-V3 shape
+# at 20 and 0, and the decode sweep (T = 64, 256, 1024) at 1 and at the
+# feasible maximum 15 (asked for as 20).
+FULL = [("mixtral", 0.2), ("a3b", 0), ("a3b", 0.2), ("a3b", 1), ("dsv3", 20), ("dsv3", 0),
+        ("decode64", 1), ("decode64", 20), ("decode256", 1), ("decode256", 20),
+        ("decode1024", 1), ("decode1024", 20)]
 
 _WEIGHT_CACHE = {}
+# the bf16 grouped GEMM's tile heights: experts with up to 32 rows get one
+# 32-row tile, 33..64 rows one 64-row tile, more rows 256-row M-tiles
+_SKINNY1, _SKINNY2, _MTILE = 32, 64, 256
+_ORACLE_THREADS = 8
 
 
 def _workload_tensors(name):
@@ -370,17 +410,55 @@ def _workload_tensors(name):
     return _WEIGHT_CACHE
 
 
-def _sample_experts(counts, pl):
-    nz = [e for e in range(len(counts)) if counts[e] > 0]
-    hot = int(np.argmax(counts))
-    cold = min(nz, key=lambda e: (counts[e], e))
-    split = [e for e in nz if pl["piece_num"][e] > 1]
-    picks = [hot, cold] + split[:1]
-    return sorted(set(picks))
+def _tile_sample_rows(c, salt):
+    """Virtual rows (0 .. c-1) of an expert with c rows to check: in each
+    256-row M-tile one row in each 128-row half the tile holds (the two
+    halves are computed by different wavefronts), in a 32- or 64-row tile
+    one row of each 32-row block. Positions inside a block vary with salt."""
+    if c <= 0:
+        return []
+    if c <= _SKINNY2:
+        blocks = [(b, min(b + 32, c)) for b in range(0, c, 32)]
+    else:
+        blocks = [(b, min(b + 128, c)) for b in range(0, c, 128)]
+    rows = []
+    for i, (a, b) in enumerate(blocks):
+        rows.append(a + (salt * 7919 + i * 104729) % (b - a))
+    return rows
+
+
+def _window_tokens(dest_row, win_off, T, want):
+    """About `want` tokens spread over every window: for each window, the
+    token of its first and of its middle row, then evenly spaced tokens."""
+    R = len(win_off) - 1
+    by_row = {}
+    for t in range(T):
+        for d in dest_row[t]:
+            by_row[int(d)] = t
+    toks = set()
+    for r in range(R):
+        a, b = int(win_off[r]), int(win_off[r + 1])
+        if b > a:
+            toks.add(by_row[a])
+            toks.add(by_row[(a + b) // 2])
+    # then tokens at an even stride until `want` (or all T) are in
+    step = max(1, T // max(1, want))
+    t = step // 2
+    while len(toks) < min(want, T):
+        toks.add(t % T)
+        t += step if t + step < 4 * T else 1
+    return np.array(sorted(toks), np.int64)
 
 
 @pytest.mark.parametrize("name,maxvio", FULL, ids=[f"{n}@{m}" for n, m in FULL])
 def test_full_size_sampled(name, maxvio):
+    """A full-size layer: the integer path and statistics whole and bit-exact;
+    the FFN on rows from every (expert, M-tile) of the grouped GEMM -- so
+    every tile of both GEMMs, K-split leftovers and both skinny heights
+    included, has rows checked -- and the combine on 64+ tokens spread over
+    every rank window, each against the oracle from the same inputs."""
+    import concurrent.futures as cf
+
     _say(f"[case] full {name}@{maxvio}")
     w = wl.WORKLOADS[name]
     shape = moe.Shape(w["T"], w["H"], w["E"], w["k"], w["F"], w["R"], w["S"], moe.MOE_BF16)
@@ -390,10 +468,11 @@ def test_full_size_sampled(name, maxvio):
     shared = cache.get("shared")
     L = run_layer(shape, lg, bias, x, wts, shared_w=shared, shared_F=w.get("shared_F"))
     ids, wgt, c, pl = check_integer_path(L, lg, bias, host(raw_bits(x)))
+    dest_ref, buf_ref_src = check_integer_path.perm
     # statistics, bit-exact against the oracle's
     st, loads = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
                               err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
-    ref = oracle.stats(ids, c["counts"], shape.R, S=shape.S, dest_row=host(L.dest_row), pl=pl,
+    ref = oracle.stats(ids, c["counts"], shape.R, S=shape.S, dest_row=dest_ref, pl=pl,
                        capacity_factor=w.get("capacity_factor", 1.0))
     for key_ in ("N", "max_count", "min_count", "active_experts", "maxvio_expert",
                  "balancedness_expert", "home_max", "maxvio_rank_home", "planned_max",
@@ -402,25 +481,73 @@ def test_full_size_sampled(name, maxvio):
                  "max_slots_needed", "ranks_over_slots", "nonlocal_rows"):
         assert st[key_] == ref[key_], key_
     assert st["planned_max"] - st["planned_min"] <= 1          # equal load
-    if shape.S >= shape.E // shape.R:
-        assert st["ranks_over_slots"] == 0
-    # FFN on sampled experts (a few rows each) and combine on sampled tokens
+    # replica slots per rank <= S on this seed (guaranteed when S >= E/R; with
+    # fewer slots, as in the decode sweep, a property of these inputs)
+    assert st["max_slots_needed"] <= shape.S and st["ranks_over_slots"] == 0
+
+    # rows to check: every (expert, M-tile) of the GEMM, and the k rows of the
+    # sampled combine tokens, all computed by the oracle from x and the weights
+    counts = c["counts"]
+    toks = _window_tokens(dest_ref, pl["win_off"], shape.T, 64)
+    assert len(toks) >= min(64, shape.T)
+    tok_rows = set(dest_ref[toks].ravel().tolist())
+    classes = {"skinny32": 0, "skinny64": 0, "mtile": 0}
+    want = {}
+    for e in range(shape.E):
+        ce = int(counts[e])
+        if ce == 0:
+            continue
+        rows = expert_rows(pl, e)
+        vr = []
+        if ce <= _SKINNY1:
+            classes["skinny32"] += 1
+            vr = _tile_sample_rows(ce, e)
+        elif ce <= _SKINNY2:
+            classes["skinny64"] += 1
+            vr = _tile_sample_rows(ce, e)
+        else:
+            for m0 in range(0, ce, _MTILE):
+                classes["mtile"] += 1
+                vr += [m0 + v for v in _tile_sample_rows(min(_MTILE, ce - m0), e * 131 + m0)]
+        sel = set(rows[vr].tolist()) | (tok_rows & set(rows.tolist()))
+        want[e] = np.array(sorted(sel), np.int64)
+    _say(f"[case] full {name}@{maxvio}: tiles {classes}, {sum(len(v) for v in want.values())} "
+         f"rows over {len(want)} experts, {len(toks)} combine tokens")
+
     xh = host(x)
     wg, wu, wd = wts
     y = host(L.y)
-    for e in _sample_experts(c["counts"], pl):
-        rows = expert_rows(pl, e)
-        pick = np.unique(np.concatenate([rows[:3], rows[-3:], rows[len(rows) // 2:][:2]]))
-        src = host(L.row_src)[pick]
-        ref_y = oracle.ffn_rows(xh[src], host(wg[e]), host(wu[e]), host(wd[e]))
-        assert_tol(y[pick], ref_y, moe.MOE_BF16, f"y expert {e}")
-    toks = np.unique(np.linspace(0, shape.T - 1, 6).astype(int))
-    dr = host(L.dest_row)[toks]
+    y_ref = {}
+
+    def run_oracle(e, rows, g, u, d):
+        return e, rows, oracle.ffn_rows(xh[buf_ref_src[rows]], g, u, d)
+
+    with cf.ThreadPoolExecutor(_ORACLE_THREADS) as ex:
+        futs = []
+        for e, rows in want.items():
+            # host copies of one expert's weights at a time; the oracle runs
+            # in worker threads (its C call releases the interpreter lock)
+            futs.append(ex.submit(run_oracle, e, rows, host(wg[e]), host(wu[e]), host(wd[e])))
+            if len(futs) >= 2 * _ORACLE_THREADS:
+                done = futs.pop(0).result()
+                y_ref[done[0]] = done
+        for f in futs:
+            done = f.result()
+            y_ref[done[0]] = done
+    full_ref = {}
+    for e, (_, rows, ref_y) in sorted(y_ref.items()):
+        assert_tol(y[rows], ref_y, moe.MOE_BF16, f"y expert {e} ({len(rows)} rows)")
+        for r, v in zip(rows.tolist(), ref_y):
+            full_ref[r] = v
+
+    # combine on the sampled tokens, from oracle rows, weights and shared expert
+    dr = dest_ref[toks]
+    y_tok = np.stack([full_ref[int(r)] for r in dr.ravel()])
     sh = None
     if shared is not None:
         sg, su, sd = (host(t[0]) for t in shared)
         sh = oracle.ffn_rows(xh[toks], sg, su, sd)
         assert_tol(host(L.shared_y)[toks], sh, moe.MOE_BF16, "shared expert")
-    out_ref = oracle.combine(y[dr.ravel()].reshape(-1, shape.H), np.arange(dr.size).reshape(dr.shape),
-                             host(L.w)[toks].astype(np.float64), sh)
-    assert_tol(host(L.out)[toks], out_ref, moe.MOE_BF16, "out")
+    out_ref = oracle.combine(y_tok, np.arange(dr.size).reshape(dr.shape),
+                             wgt[toks].astype(np.float64), sh)
+    assert_tol(host(L.out)[toks], out_ref, moe.MOE_BF16, f"out ({len(toks)} tokens)")
