@@ -17,7 +17,7 @@ import os
 __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "Shape", "StatsT", "lib_path", "load",
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
-    "moe_route", "moe_count", "moe_plan", "moe_permute", "moe_grouped_gemm",
+    "moe_route", "moe_count", "moe_count_noalloc", "moe_plan", "moe_permute", "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
     "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
     "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
+    "moe_count_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -129,6 +130,7 @@ def load():
         "moe_workspace_bytes": (ctypes.c_size_t, [_SP]),
         "moe_route": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_count": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+        "moe_count_noalloc": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_plan": (st, [_SP, _VP, _VP, _VP]),
         "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -302,6 +304,17 @@ def moe_count(shape, ids, counts, offsets, eidx, rank_load, err, ws, stream=None
             _ptr(rank_load, i32, "rank_load", shape.R), _ptr(err, i32, "err", 1),
             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _ok(load().moe_count(*args), "moe_count")
+
+
+def moe_count_noalloc(shape, ids, counts, offsets, eidx, rank_load, err, stream=None):
+    """moe_count without a workspace (the library's fixed device scratch)."""
+    import torch
+
+    i32 = torch.int32
+    args = (ctypes.byref(shape), _ptr(ids, i32, "ids", shape.N), _ptr(counts, i32, "counts", shape.E),
+            _ptr(offsets, i32, "offsets", shape.E + 1), _ptr(eidx, i32, "eidx", shape.N),
+            _ptr(rank_load, i32, "rank_load", shape.R), _ptr(err, i32, "err", 1), _stream(stream))
+    _ok(load().moe_count_noalloc(*args), "moe_count_noalloc")
 
 
 def moe_plan(shape, counts, plan, stream=None):

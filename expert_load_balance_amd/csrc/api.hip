@@ -111,6 +111,20 @@ moe_status_t moe_count(const moe_shape_t* shape, const int32_t* d_ids, int32_t* 
                                 static_cast<char*>(d_ws), as_stream(stream)));
 }
 
+moe_status_t moe_count_noalloc(const moe_shape_t* shape, const int32_t* d_ids, int32_t* d_counts,
+                               int32_t* d_offsets, int32_t* d_eidx, int32_t* d_rank_load,
+                               int32_t* d_err, moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_ids, N) || !d_counts || !d_offsets || bad(d_eidx, N) || !d_rank_load || !d_err)
+        return MOE_EINVAL;
+    if (2 * moe::count_table_bytes(N, shape->E) > moe::kCountScratchBytes) return MOE_EINVAL;
+    return dev(moe_launch_count_noalloc(*shape, d_ids, d_counts, d_offsets, d_eidx, d_rank_load,
+                                        d_err, as_stream(stream)));
+}
+
 moe_status_t moe_plan(const moe_shape_t* shape, const int32_t* d_counts, int32_t* d_plan,
                       moe_stream_t stream)
 {

@@ -78,6 +78,17 @@ struct WsLayout {
 
 constexpr int kCountChunk = 1024;  // assignments per counting workgroup
 
+// Counting workgroups of the multi-launch count, and the bytes of one of its
+// two per-workgroup tables (int32[B][E], 256-byte aligned).
+inline int count_blocks(int64_t N) { return (int)((N + kCountChunk - 1) / kCountChunk); }
+inline size_t count_table_bytes(int64_t N, int E)
+{
+    const int64_t B = count_blocks(N);
+    return ((size_t)(B > 0 ? B : 1) * (size_t)E * 4 + 255) & ~size_t(255);
+}
+// Fixed device scratch of moe_count_noalloc: both tables must fit.
+constexpr size_t kCountScratchBytes = size_t(8) << 20;
+
 // bf16 grouped GEMM geometry shared by the workspace layout and the kernels:
 // 256 x 256 tiles, K in 64-deep stages, at most kGemmMaxGrid persistent
 // workgroups. Tiles left over after the last full round of workgroups are
@@ -114,11 +125,10 @@ inline WsLayout ws_layout(const moe_shape_t& s)
 {
     WsLayout w;
     const int64_t N = (int64_t)s.T * s.k;
-    const int64_t B = (N + kCountChunk - 1) / kCountChunk;
-    w.count_blocks = (int)B;
+    w.count_blocks = count_blocks(N);
     size_t o = 0;
-    w.blk_hist = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
-    w.blk_base = o;  o = align256(o + (size_t)(B > 0 ? B : 1) * s.E * 4);
+    w.blk_hist = o;  o += count_table_bytes(N, s.E);
+    w.blk_base = o;  o += count_table_bytes(N, s.E);
     w.sched = o;     o = align256(o + (size_t)(4 * (2 * s.E + 1) + 64) * 4);
     w.wtab = o;      o = align256(o + (size_t)2 * s.E * 3 * 8);
     w.vrow = o;      o = align256(o + (size_t)(N > 0 ? N : 1) * 4);
@@ -240,6 +250,12 @@ hipError_t moe_launch_route(const moe_shape_t& s, const float* logits, const flo
 hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
                             int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
                             char* ws, hipStream_t st);
+// moe_count with its tables in the library's fixed device scratch
+// (kCountScratchBytes per GPU) instead of a workspace; the caller checks
+// 2 * count_table_bytes(N, E) <= kCountScratchBytes.
+hipError_t moe_launch_count_noalloc(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                                    int32_t* offsets, int32_t* eidx, int32_t* rank_load,
+                                    int32_t* err, hipStream_t st);
 hipError_t moe_launch_plan(const moe_shape_t& s, const int32_t* counts, int32_t* plan,
                            hipStream_t st);
 hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t* ids,

@@ -20,6 +20,8 @@
 //      rank among them is the popcount of the lower matching lanes. The
 //      per-wave match counts, prefixed over the four wavefronts in LDS, and
 //      the running per-expert base give eidx in flat (t*k+j) order.
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -281,15 +283,18 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
 
 }  // namespace
 
-hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
-                            int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
-                            char* ws, hipStream_t st)
+namespace {
+
+// The count proper, with the multi-launch path's per-workgroup tables at
+// blk_hist and blk_base (int32[B][E] each; unused up to 16384 assignments).
+// Every entry of both tables is written before it is read, so they need no
+// clearing between calls.
+hipError_t launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
+                        int32_t* blk_hist, int32_t* blk_base, hipStream_t st)
 {
-    const moe::WsLayout L = moe::ws_layout(s);
     const int64_t N = (int64_t)s.T * s.k;
-    int32_t* blk_hist = reinterpret_cast<int32_t*>(ws + L.blk_hist);
-    int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
-    const int B = L.count_blocks;
+    const int B = moe::count_blocks(N);
     if (N <= kFusedMax) {
         count_fused_kernel<<<1, kFusedThreads, 0, st>>>((int)N, s.k, s.E, s.R, ids, counts, offsets,
                                                          eidx, rank_load, err);
@@ -306,4 +311,65 @@ hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* c
     if (e != hipSuccess || B == 0) return e;
     count_rank_kernel<<<B, kThreads, 0, st>>>((int)N, s.E, ids, blk_base, eidx);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t moe_launch_count(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                            int32_t* offsets, int32_t* eidx, int32_t* rank_load, int32_t* err,
+                            char* ws, hipStream_t st)
+{
+    const moe::WsLayout L = moe::ws_layout(s);
+    return launch_count(s, ids, counts, offsets, eidx, rank_load, err,
+                        reinterpret_cast<int32_t*>(ws + L.blk_hist),
+                        reinterpret_cast<int32_t*>(ws + L.blk_base), st);
+}
+
+// ---- the count without a caller workspace --------------------------------
+// For callers that cannot allocate (graph capture, allocation-free loops):
+// the multi-launch path's two tables live in this fixed device array instead
+// of the workspace. Each GPU the library runs on holds its own copy until the
+// process ends; every call on a GPU shares it, so calls that overlap on one
+// GPU (other streams, other host threads) race on it.
+static __device__ __align__(256) char scratch[moe::kCountScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // the array's device address on each GPU, once known
+
+// The device address of `scratch` on the current GPU, looked up once per
+// device (host code must not use the array's name as a device address).
+hipError_t scratch_on_current_device(char** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *out = static_cast<char*>(g_scratch[dev]);
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t moe_launch_count_noalloc(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                                    int32_t* offsets, int32_t* eidx, int32_t* rank_load,
+                                    int32_t* err, hipStream_t st)
+{
+    char* p = nullptr;
+    const hipError_t e = scratch_on_current_device(&p);
+    if (e != hipSuccess) return e;
+    const int64_t N = (int64_t)s.T * s.k;
+    const size_t table = moe::count_table_bytes(N, s.E);
+    return launch_count(s, ids, counts, offsets, eidx, rank_load, err,
+                        reinterpret_cast<int32_t*>(p), reinterpret_cast<int32_t*>(p + table), st);
 }

@@ -181,6 +181,21 @@ moe_status_t moe_count(const moe_shape_t *shape, const int32_t *d_ids, int32_t *
                        int32_t *d_offsets, int32_t *d_eidx, int32_t *d_rank_load, int32_t *d_err,
                        void *d_ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_count for callers that cannot allocate device memory (code under HIP
+ * graph capture, allocation-free serving loops): the same results as
+ * moe_count, bit for bit, with no workspace argument. Above 16384
+ * assignments the count keeps two int32[ceil(N/1024)][E] tables (each
+ * rounded up to 256 bytes) in a fixed 8 MiB device array of the library
+ * instead: N up to 4194304 at E = 256 (up to 16384 at any E); a larger
+ * shape returns MOE_EINVAL before anything is launched. Each GPU holds its
+ * own copy of that array until the process ends; its address is looked up
+ * on the first call on each device (the device current at the call). Calls
+ * that overlap on one GPU (other streams or host threads) share the array
+ * and race: order them. Allocates nothing. */
+moe_status_t moe_count_noalloc(const moe_shape_t *shape, const int32_t *d_ids, int32_t *d_counts,
+                               int32_t *d_offsets, int32_t *d_eidx, int32_t *d_rank_load,
+                               int32_t *d_err, moe_stream_t stream);
+
 /* [MoonEP] paragraphs 3-4: every rank receives the same number of
  * assignments, by replicas planned on the device from the router output;
  * with S = n slots every expert a rank computes is local.

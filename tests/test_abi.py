@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 33
+    assert len(names) == 34
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -78,6 +78,11 @@ def test_null_and_bad_shape_rejected_before_launch(lib):
     assert lib.moe_stats(ctypes.byref(s), p, p, p, None, None, None, None, 0.0, p, 1 << 20,
                          ctypes.byref(st), None, None) == 1                 # factor must be > 0
     assert moe.moe_status_str(4).startswith("device error word")
+    # the allocation-free count: NULLs, and a shape whose count tables exceed
+    # its fixed 8 MiB scratch (N = 2^23 assignments over 256 experts)
+    assert lib.moe_count_noalloc(ctypes.byref(s), None, p, p, p, p, p, None) == 1
+    big = moe.Shape(1 << 20, 64, 256, 8, 64, 32, 8, moe.MOE_BF16)
+    assert lib.moe_count_noalloc(ctypes.byref(big), p, p, p, p, p, p, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
