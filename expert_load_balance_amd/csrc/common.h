@@ -70,6 +70,7 @@ struct WsLayout {
     size_t wtab;                // gemm by segment: uint64[2E][3] weight addresses
     size_t vrow;                // gemm: int32[N] expert-sorted row -> buf row
     size_t part;                // gemm bf16: float[units][256][256] partial tiles (K-split leftovers)
+    size_t skpart;              // gemm bf16: float[2 grid][32 + 64][256] skinny partial tiles
     size_t h;                   // gemm: dtype[N][F] SwiGLU activations
     size_t stats;               // stats: int64[kStatsSlots(R)]
     size_t total;
@@ -133,6 +134,7 @@ inline WsLayout ws_layout(const moe_shape_t& s)
     w.wtab = o;      o = align256(o + (size_t)2 * s.E * 3 * 8);
     w.vrow = o;      o = align256(o + (size_t)(N > 0 ? N : 1) * 4);
     w.part = o;      o = align256(o + (size_t)gemm_part_units(s) * kGemmTile * kGemmTile * 4);
+    w.skpart = o;    o = align256(o + (s.dtype == MOE_BF16 ? (size_t)2 * kGemmMaxGrid * (32 + 64) * kGemmTile * 4 : 0));
     w.h = o;         o = align256(o + (size_t)N * s.F * (s.dtype == MOE_BF16 ? 2 : 4));
     w.stats = o;     o = align256(o + (size_t)stats_slots(s.R) * 8);
     w.total = o;

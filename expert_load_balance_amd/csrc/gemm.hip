@@ -757,10 +757,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 // weights, so its LDS stage holds only SKM rows of activations next to the
 // 32 KB weight tile and the ring is deeper: 4 stages (three stages of weight
 // copies in flight per CU; 160 KB for SKM = 64), 3 for down's SKM = 64.
-// Same N-tiles,
-// K stages, swizzle, copy wrapper and epilogues as the 256-row kernel; 4
-// waves, each SKM rows x 64 B-rows (gate/up: 32 gate and the same 32 up
-// columns).
+// Same N-tiles, K stages, swizzle, copy wrapper and epilogues as the 256-row
+// kernel; 4 waves, each SKM rows x 64 B-rows (gate/up: 32 gate and the same
+// 32 up columns).
+//
+// Balance: whole rounds of tiles go to the workgroups in turn (slot w takes
+// tiles w, w + P, ...); the n tiles left over (n < P), each KT stages deep,
+// form one run of n*KT stages that is cut into equal contiguous pieces, one
+// per workgroup (stream-K; at least kSkMinStages stages each, so a few
+// tiles use fewer workgroups). A piece that covers a whole tile finishes it;
+// a tile cut by a piece boundary is finished by the fixup kernel, which sums
+// its parts in order. A piece is cut at most twice, so it writes at most two
+// fp32 partial tiles: its first segment to slot 2q, its last (when the first
+// is not also the last) to slot 2q + 1 (q: its piece).
 template <int SKM>
 struct Skinny {
     static constexpr int kSlots = 4;
@@ -771,18 +780,58 @@ struct Skinny {
     static constexpr int kBlocks = SKM / 32;                  // 32-row blocks per wave
     static constexpr int kSchedOff = SKM == 32 ? 2 : 3;       // tile_start prefix (x (E+1))
 };
+constexpr int kSkMinStages = 8;
+// parts of one cut tile: pieces hold at least KT / 32 stages (sk_cut), so a
+// tile meets at most 33 of them
+constexpr int kSkMaxParts = 34;
+
+// The stream-K cut of n tiles of KT stages over P workgroups: workgroup
+// piece q covers stages [first(q), first(q + 1)); pieces >= Pe are empty.
+struct SkCut {
+    int64_t W;  // n * KT
+    int Pe;     // pieces in use
+    __host__ __device__ int64_t first(int q) const { return q >= Pe ? W : (int64_t)q * W / Pe; }
+    // the piece holding stage g (0 <= g < W)
+    __host__ __device__ int piece_of(int64_t g) const { return (int)(((g + 1) * Pe - 1) / W); }
+};
+__host__ __device__ inline SkCut sk_cut(int n, int KT, int P)
+{
+    SkCut c;
+    c.W = (int64_t)n * KT;
+    // pieces of at least kSkMinStages stages and at least KT / 32, so that
+    // no tile is cut into more than kSkMaxParts parts
+    const int minlen = max(kSkMinStages, (KT + 31) / 32);
+    const int64_t by_min = c.W / minlen;
+    c.Pe = (int)(by_min < P ? (by_min > 1 ? by_min : 1) : P);
+    return c;
+}
+// Tiles done whole, in rounds: all of them when the last round would keep at
+// least half the workgroups busy (cutting its tiles then saves less than the
+// partial tiles cost), else the full rounds only.
+__host__ __device__ inline int sk_full_tiles(int total, int P)
+{
+    const int full = total / P * P;
+    return total - full > P / 2 ? total : full;
+}
+// partial slot of the segment of piece q that starts at stage g
+__host__ __device__ inline int sk_slot(const SkCut& c, int q, int64_t g)
+{
+    return g == c.first(q) ? 2 * q : 2 * q + 1;
+}
 
 // the SKM-row tiles of one launch (a phase of the skinny kernel below); the
 // ring is the kernel's whole LDS, shared by its phases. The schedule is read
 // with scalar loads and each lane keeps the gathered rows it needs in
-// registers, so that all four slots fit for both tile heights.
+// registers, so that all four slots fit for both tile heights. Piece q of
+// the phase goes to workgroup slot (q + qofs) mod P, so a phase that uses
+// fewer than P workgroups leaves the next phase the ones it did not use.
 template <int MODE, int SKM>
-__device__ __forceinline__ void skinny_phase(
+__device__ __forceinline__ int skinny_phase(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
-    char* ring)
+    float* __restrict__ part, char* ring, int qofs)
 {
     using SK = Skinny<SKM>;
     // down's 64-row tiles keep three slots (measured 1-5 % faster than four
@@ -797,10 +846,40 @@ __device__ __forceinline__ void skinny_phase(
     };
     const int KT = (MODE == kGateUp ? H : F) / kTK;
     const int total = ssched(G) * ntiles_n;
+    if (total == 0) return 0;
     const int P = gridDim.x;
+    // whole rounds of tiles first (workgroup slot w takes tiles w, w + P, ...),
+    // then the stream-K pieces of the tiles left over
+    const int nfull = sk_full_tiles(total, P);
+    const SkCut cut = sk_cut(total - nfull, KT, P);
     const int per_xcd = P / 8;
     const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (my_slot >= total) return;
+    const int q = (my_slot - qofs % P + P) % P;  // this workgroup's piece of the leftover
+    int t_full = my_slot;
+    int64_t g = cut.first(q);
+    const int64_t g_end = cut.first(q + 1);
+    // the workgroup's segments in order: (tile, first stage, end stage, partial slot or -1)
+    struct Seg {
+        int t, k0, k1, pslot;
+    };
+    auto next_seg = [&](Seg& sg) {
+        if (t_full < nfull) {
+            sg = Seg{t_full, 0, KT, -1};
+            t_full += P;
+            return true;
+        }
+        if (g < g_end) {
+            const int tl = (int)(g / KT);
+            const int k0 = (int)(g - (int64_t)tl * KT);
+            const int k1 = (int)min<int64_t>((int64_t)KT, k0 + (g_end - g));
+            sg = Seg{nfull + tl, k0, k1, (k0 == 0 && k1 == KT) ? -1 : sk_slot(cut, q, g)};
+            g += k1 - k0;
+            return true;
+        }
+        return false;
+    };
+    Seg cur;
+    if (!next_seg(cur)) return cut.Pe;
 
     const int tid = threadIdx.x;
     const int wave = uni(tid >> 6), lane = tid & 63;
@@ -818,9 +897,11 @@ __device__ __forceinline__ void skinny_phase(
     }
     constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
 
-    // the next unit's tile is looked up while this one's copies fly
-    TileRef rn = tile_of<MODE>(my_slot, G, ntiles_n, ssched);
-    for (int Lu = my_slot; Lu < total; Lu += P) {
+    // the next segment's tile is looked up while this one's copies fly
+    TileRef rn = tile_of<MODE>(cur.t, G, ntiles_n, ssched);
+    for (;;) {
+        const int k0 = uni(cur.k0), nst = uni(cur.k1 - cur.k0), pslot = uni(cur.pslot);
+        const bool whole = pslot < 0;
         const TileRef r0 = rn;
         const int e = uni(r0.e), n0 = uni(r0.n0), rows = uni(r0.rows), hrow0 = uni(r0.hrow0);
         // gathered rows: gate/up, the activation row of each A copy (needed
@@ -838,15 +919,17 @@ __device__ __forceinline__ void skinny_phase(
         if (MODE == kGateUp) load_grow();
 
         // copy sources: A row 8 wave + lane/8 (one instruction per wave), B as
-        // in the 256-row kernel (8 instructions per wave)
+        // in the 256-row kernel (8 instructions per wave); both start at
+        // stage k0
+        const size_t kofs = (size_t)k0 * kTK;
         const char *abase, *bbase0, *bbase1;
         if (MODE == kGateUp) {
-            abase = uni_ptr(reinterpret_cast<const char*>(a_src));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 0, F, H)));
-            bbase1 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w1, e, 1, F, H)));
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src + kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 0, F, H) + kofs));
+            bbase1 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w1, e, 1, F, H) + kofs));
         } else {
-            abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)hrow0 * F));
-            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 2, F, H)));
+            abase = uni_ptr(reinterpret_cast<const char*>(a_src + (size_t)hrow0 * F + kofs));
+            bbase0 = uni_ptr(reinterpret_cast<const char*>(group_w(wtab, w0, e, 2, F, H) + kofs));
             bbase1 = bbase0;
         }
         // A copy instruction q = wave + 4 i fills rows 8q .. 8q+7
@@ -881,20 +964,22 @@ __device__ __forceinline__ void skinny_phase(
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) acc[b][j][q] = 0.0f;
+                for (int qq = 0; qq < 16; ++qq) acc[b][j][qq] = 0.0f;
         constexpr int kAhead = kSkSlots - 1;  // stages in flight beyond the current one
-        for (int st = 0; st < kAhead && st < KT; ++st) copy_stage(st);
+        for (int st = 0; st < kAhead && st < nst; ++st) copy_stage(st);
         if (MODE == kDown) load_grow();
-        if (Lu + P < total) rn = tile_of<MODE>(Lu + P, G, ntiles_n, ssched);
+        Seg nxt;
+        const bool more = next_seg(nxt);
+        if (more) rn = tile_of<MODE>(nxt.t, G, ntiles_n, ssched);
 
-        for (int s = 0; s < KT; ++s) {
+        for (int s = 0; s < nst; ++s) {
             // stage s landed: this wave's copies of later stages issued so far
-            const int after = min(KT - 1, s + kAhead - 1) - s;
+            const int after = min(nst - 1, s + kAhead - 1) - s;
             if (after >= 2) wait_vm_lgkm<2 * kSkPerStage>();
             else if (after == 1) wait_vm_lgkm<kSkPerStage>();
             else wait_vm_lgkm<0>();
             slot_barrier();  // ... in every wave; and stage s-1's slot is free
-            if (s + kAhead < KT) copy_stage(s + kAhead);
+            if (s + kAhead < nst) copy_stage(s + kAhead);
             const char* slot = ring + (s % kSkSlots) * kSkSlot;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -911,50 +996,74 @@ __device__ __forceinline__ void skinny_phase(
             }
         }
 
-        // epilogue: acc[b][j][4 g4 + q] is row 32 b + (lane & 31), B-row block
-        // j column 8 g4 + 4 (lane >> 5) + q
+        // epilogue: acc[b][j][4 g4 + qq] is row 32 b + (lane & 31), B-row block
+        // j column 8 g4 + 4 (lane >> 5) + qq
+        if (whole) {
 #pragma unroll
-        for (int b = 0; b < kNB; ++b) {
-            const int row = 32 * b + fr;
-            if (row >= rows) continue;
-            if (MODE == kGateUp) {
-                uint16_t* dst = out + (size_t)(hrow0 + row) * F;
+            for (int b = 0; b < kNB; ++b) {
+                const int row = 32 * b + fr;
+                if (row >= rows) continue;
+                if (MODE == kGateUp) {
+                    uint16_t* dst = out + (size_t)(hrow0 + row) * F;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int col = n0 + 32 * wave + g4 * 8 + fh * 4;
-                    if (col >= F) continue;
-                    float hv[4];
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int col = n0 + 32 * wave + g4 * 8 + fh * 4;
+                        if (col >= F) continue;
+                        float hv[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        hv[q] = fast_silu(acc[b][0][g4 * 4 + q]) * acc[b][1][g4 * 4 + q];
-                    uint2 pk;
-                    pk.x = moe::pack_bf16x2(hv[0], hv[1]);
-                    pk.y = moe::pack_bf16x2(hv[2], hv[3]);
-                    *reinterpret_cast<uint2*>(dst + col) = pk;
-                    if (gu_out) store_gu(gu_out, hrow0 + row, F, col, acc[b][0], acc[b][1], g4);
+                        for (int qq = 0; qq < 4; ++qq)
+                            hv[qq] = fast_silu(acc[b][0][g4 * 4 + qq]) * acc[b][1][g4 * 4 + qq];
+                        uint2 pk;
+                        pk.x = moe::pack_bf16x2(hv[0], hv[1]);
+                        pk.y = moe::pack_bf16x2(hv[2], hv[3]);
+                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                        if (gu_out) store_gu(gu_out, hrow0 + row, F, col, acc[b][0], acc[b][1], g4);
+                    }
+                } else {
+                    uint16_t* dst = out + (size_t)grow[b] * H;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int col = n0 + 64 * wave + 32 * j + g4 * 8 + fh * 4;
+                            if (col >= H) continue;
+                            uint2 pk;
+                            pk.x = moe::pack_bf16x2(acc[b][j][g4 * 4 + 0], acc[b][j][g4 * 4 + 1]);
+                            pk.y = moe::pack_bf16x2(acc[b][j][g4 * 4 + 2], acc[b][j][g4 * 4 + 3]);
+                            *reinterpret_cast<uint2*>(dst + col) = pk;
+                        }
                 }
-            } else {
-                uint16_t* dst = out + (size_t)grow[b] * H;
+            }
+        } else {
+            // a cut tile: its fp32 partial [SKM][256] in B-row order (gate/up:
+            // gate columns 0..127, up columns 128..255); padding rows too
+            float* dst = part + (size_t)pslot * SKM * kTN;
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) {
+                const int row = 32 * b + fr;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int col = n0 + 64 * wave + 32 * j + g4 * 8 + fh * 4;
-                        if (col >= H) continue;
-                        uint2 pk;
-                        pk.x = moe::pack_bf16x2(acc[b][j][g4 * 4 + 0], acc[b][j][g4 * 4 + 1]);
-                        pk.y = moe::pack_bf16x2(acc[b][j][g4 * 4 + 2], acc[b][j][g4 * 4 + 3]);
-                        *reinterpret_cast<uint2*>(dst + col) = pk;
+                        const int c = (MODE == kGateUp ? j * 128 + 32 * wave : 64 * wave + 32 * j) +
+                                      g4 * 8 + fh * 4;
+                        *reinterpret_cast<float4*>(dst + (size_t)row * kTN + c) =
+                            make_float4(acc[b][j][g4 * 4 + 0], acc[b][j][g4 * 4 + 1],
+                                        acc[b][j][g4 * 4 + 2], acc[b][j][g4 * 4 + 3]);
                     }
             }
         }
-        // everyone is done with the ring before the next unit
+        // everyone is done with the ring before the next segment
         wait_vm_lgkm<63>();
         slot_barrier();
+        if (!more) break;
+        cur = nxt;
     }
+    return cut.Pe;
 }
 
-// Both skinny tile sizes in one launch: the 32-row tiles, then the 64-row.
+// Both skinny tile sizes in one launch: the 32-row tiles, then the 64-row
+// ones on the workgroups the first phase left idle first.
 constexpr int kSkinnyRing = Skinny<32>::kSlots * Skinny<32>::kSlot > Skinny<64>::kSlots * Skinny<64>::kSlot
                                 ? Skinny<32>::kSlots * Skinny<32>::kSlot
                                 : Skinny<64>::kSlots * Skinny<64>::kSlot;
@@ -964,11 +1073,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out)
+    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
+    float* __restrict__ part32, float* __restrict__ part64)
 {
     __shared__ __attribute__((aligned(1024))) char ring[kSkinnyRing];
-    skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring);
-    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, ring);
+    const int used = skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out,
+                                            gu_out, part32, ring, 0);
+    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, part64,
+                           ring, used);
+}
+
+// Finishes the skinny tiles cut by the stream-K split of the leftover
+// tiles: workgroup b takes the piece boundary q = b / 2 + 1 (phase 32 first,
+// then phase 64) and, if that boundary is the first one inside a tile, sums
+// the tile's parts (pieces in order) for 32 of its rows (half b % 2) and
+// applies the whole-tile epilogue.
+constexpr int kSkFixupHalves = 2;
+
+template <int MODE, int SKM>
+__device__ __forceinline__ void skinny_fixup(int G, int ntiles_n, int H, int F, int P, int b,
+                                             const int32_t* __restrict__ sched,
+                                             const int32_t* __restrict__ vrow,
+                                             const float* __restrict__ part,
+                                             uint16_t* __restrict__ out,
+                                             uint16_t* __restrict__ gu_out)
+{
+    using SK = Skinny<SKM>;
+    auto ssched = [&](int i) { return i <= G ? sched[SK::kSchedOff * (G + 1) + i] : sched[i]; };
+    const int KT = (MODE == kGateUp ? H : F) / kTK;
+    const int total = ssched(G) * ntiles_n;
+    if (total == 0) return;
+    const int nfull = sk_full_tiles(total, P);  // tiles done whole, in rounds
+    const SkCut cut = sk_cut(total - nfull, KT, P);
+    const int qb = b / kSkFixupHalves + 1;    // boundary between pieces qb - 1 and qb
+    const int half = b % kSkFixupHalves;
+    if (qb >= cut.Pe || half * 32 >= SKM) return;
+    const int64_t gb = cut.first(qb);
+    const int t = (int)(gb / KT);
+    const int64_t t0 = (int64_t)t * KT, t1 = t0 + KT;
+    if (gb == t0) return;                          // the boundary is between tiles
+    if (cut.first(qb - 1) > t0) return;            // an earlier boundary cuts this tile
+    const TileRef r = tile_of<MODE>(nfull + t, G, ntiles_n, [&](int i) { return ssched(i); });
+    const int q_lo = cut.piece_of(t0), q_hi = cut.piece_of(t1 - 1);
+    constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
+    constexpr int kRowsPerPass = kThreads / kQuads;
+    const int c = (threadIdx.x % kQuads) * 4;
+    const int row_end = min(r.rows, half * 32 + 32);
+    // the parts' slots, in piece order (at most kSkMaxParts)
+    __shared__ int slot[kSkMaxParts];
+    const int np = q_hi - q_lo + 1;
+    if ((int)threadIdx.x < np) {
+        const int qq = q_lo + (int)threadIdx.x;
+        slot[threadIdx.x] = sk_slot(cut, qq, max(cut.first(qq), t0));
+    }
+    __syncthreads();
+    for (int row = half * 32 + threadIdx.x / kQuads; row < row_end; row += kRowsPerPass) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), u = a;
+        // eight parts' loads in flight at a time, summed in piece order
+        for (int i0 = 0; i0 < np; i0 += 8) {
+            float4 va[8], vu[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i0 + i < np) {
+                    const float* src = part + ((size_t)slot[i0 + i] * SKM + row) * kTN + c;
+                    va[i] = *reinterpret_cast<const float4*>(src);
+                    if (MODE == kGateUp) vu[i] = *reinterpret_cast<const float4*>(src + kTN / 2);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i0 + i < np) {
+                    a.x += va[i].x; a.y += va[i].y; a.z += va[i].z; a.w += va[i].w;
+                    if (MODE == kGateUp) {
+                        u.x += vu[i].x; u.y += vu[i].y; u.z += vu[i].z; u.w += vu[i].w;
+                    }
+                }
+            }
+        }
+        uint2 pk;
+        if (MODE == kGateUp) {
+            if (r.n0 + c >= F) continue;
+            pk.x = moe::pack_bf16x2(fast_silu(a.x) * u.x, fast_silu(a.y) * u.y);
+            pk.y = moe::pack_bf16x2(fast_silu(a.z) * u.z, fast_silu(a.w) * u.w);
+            *reinterpret_cast<uint2*>(out + (size_t)(r.hrow0 + row) * F + r.n0 + c) = pk;
+            if (gu_out) {
+                uint16_t* d = gu_out + (size_t)(r.hrow0 + row) * 2 * F + r.n0 + c;
+                pk.x = moe::pack_bf16x2(a.x, a.y);
+                pk.y = moe::pack_bf16x2(a.z, a.w);
+                *reinterpret_cast<uint2*>(d) = pk;
+                pk.x = moe::pack_bf16x2(u.x, u.y);
+                pk.y = moe::pack_bf16x2(u.z, u.w);
+                *reinterpret_cast<uint2*>(d + F) = pk;
+            }
+        } else {
+            if (r.n0 + c >= H) continue;
+            pk.x = moe::pack_bf16x2(a.x, a.y);
+            pk.y = moe::pack_bf16x2(a.z, a.w);
+            *reinterpret_cast<uint2*>(out + (size_t)vrow[r.hrow0 + row] * H + r.n0 + c) = pk;
+        }
+    }
 }
 
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
@@ -978,15 +1181,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
 // tile b / 16, rows 16 (b % 16) .. +15; a thread owns one 4-column group.
 constexpr int kFixupRows = 16;
 constexpr int kFixupSlabs = kTM / kFixupRows;
+// split leftover tiles: at most half the persistent grid (each gets >= 2 parts)
+constexpr int kFixupGrid = moe::kGemmMaxGrid / 2 * kFixupSlabs;
 
+// Workgroups past the first kFixupGrid finish the skinny kernel's cut tiles
+// (P * kSkFixupHalves per tile height).
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, int H, int F, int P,
                                                          const int32_t* __restrict__ sched,
                                                          const int32_t* __restrict__ vrow,
                                                          const float* __restrict__ part,
+                                                         const float* __restrict__ part32,
+                                                         const float* __restrict__ part64,
                                                          uint16_t* __restrict__ out,
                                                          uint16_t* __restrict__ gu_out)
 {
+    if ((int)blockIdx.x >= kFixupGrid) {
+        const int b = (int)blockIdx.x - kFixupGrid, nb = P * kSkFixupHalves;
+        if (b < nb)
+            skinny_fixup<MODE, 32>(G, ntiles_n, H, F, P, b, sched, vrow, part32, out, gu_out);
+        else
+            skinny_fixup<MODE, 64>(G, ntiles_n, H, F, P, b - nb, sched, vrow, part64, out, gu_out);
+        return;
+    }
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
     const Balance bal = balance_of(sched[G] * ntiles_n, P, KT_all);
     const int lt = blockIdx.x / kFixupSlabs;
@@ -1171,8 +1388,6 @@ int persistent_grid()
     return grid;
 }
 
-// split leftover tiles: at most half the persistent grid (each gets >= 2 parts)
-constexpr int kFixupGrid = moe::kGemmMaxGrid / 2 * kFixupSlabs;
 
 int max_mtiles(const moe_shape_t& s, int bm, int G)
 {
@@ -1223,14 +1438,16 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const uint16_t* av = static_cast<const uint16_t*>(a);
         const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
         const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+        float* sk32 = reinterpret_cast<float*>(ws + W.skpart);
+        float* sk64 = sk32 + (size_t)2 * moe::kGemmMaxGrid * 32 * kTN;
         gemm_skinny_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
-                                                             wu, g.wtab, h, gu_out);
+                                                             wu, g.wtab, h, gu_out, sk32, sk64);
         gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
                                                            wu, g.wtab, h, part, gu_out);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        fixup_kernel<kGateUp><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow,
-                                                                part, h, gu_out);
+        fixup_kernel<kGateUp><<<kFixupGrid + 2 * P * kSkFixupHalves, kThreads, 0, st>>>(
+            g.G, ntn, s.H, s.F, P, sched, vrow, part, sk32, sk64, h, gu_out);
     } else {
         const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.F + kFM - 1) / kFM;
@@ -1256,14 +1473,16 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
         const uint16_t* hv = reinterpret_cast<const uint16_t*>(ws + W.h);
         const uint16_t* wd = static_cast<const uint16_t*>(w_down);
         uint16_t* yv = static_cast<uint16_t*>(y);
+        float* sk32 = reinterpret_cast<float*>(ws + W.skpart);
+        float* sk64 = sk32 + (size_t)2 * moe::kGemmMaxGrid * 32 * kTN;
         gemm_skinny_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                           nullptr, g.wtab, yv, nullptr);
+                                                           nullptr, g.wtab, yv, nullptr, sk32, sk64);
         gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
                                                          nullptr, g.wtab, yv, part, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        fixup_kernel<kDown><<<kFixupGrid, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, P, sched, vrow, part,
-                                                              yv, nullptr);
+        fixup_kernel<kDown><<<kFixupGrid + 2 * P * kSkFixupHalves, kThreads, 0, st>>>(
+            g.G, ntn, s.H, s.F, P, sched, vrow, part, sk32, sk64, yv, nullptr);
     } else {
         const int mtiles = max_mtiles(s, kFM, g.G);
         const int nt = (s.H + kFM - 1) / kFM;
