@@ -3,12 +3,17 @@ SwiGLU expert FFN with the replicas' weight gradients summed into the home
 expert, dispatch, gate) against the CPU oracle, whose backward is pinned by
 central differences of the forward.
 
+Each backward entry point is fed the same inputs as the oracle's step: the
+oracle's forward integers, permuted rows and gate weights (uploaded to the
+device) and seeded upstream gradients. The whole chain is also run on the
+device from the GPU forward's own buffers and compared with the oracle's
+chain from the layer's inputs.
+
 Bar (bf16 layers): bf16 outputs (dy, dbuf, dx) and the weight gradients --
 fp32 stores, but computed through the bf16-rounded g, u, dg, du and h --
-within 2e-2 * max|ref|; dw and dlogits (fp32 from bf16 inputs) within
-1e-5 * max|ref|. fp32 layers (the hotspot fixture and a random small shape):
-everything within 1e-5 * max|ref|.
-The oracle runs in double on the GPU's own bf16 inputs of each step.
+within 2e-2 * max|ref|; dw and dlogits (fp32 from identical inputs) within
+1e-5 * max|ref|; the chain within 2e-2 * max|ref|. fp32 layers (the hotspot
+fixture and a random small shape): everything within 1e-5 * max|ref|.
 Full-size shapes check sampled rows of dbuf and sampled columns f of every
 weight gradient (the FFN splits over f, so the oracle on those columns gives
 the exact entries).
@@ -24,7 +29,8 @@ torch = pytest.importorskip("torch")
 import expert_load_balance_amd as moe  # noqa: E402
 from expert_load_balance_amd.layer import alloc  # noqa: E402
 
-from test_gpu_parity import DEV, assert_tol, host, make_weights, run_layer  # noqa: E402
+from test_gpu_parity import (DEV, assert_tol, host, make_weights, oracle_forward,  # noqa: E402
+                             run_layer, upload_bits, upload_plan)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,33 +40,70 @@ def _say(msg):
 
 
 class Backward:
-    """Forward through the layer, then every backward entry point."""
+    """The forward on the device (for the chain), the oracle's forward, and
+    every backward entry point on inputs both sides share."""
 
     def __init__(self, shape, lg, bias, seed):
         s = shape
         self.shape = s
         act = torch.bfloat16 if s.dtype == moe.MOE_BF16 else torch.float32
+        self.act = act
         self.x = synth.device_normal((s.T, s.H), 1.0, seed, act, DEV)
         self.wts = make_weights(s.E, s.F, s.H, s.dtype, seed)
         self.L = run_layer(s, lg, bias, self.x, self.wts)
-        L = self.L
+        o = oracle_forward(s, lg, bias, self.x)
+        self.o, self.pl = o, o["pl"]
+        # the oracle's forward on the device, and seeded upstream gradients
+        self.d_ids = torch.from_numpy(o["ids"]).to(DEV)
+        self.w32 = o["w"].astype(np.float32)
+        self.d_w = torch.from_numpy(self.w32).to(DEV)
+        self.d_dest = torch.from_numpy(o["dest"]).to(DEV)
+        self.d_buf = upload_bits(o["buf_bits"], act)
+        self.d_plan = upload_plan(o["pl"], s)
         self.dout = synth.device_normal((s.T, s.H), 1.0, seed + 100, act, DEV)
+        self.y_in = synth.device_normal((s.N, s.H), 0.5, seed + 101, act, DEV)
+        self.dy_in = synth.device_normal((s.N, s.H), 1.0, seed + 102, act, DEV)
+        self.dbuf_in = synth.device_normal((s.N, s.H), 1.0, seed + 103, act, DEV)
+        self.dw_in = synth.device_normal((s.T, s.k), 1.0, seed + 104, torch.float32, DEV)
+        # the four steps
         self.dy = alloc((s.N, s.H), act, DEV)
         self.dw = alloc((s.T, s.k), torch.float32, DEV)
-        moe.moe_combine_backward(s, self.dout, L.y, L.dest_row, L.w, self.dy, self.dw)
+        moe.moe_combine_backward(s, self.dout, self.y_in, self.d_dest, self.d_w, self.dy, self.dw)
         self.dbuf = alloc((s.N, s.H), act, DEV)
-        self.dW = [alloc((s.E, s.F, s.H), torch.float32, DEV), alloc((s.E, s.F, s.H), torch.float32, DEV),
-                   alloc((s.E, s.H, s.F), torch.float32, DEV)]
-        for t in self.dW:
-            t.fill_(float("nan"))                     # every entry must be written
+        self.dW = self.new_grads()
         self.ws = alloc((moe.moe_backward_workspace_bytes(s),), torch.uint8, DEV)
-        moe.moe_ffn_backward(s, L.buf, L.plan, *self.wts, self.dy, self.dbuf, *self.dW, self.ws)
+        moe.moe_ffn_backward(s, self.d_buf, self.d_plan, *self.wts, self.dy_in, self.dbuf,
+                             *self.dW, self.ws)
         self.dx = alloc((s.T, s.H), act, DEV)
-        moe.moe_permute_backward(s, self.dbuf, L.dest_row, self.dx)
+        moe.moe_permute_backward(s, self.dbuf_in, self.d_dest, self.dx)
         self.dlogits = alloc((s.T, s.E), torch.float32, DEV)
-        moe.moe_route_backward(s, L.ids, L.w, self.dw, self.dlogits)
+        moe.moe_route_backward(s, self.d_ids, self.d_w, self.dw_in, self.dlogits)
         torch.cuda.synchronize()
-        self.pl = {k_: host(v) for k_, v in moe.plan_tables(L.plan, s).items()}
+
+    def new_grads(self):
+        s = self.shape
+        dW = [alloc((s.E, s.F, s.H), torch.float32, DEV), alloc((s.E, s.F, s.H), torch.float32, DEV),
+              alloc((s.E, s.H, s.F), torch.float32, DEV)]
+        for t in dW:
+            t.fill_(float("nan"))                     # every entry must be written
+        return dW
+
+    def chain(self):
+        """The whole backward on the device from dout, through the GPU
+        forward's own y, rows, plan and gate weights."""
+        s, L = self.shape, self.L
+        dy = alloc((s.N, s.H), self.act, DEV)
+        dw = alloc((s.T, s.k), torch.float32, DEV)
+        moe.moe_combine_backward(s, self.dout, L.y, L.dest_row, L.w, dy, dw)
+        dbuf = alloc((s.N, s.H), self.act, DEV)
+        dW = self.new_grads()
+        moe.moe_ffn_backward(s, L.buf, L.plan, *self.wts, dy, dbuf, *dW, self.ws)
+        dx = alloc((s.T, s.H), self.act, DEV)
+        moe.moe_permute_backward(s, dbuf, L.dest_row, dx)
+        dl = alloc((s.T, s.E), torch.float32, DEV)
+        moe.moe_route_backward(s, L.ids, L.w, dw, dl)
+        torch.cuda.synchronize()
+        return dx, dl, dW
 
 
 SMALL = [
@@ -82,6 +125,10 @@ SMALL_F32 = [
 SMALL = [c + (moe.MOE_BF16,) for c in SMALL] + SMALL_F32
 
 
+def _f64(t):
+    return host(t).astype(np.float64)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_small(case):
     name, T, H, E, k, F, R, sb, dtype = case
@@ -94,63 +141,55 @@ def test_backward_small(case):
         bias = synth.zipf_bias(E, sb, 51).astype(np.float32) if sb else None
     act_tol = dtype                                 # bf16 outputs: bf16 bar; fp32: fp32 bar
     b = Backward(shape, lg, bias, 52)
-    L = b.L
-    dest = host(L.dest_row)
-    y = host(L.y).astype(np.float64)
-    w = host(L.w).astype(np.float64)
-    dout = host(b.dout).astype(np.float64)
-    # combine backward on the GPU's own y and w
-    dy_ref, dw_ref = oracle.combine_backward(dout, y, dest, w)
+    o = b.o
+    w = b.w32.astype(np.float64)
+    # combine backward
+    dy_ref, dw_ref = oracle.combine_backward(_f64(b.dout), _f64(b.y_in), o["dest"], w)
     assert_tol(host(b.dy), dy_ref, act_tol, "dy")
     assert_tol(host(b.dw), dw_ref, moe.MOE_F32, "dw")
-    # FFN backward on the GPU's buf and dy
-    buf = host(L.buf).astype(np.float64)
-    dyg = host(b.dy).astype(np.float64)
-    wh = [host(t).astype(np.float64) for t in b.wts]
-    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dyg, b.pl, *wh)
+    # FFN backward
+    wh = [_f64(t) for t in b.wts]
+    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(o["buf"], _f64(b.dy_in), o["pl"], *wh)
     assert_tol(host(b.dbuf), dbuf_ref, act_tol, "dbuf")
     for got, ref, nm in zip(b.dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
         g = host(got)
         assert np.isfinite(g).all(), nm
         assert_tol(g, ref, act_tol, nm)
-    idle = np.where(host(L.counts) == 0)[0]
+    idle = np.where(o["c"]["counts"] == 0)[0]
     for e in idle:                                   # experts nobody chose: zero gradients
         assert not host(b.dW[0][e]).any() and not host(b.dW[2][e]).any()
     # dispatch and gate backward
-    assert_tol(host(b.dx), oracle.permute_backward(host(b.dbuf).astype(np.float64), dest),
-               act_tol, "dx")
-    dl_ref = oracle.route_backward(host(L.ids), w, host(b.dw).astype(np.float64), E)
+    assert_tol(host(b.dx), oracle.permute_backward(_f64(b.dbuf_in), o["dest"]), act_tol, "dx")
+    dl_ref = oracle.route_backward(o["ids"], w, _f64(b.dw_in), E)
     assert_tol(host(b.dlogits), dl_ref, moe.MOE_F32, "dlogits")
     if name == "idle_experts":
         assert len(idle) > 0
 
 
 def test_backward_chain_against_the_oracle_layer():
-    """The whole chain from dout, every step in the oracle (double, from the
-    forward's bf16 inputs): dx, dlogits and the weight gradients."""
+    """The whole chain from dout on the device (from the GPU forward) against
+    every step in the oracle (double, from the layer's inputs): dx, dlogits
+    and the weight gradients."""
     T, H, E, k, F, R = 256, 128, 8, 2, 128, 4
     shape = moe.Shape(T, H, E, k, F, R, 1, moe.MOE_BF16)
     lg = synth.router_logits(T, E, 53)
     bias = synth.zipf_bias(E, 0.7, 53).astype(np.float32)
     b = Backward(shape, lg, bias, 54)
-    ids, w, _ = oracle.route(lg, bias, k)
-    c = oracle.count(ids, E, R)
-    pl = oracle.plan(c["counts"], R)
-    xh = host(b.x).astype(np.float64)
-    buf, dest, _ = oracle.permute(xh, ids, c["eidx"], pl)
-    wh = [host(t).astype(np.float64) for t in b.wts]
+    o = b.o
+    ids, w, pl, dest, buf = o["ids"], o["w"], o["pl"], o["dest"], o["buf"]
+    wh = [_f64(t) for t in b.wts]
     y = np.zeros((T * k, H))
     for e in range(E):
         rows = [r for p in range(pl["piece_num"][e])
                 for r in range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p])]
         if rows:
             y[rows] = oracle.ffn_rows(buf[rows], wh[0][e], wh[1][e], wh[2][e])
-    dy, dw = oracle.combine_backward(host(b.dout).astype(np.float64), y, dest, w)
+    dy, dw = oracle.combine_backward(_f64(b.dout), y, dest, w)
     dbuf, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dy, pl, *wh)
-    assert_tol(host(b.dx), oracle.permute_backward(dbuf, dest), moe.MOE_BF16, "dx (chain)")
-    assert_tol(host(b.dlogits), oracle.route_backward(ids, w, dw, E), moe.MOE_BF16,
-               "dlogits (chain)")
-    for got, ref, nm in zip(b.dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
+    dx, dl, dW = b.chain()
+    assert_tol(host(dx), oracle.permute_backward(dbuf, dest), moe.MOE_BF16, "dx (chain)")
+    assert_tol(host(dl), oracle.route_backward(ids, w, dw, E), moe.MOE_BF16, "dlogits (chain)")
+    for got, ref, nm in zip(dW, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
         assert_tol(host(got), ref, moe.MOE_BF16, nm + " (chain)")
 
 
@@ -163,8 +202,8 @@ def test_backward_full_size(name, maxvio):
     shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
     lg, bias = wl.logits_and_bias(name, maxvio)
     b = Backward(shape, lg, bias, w_["seed"])
-    L, pl = b.L, b.pl
-    counts = host(L.counts)
+    pl = b.pl
+    counts = b.o["c"]["counts"]
     for t, nm in zip(b.dW, ("dW_gate", "dW_up", "dW_down")):
         assert bool(torch.isfinite(t).all()), nm
     rng = np.random.default_rng(9)
@@ -172,8 +211,8 @@ def test_backward_full_size(name, maxvio):
     rows = np.array([r for p in range(pl["piece_num"][e])
                      for r in range(pl["piece_row"][e, p], pl["piece_row"][e, p] + pl["piece_cnt"][e, p])])
     assert pl["piece_num"][e] >= 1 and len(rows) == counts[e]
-    xr = host(L.buf[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
-    dyr = host(b.dy[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    xr = b.o["buf"][rows]
+    dyr = host(b.dy_in[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
     wg, wu, wd = (host(t[e]).astype(np.float64) for t in b.wts)
     # sampled columns f of the weight gradients (exact: the FFN splits over f)
     fs = np.sort(rng.choice(F, 6, replace=False))
@@ -206,17 +245,15 @@ def test_backward_with_saved_gate_up(case):
     L = b.L
     y2 = alloc((shape.N, H), torch.bfloat16, DEV)
     gu = alloc((shape.N, 2 * F), torch.bfloat16, DEV)
-    moe.moe_grouped_gemm_train(shape, L.buf, L.plan, *b.wts, y2, gu, L.ws)
+    moe.moe_grouped_gemm_train(shape, b.d_buf, b.d_plan, *b.wts, y2, gu, L.ws)
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), L.y.view(torch.int16))
     dbuf2 = alloc((shape.N, H), torch.bfloat16, DEV)
     dW2 = [torch.full_like(t, float("nan")) for t in b.dW]
-    moe.moe_ffn_backward(shape, L.buf, L.plan, *b.wts, b.dy, dbuf2, *dW2, b.ws, gu=gu)
+    moe.moe_ffn_backward(shape, b.d_buf, b.d_plan, *b.wts, b.dy_in, dbuf2, *dW2, b.ws, gu=gu)
     torch.cuda.synchronize()
-    buf = host(L.buf).astype(np.float64)
-    dyg = host(b.dy).astype(np.float64)
     wh = [host(t).astype(np.float64) for t in b.wts]
-    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(buf, dyg, b.pl, *wh)
+    dbuf_ref, dwg, dwu, dwd = oracle.expert_ffn_backward(b.o["buf"], _f64(b.dy_in), b.pl, *wh)
     assert_tol(host(dbuf2), dbuf_ref, moe.MOE_BF16, "dbuf (saved g|u)")
     for got, ref, nm in zip(dW2, (dwg, dwu, dwd), ("dW_gate", "dW_up", "dW_down")):
         assert_tol(host(got), ref, moe.MOE_BF16, nm + " (saved g|u)")
@@ -239,18 +276,16 @@ def test_backward_replica_reduction(case):
     lg = synth.router_logits(T, E, 57)
     bias = synth.zipf_bias(E, sb, 57).astype(np.float32)
     b = Backward(shape, lg, bias, 58)
-    L = b.L
     n = E // R
     rgrad = torch.full((moe.moe_replica_grad_bytes(shape) // 4,), float("nan"), dtype=torch.float32,
                        device=DEV)
     dW2 = [torch.full_like(t, float("nan")) for t in b.dW]
     dbuf2 = alloc((shape.N, H), torch.bfloat16, DEV)
-    moe.moe_ffn_backward_replicas(shape, L.buf, L.plan, *b.wts, b.dy, dbuf2, *dW2, rgrad, b.ws)
+    moe.moe_ffn_backward_replicas(shape, b.d_buf, b.d_plan, *b.wts, b.dy_in, dbuf2, *dW2, rgrad,
+                                  b.ws)
     torch.cuda.synchronize()
-    buf = host(L.buf).astype(np.float64)
-    dyg = host(b.dy).astype(np.float64)
     wh = [host(t).astype(np.float64) for t in b.wts]
-    rg, ru, rd, slots = oracle.replica_backward(buf, dyg, b.pl, *wh)
+    rg, ru, rd, slots = oracle.replica_backward(b.o["buf"], _f64(b.dy_in), b.pl, *wh)
     assert len(slots) > 0
     rv = host(rgrad).reshape(R, n, 3, F * H)
     for r in range(R):

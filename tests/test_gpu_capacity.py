@@ -75,10 +75,24 @@ class CapacityRun:
         assert int(self.err.item()) == 0
 
 
-def check_dispatch_and_plan(run, x_bits):
+def bits_to_f64(bits):
+    """Raw bf16 (int16) or fp32 (int32) bits as float64 values."""
+    if bits.dtype == np.int16:
+        return (bits.astype(np.int32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def check_dispatch_and_plan(run, x_bits, lg, bias):
+    """Bit-exact against the oracle's route, count, capacity dispatch and
+    repacking on the same inputs. Returns the oracle's (dest_row, buf as
+    float64, ids, gate weights, counts)."""
     s, cap = run.shape, run.cap
-    ids = host(run.ids)
-    buf, dest = oracle.capacity_dispatch(x_bits, ids, host(run.eidx), s.E, cap)
+    ids, w, _ = oracle.route(lg, bias, s.k)
+    c = oracle.count(ids, s.E, s.R)
+    np.testing.assert_array_equal(host(run.ids), ids, err_msg="ids")
+    np.testing.assert_array_equal(host(run.eidx), c["eidx"], err_msg="eidx")
+    np.testing.assert_array_equal(host(run.counts), c["counts"], err_msg="counts")
+    buf, dest = oracle.capacity_dispatch(x_bits, ids, c["eidx"], s.E, cap)
     np.testing.assert_array_equal(host(run.dest), dest, err_msg="dest_row")
     np.testing.assert_array_equal(host(raw_bits(run.buf)), buf, err_msg="buf (padding included)")
     # the capacity plan: expert e home on rank e / n, one piece of cap rows at e * cap
@@ -95,9 +109,9 @@ def check_dispatch_and_plan(run, x_bits):
     np.testing.assert_array_equal(host(t["seg_num"]), np.full(s.R, n))
     np.testing.assert_array_equal(host(t["seg_expert"])[:, :n], e.reshape(s.R, n))
     assert not (host(run.plan) == -7).any()
-    np.testing.assert_array_equal(host(run.mapping), oracle.repack(host(run.counts), s.R),
+    np.testing.assert_array_equal(host(run.mapping), oracle.repack(c["counts"], s.R),
                                   err_msg="mapping")
-    return dest
+    return dest, bits_to_f64(buf), ids, w, c["counts"]
 
 
 SMALL = [
@@ -121,18 +135,15 @@ def test_capacity_path_small(case):
     x = synth.device_normal((T, H), 1.0, 41, act, DEV)
     wts = make_weights(E, F, H, dtype, 6)
     run = CapacityRun(shape, lg, bias, x, wts, cf)
-    ids, w, _ = oracle.route(lg, bias, k)
-    np.testing.assert_array_equal(host(run.ids), ids)
-    dest = check_dispatch_and_plan(run, host(raw_bits(x)))
+    dest, bufh, ids, w, _ = check_dispatch_and_plan(run, host(raw_bits(x)), lg, bias)
     # the FFN over every row of the static buffer (padding rows give zeros)
     wg, wu, wd = (host(t) for t in wts)
-    bufh = host(run.buf)
     y_ref = np.concatenate([oracle.ffn_rows(bufh[e * run.cap:(e + 1) * run.cap], wg[e], wu[e], wd[e])
                             for e in range(E)])
     assert_tol(host(run.y), y_ref, dtype, "y")
     pad = np.abs(bufh).sum(1) == 0
     assert not host(run.y)[pad].any()
-    out_ref = oracle.combine(y_ref, dest, host(run.w).astype(np.float64))
+    out_ref = oracle.combine(y_ref, dest, w)
     assert_tol(host(run.out), out_ref, dtype, "out")
     if cf < 1.0:
         assert (dest < 0).any()          # the case really drops
@@ -148,12 +159,11 @@ def test_capacity_fixture_fp32():
     wts = make_weights(8, 128, 64, moe.MOE_F32, 1)
     run = CapacityRun(shape, lg, bias, x, wts, 1.25)
     assert run.cap == fix["capacity"] == 5
-    dest = check_dispatch_and_plan(run, host(raw_bits(x)))
-    ids = host(run.ids)
+    dest, bufh, ids, _, _ = check_dispatch_and_plan(run, host(raw_bits(x)), lg, bias)
     kept = np.bincount(ids.ravel()[dest.ravel() >= 0], minlength=8)
     np.testing.assert_array_equal(kept, fix["processed"])
     assert (dest < 0).sum() == sum(fix["overflow"]) == 5
-    pad = (np.abs(host(run.buf)).sum(1) == 0).reshape(8, 5).sum(1)
+    pad = (np.abs(bufh).sum(1) == 0).reshape(8, 5).sum(1)
     np.testing.assert_array_equal(pad, fix["padding"])
     # the page's repacking and its rank demand
     np.testing.assert_array_equal(host(run.mapping), [0, 1, 2, 3, 3, 2, 1, 0])
@@ -194,10 +204,7 @@ def test_capacity_full_size_sampled(name, maxvio, cf):
     x = synth.device_normal((w["T"], w["H"]), 1.0, w["seed"] * 7 + 1, torch.bfloat16, DEV)
     wts = make_weights(w["E"], w["F"], w["H"], moe.MOE_BF16, w["seed"])
     run = CapacityRun(shape, lg, bias, x, wts, cf)
-    ids, wgt, _ = oracle.route(lg, bias, shape.k)
-    np.testing.assert_array_equal(host(run.ids), ids)
-    dest = check_dispatch_and_plan(run, host(raw_bits(x)))
-    c = host(run.counts)
+    dest, _, ids, wgt, c = check_dispatch_and_plan(run, host(raw_bits(x)), lg, bias)
     st = oracle.stats(ids, c, shape.R, capacity_factor=cf)
     assert (dest < 0).sum() == st["overflow"]
     # FFN on sampled rows of the hottest and coldest non-empty expert and a
@@ -214,11 +221,16 @@ def test_capacity_full_size_sampled(name, maxvio, cf):
         assert_tol(y[rows], ref, moe.MOE_BF16, f"y expert {e}")
         if kept < run.cap:
             assert not y[e * run.cap + kept].any()     # a padding row
+    # the kept rows of the sampled tokens, from the oracle's FFN of their x rows
     toks = np.unique(np.linspace(0, shape.T - 1, 6).astype(int))
     d = dest[toks]
     keep = d >= 0
     yr = np.zeros((d.size, shape.H))
-    yr[keep.ravel()] = y[d[keep]]
+    flat = d.ravel()
+    src = np.repeat(toks, shape.k)
+    for e in sorted({int(r) // run.cap for r in flat[flat >= 0]}):
+        sel = np.nonzero((flat >= 0) & (flat // run.cap == e))[0]
+        yr[sel] = oracle.ffn_rows(xh[src[sel]], host(wts[0][e]), host(wts[1][e]), host(wts[2][e]))
     out_ref = oracle.combine(yr, np.where(keep, np.arange(d.size).reshape(d.shape), -1),
-                             host(run.w)[toks].astype(np.float64))
+                             wgt[toks].astype(np.float64))
     assert_tol(host(run.out)[toks], out_ref, moe.MOE_BF16, "out")

@@ -99,6 +99,35 @@ def raw_bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
+def oracle_forward(shape, lg, bias, x):
+    """The oracle's forward integers and gate weights on the same inputs:
+    ids, w (double), count dict, plan, and the permutation of x -- buf as the
+    raw bits of x's rows, dest_row, row_src -- plus buf as float64 values."""
+    ids, w, err = oracle.route(lg, bias, shape.k)
+    assert err == 0
+    c = oracle.count(ids, shape.E, shape.R)
+    pl = oracle.plan(c["counts"], shape.R)
+    bits, dest, src = oracle.permute(host(raw_bits(x)), ids, c["eidx"], pl)
+    return dict(ids=ids, w=w, c=c, pl=pl, buf_bits=bits, dest=dest, src=src,
+                buf=host(x).astype(np.float64)[src])
+
+
+def upload_plan(pl, shape):
+    """The oracle's plan tables as a device plan block (the layout
+    moe_plan_layout gives)."""
+    plan = alloc((moe.moe_plan_layout(shape)["total"],), torch.int32, DEV)
+    plan.fill_(-1)
+    views = moe.plan_tables(plan, shape)
+    for name in oracle.PLAN_TABLES:
+        views[name].copy_(torch.from_numpy(np.ascontiguousarray(pl[name], np.int32)))
+    return plan
+
+
+def upload_bits(bits, dtype):
+    """Host raw bits (int16 for bf16, int32 for fp32) as a device tensor of dtype."""
+    return torch.from_numpy(np.ascontiguousarray(bits)).to(DEV).view(dtype)
+
+
 def expert_rows(pl, e):
     """buf rows of expert e, in virtual-row order (pieces in rank order)."""
     rows = []

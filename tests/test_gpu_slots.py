@@ -21,7 +21,8 @@ torch = pytest.importorskip("torch")
 import expert_load_balance_amd as moe  # noqa: E402
 from expert_load_balance_amd.layer import alloc  # noqa: E402
 
-from test_gpu_parity import DEV, assert_tol, host, make_weights, raw_bits, run_layer  # noqa: E402
+from test_gpu_parity import (DEV, assert_tol, host, make_weights, oracle_forward,  # noqa: E402
+                             raw_bits, run_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,14 +65,16 @@ def check_pool(pool, shape, pl, wts):
 
 
 def slot_run(shape, lg, bias, seed, modify=None):
-    """route/count/plan/permute, prefetch, then the slot GEMM; returns host
-    arrays for the oracle comparison."""
+    """route/count/plan/permute, prefetch, then the slot GEMM on the device;
+    and the oracle's forward on the same inputs (its plan and permuted rows,
+    for the comparison)."""
     act = torch.bfloat16 if shape.dtype == moe.MOE_BF16 else torch.float32
     x = synth.device_normal((shape.T, shape.H), 1.0, seed, act, DEV)
     wts = make_weights(shape.E, shape.F, shape.H, shape.dtype, seed)
     L = run_layer(shape, lg, bias, x, wts)
-    gt = moe.plan_tables(L.plan, shape)
-    pl = {k: host(v) for k, v in gt.items()}
+    o = oracle_forward(shape, lg, bias, x)
+    pl = o["pl"]
+    L.oracle_buf = o["buf"]
     pool = make_pool(shape)
     moe.moe_prefetch_replicas(shape, L.plan, *wts, pool if pool.numel() > 1 else None)
     torch.cuda.synchronize()
@@ -106,10 +109,9 @@ def test_slots_small(case):
     L, pl, pool, wts, y = slot_run(shape, lg, bias, 42)
     if moe.moe_pool_bytes(shape):
         check_pool(pool, shape, pl, wts)
-    buf = host(L.buf).astype(np.float64)
     wh = [host(w).astype(np.float64) for w in wts]
-    ph = host(pool_view(pool, shape)).astype(np.float64) if moe.moe_pool_bytes(shape) else None
-    ref = oracle.slot_ffn(buf, pl, S, *wh, ph)
+    ph = oracle.prefetch(pl, S, *wh) if moe.moe_pool_bytes(shape) else None
+    ref = oracle.slot_ffn(L.oracle_buf, pl, S, *wh, ph)
     assert_tol(host(y), ref, dtype, "y (slots)")
 
 
@@ -128,9 +130,10 @@ def test_slot_gemm_reads_the_slots():
     L, pl, pool, wts, y = slot_run(shape, lg, bias, 44, modify=double_down)
     src = oracle.slot_sources(pl, shape.S)
     assert (src >= 0).any()                          # some segment reads a slot
-    buf = host(L.buf).astype(np.float64)
+    buf = L.oracle_buf
     wh = [host(w).astype(np.float64) for w in wts]
-    ph = host(pool_view(pool, shape)).astype(np.float64)
+    ph = oracle.prefetch(pl, shape.S, *wh)
+    double_down(ph, pl)                              # the same change on the oracle's pool
     ref = oracle.slot_ffn(buf, pl, shape.S, *wh, ph)
     assert_tol(host(y), ref, shape.dtype, "y (modified pool)")
     home = oracle.slot_ffn(buf, pl, 0, *wh, ph)
@@ -180,9 +183,8 @@ def test_slots_full_size(name, maxvio):
     j, e = int(src[r, i]), int(pl["seg_expert"][r, i])
     row0, cnt = int(pl["seg_row"][r, i]), int(pl["seg_cnt"][r, i])
     rows = np.unique(np.linspace(row0, row0 + cnt - 1, 6).astype(int))
-    wsl = [pv[r, j, q].float().cpu().numpy() for q in range(3)]
-    ref = oracle.ffn_rows(host(L.buf[rows]).astype(np.float64), wsl[0].reshape(F, H),
-                          wsl[1].reshape(F, H), wsl[2].reshape(H, F))
+    wsl = [host(wts[q][e]) for q in range(3)]      # a filled slot holds its expert's weights
+    ref = oracle.ffn_rows(L.oracle_buf[rows], wsl[0], wsl[1], wsl[2])
     assert_tol(host(y[rows]), ref, moe.MOE_BF16, f"replica rows of expert {e} on rank {r}")
 
 
