@@ -742,7 +742,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
         }
         Lu = Ln;
         u = un;
-#pragma unroll
         for (int i = 0; i < kRowLoads; ++i) rw[i] = nrw[i];
     }
     };

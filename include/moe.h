@@ -263,13 +263,15 @@ moe_status_t moe_gemm_down(const moe_shape_t *shape, const int32_t *d_plan, cons
  * slots in slot_expert[r] order (ascending expert id); slot j < min(S, n)
  * holds that expert's three projections. */
 
-/* Bytes of the slot pool for this shape: R * min(S, n) * 3 * F * H * dtype
+/* [MoonEP] paragraphs 3-4 (S prefetch slots per rank, one pool for every
+ * layer). Bytes of the slot pool for this shape: R * min(S, n) * 3 * F * H * dtype
  * bytes, laid out pool[r][j][q][F*H] with q = 0 gate [F][H], 1 up [F][H],
  * 2 down [H][F] (each exactly the home expert's slice). 0 on a bad shape or
  * when S = 0. */
 size_t moe_pool_bytes(const moe_shape_t *shape);
 
-/* The prefetch: copies, for every rank r and slot j < min(S, n) that the plan
+/* [MoonEP] paragraph 3 (the planned replicas' weights prefetched before the
+ * GEMM). The prefetch: copies, for every rank r and slot j < min(S, n) that the plan
  * fills (slot_expert[r][j] >= 0), that expert's gate, up and down slices into
  * pool[r][j], bit for bit. Slots without an expert are not written.
  *   d_plan the moe_plan block; d_w_gate, d_w_up dtype[E][F][H];
@@ -279,7 +281,9 @@ moe_status_t moe_prefetch_replicas(const moe_shape_t *shape, const int32_t *d_pl
                                    const void *d_w_gate, const void *d_w_up, const void *d_w_down,
                                    void *d_pool, size_t pool_bytes, moe_stream_t stream);
 
-/* moe_grouped_gemm as the R ranks would run it: one group per plan segment
+/* [Primer] phase (c) on each rank's local experts; [MoonEP] paragraph 4
+ * (with S = n slots every expert a rank computes is local).
+ * moe_grouped_gemm as the R ranks would run it: one group per plan segment
  * (rank r's i-th expert run, contiguous rows of d_a), each with its own
  * weights -- the slot pool[r][j] for a replica segment whose expert holds
  * slot j < min(S, n) of rank r, the home slices for a home segment and for
@@ -331,13 +335,13 @@ moe_status_t moe_stats(const moe_shape_t *shape, const int32_t *d_counts, const 
  * weight gradient. bf16 runs on MFMA; fp32 (small shapes such as the
  * hotspot fixture) on plain FMA kernels, one thread per output element. */
 
-/* Device workspace moe_ffn_backward needs: x and dy in expert order, the
+/* [Primer] phase (c) in reverse. Device workspace moe_ffn_backward needs: x and dy in expert order, the
  * recomputed g | u, dg | du and h (about N * (2H + 5F) * dtype bytes), a
  * schedule, a zero page and (bf16, few wide experts) fp32 partials of dx.
  * 0 on a bad shape. */
 size_t moe_backward_workspace_bytes(const moe_shape_t *shape);
 
-/* Combine backward. With out[t] = sum_j w[t][j] y[dest_row[t][j]]:
+/* [Primer] phase (d) in reverse. Combine backward. With out[t] = sum_j w[t][j] y[dest_row[t][j]]:
  *   dy[dest_row[t][j]] = w[t][j] * dout[t]   (bf16, one rounding)
  *   dw[t][j] = sum_h dout[t][h] * y[dest_row[t][j]][h]   (fp32 accumulate)
  * Rows of dy that no assignment names are not written (with the equal-load
@@ -348,7 +352,8 @@ moe_status_t moe_combine_backward(const moe_shape_t *shape, const void *d_dout, 
                                   const int32_t *d_dest_row, const float *d_w, void *d_dy,
                                   float *d_dw, moe_stream_t stream);
 
-/* SwiGLU expert FFN backward over the plan (the moe_grouped_gemm forward's
+/* [Primer] phase (c) in reverse; [MoonEP] paragraph 3 (every piece of an
+ * expert adds into its home expert's gradient). SwiGLU expert FFN backward over the plan (the moe_grouped_gemm forward's
  * adjoint): recomputes g | u from d_buf, then
  *   dh = dy W_down, dg = dh u s (1 + g (1 - s)), du = dh silu(g) (s the
  *   logistic of g), dbuf = dg W_gate + du W_up,
@@ -367,7 +372,7 @@ moe_status_t moe_ffn_backward(const moe_shape_t *shape, const void *d_buf, const
                               float *d_dw_up, float *d_dw_down, void *d_ws, size_t ws_bytes,
                               moe_stream_t stream);
 
-/* Bytes of the replica weight-gradient slots: R * n * 3 * F * H * 4 (fp32),
+/* [MoonEP] paragraph 3 (replica gradients reduced home). Bytes of the replica weight-gradient slots: R * n * 3 * F * H * 4 (fp32),
  * laid out [R][n][3][F*H] -- slot r*n + j holds the gradient of rank r's
  * j-th replica expert (slot_expert order), gate | up | down. 0 on a bad
  * shape. */
@@ -392,7 +397,7 @@ moe_status_t moe_ffn_backward_replicas(const moe_shape_t *shape, const void *d_b
                                        size_t rgrad_bytes, void *d_ws, size_t ws_bytes,
                                        moe_stream_t stream);
 
-/* The forward grouped GEMM of a training step: moe_grouped_gemm, and (bf16)
+/* [Primer] phase (c), training. The forward grouped GEMM of a training step: moe_grouped_gemm, and (bf16)
  * the gate and up projections kept in d_gu bf16[N][2F] (row x in expert
  * order -- the order moe_ffn_backward uses -- g in columns [0, F), u in
  * [F, 2F)), so that moe_ffn_backward(d_gu = this buffer) skips its
@@ -402,13 +407,13 @@ moe_status_t moe_grouped_gemm_train(const moe_shape_t *shape, const void *d_a,
                                     const void *d_w_up, const void *d_w_down, void *d_y,
                                     void *d_gu, void *d_ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Dispatch backward: dx[t] = sum_j dbuf[dest_row[t][j]] (fp32 accumulate in
+/* [Primer] phase (b) in reverse. Dispatch backward: dx[t] = sum_j dbuf[dest_row[t][j]] (fp32 accumulate in
  * j order, one rounding). d_dbuf dtype[N][H]; d_dest_row int32[T][k];
  * d_dx dtype[T][H] out. */
 moe_status_t moe_permute_backward(const moe_shape_t *shape, const void *d_dbuf,
                                   const int32_t *d_dest_row, void *d_dx, moe_stream_t stream);
 
-/* Gate backward: w is the softmax of the selected raw logits, so
+/* [Primer] phase (a) in reverse. Gate backward: w is the softmax of the selected raw logits, so
  *   dlogits[t][ids[t][j]] = w[t][j] * (dw[t][j] - sum_j' w[t][j'] dw[t][j']),
  * and 0 for experts not selected ([Interview] editor's note: the balancing
  * bias only selects; it has no gradient here). d_ids int32[T][k];
@@ -420,12 +425,13 @@ moe_status_t moe_route_backward(const moe_shape_t *shape, const int32_t *d_ids, 
  * [Primer] phase (a): the router scores every expert for every token. The
  * pages do not print the router; it is read as a linear layer. */
 
-/* Device workspace moe_router needs for this shape, in bytes: 0 when one
+/* [Primer] phase (a). Device workspace moe_router needs for this shape, in bytes: 0 when one
  * K-range covers H (fp32, or enough token tiles to fill the GPU); else
  * parts * T * E * 4 for the per-range fp32 partial logits. 0 on a bad shape. */
 size_t moe_router_workspace_bytes(const moe_shape_t *shape);
 
-/* logits[t][e] = sum_h x[t][h] * W_r[e][h], accumulated in fp32 (bf16 x and
+/* [Primer] phase (a): the router scores, read as a linear layer, then the
+ * top-k gating. logits[t][e] = sum_h x[t][h] * W_r[e][h], accumulated in fp32 (bf16 x and
  * W_r: MFMA; where H is split into K-ranges, the ranges' fp32 partial sums
  * are added in range order, so results are the same on every call; fp32: FMA
  * in h order), written to d_logits, then exactly moe_route on those logits
@@ -456,12 +462,14 @@ moe_status_t moe_bias_update(const moe_shape_t *shape, const int32_t *d_counts, 
  * from rank placement": a static expert -> rank mapping that pairs hot and
  * cold experts. */
 
-/* Per-expert capacity ceil(N / E * capacity_factor) (the moe_stats figure),
+/* [Hotspot] "Make expert capacity, overflow, and padding explicit".
+ * Per-expert capacity ceil(N / E * capacity_factor) (the moe_stats figure),
  * or -1 for an invalid shape or factor, or when E * capacity does not fit
  * int32. */
 int32_t moe_capacity_rows(const moe_shape_t *shape, double capacity_factor);
 
-/* Fixed-capacity dispatch into a static [E][cap] buffer. An expert keeps its
+/* [Hotspot] "Make expert capacity, overflow, and padding explicit".
+ * Fixed-capacity dispatch into a static [E][cap] buffer. An expert keeps its
  * first cap assignments in stable order: assignment (t,j) of expert e with
  * eidx v < cap goes to row e*cap + v; the others are dropped (dest_row -1).
  * Rows e*cap + v with v >= counts[e] are padding and are written as zeros.
@@ -472,7 +480,8 @@ moe_status_t moe_capacity_dispatch(const moe_shape_t *shape, int32_t cap, const 
                                    const void *d_x, const int32_t *d_ids, const int32_t *d_eidx,
                                    void *d_buf, int32_t *d_dest_row, moe_stream_t stream);
 
-/* The plan block (moe_plan_layout) of the capacity layout: expert e is home
+/* [Hotspot] "Make expert capacity, overflow, and padding explicit"; [Primer]
+ * phase (c). The plan block (moe_plan_layout) of the capacity layout: expert e is home
  * on rank e / (E/R) with one piece of cap rows at row e*cap, no replicas.
  * With it, moe_grouped_gemm over the shape {T = E*cap, k = 1, H, E, F, R, S,
  * dtype} runs the expert FFN over the whole static buffer, padding rows
@@ -480,14 +489,16 @@ moe_status_t moe_capacity_dispatch(const moe_shape_t *shape, int32_t cap, const 
 moe_status_t moe_capacity_plan(const moe_shape_t *shape, int32_t cap, int32_t *d_plan,
                                moe_stream_t stream);
 
-/* moe_combine over the capacity buffer: d_y dtype[E*cap][H]; dropped
+/* [Hotspot] "Make expert capacity, overflow, and padding explicit"; [Primer]
+ * phase (d). moe_combine over the capacity buffer: d_y dtype[E*cap][H]; dropped
  * assignments (dest_row -1) contribute nothing; other arguments as in
  * moe_combine. */
 moe_status_t moe_capacity_combine(const moe_shape_t *shape, int32_t cap, const void *d_y,
                                   const int32_t *d_dest_row, const float *d_w,
                                   const void *d_shared_y, void *d_out, moe_stream_t stream);
 
-/* Greedy balanced repacking: experts in order of decreasing demand (equal
+/* [Hotspot] "Separate expert demand from rank placement" (the proposed
+ * mapping). Greedy balanced repacking: experts in order of decreasing demand (equal
  * demand: lower id first) each go to the least-loaded rank that holds fewer
  * than E/R experts (equal load: lower rank). Reproduces the page's mapping
  * {0,7},{1,6},{2,5},{3,4} for the fixture demand. d_counts int32[E];
