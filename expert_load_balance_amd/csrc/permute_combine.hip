@@ -12,8 +12,12 @@
 // fully coalesced) and writes it to its k destination rows, so HBM sees the
 // algorithmic (T + N) * H * bytes. Combine reads the k rows it needs and
 // writes out[t] once: (N + T) * H * bytes (+ T * H * bytes with a shared
-// expert). Rows are contiguous, so register staging already gives whole
-// 64-byte-segment transactions; there is no transpose that LDS would help.
+// expert). Rows are contiguous in both source and destination, so staging
+// through registers already gives whole-line transactions; there is no
+// transpose or reuse that an LDS stage would serve. Measured on MI355X: the
+// dispatch of the DeepSeek-V3 shape (1.06 GB) runs at 5.6 TB/s of kernel
+// time, faster than the runtime's own device-to-device copy (5.3 TB/s on
+// 1 GiB), and its HBM counter bytes equal the algorithmic bytes (1.01x).
 #include "common.h"
 
 namespace {
