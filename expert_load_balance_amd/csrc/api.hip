@@ -20,9 +20,11 @@ moe_status_t check(const moe_shape_t* s)
     if (N * wide >= (int64_t(1) << 40)) return MOE_EINVAL;
     if (s->dtype == MOE_BF16) {
         if (s->H % 64 || s->F % 64) return MOE_EUNSUPPORTED;
-        // the GEMM addresses rows of the buffer and of one expert's weights
-        // with 32-bit byte offsets
-        if (N * s->H * 2 >= (int64_t(1) << 32) || (int64_t)s->F * s->H * 2 >= (int64_t(1) << 32))
+        // the GEMM addresses rows of the buffer, of one expert's weights and
+        // of one 256-row tile of h with 32-bit byte offsets, all below the
+        // out-of-range offset its padding rows take
+        const int64_t lim = (int64_t(1) << 32) - 128;
+        if (N * s->H * 2 >= lim || (int64_t)s->F * s->H * 2 >= lim || (int64_t)512 * s->F >= lim)
             return MOE_EUNSUPPORTED;
     } else if (s->dtype == MOE_F32) {
         if (s->H % 4 || s->F % 4) return MOE_EUNSUPPORTED;

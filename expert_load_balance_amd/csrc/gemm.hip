@@ -379,7 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     // Rows a lane needs from vrow, per unit: gate/up, the activation row of
     // each of its copies (slot row 8 (wave + 4 i) + lane / 8); down, the
     // output row of each of its accumulator blocks i (tile row
-    // wm * 128 + 32 i + lane % 32). Rows past the unit's end read row 0's.
+    // wm * 128 + 32 i + lane % 32). Rows past the unit's end look up row 0's
+    // (their A copies land zeros, see setup).
     constexpr int kRowLoads = MODE == kGateUp ? kCopiesWave : 4;
     auto load_rows = [&](const Unit& u, int* rw) {
 #pragma unroll
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
     // per-unit copy sources: uniform bases + per-lane 32-bit offsets. Copy
     // instruction q (0..31) of an operand fills slot rows 8q .. 8q+7; wave w
-    // issues q = w + 4 i; lane l takes row 8q + l/8, slot chunk l % 8.
+    // issues q = w + 4 i; lane l takes row 8q + l/8, slot chunk l % 8. A rows
+    // past the unit's end take the out-of-range offset and land as zeros.
     const char *abase = nullptr, *bbase0 = nullptr, *bbase1 = nullptr;
     uint32_t aoff[kCopiesWave], boff[kCopiesWave];
     auto setup = [&](const Unit& u, const int* rw) {
@@ -409,10 +411,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
             const int r = 8 * (wave + 4 * i) + (lane >> 3);
             const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
             if (MODE == kGateUp) {
-                aoff[i] = (uint32_t)rw[i] * (uint32_t)H * 2u + ch;
+                aoff[i] = r < u.rows ? (uint32_t)rw[i] * (uint32_t)H * 2u + ch : kZeroRow;
                 boff[i] = (uint32_t)min(u.n0 + (r & 127), F - 1) * (uint32_t)H * 2u + ch;
             } else {
-                aoff[i] = (uint32_t)min(r, u.rows - 1) * (uint32_t)F * 2u + ch;
+                aoff[i] = r < u.rows ? (uint32_t)r * (uint32_t)F * 2u + ch : kZeroRow;
                 boff[i] = (uint32_t)min(u.n0 + r, H - 1) * (uint32_t)F * 2u + ch;
             }
         }
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     // copies of stage st (gate/up: B instructions q < 16, i.e. i < 4, hold
     // gate rows)
     auto copy_a = [&](int st, int i) {
-        copy16(abase + st * (kTK * 2), aoff[i], slots_u + a_slot(st) + wave * 1024 + i * 4096);
+        copy16_or_zero(abase + st * (kTK * 2), aoff[i], slots_u + a_slot(st) + wave * 1024 + i * 4096);
     };
     auto copy_b = [&](int st, int i) {
         copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
@@ -906,7 +908,7 @@ __device__ __forceinline__ int skinny_phase(
         // gathered rows: gate/up, the activation row of each A copy (needed
         // for the copies); down, the output row of each accumulator block,
         // read after the first copies go out (rows past the tile's repeat its
-        // last)
+        // last; their A copies land zeros)
         int grow[kNB > SK::kACopies ? kNB : SK::kACopies];
         auto load_grow = [&]() {
 #pragma unroll
@@ -937,8 +939,9 @@ __device__ __forceinline__ int skinny_phase(
         for (int i = 0; i < SK::kACopies; ++i) {
             const int ra = 8 * (wave + 4 * i) + (lane >> 3);
             const uint32_t ch = (uint32_t)(((lane & 7) ^ swz(ra)) * 16);
-            aoff[i] = MODE == kGateUp ? (uint32_t)grow[i] * (uint32_t)H * 2u + ch
-                                      : (uint32_t)min(ra, rows - 1) * (uint32_t)F * 2u + ch;
+            aoff[i] = ra >= rows ? kZeroRow
+                      : MODE == kGateUp ? (uint32_t)grow[i] * (uint32_t)H * 2u + ch
+                                        : (uint32_t)ra * (uint32_t)F * 2u + ch;
         }
 #pragma unroll
         for (int i = 0; i < kCopiesWave; ++i) {
@@ -951,7 +954,7 @@ __device__ __forceinline__ int skinny_phase(
             const uint32_t slot = ring_u + (uint32_t)(st % kSkSlots) * kSkSlot;
 #pragma unroll
             for (int i = 0; i < SK::kACopies; ++i)
-                copy16(abase + st * (kTK * 2), aoff[i], slot + wave * 1024 + i * 4096);
+                copy16_or_zero(abase + st * (kTK * 2), aoff[i], slot + wave * 1024 + i * 4096);
 #pragma unroll
             for (int i = 0; i < kCopiesWave; ++i)
                 copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],

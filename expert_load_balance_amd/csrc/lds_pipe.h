@@ -34,6 +34,31 @@ __device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// The same copy through a buffer descriptor (base, byte range kCopyRange,
+// 32-bit data format: the gfx9 family's raw-buffer setting). A lane whose
+// offset is kZeroRow or more is out of the descriptor's range: the hardware
+// reads no memory for it and writes zeros to its 16 LDS bytes. Padding rows
+// of a ragged tile take kZeroRow, so their MFMAs multiply zeros (measured:
+// zero operands draw less power, and these MFMAs run at a higher clock).
+// Every other lane's offset must stay below kZeroRow.
+constexpr uint32_t kZeroRow = 0xFFFFFFF0u;
+constexpr uint32_t kCopyRange = kZeroRow;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_or_zero(const void* base, uint32_t voff, uint32_t lds)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    i32x4 rsrc;
+    rsrc[0] = (int32_t)(uint32_t)b;
+    rsrc[1] = (int32_t)(uint32_t)(b >> 32);  // stride 0, no swizzle
+    rsrc[2] = (int32_t)kCopyRange;
+    rsrc[3] = 0x00020000;  // data format 32
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // The same copy from a per-lane 64-bit address (no uniform base): for
 // operands whose rows come from several places (a zero page for padding).
 #pragma clang diagnostic push

@@ -81,7 +81,9 @@ typedef void *moe_stream_t; /* a hipStream_t */
  * Limits (checked by every entry point): 0 <= T, 1 <= k <= min(E, 64),
  * 1 <= E <= 256, 1 <= R <= 64, E % R == 0, 0 <= S, 1 <= H, 1 <= F,
  * T*k < 2^31, (T*k)*max(H,F) < 2^40.
- * MOE_BF16 additionally needs H % 64 == 0 and F % 64 == 0 (GEMM K-steps);
+ * MOE_BF16 additionally needs H % 64 == 0 and F % 64 == 0 (GEMM K-steps),
+ * and (T*k)*H*2, F*H*2 and 512*F below 2^32 - 128 (the GEMM addresses operand
+ * rows with 32-bit byte offsets); MOE_EUNSUPPORTED otherwise.
  * MOE_F32 needs H % 4 == 0 and F % 4 == 0 (16-byte rows). */
 typedef struct moe_shape {
     int32_t T;     /* tokens in the batch                                  */

@@ -50,6 +50,10 @@ def test_shape_validation(lib):
     assert moe.moe_check_shape(bf.replace(T=32767)) == 0           # N*H*2 just below 2^32
     assert moe.moe_check_shape(bf.replace(T=32768)) == 2           # N*H*2 == 2^32
     assert moe.moe_check_shape(bf.replace(T=16, F=262144)) == 2     # F*H*2 >= 2^32
+    # and one 256-row tile of h (256 x F): 512 F below 2^32 - 128
+    narrow = bf.replace(T=16, H=64)
+    assert moe.moe_check_shape(narrow.replace(F=(1 << 23) - 64)) == 0
+    assert moe.moe_check_shape(narrow.replace(F=1 << 23)) == 2
 
 
 def test_plan_layout_and_workspace(lib):
