@@ -319,25 +319,25 @@ __device__ __forceinline__ const T* group_w(const uint64_t* wtab, const T* base,
     return base + (size_t)g * F * H;
 }
 
+// The 256-row tiles on P workgroups of the launch, this one being bid
+// (0 <= bid < P, P a multiple of 8). slots: the whole LDS, A slots 0, 1,
+// then B slots 0, 1, 2.
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
-    int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
-    const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
-    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, float* __restrict__ part,
-    uint16_t* __restrict__ gu_out)
+__device__ __forceinline__ void main_tiles(
+    int P, int bid, char* slots, int G, int ntiles_n, int H, int F,
+    const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sched,
+    const int32_t* __restrict__ vrow, const uint16_t* __restrict__ w0,
+    const uint16_t* __restrict__ w1, const uint64_t* __restrict__ wtab,
+    uint16_t* __restrict__ out, float* __restrict__ part, uint16_t* __restrict__ gu_out)
 {
-    // the whole LDS: A slots 0, 1, then B slots 0, 1, 2
-    __shared__ __attribute__((aligned(1024))) char slots[(kASlots + kBSlots) * kOpBytes];
     auto sc = [&](int i) { return ldc(sched, i); };
 
     const int K = MODE == kGateUp ? H : F;
     const int KT_all = K / kTK;
-    const int P = gridDim.x;
     const Balance bal = balance_of(sc(G) * ntiles_n, P, KT_all);
     const int total = bal.full + bal.L * bal.S;
     const int per_xcd = P / 8;
-    const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int my_slot = (bid % 8) * per_xcd + bid / 8;
 
     const int tid = threadIdx.x;
     const int wave = uni(tid >> 6), lane = tid & 63;
@@ -832,7 +832,7 @@ __device__ __forceinline__ int skinny_phase(
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
-    float* __restrict__ part, char* ring, int qofs)
+    float* __restrict__ part, char* ring, int qofs, int P, int bid)
 {
     using SK = Skinny<SKM>;
     // down's 64-row tiles keep three slots (measured 1-5 % faster than four
@@ -848,13 +848,12 @@ __device__ __forceinline__ int skinny_phase(
     const int KT = (MODE == kGateUp ? H : F) / kTK;
     const int total = ssched(G) * ntiles_n;
     if (total == 0) return 0;
-    const int P = gridDim.x;
     // whole rounds of tiles first (workgroup slot w takes tiles w, w + P, ...),
     // then the stream-K pieces of the tiles left over
     const int nfull = sk_full_tiles(total, P);
     const SkCut cut = sk_cut(total - nfull, KT, P);
     const int per_xcd = P / 8;
-    const int my_slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int my_slot = (bid % 8) * per_xcd + bid / 8;
     const int q = (my_slot - qofs % P + P) % P;  // this workgroup's piece of the leftover
     int t_full = my_slot;
     int64_t g = cut.first(q);
@@ -1064,25 +1063,61 @@ __device__ __forceinline__ int skinny_phase(
     return cut.Pe;
 }
 
-// Both skinny tile sizes in one launch: the 32-row tiles, then the 64-row
-// ones on the workgroups the first phase left idle first.
 constexpr int kSkinnyRing = Skinny<32>::kSlots * Skinny<32>::kSlot > Skinny<64>::kSlots * Skinny<64>::kSlot
                                 ? Skinny<32>::kSlots * Skinny<32>::kSlot
                                 : Skinny<64>::kSlots * Skinny<64>::kSlot;
+constexpr int kGemmLds = kSkinnyRing > (kASlots + kBSlots) * kOpBytes ? kSkinnyRing
+                                                                      : (kASlots + kBSlots) * kOpBytes;
 
+// Relative cost of one K-stage of a tile, for splitting a launch between
+// skinny and 256-row tiles.
+#ifndef MOE_COST_MAIN
+#define MOE_COST_MAIN 1.6f
+#endif
+constexpr float kCostSk32 = 1.0f, kCostSk64 = 1.1f, kCostMain = MOE_COST_MAIN;
+
+// Workgroups of a launch of P that take the skinny tiles; the others take
+// the 256-row tiles, at the same time. A skinny tile streams its weights and
+// a 256-row one is bound by its MFMAs, so running both side by side overlaps
+// the two. The split follows the estimated work: a multiple of 8 (as many on
+// every XCD), at least 8 for either kind that has tiles. Every workgroup and
+// the fixup kernel compute the same split from the schedule.
+__device__ __forceinline__ int skinny_wgs(int G, int ntiles_n, int P, const int32_t* sched)
+{
+    const int tm = ldc(sched, G) * ntiles_n;
+    const int t32 = ldc(sched, Skinny<32>::kSchedOff * (G + 1) + G) * ntiles_n;
+    const int t64 = ldc(sched, Skinny<64>::kSchedOff * (G + 1) + G) * ntiles_n;
+    if (t32 + t64 == 0) return 0;
+    if (tm == 0) return P;
+    const float sk = kCostSk32 * (float)t32 + kCostSk64 * (float)t64;
+    const float mn = kCostMain * (float)tm;
+    const int ps = ((int)((float)P * sk / (sk + mn)) + 4) / 8 * 8;
+    return min(max(ps, 8), P - 8);
+}
+
+// The grouped GEMM of one projection: workgroups [0, Ps) take the skinny
+// tiles (32-row ones, then 64-row ones on the workgroups the first phase left
+// idle first), the rest the 256-row tiles.
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     int G, int ntiles_n, int H, int F, const uint16_t* __restrict__ a_src,
     const int32_t* __restrict__ sched, const int32_t* __restrict__ vrow,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
     const uint64_t* __restrict__ wtab, uint16_t* __restrict__ out, uint16_t* __restrict__ gu_out,
-    float* __restrict__ part32, float* __restrict__ part64)
+    float* __restrict__ part, float* __restrict__ part32, float* __restrict__ part64)
 {
-    __shared__ __attribute__((aligned(1024))) char ring[kSkinnyRing];
-    const int used = skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out,
-                                            gu_out, part32, ring, 0);
-    skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out, part64,
-                           ring, used);
+    __shared__ __attribute__((aligned(1024))) char lds[kGemmLds];
+    const int P = gridDim.x, b = blockIdx.x;
+    const int Ps = skinny_wgs(G, ntiles_n, P, sched);
+    if (b < Ps) {
+        const int used = skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab,
+                                                out, gu_out, part32, lds, 0, Ps, b);
+        skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out,
+                               part64, lds, used, Ps, b);
+        return;
+    }
+    main_tiles<MODE>(P - Ps, b - Ps, lds, G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out,
+                     part, gu_out);
 }
 
 // Finishes the skinny tiles cut by the stream-K split of the leftover
@@ -1198,16 +1233,17 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
                                                          uint16_t* __restrict__ out,
                                                          uint16_t* __restrict__ gu_out)
 {
+    const int Ps = skinny_wgs(G, ntiles_n, P, sched);
     if ((int)blockIdx.x >= kFixupGrid) {
-        const int b = (int)blockIdx.x - kFixupGrid, nb = P * kSkFixupHalves;
+        const int b = (int)blockIdx.x - kFixupGrid, nb = Ps * kSkFixupHalves;
         if (b < nb)
-            skinny_fixup<MODE, 32>(G, ntiles_n, H, F, P, b, sched, vrow, part32, out, gu_out);
+            skinny_fixup<MODE, 32>(G, ntiles_n, H, F, Ps, b, sched, vrow, part32, out, gu_out);
         else
-            skinny_fixup<MODE, 64>(G, ntiles_n, H, F, P, b - nb, sched, vrow, part64, out, gu_out);
+            skinny_fixup<MODE, 64>(G, ntiles_n, H, F, Ps, b - nb, sched, vrow, part64, out, gu_out);
         return;
     }
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
-    const Balance bal = balance_of(sched[G] * ntiles_n, P, KT_all);
+    const Balance bal = balance_of(sched[G] * ntiles_n, P - Ps, KT_all);
     const int lt = blockIdx.x / kFixupSlabs;
     if (bal.S == 1 || lt >= bal.L) return;
     const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, [&](int i) { return sched[i]; });
@@ -1442,10 +1478,8 @@ hipError_t moe_launch_gemm_gateup(const moe_shape_t& s, const void* a, const int
         const uint16_t* wu = static_cast<const uint16_t*>(w_up);
         float* sk32 = reinterpret_cast<float*>(ws + W.skpart);
         float* sk64 = sk32 + (size_t)2 * moe::kGemmMaxGrid * 32 * kTN;
-        gemm_skinny_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
-                                                             wu, g.wtab, h, gu_out, sk32, sk64);
         gemm_bf16_kernel<kGateUp><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, av, sched, vrow, wg,
-                                                           wu, g.wtab, h, part, gu_out);
+                                                           wu, g.wtab, h, gu_out, part, sk32, sk64);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         fixup_kernel<kGateUp><<<kFixupGrid + 2 * P * kSkFixupHalves, kThreads, 0, st>>>(
@@ -1477,10 +1511,8 @@ hipError_t moe_launch_gemm_down(const moe_shape_t& s, const int32_t* plan, const
         uint16_t* yv = static_cast<uint16_t*>(y);
         float* sk32 = reinterpret_cast<float*>(ws + W.skpart);
         float* sk64 = sk32 + (size_t)2 * moe::kGemmMaxGrid * 32 * kTN;
-        gemm_skinny_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                           nullptr, g.wtab, yv, nullptr, sk32, sk64);
         gemm_bf16_kernel<kDown><<<P, kThreads, 0, st>>>(g.G, ntn, s.H, s.F, hv, sched, vrow, wd,
-                                                         nullptr, g.wtab, yv, part, nullptr);
+                                                         nullptr, g.wtab, yv, nullptr, part, sk32, sk64);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         fixup_kernel<kDown><<<kFixupGrid + 2 * P * kSkFixupHalves, kThreads, 0, st>>>(
