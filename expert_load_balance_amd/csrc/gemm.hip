@@ -30,14 +30,27 @@ using namespace moe::lds;
 
 constexpr int kThreads = 256;
 
+// Relative cost of one K-stage of a bf16 tile on one CU: a skinny tile
+// streams 36 or 40 KB of operands (per-CU copy rate bound), a 256-row tile
+// runs 64 MFMAs per wave on 64 KB. For splitting a launch between the two
+// kinds (measured: 1.0 and 2.4 for the 256-row stage were both slower).
+constexpr float kCostSk32 = 1.0f, kCostSk64 = 1.1f, kCostMain = 1.6f;
+// Least share of that cost on skinny tiles for which the last rows of
+// larger groups go to skinny tiles (below it, the split's granularity of 8
+// workgroups decides the balance).
+constexpr float kTailMinShare = 1.0f / 16;
+
 // schedule layout inside the workspace region (int32), G groups (experts, or
 // plan segments; see moe::GemmGroups):
 //   [0 .. G]            tile_start: prefix of the group's M-tiles of bm rows
 //   [G+1 .. 2G+1]       row_start:  prefix of the group's rows c_g
-//   [2G+2 .. 3G+2]      prefix of (0 < c_g <= sk1): one sk1-row tile each
-//   [3G+3 .. 4G+3]      prefix of (sk1 < c_g <= sk2): one sk2-row tile each
-// Groups with a skinny tile get no M-tile (sk1 = sk2 = 0: every group is
-// cut into M-tiles).
+//   [2G+2 .. 3G+2]      prefix of (0 < t_g <= sk1): one sk1-row tile each
+//   [3G+3 .. 4G+3]      prefix of (sk1 < t_g <= sk2): one sk2-row tile each
+// Groups of at most sk2 rows get one skinny tile (t_g = c_g), larger ones
+// bm-row M-tiles. With tails, the last t_g = c_g mod bm rows of a larger
+// group go to one skinny tile instead when t_g <= sk2; tails are taken when
+// the skinny tiles then hold at least kTailMinShare of the estimated cost.
+// sk1 = sk2 = 0: every group is cut into M-tiles only.
 
 // rows of group g: by expert, the sum of its pieces; by segment, the
 // segment's count (group r*2n + i, none past seg_num[r])
@@ -70,17 +83,44 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(int G, int E, int R,
     __shared__ int32_t rs[moe::kMaxGroups + 1];
     const moe::PlanLayout L = moe::plan_layout(E, R);
     const int tid = threadIdx.x;
-    int v[2][4];
+    int cg[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int g = 2 * tid + h;
-        const int c = g < G ? group_rows(g, E, R, seg != 0, plan, L) : 0;
-        const bool t1 = c > 0 && c <= sk1;
-        const bool t2 = c > sk1 && c <= sk2;
-        v[h][0] = (t1 || t2) ? 0 : (c + bm - 1) / bm;
+        cg[h] = g < G ? group_rows(g, E, R, seg != 0, plan, L) : 0;
+    }
+    // the tiles with tails, summed over the groups: tails or not
+    int tm = 0, ts1 = 0, ts2 = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int full = cg[h] / bm, tail = cg[h] - full * bm;
+        tm += full + (tail > sk2 ? 1 : 0);
+        ts1 += tail > 0 && tail <= sk1 ? 1 : 0;
+        ts2 += tail > sk1 && tail <= sk2 ? 1 : 0;
+    }
+    sh[0][tid] = tm;
+    sh[1][tid] = ts1;
+    sh[2][tid] = ts2;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (tid < off)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) sh[q][tid] += sh[q][tid + off];
+        __syncthreads();
+    }
+    const float cost_sk = kCostSk32 * (float)sh[1][0] + kCostSk64 * (float)sh[2][0];
+    const bool tails = sk2 > 0 && cost_sk >= kTailMinShare * (cost_sk + kCostMain * (float)sh[0][0]);
+    __syncthreads();
+    int v[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = cg[h];
+        const int full = c / bm;
+        const int tail = tails || c <= sk2 ? c - full * bm : 0;  // rows for a skinny tile
+        v[h][0] = full + (tail > sk2 || (tail == 0 && c > full * bm) ? 1 : 0);
         v[h][1] = c;
-        v[h][2] = t1 ? 1 : 0;
-        v[h][3] = t2 ? 1 : 0;
+        v[h][2] = tail > 0 && tail <= sk1 ? 1 : 0;
+        v[h][3] = tail > sk1 && tail <= sk2 ? 1 : 0;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) sh[q][tid] = v[0][q] + v[1][q];
@@ -241,7 +281,9 @@ __host__ __device__ constexpr int read_order(int n) { return n == 0 ? 0 : n <= 4
 struct TileRef {
     int e, n0, rows, hrow0;
 };
-template <int MODE, typename SC>
+// SKINNY: t indexes a skinny-tile table (one tile per group and N-tile),
+// whose tile holds the group's rows past its whole M-tiles.
+template <int MODE, bool SKINNY = false, typename SC>
 __device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
 {
     int lo = 0, hi = E - 1;
@@ -254,7 +296,7 @@ __device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
     const int local = t - sc(lo) * ntiles_n;
     const int nt = local / mt_e, mt = local % mt_e;
     const int c_e = sc(E + 1 + lo + 1) - sc(E + 1 + lo);
-    const int v0 = mt * kTM;
+    const int v0 = SKINNY ? c_e / kTM * kTM : mt * kTM;
     TileRef r;
     r.e = lo;
     r.n0 = nt * (MODE == kGateUp ? kTN / 2 : kTN);
@@ -754,7 +796,8 @@ __device__ __forceinline__ void main_tiles(
 // ------------------------------------------------------- bf16, skinny ----
 // Experts with at most 64 rows (decode-like batches, cold experts under
 // skew) get one SKM-row tile per N-tile (SKM = 32 or 64) instead of a mostly
-// empty 256-row M-tile. Such a tile is bound by streaming the expert's
+// empty 256-row M-tile; so do the last 1..64 rows of a larger expert, past
+// its whole 256-row M-tiles. Such a tile is bound by streaming the expert's
 // weights, so its LDS stage holds only SKM rows of activations next to the
 // 32 KB weight tile and the ring is deeper: 4 stages (three stages of weight
 // copies in flight per CU; 160 KB for SKM = 64), 3 for down's SKM = 64.
@@ -898,7 +941,7 @@ __device__ __forceinline__ int skinny_phase(
     constexpr int kB1 = MODE == kGateUp ? 128 * 128 : 32 * 128;  // block 1 offset
 
     // the next segment's tile is looked up while this one's copies fly
-    TileRef rn = tile_of<MODE>(cur.t, G, ntiles_n, ssched);
+    TileRef rn = tile_of<MODE, true>(cur.t, G, ntiles_n, ssched);
     for (;;) {
         const int k0 = uni(cur.k0), nst = uni(cur.k1 - cur.k0), pslot = uni(cur.pslot);
         const bool whole = pslot < 0;
@@ -971,7 +1014,7 @@ __device__ __forceinline__ int skinny_phase(
         if (MODE == kDown) load_grow();
         Seg nxt;
         const bool more = next_seg(nxt);
-        if (more) rn = tile_of<MODE>(nxt.t, G, ntiles_n, ssched);
+        if (more) rn = tile_of<MODE, true>(nxt.t, G, ntiles_n, ssched);
 
         for (int s = 0; s < nst; ++s) {
             // stage s landed: this wave's copies of later stages issued so far
@@ -1069,13 +1112,6 @@ constexpr int kSkinnyRing = Skinny<32>::kSlots * Skinny<32>::kSlot > Skinny<64>:
 constexpr int kGemmLds = kSkinnyRing > (kASlots + kBSlots) * kOpBytes ? kSkinnyRing
                                                                       : (kASlots + kBSlots) * kOpBytes;
 
-// Relative cost of one K-stage of a tile, for splitting a launch between
-// skinny and 256-row tiles.
-#ifndef MOE_COST_MAIN
-#define MOE_COST_MAIN 1.6f
-#endif
-constexpr float kCostSk32 = 1.0f, kCostSk64 = 1.1f, kCostMain = MOE_COST_MAIN;
-
 // Workgroups of a launch of P that take the skinny tiles; the others take
 // the 256-row tiles, at the same time. A skinny tile streams its weights and
 // a 256-row one is bound by its MFMAs, so running both side by side overlaps
@@ -1150,7 +1186,7 @@ __device__ __forceinline__ void skinny_fixup(int G, int ntiles_n, int H, int F, 
     const int64_t t0 = (int64_t)t * KT, t1 = t0 + KT;
     if (gb == t0) return;                          // the boundary is between tiles
     if (cut.first(qb - 1) > t0) return;            // an earlier boundary cuts this tile
-    const TileRef r = tile_of<MODE>(nfull + t, G, ntiles_n, [&](int i) { return ssched(i); });
+    const TileRef r = tile_of<MODE, true>(nfull + t, G, ntiles_n, [&](int i) { return ssched(i); });
     const int q_lo = cut.piece_of(t0), q_hi = cut.piece_of(t1 - 1);
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
     constexpr int kRowsPerPass = kThreads / kQuads;

@@ -157,6 +157,12 @@ SMALL = [
     ("bf16_skinny_boundary", 64, 1024, 4, 2, 256, 2, 1, moe.MOE_BF16, 0.0),
     # skinny tiles with 1 and 2 K-stages (gate/up K = 64, down K = 128)
     ("bf16_skinny_short_k", 40, 64, 8, 2, 128, 4, 2, moe.MOE_BF16, 0.5),
+    # experts of 292, 322 and 286 rows: a 256-row M-tile each plus a 36-row
+    # tail (64-row skinny tile), a 66-row one (second M-tile) and a 30-row one
+    # (32-row skinny tile); the skinny tails are cut by the stream-K split
+    ("bf16_tails_mixed", 900, 256, 3, 1, 384, 3, 1, moe.MOE_BF16, 0.0),
+    # 291, 289, 278, 292 rows: tails of 35, 33, 22 and 36 rows over 16 K-stages
+    ("bf16_tails_long_k", 1150, 1024, 4, 1, 256, 4, 1, moe.MOE_BF16, 0.0),
 ]
 
 
@@ -174,6 +180,11 @@ def test_layer_small_full_parity(case):
     xh = host(x)
     ids, w, c, pl = check_integer_path(L, lg, bias, host(raw_bits(x)))
     dest_ref, src_ref = check_integer_path.perm
+    if dtype == moe.MOE_BF16:
+        cls = _tile_classes(c["counts"])
+        _say(f"[case] {name}: tiles {cls}")
+        if name.startswith("bf16_tails"):
+            assert cls["tail32"] > 0 and cls["tail64"] > 0, cls
     # FFN per expert on its rows, oracle in double from the same rounded inputs
     wg, wu, wd = (host(t) for t in wts)
     buf_ref = xh[src_ref]
@@ -418,9 +429,39 @@ FULL = [("mixtral", 0.2), ("a3b", 0), ("a3b", 0.2), ("a3b", 1), ("dsv3", 20), ("
 
 _WEIGHT_CACHE = {}
 # the bf16 grouped GEMM's tile heights: experts with up to 32 rows get one
-# 32-row tile, 33..64 rows one 64-row tile, more rows 256-row M-tiles
+# 32-row tile, 33..64 rows one 64-row tile, more rows 256-row M-tiles; when
+# the skinny tiles would then hold at least 1/16 of the estimated work
+# (per K-stage: 1.0 for a 32-row tile, 1.1 for a 64-row one, 1.6 for an
+# M-tile), the last c mod 256 <= 64 rows of a larger expert get a skinny
+# tile of their own instead of one more M-tile
 _SKINNY1, _SKINNY2, _MTILE = 32, 64, 256
 _ORACLE_THREADS = 8
+
+
+def _tile_classes(counts):
+    """How many tiles of each kind the bf16 grouped GEMM runs per N-tile:
+    skinny tiles of experts with at most 64 rows, 256-row M-tiles, and the
+    skinny tails of larger experts."""
+    tm = ts1 = ts2 = 0
+    for ce in (int(v) for v in counts):
+        full, tail = divmod(ce, _MTILE)
+        tm += full + (1 if tail > _SKINNY2 else 0)
+        ts1 += 1 if 0 < tail <= _SKINNY1 else 0
+        ts2 += 1 if _SKINNY1 < tail <= _SKINNY2 else 0
+    cost_sk = 1.0 * ts1 + 1.1 * ts2
+    tails = cost_sk >= (cost_sk + 1.6 * tm) / 16
+    cls = {"skinny32": 0, "skinny64": 0, "mtile": 0, "tail32": 0, "tail64": 0}
+    for ce in (int(v) for v in counts):
+        full, tail = divmod(ce, _MTILE)
+        if full and not tails:
+            cls["mtile"] += -(-ce // _MTILE)
+            continue
+        cls["mtile"] += full + (1 if tail > _SKINNY2 else 0)
+        if 0 < tail <= _SKINNY1:
+            cls["tail32" if full else "skinny32"] += 1
+        elif _SKINNY1 < tail <= _SKINNY2:
+            cls["tail64" if full else "skinny64"] += 1
+    return cls
 
 
 def _workload_tensors(name):
@@ -520,24 +561,18 @@ def test_full_size_sampled(name, maxvio):
     toks = _window_tokens(dest_ref, pl["win_off"], shape.T, 64)
     assert len(toks) >= min(64, shape.T)
     tok_rows = set(dest_ref[toks].ravel().tolist())
-    classes = {"skinny32": 0, "skinny64": 0, "mtile": 0}
+    classes = _tile_classes(counts)
     want = {}
     for e in range(shape.E):
         ce = int(counts[e])
         if ce == 0:
             continue
         rows = expert_rows(pl, e)
+        # one row per 128-row half of each M-tile, per 32-row block of a
+        # skinny tile or tail (the tiles as _tile_classes counts them)
         vr = []
-        if ce <= _SKINNY1:
-            classes["skinny32"] += 1
-            vr = _tile_sample_rows(ce, e)
-        elif ce <= _SKINNY2:
-            classes["skinny64"] += 1
-            vr = _tile_sample_rows(ce, e)
-        else:
-            for m0 in range(0, ce, _MTILE):
-                classes["mtile"] += 1
-                vr += [m0 + v for v in _tile_sample_rows(min(_MTILE, ce - m0), e * 131 + m0)]
+        for m0 in range(0, ce, _MTILE):
+            vr += [m0 + v for v in _tile_sample_rows(min(_MTILE, ce - m0), e * 131 + m0)]
         sel = set(rows[vr].tolist()) | (tok_rows & set(rows.tolist()))
         want[e] = np.array(sorted(sel), np.int64)
     _say(f"[case] full {name}@{maxvio}: tiles {classes}, {sum(len(v) for v in want.values())} "
