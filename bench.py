@@ -750,9 +750,8 @@ def main():
                      "unit": "GB/s" if hbm else "TFLOP/s",
                      "frac": r["gemm_hbm_frac"] if hbm else r["gemm_mfma_frac"],
                      "traffic": traffic_for(name, maxvio),
-                     "kernel": "routed grouped GEMM: schedule_kernel + gemm_skinny_kernel<0> + "
-                               "gemm_bf16_kernel<0> + fixup_kernel<0> + gemm_skinny_kernel<1> + "
-                               "gemm_bf16_kernel<1> + fixup_kernel<1>",
+                     "kernel": "routed grouped GEMM: schedule_kernel + gemm_bf16_kernel<0> + "
+                               "fixup_kernel<0> + gemm_bf16_kernel<1> + fixup_kernel<1>",
                      "ms_per_call": r["gemm_ms"]["mean"],
                      "bytes_per_call": r["gemm_bytes"], "flops_per_call": r["gemm_flops"],
                      "mfma_frac": r["gemm_mfma_frac"], "hbm_frac": r["gemm_hbm_frac"]},
