@@ -502,6 +502,14 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
     sy = L.shared_y if shared else None
     t_comb = time_flushed(moe.bind(moe.moe_combine, shape, L.y, L.dest_row, L.w, sy, L.out,
                                    stream=stream), flush)
+    # the runtime's device-to-device copy of as many bytes as the dispatch
+    # moves (half read, half written), timed the same way: the ceiling of a
+    # row move of this size, launch and ramp included
+    half = (T + T * k) * H * (2 if dtype == moe.MOE_BF16 else 4) // 2
+    cp_src = torch.empty(half, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    t_copy = time_flushed(lambda: cp_dst.copy_(cp_src), flush)
+    del cp_src, cp_dst
     route_ids = torch.empty_like(L.ids)
     route_w = torch.empty_like(L.w)
     route_err = torch.zeros_like(L.err)
@@ -555,6 +563,7 @@ def run_workload(name, maxvio, steps, warmup, capacity_factor=None, extras=True)
         else "mfma",
         gu_tflops=4.0 * N * H * F / gu_s / 1e12, dn_tflops=2.0 * N * H * F / dn_s / 1e12,
         permute_us=t_perm * 1e6, combine_us=t_comb * 1e6, route_us=t_route * 1e6,
+        copy_same_bytes_us=t_copy * 1e6,
         permute_hbm_frac=perm_bytes / t_perm / 1e9 / PEAK_HBM_GBS,
         combine_hbm_frac=comb_bytes / t_comb / 1e9 / PEAK_HBM_GBS,
         route_hbm_frac=route_bytes / t_route / 1e9 / PEAK_HBM_GBS,
@@ -598,6 +607,7 @@ def summary(q):
         "permute_hbm_frac": r4(q["permute_hbm_frac"]), "combine_hbm_frac": r4(q["combine_hbm_frac"]),
         "route_hbm_frac": r4(q["route_hbm_frac"]),
         "permute_us": round(q["permute_us"], 2), "combine_us": round(q["combine_us"], 2),
+        "copy_same_bytes_as_permute_us": round(q["copy_same_bytes_us"], 2),
         "route_us": round(q["route_us"], 2),
         "plan": {k_: q["stats"][k_] for k_ in ("planned_max", "planned_min", "replica_pieces",
                                                "max_slots_needed", "ranks_over_slots")},
