@@ -33,7 +33,9 @@ constexpr int kThreads = 256;
 // Relative cost of one K-stage of a bf16 tile on one CU: a skinny tile
 // streams 36 or 40 KB of operands (per-CU copy rate bound), a 256-row tile
 // runs 64 MFMAs per wave on 64 KB. For splitting a launch between the two
-// kinds (measured: 1.0 and 2.4 for the 256-row stage were both slower).
+// kinds. The 256-row cost was swept from 1.0 to 3.2 over six workloads:
+// 1.6-1.8 is best; from 2.0 up the skinny side gets 8 workgroups too few on
+// some and finishes last.
 constexpr float kCostSk32 = 1.0f, kCostSk64 = 1.1f, kCostMain = 1.6f;
 // Least share of that cost on skinny tiles for which the last rows of
 // larger groups go to skinny tiles (below it, the split's granularity of 8
@@ -796,14 +798,14 @@ __device__ __forceinline__ void main_tiles(
 // ------------------------------------------------------- bf16, skinny ----
 // Experts with at most 64 rows (decode-like batches, cold experts under
 // skew) get one SKM-row tile per N-tile (SKM = 32 or 64) instead of a mostly
-// empty 256-row M-tile; so do the last 1..64 rows of a larger expert, past
-// its whole 256-row M-tiles. Such a tile is bound by streaming the expert's
-// weights, so its LDS stage holds only SKM rows of activations next to the
-// 32 KB weight tile and the ring is deeper: 4 stages (three stages of weight
-// copies in flight per CU; 160 KB for SKM = 64), 3 for down's SKM = 64.
-// Same N-tiles, K stages, swizzle, copy wrapper and epilogues as the 256-row
-// kernel; 4 waves, each SKM rows x 64 B-rows (gate/up: 32 gate and the same
-// 32 up columns).
+// empty 256-row M-tile; when the schedule takes tails, so do the last 1..64
+// rows of a larger expert, past its whole 256-row M-tiles. Such a tile is
+// bound by streaming the expert's weights, so its LDS stage holds only SKM
+// rows of activations next to the 32 KB weight tile and the ring is deeper:
+// 4 stages (three stages of weight copies in flight per CU; 160 KB for
+// SKM = 64), 3 for down's SKM = 64. Same N-tiles, K stages, swizzle, copy
+// wrappers and epilogues as the 256-row tiles; 4 waves, each SKM rows x 64
+// B-rows (gate/up: 32 gate and the same 32 up columns).
 //
 // Balance: whole rounds of tiles go to the workgroups in turn (slot w takes
 // tiles w, w + P, ...); the n tiles left over (n < P), each KT stages deep,
@@ -1112,23 +1114,31 @@ constexpr int kSkinnyRing = Skinny<32>::kSlots * Skinny<32>::kSlot > Skinny<64>:
 constexpr int kGemmLds = kSkinnyRing > (kASlots + kBSlots) * kOpBytes ? kSkinnyRing
                                                                       : (kASlots + kBSlots) * kOpBytes;
 
-// Workgroups of a launch of P that take the skinny tiles; the others take
-// the 256-row tiles, at the same time. A skinny tile streams its weights and
-// a 256-row one is bound by its MFMAs, so running both side by side overlaps
-// the two. The split follows the estimated work: a multiple of 8 (as many on
-// every XCD), at least 8 for either kind that has tiles. Every workgroup and
-// the fixup kernel compute the same split from the schedule.
-__device__ __forceinline__ int skinny_wgs(int G, int ntiles_n, int P, const int32_t* sched)
+// How a launch of P workgroups splits between the two kinds of tile: the
+// first ps take the skinny tiles and the other pm the 256-row tiles, at the
+// same time. A skinny tile streams its weights and a 256-row one is bound by
+// its MFMAs, so running both side by side overlaps the two. The split
+// follows the estimated work: a multiple of 8 (as many on every XCD), at
+// least 8 for either kind that has tiles. Below 16 workgroups both kinds
+// cannot have 8: then every workgroup takes the skinny tiles and then the
+// 256-row ones (serial; ps = pm = P). Every workgroup and the fixup kernel
+// compute the same split from the schedule.
+struct Split {
+    int ps, pm;
+    bool serial;
+};
+__device__ __forceinline__ Split gemm_split(int G, int ntiles_n, int P, const int32_t* sched)
 {
     const int tm = ldc(sched, G) * ntiles_n;
     const int t32 = ldc(sched, Skinny<32>::kSchedOff * (G + 1) + G) * ntiles_n;
     const int t64 = ldc(sched, Skinny<64>::kSchedOff * (G + 1) + G) * ntiles_n;
-    if (t32 + t64 == 0) return 0;
-    if (tm == 0) return P;
+    if (t32 + t64 == 0) return Split{0, P, false};
+    if (tm == 0) return Split{P, 0, false};
+    if (P < 16) return Split{P, P, true};
     const float sk = kCostSk32 * (float)t32 + kCostSk64 * (float)t64;
     const float mn = kCostMain * (float)tm;
-    const int ps = ((int)((float)P * sk / (sk + mn)) + 4) / 8 * 8;
-    return min(max(ps, 8), P - 8);
+    const int ps = min(max(((int)((float)P * sk / (sk + mn)) + 4) / 8 * 8, 8), P - 8);
+    return Split{ps, P - ps, false};
 }
 
 // The grouped GEMM of one projection: workgroups [0, Ps) take the skinny
@@ -1144,16 +1154,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 {
     __shared__ __attribute__((aligned(1024))) char lds[kGemmLds];
     const int P = gridDim.x, b = blockIdx.x;
-    const int Ps = skinny_wgs(G, ntiles_n, P, sched);
-    if (b < Ps) {
+    const Split sp = gemm_split(G, ntiles_n, P, sched);
+    if (b < sp.ps) {
         const int used = skinny_phase<MODE, 32>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab,
-                                                out, gu_out, part32, lds, 0, Ps, b);
+                                                out, gu_out, part32, lds, 0, sp.ps, b);
         skinny_phase<MODE, 64>(G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, gu_out,
-                               part64, lds, used, Ps, b);
-        return;
+                               part64, lds, used, sp.ps, b);
+        if (!sp.serial) return;
     }
-    main_tiles<MODE>(P - Ps, b - Ps, lds, G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out,
-                     part, gu_out);
+    // (the skinny phases end with every copy landed and a barrier, so the
+    // LDS is free here in the serial case)
+    const int mb = sp.serial ? b : b - sp.ps;
+    main_tiles<MODE>(sp.pm, mb, lds, G, ntiles_n, H, F, a_src, sched, vrow, w0, w1, wtab, out, part,
+                     gu_out);
 }
 
 // Finishes the skinny tiles cut by the stream-K split of the leftover
@@ -1269,17 +1282,18 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
                                                          uint16_t* __restrict__ out,
                                                          uint16_t* __restrict__ gu_out)
 {
-    const int Ps = skinny_wgs(G, ntiles_n, P, sched);
+    const Split sp = gemm_split(G, ntiles_n, P, sched);
     if ((int)blockIdx.x >= kFixupGrid) {
-        const int b = (int)blockIdx.x - kFixupGrid, nb = Ps * kSkFixupHalves;
+        const int b = (int)blockIdx.x - kFixupGrid, nb = sp.ps * kSkFixupHalves;
         if (b < nb)
-            skinny_fixup<MODE, 32>(G, ntiles_n, H, F, Ps, b, sched, vrow, part32, out, gu_out);
+            skinny_fixup<MODE, 32>(G, ntiles_n, H, F, sp.ps, b, sched, vrow, part32, out, gu_out);
         else
-            skinny_fixup<MODE, 64>(G, ntiles_n, H, F, Ps, b - nb, sched, vrow, part64, out, gu_out);
+            skinny_fixup<MODE, 64>(G, ntiles_n, H, F, sp.ps, b - nb, sched, vrow, part64, out,
+                                   gu_out);
         return;
     }
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
-    const Balance bal = balance_of(sched[G] * ntiles_n, P - Ps, KT_all);
+    const Balance bal = balance_of(sched[G] * ntiles_n, sp.pm, KT_all);
     const int lt = blockIdx.x / kFixupSlabs;
     if (bal.S == 1 || lt >= bal.L) return;
     const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, [&](int i) { return sched[i]; });
