@@ -219,6 +219,47 @@ def time_flushed(fn, flush, reps=30):
     return sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / reps
 
 
+def measured_peaks():
+    """Measured counterparts of the spec peaks: the bf16 MFMA rate of the
+    library's calibration probe (four workgroups per CU, registers only,
+    operands that change from one MFMA to the next) and the faster of two
+    1 GiB device-to-device copies (the runtime's and the library's streaming
+    copy probe), with the caches flushed before each."""
+    import torch
+
+    import expert_load_balance_amd as moe
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, iters = 4 * cus, 2048
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def probe():
+        moe.moe_probe_mfma(wg, iters, sink, stream=stream)
+
+    t_settle = time.perf_counter() + 0.2
+    while time.perf_counter() < t_settle:
+        probe()
+        torch.cuda.synchronize()
+    t_mfma = time_back_to_back(probe, reps=20)
+    flops = wg * 4 * 4 * iters * 2.0 * 32 * 32 * 16
+    flush = Flusher()
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t_rt = time_flushed(lambda: b.copy_(a), flush, reps=10)
+    t_probe = time_flushed(lambda: moe.moe_probe_copy(a, b, 8 * cus, stream=stream), flush, reps=10)
+    del a, b, flush, sink
+    torch.cuda.empty_cache()
+    rt, pr = 2.0 * (1 << 30) / t_rt / 1e9, 2.0 * (1 << 30) / t_probe / 1e9
+    return {"mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
+            "hbm_copy_gbs": round(max(rt, pr), 1),
+            "hbm_copy_runtime_gbs": round(rt, 1), "hbm_copy_probe_gbs": round(pr, 1),
+            "how": f"moe_probe_mfma: {wg} workgroups x 4 waves x {4 * iters} "
+                   "v_mfma_f32_32x32x16_bf16, back to back; 1 GiB device copy (read + write) by "
+                   f"the runtime and by moe_probe_copy ({8 * cus} workgroups), the faster one, "
+                   "512 MB flush before each"}
+
+
 def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shared=None):
     """The same layer through the fixed-capacity baseline: route, count,
     dispatch into [E][cap] (drop and pad), the expert FFN over the whole
@@ -769,6 +810,12 @@ def main():
     rec.update({k_: v_ for k_, v_ in summary(r).items()
                 if k_ not in ("tokens_per_s", "ms_per_step")})
     rec["gemm_src_sha16"] = kernel_src_sha()
+    if not args.layer_only:
+        mp = measured_peaks()
+        rec["measured_peaks"] = mp
+        rec["roofline"]["frac_of_measured_peak"] = (
+            r["gemm_gbs"] / mp["hbm_copy_gbs"] if hbm else r["gemm_tflops"] / mp["mfma_bf16_tflops"])
+        rec["roofline"]["mfma_frac_of_measured_peak"] = r["gemm_tflops"] / mp["mfma_bf16_tflops"]
     if not args.no_cpu_baseline:
         lg_np, bias_np, x, wts, shared = r["inputs"]
         rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, shared,

@@ -24,8 +24,8 @@ __all__ = [
     "bind", "moe_pool_bytes", "moe_prefetch_replicas", "moe_grouped_gemm_slots",
     "moe_backward_workspace_bytes", "moe_combine_backward", "moe_ffn_backward",
     "moe_permute_backward", "moe_route_backward", "moe_grouped_gemm_train",
-    "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
-    "EXPORTED_SYMBOLS",
+    "moe_replica_grad_bytes", "moe_ffn_backward_replicas", "moe_probe_mfma",
+    "moe_probe_copy", "EXPORTED_SYMBOLS",
 ]
 
 MOE_F32 = 0
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
     "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
-    "moe_count_noalloc",
+    "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -131,6 +131,8 @@ def load():
         "moe_route": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_count": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_count_noalloc": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_probe_mfma": (st, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
+        "moe_probe_copy": (st, [_VP, _VP, ctypes.c_size_t, ctypes.c_int32, _VP]),
         "moe_plan": (st, [_SP, _VP, _VP, _VP]),
         "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -304,6 +306,27 @@ def moe_count(shape, ids, counts, offsets, eidx, rank_load, err, ws, stream=None
             _ptr(rank_load, i32, "rank_load", shape.R), _ptr(err, i32, "err", 1),
             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _ok(load().moe_count(*args), "moe_count")
+
+
+def moe_probe_mfma(workgroups, iters, sink, stream=None):
+    """The calibration probe: workgroups x 4 waves x 4 * iters bf16 MFMAs
+    (32x32x16) on registers only; sink: float32 tensor of at least
+    workgroups * 256 elements."""
+    import torch
+
+    args = (int(workgroups), int(iters), _ptr(sink, torch.float32, "sink"), sink.numel(),
+            _stream(stream))
+    _ok(load().moe_probe_mfma(*args), "moe_probe_mfma")
+
+
+def moe_probe_copy(src, dst, workgroups, stream=None):
+    """The HBM calibration probe: copies src into dst (same byte size, a
+    multiple of 16) with `workgroups` workgroups."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    args = (_ptr(src, None, "src"), _ptr(dst, None, "dst"), nbytes, int(workgroups), _stream(stream))
+    _ok(load().moe_probe_copy(*args), "moe_probe_copy")
 
 
 def moe_count_noalloc(shape, ids, counts, offsets, eidx, rank_load, err, stream=None):

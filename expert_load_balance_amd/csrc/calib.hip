@@ -1,0 +1,114 @@
+// calib.hip -- calibration probes for the measurements, the measured
+// counterparts of the spec peaks the rooflines divide by: the bf16 MFMA rate
+// this GPU sustains with no memory traffic at all, and a plain streaming
+// copy for HBM.
+//
+// Every wave runs four independent accumulator chains of
+// v_mfma_f32_32x32x16_bf16, each on its own pair of operands, so
+// consecutive MFMAs switch inputs the way a GEMM's do: the matrix cores
+// draw the power of real data (operands that never change draw less and
+// run at a higher clock under the power limit).
+#include "common.h"
+
+namespace {
+
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kProbeThreads = 256;
+constexpr int kChains = 4;
+
+// eight bf16 values of magnitude in [2^-7, 2^-6) with hashed sign and
+// mantissa bits (no zeros, no specials)
+__device__ __forceinline__ probe_bf16x8 operand(unsigned seed)
+{
+    probe_bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        unsigned h = (seed * 8u + (unsigned)i + 1u) * 2654435761u;
+        h ^= h >> 13;
+        h *= 0x85ebca6bu;
+        h ^= h >> 16;
+        const unsigned short bits =
+            (unsigned short)(((h >> 8) & 0x8000u) | (120u << 7) | (h & 0x7fu));
+        v[i] = __builtin_bit_cast(__bf16, bits);
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters,
+                                                                  float* __restrict__ sink)
+{
+    const unsigned id = blockIdx.x * kProbeThreads + threadIdx.x;
+    probe_bf16x8 a[kChains], b[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+        a[c] = operand(id * 2u * kChains + 2u * c);
+        b[c] = operand(id * 2u * kChains + 2u * c + 1u);
+    }
+    probe_f32x16 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[c][q] = 0.0f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s += acc[c][q];
+    sink[id] = s;  // keeps every chain live
+}
+
+// a streaming copy: each thread moves kCopyVecs 16-byte vectors per round
+// (all loads issued before the stores), rounds striding over the grid
+constexpr int kCopyVecs = 4;
+
+__global__ __launch_bounds__(kProbeThreads) void copy_probe_kernel(const uint4* __restrict__ src,
+                                                                  uint4* __restrict__ dst,
+                                                                  int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * kProbeThreads * kCopyVecs;
+    for (int64_t base = ((int64_t)blockIdx.x * kProbeThreads) * kCopyVecs + threadIdx.x; base < n;
+         base += stride) {
+        uint4 v[kCopyVecs];
+#pragma unroll
+        for (int j = 0; j < kCopyVecs; ++j) {
+            const int64_t i = base + (int64_t)j * kProbeThreads;
+            if (i < n) v[j] = src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kCopyVecs; ++j) {
+            const int64_t i = base + (int64_t)j * kProbeThreads;
+            if (i < n) dst[i] = v[j];
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_probe_copy(const void* d_src, void* d_dst, size_t bytes,
+                                       int32_t workgroups, moe_stream_t stream)
+{
+    if (d_src == nullptr || d_dst == nullptr || bytes == 0 || bytes % 16 != 0 || workgroups < 1 ||
+        reinterpret_cast<uintptr_t>(d_src) % 16 != 0 || reinterpret_cast<uintptr_t>(d_dst) % 16 != 0)
+        return MOE_EINVAL;
+    copy_probe_kernel<<<workgroups, kProbeThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint4*>(d_src), static_cast<uint4*>(d_dst), (int64_t)(bytes / 16));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}
+
+extern "C" moe_status_t moe_probe_mfma(int32_t workgroups, int32_t iters, float* d_sink,
+                                       size_t sink_floats, moe_stream_t stream)
+{
+    if (workgroups < 1 || iters < 1 || d_sink == nullptr ||
+        sink_floats < (size_t)workgroups * kProbeThreads)
+        return MOE_EINVAL;
+    mfma_probe_kernel<<<workgroups, kProbeThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        iters, d_sink);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}

@@ -508,6 +508,25 @@ moe_status_t moe_capacity_combine(const moe_shape_t *shape, int32_t cap, const v
 moe_status_t moe_repack(const moe_shape_t *shape, const int32_t *d_counts, int32_t *d_mapping,
                         moe_stream_t stream);
 
+/* ---- Calibration (measurement only) --------------------------------------
+ * Not a step of the method: a probe for measured peaks beside the spec
+ * ones. Runs `workgroups` workgroups of 256 threads; every wave performs
+ * 4 * iters v_mfma_f32_32x32x16_bf16 (2*32*32*16 flops each) on registers
+ * only, four independent chains on four operand pairs of bf16 values of
+ * magnitude 2^-7..2^-6 with hashed signs and mantissas. d_sink float[] out,
+ * at least workgroups * 256 entries (one sum per lane, only to keep the
+ * work). MOE_EINVAL for workgroups < 1, iters < 1, a NULL or short sink. */
+moe_status_t moe_probe_mfma(int32_t workgroups, int32_t iters, float *d_sink, size_t sink_floats,
+                            moe_stream_t stream);
+
+/* Calibration probe for HBM: copies `bytes` from d_src to d_dst (device
+ * buffers, 16-byte aligned, bytes a multiple of 16, not overlapping) with
+ * `workgroups` workgroups of 256 threads, each thread moving four 16-byte
+ * vectors per round (loads before stores). MOE_EINVAL for NULL or
+ * misaligned buffers, bytes 0 or not a multiple of 16, workgroups < 1. */
+moe_status_t moe_probe_copy(const void *d_src, void *d_dst, size_t bytes, int32_t workgroups,
+                            moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

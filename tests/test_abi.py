@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 34
+    assert len(names) == 36
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -54,6 +54,27 @@ def test_shape_validation(lib):
     narrow = bf.replace(T=16, H=64)
     assert moe.moe_check_shape(narrow.replace(F=(1 << 23) - 64)) == 0
     assert moe.moe_check_shape(narrow.replace(F=1 << 23)) == 2
+
+
+def test_probe_rejects_bad_arguments(lib):
+    """The calibration probe rejects its arguments on the host (no launch)."""
+    f = lib.moe_probe_mfma
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p(0x1000)
+    assert f(0, 1, p, 256, None) == 1            # no workgroups
+    assert f(1, 0, p, 256, None) == 1            # no iterations
+    assert f(1, 1, None, 256, None) == 1         # no sink
+    assert f(2, 1, p, 511, None) == 1            # sink shorter than 2 x 256
+    g = lib.moe_probe_copy
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    q = ctypes.c_void_p(0x2000)
+    assert g(None, q, 64, 1, None) == 1          # no source
+    assert g(p, q, 0, 1, None) == 1              # nothing to copy
+    assert g(p, q, 40, 1, None) == 1             # not whole 16-byte vectors
+    assert g(p, ctypes.c_void_p(0x2008), 64, 1, None) == 1  # misaligned
+    assert g(p, q, 64, 0, None) == 1             # no workgroups
 
 
 def test_plan_layout_and_workspace(lib):
