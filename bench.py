@@ -222,9 +222,10 @@ def time_flushed(fn, flush, reps=30):
 def measured_peaks():
     """Measured counterparts of the spec peaks: the bf16 MFMA rate of the
     library's calibration probe (four workgroups per CU, registers only,
-    operands that change from one MFMA to the next) and the faster of two
-    1 GiB device-to-device copies (the runtime's and the library's streaming
-    copy probe), with the caches flushed before each."""
+    operands that change from one MFMA to the next), the faster of two
+    2 GiB device-to-device copies (the runtime's and the library's streaming
+    copy probe) and the library's read probe over 4 GiB, with the caches
+    flushed before each copy and read."""
     import torch
 
     import expert_load_balance_amd as moe
@@ -244,20 +245,30 @@ def measured_peaks():
     t_mfma = time_back_to_back(probe, reps=20)
     flops = wg * 4 * 4 * iters * 2.0 * 32 * 32 * 16
     flush = Flusher()
-    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    t_rt = time_flushed(lambda: b.copy_(a), flush, reps=10)
-    t_probe = time_flushed(lambda: moe.moe_probe_copy(a, b, 8 * cus, stream=stream), flush, reps=10)
-    del a, b, flush, sink
+    # 4 GiB: long enough that the launch, the ramp and the write-back of the
+    # flush's dirty lines weigh little (a flushed 1 GiB read measured about
+    # 20 % below a flushed 4 GiB one)
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    half = big.numel() // 2
+    a, b = big[:half], big[half:]
+    t_rt = time_flushed(lambda: b.copy_(a), flush, reps=5)
+    t_probe = time_flushed(lambda: moe.moe_probe_copy(a, b, 8 * cus, stream=stream), flush, reps=5)
+    rsink = torch.empty(4 * cus * 256, dtype=torch.int32, device="cuda")
+    t_read = time_flushed(lambda: moe.moe_probe_read(big, 4 * cus, rsink, stream=stream), flush, reps=5)
+    del a, b, big, flush, sink, rsink
     torch.cuda.empty_cache()
-    rt, pr = 2.0 * (1 << 30) / t_rt / 1e9, 2.0 * (1 << 30) / t_probe / 1e9
+    rt, pr = 2.0 * half / t_rt / 1e9, 2.0 * half / t_probe / 1e9
+    rd = 2.0 * half / t_read / 1e9
     return {"mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
             "hbm_copy_gbs": round(max(rt, pr), 1),
             "hbm_copy_runtime_gbs": round(rt, 1), "hbm_copy_probe_gbs": round(pr, 1),
+            "hbm_read_gbs": round(rd, 1),
             "how": f"moe_probe_mfma: {wg} workgroups x 4 waves x {4 * iters} "
-                   "v_mfma_f32_32x32x16_bf16, back to back; 1 GiB device copy (read + write) by "
-                   f"the runtime and by moe_probe_copy ({8 * cus} workgroups), the faster one, "
-                   "512 MB flush before each"}
+                   "v_mfma_f32_32x32x16_bf16, back to back; 2 GiB device copy (2 GiB read + "
+                   "2 GiB written) by the runtime and by moe_probe_copy "
+                   f"({8 * cus} workgroups), the faster one; 4 GiB read by moe_probe_read "
+                   f"({4 * cus} workgroups, one contiguous chunk each); 512 MB flush before "
+                   "each copy and read"}
 
 
 def time_capacity_layer(shape, lg, bias, x, wts, cf, steps, warmup, L=None, shared=None):
@@ -816,6 +827,8 @@ def main():
         rec["roofline"]["frac_of_measured_peak"] = (
             r["gemm_gbs"] / mp["hbm_copy_gbs"] if hbm else r["gemm_tflops"] / mp["mfma_bf16_tflops"])
         rec["roofline"]["mfma_frac_of_measured_peak"] = r["gemm_tflops"] / mp["mfma_bf16_tflops"]
+        if hbm:  # the GEMM's bytes are mostly weight reads: against a plain read stream too
+            rec["roofline"]["frac_of_measured_read_peak"] = r["gemm_gbs"] / mp["hbm_read_gbs"]
     if not args.no_cpu_baseline:
         lg_np, bias_np, x, wts, shared = r["inputs"]
         rec["cpu_baseline"] = cpu_baseline(name, maxvio, lg_np, bias_np, x, wts, shared,

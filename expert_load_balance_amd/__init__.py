@@ -25,7 +25,7 @@ __all__ = [
     "moe_backward_workspace_bytes", "moe_combine_backward", "moe_ffn_backward",
     "moe_permute_backward", "moe_route_backward", "moe_grouped_gemm_train",
     "moe_replica_grad_bytes", "moe_ffn_backward_replicas", "moe_probe_mfma",
-    "moe_probe_copy", "EXPORTED_SYMBOLS",
+    "moe_probe_copy", "moe_probe_read", "EXPORTED_SYMBOLS",
 ]
 
 MOE_F32 = 0
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
     "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
-    "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy",
+    "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy", "moe_probe_read",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -133,6 +133,7 @@ def load():
         "moe_count_noalloc": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_probe_mfma": (st, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
         "moe_probe_copy": (st, [_VP, _VP, ctypes.c_size_t, ctypes.c_int32, _VP]),
+        "moe_probe_read": (st, [_VP, ctypes.c_size_t, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
         "moe_plan": (st, [_SP, _VP, _VP, _VP]),
         "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -327,6 +328,18 @@ def moe_probe_copy(src, dst, workgroups, stream=None):
         raise ValueError("src and dst differ in size")
     args = (_ptr(src, None, "src"), _ptr(dst, None, "dst"), nbytes, int(workgroups), _stream(stream))
     _ok(load().moe_probe_copy(*args), "moe_probe_copy")
+
+
+def moe_probe_read(src, workgroups, sink, stream=None):
+    """The HBM read probe: reads src (a multiple of 16 bytes) in `workgroups`
+    contiguous chunks; sink: int32 tensor of at least workgroups * 256
+    elements (per-thread XOR of the vectors read)."""
+    import torch
+
+    nbytes = src.numel() * src.element_size()
+    args = (_ptr(src, None, "src"), nbytes, int(workgroups), _ptr(sink, torch.int32, "sink"),
+            sink.numel(), _stream(stream))
+    _ok(load().moe_probe_read(*args), "moe_probe_read")
 
 
 def moe_count_noalloc(shape, ids, counts, offsets, eidx, rank_load, err, stream=None):

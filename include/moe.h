@@ -527,6 +527,18 @@ moe_status_t moe_probe_mfma(int32_t workgroups, int32_t iters, float *d_sink, si
 moe_status_t moe_probe_copy(const void *d_src, void *d_dst, size_t bytes, int32_t workgroups,
                             moe_stream_t stream);
 
+/* Calibration probe for HBM reads: reads `bytes` of d_src (device, 16-byte
+ * aligned, bytes a multiple of 16) with `workgroups` workgroups of 256
+ * threads, workgroup b taking the b-th of `workgroups` equal contiguous
+ * chunks (the last one may be shorter or empty), eight 16-byte loads in
+ * flight per thread. d_sink uint32[] out, at least workgroups * 256 entries:
+ * thread t of workgroup b stores the XOR of the four words of every vector
+ * i of its chunk with i mod 256 == t. MOE_EINVAL for NULL or misaligned
+ * buffers, bytes 0 or not a multiple of 16, workgroups < 1, a short sink, or
+ * a chunk above 2^31 - 32768 bytes. */
+moe_status_t moe_probe_read(const void *d_src, size_t bytes, int32_t workgroups, uint32_t *d_sink,
+                            size_t sink_words, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 36
+    assert len(names) == 37
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -75,6 +75,18 @@ def test_probe_rejects_bad_arguments(lib):
     assert g(p, q, 40, 1, None) == 1             # not whole 16-byte vectors
     assert g(p, ctypes.c_void_p(0x2008), 64, 1, None) == 1  # misaligned
     assert g(p, q, 64, 0, None) == 1             # no workgroups
+    h = lib.moe_probe_read
+    h.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    h.restype = ctypes.c_int
+    assert h(None, 64, 1, q, 256, None) == 1      # no source
+    assert h(p, 0, 1, q, 256, None) == 1          # nothing to read
+    assert h(p, 40, 1, q, 256, None) == 1         # not whole 16-byte vectors
+    assert h(ctypes.c_void_p(0x1008), 64, 1, q, 256, None) == 1  # misaligned
+    assert h(p, 64, 0, q, 256, None) == 1         # no workgroups
+    assert h(p, 64, 2, q, 511, None) == 1         # sink shorter than 2 x 256
+    assert h(p, 64, 1, None, 256, None) == 1      # no sink
+    assert h(p, 1 << 31, 1, q, 256, None) == 1    # one chunk of 2 GiB
 
 
 def test_plan_layout_and_workspace(lib):
