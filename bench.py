@@ -169,18 +169,26 @@ def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, ffn_bu
 
 
 class Flusher:
-    """Writes a 512 MB device buffer: more than the 256 MB Infinity Cache and
-    the L2s, so the next kernel reads its operands from HBM."""
+    """Writes a 512 MB device buffer, then reads another one: more than the
+    256 MB Infinity Cache and the L2s, so the next kernel reads its operands
+    from HBM. The read evicts the written lines, so their write-back happens
+    here and not inside the next kernel."""
 
     def __init__(self, nbytes=512 << 20):
         import torch
 
         self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.rbuf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        self.sink = torch.empty(self.wg * 256, dtype=torch.int32, device="cuda")
         self.v = 0
 
     def __call__(self):
+        import expert_load_balance_amd as moe
+
         self.v ^= 0x5A5A5A5A
         self.buf.fill_(self.v)
+        moe.moe_probe_read(self.rbuf, self.wg, self.sink)
 
 
 def time_back_to_back(fn, reps=50):
