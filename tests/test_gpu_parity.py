@@ -527,23 +527,52 @@ def test_full_size_sampled(name, maxvio):
     every tile of both GEMMs, K-split leftovers and both skinny heights
     included, has rows checked -- and the combine on 64+ tokens spread over
     every rank window, each against the oracle from the same inputs."""
-    import concurrent.futures as cf
-
     _say(f"[case] full {name}@{maxvio}")
     w = wl.WORKLOADS[name]
     shape = moe.Shape(w["T"], w["H"], w["E"], w["k"], w["F"], w["R"], w["S"], moe.MOE_BF16)
     lg, bias = wl.logits_and_bias(name, maxvio)
     cache = _workload_tensors(name)
-    x, wts = cache["x"], cache["wts"]
-    shared = cache.get("shared")
-    L = run_layer(shape, lg, bias, x, wts, shared_w=shared, shared_F=w.get("shared_F"))
+    _check_full_layer(f"{name}@{maxvio}", shape, lg, bias, cache["x"], cache["wts"],
+                      shared=cache.get("shared"), shared_F=w.get("shared_F"),
+                      capacity_factor=w.get("capacity_factor", 1.0))
+
+
+def test_largest_bf16_shape():
+    """The largest layer the bf16 path accepts: the dispatch buffer (N x H
+    bf16, N = T k) 128 KB short of the 4 GiB its 32-bit copy offsets reach,
+    one more token rejected on the host. Checked like the full-size layers."""
+    T, H, E, k, F, R, S = 32767, 8192, 16, 8, 256, 8, 2
+    shape = moe.Shape(T, H, E, k, F, R, S, moe.MOE_BF16)
+    assert T * k * H * 2 == (1 << 32) - (128 << 10)
+    assert moe.moe_check_shape(shape) == 0
+    assert moe.moe_check_shape(shape.replace(T=T + 1)) == 2
+    _WEIGHT_CACHE.clear()
+    torch.cuda.empty_cache()
+    seed = 9
+    lg = synth.router_logits(T, E, seed)
+    x = synth.device_normal((T, H), 1.0, seed * 7 + 1, torch.bfloat16, DEV)
+    wts = make_weights(E, F, H, moe.MOE_BF16, seed)
+    _say(f"[case] largest bf16 shape T={T} H={H} E={E} k={k} F={F}")
+    _check_full_layer("largest", shape, lg, None, x, wts)
+    del x, wts
+    torch.cuda.empty_cache()
+
+
+def _check_full_layer(label, shape, lg, bias, x, wts, shared=None, shared_F=None,
+                      capacity_factor=1.0):
+    """Runs the layer and checks it against the oracle: the integer path and
+    statistics whole, the FFN on rows from every (expert, M-tile), the
+    combine on 64+ tokens over every rank window."""
+    import concurrent.futures as cf
+
+    L = run_layer(shape, lg, bias, x, wts, shared_w=shared, shared_F=shared_F)
     ids, wgt, c, pl = check_integer_path(L, lg, bias, host(raw_bits(x)))
     dest_ref, buf_ref_src = check_integer_path.perm
     # statistics, bit-exact against the oracle's
     st, loads = moe.moe_stats(shape, L.counts, L.ids, L.plan, L.ws, dest_row=L.dest_row,
-                              err=L.err, capacity_factor=w.get("capacity_factor", 1.0))
+                              err=L.err, capacity_factor=capacity_factor)
     ref = oracle.stats(ids, c["counts"], shape.R, S=shape.S, dest_row=dest_ref, pl=pl,
-                       capacity_factor=w.get("capacity_factor", 1.0))
+                       capacity_factor=capacity_factor)
     for key_ in ("N", "max_count", "min_count", "active_experts", "maxvio_expert",
                  "balancedness_expert", "home_max", "maxvio_rank_home", "planned_max",
                  "planned_min", "maxvio_rank_planned", "capacity", "processed", "overflow",
@@ -575,12 +604,14 @@ def test_full_size_sampled(name, maxvio):
             vr += [m0 + v for v in _tile_sample_rows(min(_MTILE, ce - m0), e * 131 + m0)]
         sel = set(rows[vr].tolist()) | (tok_rows & set(rows.tolist()))
         want[e] = np.array(sorted(sel), np.int64)
-    _say(f"[case] full {name}@{maxvio}: tiles {classes}, {sum(len(v) for v in want.values())} "
+    _say(f"[case] full {label}: tiles {classes}, {sum(len(v) for v in want.values())} "
          f"rows over {len(want)} experts, {len(toks)} combine tokens")
 
     xh = host(x)
     wg, wu, wd = wts
-    y = host(L.y)
+
+    def y_rows(rows):  # gathered on the device: y is up to 4 GiB
+        return host(L.y[torch.from_numpy(rows).to(DEV)])
     y_ref = {}
 
     def run_oracle(e, rows, g, u, d):
@@ -600,7 +631,7 @@ def test_full_size_sampled(name, maxvio):
             y_ref[done[0]] = done
     full_ref = {}
     for e, (_, rows, ref_y) in sorted(y_ref.items()):
-        assert_tol(y[rows], ref_y, moe.MOE_BF16, f"y expert {e} ({len(rows)} rows)")
+        assert_tol(y_rows(rows), ref_y, moe.MOE_BF16, f"y expert {e} ({len(rows)} rows)")
         for r, v in zip(rows.tolist(), ref_y):
             full_ref[r] = v
 
