@@ -479,10 +479,10 @@ __device__ __forceinline__ void main_tiles(
         copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
                slots_u + b_slot(st) + wave * 1024 + i * 4096);
     };
-    // A and B of stage 0 (head), then of stage 1 and B of stage 2 (tail), in
-    // this order: the waits below count the copies issued after the ones
-    // they wait for. Between the two a finished tile can be staged in the
-    // slots the tail fills.
+    // A and B of stage 0 (head), then of stage 1 (tail), in this order: the
+    // waits below count the copies issued after the ones they wait for.
+    // Between the two a finished tile can be staged in the slots the tail
+    // fills.
     auto prologue_head = [&]() {
 #pragma unroll
         for (int i = 0; i < kCopiesWave; ++i) copy_a(0, i);
@@ -495,10 +495,6 @@ __device__ __forceinline__ void main_tiles(
             for (int i = 0; i < kCopiesWave; ++i) copy_a(1, i);
 #pragma unroll
             for (int i = 0; i < kCopiesWave; ++i) copy_b(1, i);
-        }
-        if (u.KT > 2) {
-#pragma unroll
-            for (int i = 0; i < kCopiesWave; ++i) copy_b(2, i);
         }
     };
 
@@ -520,12 +516,15 @@ __device__ __forceinline__ void main_tiles(
     };
 
     // k-steps 0 and 1 of stage s: MFMAs interleaved with the reads of sets
-    // 1, 2, 3; then the wait for this wave's copies of stage s+1 (WAIT: the
-    // copies issued after them, B of stage s+2 when it exists) and the
-    // barrier. Reads: n-th read of k-step kk covers set-read index
-    // 12 kk + n over the sequence (set 1: 8 reads, set 2: 8, set 3: 8).
-    auto first_half = [&](auto wait_tag, int s) {
+    // 1, 2, 3 and, CB, the copies of B of stage s+2 into the B slot stage s-1
+    // freed at its barrier (one copy per four MFMAs); then the wait for this
+    // wave's copies of stage s+1 (WAIT: the copies issued after them, those
+    // B copies) and the barrier. Reads: n-th read of k-step kk covers
+    // set-read index 12 kk + n over the sequence (set 1: 8 reads, set 2: 8,
+    // set 3: 8).
+    auto first_half = [&](auto wait_tag, auto cb_tag, int s) {
         constexpr int WAIT = decltype(wait_tag)::value;
+        constexpr bool CB = decltype(cb_tag)::value;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             int n = 0;
@@ -535,6 +534,8 @@ __device__ __forceinline__ void main_tiles(
                 if ((m & 3) != 3) {
                     const int idx = 12 * kk + n++;  // 0..23
                     read(s, 1 + idx / 8, read_order(idx % 8));
+                } else if (CB) {
+                    copy_b(s + 2, 4 * kk + (m >> 2));
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -543,11 +544,11 @@ __device__ __forceinline__ void main_tiles(
         slot_barrier();
     };
     // k-steps 2 and 3 of stage s: stage s's slots are free; CA copies A of
-    // stage s+2 into its A slot, CB B of stage s+3 into its B slot; NEXT
-    // reads set 0 of stage s+1.
-    auto second_half = [&](auto ca_tag, auto cb_tag, auto next_tag, int s) {
+    // stage s+2 into its A slot (one copy per four MFMAs); NEXT reads set 0
+    // of stage s+1. So every quarter of a stage issues a quarter of the
+    // copies.
+    auto second_half = [&](auto ca_tag, auto next_tag, int s) {
         constexpr bool CA = decltype(ca_tag)::value;
-        constexpr bool CB = decltype(cb_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
 #pragma unroll
         for (int kk = 2; kk < 4; ++kk) {
@@ -555,10 +556,7 @@ __device__ __forceinline__ void main_tiles(
             for (int m = 0; m < 16; ++m) {
                 mfma(kk, m);
                 if (NEXT && (m & 3) == 0) read(s + 1, 0, read_order(4 * (kk - 2) + (m >> 2)));
-                if (m & 1) {
-                    if (kk == 2 && CA) copy_a(s + 2, m >> 1);
-                    if (kk == 3 && CB) copy_b(s + 3, m >> 1);
-                }
+                if (CA && (m & 3) == 1) copy_a(s + 2, 4 * (kk - 2) + (m >> 2));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -617,48 +615,43 @@ __device__ __forceinline__ void main_tiles(
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-        // stage 0 landed: the copies of stages 1 and 2 (and, with a next
-        // unit, its row loads) were issued after it
+        // stage 0 landed: the copies of stage 1 (and, with a next unit, its
+        // row loads) were issued after it
         if (has_next) {
-            if (u.KT >= 3) wait_vm_lgkm<3 * kCopiesWave + kRowLoads>();
-            else if (u.KT == 2) wait_vm_lgkm<2 * kCopiesWave + kRowLoads>();
+            if (u.KT >= 2) wait_vm_lgkm<2 * kCopiesWave + kRowLoads>();
             else wait_vm_lgkm<kRowLoads>();
         } else {
-            if (u.KT >= 3) wait_vm_lgkm<3 * kCopiesWave>();
-            else if (u.KT == 2) wait_vm_lgkm<2 * kCopiesWave>();
+            if (u.KT >= 2) wait_vm_lgkm<2 * kCopiesWave>();
             else wait_vm_lgkm<0>();
         }
         slot_barrier();
 #pragma unroll
         for (int n = 0; n < 8; ++n) read(0, 0, read_order(n));
 
+        // stage s issues B and A of stage s+2 (while that exists) and waits
+        // for stage s+1 (while that exists)
         int s = 0;
-        for (; s + 3 < u.KT; ++s) {
-            first_half(W8{}, s);
-            second_half(Yes{}, Yes{}, Yes{}, s);
-        }
-        if (s + 2 < u.KT) {
-            first_half(W8{}, s);
-            second_half(Yes{}, No{}, Yes{}, s);
-            ++s;
+        for (; s + 2 < u.KT; ++s) {
+            first_half(W8{}, Yes{}, s);
+            second_half(Yes{}, Yes{}, s);
         }
         if (s + 1 < u.KT) {
-            first_half(W0{}, s);
-            second_half(No{}, No{}, Yes{}, s);
+            first_half(W0{}, No{}, s);
+            second_half(No{}, Yes{}, s);
             ++s;
         }
         // last stage: after its barrier every slot is free, so the next
         // unit's first stage goes out before this unit's last MFMAs. Its row
         // loads completed with the wait above; the empty asm keeps their
         // first use here, where no copy is in flight to wait for.
-        first_half(W0{}, s);
+        first_half(W0{}, No{}, s);
         if (has_next) {
 #pragma unroll
             for (int i = 0; i < kRowLoads; ++i) asm volatile("" : "+v"(nrw[i]));
             setup(un, nrw);
             prologue_head();
         }
-        second_half(No{}, No{}, No{}, s);
+        second_half(No{}, No{}, s);
 
         // ---- epilogue: acc[i][j][4*g4 + q] is row wm*128 + 32 i + (lane & 31),
         // column (block j) 8 g4 + 4 (lane >> 5) + q, q = 0..3.
