@@ -21,23 +21,19 @@
 // the experts for the counts and the donor orders. The transfer loop runs
 // on the first wavefront, lane r owning rank r: its argmaxes are a DPP /
 // permlane max, then the lowest lane holding it (by ballot); the donor walk
-// is a prefix sum over the donor's experts, lane i taking its i-th in donor
-// order (a serial walk on one lane past 64 experts a rank). Lane r of the
-// first wavefront lays out rank r's window; then the wavefronts take
-// experts in turn, lane r the piece on rank r, compacted in rank order with
-// a ballot. Every entry of the plan block is written.
+// is a prefix sum over the donor's remaining counts, kept in donor order,
+// lane i taking its i-th (a serial walk on one lane past 64 experts a
+// rank). The windows and the pieces are laid out by groups of lanes, one
+// rank's 2n candidate segments or one expert's R candidate pieces a group,
+// several groups a wavefront; ballots place the non-empty entries and a
+// wavefront permute packs them to the front, so that every table is written
+// with whole-wavefront stores. Every entry of the plan block is written.
 #include <climits>
 
 #include "common.h"
 
 namespace {
 
-// Wavefront max without LDS: DPP moves inside rows of 16 lanes (xor 1,
-// xor 2, then the half-row and row mirrors, which for a commutative op pair
-// each lane with the other half of its reduced group), then the gfx950
-// permlane swaps across rows of 16 and of 32. Each swap gets an opaque copy
-// as its second operand (with the same value twice the compiler was seen to
-// drop the second half of a swap).
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v)
 {
@@ -49,17 +45,48 @@ __device__ __forceinline__ int opaque(int v)
     asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
 }
-__device__ __forceinline__ int wave_max(int v)
+// Two wavefront maxes at once, without LDS: DPP moves inside rows of 16
+// lanes (xor 1, xor 2, then the half-row and row mirrors, which for a
+// commutative op pair each lane with the other half of its reduced group),
+// then the gfx950 permlane swaps across rows of 16 and of 32; the steps of
+// the two interleave, each hiding the other's latency. Each swap gets an
+// opaque copy as its second operand (with the same value twice the
+// compiler was seen to drop the second half of a swap).
+__device__ __forceinline__ void wave_max2(int& a, int& b)
 {
-    v = max(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = max(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = max(v, dpp<0x141>(v));  // lane i <-> 7-i in each 8
-    v = max(v, dpp<0x140>(v));  // lane i <-> 15-i in each 16
-    const auto a = __builtin_amdgcn_permlane16_swap(v, opaque(v), false, false);
-    v = max((int)a[0], (int)a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(v, opaque(v), false, false);
-    return max((int)b[0], (int)b[1]);
+    a = max(a, dpp<0xB1>(a));
+    b = max(b, dpp<0xB1>(b));
+    a = max(a, dpp<0x4E>(a));
+    b = max(b, dpp<0x4E>(b));
+    a = max(a, dpp<0x141>(a));
+    b = max(b, dpp<0x141>(b));
+    a = max(a, dpp<0x140>(a));
+    b = max(b, dpp<0x140>(b));
+    const auto a1 = __builtin_amdgcn_permlane16_swap(a, opaque(a), false, false);
+    const auto b1 = __builtin_amdgcn_permlane16_swap(b, opaque(b), false, false);
+    a = max((int)a1[0], (int)a1[1]);
+    b = max((int)b1[0], (int)b1[1]);
+    const auto a2 = __builtin_amdgcn_permlane32_swap(a, opaque(a), false, false);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(b, opaque(b), false, false);
+    a = max((int)a2[0], (int)a2[1]);
+    b = max((int)b2[0], (int)b2[1]);
 }
+
+// Lanes below this one, as a ballot mask.
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Bits [g * w, g * w + w) of a ballot (w <= 64).
+__device__ __forceinline__ uint64_t group_bits(int g, int w)
+{
+    return (w == 64 ? ~0ull : ((1ull << w) - 1)) << (g * w);
+}
+
+// Forward permute inside the wavefront: the value of every lane lands in
+// lane `to` (a permutation of the lanes).
+__device__ __forceinline__ int send_to(int to, int v) { return __builtin_amdgcn_ds_permute(to * 4, v); }
 
 __device__ __forceinline__ int wave_sum(int v)
 {
@@ -75,6 +102,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
                                                             int32_t* __restrict__ plan)
 {
     __shared__ int32_t cnt[256], rem[256], order[256], take[256], home_row[256], rep_row[256];
+    __shared__ int32_t remo[256];  // remaining count of order[i] (the transfer loop's view)
     __shared__ int32_t quota[64], load[64], donor[64], ptr[64], win[65];
     __shared__ int32_t wsum[kPlanThreads / 64];
 
@@ -127,6 +155,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
             for (int x = r0; x < r0 + n; ++x)
                 pos += (cnt[x] > cnt[e] || (cnt[x] == cnt[e] && x < e)) ? 1 : 0;
             order[r0 + pos] = e;
+            remo[r0 + pos] = cnt[e];
         }
     }
     __syncthreads();
@@ -147,16 +176,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
             }
             // argmaxes, ties to the lower rank: the wavefront max, then the
             // lowest lane holding it
-            const int best_def = wave_max(lane < R ? def : -1);
+            int best_def = lane < R ? def : -1, best_exc = lane < R ? exc : INT_MIN;
+            wave_max2(best_def, best_exc);
             if (best_def <= 0) break;  // uniform
             const int s = __ffsll((unsigned long long)__ballot(lane < R && def == best_def)) - 1;
-            const int best_exc = wave_max(lane < R ? exc : INT_MIN);
             const int l = __ffsll((unsigned long long)__ballot(lane < R && exc == best_exc)) - 1;
             if (n <= 64) {
                 // the walk over l's experts in donor order as a prefix sum: the
                 // i-th takes min(rem_i, d - (rem of the ones before it)), at least 0
                 const int e = lane < n ? order[l * n + lane] : 0;
-                const int r = lane < n ? rem[e] : 0;
+                const int r = lane < n ? remo[l * n + lane] : 0;
                 int incl = r;
                 if (n <= 16) {  // inside the first row of 16 lanes: DPP shifts
                     if (n > 1) incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);
@@ -173,20 +202,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
                 const int t = room <= 0 ? 0 : (room < r ? room : r);
                 if (t > 0) {
                     take[s * n + (e - l * n)] = t;
-                    rem[e] = r - t;
+                    remo[l * n + lane] = r - t;
                 }
             } else if (lane == 0) {  // more than 64 experts a rank: one step at a time
                 int d = best_def;
                 int p = ptr[l];
                 while (d > 0 && p < n) {
                     const int e = order[l * n + p];
-                    const int t = rem[e] < d ? rem[e] : d;
+                    const int r = remo[l * n + p];
+                    const int t = r < d ? r : d;
                     if (t > 0) {
                         take[s * n + (e - l * n)] = t;
-                        rem[e] -= t;
+                        remo[l * n + p] = r - t;
                         d -= t;
                     }
-                    if (rem[e] == 0) ++p;
+                    if (r - t == 0) ++p;
                 }
                 ptr[l] = p;
             }
@@ -199,9 +229,74 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
         }
     }
     __syncthreads();
+    // back to expert order for the layout below
+    if (R > 1)
+        for (int i = tid; i < E; i += kPlanThreads) rem[order[i]] = remo[i];
+    __syncthreads();
 
-    // per-rank windows: segments in expert id order, replica slots
-    if (wave == 0 && lane < R) {
+    // Per-rank windows: segments in expert id order (the lower id block
+    // first), replica slots. Rank r's 2n candidate segments (pass 0: its
+    // first block, pass 1: the other) sit in 2n consecutive lanes; ballots
+    // place the non-empty ones, a prefix sum gives their rows, and a
+    // wavefront permute packs them to the front so that every table is
+    // written by one coalesced store (the rest -1). More than 32 experts a
+    // rank: one lane per rank.
+    if (2 * n <= 64) {
+        const int gs = 2 * n, gpw = 64 / gs;
+        const int g = lane / gs, j = lane % gs;
+        const int pass = j / n, i = j % n;
+        for (int base = wave * gpw; base < R; base += (kPlanThreads / 64) * gpw) {
+            const int r = base + g;
+            const bool act = g < gpw && r < R;  // uniform over the group
+            const int l = act ? donor[r] : -1;
+            int c = 0, e = -1, home = 0;
+            if (act) {
+                int blk;
+                if (l < 0) blk = pass == 0 ? r : -1;
+                else blk = (pass == 0) == (l < r) ? l : r;
+                if (blk >= 0) {
+                    e = blk * n + i;
+                    home = blk == r;
+                    c = home ? rem[e] : take[r * n + i];
+                }
+            }
+            const uint64_t gm = act ? group_bits(g, gs) : 0ull, below = lanes_below(lane);
+            const uint64_t has = __ballot(act && c > 0), rep = __ballot(act && c > 0 && !home);
+            const int pos = __popcll(has & gm & below), ns = __popcll(has & gm);
+            const int spos = __popcll(rep & gm & below), nslot = __popcll(rep & gm);
+            int incl = c;  // prefix sum of the counts inside the group
+            for (int off = 1; off < gs; off <<= 1) {
+                const int v = __shfl_up(incl, off, 64);
+                if (j >= off) incl += v;
+            }
+            const int row = act ? win[r] + incl - c : 0;
+            if (act && c > 0) {
+                if (home) home_row[e] = row;
+                else rep_row[r * n + i] = row;
+            }
+            // segment k of rank r comes from the k-th non-empty lane; the
+            // empty ones follow in order (a permutation of the group)
+            const int to = act ? g * gs + (c > 0 ? pos : ns + (j - pos)) : lane;
+            const int se = send_to(to, e), sr = send_to(to, row), scn = send_to(to, c);
+            if (act) {
+                const int64_t o = (int64_t)r * gs + j;  // j is now the segment index
+                plan[L.seg_expert + o] = j < ns ? se : -1;
+                plan[L.seg_row + o] = j < ns ? sr : -1;
+                plan[L.seg_cnt + o] = j < ns ? scn : -1;
+            }
+            const int sto = act ? g * gs + (c > 0 && !home ? spos : nslot + (j - spos)) : lane;
+            const int sl = send_to(sto, e);
+            if (act && j < n) plan[L.slot_expert + (int64_t)r * n + j] = j < nslot ? sl : -1;
+            if (act && j == 0) {
+                plan[L.seg_num + r] = ns;
+                plan[L.slots_needed + r] = nslot;
+                plan[L.quota + r] = quota[r];
+                plan[L.donor + r] = l;
+                plan[L.win_off + r + 1] = win[r + 1];
+                if (r == 0) plan[L.win_off] = 0;
+            }
+        }
+    } else if (wave == 0 && lane < R) {
         const int r = lane;
         const int l = donor[r];
         int row = win[r];
@@ -243,35 +338,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
     }
     __syncthreads();
 
-    // per-expert pieces in rank order: lane r of the expert's wavefront
-    // holds its piece on rank r (if any) and writes it at its rank among the
-    // non-empty pieces; lanes from the piece count on fill with -1
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int e = wave; e < E; e += kPlanThreads / 64) {
-        const int h = e / n;
-        int c = 0, row = -1;
-        if (lane < R) {
-            if (lane == h) {
-                c = rem[e];
-                row = home_row[e];
-            } else if (donor[lane] == h) {
-                c = take[lane * n + (e - h * n)];
-                row = rep_row[lane * n + (e - h * n)];
+    // Per-expert pieces in rank order: an expert's R candidate pieces (rank
+    // r: its home remainder when r is its home rank, what r took from it
+    // when r is a receiver of its home rank) sit in R consecutive lanes, 64 / R
+    // experts a wavefront; packed to the front by a permute as above.
+    {
+        const int gpw = 64 / R;
+        const int g = lane / R, r = lane % R;
+        for (int base = wave * gpw; base < E; base += (kPlanThreads / 64) * gpw) {
+            const int e = base + g;
+            const bool act = g < gpw && e < E;  // uniform over the group
+            int c = 0, row = -1;
+            if (act) {
+                const int h = e / n;
+                if (r == h) {
+                    c = rem[e];
+                    row = home_row[e];
+                } else if (donor[r] == h) {
+                    c = take[r * n + (e - h * n)];
+                    row = rep_row[r * n + (e - h * n)];
+                }
+            }
+            const uint64_t gm = act ? group_bits(g, R) : 0ull;
+            const uint64_t has = __ballot(act && c > 0);
+            const int pos = __popcll(has & gm & lanes_below(lane)), np = __popcll(has & gm);
+            const int to = act ? g * R + (c > 0 ? pos : np + (r - pos)) : lane;
+            const int sk = send_to(to, r), sw = send_to(to, row), sc = send_to(to, c);
+            if (act) {
+                const int64_t o = (int64_t)e * R + r;  // r is now the piece index
+                plan[L.piece_rank + o] = r < np ? sk : -1;
+                plan[L.piece_row + o] = r < np ? sw : -1;
+                plan[L.piece_cnt + o] = r < np ? sc : -1;
+                if (r == 0) plan[L.piece_num + e] = np;
             }
         }
-        const uint64_t has = __ballot(c > 0);
-        const int np = __popcll(has);
-        int32_t* pr = plan + L.piece_rank + (size_t)e * R;
-        int32_t* pw = plan + L.piece_row + (size_t)e * R;
-        int32_t* pc = plan + L.piece_cnt + (size_t)e * R;
-        if (c > 0) {
-            const int pos = __popcll(has & lt_mask);
-            pr[pos] = lane;
-            pw[pos] = row;
-            pc[pos] = c;
-        }
-        if (lane < R && lane >= np) pr[lane] = pw[lane] = pc[lane] = -1;
-        if (lane == 0) plan[L.piece_num + e] = np;
     }
 }
 
