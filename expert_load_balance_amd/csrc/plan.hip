@@ -45,14 +45,15 @@ __device__ __forceinline__ int opaque(int v)
     asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
 }
-// Two wavefront maxes at once, without LDS: DPP moves inside rows of 16
-// lanes (xor 1, xor 2, then the half-row and row mirrors, which for a
-// commutative op pair each lane with the other half of its reduced group),
-// then the gfx950 permlane swaps across rows of 16 and of 32; the steps of
-// the two interleave, each hiding the other's latency. Each swap gets an
+// Two maxes over lanes 0 .. w-1 at once (w = 16, 32 or 64; w-lane groups
+// reduce alike), without LDS: DPP moves inside rows of 16 lanes (xor 1,
+// xor 2, then the half-row and row mirrors, which for a commutative op pair
+// each lane with the other half of its reduced group), then, past 16 lanes,
+// the gfx950 permlane swaps across rows of 16 and of 32; the steps of the
+// two interleave, each hiding the other's latency. Each swap gets an
 // opaque copy as its second operand (with the same value twice the
 // compiler was seen to drop the second half of a swap).
-__device__ __forceinline__ void wave_max2(int& a, int& b)
+__device__ __forceinline__ void wave_max2(int& a, int& b, int w)
 {
     a = max(a, dpp<0xB1>(a));
     b = max(b, dpp<0xB1>(b));
@@ -62,14 +63,18 @@ __device__ __forceinline__ void wave_max2(int& a, int& b)
     b = max(b, dpp<0x141>(b));
     a = max(a, dpp<0x140>(a));
     b = max(b, dpp<0x140>(b));
-    const auto a1 = __builtin_amdgcn_permlane16_swap(a, opaque(a), false, false);
-    const auto b1 = __builtin_amdgcn_permlane16_swap(b, opaque(b), false, false);
-    a = max((int)a1[0], (int)a1[1]);
-    b = max((int)b1[0], (int)b1[1]);
-    const auto a2 = __builtin_amdgcn_permlane32_swap(a, opaque(a), false, false);
-    const auto b2 = __builtin_amdgcn_permlane32_swap(b, opaque(b), false, false);
-    a = max((int)a2[0], (int)a2[1]);
-    b = max((int)b2[0], (int)b2[1]);
+    if (w > 16) {  // uniform
+        const auto a1 = __builtin_amdgcn_permlane16_swap(a, opaque(a), false, false);
+        const auto b1 = __builtin_amdgcn_permlane16_swap(b, opaque(b), false, false);
+        a = max((int)a1[0], (int)a1[1]);
+        b = max((int)b1[0], (int)b1[1]);
+    }
+    if (w > 32) {
+        const auto a2 = __builtin_amdgcn_permlane32_swap(a, opaque(a), false, false);
+        const auto b2 = __builtin_amdgcn_permlane32_swap(b, opaque(b), false, false);
+        a = max((int)a2[0], (int)a2[1]);
+        b = max((int)b2[0], (int)b2[1]);
+    }
 }
 
 // Lanes below this one, as a ballot mask.
@@ -174,11 +179,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
                 def = (!my_filled && d > 0) ? d : -1;
                 exc = -d;
             }
-            // argmaxes, ties to the lower rank: the wavefront max, then the
-            // lowest lane holding it
+            // argmaxes, ties to the lower rank: the max over the R lanes
+            // (lane 0's copy, a scalar), then the lowest lane holding it
             int best_def = lane < R ? def : -1, best_exc = lane < R ? exc : INT_MIN;
-            wave_max2(best_def, best_exc);
-            if (best_def <= 0) break;  // uniform
+            wave_max2(best_def, best_exc, R <= 16 ? 16 : R <= 32 ? 32 : 64);
+            best_def = __builtin_amdgcn_readfirstlane(best_def);
+            best_exc = __builtin_amdgcn_readfirstlane(best_exc);
+            if (best_def <= 0) break;
             const int s = __ffsll((unsigned long long)__ballot(lane < R && def == best_def)) - 1;
             const int l = __ffsll((unsigned long long)__ballot(lane < R && exc == best_exc)) - 1;
             if (n <= 64) {
