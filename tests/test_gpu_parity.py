@@ -163,6 +163,9 @@ SMALL = [
     ("bf16_tails_mixed", 900, 256, 3, 1, 384, 3, 1, moe.MOE_BF16, 0.0),
     # 291, 289, 278, 292 rows: tails of 35, 33, 22 and 36 rows over 16 K-stages
     ("bf16_tails_long_k", 1150, 1024, 4, 1, 256, 4, 1, moe.MOE_BF16, 0.0),
+    # twelve ranks of three experts, odd k: lane groupings that do not tile
+    # a wavefront in the plan, and the dispatch's piece lookup
+    ("bf16_odd_ranks", 300, 128, 36, 5, 128, 12, 2, moe.MOE_BF16, 0.6),
 ]
 
 
@@ -378,6 +381,37 @@ def test_plan_random_skew_bit_exact():
         got = moe.plan_tables(plan, shape)
         for t in oracle.PLAN_TABLES:
             np.testing.assert_array_equal(host(got[t]), ref[t], err_msg=f"{t} trial {trial}")
+
+
+# ranks and experts per rank that tile a wavefront unevenly: R not dividing
+# 64 (the piece layout's lane groups leave lanes over), 2n not dividing 64
+# (the window layout's), and 2n > 64 (one lane per rank)
+ODD_PLAN_SHAPES = [(24, 3), (30, 5), (36, 12), (96, 24), (160, 40), (240, 48), (252, 63), (198, 6)]
+
+
+@pytest.mark.parametrize("E,R", ODD_PLAN_SHAPES, ids=[f"E{e}_R{r}" for e, r in ODD_PLAN_SHAPES])
+def test_plan_odd_groupings_bit_exact(E, R):
+    rng = np.random.default_rng(E * 131 + R)
+    for trial in range(6):
+        if trial == 0:
+            counts = np.full(E, 5, np.int32)                       # balanced
+        elif trial == 1:
+            counts = np.zeros(E, np.int32)
+            counts[E // 2] = 4000                                   # one hot expert
+        elif trial % 2:
+            counts = rng.zipf(1.3 + 0.1 * trial, E).clip(max=20000).astype(np.int32)
+        else:
+            counts = rng.integers(0, 400, E).astype(np.int32)
+        shape = moe.Shape(int(counts.sum()) or 1, 64, E, 1, 64, R, 1, moe.MOE_BF16)
+        plan = alloc((moe.moe_plan_layout(shape)["total"],), torch.int32, DEV)
+        plan.fill_(-7)
+        moe.moe_plan(shape, torch.from_numpy(counts).to(DEV), plan)
+        torch.cuda.synchronize()
+        ref = oracle.plan(counts, R)
+        got = moe.plan_tables(plan, shape)
+        for t in oracle.PLAN_TABLES:
+            np.testing.assert_array_equal(host(got[t]), ref[t], err_msg=f"{t} trial {trial}")
+        assert not (host(plan) == -7).any()
 
 
 def test_empty_batch():
