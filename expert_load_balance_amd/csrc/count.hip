@@ -39,13 +39,25 @@ __global__ __launch_bounds__(kThreads) void count_hist_kernel(int N, int k, int 
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * moe::kCountChunk;
     int bad = 0;
+    // lane l holds assignment base + 256 m + 64 w + l: with k dividing 64 a
+    // token's earlier assignments are in the lanes below (shuffles)
+    const bool by_lanes = 64 % k == 0;
+    const int lane = threadIdx.x % moe::kWave;
     for (int i = threadIdx.x; i < moe::kCountChunk; i += kThreads) {
         const int64_t a = base + i;
-        if (a >= N) break;
-        const int32_t e = ids[a];
-        const int j = (int)(a % k);
-        for (int jj = 1; jj <= j; ++jj)
-            if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
+        const int32_t e = a < N ? ids[a] : -1;
+        if (by_lanes) {
+            const int j = lane % k;  // = a % k
+            for (int jj = 1; jj < k; ++jj) {
+                const int32_t o = __shfl(e, lane - jj);
+                if (jj <= j && a < N && o == e) bad |= MOE_ERR_REPEAT;
+            }
+        } else if (a < N) {
+            const int j = (int)(a % k);
+            for (int jj = 1; jj <= j; ++jj)
+                if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
+        }
+        if (a >= N) continue;
         if (e < 0 || e >= E) {
             bad |= MOE_ERR_RANGE;
             continue;
@@ -195,15 +207,27 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
         const int a = a0 + 64 * i;
         ev[i] = 64 * i < C && a < N ? ids[a] : -1;
     }
+    // a token's k assignments: when k divides 64 they sit in k adjacent
+    // lanes of one round (chunks start at multiples of 64), so the earlier
+    // ones come from the lanes below by shuffles; otherwise from memory
+    const bool by_lanes = 64 % k == 0;
 #pragma unroll
     for (int i = 0; i < kFusedRounds; ++i) {
+        if (64 * i >= C) break;
         const int a = a0 + 64 * i;
-        if (64 * i >= C || a >= N) break;
         const int32_t e = ev[i];
-        const int j = a % k;
-        for (int jj = 1; jj <= j; ++jj)
-            if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
-        if (e < 0 || e >= E) bad |= MOE_ERR_RANGE;
+        if (by_lanes) {
+            const int j = lane % k;  // = a % k
+            for (int jj = 1; jj < k; ++jj) {
+                const int32_t o = __shfl(e, lane - jj);
+                if (jj <= j && a < N && o == e) bad |= MOE_ERR_REPEAT;
+            }
+        } else if (a < N) {
+            const int j = a % k;
+            for (int jj = 1; jj <= j; ++jj)
+                if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
+        }
+        if (a < N && (e < 0 || e >= E)) bad |= MOE_ERR_RANGE;
     }
     __syncthreads();
 
