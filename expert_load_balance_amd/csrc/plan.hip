@@ -45,7 +45,7 @@ __device__ __forceinline__ int opaque(int v)
     asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
 }
-// Two maxes over lanes 0 .. w-1 at once (w = 16, 32 or 64; w-lane groups
+// Two maxes over lanes 0 .. W-1 at once (W = 16, 32 or 64; W-lane groups
 // reduce alike), without LDS: DPP moves inside rows of 16 lanes (xor 1,
 // xor 2, then the half-row and row mirrors, which for a commutative op pair
 // each lane with the other half of its reduced group), then, past 16 lanes,
@@ -53,7 +53,8 @@ __device__ __forceinline__ int opaque(int v)
 // two interleave, each hiding the other's latency. Each swap gets an
 // opaque copy as its second operand (with the same value twice the
 // compiler was seen to drop the second half of a swap).
-__device__ __forceinline__ void wave_max2(int& a, int& b, int w)
+template <int W>
+__device__ __forceinline__ void wave_max2(int& a, int& b)
 {
     a = max(a, dpp<0xB1>(a));
     b = max(b, dpp<0xB1>(b));
@@ -63,13 +64,13 @@ __device__ __forceinline__ void wave_max2(int& a, int& b, int w)
     b = max(b, dpp<0x141>(b));
     a = max(a, dpp<0x140>(a));
     b = max(b, dpp<0x140>(b));
-    if (w > 16) {  // uniform
+    if constexpr (W > 16) {
         const auto a1 = __builtin_amdgcn_permlane16_swap(a, opaque(a), false, false);
         const auto b1 = __builtin_amdgcn_permlane16_swap(b, opaque(b), false, false);
         a = max((int)a1[0], (int)a1[1]);
         b = max((int)b1[0], (int)b1[1]);
     }
-    if (w > 32) {
+    if constexpr (W > 32) {
         const auto a2 = __builtin_amdgcn_permlane32_swap(a, opaque(a), false, false);
         const auto b2 = __builtin_amdgcn_permlane32_swap(b, opaque(b), false, false);
         a = max((int)a2[0], (int)a2[1]);
@@ -101,13 +102,115 @@ __device__ __forceinline__ int wave_sum(int v)
 }
 
 
+// The transfer loop, on one wavefront, lane r holding rank r's quota and
+// load: at most R - 1 fills (the LDS writes of a wavefront reach its own
+// later reads in order, so no barrier inside). A fill takes s, the unfilled
+// rank of largest deficit d, and l, the rank of largest excess (ties to the
+// lower rank both; d <= 0 ends the loop), moves d assignments from l's home
+// experts in donor order to s and marks s filled. The next fill's choice
+// depends only on the loads, so it is made while this fill's walk reads
+// l's remaining counts. W: lanes the argmaxes span (R <= W). SCAN: the
+// walk over l's n experts as a prefix sum, by DPP shifts inside the first
+// row (16: n <= 16) or by shuffles (64: n <= 64), the i-th expert giving
+// min(rem_i, d - (rem of the ones before it)), at least 0; 0: one lane
+// walks them in turn (n > 64). donor[r] ends as r's donor, -1 if none.
+constexpr int kZeroEntry = 256;  // E <= 256
+
+template <int W, int SCAN>
+__device__ __forceinline__ void transfer_loop(int R, int n, int lane, int my_q, int my_load,
+                                              int2* ro, int32_t* take, int32_t* ptr,
+                                              int32_t* donor)
+{
+    bool my_filled = false;
+    int my_donor = -1;
+    // argmaxes: the max over the lanes (lane 0's copy, a scalar), then the
+    // lowest lane holding it
+    auto pick = [&](int& d, int& s, int& l) {
+        int def = -1, exc = INT_MIN;
+        if (lane < R) {
+            const int dd = my_q - my_load;
+            def = (!my_filled && dd > 0) ? dd : -1;
+            exc = -dd;
+        }
+        int bd = def, be = exc;
+        wave_max2<W>(bd, be);
+        d = __builtin_amdgcn_readfirstlane(bd);
+        be = __builtin_amdgcn_readfirstlane(be);
+        s = __ffsll((unsigned long long)__ballot(lane < R && def == d)) - 1;
+        l = __ffsll((unsigned long long)__ballot(lane < R && exc == be)) - 1;
+    };
+    int d, s, l;
+    pick(d, s, l);
+    for (int it = 0; it < R && d > 0; ++it) {
+        if (lane == l) my_load -= d;
+        if (lane == s) {
+            my_load = my_q;
+            my_filled = true;
+            my_donor = l;
+        }
+        if constexpr (SCAN == 0) {
+            if (lane == 0) {
+                int left = d;
+                int p = ptr[l];
+                while (left > 0 && p < n) {
+                    const int e = ro[l * n + p].y;
+                    const int r = ro[l * n + p].x;
+                    const int t = r < left ? r : left;
+                    if (t > 0) {
+                        take[s * n + (e - l * n)] = t;
+                        ro[l * n + p].x = r - t;
+                        left -= t;
+                    }
+                    if (r - t == 0) ++p;
+                }
+                ptr[l] = p;
+            }
+            pick(d, s, l);
+        } else {
+            // lanes past n read the zero entry (they take nothing); the
+            // next choice is made while the read is in flight (kept apart
+            // from the walk's arithmetic by a scheduling barrier)
+            const int2 v = ro[lane < n ? l * n + lane : kZeroEntry];
+            int d2, s2, l2;
+            pick(d2, s2, l2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int r = v.x, e = v.y;
+            int incl = r;
+            if constexpr (SCAN == 16) {
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);
+            } else {
+                for (int off = 1; off < n; off <<= 1) {  // n is uniform
+                    const int v = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += v;
+                }
+            }
+            const int room = d - (incl - r);
+            const int t = room <= 0 ? 0 : (room < r ? room : r);
+            if (t > 0) {
+                take[s * n + (e - l * n)] = t;
+                ro[l * n + lane].x = r - t;
+            }
+            d = d2;
+            s = s2;
+            l = l2;
+        }
+    }
+    if (lane < R) donor[lane] = my_donor;
+}
+
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ plan)
 {
-    __shared__ int32_t cnt[256], rem[256], order[256], take[256], home_row[256], rep_row[256];
-    __shared__ int32_t remo[256];  // remaining count of order[i] (the transfer loop's view)
+    __shared__ int32_t cnt[256], rem[256], take[256], home_row[256], rep_row[256];
+    // the experts in donor order inside every home block, with what remains
+    // of each (the transfer loop's view): (remaining count, expert id); one
+    // more entry of zeros
+    __shared__ int2 ro[kZeroEntry + 1];
     __shared__ int32_t quota[64], load[64], donor[64], ptr[64], win[65];
     __shared__ int32_t wsum[kPlanThreads / 64];
 
@@ -150,7 +253,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
         if (lane >= off) incl += v;
     }
     if (wave == 0 && lane < R) win[lane + 1] = incl;
-    if (tid == 0) win[0] = 0;
+    if (tid == 0) {
+        win[0] = 0;
+        ro[kZeroEntry] = make_int2(0, 0);
+    }
 
     // donor order inside every rank's home block: (count desc, id asc)
     if (R > 1) {
@@ -159,86 +265,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
             int pos = 0;
             for (int x = r0; x < r0 + n; ++x)
                 pos += (cnt[x] > cnt[e] || (cnt[x] == cnt[e] && x < e)) ? 1 : 0;
-            order[r0 + pos] = e;
-            remo[r0 + pos] = cnt[e];
+            ro[r0 + pos] = make_int2(cnt[e], e);
         }
     }
     __syncthreads();
 
-    // transfer loop: at most R - 1 fills, on the first wavefront alone (its
-    // LDS writes reach its own later reads in order, so no barrier inside)
+    // transfer loop (E <= 256 and R | E: past 16 ranks a rank has at most 15
+    // experts, past 32 at most 7)
     if (wave == 0) {
-        // lane r's rank: quota, load and whether it has been filled
         const int my_q = lane < R ? quota[lane] : 0;
-        int my_load = lane < R ? load[lane] : 0;
-        bool my_filled = false;
-        for (int it = 0; it < R; ++it) {
-            int def = -1, exc = -1;
-            if (lane < R) {
-                const int d = my_q - my_load;
-                def = (!my_filled && d > 0) ? d : -1;
-                exc = -d;
-            }
-            // argmaxes, ties to the lower rank: the max over the R lanes
-            // (lane 0's copy, a scalar), then the lowest lane holding it
-            int best_def = lane < R ? def : -1, best_exc = lane < R ? exc : INT_MIN;
-            wave_max2(best_def, best_exc, R <= 16 ? 16 : R <= 32 ? 32 : 64);
-            best_def = __builtin_amdgcn_readfirstlane(best_def);
-            best_exc = __builtin_amdgcn_readfirstlane(best_exc);
-            if (best_def <= 0) break;
-            const int s = __ffsll((unsigned long long)__ballot(lane < R && def == best_def)) - 1;
-            const int l = __ffsll((unsigned long long)__ballot(lane < R && exc == best_exc)) - 1;
-            if (n <= 64) {
-                // the walk over l's experts in donor order as a prefix sum: the
-                // i-th takes min(rem_i, d - (rem of the ones before it)), at least 0
-                const int e = lane < n ? order[l * n + lane] : 0;
-                const int r = lane < n ? remo[l * n + lane] : 0;
-                int incl = r;
-                if (n <= 16) {  // inside the first row of 16 lanes: DPP shifts
-                    if (n > 1) incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);
-                    if (n > 2) incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);
-                    if (n > 4) incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);
-                    if (n > 8) incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);
-                } else {
-                    for (int off = 1; off < n; off <<= 1) {  // n is uniform
-                        const int v = __shfl_up(incl, off, 64);
-                        if (lane >= off) incl += v;
-                    }
-                }
-                const int room = best_def - (incl - r);
-                const int t = room <= 0 ? 0 : (room < r ? room : r);
-                if (t > 0) {
-                    take[s * n + (e - l * n)] = t;
-                    remo[l * n + lane] = r - t;
-                }
-            } else if (lane == 0) {  // more than 64 experts a rank: one step at a time
-                int d = best_def;
-                int p = ptr[l];
-                while (d > 0 && p < n) {
-                    const int e = order[l * n + p];
-                    const int r = remo[l * n + p];
-                    const int t = r < d ? r : d;
-                    if (t > 0) {
-                        take[s * n + (e - l * n)] = t;
-                        remo[l * n + p] = r - t;
-                        d -= t;
-                    }
-                    if (r - t == 0) ++p;
-                }
-                ptr[l] = p;
-            }
-            if (lane == l) my_load -= best_def;
-            if (lane == s) {
-                my_load = my_q;
-                my_filled = true;
-            }
-            if (lane == 0) donor[s] = l;
-        }
+        const int my_load = lane < R ? load[lane] : 0;
+        if (R > 32)
+            transfer_loop<64, 16>(R, n, lane, my_q, my_load, ro, take, ptr, donor);
+        else if (R > 16)
+            transfer_loop<32, 16>(R, n, lane, my_q, my_load, ro, take, ptr, donor);
+        else if (n <= 16)
+            transfer_loop<16, 16>(R, n, lane, my_q, my_load, ro, take, ptr, donor);
+        else if (n <= 64)
+            transfer_loop<16, 64>(R, n, lane, my_q, my_load, ro, take, ptr, donor);
+        else
+            transfer_loop<16, 0>(R, n, lane, my_q, my_load, ro, take, ptr, donor);
     }
     __syncthreads();
     // back to expert order for the layout below
     if (R > 1)
-        for (int i = tid; i < E; i += kPlanThreads) rem[order[i]] = remo[i];
+        for (int i = tid; i < E; i += kPlanThreads) rem[ro[i].y] = ro[i].x;
     __syncthreads();
 
     // Per-rank windows: segments in expert id order (the lower id block
