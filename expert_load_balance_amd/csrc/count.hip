@@ -208,26 +208,32 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
         ev[i] = 64 * i < C && a < N ? ids[a] : -1;
     }
     // a token's k assignments: when k divides 64 they sit in k adjacent
-    // lanes of one round (chunks start at multiples of 64), so the earlier
-    // ones come from the lanes below by shuffles; otherwise from memory
+    // lanes of one round (chunks start at multiples of 64). Then a repeat
+    // of an in-range id shows in the same-expert lane mask of the ranking
+    // below, and only a round holding an out-of-range id compares the raw
+    // ids here, the earlier ones from the lanes below by shuffles.
+    // Otherwise the earlier ids come from memory.
     const bool by_lanes = 64 % k == 0;
 #pragma unroll
     for (int i = 0; i < kFusedRounds; ++i) {
         if (64 * i >= C) break;
         const int a = a0 + 64 * i;
         const int32_t e = ev[i];
+        const bool out = a < N && (e < 0 || e >= E);
+        if (out) bad |= MOE_ERR_RANGE;
         if (by_lanes) {
-            const int j = lane % k;  // = a % k
-            for (int jj = 1; jj < k; ++jj) {
-                const int32_t o = __shfl(e, lane - jj);
-                if (jj <= j && a < N && o == e) bad |= MOE_ERR_REPEAT;
+            if (__ballot(out)) {
+                const int j = lane % k;  // = a % k
+                for (int jj = 1; jj < k; ++jj) {
+                    const int32_t o = __shfl(e, lane - jj);
+                    if (jj <= j && a < N && o == e) bad |= MOE_ERR_REPEAT;
+                }
             }
         } else if (a < N) {
             const int j = a % k;
             for (int jj = 1; jj <= j; ++jj)
                 if (ids[a - jj] == e) bad |= MOE_ERR_REPEAT;
         }
-        if (a < N && (e < 0 || e >= E)) bad |= MOE_ERR_RANGE;
     }
     __syncthreads();
 
@@ -235,6 +241,8 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // the lanes of this lane's token (k divides 64)
+    const uint64_t tok_mask = k >= 64 ? ~0ull : (((1ull << k) - 1) << (lane - lane % k));
     int32_t loc[kFusedRounds];
 #pragma unroll
     for (int i = 0; i < kFusedRounds; ++i) {
@@ -249,6 +257,7 @@ __global__ __launch_bounds__(kFusedThreads) void count_fused_kernel(int N, int k
             match &= bit ? bal : ~bal;
         }
         const int rank = __popcll(match & lt_mask);
+        if (by_lanes && ok && __popcll(match & tok_mask) > 1) bad |= MOE_ERR_REPEAT;
         // every matching lane reads the running count before the first of
         // them (rank 0) advances it: one wavefront's LDS operations execute
         // in order

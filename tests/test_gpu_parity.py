@@ -339,6 +339,35 @@ def test_count_repeats_across_chunks():
         np.testing.assert_array_equal(host(L.eidx), c["eidx"])
 
 
+@pytest.mark.parametrize("T,k,E", [(1024, 8, 128), (300, 2, 8), (2500, 8, 64), (256, 64, 64)])
+def test_count_error_word_matches_oracle(T, k, E):
+    # k divides 64, so a token's ids sit in adjacent lanes of one round.
+    # The error word equals the oracle's, bit for bit, for in-range repeats
+    # (in a late round of the one-workgroup count; T = 2500, k = 8 takes
+    # the three-launch path), out-of-range ids, a token repeating one
+    # out-of-range id (RANGE and REPEAT), and a mix in one round.
+    R = 4
+    shape = moe.Shape(T, 64, E, k, 64, R, 1, moe.MOE_BF16)
+    rng = np.random.default_rng(T + k)
+    base = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    cases = [[], [(T - 1, k - 1, ("copy", 0))], [(T // 2, 1, ("set", E + 3))],
+             [(T // 3, 0, ("set", -7)), (T // 3, k - 1, ("set", -7))],
+             [(5, 1, ("set", E)), (6, k - 1, ("copy", 0))]]
+    for muts in cases:
+        ids = base.copy()
+        for t, j, (how, v) in muts:
+            ids[t, j] = ids[t, v] if how == "copy" else v
+        L = MoeLayerBuffers(shape, DEV)
+        d_ids = torch.from_numpy(ids).to(DEV)
+        moe.moe_count(shape, d_ids, L.counts, L.offsets, L.eidx, L.rank_load, L.err, L.ws)
+        torch.cuda.synchronize()
+        c = oracle.count(ids, E, R)
+        assert int(L.err.item()) == c["err"], (muts, int(L.err.item()), c["err"])
+        np.testing.assert_array_equal(host(L.counts), c["counts"])
+        np.testing.assert_array_equal(host(L.eidx), c["eidx"])
+    assert oracle.count(base, E, R)["err"] == 0
+
+
 PLAN_VECTORS = [
     ("fixture", [9, 6, 5, 4, 3, 2, 2, 1], 4),
     ("balanced", [7] * 16, 8),
