@@ -283,17 +283,10 @@ __host__ __device__ constexpr int read_order(int n) { return n == 0 ? 0 : n <= 4
 struct TileRef {
     int e, n0, rows, hrow0;
 };
-// SKINNY: t indexes a skinny-tile table (one tile per group and N-tile),
-// whose tile holds the group's rows past its whole M-tiles.
-template <int MODE, bool SKINNY = false, typename SC>
-__device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
+// The tile t of group lo (lo: the group whose tiles hold t).
+template <int MODE, bool SKINNY, typename SC>
+__device__ __forceinline__ TileRef tile_in_group(int t, int lo, int E, int ntiles_n, SC sc)
 {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sc(mid) * ntiles_n <= t) lo = mid;
-        else hi = mid - 1;
-    }
     const int mt_e = sc(lo + 1) - sc(lo);
     const int local = t - sc(lo) * ntiles_n;
     const int nt = local / mt_e, mt = local % mt_e;
@@ -305,6 +298,37 @@ __device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
     r.rows = min(kTM, c_e - v0);
     r.hrow0 = sc(E + 1 + lo) + v0;
     return r;
+}
+
+// SKINNY: t indexes a skinny-tile table (one tile per group and N-tile),
+// whose tile holds the group's rows past its whole M-tiles.
+template <int MODE, bool SKINNY = false, typename SC>
+__device__ __forceinline__ TileRef tile_of(int t, int E, int ntiles_n, SC sc)
+{
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sc(mid) * ntiles_n <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return tile_in_group<MODE, SKINNY>(t, lo, E, ntiles_n, sc);
+}
+
+// tile_of for a whole workgroup (every thread calls it, with the same t):
+// the group is found in one round of independent loads, thread i testing
+// whether t falls in groups i, i + 256, ... (one non-empty interval holds
+// it), instead of a binary search of dependent loads. For kernels whose
+// first step is the lookup (the fixups).
+template <int MODE, bool SKINNY = false, typename SC>
+__device__ __forceinline__ TileRef tile_of_wg(int t, int E, int ntiles_n, SC sc)
+{
+    __shared__ int grp;
+    for (int i = threadIdx.x; i < E; i += kThreads)
+        if (sc(i) * ntiles_n <= t && t < sc(i + 1) * ntiles_n) grp = i;
+    __syncthreads();
+    // (callers pass a tile of the launch, so one group matched; the clamp
+    // only keeps the reads in the table)
+    return tile_in_group<MODE, SKINNY>(t, min(max(grp, 0), E - 1), E, ntiles_n, sc);
 }
 
 // Work split of `tiles` tiles over P workgroups: `full` whole-tile units,
@@ -1192,7 +1216,7 @@ __device__ __forceinline__ void skinny_fixup(int G, int ntiles_n, int H, int F, 
     const int64_t t0 = (int64_t)t * KT, t1 = t0 + KT;
     if (gb == t0) return;                          // the boundary is between tiles
     if (cut.first(qb - 1) > t0) return;            // an earlier boundary cuts this tile
-    const TileRef r = tile_of<MODE, true>(nfull + t, G, ntiles_n, [&](int i) { return ssched(i); });
+    const TileRef r = tile_of_wg<MODE, true>(nfull + t, G, ntiles_n, [&](int i) { return ssched(i); });
     const int q_lo = cut.piece_of(t0), q_hi = cut.piece_of(t1 - 1);
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
     constexpr int kRowsPerPass = kThreads / kQuads;
@@ -1256,15 +1280,16 @@ __device__ __forceinline__ void skinny_fixup(int G, int ntiles_n, int H, int F, 
 // Finishes the K-split leftover tiles of a bf16 GEMM launch: sums the fp32
 // partial tiles of each leftover tile in part order and writes the result
 // the whole-tile epilogue would have written (gate/up: bf16 silu(g) * u into
-// h; down: bf16 y rows at their buffer rows). Workgroup b takes leftover
+// h; down: bf16 y rows at their buffer rows). Main item b takes leftover
 // tile b / 16, rows 16 (b % 16) .. +15; a thread owns one 4-column group.
 constexpr int kFixupRows = 16;
 constexpr int kFixupSlabs = kTM / kFixupRows;
 // split leftover tiles: at most half the persistent grid (each gets >= 2 parts)
 constexpr int kFixupGrid = moe::kGemmMaxGrid / 2 * kFixupSlabs;
 
-// Workgroups past the first kFixupGrid finish the skinny kernel's cut tiles
-// (P * kSkFixupHalves per tile height).
+// The first 2 P kSkFixupHalves workgroups finish the skinny kernel's cut
+// tiles (P * kSkFixupHalves per tile height), the next kFixupGrid (main
+// items) the K-split leftover tiles.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, int H, int F, int P,
                                                          const int32_t* __restrict__ sched,
@@ -1276,8 +1301,13 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
                                                          uint16_t* __restrict__ gu_out)
 {
     const Split sp = gemm_split(G, ntiles_n, P, sched);
-    if ((int)blockIdx.x >= kFixupGrid) {
-        const int b = (int)blockIdx.x - kFixupGrid, nb = sp.ps * kSkFixupHalves;
+    // the skinny items first, so that they are not dispatched behind the
+    // main items' (mostly idle) workgroups (measured: decode T = 256 at
+    // maxvio 15, -3.5 us over its two fixups)
+    const int nsk = 2 * P * kSkFixupHalves;
+    const int mbx = (int)blockIdx.x - nsk;  // main item, if >= 0
+    if (mbx < 0) {
+        const int b = (int)blockIdx.x, nb = sp.ps * kSkFixupHalves;
         if (b < nb)
             skinny_fixup<MODE, 32>(G, ntiles_n, H, F, sp.ps, b, sched, vrow, part32, out, gu_out);
         else
@@ -1287,13 +1317,13 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(int G, int ntiles_n, in
     }
     const int KT_all = (MODE == kGateUp ? H : F) / kTK;
     const Balance bal = balance_of(sched[G] * ntiles_n, sp.pm, KT_all);
-    const int lt = blockIdx.x / kFixupSlabs;
+    const int lt = mbx / kFixupSlabs;
     if (bal.S == 1 || lt >= bal.L) return;
-    const TileRef r = tile_of<MODE>(bal.full + lt, G, ntiles_n, [&](int i) { return sched[i]; });
+    const TileRef r = tile_of_wg<MODE>(bal.full + lt, G, ntiles_n, [&](int i) { return sched[i]; });
     constexpr int kQuads = MODE == kGateUp ? kTN / 2 / 4 : kTN / 4;  // 4-column groups per row
     constexpr int kRowsPerPass = kThreads / kQuads;
     const int c = (threadIdx.x % kQuads) * 4;
-    const int row0 = (int)(blockIdx.x % kFixupSlabs) * kFixupRows;
+    const int row0 = (int)(mbx % kFixupSlabs) * kFixupRows;
     const int row_end = min(r.rows, row0 + kFixupRows);
     for (int row = row0 + threadIdx.x / kQuads; row < row_end;
          row += kRowsPerPass) {
