@@ -56,8 +56,8 @@ def parse():
                          "kept) and the backward chain, --steps times; one JSON line of its "
                          "figures (for kernel traces of the backward)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=None,
-                    help="buffer rows in the oracle's timed FFN sample (default: about 15 s "
-                         "of FFN work)")
+                    help="buffer rows in the oracle's timed FFN sample (default: 256 * k, "
+                         "256 tokens' worth of assignments)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (a known "
                          "byte count for calibrating HBM counters), then exit")
@@ -96,14 +96,15 @@ def traffic_for(workload, maxvio):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, ffn_budget_s=15.0):
+def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, n_shared_tokens=64):
     """The oracle, as it stands, on the same workload, single-threaded and
     pinned to one host core. Route, count, plan, permute and combine run on
     every token; the SwiGLU FFN runs on the first `n_ffn_rows` rows of the
-    buffer (by default about `ffn_budget_s` seconds of work; all rows when
-    they fit) and, with the shared expert on as many tokens, is extrapolated
-    per row to the whole layer (every row costs the same 3*H*F multiply-adds).
-    Host copies of the inputs are made before the clock starts."""
+    buffer (by default 256 * k: 256 tokens' worth of assignments, about 30 s
+    on the DeepSeek-V3 shape; all rows when they fit) and the shared expert
+    on the first `n_shared_tokens` tokens; both are extrapolated per row to
+    the whole layer (every row costs the same 3*H*F multiply-adds). Host
+    copies of the inputs are made before the clock starts."""
     import numpy as np
 
     import oracle
@@ -112,9 +113,7 @@ def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, ffn_bu
     w = WORKLOADS[name]
     T, H, E, k, F, R = (w[c] for c in ("T", "H", "E", "k", "F", "R"))
     N = T * k
-    est_row_s = 3.0 * H * F / 1.6e9                # the plain C loop: ~1.6 G multiply-adds/s
-    n_rows = n_ffn_rows or max(1, min(N, int(ffn_budget_s / est_row_s)))
-    n_rows = min(n_rows, N)
+    n_rows = max(1, min(N, n_ffn_rows or 256 * k))
     xs = x.float().cpu().numpy()
     ids0, _, _ = oracle.route(lg, bias, k)
     c0 = oracle.count(ids0, E, R)
@@ -130,7 +129,7 @@ def cpu_baseline(name, maxvio, lg, bias, x, wts, shared, n_ffn_rows=None, ffn_bu
     used = sorted({e for _, _, e in take})
     wh = {e: tuple(t[e].float().cpu().numpy() for t in wts) for e in used}
     sh = tuple(t[0].float().cpu().numpy() for t in shared) if shared is not None else None
-    n_sh = min(T, max(1, n_rows // k)) if shared is not None else 0
+    n_sh = min(T, max(1, n_shared_tokens)) if shared is not None else 0
 
     prev = os.sched_getaffinity(0)
     core = min(prev)
