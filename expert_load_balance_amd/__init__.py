@@ -17,7 +17,8 @@ import os
 __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "Shape", "StatsT", "lib_path", "load",
     "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
-    "moe_route", "moe_count", "moe_count_noalloc", "moe_plan", "moe_permute", "moe_grouped_gemm",
+    "moe_route", "moe_count", "moe_count_noalloc", "moe_plan", "moe_count_plan", "moe_permute",
+    "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
     "moe_repack", "capacity_shape", "moe_router_workspace_bytes", "moe_router", "moe_bias_update", "plan_tables",
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "moe_prefetch_replicas", "moe_grouped_gemm_slots", "moe_backward_workspace_bytes",
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
     "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
-    "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy", "moe_probe_read",
+    "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy", "moe_probe_read", "moe_count_plan",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -135,6 +136,7 @@ def load():
         "moe_probe_copy": (st, [_VP, _VP, ctypes.c_size_t, ctypes.c_int32, _VP]),
         "moe_probe_read": (st, [_VP, ctypes.c_size_t, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
         "moe_plan": (st, [_SP, _VP, _VP, _VP]),
+        "moe_count_plan": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]),
         "moe_permute": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_grouped_gemm": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_gemm_schedule": (st, [_SP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -359,6 +361,21 @@ def moe_plan(shape, counts, plan, stream=None):
     total = moe_plan_layout(shape)["total"]
     _ok(load().moe_plan(ctypes.byref(shape), _ptr(counts, torch.int32, "counts", shape.E),
                         _ptr(plan, torch.int32, "plan", total), _stream(stream)), "moe_plan")
+
+
+def moe_count_plan(shape, ids, counts, offsets, eidx, rank_load, err, ws, plan, stream=None):
+    """moe_count then moe_plan on its counts (one launch up to 16384
+    assignments)."""
+    import torch
+
+    i32 = torch.int32
+    total = moe_plan_layout(shape)["total"]
+    args = (ctypes.byref(shape), _ptr(ids, i32, "ids", shape.N), _ptr(counts, i32, "counts", shape.E),
+            _ptr(offsets, i32, "offsets", shape.E + 1), _ptr(eidx, i32, "eidx", shape.N),
+            _ptr(rank_load, i32, "rank_load", shape.R), _ptr(err, i32, "err", 1),
+            _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
+            _ptr(plan, i32, "plan", total), _stream(stream))
+    _ok(load().moe_count_plan(*args), "moe_count_plan")
 
 
 def moe_permute(shape, x, ids, eidx, plan, buf, dest_row, row_src, stream=None):

@@ -136,6 +136,22 @@ moe_status_t moe_plan(const moe_shape_t* shape, const int32_t* d_counts, int32_t
     return dev(moe_launch_plan(*shape, d_counts, d_plan, as_stream(stream)));
 }
 
+moe_status_t moe_count_plan(const moe_shape_t* shape, const int32_t* d_ids, int32_t* d_counts,
+                            int32_t* d_offsets, int32_t* d_eidx, int32_t* d_rank_load,
+                            int32_t* d_err, void* d_ws, size_t ws_bytes, int32_t* d_plan,
+                            moe_stream_t stream)
+{
+    moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    const int64_t N = (int64_t)shape->T * shape->k;
+    if (bad(d_ids, N) || !d_counts || !d_offsets || bad(d_eidx, N) || !d_rank_load || !d_err ||
+        !d_ws || !d_plan)
+        return MOE_EINVAL;
+    if (ws_bytes < moe::ws_layout(*shape).total) return MOE_EINVAL;
+    return dev(moe_launch_count_plan(*shape, d_ids, d_counts, d_offsets, d_eidx, d_rank_load, d_err,
+                                     static_cast<char*>(d_ws), d_plan, as_stream(stream)));
+}
+
 moe_status_t moe_permute(const moe_shape_t* shape, const void* d_x, const int32_t* d_ids,
                          const int32_t* d_eidx, const int32_t* d_plan, void* d_buf,
                          int32_t* d_dest_row, int32_t* d_row_src, moe_stream_t stream)

@@ -260,6 +260,11 @@ hipError_t moe_launch_count_noalloc(const moe_shape_t& s, const int32_t* ids, in
                                     int32_t* err, hipStream_t st);
 hipError_t moe_launch_plan(const moe_shape_t& s, const int32_t* counts, int32_t* plan,
                            hipStream_t st);
+// moe_launch_count then moe_launch_plan, in one launch up to 16384
+// assignments.
+hipError_t moe_launch_count_plan(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                                 int32_t* offsets, int32_t* eidx, int32_t* rank_load,
+                                 int32_t* err, char* ws, int32_t* plan, hipStream_t st);
 hipError_t moe_launch_permute(const moe_shape_t& s, const void* x, const int32_t* ids,
                               const int32_t* eidx, const int32_t* plan, void* buf,
                               int32_t* dest_row, int32_t* row_src, hipStream_t st);

@@ -31,6 +31,7 @@
 #include <climits>
 
 #include "common.h"
+#include "count_fused.h"
 
 namespace {
 
@@ -203,8 +204,10 @@ __device__ __forceinline__ void transfer_loop(int R, int n, int lane, int my_q, 
 
 constexpr int kPlanThreads = 1024;
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ plan)
+// The plan from the counts (global memory, or the fused count's LDS copy).
+// Every thread of the workgroup calls it.
+__device__ __forceinline__ void plan_body(int E, int R, const int32_t* __restrict__ counts,
+                                          int32_t* __restrict__ plan)
 {
     __shared__ int32_t cnt[256], rem[256], take[256], home_row[256], rep_row[256];
     // the experts in donor order inside every home block, with what remains
@@ -433,11 +436,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const 
     }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int E, int R, const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ plan)
+{
+    plan_body(E, R, counts, plan);
+}
+
+// Count and plan in one launch (up to 16384 assignments, where the count is
+// one workgroup of the same size): the plan reads the counts from the
+// count's LDS copy. Results are those of the two launches, bit for bit.
+static_assert(kPlanThreads == moe::cnt::kFusedThreads, "one workgroup runs both");
+__global__ __launch_bounds__(kPlanThreads) void count_plan_kernel(
+    int N, int k, int E, int R, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ eidx, int32_t* __restrict__ rank_load,
+    int32_t* err, int32_t* __restrict__ plan)
+{
+    __shared__ int32_t hist[256];
+    moe::cnt::count_fused_body(N, k, E, R, ids, counts, offsets, eidx, rank_load, err, hist);
+    __syncthreads();
+    plan_body(E, R, hist, plan);
+}
+
 }  // namespace
 
 hipError_t moe_launch_plan(const moe_shape_t& s, const int32_t* counts, int32_t* plan,
                            hipStream_t st)
 {
     plan_kernel<<<1, kPlanThreads, 0, st>>>(s.E, s.R, counts, plan);
+    return hipGetLastError();
+}
+
+hipError_t moe_launch_count_plan(const moe_shape_t& s, const int32_t* ids, int32_t* counts,
+                                 int32_t* offsets, int32_t* eidx, int32_t* rank_load,
+                                 int32_t* err, char* ws, int32_t* plan, hipStream_t st)
+{
+    const int64_t N = (int64_t)s.T * s.k;
+    if (N > moe::cnt::kFusedMax) {
+        const hipError_t e = moe_launch_count(s, ids, counts, offsets, eidx, rank_load, err, ws, st);
+        if (e != hipSuccess) return e;
+        return moe_launch_plan(s, counts, plan, st);
+    }
+    count_plan_kernel<<<1, kPlanThreads, 0, st>>>((int)N, s.k, s.E, s.R, ids, counts, offsets,
+                                                   eidx, rank_load, err, plan);
     return hipGetLastError();
 }

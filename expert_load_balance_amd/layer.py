@@ -9,11 +9,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_BF16, Shape, moe_combine, moe_count, moe_gemm_down, moe_gemm_gateup,
+from . import (MOE_BF16, Shape, moe_combine, moe_count_plan, moe_gemm_down, moe_gemm_gateup,
                moe_gemm_schedule, moe_grouped_gemm_slots, moe_grouped_gemm_train, moe_permute,
                moe_plan, moe_plan_layout, moe_prefetch_replicas, moe_route, moe_workspace_bytes)
 
-STAGES = ("route", "count", "plan", "permute", "gemm_schedule", "gemm_gateup", "gemm_down",
+STAGES = ("route", "count_plan", "permute", "gemm_schedule", "gemm_gateup", "gemm_down",
           "shared", "combine")
 
 
@@ -65,7 +65,8 @@ class MoeLayerBuffers:
 
     def forward(self, logits, bias, x, w_gate, w_up, w_down, shared_w=None, stream=None,
                 marks=None, pool=None, gu=None):
-        """Route -> count -> plan -> permute -> grouped GEMM -> (shared) -> combine.
+        """Route -> count + plan (one launch up to 16384 assignments) -> permute ->
+        grouped GEMM -> (shared) -> combine.
 
         marks: optional dict stage -> (start_event, end_event) recorded around
         each stage on the stream ("gemm" spans the routed grouped GEMM's three
@@ -86,13 +87,10 @@ class MoeLayerBuffers:
         mark("route", 0)
         moe_route(s, logits, bias, self.ids, self.w, self.err, st)
         mark("route", 1)
-        mark("count", 0)
-        moe_count(s, self.ids, self.counts, self.offsets, self.eidx, self.rank_load, self.err,
-                  self.ws, st)
-        mark("count", 1)
-        mark("plan", 0)
-        moe_plan(s, self.counts, self.plan, st)
-        mark("plan", 1)
+        mark("count_plan", 0)
+        moe_count_plan(s, self.ids, self.counts, self.offsets, self.eidx, self.rank_load, self.err,
+                       self.ws, self.plan, st)
+        mark("count_plan", 1)
         if pool is not None:
             mark("prefetch", 0)
             moe_prefetch_replicas(s, self.plan, w_gate, w_up, w_down, pool, st)

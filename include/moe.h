@@ -214,6 +214,18 @@ moe_status_t moe_count_noalloc(const moe_shape_t *shape, const int32_t *d_ids, i
 moe_status_t moe_plan(const moe_shape_t *shape, const int32_t *d_counts, int32_t *d_plan,
                       moe_stream_t stream);
 
+/* [Hotspot] "Separate expert demand from rank placement" then [MoonEP]
+ * paragraphs 3-4: moe_count followed by moe_plan on its counts, with the
+ * same arguments and results, bit for bit. Up to 16384 assignments (the
+ * decode regime, where a launch costs more than either step's work) both
+ * run in one single-workgroup launch, the plan reading the counts from the
+ * workgroup's LDS; above that it is the two calls' launches in turn.
+ *   d_ids .. d_err, d_ws / ws_bytes as moe_count; d_plan as moe_plan. */
+moe_status_t moe_count_plan(const moe_shape_t *shape, const int32_t *d_ids, int32_t *d_counts,
+                            int32_t *d_offsets, int32_t *d_eidx, int32_t *d_rank_load,
+                            int32_t *d_err, void *d_ws, size_t ws_bytes, int32_t *d_plan,
+                            moe_stream_t stream);
+
 /* [Primer] phase (b) (a token goes only to its k experts); [MoonEP]
  * paragraph 3 (zero-copy placement into static shapes). Assignment (t,j)
  * with expert e and stable index v goes to piece p of e with

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 37
+    assert len(names) == 38
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -108,6 +108,11 @@ def test_null_and_bad_shape_rejected_before_launch(lib):
     assert lib.moe_route(ctypes.byref(s.replace(R=3)), p, None, p, p, p, None) == 1
     assert lib.moe_count(ctypes.byref(s), p, p, p, p, p, p, p, 1, None) == 1  # workspace too small
     assert lib.moe_plan(ctypes.byref(s), None, p, None) == 1
+    ws_ok = moe.moe_workspace_bytes(s)
+    assert lib.moe_count_plan(ctypes.byref(s), p, p, p, p, p, p, p, 1, p, None) == 1  # short ws
+    assert lib.moe_count_plan(ctypes.byref(s), p, p, p, p, p, p, p, ws_ok, None, None) == 1  # no plan
+    assert lib.moe_count_plan(ctypes.byref(s.replace(R=3)), p, p, p, p, p, p, p, ws_ok, p,
+                              None) == 1
     assert lib.moe_permute(ctypes.byref(s), p, p, p, p, None, p, p, None) == 1
     assert lib.moe_grouped_gemm(ctypes.byref(s), p, p, p, p, p, p, p, 1, None) == 1
     assert lib.moe_combine(ctypes.byref(s), p, p, None, None, p, None) == 1

@@ -368,6 +368,40 @@ def test_count_error_word_matches_oracle(T, k, E):
     assert oracle.count(base, E, R)["err"] == 0
 
 
+COUNT_PLAN_SHAPES = [(1, 8, 2, 4), (256, 128, 8, 16), (2048, 8, 8, 8), (2048, 256, 8, 64),
+                     (3277, 36, 5, 12), (1, 256, 64, 32), (16384, 64, 1, 4), (16385, 64, 1, 4),
+                     (2049, 256, 8, 32)]
+
+
+@pytest.mark.parametrize("T,E,k,R", COUNT_PLAN_SHAPES,
+                         ids=[f"T{t}_E{e}_k{k}_R{r}" for t, e, k, r in COUNT_PLAN_SHAPES])
+def test_count_plan_matches_separate_calls(T, E, k, R):
+    # The fused count + plan (one launch up to 16384 assignments, the two
+    # launches above: T = 16385 with k = 1 and T = 2049 with k = 8) gives
+    # moe_count's and moe_plan's outputs bit for bit, and the oracle's.
+    shape = moe.Shape(T, 64, E, k, 64, R, 1, moe.MOE_BF16)
+    rng = np.random.default_rng(T * 7 + E + k + R)
+    skew = rng.zipf(1.5, E).astype(np.float64)             # uneven expert popularity
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=skew / skew.sum())
+                    for _ in range(T)]).astype(np.int32)
+    d_ids = torch.from_numpy(ids).to(DEV)
+    A, B = MoeLayerBuffers(shape, DEV), MoeLayerBuffers(shape, DEV)
+    moe.moe_count(shape, d_ids, A.counts, A.offsets, A.eidx, A.rank_load, A.err, A.ws)
+    moe.moe_plan(shape, A.counts, A.plan)
+    moe.moe_count_plan(shape, d_ids, B.counts, B.offsets, B.eidx, B.rank_load, B.err, B.ws, B.plan)
+    torch.cuda.synchronize()
+    for name in ("counts", "offsets", "eidx", "rank_load", "err", "plan"):
+        np.testing.assert_array_equal(host(getattr(B, name)), host(getattr(A, name)), err_msg=name)
+    c = oracle.count(ids, E, R)
+    np.testing.assert_array_equal(host(B.counts), c["counts"])
+    np.testing.assert_array_equal(host(B.eidx), c["eidx"])
+    pl = oracle.plan(c["counts"], R)
+    gt = moe.plan_tables(B.plan, shape)
+    for name in oracle.PLAN_TABLES:
+        np.testing.assert_array_equal(host(gt[name]), pl[name], err_msg=name)
+    assert int(B.err.item()) == 0
+
+
 PLAN_VECTORS = [
     ("fixture", [9, 6, 5, 4, 3, 2, 2, 1], 4),
     ("balanced", [7] * 16, 8),
