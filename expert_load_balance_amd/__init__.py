@@ -16,8 +16,8 @@ import os
 
 __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "Shape", "StatsT", "lib_path", "load",
-    "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_workspace_bytes",
-    "moe_route", "moe_count", "moe_count_noalloc", "moe_plan", "moe_count_plan", "moe_permute",
+    "moe_status_str", "moe_check_shape", "moe_plan_layout", "moe_plan_bytes", "moe_plan_bind",
+    "moe_workspace_bytes", "moe_route", "moe_count", "moe_count_noalloc", "moe_plan", "moe_count_plan", "moe_permute",
     "moe_grouped_gemm",
     "moe_gemm_schedule", "moe_gemm_gateup", "moe_gemm_down", "moe_combine", "moe_stats",
     "moe_capacity_rows", "moe_capacity_dispatch", "moe_capacity_plan", "moe_capacity_combine",
@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "moe_combine_backward", "moe_ffn_backward", "moe_permute_backward", "moe_route_backward",
     "moe_grouped_gemm_train", "moe_replica_grad_bytes", "moe_ffn_backward_replicas",
     "moe_count_noalloc", "moe_probe_mfma", "moe_probe_copy", "moe_probe_read", "moe_count_plan",
+    "moe_plan_bytes", "moe_plan_bind",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +84,14 @@ class PlanLayoutT(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "quota", "win_off", "seg_num", "seg_expert", "seg_row", "seg_cnt", "slots_needed",
         "slot_expert", "donor", "piece_num", "piece_rank", "piece_row", "piece_cnt", "total")]
+
+
+PLAN_T_FIELDS = ("quota", "win_off", "seg_expert", "seg_row", "seg_cnt", "seg_num", "slot_expert",
+                 "slots_needed", "piece_rank", "piece_row", "piece_cnt", "piece_num", "donor")
+
+
+class PlanT(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in PLAN_T_FIELDS]
 
 
 class StatsT(ctypes.Structure):
@@ -129,6 +138,8 @@ def load():
         "moe_check_shape": (st, [_SP]),
         "moe_plan_layout": (st, [_SP, ctypes.POINTER(PlanLayoutT)]),
         "moe_workspace_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_plan_bytes": (ctypes.c_size_t, [_SP]),
+        "moe_plan_bind": (st, [_SP, _VP, ctypes.POINTER(PlanT)]),
         "moe_route": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "moe_count": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
         "moe_count_noalloc": (st, [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -283,6 +294,19 @@ def moe_plan_layout(shape: Shape) -> dict:
     out = PlanLayoutT()
     _ok(load().moe_plan_layout(ctypes.byref(shape), ctypes.byref(out)), "moe_plan_layout")
     return {n: getattr(out, n) for n, _ in out._fields_}
+
+
+def moe_plan_bytes(shape: Shape) -> int:
+    return int(load().moe_plan_bytes(ctypes.byref(shape)))
+
+
+def moe_plan_bind(shape: Shape, block_addr: int) -> dict:
+    """Table name -> address inside the plan block at `block_addr` (an
+    integer address; the block is never dereferenced)."""
+    out = PlanT()
+    _ok(load().moe_plan_bind(ctypes.byref(shape), ctypes.c_void_p(block_addr), ctypes.byref(out)),
+        "moe_plan_bind")
+    return {n: getattr(out, n) for n in PLAN_T_FIELDS}
 
 
 def moe_workspace_bytes(shape: Shape) -> int:

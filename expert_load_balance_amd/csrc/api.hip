@@ -82,6 +82,35 @@ moe_status_t moe_plan_layout(const moe_shape_t* shape, moe_plan_layout_t* out)
     return MOE_OK;
 }
 
+size_t moe_plan_bytes(const moe_shape_t* shape)
+{
+    if (check(shape) != MOE_OK) return 0;
+    return (size_t)moe::plan_layout(shape->E, shape->R).total * sizeof(int32_t);
+}
+
+moe_status_t moe_plan_bind(const moe_shape_t* shape, void* block, moe_plan_t* out)
+{
+    const moe_status_t st = check(shape);
+    if (st != MOE_OK) return st;
+    if (!block || !out) return MOE_EINVAL;
+    const moe::PlanLayout L = moe::plan_layout(shape->E, shape->R);
+    int32_t* b = static_cast<int32_t*>(block);
+    out->quota = b + L.quota;
+    out->win_off = b + L.win_off;
+    out->seg_expert = b + L.seg_expert;
+    out->seg_row = b + L.seg_row;
+    out->seg_cnt = b + L.seg_cnt;
+    out->seg_num = b + L.seg_num;
+    out->slot_expert = b + L.slot_expert;
+    out->slots_needed = b + L.slots_needed;
+    out->piece_rank = b + L.piece_rank;
+    out->piece_row = b + L.piece_row;
+    out->piece_cnt = b + L.piece_cnt;
+    out->piece_num = b + L.piece_num;
+    out->donor = b + L.donor;
+    return MOE_OK;
+}
+
 size_t moe_workspace_bytes(const moe_shape_t* shape)
 {
     if (check(shape) != MOE_OK) return 0;

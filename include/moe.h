@@ -151,6 +151,23 @@ moe_status_t moe_check_shape(const moe_shape_t *shape);
 /* Fills *out with the plan block layout for this shape. */
 moe_status_t moe_plan_layout(const moe_shape_t *shape, moe_plan_layout_t *out);
 
+/* The plan block's tables by name: pointers into one block (the layout
+ * above). Every call that takes a plan takes the block's base, d_plan. */
+typedef struct moe_plan {
+    int32_t *quota, *win_off, *seg_expert, *seg_row, *seg_cnt, *seg_num, *slot_expert,
+        *slots_needed, *piece_rank, *piece_row, *piece_cnt, *piece_num, *donor;
+} moe_plan_t;
+
+/* [MoonEP] paragraph 3 (static buffer shapes: the plan's tables have a size
+ * fixed by the shape). Bytes of the plan block: layout.total * 4; 0 on a
+ * bad shape. The caller allocates one block of this size. */
+size_t moe_plan_bytes(const moe_shape_t *shape);
+
+/* Carves a plan block of moe_plan_bytes(shape) bytes at `block` (device or
+ * host memory; never dereferenced) into the named table pointers of *out.
+ * MOE_EINVAL on a NULL block or out. */
+moe_status_t moe_plan_bind(const moe_shape_t *shape, void *block, moe_plan_t *out);
+
 /* Bytes of device workspace moe_count, moe_grouped_gemm and moe_stats need
  * (count scratch, GEMM tile schedule, the SwiGLU activations h[N][F], the
  * statistics reductions). 0 on a bad

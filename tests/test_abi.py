@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 38
+    assert len(names) == 40
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(moe.EXPORTED_SYMBOLS) == names
@@ -125,6 +125,26 @@ def test_null_and_bad_shape_rejected_before_launch(lib):
     assert lib.moe_count_noalloc(ctypes.byref(s), None, p, p, p, p, p, None) == 1
     big = moe.Shape(1 << 20, 64, 256, 8, 64, 32, 8, moe.MOE_BF16)
     assert lib.moe_count_noalloc(ctypes.byref(big), p, p, p, p, p, p, None) == 1
+
+
+def test_plan_bytes_and_bind_follow_the_layout(lib):
+    # the named tables of moe_plan_bind sit at the layout's offsets of one
+    # block of moe_plan_bytes (host arithmetic only; the block is not touched)
+    for shp in [(16, 64, 8, 2, 128, 4, 2), (300, 64, 36, 5, 64, 12, 2), (8192, 7168, 256, 8, 2048, 32, 8)]:
+        s = moe.Shape(*shp, moe.MOE_BF16)
+        L = moe.moe_plan_layout(s)
+        assert moe.moe_plan_bytes(s) == 4 * L["total"]
+        base = 1 << 20
+        t = moe.moe_plan_bind(s, base)
+        for name in moe.PLAN_T_FIELDS:
+            assert t[name] == base + 4 * L[name], name
+    bad = moe.Shape(16, 64, 8, 2, 128, 3, 2, moe.MOE_BF16)     # R does not divide E
+    assert moe.moe_plan_bytes(bad) == 0
+    out = moe.PlanT()
+    assert lib.moe_plan_bind(ctypes.byref(bad), ctypes.c_void_p(1 << 20), ctypes.byref(out)) == 1
+    good = moe.Shape(16, 64, 8, 2, 128, 4, 2, moe.MOE_BF16)
+    assert lib.moe_plan_bind(ctypes.byref(good), None, ctypes.byref(out)) == 1
+    assert lib.moe_plan_bind(ctypes.byref(good), ctypes.c_void_p(1 << 20), None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
