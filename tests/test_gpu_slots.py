@@ -177,15 +177,19 @@ def test_slots_full_size(name, maxvio):
     moe.moe_grouped_gemm(shape, L.buf, L.plan, *wts, L.y, L.ws)
     torch.cuda.synchronize()
     assert_tol(host(y), host(L.y).astype(np.float64), moe.MOE_BF16, "y slots vs y experts")
-    # sampled rows of the first replica segment that reads a slot, vs the oracle
+    # every replica segment that reads a slot: its first, middle and last rows
+    # against the oracle (a filled slot holds its expert's weights)
     src = oracle.slot_sources(pl, S)
-    r, i = map(int, np.argwhere(src >= 0)[0])
-    j, e = int(src[r, i]), int(pl["seg_expert"][r, i])
-    row0, cnt = int(pl["seg_row"][r, i]), int(pl["seg_cnt"][r, i])
-    rows = np.unique(np.linspace(row0, row0 + cnt - 1, 6).astype(int))
-    wsl = [host(wts[q][e]) for q in range(3)]      # a filled slot holds its expert's weights
-    ref = oracle.ffn_rows(L.oracle_buf[rows], wsl[0], wsl[1], wsl[2])
-    assert_tol(host(y[rows]), ref, moe.MOE_BF16, f"replica rows of expert {e} on rank {r}")
+    segs = [tuple(map(int, ri)) for ri in np.argwhere(src >= 0)]
+    assert segs
+    yh = host(y)
+    for r, i in segs:
+        e = int(pl["seg_expert"][r, i])
+        row0, cnt = int(pl["seg_row"][r, i]), int(pl["seg_cnt"][r, i])
+        rows = np.unique(np.linspace(row0, row0 + cnt - 1, 3).astype(int))
+        wsl = [host(wts[q][e]) for q in range(3)]
+        ref = oracle.ffn_rows(L.oracle_buf[rows], wsl[0], wsl[1], wsl[2])
+        assert_tol(yh[rows], ref, moe.MOE_BF16, f"replica rows of expert {e} on rank {r}, slot {int(src[r, i])}")
 
 
 def test_layer_forward_with_pool():
