@@ -1031,15 +1031,24 @@ __device__ __forceinline__ int skinny_phase(
             boff[i] = MODE == kGateUp ? (uint32_t)min(n0 + (rb & 127), F - 1) * (uint32_t)H * 2u + ch
                                       : (uint32_t)min(n0 + rb, H - 1) * (uint32_t)F * 2u + ch;
         }
+        // stage st of the segment covers its K-stage (st + rot) mod nst with
+        // rot = tile mod nst: as in the 256-row tiles' down projection,
+        // neighbouring tiles (each streaming its own weight tile) copy
+        // different 128-byte columns at once, so rows a power of two bytes
+        // apart do not crowd a few memory channels. Measured against the
+        // unstaggered build: decode64 @ 1 gate/up (all skinny, 8 KB rows)
+        // 8 % faster, decode256 1-2 %, no change elsewhere.
+        const int rot = uni(cur.t % nst);
         auto copy_stage = [&](int st) {
             const uint32_t slot = ring_u + (uint32_t)(st % kSkSlots) * kSkSlot;
+            const int x = st + rot;
+            const int kb = (x >= nst ? x - nst : x) * (kTK * 2);
 #pragma unroll
             for (int i = 0; i < SK::kACopies; ++i)
-                copy16_or_zero(abase + st * (kTK * 2), aoff[i], slot + wave * 1024 + i * 4096);
+                copy16_or_zero(abase + kb, aoff[i], slot + wave * 1024 + i * 4096);
 #pragma unroll
             for (int i = 0; i < kCopiesWave; ++i)
-                copy16((i < 4 ? bbase0 : bbase1) + st * (kTK * 2), boff[i],
-                       slot + kSkA + wave * 1024 + i * 4096);
+                copy16((i < 4 ? bbase0 : bbase1) + kb, boff[i], slot + kSkA + wave * 1024 + i * 4096);
         };
         f32x16 acc[kNB][2];
 #pragma unroll
